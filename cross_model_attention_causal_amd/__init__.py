@@ -1,0 +1,332 @@
+"""Python binding of ``libcma.so``: cross-model reuse of causal attention maps on MI355X.
+
+Argument marshalling only. Every step of the path runs in the library's HIP
+kernels; torch tensors provide device memory and the current HIP stream. There
+is no fallback: if the library is missing or a tensor is not on the GPU, the
+call raises.
+
+Entry points (same names as the C ABI in ``include/cma.h``):
+``attn_maps``, ``head_map_cosine``, ``block_compress``, ``mapped_av``,
+``onehot_mix``, ``mapped_layers``; ``Varlen`` describes packed sequences.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcma.so")
+
+CMA_OK, CMA_EINVAL, CMA_EUNSUPPORTED, CMA_ENOSPC, CMA_EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+DENSE, PACKED = 0, 1
+SRC_DENSE, SRC_BSR = 0, 1
+BLOCK = 64
+
+EXPORTS = [
+    "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
+    "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks",
+    "cma_block_compress_workspace", "cma_block_compress", "cma_mapped_av_workspace",
+    "cma_mapped_av", "cma_onehot_mix", "cma_mapped_layers",
+]
+
+
+class CmaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"cma status {status}: {msg}")
+        self.status = status
+
+
+class _CVarlen(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("cu_seqlens_q", ctypes.c_void_p),
+                ("cu_seqlens_k", ctypes.c_void_p), ("seqused_q", ctypes.c_void_p),
+                ("seqused_k", ctypes.c_void_p), ("max_seqlen_q", ctypes.c_int32),
+                ("max_seqlen_k", ctypes.c_int32), ("total_q", ctypes.c_int64),
+                ("total_k", ctypes.c_int64)]
+
+
+class _CMapsSrc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("maps", ctypes.c_void_p), ("maps_dt", ctypes.c_int),
+                ("layout", ctypes.c_int), ("head_stride", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("vals", ctypes.c_void_p), ("n_block_rows", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load ``libcma.so`` and declare its C signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python __graft_entry__.py` or "
+                          "`python cross_model_attention_causal_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+    F = ctypes.c_float
+    sig = {
+        "cma_version": (ctypes.c_int, []),
+        "cma_last_error": (ctypes.c_char_p, []),
+        "cma_maps_elems": (I64, [I32, P, P, ctypes.c_int]),
+        "cma_attn_maps": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, P, ctypes.c_int,
+                                         ctypes.c_int, I64, P]),
+        "cma_head_map_cosine_workspace": (SZ, [I32, I32, I32, I64, ctypes.c_int]),
+        "cma_head_map_cosine": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, I32, I64, I64, I64,
+                                               I64, I64, P, P, P, P, SZ, P]),
+        "cma_bsr_max_blocks": (I64, [I32, I32, P]),
+        "cma_block_compress_workspace": (SZ, [I32, I32, I32, I64]),
+        "cma_block_compress": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, F, I32, P, P,
+                                              P, I64, P, P, P, P, SZ, P]),
+        "cma_mapped_av_workspace": (SZ, [P, I32, I32, I64]),
+        "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, P, ctypes.c_int, I32, P, P,
+                                         ctypes.c_int, P, SZ, P]),
+        "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
+        "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != CMA_OK:
+        raise CmaError(status, _lib.cma_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Varlen:
+    """Packed sequences: start rows ``cu_q``/``cu_k`` (host sequences of n+1 ints)
+    and optional used lengths ``used_q``/``used_k`` (host sequences of n ints).
+
+    Device copies are made once; host copies size the outputs.
+    """
+
+    def __init__(self, cu_q, cu_k=None, used_q=None, used_k=None, device="cuda"):
+        torch = _torch()
+        self.cu_q_host = np.asarray(cu_q, dtype=np.int64)
+        self.cu_k_host = np.asarray(cu_k if cu_k is not None else cu_q, dtype=np.int64)
+        n = len(self.cu_q_host) - 1
+        self.n_seqs = n
+        if used_k is None and cu_k is None:
+            used_k = used_q  # keys share the query layout
+        self.lens_q = np.asarray(used_q if used_q is not None else np.diff(self.cu_q_host), dtype=np.int64)
+        self.lens_k = np.asarray(used_k if used_k is not None else np.diff(self.cu_k_host), dtype=np.int64)
+        mk = lambda a: torch.tensor(np.asarray(a, dtype=np.int32), device=device)
+        self.cu_q = mk(self.cu_q_host)
+        self.cu_k = mk(self.cu_k_host)
+        self.used_q = mk(self.lens_q) if used_q is not None else None
+        self.used_k = mk(self.lens_k) if used_k is not None else None
+        self.max_q = int(self.lens_q.max()) if n else 0
+        self.max_k = int(self.lens_k.max()) if n else 0
+        self.n_block_rows = int(sum((int(x) + BLOCK - 1) // BLOCK for x in self.lens_q))
+
+    @staticmethod
+    def from_lengths(lens_q, lens_k=None, device="cuda"):
+        cu_q = np.concatenate([[0], np.cumsum(lens_q)])
+        cu_k = np.concatenate([[0], np.cumsum(lens_k)]) if lens_k is not None else None
+        return Varlen(cu_q, cu_k, device=device)
+
+    def c(self, total_q, total_k):
+        v = _CVarlen()
+        v.n_seqs = self.n_seqs
+        v.cu_seqlens_q = self.cu_q.data_ptr()
+        v.cu_seqlens_k = self.cu_k.data_ptr()
+        v.seqused_q = self.used_q.data_ptr() if self.used_q is not None else None
+        v.seqused_k = self.used_k.data_ptr() if self.used_k is not None else None
+        v.max_seqlen_q = self.max_q
+        v.max_seqlen_k = self.max_k
+        v.total_q = int(total_q)
+        v.total_k = int(total_k)
+        return v
+
+    def maps_elems(self, layout):
+        lib = load_library()
+        lq = np.ascontiguousarray(self.lens_q, dtype=np.int32)
+        lk = np.ascontiguousarray(self.lens_k, dtype=np.int32)
+        r = lib.cma_maps_elems(self.n_seqs, lq.ctypes.data, lk.ctypes.data, layout)
+        if r < 0:
+            raise ValueError("inconsistent sequence lengths")
+        return int(r)
+
+
+def attn_maps(q, k, scale, bias, vl: Varlen, layout=PACKED, out_dtype=None, out=None):
+    """Causal maps of every (head, sequence); returns ``[H, head_stride]`` (see cma.h)."""
+    torch = _torch()
+    lib = load_library()
+    H, Tq, d = q.shape
+    out_dtype = out_dtype or torch.bfloat16
+    stride = vl.maps_elems(layout)
+    if out is None:
+        out = torch.empty((H, stride), dtype=out_dtype, device=q.device)
+    cvl = vl.c(Tq, k.shape[1])
+    _check(lib.cma_attn_maps(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dt(q), H, d, ctypes.byref(cvl),
+                             _dev_ptr(scale, "scale"), _dev_ptr(bias, "bias"), _dev_ptr(out, "out"),
+                             _dt(out), layout, out.shape[1], _stream()))
+    return out
+
+
+def head_map_cosine(recv, send, n_batch, n_recv, n_send, length, recv_hstride, recv_bstride,
+                    send_hstride, send_bstride, want_cos=True, want_margin=True):
+    """Cosine head map of ``n_batch`` problems; ``recv``/``send`` are base tensors
+    addressed with element strides. Returns (cos or None, argmax int32, margin or None)."""
+    torch = _torch()
+    lib = load_library()
+    dev = recv.device
+    dt = _dt(recv)
+    ws_bytes = lib.cma_head_map_cosine_workspace(n_batch, n_recv, n_send, length, dt)
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    cos = torch.empty((n_batch, n_recv, n_send), dtype=torch.float32, device=dev) if want_cos else None
+    arg = torch.empty((n_batch, n_recv), dtype=torch.int32, device=dev)
+    mar = torch.empty((n_batch, n_recv), dtype=torch.float32, device=dev) if want_margin else None
+    _check(lib.cma_head_map_cosine(recv.data_ptr(), send.data_ptr(), dt, n_batch, n_recv, n_send,
+                                   length, recv_hstride, recv_bstride, send_hstride, send_bstride,
+                                   _dev_ptr(cos, "cos"), _dev_ptr(arg, "argmax"),
+                                   _dev_ptr(mar, "margin"), ws.data_ptr(), ws_bytes, _stream()))
+    return cos, arg, mar
+
+
+def bsr_max_blocks(n_heads, lens):
+    lib = load_library()
+    a = np.ascontiguousarray(lens, dtype=np.int32)
+    return int(lib.cma_bsr_max_blocks(n_heads, len(a), a.ctypes.data))
+
+
+class Workspace:
+    """Reusable device scratch for repeated calls (no allocation once large enough)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=False,
+                   want_stats=False, workspace: Workspace | None = None, bsr=None):
+    """Two-phase block-sparse compression. Returns a dict with row_ptr, col_idx,
+    vals (bf16 [capacity, 64, 64]), nnz (device int32[1]) and optional masses/stats.
+    ``bsr`` may pass preallocated output arrays to reuse."""
+    torch = _torch()
+    lib = load_library()
+    H, Tq, d = q.shape
+    dev = q.device
+    nbr = vl.n_block_rows
+    if bsr is None:
+        if capacity is None:
+            capacity = bsr_max_blocks(H, vl.lens_q)
+        bsr = dict(row_ptr=torch.empty(H * nbr + 1, dtype=torch.int32, device=dev),
+                   col_idx=torch.empty(max(1, capacity), dtype=torch.int32, device=dev),
+                   vals=torch.empty((max(1, capacity), BLOCK, BLOCK), dtype=torch.bfloat16, device=dev),
+                   nnz=torch.empty(1, dtype=torch.int32, device=dev), capacity=capacity)
+    n_tri = int(sum(((int(n) + BLOCK - 1) // BLOCK) * ((int(n) + BLOCK - 1) // BLOCK + 1) // 2 for n in vl.lens_q))
+    mass = torch.empty((H, n_tri), dtype=torch.float32, device=dev) if want_mass else None
+    stats = torch.empty((H, Tq, 2), dtype=torch.float32, device=dev) if want_stats else None
+    ws_bytes = lib.cma_block_compress_workspace(H, nbr, vl.max_q, Tq)
+    ws = (workspace or Workspace()).get(ws_bytes, dev)
+    cvl = vl.c(Tq, k.shape[1])
+    _check(lib.cma_block_compress(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dt(q), H, d, ctypes.byref(cvl),
+                                  _dev_ptr(scale, "scale"), _dev_ptr(bias, "bias"), float(tau), nbr,
+                                  _dev_ptr(bsr["row_ptr"], "row_ptr"), _dev_ptr(bsr["col_idx"], "col_idx"),
+                                  _dev_ptr(bsr["vals"], "vals"), bsr["capacity"],
+                                  _dev_ptr(bsr["nnz"], "nnz"), _dev_ptr(mass, "block_mass"),
+                                  _dev_ptr(stats, "row_stats"), ws.data_ptr(), ws.numel(), _stream()))
+    out = dict(bsr)
+    out.update(block_mass=mass, row_stats=stats, n_block_rows=nbr, n_heads=H)
+    return out
+
+
+def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_stride=None,
+              workspace: Workspace | None = None, out=None, q_rows=None):
+    """O_h = (sum_j M[h, j] A_j) V_h. ``src`` is either a block_compress result
+    (dict with row_ptr/col_idx/vals/n_block_rows) or ``("dense", maps, layout)``.
+    ``q_rows`` is the row count of the output tensor (default: v's rows)."""
+    torch = _torch()
+    lib = load_library()
+    dev = v.device
+    H, Tk, d = v.shape
+    out_dtype = out_dtype or v.dtype
+    Tq = q_rows if q_rows is not None else Tk
+    if out is None:
+        out = torch.empty((n_recv, Tq, d), dtype=out_dtype, device=dev)
+    s = _CMapsSrc()
+    if isinstance(src, dict):
+        s.kind = SRC_BSR
+        s.row_ptr = _dev_ptr(src["row_ptr"], "row_ptr")
+        s.col_idx = _dev_ptr(src["col_idx"], "col_idx")
+        s.vals = _dev_ptr(src["vals"], "vals")
+        s.n_block_rows = src["n_block_rows"]
+    else:
+        _, maps, layout = src
+        s.kind = SRC_DENSE
+        s.maps = _dev_ptr(maps, "maps")
+        s.maps_dt = _dt(maps)
+        s.layout = layout
+        s.head_stride = maps.shape[1]
+    if M_seq_stride is None:
+        M_seq_stride = 0 if M.shape[0] == 1 else n_recv * n_send
+    ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_recv, d, Tk)
+    ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
+    cvl = vl.c(Tq, Tk)
+    _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv,
+                             _dev_ptr(v, "v"), _dt(v), d, ctypes.byref(cvl), _dev_ptr(out, "out"),
+                             _dt(out), ws.data_ptr() if ws is not None else None,
+                             ws.numel() if ws is not None else 0, _stream()))
+    return out
+
+
+def onehot_mix(argmax, n_send):
+    torch = _torch()
+    lib = load_library()
+    B, Hr = argmax.shape
+    M = torch.empty((B, Hr, n_send), dtype=torch.float32, device=argmax.device)
+    _check(lib.cma_onehot_mix(_dev_ptr(argmax, "argmax"), B, Hr, n_send, _dev_ptr(M, "M"), _stream()))
+    return M
+
+
+def mapped_layers(n_layers, ratio):
+    lib = load_library()
+    buf = (ctypes.c_int32 * max(1, n_layers))()
+    n = lib.cma_mapped_layers(n_layers, float(ratio), buf, n_layers)
+    if n < 0:
+        raise CmaError(n, lib.cma_last_error().decode())
+    return [int(buf[i]) for i in range(n)]

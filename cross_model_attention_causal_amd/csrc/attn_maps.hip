@@ -1,0 +1,183 @@
+// Causal attention probability maps (GLIDE II-B; materialised as IAM Method 4
+// requires). Two sweeps per 64-query block-row: the first finds each query's
+// softmax max and normaliser with an online update, the second recomputes the
+// scores and writes exp(s - max) / sum. Recomputing QK^T is cheaper than a
+// round trip of the map: writing the map is the HBM cost of this stage.
+#include "kernels.hpp"
+#include "score.hpp"
+
+namespace cma {
+
+// Store 4 consecutive map entries of one row, starting at element index `idx`
+// of the output, writing only the first `cnt` (0..4) of them.
+template <bool BF16>
+__device__ __forceinline__ void store4(void* out, int64_t idx, const float p[4], int cnt) {
+  if (BF16) {
+    uint16_t* o = reinterpret_cast<uint16_t*>(out) + idx;
+    if (cnt == 4 && (idx & 3) == 0) {
+      u32x2 w = {pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
+      *reinterpret_cast<u32x2*>(o) = w;
+    } else {
+      for (int e = 0; e < cnt; ++e) o[e] = f2bf(p[e]);
+    }
+  } else {
+    float* o = reinterpret_cast<float*>(out) + idx;
+    if (cnt == 4 && (idx & 3) == 0) {
+      *reinterpret_cast<f32x4*>(o) = f32x4{p[0], p[1], p[2], p[3]};
+    } else {
+      for (int e = 0; e < cnt; ++e) o[e] = p[e];
+    }
+  }
+}
+
+// grid (n_block_rows, n_seqs, n_heads), 512 threads = 8 waves:
+// wave w owns queries 32*(w&1) .. +31 of the block-row and key blocks c = (w>>1) mod 4.
+template <int D, bool PACKED, bool OUT_BF16>
+__global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
+  const int h = blockIdx.z, s = blockIdx.y;
+  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest block-rows first
+  const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  if (!seq_ok(a.vl, s, nq, nk) || 64 * r >= nq) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int qt = wave & 1, kp = wave >> 1;
+  const int i = 64 * r + 32 * qt + (lane & 31);
+  const bool valid = i < nq;
+  const int last = nk - nq + i;  // last visible key of this query
+  const int rowmax = min(64 * r + 63, nq - 1);
+  const int cmax = (nk - nq + rowmax) >> 6;
+
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D;
+  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
+  const float scale_l2 = a.scale[h] * kLog2e;
+  const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+
+  QOperand<D> qop;
+  load_query<D>(qop, qrow, valid);
+
+  f32x16 acc[2];
+  float t[32];
+  float m = -INFINITY, l = 0.0f;
+  for (int c = kp; c <= cmax; c += 4) {
+    score_block<D>(acc, qop, kseq, 64 * c, nk);
+    logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+    online_update(t, m, l);
+  }
+
+  __shared__ float sm[4][64], sl[4][64];
+  if (lane < 32) {
+    sm[kp][32 * qt + lane] = m;
+    sl[kp][32 * qt + lane] = l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][32 * qt + (lane & 31)]);
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = sm[w][32 * qt + (lane & 31)];
+    if (mw != -INFINITY) L += sl[w][32 * qt + (lane & 31)] * exp2f_fast(mw - M);
+  }
+  const float lse = M + log2f_fast(L);
+
+  const int64_t base = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED) +
+                       map_row_off(i, nq, nk, PACKED);
+  const int wend = PACKED ? last + 1 : nk;  // entries of this row that exist in the layout
+  const int cend = PACKED ? cmax : (nk - 1) >> 6;
+  const int half = lane >> 5;
+  for (int c = kp; c <= cend; c += 4) {
+    const bool live = c <= cmax;
+    if (live) {
+      score_block<D>(acc, qop, kseq, 64 * c, nk);
+      logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+    }
+    if (!valid) continue;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int key0 = 64 * c + 32 * kt + 8 * g + 4 * half;
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = live ? exp2f_fast(t[kt * 16 + 4 * g + e] - lse) : 0.0f;
+        const int cnt = max(0, min(4, wend - key0));
+        if (cnt > 0) store4<OUT_BF16>(a.maps, base + key0, p, cnt);
+      }
+    }
+  }
+}
+
+// fp32 inputs: one workgroup per (query row, sequence, head), scores on VALU.
+// Used for small fp32 problems; three passes over the keys (max, sum, write).
+template <bool PACKED>
+__global__ __launch_bounds__(256) void k_attn_maps_f32(AttnMapsArgs a, int d) {
+  const int h = blockIdx.z, s = blockIdx.y, i = blockIdx.x;
+  const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
+  const float* qrow = a.qf + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * d;
+  const float* kseq = a.kf + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * d;
+  const float scale = a.scale[h], bias = a.bias ? a.bias[h] : 0.0f;
+  const int last = nk - nq + i;
+  __shared__ float red[256];
+  auto logit = [&](int j) {
+    const float* kr = kseq + (int64_t)j * d;
+    float acc = 0.0f;
+    for (int e = 0; e < d; ++e) acc = fmaf(qrow[e], kr[e], acc);
+    return acc * scale + (j == 0 ? bias : 0.0f);
+  };
+  float mx = -INFINITY;
+  for (int j = threadIdx.x; j <= last; j += 256) mx = fmaxf(mx, logit(j));
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float sum = 0.0f;
+  for (int j = threadIdx.x; j <= last; j += 256) sum += expf(logit(j) - mx);
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float inv = 1.0f / red[0];
+  const int64_t base = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED) +
+                       map_row_off(i, nq, nk, PACKED);
+  const int wend = PACKED ? last + 1 : nk;
+  for (int j = threadIdx.x; j < wend; j += 256) {
+    const float p = j <= last ? expf(logit(j) - mx) * inv : 0.0f;
+    if (a.out_bf16)
+      reinterpret_cast<uint16_t*>(a.maps)[base + j] = f2bf(p);
+    else
+      reinterpret_cast<float*>(a.maps)[base + j] = p;
+  }
+}
+
+template <int D>
+static hipError_t launch_bf16(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
+  if (a.packed) {
+    if (a.out_bf16) hipLaunchKernelGGL((k_attn_maps<D, true, true>), grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_maps<D, true, false>), grid, dim3(512), 0, st, a);
+  } else {
+    if (a.out_bf16) hipLaunchKernelGGL((k_attn_maps<D, false, true>), grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_maps<D, false, false>), grid, dim3(512), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, hipStream_t st) {
+  if (a.n_heads == 0 || a.vl.n_seqs == 0 || max_q == 0) return hipSuccess;
+  if (a.in_bf16) {
+    dim3 grid((max_q + 63) / 64, a.vl.n_seqs, a.n_heads);
+    return d == 64 ? launch_bf16<64>(a, grid, st) : launch_bf16<128>(a, grid, st);
+  }
+  dim3 grid(max_q, a.vl.n_seqs, a.n_heads);
+  if (a.packed) hipLaunchKernelGGL((k_attn_maps_f32<true>), grid, dim3(256), 0, st, a, d);
+  else hipLaunchKernelGGL((k_attn_maps_f32<false>), grid, dim3(256), 0, st, a, d);
+  return hipGetLastError();
+}
+
+}  // namespace cma

@@ -1,0 +1,331 @@
+// C ABI: argument validation (before any HIP call), workspace sizing, dispatch.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.hpp"
+
+using namespace cma;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CMA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  static const bool sync_debug = [] {
+    const char* s = getenv("CMA_SYNC_DEBUG");
+    return s && s[0] == '1';
+  }();
+  if (sync_debug) {
+    hipError_t e2 = hipDeviceSynchronize();
+    if (e2 != hipSuccess) return fail(CMA_EHIP, "%s (sync): %s", what, hipGetErrorString(e2));
+  }
+  return CMA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+int check_varlen(const cma_varlen* vl, bool need_k) {
+  if (!vl) return fail(CMA_EINVAL, "varlen descriptor is NULL");
+  if (vl->n_seqs < 0) return fail(CMA_EINVAL, "n_seqs < 0");
+  if (vl->n_seqs > 0 && (!vl->cu_seqlens_q || (need_k && !vl->cu_seqlens_k)))
+    return fail(CMA_EINVAL, "cu_seqlens pointer is NULL");
+  if (vl->max_seqlen_q < 0 || vl->max_seqlen_k < 0) return fail(CMA_EINVAL, "negative max_seqlen");
+  if (vl->total_q < 0 || vl->total_k < 0) return fail(CMA_EINVAL, "negative total rows");
+  if (vl->max_seqlen_q > vl->total_q || (need_k && vl->max_seqlen_k > vl->total_k))
+    return fail(CMA_EINVAL, "max_seqlen exceeds the tensor rows");
+  return CMA_OK;
+}
+
+Varlen to_varlen(const cma_varlen* vl) {
+  Varlen v;
+  v.n_seqs = vl->n_seqs;
+  v.cu_q = vl->cu_seqlens_q;
+  v.cu_k = vl->cu_seqlens_k ? vl->cu_seqlens_k : vl->cu_seqlens_q;
+  v.used_q = vl->seqused_q;
+  v.used_k = vl->seqused_k;
+  v.total_q = vl->total_q;
+  v.total_k = vl->cu_seqlens_k ? vl->total_k : vl->total_q;
+  return v;
+}
+
+bool dtype_ok(cma_dtype d) { return d == CMA_F32 || d == CMA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+int cma_version(void) { return 100; }
+
+const char* cma_last_error(void) { return g_err; }
+
+int64_t cma_maps_elems(int32_t n_seqs, const int32_t* len_q, const int32_t* len_k,
+                       cma_map_layout layout) {
+  if (n_seqs < 0 || (n_seqs > 0 && (!len_q || !len_k))) return -1;
+  int64_t tot = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    const int64_t nq = len_q[s], nk = len_k[s];
+    if (nq < 0 || nk < nq) return -1;
+    tot += layout == CMA_MAP_PACKED ? nq * (nk - nq) + nq * (nq + 1) / 2 : nq * nk;
+  }
+  return tot;
+}
+
+int cma_attn_maps(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                  const cma_varlen* vl, const float* logit_scale, const float* key0_bias,
+                  void* maps, cma_dtype out_dt, cma_map_layout layout, int64_t head_stride,
+                  void* stream) {
+  if (int e = check_varlen(vl, true)) return e;
+  if (n_heads < 0) return fail(CMA_EINVAL, "n_heads < 0");
+  if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
+  if (layout != CMA_MAP_DENSE && layout != CMA_MAP_PACKED) return fail(CMA_EINVAL, "bad layout");
+  if (n_heads == 0 || vl->n_seqs == 0) return CMA_OK;
+  if (!q || !k || !logit_scale || !maps) return fail(CMA_EINVAL, "NULL q, k, logit_scale or maps");
+  if (head_stride < 0) return fail(CMA_EINVAL, "negative head_stride");
+  if (in_dt == CMA_BF16) {
+    if (d != 64 && d != 128) return fail(CMA_EUNSUPPORTED, "bf16 attn_maps supports d = 64 or 128 (got %d)", d);
+    if (!aligned16(q) || !aligned16(k)) return fail(CMA_EINVAL, "q and k must be 16-byte aligned");
+  } else if (d < 1 || d > 256) {
+    return fail(CMA_EUNSUPPORTED, "fp32 attn_maps supports 1 <= d <= 256 (got %d)", d);
+  }
+  AttnMapsArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.qf = static_cast<const float*>(q);
+  a.kf = static_cast<const float*>(k);
+  a.vl = to_varlen(vl);
+  a.scale = logit_scale;
+  a.bias = key0_bias;
+  a.maps = maps;
+  a.head_stride = head_stride;
+  a.n_heads = n_heads;
+  a.in_bf16 = in_dt == CMA_BF16;
+  a.out_bf16 = out_dt == CMA_BF16;
+  a.packed = layout == CMA_MAP_PACKED;
+  return hip_status(launch_attn_maps(a, d, vl->max_seqlen_q, static_cast<hipStream_t>(stream)),
+                    "attn_maps launch");
+}
+
+size_t cma_head_map_cosine_workspace(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t len,
+                                     cma_dtype dt) {
+  if (n_batch <= 0 || n_recv <= 0 || n_send <= 0 || len <= 0) return 0;
+  return plan_cosine(n_batch, n_recv, n_send, len, dt == CMA_BF16).ws_bytes;
+}
+
+int cma_head_map_cosine(const void* recv, const void* send, cma_dtype dt, int32_t n_batch,
+                        int32_t n_recv, int32_t n_send, int64_t len, int64_t recv_hstride,
+                        int64_t recv_bstride, int64_t send_hstride, int64_t send_bstride,
+                        float* cos, int32_t* argmax, float* margin, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt)) return fail(CMA_EINVAL, "bad dtype");
+  if (n_batch < 0 || n_recv < 0 || n_send < 0 || len < 0) return fail(CMA_EINVAL, "negative size");
+  if (n_batch == 0 || n_recv == 0) return CMA_OK;
+  if (n_send == 0) return fail(CMA_EINVAL, "n_send must be positive");
+  if (n_send > 384) return fail(CMA_EUNSUPPORTED, "n_send > 384");
+  if (len == 0) return fail(CMA_EINVAL, "len must be positive");
+  if (!recv || !send || !argmax) return fail(CMA_EINVAL, "NULL recv, send or argmax");
+  if (recv_hstride < 0 || recv_bstride < 0 || send_hstride < 0 || send_bstride < 0)
+    return fail(CMA_EINVAL, "negative stride");
+  if (dt == CMA_BF16) {
+    if (!aligned16(recv) || !aligned16(send)) return fail(CMA_EINVAL, "recv/send must be 16-byte aligned");
+    if ((recv_hstride | recv_bstride | send_hstride | send_bstride) % 8)
+      return fail(CMA_EINVAL, "bf16 strides must be multiples of 8 elements");
+  }
+  const CosinePlan pl = plan_cosine(n_batch, n_recv, n_send, len, dt == CMA_BF16);
+  if (!workspace || workspace_bytes < pl.ws_bytes)
+    return fail(CMA_ENOSPC, "workspace of %zu bytes needed", pl.ws_bytes);
+  CosineArgs a{};
+  a.recv = recv;
+  a.send = send;
+  a.bf16 = dt == CMA_BF16;
+  a.n_batch = n_batch;
+  a.n_recv = n_recv;
+  a.n_send = n_send;
+  a.len = len;
+  a.rh = recv_hstride;
+  a.rb = recv_bstride;
+  a.sh = send_hstride;
+  a.sb = send_bstride;
+  a.cos = cos;
+  a.argmax = argmax;
+  a.margin = margin;
+  float* ws = static_cast<float*>(workspace);
+  a.part = ws;
+  a.rnorm = a.part + (size_t)pl.splits * n_batch * n_recv * n_send;
+  a.snorm = a.rnorm + (size_t)pl.splits * n_batch * n_recv;
+  a.splits = pl.splits;
+  a.kchunk = pl.kchunk;
+  return hip_status(launch_cosine(a, static_cast<hipStream_t>(stream)), "head_map_cosine launch");
+}
+
+int64_t cma_bsr_max_blocks(int32_t n_heads, int32_t n_seqs, const int32_t* len_host) {
+  if (n_heads < 0 || n_seqs < 0 || (n_seqs > 0 && !len_host)) return -1;
+  int64_t tot = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    if (len_host[s] < 0) return -1;
+    const int64_t R = (len_host[s] + kBlock - 1) / kBlock;
+    tot += R * (R + 1) / 2;
+  }
+  return tot * n_heads;
+}
+
+size_t cma_block_compress_workspace(int32_t n_heads, int32_t n_block_rows, int32_t max_seqlen,
+                                    int64_t total_q) {
+  (void)max_seqlen;
+  if (n_heads < 0 || n_block_rows < 0 || total_q < 0) return 0;
+  return compress_ws_bytes(n_heads, n_block_rows, total_q);
+}
+
+int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                       const cma_varlen* vl, const float* logit_scale, const float* key0_bias,
+                       float tau, int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx,
+                       void* vals, int64_t capacity, int32_t* nnz, float* block_mass,
+                       float* row_stats, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int e = check_varlen(vl, true)) return e;
+  if (in_dt != CMA_BF16) return fail(CMA_EUNSUPPORTED, "block_compress needs bf16 q and k");
+  if (d != 64 && d != 128) return fail(CMA_EUNSUPPORTED, "block_compress supports d = 64 or 128 (got %d)", d);
+  if (!(tau > 0.0f) || std::isnan(tau)) return fail(CMA_EINVAL, "tau must be > 0");
+  if (n_heads < 0 || n_block_rows < 0 || capacity < 0) return fail(CMA_EINVAL, "negative size");
+  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
+    return fail(CMA_EUNSUPPORTED, "max_seqlen_q > %d", kMaxBlockRows * kBlock);
+  if (!row_ptr || !nnz) return fail(CMA_EINVAL, "NULL row_ptr or nnz");
+  if (capacity > 0 && (!col_idx || !vals)) return fail(CMA_EINVAL, "NULL col_idx or vals");
+  if (vals && !aligned16(vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
+  if (n_heads > 0 && vl->n_seqs > 0) {
+    if (!q || !k || !logit_scale) return fail(CMA_EINVAL, "NULL q, k or logit_scale");
+    if (!aligned16(q) || !aligned16(k)) return fail(CMA_EINVAL, "q and k must be 16-byte aligned");
+  }
+  const size_t need = compress_ws_bytes(n_heads, n_block_rows, vl->total_q);
+  if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
+  CompressArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.vl = to_varlen(vl);
+  a.scale = logit_scale;
+  a.bias = key0_bias;
+  a.tau = tau;
+  a.n_heads = n_heads;
+  a.n_block_rows = n_block_rows;
+  a.nrb_max = (vl->max_seqlen_q + kBlock - 1) / kBlock;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.vals = static_cast<uint16_t*>(vals);
+  a.capacity = capacity;
+  a.nnz = nnz;
+  a.block_mass = block_mass;
+  a.row_stats = row_stats;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  char* w = static_cast<char*>(workspace);
+  const size_t g = (size_t)n_heads * n_block_rows;
+  a.counts = reinterpret_cast<int32_t*>(w);
+  w += al(g * sizeof(int32_t));
+  a.kept = reinterpret_cast<uint32_t*>(w);
+  w += al(g * kWords * sizeof(uint32_t));
+  a.lse2 = reinterpret_cast<float*>(w);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n_heads == 0 || vl->n_seqs == 0 || a.nrb_max == 0) {
+    // nothing to compress: row_ptr = 0, nnz = 0 (a fill kernel, safe under graph capture)
+    hipError_t e = launch_fill_i32(row_ptr, (int64_t)n_heads * n_block_rows + 1, 0, st);
+    if (e == hipSuccess) e = launch_fill_i32(nnz, 1, 0, st);
+    return hip_status(e, "block_compress (empty)");
+  }
+  return hip_status(launch_compress(a, d, st), "block_compress launch");
+}
+
+size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k) {
+  if (!src || src->kind != CMA_SRC_BSR || n_recv <= 0 || d <= 0 || total_k <= 0) return 0;
+  return (size_t)n_recv * d * total_k * sizeof(uint16_t);
+}
+
+int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
+                  int32_t n_recv, const void* v, cma_dtype v_dt, int32_t d, const cma_varlen* vl,
+                  void* out, cma_dtype out_dt, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!src) return fail(CMA_EINVAL, "NULL maps source");
+  if (int e = check_varlen(vl, true)) return e;
+  if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
+  if (n_send < 0 || n_recv < 0 || M_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
+  if (d != 64 && d != 128) return fail(CMA_EUNSUPPORTED, "mapped_av supports d = 64 or 128 (got %d)", d);
+  if (n_recv == 0 || vl->n_seqs == 0) return CMA_OK;
+  if (n_send == 0 || n_send > 64) return fail(CMA_EUNSUPPORTED, "mapped_av supports 1 <= n_send <= 64");
+  if (!M || !v || !out) return fail(CMA_EINVAL, "NULL M, v or out");
+  MappedAvArgs a{};
+  a.n_send = n_send;
+  a.n_recv = n_recv;
+  a.d = d;
+  a.M = M;
+  a.M_stride = M_seq_stride;
+  a.v = v;
+  a.v_bf16 = v_dt == CMA_BF16;
+  a.vl = to_varlen(vl);
+  a.out = out;
+  a.out_bf16 = out_dt == CMA_BF16;
+  a.max_q = vl->max_seqlen_q;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (src->kind == CMA_SRC_DENSE) {
+    if (!src->maps) return fail(CMA_EINVAL, "NULL maps");
+    if (!dtype_ok(src->maps_dt)) return fail(CMA_EINVAL, "bad maps dtype");
+    if (src->layout != CMA_MAP_DENSE && src->layout != CMA_MAP_PACKED) return fail(CMA_EINVAL, "bad layout");
+    if (src->head_stride < 0) return fail(CMA_EINVAL, "negative head_stride");
+    a.maps = src->maps;
+    a.maps_bf16 = src->maps_dt == CMA_BF16;
+    a.packed = src->layout == CMA_MAP_PACKED;
+    a.head_stride = src->head_stride;
+    return hip_status(launch_mapped_av_dense(a, st), "mapped_av (dense) launch");
+  }
+  if (src->kind != CMA_SRC_BSR) return fail(CMA_EINVAL, "bad source kind");
+  if (v_dt != CMA_BF16 || d != 128) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av needs bf16 V and d = 128");
+  if (n_send > 32) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av supports n_send <= 32");
+  if (!src->row_ptr || !src->col_idx || !src->vals) return fail(CMA_EINVAL, "NULL block-sparse arrays");
+  if (!aligned16(src->vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
+  if (src->n_block_rows < 0) return fail(CMA_EINVAL, "negative n_block_rows");
+  if (vl->max_seqlen_q > vl->max_seqlen_k && vl->max_seqlen_k > 0)
+    return fail(CMA_EINVAL, "block-sparse maps are square: max_seqlen_q must not exceed max_seqlen_k");
+  const size_t need = (size_t)n_recv * d * vl->total_k * sizeof(uint16_t);
+  if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
+  if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
+  a.row_ptr = src->row_ptr;
+  a.col_idx = src->col_idx;
+  a.vals = static_cast<const uint16_t*>(src->vals);
+  a.n_block_rows = src->n_block_rows;
+  a.vt = static_cast<uint16_t*>(workspace);
+  return hip_status(launch_mapped_av_bsr(a, st), "mapped_av (block-sparse) launch");
+}
+
+int cma_onehot_mix(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32_t n_send, float* M,
+                   void* stream) {
+  if (n_batch < 0 || n_recv < 0 || n_send < 0) return fail(CMA_EINVAL, "negative size");
+  if ((int64_t)n_batch * n_recv * n_send == 0) return CMA_OK;
+  if (!argmax || !M) return fail(CMA_EINVAL, "NULL argmax or M");
+  return hip_status(launch_onehot(argmax, n_batch, n_recv, n_send, M, static_cast<hipStream_t>(stream)),
+                    "onehot_mix launch");
+}
+
+int cma_mapped_layers(int32_t n_layers, double ratio, int32_t* out, int32_t cap) {
+  if (n_layers < 0 || !(ratio >= 0.0) || cap < 0 || (cap > 0 && !out))
+    return fail(CMA_EINVAL, "bad arguments");
+  auto half_up = [](double x) { return (int32_t)std::floor(x + 0.5); };
+  const int32_t hi = half_up(0.8 * n_layers), lo = half_up(0.2 * n_layers);
+  const int32_t avail = (n_layers - hi) + std::max(0, hi - lo);
+  const int32_t want = std::min(half_up(ratio * n_layers), avail);
+  int32_t k = 0;
+  for (int32_t l = n_layers - 1; l >= hi && k < want; --l, ++k)
+    if (k < cap) out[k] = l;
+  for (int32_t l = lo; l < hi && k < want; ++l, ++k)
+    if (k < cap) out[k] = l;
+  return want;
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// Shared device helpers for the gfx950 kernels: bf16 conversion, MFMA wrappers,
+// cross-lane exchange and packed-sequence index math.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cma.h"
+
+namespace cma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBlock = 64;  // block-sparse tile edge (rows and columns)
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ------------------------------------------------------------------ MFMA
+// 16x16x32 bf16: A[m=l%16][k=8(l/16)+e], B[k=8(l/16)+e][n=l%16], D[m=4(l/16)+v][n=l%16]
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 32x32x16 bf16: A[m=l%32][k=8(l/32)+e], B[k=8(l/32)+e][n=l%32],
+//                D[m=8(v/4)+4(l/32)+(v%4)][n=l%32]
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// 16-byte load of 8 bf16 elements [j0, j0+8) of a row that is valid for j < n;
+// elements at or beyond n read as zero (and are never touched in memory).
+__device__ __forceinline__ u32x4 ldg16_guard(const uint16_t* row, int64_t j0, int64_t n) {
+  if (j0 + 8 <= n) return ldg16(row + j0);
+  u32x4 r = {0u, 0u, 0u, 0u};
+  if (j0 >= n) return r;
+  uint16_t t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = (j0 + e < n) ? row[j0 + e] : (uint16_t)0;
+  r[0] = t[0] | ((uint32_t)t[1] << 16);
+  r[1] = t[2] | ((uint32_t)t[3] << 16);
+  r[2] = t[4] | ((uint32_t)t[5] << 16);
+  r[3] = t[6] | ((uint32_t)t[7] << 16);
+  return r;
+}
+
+// As ldg16_guard, for rows that may not be 16-byte aligned.
+__device__ __forceinline__ u32x4 ldg16_guard_any(const uint16_t* row, int64_t j0, int64_t n) {
+  if (((reinterpret_cast<uintptr_t>(row + j0)) & 15) == 0) return ldg16_guard(row, j0, n);
+  uint16_t t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = (j0 + e < n) ? row[j0 + e] : (uint16_t)0;
+  u32x4 r;
+  r[0] = t[0] | ((uint32_t)t[1] << 16);
+  r[1] = t[2] | ((uint32_t)t[3] << 16);
+  r[2] = t[4] | ((uint32_t)t[5] << 16);
+  r[3] = t[6] | ((uint32_t)t[7] << 16);
+  return r;
+}
+
+// ------------------------------------------------------------------ cross-lane
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// ------------------------------------------------------------------ packed sequences
+struct Varlen {
+  int32_t n_seqs;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* used_q;
+  const int32_t* used_k;
+  int64_t total_q;
+  int64_t total_k;
+};
+
+__device__ __forceinline__ int32_t seq_len_q(const Varlen& v, int s) {
+  return v.used_q ? v.used_q[s] : v.cu_q[s + 1] - v.cu_q[s];
+}
+__device__ __forceinline__ int32_t seq_len_k(const Varlen& v, int s) {
+  return v.used_k ? v.used_k[s] : v.cu_k[s + 1] - v.cu_k[s];
+}
+
+// Elements of one (head, sequence) map in the given layout.
+__device__ __forceinline__ int64_t map_elems(int64_t nq, int64_t nk, bool packed) {
+  return packed ? nq * (nk - nq) + nq * (nq + 1) / 2 : nq * nk;
+}
+// Element offset of row i inside one (head, sequence) map.
+__device__ __forceinline__ int64_t map_row_off(int64_t i, int64_t nq, int64_t nk, bool packed) {
+  return packed ? i * (nk - nq) + i * (i + 1) / 2 : i * nk;
+}
+// Offset of sequence s's map inside a head's map area (sum over earlier sequences).
+__device__ __forceinline__ int64_t map_seq_off(const Varlen& v, int s, bool packed) {
+  int64_t off = 0;
+  for (int t = 0; t < s; ++t) off += map_elems(seq_len_q(v, t), seq_len_k(v, t), packed);
+  return off;
+}
+// Block-rows of earlier sequences, and packed lower-triangular block counts of
+// earlier sequences (for block statistics).
+__device__ __forceinline__ void block_offsets(const Varlen& v, int s, int32_t& roff, int64_t& tri_off) {
+  int32_t r = 0;
+  int64_t t = 0;
+  for (int u = 0; u < s; ++u) {
+    int32_t R = (seq_len_q(v, u) + kBlock - 1) / kBlock;
+    r += R;
+    t += (int64_t)R * (R + 1) / 2;
+  }
+  roff = r;
+  tri_off = t;
+}
+
+// Sequence bounds are trusted to be consistent (nondecreasing cu_seqlens, used
+// lengths within the reserved rows); these checks keep every access inside the
+// tensors even when they are not.
+__device__ __forceinline__ bool seq_ok(const Varlen& v, int s, int32_t nq, int32_t nk) {
+  int64_t q0 = v.cu_q[s], k0 = v.cu_k[s];
+  return nq >= 0 && nk >= 0 && nq <= nk && q0 >= 0 && k0 >= 0 && q0 + nq <= v.total_q &&
+         k0 + nk <= v.total_k;
+}
+
+}  // namespace cma

@@ -1,0 +1,97 @@
+// Argument blocks and launchers shared between the C ABI layer and the kernels.
+#pragma once
+#include "common.hpp"
+
+namespace cma {
+
+struct AttnMapsArgs {
+  const uint16_t* q;  // bf16 inputs
+  const uint16_t* k;
+  const float* qf;    // fp32 inputs
+  const float* kf;
+  Varlen vl;
+  const float* scale;
+  const float* bias;
+  void* maps;
+  int64_t head_stride;
+  int32_t n_heads;
+  bool in_bf16, out_bf16, packed;
+};
+hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, hipStream_t st);
+
+struct CosineArgs {
+  const void* recv;
+  const void* send;
+  bool bf16;
+  int32_t n_batch, n_recv, n_send;
+  int64_t len, rh, rb, sh, sb;
+  float* cos;
+  int32_t* argmax;
+  float* margin;
+  float* part;   // [splits][n_batch][n_recv][n_send]
+  float* rnorm;  // [splits][n_batch][n_recv]
+  float* snorm;  // [splits][n_batch][n_send]
+  int32_t splits;
+  int64_t kchunk;
+};
+struct CosinePlan {
+  int32_t splits;
+  int64_t kchunk;
+  size_t ws_bytes;
+};
+CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t len, bool bf16);
+hipError_t launch_cosine(const CosineArgs& a, hipStream_t st);
+
+struct CompressArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  Varlen vl;
+  const float* scale;
+  const float* bias;
+  float tau;
+  int32_t n_heads, n_block_rows, nrb_max;
+  int32_t* row_ptr;
+  int32_t* col_idx;
+  uint16_t* vals;
+  int64_t capacity;
+  int32_t* nnz;
+  float* block_mass;
+  float* row_stats;
+  // workspace
+  int32_t* counts;     // [n_heads * n_block_rows]
+  uint32_t* kept;      // [n_heads * n_block_rows * kWords]
+  float* lse2;         // [n_heads * total_q] log2-domain log-sum-exp per query row
+};
+constexpr int kMaxBlockRows = 256;  // sequences up to 16384 tokens
+constexpr int kWords = kMaxBlockRows / 32;
+size_t compress_ws_bytes(int32_t n_heads, int32_t n_block_rows, int64_t total_q);
+hipError_t launch_compress(const CompressArgs& a, int d, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t st);
+
+struct MappedAvArgs {
+  // dense source
+  const void* maps;
+  bool maps_bf16, packed;
+  int64_t head_stride;
+  // bsr source
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const uint16_t* vals;
+  int32_t n_block_rows;
+  int32_t n_send, n_recv, d;
+  const float* M;
+  int64_t M_stride;
+  const void* v;
+  bool v_bf16;
+  Varlen vl;
+  void* out;
+  bool out_bf16;
+  uint16_t* vt;  // workspace: [n_recv][d][total_k] transposed V (bsr path)
+  int32_t max_q;
+};
+hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);
+hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st);
+hipError_t launch_onehot(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32_t n_send,
+                         float* M, hipStream_t st);
+
+}  // namespace cma

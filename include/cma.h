@@ -1,0 +1,222 @@
+/*
+ * cma.h -- C ABI of the MI355X (gfx950) library for cross-model reuse of causal
+ * attention probability maps.
+ *
+ * Sources (web pages; sections named after their own headings):
+ *  [IAM]     "IAM: Efficient Inference through Attention Mapping between
+ *            Different-scale LLMs", paper notes (ACL 2025): Method 1 (cosine of
+ *            flattened maps), Method 2 (mapped-layer order), Method 4 (per-head
+ *            argmax at prefill; decode reuses the small model's attention rows).
+ *  [MapFlow] news article on "Accelerating Cross-Model LLM Inference via
+ *            Attention Map Reuse": approach section (receiver heads are learned
+ *            linear combinations of sender head maps; receiver keeps its own V),
+ *            storage-and-execution section (block-sparse retention of regular
+ *            2-D blocks by cumulative probability, two phases -- block
+ *            statistics, then extraction -- without the dense map; fused kernel
+ *            that mixes heads on chip and multiplies by V).
+ *  [GLIDE]   "GLIDE: Guided Layerwise Hybrid Attention", sections II-A/II-B
+ *            (causal scaled dot-product softmax attention).
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked [host]. The caller allocates and
+ *    owns all memory; the library never allocates, frees or keeps pointers.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and the
+ *    call returns before it completes. The return value reports argument
+ *    validation (done before any HIP call) and launch errors only; faults
+ *    surface at the caller's next synchronisation.
+ *  - Errors: CMA_OK (0) or a negative status; cma_last_error() gives a message
+ *    (thread-local). Nothing is launched when validation fails.
+ *  - Layout: head-major [H, T, d] row-major tensors. Several sequences are
+ *    packed along T and described by cma_varlen. Query row i of a sequence with
+ *    nq query rows and nk keys sits at key position nk - nq + i (bottom-right
+ *    alignment) and sees keys 0 .. nk - nq + i.
+ *  - Results are deterministic: identical inputs give bitwise identical outputs
+ *    (no floating-point atomics in reductions).
+ *  - bf16 is stored as 16-bit bit patterns (uint16); conversions from fp32 round
+ *    to nearest even.
+ */
+#ifndef CMA_H
+#define CMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CMA_OK 0
+#define CMA_EINVAL (-1)       /* NULL required pointer, bad sizes, inconsistent arguments */
+#define CMA_EUNSUPPORTED (-2) /* head dim, dtype or layout combination not built */
+#define CMA_ENOSPC (-3)       /* workspace smaller than the size the call requires */
+#define CMA_EHIP (-4)         /* a HIP launch or runtime call failed */
+
+typedef enum { CMA_F32 = 0, CMA_BF16 = 1 } cma_dtype;
+
+/* Map storage. DENSE: each (head, sequence) map is nq x nk row-major. PACKED:
+ * only the visible entries, row by row; row i holds nk - nq + i + 1 entries and
+ * starts at i*(nk - nq) + i*(i+1)/2 (for a square map: i(i+1)/2 + j). Per head,
+ * the sequences' maps follow each other in sequence order; head h starts at
+ * h * head_stride elements. */
+typedef enum { CMA_MAP_DENSE = 0, CMA_MAP_PACKED = 1 } cma_map_layout;
+
+/* Packed variable-length sequences.
+ * cu_seqlens_q/k: [n_seqs + 1] int32 start rows of each sequence in the query
+ *   (Q, output) and key (K, V) tensors; nondecreasing.
+ * seqused_q/k: optional [n_seqs] rows actually used per sequence (defaults to
+ *   the cu_seqlens spacing); lets a sequence use a prefix of its reserved rows.
+ * max_seqlen_q/k [host]: upper bounds of the used lengths (grid sizing).
+ * total_q/k [host]: rows of the query / key tensors (bounds for validation;
+ *   rows beyond them are never touched). */
+typedef struct {
+  int32_t n_seqs;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* seqused_q;
+  const int32_t* seqused_k;
+  int32_t max_seqlen_q;
+  int32_t max_seqlen_k;
+  int64_t total_q;
+  int64_t total_k;
+} cma_varlen;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int cma_version(void);
+/* Message for the last non-OK status returned on this thread. */
+const char* cma_last_error(void);
+
+/* Elements per head of a map buffer for the given host-side sequence lengths
+ * ([host] arrays of n_seqs); -1 on invalid arguments. */
+int64_t cma_maps_elems(int32_t n_seqs, const int32_t* len_q, const int32_t* len_k,
+                       cma_map_layout layout);
+
+/*
+ * cma_attn_maps -- causal attention probability maps per head ([GLIDE] II-B;
+ * materialised explicitly as [IAM] Method 4 requires).
+ *   A_ij = softmax_j( logit_scale[h] * <q_i, k_j> + key0_bias[h] * [j == 0] )
+ * over the visible keys j; invisible entries are 0 (DENSE) or absent (PACKED).
+ * q [n_heads, total_q, d], k [n_heads, total_k, d] in `in_dt` (bf16 or f32);
+ * logit_scale [n_heads] (beta_h / sqrt(d)); key0_bias [n_heads] or NULL (0);
+ * maps: n_heads * head_stride elements of `out_dt`; head_stride >=
+ * cma_maps_elems(...). d must be 64 or 128. Each sequence needs nq <= nk.
+ * Returns EINVAL for bad pointers/sizes, EUNSUPPORTED for other d.
+ */
+int cma_attn_maps(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                  const cma_varlen* vl, const float* logit_scale, const float* key0_bias,
+                  void* maps, cma_dtype out_dt, cma_map_layout layout, int64_t head_stride,
+                  void* stream);
+
+/*
+ * cma_head_map_cosine -- head mapping by cosine similarity of flattened maps
+ * ([IAM] Methods 1 and 4). For each problem b of n_batch:
+ *   cos[b,h,j] = <R_bh, S_bj> / (|R_bh| |S_bj|)   (0 if a norm is 0)
+ *   argmax[b,h] = the j with the largest cos (lowest j on ties)
+ *   margin[b,h] = largest minus second-largest cos (+inf if n_send == 1)
+ * R_bh = recv + b*recv_bstride + h*recv_hstride, S_bj likewise, each `len`
+ * elements of `dt` (bf16 or f32). Strides are in elements and must be
+ * multiples of 8; pointers 16-byte aligned. cos [n_batch, n_recv, n_send] and
+ * margin [n_batch, n_recv] may be NULL; argmax [n_batch, n_recv] is required.
+ * Computed as a split-K Gram product with fp32 accumulation, reduced in a fixed
+ * order. Needs `workspace` of cma_head_map_cosine_workspace(...) bytes.
+ */
+size_t cma_head_map_cosine_workspace(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t len,
+                                     cma_dtype dt);
+int cma_head_map_cosine(const void* recv, const void* send, cma_dtype dt, int32_t n_batch,
+                        int32_t n_recv, int32_t n_send, int64_t len, int64_t recv_hstride,
+                        int64_t recv_bstride, int64_t send_hstride, int64_t send_bstride,
+                        float* cos, int32_t* argmax, float* margin, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * cma_block_compress -- two-phase block-sparse compression of causal maps
+ * ([MapFlow] storage and execution), never forming the dense map.
+ * Phase 1 sweeps QK^T once per block-row with an online softmax and keeps, per
+ * 64x64 block (r, c <= r), its probability mass; per block-row the masses are
+ * normalised by their sum, ordered largest first (ties: lower column) and the
+ * shortest prefix whose running sum reaches `tau` is kept (tau >= 1 keeps all).
+ * Phase 2 recomputes only the kept blocks and writes them as bf16.
+ * Sequences are square (prefill): sequence s has n_s = used query rows; its
+ * keys are rows cu_seqlens_k[s] .. + n_s. Blocks are laid out per sequence from
+ * its first token; edge blocks are zero-padded.
+ * Outputs (block-sparse row format, BSR):
+ *   row_ptr [n_heads * n_block_rows + 1] int32, n_block_rows = sum_s ceil(n_s/64);
+ *     global block-row g = h * n_block_rows + (block-rows of earlier sequences) + r;
+ *   col_idx [capacity] int32, kept block columns (sequence-local), ascending per row;
+ *   vals [capacity, 64, 64] bf16 row-major blocks, zeros above the diagonal;
+ *   nnz [1] int32: number of kept blocks. If nnz > capacity nothing is written to
+ *     col_idx / vals (row_ptr and nnz still are): allocate nnz and call again.
+ *     cma_bsr_max_blocks() is always enough.
+ *   block_mass (optional) [n_heads, sum_s R_s(R_s+1)/2] fp32 masses, per sequence
+ *     packed lower-triangular (offset + r(r+1)/2 + c);
+ *   row_stats (optional) [n_heads, total_q, 2] fp32 (row max of the logits,
+ *     sum of exp(logit - max)) at each query row.
+ * Requires d in {64, 128}, max_seqlen_q <= 16384, tau > 0. Workspace:
+ * cma_block_compress_workspace(...) bytes.
+ */
+int64_t cma_bsr_max_blocks(int32_t n_heads, int32_t n_seqs, const int32_t* len_host);
+size_t cma_block_compress_workspace(int32_t n_heads, int32_t n_block_rows, int32_t max_seqlen,
+                                    int64_t total_q);
+int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                       const cma_varlen* vl, const float* logit_scale, const float* key0_bias,
+                       float tau, int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx,
+                       void* vals, int64_t capacity, int32_t* nnz, float* block_mass,
+                       float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Where cma_mapped_av reads the sender maps from. */
+typedef enum { CMA_SRC_DENSE = 0, CMA_SRC_BSR = 1 } cma_src_kind;
+typedef struct {
+  cma_src_kind kind;
+  /* CMA_SRC_DENSE: maps as written by cma_attn_maps (any nq <= nk, incl. decode rows) */
+  const void* maps;
+  cma_dtype maps_dt;
+  cma_map_layout layout;
+  int64_t head_stride;
+  /* CMA_SRC_BSR: output of cma_block_compress (square sequences) */
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* vals;
+  int32_t n_block_rows;
+} cma_maps_src;
+
+/*
+ * cma_mapped_av -- fused mapped attention x V ([MapFlow] approach and fused
+ * kernel; [IAM] Method 4 decode with a one-hot M):
+ *   O_h = ( sum_j M[s][h][j] * A_j ) @ V_h     for every sequence s,
+ * where A_j is sender head j's map as stored (zeros off the kept blocks for a
+ * BSR source). The mixed map is formed on chip and never written to memory.
+ * M: fp32 [*, n_recv, n_send], sequence s uses M + s * M_seq_stride
+ * (M_seq_stride = 0: one matrix for all). v [n_recv, total_k, d] and
+ * out [n_recv, total_q, d] in v_dt / out_dt (bf16 or f32); accumulation is fp32.
+ * d in {64, 128}. A BSR source needs bf16 V, d = 128 and n_send <= 64, and
+ * `workspace` of cma_mapped_av_workspace(...) bytes (a transposed copy of V);
+ * a dense source needs no workspace.
+ */
+size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k);
+int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
+                  int32_t n_recv, const void* v, cma_dtype v_dt, int32_t d, const cma_varlen* vl,
+                  void* out, cma_dtype out_dt, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * cma_onehot_mix -- IAM head map as a mixing matrix ([IAM] Method 4):
+ * M[b][h][j] = (j == argmax[b][h]) for argmax [n_batch, n_recv] (device);
+ * M [n_batch, n_recv, n_send] fp32 (device). Indices outside [0, n_send) give
+ * an all-zero row.
+ */
+int cma_onehot_mix(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32_t n_send,
+                   float* M, void* stream);
+
+/*
+ * cma_mapped_layers -- receiver layers to map for a ratio ([IAM] Method 2):
+ * from the last layer down to layer round(0.8 L), then from layer round(0.2 L)
+ * upwards; the first round(0.2 L) layers are never mapped. Writes up to `cap`
+ * 0-indexed layers in priority order to out [host]; returns the count
+ * (round-half-up(ratio * L), clamped to the available layers) or a negative
+ * status.
+ */
+int cma_mapped_layers(int32_t n_layers, double ratio, int32_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CMA_H */

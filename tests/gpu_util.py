@@ -1,0 +1,45 @@
+"""Helpers for GPU tests: moving seeded inputs to the device and comparing with the oracle."""
+import numpy as np
+import torch
+
+import synth
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 on the GPU."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def dev_i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+
+
+def host64(t):
+    """GPU tensor (bf16 or fp32) -> float64 numpy, exact."""
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def f64(bits_or_f32):
+    """Stored input values as float64 (bf16 bits widened exactly, or fp32)."""
+    a = np.asarray(bits_or_f32)
+    if a.dtype == np.uint16:
+        return synth.bf16_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def bf16_bits_from_f64(x):
+    """Exactly-representable bf16 values (float64) -> uint16 bits."""
+    return synth.bf16_from_f32(np.asarray(x, dtype=np.float32))
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((got - ref).ravel())
+    return num / den if den > 0 else num

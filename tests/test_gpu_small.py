@@ -1,0 +1,236 @@
+"""GPU parity at small sizes: every stage against the oracle on the same seeded inputs.
+
+Shapes span several tiles and end in ragged tails (lengths not multiples of 64,
+head counts not multiples of the tile widths). Tolerances: relative L2 1e-5 for
+fp32 outputs and 1e-2 for bf16 outputs (fp32 accumulation); head-map indices and
+kept-block sets bit-exact wherever the oracle's decision margin exceeds 1e-4.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import dev_bf16, dev_f32, dev_i32, f64, host64, rel_l2, bf16_bits_from_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def cma():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import cross_model_attention_causal_amd as c
+    c.load_library()
+    return c
+
+
+# ------------------------------------------------------------------ tiny fp32 workload
+def test_cfg1_tiny_fp32_all_stages(cma):
+    say("cfg1: tiny fp32, 128 tokens, d=64, 4 sender / 2 receiver heads")
+    x = synth.cfg1()
+    vl = cma.Varlen(x["cu"], x["cu"])
+    n = x["n"]
+    # stage 1: dense fp32 maps
+    sm = cma.attn_maps(dev_f32(x["send_q"]), dev_f32(x["send_k"]), dev_f32(x["send_scale"]),
+                       dev_f32(x["send_bias"]), vl, layout=cma.DENSE, out_dtype=torch.float32)
+    rm = cma.attn_maps(dev_f32(x["recv_q"]), dev_f32(x["recv_k"]), dev_f32(x["recv_scale"]),
+                       dev_f32(x["recv_bias"]), vl, layout=cma.DENSE, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    S = np.stack([oracle.causal_map(f64(x["send_q"][j]), f64(x["send_k"][j]), 0.125) for j in range(4)])
+    R = np.stack([oracle.causal_map(f64(x["recv_q"][j]), f64(x["recv_k"][j]), 0.125) for j in range(2)])
+    Sr, Rr = oracle.round_f32(S), oracle.round_f32(R)
+    assert rel_l2(host64(sm).reshape(4, n, n), Sr) <= 1e-5
+    assert rel_l2(host64(rm).reshape(2, n, n), Rr) <= 1e-5
+    # stage 2: cosine 2 x 4 on oracle-stored maps
+    cos, arg, mar = cma.head_map_cosine(dev_f32(Rr.reshape(2, -1)), dev_f32(Sr.reshape(4, -1)), 1, 2, 4,
+                                        n * n, n * n, 0, n * n, 0)
+    torch.cuda.synchronize()
+    ocos, oarg, omar = oracle.head_map(Rr.reshape(2, -1), Sr.reshape(4, -1))
+    assert rel_l2(host64(cos)[0], ocos) <= 1e-5
+    for h in range(2):
+        if omar[h] > 1e-4:
+            assert int(arg[0, h]) == oarg[h]
+    # stage 4: dense mapped x V, fp32, on oracle-stored maps
+    O = cma.mapped_av(("dense", dev_f32(Sr.reshape(4, -1)), cma.DENSE), 4, dev_f32(x["M"]), 2,
+                      dev_f32(x["v"]), vl, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oO = oracle.mapped_av_dense(Sr, x["M"][0].astype(np.float64), f64(x["v"]))
+    assert rel_l2(host64(O), oracle.round_f32(oO)) <= 1e-5
+    # chained: GPU maps feed GPU mapped_av
+    O2 = cma.mapped_av(("dense", sm, cma.DENSE), 4, dev_f32(x["M"]), 2, dev_f32(x["v"]), vl,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert rel_l2(host64(O2), oracle.round_f32(oO)) <= 1e-5
+
+
+# ------------------------------------------------------------------ attn_maps bf16
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("layout", ["packed", "dense"])
+def test_attn_maps_bf16_varlen(cma, d, layout):
+    lens = [130, 64, 7, 200]
+    say(f"attn_maps bf16 d={d} layout={layout} lens={lens}")
+    x = synth.attention_inputs(101 + d, 5, lens, d=d)
+    vl = cma.Varlen(x["cu_q"], x["cu_k"])
+    lay = cma.PACKED if layout == "packed" else cma.DENSE
+    for out_dtype, tol in ((torch.bfloat16, 1e-2), (torch.float32, 1e-5)):
+        maps = cma.attn_maps(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_f32(x["scale"]), dev_f32(x["bias"]),
+                             vl, layout=lay, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        got = host64(maps)
+        q, k = f64(x["q"]), f64(x["k"])
+        om = oracle.attn_maps(q, k, x["scale"], x["bias"], x["cu_q"], x["cu_k"])
+        rnd = oracle.round_bf16 if out_dtype == torch.bfloat16 else oracle.round_f32
+        for h in range(5):
+            ref = np.concatenate([(oracle.pack_rows(A) if lay == cma.PACKED else A.ravel()) for A in om[h]])
+            assert got.shape[1] == ref.size
+            err = rel_l2(got[h], rnd(ref))
+            assert err <= tol, (h, err)
+            if out_dtype == torch.bfloat16:
+                # stored values: at most one bf16 step from the oracle's rounding
+                assert np.max(np.abs(got[h] - rnd(ref)) / np.maximum(np.abs(ref), 1e-30)) <= 2 ** -7
+
+
+def test_attn_maps_decode_rows(cma):
+    """Query rows at the end of longer key spans (bottom-right alignment)."""
+    lq, lk = [1, 3, 1], [513, 77, 1000]
+    say(f"attn_maps decode rows lq={lq} lk={lk}")
+    x = synth.attention_inputs(7, 4, lq, d=128, k_lengths=lk)
+    vl = cma.Varlen(x["cu_q"], x["cu_k"])
+    for lay in (cma.PACKED, cma.DENSE):
+        maps = cma.attn_maps(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_f32(x["scale"]), dev_f32(x["bias"]),
+                             vl, layout=lay, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        got = host64(maps)
+        om = oracle.attn_maps(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], x["cu_k"])
+        for h in range(4):
+            ref = np.concatenate([(oracle.pack_rows(A) if lay == cma.PACKED else A.ravel()) for A in om[h]])
+            assert rel_l2(got[h], oracle.round_f32(ref)) <= 1e-5
+
+
+# ------------------------------------------------------------------ cosine bf16
+def test_head_map_cosine_bf16(cma):
+    n = 200
+    lens = [n]
+    say("head_map_cosine bf16: 130 receivers x 37 senders over 20100 entries")
+    xs = synth.attention_inputs(201, 37, lens, d=128, heads_per_layer=37)
+    xr = synth.attention_inputs(202, 130, lens, d=128, heads_per_layer=65)
+    S = np.stack([oracle.pack_rows(oracle.causal_map(f64(xs["q"][j]), f64(xs["k"][j]), xs["scale"][j], xs["bias"][j]))
+                  for j in range(37)])
+    R = np.stack([oracle.pack_rows(oracle.causal_map(f64(xr["q"][j]), f64(xr["k"][j]), xr["scale"][j], xr["bias"][j]))
+                  for j in range(130)])
+    Sb, Rb = oracle.round_bf16(S), oracle.round_bf16(R)
+    L = Sb.shape[1]
+    # pad rows to a multiple of 8 elements (16-byte aligned rows)
+    Lp = (L + 7) // 8 * 8
+    Sp = np.zeros((37, Lp)); Sp[:, :L] = Sb
+    Rp = np.zeros((130, Lp)); Rp[:, :L] = Rb
+    cos, arg, mar = cma.head_map_cosine(dev_bf16(bf16_bits_from_f64(Rp)), dev_bf16(bf16_bits_from_f64(Sp)),
+                                        1, 130, 37, L, Lp, 0, Lp, 0)
+    torch.cuda.synchronize()
+    ocos, oarg, omar = oracle.head_map(Rb, Sb)
+    assert rel_l2(host64(cos)[0], ocos) <= 1e-5
+    big = omar > 1e-4
+    assert np.array_equal(host64(arg)[0][big].astype(int), oarg[big])
+    assert np.allclose(host64(mar)[0], omar, atol=1e-5)
+
+
+def test_head_map_cosine_batched_strided(cma):
+    """Batched problems addressed with head and batch strides, like per-prompt mapping."""
+    B, Hr, Hs, L = 3, 20, 28, 4100
+    say(f"head_map_cosine batched B={B} Hr={Hr} Hs={Hs} L={L}")
+    r = np.random.default_rng(5)
+    Lp = 4104
+    # layout [head][batch][Lp] for both, like attn_maps output over several sequences
+    R = r.uniform(0, 1, (Hr, B, Lp)) ** 4
+    S = r.uniform(0, 1, (Hs, B, Lp)) ** 4
+    R[..., L:] = 0
+    S[..., L:] = 0
+    Rb, Sb = oracle.round_bf16(R), oracle.round_bf16(S)
+    cos, arg, mar = cma.head_map_cosine(dev_bf16(bf16_bits_from_f64(Rb)), dev_bf16(bf16_bits_from_f64(Sb)),
+                                        B, Hr, Hs, L, B * Lp, Lp, B * Lp, Lp)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ocos, oarg, omar = oracle.head_map(Rb[:, b, :L], Sb[:, b, :L])
+        assert rel_l2(host64(cos)[b], ocos) <= 1e-5
+        big = omar > 1e-4
+        assert np.array_equal(host64(arg)[b][big].astype(int), oarg[big])
+
+
+# ------------------------------------------------------------------ block compress
+@pytest.mark.parametrize("tau", [0.9, 1.0])
+def test_block_compress_small(cma, tau):
+    lens = [200, 64, 130, 5]
+    H = 3
+    say(f"block_compress lens={lens} H={H} tau={tau}")
+    x = synth.attention_inputs(301, H, lens, d=128)
+    vl = cma.Varlen(x["cu_q"], x["cu_k"])
+    out = cma.block_compress(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_f32(x["scale"]), dev_f32(x["bias"]),
+                             vl, tau, want_mass=True, want_stats=True)
+    torch.cuda.synchronize()
+    ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], tau)
+    nnz = int(out["nnz"].item())
+    row_ptr = host64(out["row_ptr"]).astype(np.int64)
+    col = host64(out["col_idx"][:nnz]).astype(np.int64)
+    vals = host64(out["vals"][:nnz])
+    assert rel_l2(host64(out["block_mass"]), ref["masses"]) <= 1e-5
+    st = host64(out["row_stats"])
+    assert rel_l2(st[..., 1], ref["row_stats"][..., 1]) <= 1e-5
+    assert np.max(np.abs(st[..., 0] - ref["row_stats"][..., 0])) <= 1e-4
+    exempt = 0
+    for g in range(len(ref["kept"])):
+        gk = list(col[row_ptr[g]: row_ptr[g + 1]])
+        if ref["margins"][g] > 1e-4:
+            assert gk == ref["kept"][g], g
+        elif gk != ref["kept"][g]:
+            exempt += 1
+        if gk == ref["kept"][g] and gk:
+            a, b = row_ptr[g], ref["row_ptr"][g]
+            assert rel_l2(vals[a: a + len(gk)], ref["vals"][b: b + len(gk)]) <= 1e-2
+    say(f"  nnz={nnz} oracle={ref['nnz']} exempt rows differing={exempt}")
+
+
+# ------------------------------------------------------------------ mapped_av block-sparse
+@pytest.mark.parametrize("n_recv", [24, 7])
+def test_mapped_av_bsr_small(cma, n_recv):
+    lens = [200, 64, 130]
+    n_send = 32
+    say(f"mapped_av bsr lens={lens} n_send={n_send} n_recv={n_recv}")
+    x = synth.attention_inputs(401, n_send, lens, d=128)
+    ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9)
+    M = synth.mix_matrix_learned(402, n_recv, n_send)
+    T = int(x["cu_q"][-1])
+    V = synth.values(403, n_recv, T, 128)
+    vl = cma.Varlen(x["cu_q"], x["cu_q"])
+    src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
+               vals=dev_bf16(bf16_bits_from_f64(ref["vals"])), n_block_rows=ref["r_tot"])
+    O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    got = host64(O)
+    rows = [(s, r) for s in range(len(lens)) for r in range((lens[s] + 63) // 64)]
+    oo = oracle.mapped_av_bsr_rows(ref["row_ptr"], ref["col_idx"], ref["vals"], n_send, lens, M, f64(V),
+                                   x["cu_q"], rows)
+    refO = np.zeros_like(got)
+    for (s, r), o in oo.items():
+        a = x["cu_q"][s] + 64 * r
+        refO[:, a: a + o.shape[1]] = o
+    assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
+
+
+def test_onehot_and_layers(cma):
+    arg = dev_i32(np.array([[2, 0, 5], [1, 1, 0]]))
+    M = host64(cma.onehot_mix(arg, 4))
+    exp = np.zeros((2, 3, 4))
+    for b, row in enumerate([[2, 0, 5], [1, 1, 0]]):
+        for h, j in enumerate(row):
+            if j < 4:
+                exp[b, h, j] = 1.0  # index 5 is out of range: all-zero row
+    assert np.array_equal(M, exp)
+    assert cma.mapped_layers(80, 0.5) == oracle.mapped_layers(80, 0.5)
