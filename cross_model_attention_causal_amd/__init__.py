@@ -23,13 +23,15 @@ CMA_OK, CMA_EINVAL, CMA_EUNSUPPORTED, CMA_ENOSPC, CMA_EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 DENSE, PACKED = 0, 1
 SRC_DENSE, SRC_BSR = 0, 1
+V_TOKEN_MAJOR, V_KEY_MAJOR = 0, 1
 BLOCK = 64
 
 EXPORTS = [
     "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
     "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks",
     "cma_block_compress_workspace", "cma_block_compress", "cma_mapped_av_workspace",
-    "cma_mapped_av", "cma_onehot_mix", "cma_mapped_layers",
+    "cma_mapped_av", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
+    "cma_timing_collect", "cma_timing_get", "cma_timing_name", "cma_timing_reset",
 ]
 
 
@@ -81,11 +83,16 @@ def load_library(path: str = LIB_PATH):
         "cma_block_compress_workspace": (SZ, [I32, I32, I32, I64]),
         "cma_block_compress": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, F, I32, P, P,
                                               P, I64, P, P, P, P, SZ, P]),
-        "cma_mapped_av_workspace": (SZ, [P, I32, I32, I64]),
-        "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, P, ctypes.c_int, I32, P, P,
-                                         ctypes.c_int, P, SZ, P]),
+        "cma_mapped_av_workspace": (SZ, [P, I32, I32, I64, ctypes.c_int]),
+        "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, P, ctypes.c_int, ctypes.c_int, I32, P,
+                                         P, ctypes.c_int, P, SZ, P]),
         "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
+        "cma_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+        "cma_timing_collect": (ctypes.c_int, []),
+        "cma_timing_get": (D, [ctypes.c_char_p, ctypes.POINTER(I64)]),
+        "cma_timing_name": (ctypes.c_char_p, [ctypes.c_int]),
+        "cma_timing_reset": (None, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -276,14 +283,18 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
 
 
 def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_stride=None,
-              workspace: Workspace | None = None, out=None, q_rows=None):
+              workspace: Workspace | None = None, out=None, q_rows=None, v_layout=V_TOKEN_MAJOR):
     """O_h = (sum_j M[h, j] A_j) V_h. ``src`` is either a block_compress result
     (dict with row_ptr/col_idx/vals/n_block_rows) or ``("dense", maps, layout)``.
-    ``q_rows`` is the row count of the output tensor (default: v's rows)."""
+    ``v`` is [n_recv, Tk, d] (V_TOKEN_MAJOR) or [n_recv, d, Tk] (V_KEY_MAJOR).
+    ``q_rows`` is the row count of the output tensor (default: Tk)."""
     torch = _torch()
     lib = load_library()
     dev = v.device
-    H, Tk, d = v.shape
+    if v_layout == V_KEY_MAJOR:
+        H, d, Tk = v.shape
+    else:
+        H, Tk, d = v.shape
     out_dtype = out_dtype or v.dtype
     Tq = q_rows if q_rows is not None else Tk
     if out is None:
@@ -304,12 +315,13 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         s.head_stride = maps.shape[1]
     if M_seq_stride is None:
         M_seq_stride = 0 if M.shape[0] == 1 else n_recv * n_send
-    ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_recv, d, Tk)
+    ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_recv, d, Tk, v_layout)
     ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
     cvl = vl.c(Tq, Tk)
     _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv,
-                             _dev_ptr(v, "v"), _dt(v), d, ctypes.byref(cvl), _dev_ptr(out, "out"),
-                             _dt(out), ws.data_ptr() if ws is not None else None,
+                             _dev_ptr(v, "v"), _dt(v), v_layout, d, ctypes.byref(cvl),
+                             _dev_ptr(out, "out"), _dt(out),
+                             ws.data_ptr() if ws is not None else None,
                              ws.numel() if ws is not None else 0, _stream()))
     return out
 
@@ -330,3 +342,29 @@ def mapped_layers(n_layers, ratio):
     if n < 0:
         raise CmaError(n, lib.cma_last_error().decode())
     return [int(buf[i]) for i in range(n)]
+
+
+def timing_enable(on=True):
+    """Bracket every library kernel launch with HIP events on its own stream."""
+    load_library().cma_timing_enable(1 if on else 0)
+
+
+def timing_collect():
+    """Wait for recorded events and return {kernel: (total_ms, launches)} so far."""
+    lib = load_library()
+    _check(lib.cma_timing_collect())
+    out = {}
+    i = 0
+    while True:
+        name = lib.cma_timing_name(i)
+        if name is None:
+            break
+        n = ctypes.c_int64(0)
+        ms = lib.cma_timing_get(name, ctypes.byref(n))
+        out[name.decode()] = (ms, int(n.value))
+        i += 1
+    return out
+
+
+def timing_reset():
+    load_library().cma_timing_reset()

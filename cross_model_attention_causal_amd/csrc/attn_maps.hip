@@ -159,11 +159,11 @@ __global__ __launch_bounds__(256) void k_attn_maps_f32(AttnMapsArgs a, int d) {
 template <int D>
 static hipError_t launch_bf16(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
   if (a.packed) {
-    if (a.out_bf16) hipLaunchKernelGGL((k_attn_maps<D, true, true>), grid, dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_maps<D, true, false>), grid, dim3(512), 0, st, a);
+    if (a.out_bf16) { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, true, true>), grid, dim3(512), 0, st, a); }
+    else { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, true, false>), grid, dim3(512), 0, st, a); }
   } else {
-    if (a.out_bf16) hipLaunchKernelGGL((k_attn_maps<D, false, true>), grid, dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_maps<D, false, false>), grid, dim3(512), 0, st, a);
+    if (a.out_bf16) { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, false, true>), grid, dim3(512), 0, st, a); }
+    else { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, false, false>), grid, dim3(512), 0, st, a); }
   }
   return hipGetLastError();
 }
@@ -175,8 +175,8 @@ hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, hipStream_t
     return d == 64 ? launch_bf16<64>(a, grid, st) : launch_bf16<128>(a, grid, st);
   }
   dim3 grid(max_q, a.vl.n_seqs, a.n_heads);
-  if (a.packed) hipLaunchKernelGGL((k_attn_maps_f32<true>), grid, dim3(256), 0, st, a, d);
-  else hipLaunchKernelGGL((k_attn_maps_f32<false>), grid, dim3(256), 0, st, a, d);
+  if (a.packed) { KernelTimer kt_("k_attn_maps_f32", st); hipLaunchKernelGGL((k_attn_maps_f32<true>), grid, dim3(256), 0, st, a, d); }
+  else { KernelTimer kt_("k_attn_maps_f32", st); hipLaunchKernelGGL((k_attn_maps_f32<false>), grid, dim3(256), 0, st, a, d); }
   return hipGetLastError();
 }
 

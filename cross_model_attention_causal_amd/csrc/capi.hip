@@ -6,9 +6,63 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
 #include "kernels.hpp"
 
 using namespace cma;
+
+// ------------------------------------------------------------------ kernel timing
+namespace {
+struct PendingTiming {
+  std::string name;
+  hipEvent_t a, b;
+};
+struct TimingState {
+  std::mutex mu;
+  std::vector<hipEvent_t> pool;
+  std::vector<PendingTiming> pending;
+  std::map<std::string, std::pair<double, int64_t>> totals;
+  std::vector<std::string> names;
+};
+std::atomic<bool> g_timing{false};
+TimingState& timing() {
+  static TimingState* t = new TimingState();  // lives for the process
+  return *t;
+}
+hipEvent_t take_event() {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+namespace cma {
+KernelTimer::KernelTimer(const char* n, hipStream_t s) : name(n), st(s), ev0(nullptr) {
+  if (!g_timing.load(std::memory_order_relaxed)) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, st) == hipSuccess) ev0 = e;
+}
+KernelTimer::~KernelTimer() {
+  if (!ev0) return;
+  hipEvent_t e1 = take_event();
+  if (!e1 || hipEventRecord(e1, st) != hipSuccess) return;
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.pending.push_back({name, static_cast<hipEvent_t>(ev0), e1});
+}
+}  // namespace cma
 
 namespace {
 
@@ -66,6 +120,58 @@ bool dtype_ok(cma_dtype d) { return d == CMA_F32 || d == CMA_BF16; }
 }  // namespace
 
 extern "C" {
+
+int cma_timing_enable(int on) {
+  g_timing.store(on != 0);
+  return CMA_OK;
+}
+
+int cma_timing_collect(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& p : t.pending) {
+    if (hipEventSynchronize(p.b) != hipSuccess) return fail(CMA_EHIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) return fail(CMA_EHIP, "elapsed time failed");
+    auto it = t.totals.find(p.name);
+    if (it == t.totals.end()) {
+      t.names.push_back(p.name);
+      it = t.totals.emplace(p.name, std::make_pair(0.0, (int64_t)0)).first;
+    }
+    it->second.first += ms;
+    it->second.second += 1;
+    t.pool.push_back(p.a);
+    t.pool.push_back(p.b);
+  }
+  t.pending.clear();
+  return CMA_OK;
+}
+
+double cma_timing_get(const char* kernel, int64_t* launches) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  auto it = kernel ? t.totals.find(kernel) : t.totals.end();
+  if (it == t.totals.end()) {
+    if (launches) *launches = 0;
+    return 0.0;
+  }
+  if (launches) *launches = it->second.second;
+  return it->second.first;
+}
+
+const char* cma_timing_name(int index) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (index < 0 || index >= (int)t.names.size()) return nullptr;
+  return t.names[index].c_str();
+}
+
+void cma_timing_reset(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.totals.clear();
+  t.names.clear();
+}
 
 int cma_version(void) { return 100; }
 
@@ -244,16 +350,20 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
   return hip_status(launch_compress(a, d, st), "block_compress launch");
 }
 
-size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k) {
-  if (!src || src->kind != CMA_SRC_BSR || n_recv <= 0 || d <= 0 || total_k <= 0) return 0;
+size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k,
+                               cma_v_layout v_layout) {
+  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_KEY_MAJOR || n_recv <= 0 || d <= 0 ||
+      total_k <= 0)
+    return 0;
   return (size_t)n_recv * d * total_k * sizeof(uint16_t);
 }
 
 int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
-                  int32_t n_recv, const void* v, cma_dtype v_dt, int32_t d, const cma_varlen* vl,
-                  void* out, cma_dtype out_dt, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+                  int32_t n_recv, const void* v, cma_dtype v_dt, cma_v_layout v_layout, int32_t d,
+                  const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   if (!src) return fail(CMA_EINVAL, "NULL maps source");
+  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR) return fail(CMA_EINVAL, "bad V layout");
   if (int e = check_varlen(vl, true)) return e;
   if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
   if (n_send < 0 || n_recv < 0 || M_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
@@ -269,6 +379,7 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   a.M_stride = M_seq_stride;
   a.v = v;
   a.v_bf16 = v_dt == CMA_BF16;
+  a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
   a.vl = to_varlen(vl);
   a.out = out;
   a.out_bf16 = out_dt == CMA_BF16;
@@ -293,14 +404,18 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   if (src->n_block_rows < 0) return fail(CMA_EINVAL, "negative n_block_rows");
   if (vl->max_seqlen_q > vl->max_seqlen_k && vl->max_seqlen_k > 0)
     return fail(CMA_EINVAL, "block-sparse maps are square: max_seqlen_q must not exceed max_seqlen_k");
-  const size_t need = (size_t)n_recv * d * vl->total_k * sizeof(uint16_t);
-  if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
-  if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
   a.row_ptr = src->row_ptr;
   a.col_idx = src->col_idx;
   a.vals = static_cast<const uint16_t*>(src->vals);
   a.n_block_rows = src->n_block_rows;
-  a.vt = static_cast<uint16_t*>(workspace);
+  if (a.v_key_major) {
+    a.vt = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
+  } else {
+    const size_t need = (size_t)n_recv * d * vl->total_k * sizeof(uint16_t);
+    if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
+    if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
+    a.vt = static_cast<uint16_t*>(workspace);
+  }
   return hip_status(launch_mapped_av_bsr(a, st), "mapped_av (block-sparse) launch");
 }
 

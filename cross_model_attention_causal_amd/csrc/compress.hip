@@ -270,7 +270,7 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t value) {
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t st) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, value);
+  { KernelTimer kt_("k_fill_i32", st); hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, value); }
   return hipGetLastError();
 }
 
@@ -288,14 +288,17 @@ static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<D>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e0 != hipSuccess) return e0;
-  hipLaunchKernelGGL((k_block_stats<D>), grid, dim3(512), lds, st, a);
+  { KernelTimer kt_("k_block_stats", st); hipLaunchKernelGGL((k_block_stats<D>), grid, dim3(512), lds, st, a); }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_bsr_scan, dim3(1), dim3(1024), 0, st, a.counts,
-                     (int64_t)a.n_heads * a.n_block_rows, a.row_ptr, a.nnz);
+  {
+    KernelTimer kt_("k_bsr_scan", st);
+    hipLaunchKernelGGL(k_bsr_scan, dim3(1), dim3(1024), 0, st, a.counts,
+                       (int64_t)a.n_heads * a.n_block_rows, a.row_ptr, a.nnz);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_block_extract<D>), grid, dim3(512), 0, st, a);
+  { KernelTimer kt_("k_block_extract", st); hipLaunchKernelGGL((k_block_extract<D>), grid, dim3(512), 0, st, a); }
   return hipGetLastError();
 }
 

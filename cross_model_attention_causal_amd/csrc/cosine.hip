@@ -230,7 +230,7 @@ template <int NT>
 static void gram_launch(const CosineArgs& a, hipStream_t st) {
   const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
   dim3 grid(n_rtiles * a.splits, a.n_batch);
-  hipLaunchKernelGGL((k_gram_bf16<NT>), grid, dim3(256), 0, st, a);
+  { KernelTimer kt_("k_gram_bf16", st); hipLaunchKernelGGL((k_gram_bf16<NT>), grid, dim3(256), 0, st, a); }
 }
 
 hipError_t launch_cosine(const CosineArgs& a, hipStream_t st) {
@@ -246,11 +246,11 @@ hipError_t launch_cosine(const CosineArgs& a, hipStream_t st) {
     else if (nt <= 21) gram_launch<21>(a, st);
     else gram_launch<24>(a, st);
   } else {
-    hipLaunchKernelGGL(k_gram_f32, dim3(a.n_send, a.n_recv, a.n_batch), dim3(256), 0, st, a);
+    { KernelTimer kt_("k_gram_f32", st); hipLaunchKernelGGL(k_gram_f32, dim3(a.n_send, a.n_recv, a.n_batch), dim3(256), 0, st, a); }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_cos_finalize, dim3(a.n_recv, a.n_batch), dim3(64), 0, st, a);
+  { KernelTimer kt_("k_cos_finalize", st); hipLaunchKernelGGL(k_cos_finalize, dim3(a.n_recv, a.n_batch), dim3(64), 0, st, a); }
   return hipGetLastError();
 }
 

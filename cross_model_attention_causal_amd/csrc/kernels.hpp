@@ -4,6 +4,15 @@
 
 namespace cma {
 
+// Brackets one kernel launch with HIP events when timing is enabled.
+struct KernelTimer {
+  KernelTimer(const char* name, hipStream_t st);
+  ~KernelTimer();
+  const char* name;
+  hipStream_t st;
+  void* ev0;
+};
+
 struct AttnMapsArgs {
   const uint16_t* q;  // bf16 inputs
   const uint16_t* k;
@@ -83,6 +92,7 @@ struct MappedAvArgs {
   int64_t M_stride;
   const void* v;
   bool v_bf16;
+  bool v_key_major;  // v is [n_recv][d][total_k]
   Varlen vl;
   void* out;
   bool out_bf16;

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_mapped_av_bsr(MappedAvArgs a) {
 }
 
 // grid (max_q, n_seqs, n_recv), 256 threads.
-template <int D>
+template <int D, bool KEY_MAJOR>
 __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
   constexpr int JS = 256 / D;  // key slots per pass
   __shared__ float bj[256];
@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
   __shared__ int nzi[64];
   __shared__ float nzw[64];
   __shared__ int nnzm;
+  __shared__ float okm[D];  // key-major accumulators (one per feature)
   const int i = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
@@ -234,6 +235,7 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
       }
     nnzm = k;
   }
+  for (int f = threadIdx.x; f < D; f += 256) okm[f] = 0.0f;
   __syncthreads();
   const int last = nk - nq + i;
   const int64_t row_off = map_seq_off(a.vl, s, a.packed) + map_row_off(i, nq, nk, a.packed);
@@ -254,11 +256,27 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
     bj[threadIdx.x] = b;
     __syncthreads();
     const int jend = min(256, last + 1 - j0);
-    for (int jj = js; jj < jend; jj += JS) {
-      const int64_t vidx = ((int64_t)h * a.vl.total_k + k0 + j0 + jj) * D + e;
-      const float vv = a.v_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.v)[vidx])
-                                : reinterpret_cast<const float*>(a.v)[vidx];
-      acc = fmaf(bj[jj], vv, acc);
+    if (!KEY_MAJOR) {
+      for (int jj = js; jj < jend; jj += JS) {
+        const int64_t vidx = ((int64_t)h * a.vl.total_k + k0 + j0 + jj) * D + e;
+        const float vv = a.v_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.v)[vidx])
+                                  : reinterpret_cast<const float*>(a.v)[vidx];
+        acc = fmaf(bj[jj], vv, acc);
+      }
+    } else {
+      // key-major V: a wave walks features; its lanes cover consecutive keys
+      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      for (int f = wave; f < D; f += 4) {
+        const int64_t vrow = ((int64_t)h * D + f) * a.vl.total_k + k0 + j0;
+        float part = 0.0f;
+        for (int jj = lane; jj < jend; jj += 64) {
+          const float vv = a.v_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.v)[vrow + jj])
+                                    : reinterpret_cast<const float*>(a.v)[vrow + jj];
+          part = fmaf(bj[jj], vv, part);
+        }
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        if (lane == 0) okm[f] += part;
+      }
     }
     __syncthreads();
   }
@@ -266,7 +284,9 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
   __syncthreads();
   if (threadIdx.x < D) {
     float o = 0.0f;
-    for (int u = 0; u < JS; ++u) o += red[u][threadIdx.x];
+    if (KEY_MAJOR) o = okm[threadIdx.x];
+    else
+      for (int u = 0; u < JS; ++u) o += red[u][threadIdx.x];
     const int64_t oi = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D + threadIdx.x;
     if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f2bf(o);
     else reinterpret_cast<float*>(a.out)[oi] = o;
@@ -284,23 +304,31 @@ __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, fl
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
   dim3 grid(a.max_q, a.vl.n_seqs, a.n_recv);
-  if (a.d == 64) hipLaunchKernelGGL((k_mapped_av_dense<64>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_mapped_av_dense<128>), grid, dim3(256), 0, st, a);
+  if (a.v_key_major) {
+    if (a.d == 64) { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<64, true>), grid, dim3(256), 0, st, a); }
+    else { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<128, true>), grid, dim3(256), 0, st, a); }
+  } else {
+    if (a.d == 64) { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<64, false>), grid, dim3(256), 0, st, a); }
+    else { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<128, false>), grid, dim3(256), 0, st, a); }
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
-  if (a.vl.total_k > 0) {
+  if (a.vl.total_k > 0 && !a.v_key_major) {
     dim3 tg((unsigned)((a.vl.total_k + 63) / 64), a.n_recv);
-    hipLaunchKernelGGL((k_transpose_v<128>), tg, dim3(256), 0, st,
-                       reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl.total_k);
+    {
+      KernelTimer kt_("k_transpose_v", st);
+      hipLaunchKernelGGL((k_transpose_v<128>), tg, dim3(256), 0, st,
+                         reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl.total_k);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int nrb = (a.max_q + 63) / 64;
   dim3 grid(2 * nrb, a.vl.n_seqs, (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg);
-  hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(256), 0, st, a);
+  { KernelTimer kt_("k_mapped_av_bsr", st); hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(256), 0, st, a); }
   return hipGetLastError();
 }
 
@@ -308,8 +336,11 @@ hipError_t launch_onehot(const int32_t* argmax, int32_t n_batch, int32_t n_recv,
                          float* M, hipStream_t st) {
   const int64_t tot = (int64_t)n_batch * n_recv * n_send;
   if (tot == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_onehot, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, argmax,
-                     (int64_t)n_batch * n_recv, n_send, M);
+  {
+    KernelTimer kt_("k_onehot", st);
+    hipLaunchKernelGGL(k_onehot, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, argmax,
+                       (int64_t)n_batch * n_recv, n_send, M);
+  }
   return hipGetLastError();
 }
 

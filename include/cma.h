@@ -80,6 +80,18 @@ typedef struct {
   int64_t total_k;
 } cma_varlen;
 
+/* Per-kernel timing (profiling aid). While enabled, every kernel the library
+ * launches is bracketed by two HIP events recorded on the launch's own stream.
+ * cma_timing_collect() waits for the recorded events (host-blocking) and adds
+ * their elapsed times to per-kernel totals; cma_timing_get() reads a kernel's
+ * total milliseconds and launch count by name (see cma_timing_name()); reset
+ * clears everything. Thread-safe; disabled by default (then no events exist). */
+int cma_timing_enable(int on);
+int cma_timing_collect(void);
+double cma_timing_get(const char* kernel, int64_t* launches);
+const char* cma_timing_name(int index); /* NULL past the last kernel seen */
+void cma_timing_reset(void);
+
 /* Library version (major*10000 + minor*100 + patch). */
 int cma_version(void);
 /* Message for the last non-OK status returned on this thread. */
@@ -162,6 +174,12 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
                        void* vals, int64_t capacity, int32_t* nnz, float* block_mass,
                        float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Layout of the receiver's V. TOKEN_MAJOR: [n_recv, total_k, d] (row t holds the
+ * d values of key t). KEY_MAJOR: [n_recv, d, total_k] (row e holds feature e of
+ * every key), the layout a V projection can write directly for a consumer that
+ * contracts over keys. */
+typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1 } cma_v_layout;
+
 /* Where cma_mapped_av reads the sender maps from. */
 typedef enum { CMA_SRC_DENSE = 0, CMA_SRC_BSR = 1 } cma_src_kind;
 typedef struct {
@@ -185,17 +203,20 @@ typedef struct {
  * where A_j is sender head j's map as stored (zeros off the kept blocks for a
  * BSR source). The mixed map is formed on chip and never written to memory.
  * M: fp32 [*, n_recv, n_send], sequence s uses M + s * M_seq_stride
- * (M_seq_stride = 0: one matrix for all). v [n_recv, total_k, d] and
+ * (M_seq_stride = 0: one matrix for all). v in `v_layout` (see cma_v_layout) and
  * out [n_recv, total_q, d] in v_dt / out_dt (bf16 or f32); accumulation is fp32.
- * d in {64, 128}. A BSR source needs bf16 V, d = 128 and n_send <= 64, and
- * `workspace` of cma_mapped_av_workspace(...) bytes (a transposed copy of V);
- * a dense source needs no workspace.
+ * d in {64, 128}, 1 <= n_send <= 64 (dense) or <= 32 (BSR). A BSR source needs
+ * bf16 V and d = 128; with TOKEN_MAJOR V it first writes a key-major copy of V
+ * into `workspace` (cma_mapped_av_workspace(...) bytes), with KEY_MAJOR V it
+ * needs no workspace and runs as a single kernel. A dense source needs no
+ * workspace.
  */
-size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k);
+size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k,
+                               cma_v_layout v_layout);
 int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
-                  int32_t n_recv, const void* v, cma_dtype v_dt, int32_t d, const cma_varlen* vl,
-                  void* out, cma_dtype out_dt, void* workspace, size_t workspace_bytes,
-                  void* stream);
+                  int32_t n_recv, const void* v, cma_dtype v_dt, cma_v_layout v_layout, int32_t d,
+                  const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /*
  * cma_onehot_mix -- IAM head map as a mixing matrix ([IAM] Method 4):

@@ -309,3 +309,44 @@ def cfg5_layer(slot: int, n_short: int = 64, short: int = 512, n_long: int = 4, 
                cu_store=cu_from_lengths(store), tau_t=tau_t, n_short=n_short, decode=decode,
                n_send=n_send, n_recv=n_recv, d=D)
     return out
+
+
+def prefill_batch(n_prompts: int = 4, n: int = 8192, n_send: int = 32, n_recv: int = 24,
+                  tau_t: int = 512, seed_offset: int = 0):
+    """Long-context prefill batch: ``n_prompts`` prompts of ``n`` tokens, one mapped layer.
+
+    The Ministral-like 8B -> 3B pair of the block-sparse workloads (32 sender
+    heads, 24 receiver heads, d = 128), batched as in IAM's long-context setting
+    (8192-token prompts at batch 4). Key-side tensors reserve one extra slot per
+    prompt (rounded up to 8 rows) for the first generated token.
+
+    * ``send_q`` [32, P*n, 128]; ``send_k`` [32, P*slot, 128] (prompt keys + decode key)
+    * ``recv_q``/``recv_k`` [24, P*tau_t, 128]: the receiver's own queries/keys on each
+      prompt's first tau_t tokens (IAM's truncated head-mapping input)
+    * ``v`` [24, P*slot, 128]: receiver values for prompt and decode keys
+    * ``dec_q`` [32, P, 128]: sender query of the first generated token per prompt
+    * ``M`` [1, 24, 32]: learned-style mixing weights (N(0, 0.2) + 1 on the diagonal)
+    Stream order: [send q, send k, send heads, recv q, recv k, recv heads, v, M, dec q].
+    """
+    ss = np.random.SeedSequence([BASE_SEED + 40 + seed_offset, n_prompts, n])
+    s = ss.spawn(9)
+    slot = (n + 1 + 7) // 8 * 8
+    out = dict(
+        send_q=_normal_bf16(_rng(s[0]), (n_send, n_prompts * n, D)),
+        send_k=_normal_bf16(_rng(s[1]), (n_send, n_prompts * slot, D)),
+    )
+    out["send_scale"], out["send_bias"] = head_scales(_rng(s[2]), 1, n_send, D)
+    out["recv_q"] = _normal_bf16(_rng(s[3]), (n_recv, n_prompts * tau_t, D))
+    out["recv_k"] = _normal_bf16(_rng(s[4]), (n_recv, n_prompts * tau_t, D))
+    out["recv_scale"], out["recv_bias"] = head_scales(_rng(s[5]), 1, n_recv, D)
+    out["v"] = _normal_bf16(_rng(s[6]), (n_recv, n_prompts * slot, D))
+    r = _rng(s[7])
+    m = r.normal(0.0, 0.2, size=(1, n_recv, n_send))
+    for h in range(min(n_recv, n_send)):
+        m[0, h, h] += 1.0
+    out["M"] = m.astype(np.float32)
+    out["dec_q"] = _normal_bf16(_rng(s[8]), (n_send, n_prompts, D))
+    out.update(n_prompts=n_prompts, n=n, slot=slot, tau_t=tau_t, n_send=n_send, n_recv=n_recv, d=D,
+               cu_q=cu_from_lengths([n] * n_prompts), cu_k=cu_from_lengths([slot] * n_prompts),
+               cu_t=cu_from_lengths([tau_t] * n_prompts))
+    return out

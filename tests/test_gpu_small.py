@@ -198,8 +198,8 @@ def test_block_compress_small(cma, tau):
 
 
 # ------------------------------------------------------------------ mapped_av block-sparse
-@pytest.mark.parametrize("n_recv", [24, 7])
-def test_mapped_av_bsr_small(cma, n_recv):
+@pytest.mark.parametrize("n_recv,key_major", [(24, False), (7, False), (24, True)])
+def test_mapped_av_bsr_small(cma, n_recv, key_major):
     lens = [200, 64, 130]
     n_send = 32
     say(f"mapped_av bsr lens={lens} n_send={n_send} n_recv={n_recv}")
@@ -211,7 +211,11 @@ def test_mapped_av_bsr_small(cma, n_recv):
     vl = cma.Varlen(x["cu_q"], x["cu_q"])
     src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
                vals=dev_bf16(bf16_bits_from_f64(ref["vals"])), n_block_rows=ref["r_tot"])
-    O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl, out_dtype=torch.bfloat16)
+    if key_major:
+        O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))), vl,
+                          out_dtype=torch.bfloat16, v_layout=cma.V_KEY_MAJOR)
+    else:
+        O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     got = host64(O)
     rows = [(s, r) for s in range(len(lens)) for r in range((lens[s] + 63) // 64)]
@@ -222,6 +226,36 @@ def test_mapped_av_bsr_small(cma, n_recv):
         a = x["cu_q"][s] + 64 * r
         refO[:, a: a + o.shape[1]] = o
     assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
+
+
+@pytest.mark.parametrize("key_major", [False, True])
+def test_mapped_av_dense_decode_rows(cma, key_major):
+    """Decode rows: one query per sequence over long contexts, one-hot and learned M."""
+    lq, lk = [1, 1, 2], [1000, 513, 300]
+    n_send, n_recv = 28, 6
+    say(f"mapped_av dense decode rows lq={lq} lk={lk} key_major={key_major}")
+    x = synth.attention_inputs(501, n_send, lq, d=128, k_lengths=lk)
+    om = oracle.attn_maps(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], x["cu_k"])
+    maps = np.stack([np.concatenate([A.ravel() for A in om[j]]) for j in range(n_send)])
+    mapsr = oracle.round_f32(maps)
+    Tk = int(x["cu_k"][-1])
+    V = synth.values(502, n_recv, Tk, 128)
+    vl = cma.Varlen(x["cu_q"], x["cu_k"])
+    Ml = synth.mix_matrix_learned(503, n_recv, n_send, n_batch=3)
+    Moh = oracle.onehot_mix(np.array([[5, 0, 27, 3, 3, 9], [1, 2, 3, 4, 5, 6], [0, 0, 0, 0, 0, 0]]), n_send).astype(np.float32)
+    for M in (Ml, Moh):
+        vd = dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))) if key_major else dev_bf16(V)
+        O = cma.mapped_av(("dense", dev_f32(mapsr), cma.DENSE), n_send, dev_f32(M), n_recv, vd, vl,
+                          out_dtype=torch.float32, q_rows=int(x["cu_q"][-1]),
+                          v_layout=cma.V_KEY_MAJOR if key_major else cma.V_TOKEN_MAJOR)
+        torch.cuda.synchronize()
+        got = host64(O)
+        off = 0
+        for s_ in range(3):
+            A = mapsr[:, off: off + lq[s_] * lk[s_]].reshape(n_send, lq[s_], lk[s_])
+            off += lq[s_] * lk[s_]
+            ref = oracle.mapped_av_dense(A, M[s_].astype(np.float64), f64(V)[:, x["cu_k"][s_]: x["cu_k"][s_] + lk[s_]])
+            assert rel_l2(got[:, x["cu_q"][s_]: x["cu_q"][s_] + lq[s_]], oracle.round_f32(ref)) <= 1e-5
 
 
 def test_onehot_and_layers(cma):
