@@ -400,6 +400,8 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   if (v_dt != CMA_BF16 || d != 128) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av needs bf16 V and d = 128");
   if (n_send > 32) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av supports n_send <= 32");
   if (!src->row_ptr || !src->col_idx || !src->vals) return fail(CMA_EINVAL, "NULL block-sparse arrays");
+  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
+    return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av supports sequences up to %d tokens", kMaxBlockRows * kBlock);
   if (!aligned16(src->vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
   if (src->n_block_rows < 0) return fail(CMA_EINVAL, "negative n_block_rows");
   if (vl->max_seqlen_q > vl->max_seqlen_k && vl->max_seqlen_k > 0)

@@ -18,20 +18,25 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBlock = 64;  // block-sparse tile edge (rows and columns)
+constexpr int kPanel = 16;  // columns per panel of a stored block
+// Element (i, j) of a stored 64x64 block: blocks are kept as four panels of 16
+// columns, each panel row-major, so a 16-column slice of consecutive rows is
+// contiguous in memory.
+__device__ __forceinline__ int blk_off(int i, int j) { return (j >> 4) * (kBlock * kPanel) + i * kPanel + (j & 15); }
 
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// fp32 -> bf16 bits, round to nearest, ties to even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// two fp32 -> packed bf16 pair (lo in the low half), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // ------------------------------------------------------------------ MFMA

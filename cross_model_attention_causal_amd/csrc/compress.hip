@@ -247,7 +247,7 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
     const int c = cols[x];
     score_block<D>(acc, qop, kseq, 64 * c, n);
     logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
-    uint16_t* blk = a.vals + (base + x) * (int64_t)(kBlock * kBlock) + iloc * kBlock;
+    uint16_t* blk = a.vals + (base + x) * (int64_t)(kBlock * kBlock);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
         for (int e = 0; e < 4; ++e) p[e] = valid ? exp2f_fast(t[kt * 16 + 4 * gq + e] - lse) : 0.0f;
         const int j = 32 * kt + 8 * gq + 4 * half;
         u32x2 w = {pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
-        *reinterpret_cast<u32x2*>(blk + j) = w;
+        *reinterpret_cast<u32x2*>(blk + blk_off(iloc, j)) = w;
       }
     if (qt == 0 && lane == 0) a.col_idx[base + x] = c;
   }

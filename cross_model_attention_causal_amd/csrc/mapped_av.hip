@@ -1,34 +1,48 @@
 // Fused mapped attention x V (MapFlow, approach and storage-and-execution
 // sections; IAM Method 4 for decode rows):  O_h = (sum_j M[h, j] A_j) V_h.
 //
-// Block-sparse source (k_mapped_av_bsr). A workgroup owns 32 query rows of one
-// block-row and 16 receiver heads and walks the union of the sender heads' kept
-// columns in ascending order. Per key block and 32-key half it
-//   1. stages the 32 senders' 32x32 sub-blocks in LDS (zeros where a sender did
-//      not keep the block),
-//   2. mixes them on the matrix cores: for 16 positions at a time
-//      D1[h, pos] = sum_j M[h, j] A_j[pos] is a 16x16x32 MFMA with M (split
-//      into bf16 high and low parts, so the mix is accurate to ~2^-16) as the A
-//      operand and the senders as the B operand, read with the transposing LDS
-//      load so that each lane gets 8 senders of one position,
-//   3. writes the mixed maps B_h (bf16) to LDS and multiplies them into V_h with
-//      32x32x16 MFMAs, accumulating O in fp32 registers.
-// V is read as a transposed copy (key index contiguous) so that the V operand
-// comes straight from memory with 16-byte loads. The mixed map never leaves LDS.
+// Block-sparse source (k_mapped_av_bsr). A workgroup (8 waves) owns 32 query
+// rows of one block-row and 16 receiver heads (2 per wave). It first builds, in
+// LDS, the table block-column -> kept block of every sender (the union of their
+// kept columns), then walks the key axis in steps of 16 keys with a two-stage
+// software pipeline:
+//   - the 32 senders' 32 x 16 sub-blocks of the NEXT step (one contiguous 1 KB
+//     piece of a stored block's 16-column panel per sender) are loaded into
+//     registers while the current step computes, and written to the other half
+//     of a double-buffered LDS stage (zeros where a sender did not keep the
+//     block);
+//   - this step's V operands (16 keys x 128 features per head, from the
+//     key-major V) are loaded at the start of the step and consumed after the
+//     mixing;
+//   - mixing runs on the matrix cores: D1[h, pos] = sum_j M[h, j] A_j[pos] for
+//     16 positions is a 16x16x32 MFMA with M (split into bf16 high and low
+//     parts, so the mix is accurate to ~2^-16) as the A operand and the senders
+//     as the B operand, read with the transposing LDS load so that each lane
+//     gets 8 senders of one position; the mixed maps B_h go to LDS as bf16;
+//   - O += B_h V_h on 32x32x16 MFMAs, fp32 accumulators in registers.
+// The mixed map never leaves LDS. A token-major V is first copied key-major into
+// the workspace (k_transpose_v).
 //
-// Dense source (k_mapped_av_dense): VALU kernel for small problems and decode
-// rows: one workgroup per (query row, sequence, receiver head); only the
-// nonzero mixing weights are visited, so a one-hot M reads one sender row.
+// Dense source (k_mapped_av_dense): one workgroup per (query row, sequence,
+// receiver head) mixes the visible part of the row into LDS (only the nonzero
+// mixing weights are read, so a one-hot M reads one sender row) and streams V
+// with 16-byte loads. Used for decode rows and small dense problems.
 #include "kernels.hpp"
 
 namespace cma {
 
+constexpr int kWaves = 8;
 constexpr int kHeadsPerWg = 16;
+constexpr int kHeadsPerWave = kHeadsPerWg / kWaves;
 constexpr int kRowsPerWg = 32;
-constexpr int kSendPerStep = 32;
-constexpr int kSendStride = 1056;  // bf16 per staged sender: 32 rows x 32 + 32 pad
-constexpr int kBStride = 40;       // bf16 per mixed-map row (32 + 8 pad)
-constexpr int kBHead = 1288;       // bf16 per mixed-map head (32 rows x 40 + 8 pad)
+constexpr int kKeysPerStep = 16;
+constexpr int kSend = 32;            // senders per workgroup (n_send <= 32)
+constexpr int kSendStride = 544;     // bf16 per staged sender: 32 rows x 16 keys + 32 pad
+constexpr int kStageElems = kSend * kSendStride;
+constexpr int kBRow = 24;            // bf16 per mixed-map row (16 + 8 pad)
+constexpr int kBHead = 776;          // bf16 per mixed-map head (32 rows x 24 + 8 pad)
+constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
+constexpr uint16_t kNoBlock = 0xffff;
 
 // Vt[h][e][t] = V[h][t][e]; grid (ceil(total_k / 64), n_heads), 256 threads.
 template <int D>
@@ -50,26 +64,69 @@ __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict_
   }
 }
 
-// grid (2 * n_block_rows_max, n_seqs, ceil(n_recv / 16)), 256 threads (4 waves).
-__global__ __launch_bounds__(256) void k_mapped_av_bsr(MappedAvArgs a) {
-  constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[kSendPerStep * kSendStride];
-  __shared__ __attribute__((aligned(16))) uint16_t bbuf[kHeadsPerWg * kBHead];
-  __shared__ int cur[kSendPerStep], endp[kSendPerStep], curcol[kSendPerStep];
-  __shared__ int cnext;
+// Work items are (sequence, block-row r, row half, head group). Items of one
+// (sequence, r) "unit" share sender rows (head groups) and V tiles (row halves),
+// so they are placed on the same XCD at the same time: the hardware deals
+// workgroup ids round-robin over the 8 XCDs, so id i runs on XCD i % 8 and is
+// that XCD's (i / 8)-th workgroup. Units are ordered longest first (r
+// descending, sequences interleaved) and dealt to XCDs in snake order so that
+// every XCD gets the same amount of work.
+constexpr int kXcds = 8;
 
-  const int s = blockIdx.y, hg = blockIdx.z;
-  const int slot = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest block-rows first
-  const int r = slot >> 1, rh = slot & 1;
+__device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_hg, int& s, int& r, int& rh, int& hg) {
+  const int per_unit = 2 * n_hg;
+  const int xcd = id % kXcds, m = id / kXcds;
+  const int k = m / per_unit, item = m % per_unit;
+  const int u = kXcds * k + ((k & 1) ? (kXcds - 1 - xcd) : xcd);
+  if (u >= n_seqs * nrb) return false;
+  r = nrb - 1 - u / n_seqs;
+  s = u % n_seqs;
+  rh = item & 1;
+  hg = item >> 1;
+  return true;
+}
+
+// grid (8 * ceil(units / 8) * 2 * n_hg), 512 threads (8 waves).
+__global__ __launch_bounds__(512) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2 * kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t bbuf[kHeadsPerWg * kBHead];
+  __shared__ uint16_t tbl[kMaxCols * kSend];  // block index - sender's first block, or kNoBlock
+  __shared__ int sbeg[kSend];
+  __shared__ uint8_t anyc[kMaxCols];
+
+  int s, r, rh, hg;
+  if (!decode_item(blockIdx.x, a.vl.n_seqs, nrb, n_hg, s, r, rh, hg)) return;
   const int32_t n = seq_len_q(a.vl, s);
   if (!seq_ok(a.vl, s, n, n) || 64 * r + kRowsPerWg * rh >= n) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int32_t roff;
   int64_t tri;
   block_offsets(a.vl, s, roff, tri);
 
-  // mixing weights, A operand of 16x16x32: lane (p = lane%16, q = lane/16) holds
-  // M[hg*16 + p][8q + e]; high and low bf16 parts.
+  // ---- block table: tbl[c][j] = kept block of sender j at column c
+  for (int x = tid; x < (r + 1) * kSend; x += 512) tbl[x] = kNoBlock;
+  for (int c = tid; c <= r; c += 512) anyc[c] = 0;
+  if (tid < kSend) {
+    sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)tid * a.n_block_rows + roff + r] : 0;
+  }
+  __syncthreads();
+  {
+    const int j = tid >> 4, e0 = tid & 15;  // 32 senders x 16 threads
+    if (j < a.n_send) {
+      const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
+      const int beg = a.row_ptr[g], end = a.row_ptr[g + 1];
+      for (int e = beg + e0; e < end; e += 16) {
+        const int c = a.col_idx[e];
+        if (c >= 0 && c <= r && e - beg < (int)kNoBlock) {
+          tbl[c * kSend + j] = (uint16_t)(e - beg);
+          anyc[c] = 1;
+        }
+      }
+    }
+  }
+
+  // ---- mixing weights, A operand of 16x16x32: lane (p, q) holds M[hg*16 + p][8q + e]
   bf16x8 mhi, mlo;
   {
     const int p = lane & 15, q = lane >> 4;
@@ -78,13 +135,13 @@ __global__ __launch_bounds__(256) void k_mapped_av_bsr(MappedAvArgs a) {
     u32x4 hi, lo;
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
-      float x[2], xh[2], xl[2];
+      float xh[2], xl[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = 8 * q + 2 * e2 + u;
-        x[u] = (h < a.n_recv && j < a.n_send) ? Ms[(int64_t)h * a.n_send + j] : 0.0f;
-        xh[u] = bf2f(f2bf(x[u]));
-        xl[u] = x[u] - xh[u];
+        const float x = (h < a.n_recv && j < a.n_send) ? Ms[(int64_t)h * a.n_send + j] : 0.0f;
+        xh[u] = bf2f(f2bf(x));
+        xl[u] = x - xh[u];
       }
       hi[e2] = pack2bf(xh[0], xh[1]);
       lo[e2] = pack2bf(xl[0], xl[1]);
@@ -92,112 +149,118 @@ __global__ __launch_bounds__(256) void k_mapped_av_bsr(MappedAvArgs a) {
     mhi = as_bf16x8(hi);
     mlo = as_bf16x8(lo);
   }
-  if (threadIdx.x < kSendPerStep) {
-    const int j = threadIdx.x;
-    if (j < a.n_send) {
-      const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
-      cur[j] = a.row_ptr[g];
-      endp[j] = a.row_ptr[g + 1];
-    } else {
-      cur[j] = 0;
-      endp[j] = 0;
-    }
-  }
-  f32x16 acc[4][4];
+  f32x16 acc[kHeadsPerWave][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < kHeadsPerWave; ++t)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) acc[t][dt] = f32x16{};
   __syncthreads();
 
+  // ---- pipeline over steps (c, quarter)
   const int64_t k0 = a.vl.cu_k[s];
-  const int row_base = 64 * r + kRowsPerWg * rh;  // first query row (sequence-local)
-  int cprev = -1;
-  while (true) {
-    if (wave == 0) {
-      int v = 0x7fffffff;
-      if (lane < kSendPerStep) {
-        int cc = cur[lane];
-        if (cprev >= 0 && cc < endp[lane] && curcol[lane] == cprev) ++cc;
-        cur[lane] = cc;
-        v = cc < endp[lane] ? a.col_idx[cc] : 0x7fffffff;
-        curcol[lane] = v;
+  const int row_base = 64 * r + kRowsPerWg * rh;
+  auto next_col = [&](int c) {
+    for (int cc = c + 1; cc <= r; ++cc)
+      if (anyc[cc]) return cc;
+    return -1;
+  };
+  // staging chunk u of this thread: sender j = x >> 6, row = (x >> 1) & 31, half = x & 1
+  auto load_stage = [&](int c, int jq, u32x4 pf[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = tid + 512 * u;
+      const int j = x >> 6, row = (x >> 1) & 31, hf = x & 1;
+      const uint16_t bi = tbl[c * kSend + j];
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (bi != kNoBlock) {
+        // panel jq of the block: rows are 16 contiguous keys
+        const uint16_t* src = a.vals + (int64_t)(sbeg[j] + bi) * (kBlock * kBlock) +
+                              jq * (kBlock * kPanel) + (kRowsPerWg * rh + row) * kPanel + 8 * hf;
+        v = ldg16(src);
       }
-      for (int off = 32; off > 0; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-      if (lane == 0) cnext = v;
+      pf[u] = v;
+    }
+  };
+  auto store_stage = [&](int buf, const u32x4 pf[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = tid + 512 * u;
+      const int j = x >> 6, row = (x >> 1) & 31, hf = x & 1;
+      *reinterpret_cast<u32x4*>(&sbuf[buf * kStageElems + j * kSendStride + row * kKeysPerStep + 8 * hf]) = pf[u];
+    }
+  };
+
+  int c = anyc[0] ? 0 : next_col(0);
+  int jq = 0, buf = 0;
+  u32x4 pf[4];
+  if (c >= 0) {
+    load_stage(c, 0, pf);
+    store_stage(0, pf);
+  }
+  __syncthreads();
+  const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
+  const int n32 = lane & 31, q2 = lane >> 5;
+  while (c >= 0) {
+    int cn = c, jqn = jq + 1;
+    if (jqn == 4) {
+      jqn = 0;
+      cn = next_col(c);
+    }
+    if (cn >= 0) load_stage(cn, jqn, pf);  // next step, into registers
+    // this step's V operands: Vt[h][32 dt + n32][key0 + 8 q2 .. +8]
+    const int64_t key0 = 64 * c + kKeysPerStep * jq;  // sequence-local
+    u32x4 vb[kHeadsPerWave][4];
+#pragma unroll
+    for (int t = 0; t < kHeadsPerWave; ++t) {
+      const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
+      if (h >= a.n_recv) continue;  // padded head slot (uniform per wave)
+      const uint16_t* vtb = a.vt + (int64_t)h * D * a.vl.total_k + k0;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vb[t][dt] = ldg16_guard_any(vtb + (int64_t)(32 * dt + n32) * a.vl.total_k, key0 + 8 * q2, n);
+    }
+    // mixing: tile = query row (16 keys of the step); 4 tiles per wave
+    {
+      const uint16_t* sb = &sbuf[buf * kStageElems];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = wave + kWaves * u;
+        const uint16_t* b0 = sb + (8 * q + e4) * kSendStride + row * kKeysPerStep + 4 * cc4;
+        const uint16_t* b1 = b0 + 4 * kSendStride;
+        lds_bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) lds_bf16x4*)(b0));
+        lds_bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) lds_bf16x4*)(b1));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
+        const u32x4 bv = {l2[0], l2[1], h2[0], h2[1]};
+        f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
+        d1 = mfma16(mhi, as_bf16x8(bv), d1);
+        d1 = mfma16(mlo, as_bf16x8(bv), d1);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bbuf[(4 * q + v) * kBHead + row * kBRow + p] = f2bf(d1[v]);
+      }
     }
     __syncthreads();
-    const int c = cnext;
-    if (c == 0x7fffffff) break;
-    cprev = c;
-    for (int jh = 0; jh < 2; ++jh) {
-      // 1. stage senders' rows [row_base, +32) x cols [32 jh, +32) of block (r, c)
-      for (int x = threadIdx.x; x < kSendPerStep * 32 * 4; x += 256) {
-        const int j = x >> 7, row = (x >> 2) & 31, ch = x & 3;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (curcol[j] == c) {
-          const uint16_t* src = a.vals + (int64_t)cur[j] * (kBlock * kBlock) +
-                                (kRowsPerWg * rh + row) * kBlock + 32 * jh + 8 * ch;
-          val = ldg16(src);
-        }
-        *reinterpret_cast<u32x4*>(&sbuf[j * kSendStride + row * 32 + 8 * ch]) = val;
-      }
-      __syncthreads();
-      // 2. mix on MFMA: tile tau covers row tau/2, keys 16*(tau%2) .. +15
-      {
-        const int q = lane >> 4, p = lane & 15;
-        const int e = (lane >> 2) & 3, cc = lane & 3;
-        for (int tau = wave; tau < 64; tau += 4) {
-          const int row = tau >> 1, jb = 16 * (tau & 1);
-          const uint16_t* b0 = &sbuf[(8 * q + e) * kSendStride + row * 32 + jb + 4 * cc];
-          const uint16_t* b1 = b0 + 4 * kSendStride;
-          lds_bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) lds_bf16x4*)(b0));
-          lds_bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) lds_bf16x4*)(b1));
-          u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
-          u32x4 bv = {l2[0], l2[1], h2[0], h2[1]};
-          f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
-          d1 = mfma16(mhi, as_bf16x8(bv), d1);
-          d1 = mfma16(mlo, as_bf16x8(bv), d1);
+    // O += B_h V_h for this wave's heads (one 16-key k-step)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) bbuf[(4 * q + v) * kBHead + row * kBStride + jb + p] = f2bf(d1[v]);
-        }
-      }
-      __syncthreads();
-      // 3. O += B_h V_h for this wave's 4 heads
-      {
-        const int n32 = lane & 31, q2 = lane >> 5;
-        const int64_t kbase = 64 * c + 32 * jh;  // sequence-local key of this half
+    for (int t = 0; t < kHeadsPerWave; ++t) {
+      const int hh = kHeadsPerWave * wave + t;
+      if (hg * kHeadsPerWg + hh >= a.n_recv) continue;
+      const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 8 * q2]));
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int hh = 4 * wave + t;
-          const int h = hg * kHeadsPerWg + hh;
-          if (h >= a.n_recv) break;
-          bf16x8 av[2];
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            av[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBStride + 16 * ks + 8 * q2]));
-          const uint16_t* vtb = a.vt + (int64_t)h * D * a.vl.total_k + k0;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const uint16_t* vrow = vtb + (int64_t)(32 * dt + n32) * a.vl.total_k;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              const u32x4 bv = ldg16_guard_any(vrow, kbase + 16 * ks + 8 * q2, n);
-              acc[t][dt] = mfma32(av[ks], as_bf16x8(bv), acc[t][dt]);
-            }
-          }
-        }
-      }
+      for (int dt = 0; dt < 4; ++dt) acc[t][dt] = mfma32(av, as_bf16x8(vb[t][dt]), acc[t][dt]);
     }
+    if (cn >= 0) store_stage(buf ^ 1, pf);
+    __syncthreads();
+    c = cn;
+    jq = jqn;
+    buf ^= 1;
   }
-  // epilogue: D[m = row][n = e]: row = 8(v/4) + 4 q2 + (v%4), e = 32 dt + lane%32
-  const int n32 = lane & 31, q2 = lane >> 5;
+  // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int h = hg * kHeadsPerWg + 4 * wave + t;
-    if (h >= a.n_recv) break;
+  for (int t = 0; t < kHeadsPerWave; ++t) {
+    const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
+    if (h >= a.n_recv) continue;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -211,21 +274,48 @@ __global__ __launch_bounds__(256) void k_mapped_av_bsr(MappedAvArgs a) {
   }
 }
 
-// grid (max_q, n_seqs, n_recv), 256 threads.
-template <int D, bool KEY_MAJOR>
+// ---------------------------------------------------------------- dense source
+// grid (max_q, n_seqs, n_recv), 256 threads; dynamic LDS holds the mixed row
+// (up to kDenseWin keys at a time).
+constexpr int kDenseWin = 8192;
+
+// 8 consecutive V values starting at element index i as floats; entries at or
+// beyond `lim` read 0 (and are not touched in memory).
+template <typename T>
+__device__ __forceinline__ void ld8(const void* p, int64_t i, int64_t lim, float v[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint16_t* b = reinterpret_cast<const uint16_t*>(p) + i;
+    if (lim >= 8 && ((reinterpret_cast<uintptr_t>(b) & 15) == 0)) {
+      const u32x4 w = ldg16(b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = e < lim ? bf2f(b[e]) : 0.0f;
+    }
+  } else {
+    const float* f = reinterpret_cast<const float*>(p) + i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = e < lim ? f[e] : 0.0f;
+  }
+}
+
+template <int D, bool KEY_MAJOR, typename VT>
 __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
-  constexpr int JS = 256 / D;  // key slots per pass
-  __shared__ float bj[256];
-  __shared__ float red[JS][D];
+  extern __shared__ float bj[];  // mixed row window [kDenseWin]
   __shared__ int nzi[64];
   __shared__ float nzw[64];
   __shared__ int nnzm;
-  __shared__ float okm[D];  // key-major accumulators (one per feature)
+  __shared__ float red[256 / (D / 8)][D];  // one row per key slot (token-major)
   const int i = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
+  const int tid = threadIdx.x;
   const float* Ms = a.M + (int64_t)s * a.M_stride + (int64_t)h * a.n_send;
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int k = 0;
     for (int j = 0; j < a.n_send; ++j)
       if (Ms[j] != 0.0f) {
@@ -235,59 +325,78 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
       }
     nnzm = k;
   }
-  for (int f = threadIdx.x; f < D; f += 256) okm[f] = 0.0f;
   __syncthreads();
   const int last = nk - nq + i;
   const int64_t row_off = map_seq_off(a.vl, s, a.packed) + map_row_off(i, nq, nk, a.packed);
-  const int e = threadIdx.x % D, js = threadIdx.x / D;
   const int64_t k0 = a.vl.cu_k[s];
-  float acc = 0.0f;
-  for (int j0 = 0; j0 <= last; j0 += 256) {
-    const int j = j0 + threadIdx.x;
-    float b = 0.0f;
-    if (j <= last) {
+  constexpr int kChunks = D / 8;          // 8-feature chunks per key (token-major)
+  constexpr int kSlots = 256 / kChunks;   // keys per pass (token-major)
+  float accv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float acck[D / 16];
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) acck[u] = 0.0f;
+  for (int w0 = 0; w0 <= last; w0 += kDenseWin) {
+    const int wlen = min(kDenseWin, last + 1 - w0);
+    for (int j = tid; j < wlen; j += 256) {
+      float b = 0.0f;
       for (int u = 0; u < nnzm; ++u) {
-        const int64_t idx = (int64_t)nzi[u] * a.head_stride + row_off + j;
-        const float x = a.maps_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.maps)[idx])
-                                    : reinterpret_cast<const float*>(a.maps)[idx];
-        b = fmaf(nzw[u], x, b);
+        const int64_t idx = (int64_t)nzi[u] * a.head_stride + row_off + w0 + j;
+        b = fmaf(nzw[u], a.maps_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.maps)[idx])
+                                     : reinterpret_cast<const float*>(a.maps)[idx], b);
       }
+      bj[j] = b;
     }
-    bj[threadIdx.x] = b;
     __syncthreads();
-    const int jend = min(256, last + 1 - j0);
-    if (!KEY_MAJOR) {
-      for (int jj = js; jj < jend; jj += JS) {
-        const int64_t vidx = ((int64_t)h * a.vl.total_k + k0 + j0 + jj) * D + e;
-        const float vv = a.v_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.v)[vidx])
-                                  : reinterpret_cast<const float*>(a.v)[vidx];
-        acc = fmaf(bj[jj], vv, acc);
+    if constexpr (KEY_MAJOR) {
+      // 16 features at a time, 16 threads per feature, 8 keys per 16-byte load
+      const int lf = tid & 15, fs = tid >> 4;
+#pragma unroll
+      for (int rnd = 0; rnd < D / 16; ++rnd) {
+        const int f = 16 * rnd + fs;
+        const int64_t vrow = ((int64_t)h * D + f) * a.vl.total_k + k0 + w0;
+        float part = 0.0f;
+        for (int j = 8 * lf; j < wlen; j += 128) {
+          float v[8];
+          ld8<VT>(a.v, vrow + j, wlen - j, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = fmaf(j + e < wlen ? bj[j + e] : 0.0f, v[e], part);
+        }
+        acck[rnd] += part;
       }
     } else {
-      // key-major V: a wave walks features; its lanes cover consecutive keys
-      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-      for (int f = wave; f < D; f += 4) {
-        const int64_t vrow = ((int64_t)h * D + f) * a.vl.total_k + k0 + j0;
-        float part = 0.0f;
-        for (int jj = lane; jj < jend; jj += 64) {
-          const float vv = a.v_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.v)[vrow + jj])
-                                    : reinterpret_cast<const float*>(a.v)[vrow + jj];
-          part = fmaf(bj[jj], vv, part);
-        }
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (lane == 0) okm[f] += part;
+      const int fc = tid % kChunks, ks = tid / kChunks;
+      for (int j = ks; j < wlen; j += kSlots) {
+        float v[8];
+        ld8<VT>(a.v, ((int64_t)h * a.vl.total_k + k0 + w0 + j) * D + 8 * fc, 8, v);
+        const float b = bj[j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) accv[e] = fmaf(b, v[e], accv[e]);
       }
     }
     __syncthreads();
   }
-  red[js][e] = acc;
+  if constexpr (KEY_MAJOR) {
+    const int lf = tid & 15, fs = tid >> 4;
+#pragma unroll
+    for (int rnd = 0; rnd < D / 16; ++rnd) {
+      float x = acck[rnd];
+      for (int off = 8; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+      if (lf == 0) red[0][16 * rnd + fs] = x;
+    }
+  } else {
+    const int fc = tid % kChunks, ks = tid / kChunks;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[ks][8 * fc + e] = accv[e];
+  }
   __syncthreads();
-  if (threadIdx.x < D) {
+  if (tid < D) {
     float o = 0.0f;
-    if (KEY_MAJOR) o = okm[threadIdx.x];
-    else
-      for (int u = 0; u < JS; ++u) o += red[u][threadIdx.x];
-    const int64_t oi = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D + threadIdx.x;
+    if constexpr (KEY_MAJOR) {
+      o = red[0][tid];
+    } else {
+      for (int u = 0; u < kSlots; ++u) o += red[u][tid];
+    }
+    const int64_t oi = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D + tid;
     if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f2bf(o);
     else reinterpret_cast<float*>(a.out)[oi] = o;
   }
@@ -301,15 +410,27 @@ __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, fl
   M[x] = argmax[row] == j ? 1.0f : 0.0f;
 }
 
+template <int D, bool KM>
+static void dense_launch(const MappedAvArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = kDenseWin * sizeof(float);
+  if (a.v_bf16) {
+    KernelTimer kt_("k_mapped_av_dense", st);
+    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t>), grid, dim3(256), lds, st, a);
+  } else {
+    KernelTimer kt_("k_mapped_av_dense", st);
+    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float>), grid, dim3(256), lds, st, a);
+  }
+}
+
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
   dim3 grid(a.max_q, a.vl.n_seqs, a.n_recv);
   if (a.v_key_major) {
-    if (a.d == 64) { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<64, true>), grid, dim3(256), 0, st, a); }
-    else { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<128, true>), grid, dim3(256), 0, st, a); }
+    if (a.d == 64) dense_launch<64, true>(a, grid, st);
+    else dense_launch<128, true>(a, grid, st);
   } else {
-    if (a.d == 64) { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<64, false>), grid, dim3(256), 0, st, a); }
-    else { KernelTimer kt_("k_mapped_av_dense", st); hipLaunchKernelGGL((k_mapped_av_dense<128, false>), grid, dim3(256), 0, st, a); }
+    if (a.d == 64) dense_launch<64, false>(a, grid, st);
+    else dense_launch<128, false>(a, grid, st);
   }
   return hipGetLastError();
 }
@@ -318,17 +439,21 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
   if (a.vl.total_k > 0 && !a.v_key_major) {
     dim3 tg((unsigned)((a.vl.total_k + 63) / 64), a.n_recv);
-    {
-      KernelTimer kt_("k_transpose_v", st);
-      hipLaunchKernelGGL((k_transpose_v<128>), tg, dim3(256), 0, st,
-                         reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl.total_k);
-    }
+    KernelTimer kt_("k_transpose_v", st);
+    hipLaunchKernelGGL((k_transpose_v<128>), tg, dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl.total_k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int nrb = (a.max_q + 63) / 64;
-  dim3 grid(2 * nrb, a.vl.n_seqs, (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg);
-  { KernelTimer kt_("k_mapped_av_bsr", st); hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(256), 0, st, a); }
+  const int n_hg = (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg;
+  const int64_t units = (int64_t)nrb * a.vl.n_seqs;
+  const int64_t rounds = (units + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(rounds * kXcds * 2 * n_hg));
+  {
+    KernelTimer kt_("k_mapped_av_bsr", st);
+    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(512), 0, st, a, nrb, n_hg);
+  }
   return hipGetLastError();
 }
 
@@ -336,11 +461,9 @@ hipError_t launch_onehot(const int32_t* argmax, int32_t n_batch, int32_t n_recv,
                          float* M, hipStream_t st) {
   const int64_t tot = (int64_t)n_batch * n_recv * n_send;
   if (tot == 0) return hipSuccess;
-  {
-    KernelTimer kt_("k_onehot", st);
-    hipLaunchKernelGGL(k_onehot, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, argmax,
-                       (int64_t)n_batch * n_recv, n_send, M);
-  }
+  KernelTimer kt_("k_onehot", st);
+  hipLaunchKernelGGL(k_onehot, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, argmax,
+                     (int64_t)n_batch * n_recv, n_send, M);
   return hipGetLastError();
 }
 

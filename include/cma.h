@@ -154,7 +154,10 @@ int cma_head_map_cosine(const void* recv, const void* send, cma_dtype dt, int32_
  *   row_ptr [n_heads * n_block_rows + 1] int32, n_block_rows = sum_s ceil(n_s/64);
  *     global block-row g = h * n_block_rows + (block-rows of earlier sequences) + r;
  *   col_idx [capacity] int32, kept block columns (sequence-local), ascending per row;
- *   vals [capacity, 64, 64] bf16 row-major blocks, zeros above the diagonal;
+ *   vals [capacity, 64, 64] bf16 blocks, zeros above the diagonal, each stored as
+ *     four panels of 16 columns: element (i, j) of a block is at
+ *     (j / 16) * 1024 + i * 16 + j % 16 (a 16-column slice of consecutive rows
+ *     is contiguous, which is how the fused pass reads it);
  *   nnz [1] int32: number of kept blocks. If nnz > capacity nothing is written to
  *     col_idx / vals (row_ptr and nnz still are): allocate nnz and call again.
  *     cma_bsr_max_blocks() is always enough.

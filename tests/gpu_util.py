@@ -43,3 +43,16 @@ def rel_l2(got, ref):
     den = np.linalg.norm(ref.ravel())
     num = np.linalg.norm((got - ref).ravel())
     return num / den if den > 0 else num
+
+
+def blocks_to_panels(vals):
+    """Row-major 64x64 blocks [nnz, 64, 64] -> the library's stored layout (four
+    16-column panels per block, each row-major), returned as [nnz, 64, 64]."""
+    v = np.asarray(vals)
+    return np.ascontiguousarray(v.reshape(-1, 64, 4, 16).transpose(0, 2, 1, 3)).reshape(-1, 64, 64)
+
+
+def blocks_from_panels(vals):
+    """Inverse of blocks_to_panels."""
+    v = np.asarray(vals)
+    return np.ascontiguousarray(v.reshape(-1, 4, 64, 16).transpose(0, 2, 1, 3)).reshape(-1, 64, 64)

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import dev_bf16, dev_f32, dev_i32, f64, host64, rel_l2, bf16_bits_from_f64
+from tests.gpu_util import (dev_bf16, dev_f32, dev_i32, f64, host64, rel_l2, bf16_bits_from_f64,
+                            blocks_to_panels, blocks_from_panels)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,11 +81,13 @@ def test_attn_maps_bf16_varlen(cma, d, layout):
     x = synth.attention_inputs(101 + d, 5, lens, d=d)
     vl = cma.Varlen(x["cu_q"], x["cu_k"])
     lay = cma.PACKED if layout == "packed" else cma.DENSE
+    outs = {}
     for out_dtype, tol in ((torch.bfloat16, 1e-2), (torch.float32, 1e-5)):
         maps = cma.attn_maps(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_f32(x["scale"]), dev_f32(x["bias"]),
                              vl, layout=lay, out_dtype=out_dtype)
         torch.cuda.synchronize()
         got = host64(maps)
+        outs[out_dtype] = got
         q, k = f64(x["q"]), f64(x["k"])
         om = oracle.attn_maps(q, k, x["scale"], x["bias"], x["cu_q"], x["cu_k"])
         rnd = oracle.round_bf16 if out_dtype == torch.bfloat16 else oracle.round_f32
@@ -96,6 +99,8 @@ def test_attn_maps_bf16_varlen(cma, d, layout):
             if out_dtype == torch.bfloat16:
                 # stored values: at most one bf16 step from the oracle's rounding
                 assert np.max(np.abs(got[h] - rnd(ref)) / np.maximum(np.abs(ref), 1e-30)) <= 2 ** -7
+    # the bf16 map is the round-to-nearest-even of the very same fp32 value
+    assert np.array_equal(outs[torch.bfloat16], oracle.round_bf16(outs[torch.float32]))
 
 
 def test_attn_maps_decode_rows(cma):
@@ -179,7 +184,7 @@ def test_block_compress_small(cma, tau):
     nnz = int(out["nnz"].item())
     row_ptr = host64(out["row_ptr"]).astype(np.int64)
     col = host64(out["col_idx"][:nnz]).astype(np.int64)
-    vals = host64(out["vals"][:nnz])
+    vals = blocks_from_panels(host64(out["vals"][:nnz]))
     assert rel_l2(host64(out["block_mass"]), ref["masses"]) <= 1e-5
     st = host64(out["row_stats"])
     assert rel_l2(st[..., 1], ref["row_stats"][..., 1]) <= 1e-5
@@ -210,7 +215,7 @@ def test_mapped_av_bsr_small(cma, n_recv, key_major):
     V = synth.values(403, n_recv, T, 128)
     vl = cma.Varlen(x["cu_q"], x["cu_q"])
     src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
-               vals=dev_bf16(bf16_bits_from_f64(ref["vals"])), n_block_rows=ref["r_tot"])
+               vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
     if key_major:
         O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))), vl,
                           out_dtype=torch.bfloat16, v_layout=cma.V_KEY_MAJOR)
