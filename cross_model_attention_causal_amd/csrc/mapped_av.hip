@@ -1,8 +1,8 @@
 // Fused mapped attention x V (MapFlow, approach and storage-and-execution
 // sections; IAM Method 4 for decode rows):  O_h = (sum_j M[h, j] A_j) V_h.
 //
-// Block-sparse source (k_mapped_av_bsr). A workgroup (8 waves) owns 32 query
-// rows of one block-row and 16 receiver heads (2 per wave). It first builds, in
+// Block-sparse source (k_mapped_av_bsr). A workgroup (16 waves) owns 32 query
+// rows of one block-row and 16 receiver heads (one per wave). It first builds, in
 // LDS, the table block-column -> kept block of every sender (the union of their
 // kept columns), then walks the key axis in steps of 16 keys with a two-stage
 // software pipeline:
@@ -11,9 +11,8 @@
 //     registers while the current step computes, and written to the other half
 //     of a double-buffered LDS stage (zeros where a sender did not keep the
 //     block);
-//   - this step's V operands (16 keys x 128 features per head, from the
-//     key-major V) are loaded at the start of the step and consumed after the
-//     mixing;
+//   - this step's V operands (16 keys x 128 features, from the key-major V)
+//     are loaded at the start of the step and consumed after the mixing;
 //   - mixing runs on the matrix cores: D1[h, pos] = sum_j M[h, j] A_j[pos] for
 //     16 positions is a 16x16x32 MFMA with M (split into bf16 high and low
 //     parts, so the mix is accurate to ~2^-16) as the A operand and the senders
@@ -32,6 +31,7 @@
 namespace cma {
 
 constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kHeadsPerWg = 16;
 constexpr int kHeadsPerWave = kHeadsPerWg / kWaves;
 constexpr int kRowsPerWg = 32;
@@ -39,8 +39,9 @@ constexpr int kKeysPerStep = 16;
 constexpr int kSend = 32;            // senders per workgroup (n_send <= 32)
 constexpr int kSendStride = 544;     // bf16 per staged sender: 32 rows x 16 keys + 32 pad
 constexpr int kStageElems = kSend * kSendStride;
-constexpr int kBRow = 24;            // bf16 per mixed-map row (16 + 8 pad)
-constexpr int kBHead = 776;          // bf16 per mixed-map head (32 rows x 24 + 8 pad)
+constexpr int kStages = 2;           // sender stage ring: current panel + the next in flight
+constexpr int kBRow = 72;            // bf16 per mixed-map row (64 keys + 8 pad)
+constexpr int kBHead = 2312;         // bf16 per mixed-map head (32 rows x 72 + 8 pad)
 constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
 constexpr uint16_t kNoBlock = 0xffff;
 
@@ -69,15 +70,16 @@ __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict_
 // so they are placed on the same XCD at the same time: the hardware deals
 // workgroup ids round-robin over the 8 XCDs, so id i runs on XCD i % 8 and is
 // that XCD's (i / 8)-th workgroup. Units are ordered longest first (r
-// descending, sequences interleaved) and dealt to XCDs in snake order so that
-// every XCD gets the same amount of work.
+// descending, sequences interleaved) and unit u goes to XCD u % 8: with up to 8
+// sequences an XCD keeps to the same sequences, whose block-rows then sweep the
+// key blocks together and share V tiles in its L2.
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_hg, int& s, int& r, int& rh, int& hg) {
   const int per_unit = 2 * n_hg;
   const int xcd = id % kXcds, m = id / kXcds;
   const int k = m / per_unit, item = m % per_unit;
-  const int u = kXcds * k + ((k & 1) ? (kXcds - 1 - xcd) : xcd);
+  const int u = kXcds * k + xcd;
   if (u >= n_seqs * nrb) return false;
   r = nrb - 1 - u / n_seqs;
   s = u % n_seqs;
@@ -86,10 +88,10 @@ __device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_h
   return true;
 }
 
-// grid (8 * ceil(units / 8) * 2 * n_hg), 512 threads (8 waves).
-__global__ __launch_bounds__(512) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg) {
+// grid (8 * ceil(units / 8) * 2 * n_hg), kThreads threads.
+__global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[2 * kStageElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[kStages * kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t bbuf[kHeadsPerWg * kBHead];
   __shared__ uint16_t tbl[kMaxCols * kSend];  // block index - sender's first block, or kNoBlock
   __shared__ int sbeg[kSend];
@@ -105,18 +107,19 @@ __global__ __launch_bounds__(512) void k_mapped_av_bsr(MappedAvArgs a, int nrb, 
   block_offsets(a.vl, s, roff, tri);
 
   // ---- block table: tbl[c][j] = kept block of sender j at column c
-  for (int x = tid; x < (r + 1) * kSend; x += 512) tbl[x] = kNoBlock;
-  for (int c = tid; c <= r; c += 512) anyc[c] = 0;
+  for (int x = tid; x < (r + 1) * kSend; x += kThreads) tbl[x] = kNoBlock;
+  for (int c = tid; c <= r; c += kThreads) anyc[c] = 0;
   if (tid < kSend) {
     sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)tid * a.n_block_rows + roff + r] : 0;
   }
   __syncthreads();
   {
-    const int j = tid >> 4, e0 = tid & 15;  // 32 senders x 16 threads
+    constexpr int kPer = kThreads / kSend;  // threads per sender
+    const int j = tid / kPer, e0 = tid % kPer;
     if (j < a.n_send) {
       const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
       const int beg = a.row_ptr[g], end = a.row_ptr[g + 1];
-      for (int e = beg + e0; e < end; e += 16) {
+      for (int e = beg + e0; e < end; e += kPer) {
         const int c = a.col_idx[e];
         if (c >= 0 && c <= r && e - beg < (int)kNoBlock) {
           tbl[c * kSend + j] = (uint16_t)(e - beg);
@@ -156,74 +159,80 @@ __global__ __launch_bounds__(512) void k_mapped_av_bsr(MappedAvArgs a, int nrb, 
     for (int dt = 0; dt < 4; ++dt) acc[t][dt] = f32x16{};
   __syncthreads();
 
-  // ---- pipeline over steps (c, quarter)
   const int64_t k0 = a.vl.cu_k[s];
   const int row_base = 64 * r + kRowsPerWg * rh;
+  const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
+  const int n32 = lane & 31, q2 = lane >> 5;
   auto next_col = [&](int c) {
-    for (int cc = c + 1; cc <= r; ++cc)
-      if (anyc[cc]) return cc;
-    return -1;
+    int cc = c + 1;
+    while (cc <= r && !anyc[cc]) ++cc;
+    return cc <= r ? cc : -1;
   };
-  // staging chunk u of this thread: sender j = x >> 6, row = (x >> 1) & 31, half = x & 1
-  auto load_stage = [&](int c, int jq, u32x4 pf[4]) {
+  int n_valid = 0;  // heads of this wave below n_recv (uniform)
+  const uint16_t* vrow[kHeadsPerWave];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 512 * u;
-      const int j = x >> 6, row = (x >> 1) & 31, hf = x & 1;
-      const uint16_t bi = tbl[c * kSend + j];
-      u32x4 v = {0u, 0u, 0u, 0u};
+  for (int t = 0; t < kHeadsPerWave; ++t) {
+    const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
+    n_valid += h < a.n_recv;
+    vrow[t] = a.vt + ((int64_t)min(h, a.n_recv - 1) * D + n32) * a.vl.total_k + k0 + 32 * q2;
+  }
+  const int64_t dstride = (int64_t)32 * a.vl.total_k;
+  const bool v_vec = ((a.vl.total_k & 7) == 0) && ((k0 & 7) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(a.vt) & 15) == 0);
+  // Stage one 16-key panel of block (r, c) for all senders into stage buffer b:
+  // each wave copies its senders' 1 KB pieces straight into LDS (16 B per lane)
+  // or zero-fills a sender that did not keep the block.
+  auto issue_stage = [&](int c, int jq, int b) {
+    uint16_t* dst0 = &sbuf[b * kStageElems];
+#pragma unroll
+    for (int u = 0; u < kSend / kWaves; ++u) {
+      const int j = wave + kWaves * u;
+      const int bi = __builtin_amdgcn_readfirstlane((int)tbl[c * kSend + j]);
+      uint16_t* dst = dst0 + j * kSendStride;
       if (bi != kNoBlock) {
-        // panel jq of the block: rows are 16 contiguous keys
         const uint16_t* src = a.vals + (int64_t)(sbeg[j] + bi) * (kBlock * kBlock) +
-                              jq * (kBlock * kPanel) + (kRowsPerWg * rh + row) * kPanel + 8 * hf;
-        v = ldg16(src);
+                              jq * (kBlock * kPanel) + (kRowsPerWg * rh) * kPanel + 8 * lane;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      } else {
+        *reinterpret_cast<u32x4*>(dst + 8 * lane) = u32x4{0u, 0u, 0u, 0u};
       }
-      pf[u] = v;
     }
   };
-  auto store_stage = [&](int buf, const u32x4 pf[4]) {
+  // V operand (head slot t, feature tile dt, k-step ks) of block c: in k-step ks,
+  // lane half q2 holds keys 32 q2 + 8 ks .. +8 (so a lane's four k-steps read 64
+  // contiguous bytes of one feature row); the mixed-map operand uses the same
+  // key order.
+  auto load_v = [&](int t, int dt, int64_t key0, bool fast, u32x4 vb[4]) {
+    const uint16_t* src = vrow[t] + dt * dstride + key0;
+    if (fast) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 512 * u;
-      const int j = x >> 6, row = (x >> 1) & 31, hf = x & 1;
-      *reinterpret_cast<u32x4*>(&sbuf[buf * kStageElems + j * kSendStride + row * kKeysPerStep + 8 * hf]) = pf[u];
+      for (int ks = 0; ks < 4; ++ks) vb[ks] = ldg16(src + 8 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = (key0 + 32 * q2 + 8 * ks + e < n) ? src[8 * ks + e] : (uint16_t)0;
+        vb[ks] = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16),
+                       e8[4] | ((uint32_t)e8[5] << 16), e8[6] | ((uint32_t)e8[7] << 16)};
+      }
     }
   };
 
   int c = anyc[0] ? 0 : next_col(0);
-  int jq = 0, buf = 0;
-  u32x4 pf[4];
-  if (c >= 0) {
-    load_stage(c, 0, pf);
-    store_stage(0, pf);
-  }
+  int buf = 0;
+  if (c >= 0) issue_stage(c, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
-  const int n32 = lane & 31, q2 = lane >> 5;
   while (c >= 0) {
-    int cn = c, jqn = jq + 1;
-    if (jqn == 4) {
-      jqn = 0;
-      cn = next_col(c);
-    }
-    if (cn >= 0) load_stage(cn, jqn, pf);  // next step, into registers
-    // this step's V operands: Vt[h][32 dt + n32][key0 + 8 q2 .. +8]
-    const int64_t key0 = 64 * c + kKeysPerStep * jq;  // sequence-local
-    u32x4 vb[kHeadsPerWave][4];
-#pragma unroll
-    for (int t = 0; t < kHeadsPerWave; ++t) {
-      const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
-      if (h >= a.n_recv) continue;  // padded head slot (uniform per wave)
-      const uint16_t* vtb = a.vt + (int64_t)h * D * a.vl.total_k + k0;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        vb[t][dt] = ldg16_guard_any(vtb + (int64_t)(32 * dt + n32) * a.vl.total_k, key0 + 8 * q2, n);
-    }
-    // mixing: tile = query row (16 keys of the step); 4 tiles per wave
-    {
+    const int cn = next_col(c);
+    // ---- mix the block's four 16-key panels into bbuf (bf16, 64 keys per row)
+    for (int jq = 0; jq < 4; ++jq) {
+      if (jq < 3) issue_stage(c, jq + 1, buf ^ 1);
+      else if (cn >= 0) issue_stage(cn, 0, buf ^ 1);
       const uint16_t* sb = &sbuf[buf * kStageElems];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kRowsPerWg / kWaves; ++u) {
         const int row = wave + kWaves * u;
         const uint16_t* b0 = sb + (8 * q + e4) * kSendStride + row * kKeysPerStep + 4 * cc4;
         const uint16_t* b1 = b0 + 4 * kSendStride;
@@ -237,24 +246,35 @@ __global__ __launch_bounds__(512) void k_mapped_av_bsr(MappedAvArgs a, int nrb, 
         d1 = mfma16(mhi, as_bf16x8(bv), d1);
         d1 = mfma16(mlo, as_bf16x8(bv), d1);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) bbuf[(4 * q + v) * kBHead + row * kBRow + p] = f2bf(d1[v]);
+        for (int v = 0; v < 4; ++v)
+          bbuf[(4 * q + v) * kBHead + row * kBRow + kKeysPerStep * jq + p] = f2bf(d1[v]);
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      buf ^= 1;
     }
-    __syncthreads();
-    // O += B_h V_h for this wave's heads (one 16-key k-step)
+    // ---- O += B_h V_h over the block's 64 keys
+    const int64_t key0 = 64 * c;
+    const bool fast = v_vec && (key0 + 64 <= n);
 #pragma unroll
     for (int t = 0; t < kHeadsPerWave; ++t) {
+      if (t >= n_valid) break;
       const int hh = kHeadsPerWave * wave + t;
-      if (hg * kHeadsPerWg + hh >= a.n_recv) continue;
-      const bf16x8 av = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 8 * q2]));
+      bf16x8 av[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[t][dt] = mfma32(av, as_bf16x8(vb[t][dt]), acc[t][dt]);
+      for (int ks = 0; ks < 4; ++ks)
+        av[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 32 * q2 + 8 * ks]));
+      u32x4 vb[2][4];
+      load_v(t, 0, key0, fast, vb[0]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        if (dt < 3) load_v(t, dt + 1, key0, fast, vb[(dt + 1) & 1]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc[t][dt] = mfma32(av[ks], as_bf16x8(vb[dt & 1][ks]), acc[t][dt]);
+      }
     }
-    if (cn >= 0) store_stage(buf ^ 1, pf);
-    __syncthreads();
+    __syncthreads();  // bbuf is rewritten by the next block's mixing
     c = cn;
-    jq = jqn;
-    buf ^= 1;
   }
   // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
@@ -452,7 +472,7 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)(rounds * kXcds * 2 * n_hg));
   {
     KernelTimer kt_("k_mapped_av_bsr", st);
-    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(512), 0, st, a, nrb, n_hg);
+    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, nrb, n_hg);
   }
   return hipGetLastError();
 }
