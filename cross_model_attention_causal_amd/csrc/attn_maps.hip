@@ -55,12 +55,30 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   load_query<D>(qop, qrow, valid);
 
   f32x16 acc[2];
-  float t[32];
   float m = -INFINITY, l = 0.0f;
-  for (int c = kp; c <= cmax; c += 4) {
-    score_block<D>(acc, qop, kseq, 64 * c, nk);
-    logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
-    online_update(t, m, l);
+  // Blocks with every key visible to every query of the wave and no sink key
+  // take the lean path on raw scores (needs a positive scale).
+  const bool raw_ok = scale_l2 > 0.0f;
+  const int first_last = nk - nq + 64 * r + 32 * qt;  // last key of the wave's first query
+  auto lean = [&](int c) { return raw_ok && c != 0 && 64 * c + 63 <= first_last; };
+  // Sweep 1: running max and sum; the next block's K is in flight meanwhile.
+  auto step1 = [&](const KTile<D>& cur, KTile<D>& nxt, int c) {
+    if (c + 4 <= cmax) load_k<D>(nxt, kseq, 64 * (c + 4), nk);
+    mma_k<D>(acc, cur, qop);
+    if (lean(c)) {
+      online_update_raw(acc, scale_l2, m, l);
+    } else {
+      float t[32];
+      logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+      online_update(t, m, l);
+    }
+  };
+  KTile<D> kb0, kb1;
+  if (kp <= cmax) load_k<D>(kb0, kseq, 64 * kp, nk);
+  for (int c = kp; c <= cmax; c += 8) {
+    step1(kb0, kb1, c);
+    if (c + 4 > cmax) break;
+    step1(kb1, kb0, c + 4);
   }
 
   __shared__ float sm[4][64], sl[4][64];
@@ -85,25 +103,45 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   const int wend = PACKED ? last + 1 : nk;  // entries of this row that exist in the layout
   const int cend = PACKED ? cmax : (nk - 1) >> 6;
   const int half = lane >> 5;
-  for (int c = kp; c <= cend; c += 4) {
-    const bool live = c <= cmax;
-    if (live) {
-      score_block<D>(acc, qop, kseq, 64 * c, nk);
-      logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+  // Sweep 2: recompute and write p = 2^(logit - lse); dense rows also get the
+  // zeros of blocks past the diagonal.
+  auto step2 = [&](const KTile<D>& cur, KTile<D>& nxt, int c) {
+    if (c <= cmax) {
+      load_k<D>(nxt, kseq, 64 * c, nk);
+      mma_k<D>(acc, nxt, qop);
+      if (lean(c)) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(fmaf(acc[kt][v], scale_l2, -lse));
+      } else {
+        float t[32];
+        logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(t[16 * kt + v] - lse);
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[kt] = f32x16{};
     }
-    if (!valid) continue;
+    if (!valid) return;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int key0 = 64 * c + 32 * kt + 8 * g + 4 * half;
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = live ? exp2f_fast(t[kt * 16 + 4 * g + e] - lse) : 0.0f;
+        const float p[4] = {acc[kt][4 * g], acc[kt][4 * g + 1], acc[kt][4 * g + 2], acc[kt][4 * g + 3]};
         const int cnt = max(0, min(4, wend - key0));
         if (cnt > 0) store4<OUT_BF16>(a.maps, base + key0, p, cnt);
       }
     }
+  };
+  for (int c = kp; c <= cend; c += 8) {
+    step2(kb0, kb1, c);
+    if (c + 4 > cend) break;
+    step2(kb1, kb0, c + 4);
   }
 }
 

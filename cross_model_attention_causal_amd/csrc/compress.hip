@@ -16,82 +16,151 @@
 // Scan (k_bsr_scan): exclusive scan of kept counts -> row_ptr, nnz.
 // Phase 2 (k_block_extract): per block-row, recompute the kept blocks' scores,
 // p = 2^(t - lse2) and store bf16 blocks and their column indices.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "score.hpp"
 
 namespace cma {
 
+// Per-sub-step K pipeline shared by both phases. A sub-step is one feature half
+// of a round of 4 key blocks. Two LDS stages alternate; the global loads of
+// sub-step u + 2 are in flight (in registers) while sub-step u is computed, and
+// sub-step u + 1 (loaded one iteration earlier) is written to the other stage at
+// the end of the iteration, before the barrier that publishes it.
+template <int D, typename Key0, typename Body>
+__device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk,
+                                                int rounds, Key0 key0_of, Body body) {
+  constexpr int FH = D / 64;
+  const int nsub = rounds * FH;
+  auto load = [&](KStageRegs& rg, int u) {
+    int key0[4];
+    const int k = u / FH;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) key0[b] = key0_of(4 * k + b);
+    if (FH == 1 || u % FH == 0) kstage_load<D, 0>(rg, kseq, nk, key0);
+    else kstage_load<D, FH - 1>(rg, kseq, nk, key0);
+  };
+  auto run = [&](int u) {
+    const uint8_t* buf = stage + (u & 1) * kStageBytes;
+    if (FH == 1 || u % FH == 0) body(u / FH, buf, std::integral_constant<int, 0>{});
+    else body(u / FH, buf, std::integral_constant<int, FH - 1>{});
+  };
+  // iteration u: regs `mine` held sub-step u (already in LDS) and now fetch u + 2;
+  // regs `next` hold sub-step u + 1. Past the end the indices are clamped: the
+  // extra loads are harmless and keep the control flow (and so the compiler's
+  // wait counting) straight.
+  auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
+    load(mine, min(u + 2, nsub - 1));
+    run(u);
+    kstage_store(stage + ((u + 1) & 1) * kStageBytes, next);
+    barrier_lds();
+  };
+  if (nsub == 0) return;
+  KStageRegs r0, r1;
+  load(r0, 0);
+  load(r1, min(1, nsub - 1));
+  kstage_store(stage, r0);
+  barrier_lds();
+  for (int u = 0; u < nsub; u += 2) {
+    iter(r0, r1, u);
+    if (u + 1 >= nsub) break;
+    iter(r1, r0, u + 1);
+  }
+}
+
+// Block statistics and selection for one (head, sequence, block-row).
+// Dynamic LDS: two K stages, then LP[64][R] = log2 of each (query, block)
+// partial sum in absolute terms (running max + log2 of the partial), so that
+// mass_c = sum_i 2^(LP[i][c] - lse_i) once the row's lse is known.
 template <int D>
 __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn[];
-  const int R = a.nrb_max;               // LDS arrays are [64][R]
-  float* P = dyn;                        // partial sums
-  float* MX = dyn + 64 * R;              // running max at each block
+  const int R = a.nrb_max;
+  uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
+  float* LP = dyn + 2 * (kStageBytes / 4);
   __shared__ float sm[4][64], sl[4][64];
-  __shared__ float Mrow[64], Lrow[64];
+  __shared__ float lse_s[64];
   __shared__ float mass[kMaxBlockRows];
-  __shared__ unsigned long long keys[kMaxBlockRows];
+  __shared__ float wts[kMaxBlockRows];
+  __shared__ int order[kMaxBlockRows];
   __shared__ uint32_t kept[kWords];
   __shared__ int kcount;
+  __shared__ float total_s;
 
   const int h = blockIdx.z, s = blockIdx.y;
   const int r = (int)gridDim.x - 1 - (int)blockIdx.x;
   const int32_t n = seq_len_q(a.vl, s);
   if (!seq_ok(a.vl, s, n, n) || 64 * r >= n) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int qt = wave & 1, kp = wave >> 1;
   const int iloc = 32 * qt + (lane & 31);
   const int i = 64 * r + iloc;
   const bool valid = i < n;
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, n - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
   const float scale_l2 = a.scale[h] * kLog2e;
   const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
 
   QOperand<D> qop;
-  load_query<D>(qop, qrow, valid);
+  load_query_clamped<D>(qop, qrow, valid);
   f32x16 acc[2];
-  float t[32];
   float m = -INFINITY, l = 0.0f;
-  for (int c = kp; c <= r; c += 4) {
-    score_block<D>(acc, qop, kseq, 64 * c, n);
-    logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
-    const float part = online_update(t, m, l);
-    if (lane < 32) {
-      P[iloc * R + c] = part;
-      MX[iloc * R + c] = m;
-    }
-  }
+  // Round k covers blocks 4k .. 4k + 3, wave (qt, kp) takes block 4k + kp.
+  // Blocks strictly between column 0 (sink bias) and the diagonal (causal mask)
+  // take the lean update on raw scores.
+  const bool raw_ok = scale_l2 > 0.0f;
+  kstage_pipeline<D>(
+      stage, kseq, n, (r + 4) / 4, [&](int c) { return 64 * min(c, r); },
+      [&](int k, const uint8_t* buf, auto fh) {
+        constexpr int FH = decltype(fh)::value;
+        const int c = 4 * k + kp;
+        if (c > r) return;
+        if (FH == 0) acc[0] = acc[1] = f32x16{};
+        kstage_mma<D, FH>(acc, buf + kp * kStageBlockBytes, qop);
+        if (FH != D / 64 - 1) return;
+        float part;
+        if (raw_ok && c != 0 && c != r) {
+          part = online_update_raw(acc, scale_l2, m, l);
+        } else {
+          float t[32];
+          logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+          part = online_update(t, m, l);
+        }
+        if (lane < 32) LP[iloc * R + c] = m + log2f_fast(part);
+      });
   if (lane < 32) {
     sm[kp][iloc] = m;
     sl[kp][iloc] = l;
   }
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const int q = threadIdx.x;
+  if (tid < 64) {
+    const int q = tid;
     float M = -INFINITY;
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][q]);
     float L = 0.0f;
     for (int w = 0; w < 4; ++w)
       if (sm[w][q] != -INFINITY) L += sl[w][q] * exp2f_fast(sm[w][q] - M);
-    Mrow[q] = M;
-    Lrow[q] = L;
+    const float lse = M + log2f_fast(L);
+    lse_s[q] = lse;
     const int iq = 64 * r + q;
     if (iq < n) {
       const int64_t tok = (int64_t)h * a.vl.total_q + a.vl.cu_q[s] + iq;
-      a.lse2[tok] = M + log2f_fast(L);
+      a.lse2[tok] = lse;
       if (a.row_stats) {
         a.row_stats[2 * tok] = M * kLn2;
         a.row_stats[2 * tok + 1] = L;
       }
     }
   }
-  if (threadIdx.x < kWords) kept[threadIdx.x] = 0u;
+  if (tid < kWords) kept[tid] = 0u;
   __syncthreads();
+  // mass_c over the valid rows, in row order
   const int nrows = min(64, n - 64 * r);
-  for (int c = threadIdx.x; c <= r; c += 512) {
+  const int nb = r + 1;
+  for (int c = tid; c < nb; c += 512) {
     float x = 0.0f;
-    for (int q = 0; q < nrows; ++q) x += P[q * R + c] * exp2f_fast(MX[q * R + c] - Mrow[q]) / Lrow[q];
+    for (int q = 0; q < nrows; ++q) x += exp2f_fast(LP[q * R + c] - lse_s[q]);
     mass[c] = x;
   }
   __syncthreads();
@@ -105,72 +174,68 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     int64_t n_tri;  // blocks per head over all sequences
     block_offsets(a.vl, a.vl.n_seqs, r_all, n_tri);
     float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * (r + 1) / 2;
-    for (int c = threadIdx.x; c <= r; c += 512) bm[c] = mass[c];
+    for (int c = tid; c < nb; c += 512) bm[c] = mass[c];
   }
-  const int nb = r + 1;
   if (a.tau >= 1.0f) {
-    for (int c = threadIdx.x; c < kMaxBlockRows; c += 512)
-      if (c < nb) atomicOr(&kept[c >> 5], 1u << (c & 31));
-    if (threadIdx.x == 0) kcount = nb;
+    for (int c = tid; c < nb; c += 512) atomicOr(&kept[c >> 5], 1u << (c & 31));
+    if (tid == 0) kcount = nb;
   } else {
     // total mass: one wave, strided partial sums then a fixed butterfly
     if (wave == 0) {
       float x = 0.0f;
       for (int c = lane; c < nb; c += 64) x += mass[c];
       for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-      if (lane == 0) sm[0][0] = x;
+      if (lane == 0) total_s = x;
     }
     __syncthreads();
-    const float total = sm[0][0];
-    int ns = 1;
-    while (ns < nb) ns <<= 1;
-    for (int c = threadIdx.x; c < ns; c += 512) {
-      if (c < nb) {
-        const float w = mass[c] / total;
-        keys[c] = ((unsigned long long)(0xffffffffu - __float_as_uint(w)) << 32) | (uint32_t)c;
-      } else {
-        keys[c] = ~0ull;
+    const float total = total_s;
+    for (int c = tid; c < nb; c += 512) wts[c] = mass[c] / total;
+    __syncthreads();
+    // rank of block c in the order weight descending, column ascending
+    for (int c = tid; c < nb; c += 512) {
+      const float wc = wts[c];
+      int rank = 0;
+      for (int c2 = 0; c2 < nb; ++c2) {
+        const float w2 = wts[c2];
+        rank += (w2 > wc) || (w2 == wc && c2 < c);
       }
+      order[rank] = c;
     }
     __syncthreads();
-    // bitonic sort, ascending key = weight descending, column ascending
-    for (int size = 2; size <= ns; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int x = threadIdx.x; x < ns / 2; x += 512) {
-          const int lo = 2 * stride * (x / stride) + (x % stride);
-          const int hi = lo + stride;
-          const bool up = (lo & size) == 0;
-          const unsigned long long kl = keys[lo], kh = keys[hi];
-          if ((kl > kh) == up) {
-            keys[lo] = kh;
-            keys[hi] = kl;
-          }
-        }
-        __syncthreads();
+    // running sum in that order (wave 0: 4 consecutive ranks per lane, then a
+    // wave-wide inclusive scan of the lane totals); keep the shortest prefix
+    // whose sum reaches tau
+    if (wave == 0) {
+      float cum[4];
+      float run = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = 4 * lane + e;
+        run += x < nb ? wts[order[x]] : 0.0f;
+        cum[e] = run;
       }
-    }
-    if (threadIdx.x == 0) {
-      float cum = 0.0f;
-      int k = nb;
-      for (int x = 0; x < nb; ++x) {
-        const int c = (int)(keys[x] & 0xffffffffu);
-        cum += mass[c] / total;
-        if (cum >= a.tau) {
-          k = x + 1;
-          break;
-        }
+      float pre = run;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(pre, off, 64);
+        if (lane >= off) pre += y;
       }
-      kcount = k;
+      const float before = pre - run;
+      int first = 4 * 64;
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (4 * lane + e < nb && before + cum[e] >= a.tau) first = 4 * lane + e;
+      for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+      if (lane == 0) kcount = first < nb ? first + 1 : nb;
     }
     __syncthreads();
-    for (int x = threadIdx.x; x < kcount; x += 512) {
-      const int c = (int)(keys[x] & 0xffffffffu);
+    for (int x = tid; x < kcount; x += 512) {
+      const int c = order[x];
       atomicOr(&kept[c >> 5], 1u << (c & 31));
     }
   }
   __syncthreads();
-  if (threadIdx.x < kWords) a.kept[g * kWords + threadIdx.x] = kept[threadIdx.x];
-  if (threadIdx.x == 0) a.counts[g] = kcount;
+  if (tid < kWords) a.kept[g * kWords + tid] = kept[tid];
+  if (tid == 0) a.counts[g] = kcount;
 }
 
 // Exclusive scan of the kept counts (one workgroup). Deterministic (integers).
@@ -201,8 +266,13 @@ __global__ __launch_bounds__(1024) void k_bsr_scan(const int32_t* counts, int64_
   }
 }
 
+// Extraction of the kept blocks of one (head, sequence, block-row): blocks are
+// taken 4 per round from the column list, wave (qt, kp) computing block 4k + kp
+// for its 32 query rows from the staged K.
 template <int D>
 __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   __shared__ int cols[kMaxBlockRows];
   __shared__ int ncols;
   const int h = blockIdx.z, s = blockIdx.y;
@@ -214,53 +284,90 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   int64_t tri_off;
   block_offsets(a.vl, s, roff, tri_off);
   const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    // column list in ascending order: one word of the kept mask per lane step
     int k = 0;
     for (int w = 0; w < kWords; ++w) {
-      uint32_t bits = a.kept[g * kWords + w];
-      while (bits) {
-        const int b = __builtin_ctz(bits);
-        cols[k++] = 32 * w + b;
-        bits &= bits - 1;
-      }
+      const uint32_t bits = a.kept[g * kWords + w];
+      const int lane = tid;
+      if (lane < 32 && (bits >> lane) & 1u) cols[k + __builtin_popcount(bits & ((1u << lane) - 1u))] = 32 * w + lane;
+      k += __builtin_popcount(bits);
     }
-    ncols = k;
+    if (tid == 0) ncols = k;
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nc = ncols;
+  if (nc == 0) return;
+  for (int x = tid; x < nc; x += 512) a.col_idx[a.row_ptr[g] + x] = cols[x];
+  const int wave = tid >> 6, lane = tid & 63;
   const int qt = wave & 1, kp = wave >> 1;
   const int iloc = 32 * qt + (lane & 31);
   const int i = 64 * r + iloc;
   const bool valid = i < n;
   const int half = lane >> 5;
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, n - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
   const float scale_l2 = a.scale[h] * kLog2e;
   const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
   const float lse = valid ? a.lse2[(int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i] : 0.0f;
   const int64_t base = a.row_ptr[g];
   QOperand<D> qop;
-  load_query<D>(qop, qrow, valid);
+  load_query_clamped<D>(qop, qrow, valid);
   f32x16 acc[2];
-  float t[32];
-  for (int x = kp; x < ncols; x += 4) {
-    const int c = cols[x];
-    score_block<D>(acc, qop, kseq, 64 * c, n);
-    logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
-    uint16_t* blk = a.vals + (base + x) * (int64_t)(kBlock * kBlock);
+  const bool raw_ok = scale_l2 > 0.0f;
+  kstage_pipeline<D>(
+      stage, kseq, n, (nc + 3) / 4, [&](int x) { return 64 * cols[min(x, nc - 1)]; },
+      [&](int k, const uint8_t* buf, auto fh) {
+        constexpr int FH = decltype(fh)::value;
+        const int x = 4 * k + kp;
+        if (x >= nc) return;
+        if (FH == 0) acc[0] = acc[1] = f32x16{};
+        kstage_mma<D, FH>(acc, buf + kp * kStageBlockBytes, qop);
+        if (FH != D / 64 - 1) return;
+        const int c = cols[x];
+        // p = 2^(logit - lse) in the accumulator registers (0 for rows past the end)
+        if (raw_ok && c != 0 && c != r) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        float p[4];
+            for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(fmaf(acc[kt][v], scale_l2, -lse));
+        } else {
+          float t[32];
+          logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = valid ? exp2f_fast(t[kt * 16 + 4 * gq + e] - lse) : 0.0f;
-        const int j = 32 * kt + 8 * gq + 4 * half;
-        u32x2 w = {pack2bf(p[0], p[1]), pack2bf(p[2], p[3])};
-        *reinterpret_cast<u32x2*>(blk + blk_off(iloc, j)) = w;
-      }
-    if (qt == 0 && lane == 0) a.col_idx[base + x] = c;
-  }
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(t[16 * kt + v] - lse);
+        }
+        if (!valid) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) acc[kt] = f32x16{};
+        }
+        // Lane (query, half) holds keys 32kt + 8g + 4half + 0..3 for g = 0..3. One
+        // exchange with the partner lane (lane ^ 32) per pair of groups leaves lane
+        // half h with the 8 consecutive keys 32kt + 16g2 + 8h .. +7, so that each
+        // store writes 16 bytes and one instruction fills a whole 1 KB run of a
+        // panel (32 rows x 16 keys).
+        uint16_t* blk = a.vals + (base + x) * (int64_t)(kBlock * kBlock);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int v0 = 8 * g2;  // elements v0..v0+3 (group 2g2), v0+4..v0+7 (group 2g2+1)
+            const uint32_t x0 = pack2bf(acc[kt][v0], acc[kt][v0 + 1]);
+            const uint32_t x1 = pack2bf(acc[kt][v0 + 2], acc[kt][v0 + 3]);
+            const uint32_t y0 = pack2bf(acc[kt][v0 + 4], acc[kt][v0 + 5]);
+            const uint32_t y1 = pack2bf(acc[kt][v0 + 6], acc[kt][v0 + 7]);
+            // lanes 0-31 keep x and receive the partner's x; lanes 32-63 receive
+            // the partner's y and keep their own y
+            const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+            const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+            const int panel = 2 * kt + g2;
+            *reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half) = w;
+          }
+      });
 }
 
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t value) {
@@ -284,12 +391,12 @@ size_t compress_ws_bytes(int32_t n_heads, int32_t n_block_rows, int64_t total_q)
 template <int D>
 static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   dim3 grid(a.nrb_max, a.vl.n_seqs, a.n_heads);
-  const size_t lds = (size_t)2 * 64 * a.nrb_max * sizeof(float);
-  hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<D>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e0 != hipSuccess) return e0;
+  const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * a.nrb_max * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   { KernelTimer kt_("k_block_stats", st); hipLaunchKernelGGL((k_block_stats<D>), grid, dim3(512), lds, st, a); }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("k_bsr_scan", st);
@@ -298,7 +405,11 @@ static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  { KernelTimer kt_("k_block_extract", st); hipLaunchKernelGGL((k_block_extract<D>), grid, dim3(512), 0, st, a); }
+  const size_t lds_x = 2 * (size_t)kStageBytes;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_extract<D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_x);
+  if (e != hipSuccess) return e;
+  { KernelTimer kt_("k_block_extract", st); hipLaunchKernelGGL((k_block_extract<D>), grid, dim3(512), lds_x, st, a); }
   return hipGetLastError();
 }
 

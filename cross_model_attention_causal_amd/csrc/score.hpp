@@ -29,14 +29,35 @@ __device__ __forceinline__ void load_query(QOperand<D>& op, const uint16_t* qrow
   }
 }
 
-// Scores of keys [key0, key0 + 64) (rows of K starting at kseq) against the
-// wave's queries. Keys at or beyond nk give 0 (the caller masks them).
+// As load_query for a row index that may lie past the sequence end: every lane
+// loads (row `safe`, an existing row) and invalid lanes then take zeros, so no
+// load sits under a divergent branch.
 template <int D>
-__device__ __forceinline__ void score_block(f32x16 acc[2], const QOperand<D>& qop,
-                                            const uint16_t* __restrict__ kseq, int key0, int nk) {
+__device__ __forceinline__ void load_query_clamped(QOperand<D>& op, const uint16_t* qrow_safe, bool valid) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 x = ldg16(qrow_safe + 16 * ks + 8 * half);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = valid ? x[e] : 0u;
+    op.v[ks] = as_bf16x8(x);
+  }
+}
+
+// One 64-key block of K as the A operand of 32x32x16 (lane holds key
+// key0 + 32kt + lane % 32, features 16ks + 8(lane/32) + e). Held in registers so
+// that the next block can be fetched while the current one is multiplied.
+template <int D>
+struct KTile {
+  u32x4 a[2][D / 16];
+};
+
+// Load keys [key0, key0 + 64) (rows of K starting at kseq); keys at or beyond nk
+// read as zero (the caller masks them).
+template <int D>
+__device__ __forceinline__ void load_k(KTile<D>& kt_, const uint16_t* __restrict__ kseq, int key0, int nk) {
   const int lane = threadIdx.x & 63;
   const int m = lane & 31, half = lane >> 5;
-  u32x4 a[2][D / 16];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int key = key0 + 32 * kt + m;
@@ -46,16 +67,99 @@ __device__ __forceinline__ void score_block(f32x16 acc[2], const QOperand<D>& qo
     for (int ks = 0; ks < D / 16; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (ok) x = ldg16(krow + 16 * ks);
-      a[kt][ks] = x;
+      kt_.a[kt][ks] = x;
     }
   }
+}
+
+template <int D>
+__device__ __forceinline__ void mma_k(f32x16 acc[2], const KTile<D>& kt_, const QOperand<D>& qop) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     f32x16 c = {};
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) c = mfma32(as_bf16x8(a[kt][ks]), qop.v[ks], c);
+    for (int ks = 0; ks < D / 16; ++ks) c = mfma32(as_bf16x8(kt_.a[kt][ks]), qop.v[ks], c);
     acc[kt] = c;
   }
+}
+
+// Scores of keys [key0, key0 + 64) against the wave's queries (load + multiply).
+template <int D>
+__device__ __forceinline__ void score_block(f32x16 acc[2], const QOperand<D>& qop,
+                                            const uint16_t* __restrict__ kseq, int key0, int nk) {
+  KTile<D> k;
+  load_k<D>(k, kseq, key0, nk);
+  mma_k<D>(acc, k, qop);
+}
+
+// ---- K staged in LDS
+// A stage holds 4 key blocks x 64 keys x 64 features (one half of D = 128, or
+// all of D = 64): 128 bytes per key as 8 chunks of 16 bytes, chunk ch of key m
+// in slot ch ^ ((m >> 1) & 7), so that the 16 lanes of one read pass (keys
+// m..m+15, one chunk column) hit 16 distinct 4-bank groups. Block b occupies
+// bytes [8192 b, 8192 (b + 1)) of the stage. The two query tiles of a block-row
+// read the same stage, so K crosses L2 -> LDS once per workgroup, in 1 KB runs.
+constexpr int kStageBlockBytes = 64 * 128;
+constexpr int kStageBytes = 4 * kStageBlockBytes;
+
+// Copy of feature half FH of the 4 blocks whose first keys are key0[b], in two
+// parts so that the global loads can be in flight while the stage in use is
+// read: kstage_load fetches into registers, kstage_store writes them to a stage.
+// 512 threads: wave w moves keys 8w .. 8w + 7 of every block, one 16-byte chunk
+// per lane and block, so each load reads 8 whole 128-byte lines and each LDS
+// write fills 1 KB contiguously. Keys at or beyond nk are clamped to nk - 1:
+// finite values the caller masks.
+struct KStageRegs {
+  u32x4 x[4];
+};
+
+template <int D, int FH>
+__device__ __forceinline__ void kstage_load(KStageRegs& rg, const uint16_t* __restrict__ kseq, int nk,
+                                            const int key0[4]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = 8 * wave + (lane >> 3), s = lane & 7;
+  const int ch = s ^ ((m >> 1) & 7);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int key = min(key0[b] + m, nk - 1);
+    rg.x[b] = ldg16(kseq + (int64_t)key * D + 64 * FH + 8 * ch);
+  }
+}
+
+__device__ __forceinline__ void kstage_store(uint8_t* stage, const KStageRegs& rg) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) *reinterpret_cast<u32x4*>(stage + b * kStageBlockBytes + 16 * tid) = rg.x[b];
+}
+
+// acc[kt] += K_half(block at blk) x Q_half^T for feature half FH (A operand from
+// the stage, B operand = the wave's queries). The two kt chains are interleaved.
+template <int D, int FH>
+__device__ __forceinline__ void kstage_mma(f32x16 acc[2], const uint8_t* blk, const QOperand<D>& qop) {
+  const int lane = threadIdx.x & 63;
+  const int hl = lane >> 5;
+  u32x4 x[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int m = 32 * kt + (lane & 31);
+      const int ch = 2 * ks + hl;
+      x[ks][kt] = *reinterpret_cast<const u32x4*>(blk + m * 128 + 16 * (ch ^ ((m >> 1) & 7)));
+    }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32(as_bf16x8(x[ks][kt]), qop.v[4 * FH + ks], acc[kt]);
+}
+
+// Workgroup barrier that waits for this wave's LDS accesses but, unlike
+// __syncthreads, not for its global loads (prefetches stay in flight). The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Key index of element (kt, v) of a score block.
@@ -96,6 +200,33 @@ __device__ __forceinline__ float online_update(const float t[32], float& m, floa
   float s = 0.0f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) s += exp2f_fast(t[e] - mn);
+  s += xor_lane(s, 32);
+  l = l * exp2f_fast(m - mn) + s;
+  m = mn;
+  return s;
+}
+
+// Online update for a block that needs no mask and no sink bias (every key is
+// visible to every query of the wave and none is key 0), taking the raw scores.
+// Requires scale_l2 > 0, so that the largest raw score gives the largest logit;
+// the exponent is one fused multiply-add, 2^(s * scale_l2 - max).
+__device__ __forceinline__ float online_update_raw(const f32x16 acc[2], float scale_l2, float& m, float& l) {
+  float b4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) b4[u] = fmaxf(acc[0][u], acc[0][u + 4]);
+#pragma unroll
+  for (int v = 8; v < 16; ++v) b4[v & 3] = fmaxf(b4[v & 3], acc[0][v]);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) b4[v & 3] = fmaxf(b4[v & 3], acc[1][v]);
+  float bm = fmaxf(fmaxf(b4[0], b4[1]), fmaxf(b4[2], b4[3]));
+  bm = fmaxf(bm, xor_lane(bm, 32)) * scale_l2;
+  const float mn = fmaxf(m, bm);
+  float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s4[v & 3] += exp2f_fast(fmaf(acc[kt][v], scale_l2, -mn));
+  float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   s += xor_lane(s, 32);
   l = l * exp2f_fast(m - mn) + s;
   m = mn;
