@@ -12,11 +12,12 @@ heads, d = 128, bf16. One step runs every stage of the path once:
   2. head_map_cosine  4 problems of 24 x 32 over 131,328 entries -> argmax, margin
   3. onehot_mix       IAM head map as a per-prompt one-hot mixing matrix
   4. block_compress   32 heads x 4 x 8192 tokens, 64x64 blocks, tau = 0.95
-  5. mapped_av        fused block-sparse mix x V for 24 receiver heads (learned M)
+  5. mapped_av        V tiled into the fused kernel's operand order, then the fused
+                      block-sparse mix x V for 24 receiver heads (learned M)
   6. decode row       first generated token: sender rows over 8193 keys, then
                       mapped x V with the one-hot IAM head map
 plus the host-side mapped-layer order. Inputs are resident in HBM before timing;
-the receiver's V is key-major (the layout its V projection writes).
+the receiver's V is token-major [heads, tokens, d].
 
 Prints one JSON line. ``--gpus N`` with N > 1 is not supported: this build runs
 on one GPU.
@@ -85,7 +86,7 @@ def main():
 
     send_q, send_k = bf(x["send_q"]), bf(x["send_k"])
     recv_q, recv_k = bf(x["recv_q"]), bf(x["recv_k"])
-    vt = bf(np.ascontiguousarray(x["v"].transpose(0, 2, 1)))  # key-major V [24, 128, P*slot]
+    v = bf(x["v"])  # token-major V [24, P*slot, 128], as a V projection writes it
     dec_q = bf(x["dec_q"])
     s_scale, s_bias = f32(x["send_scale"]), f32(x["send_bias"])
     r_scale, r_bias = f32(x["recv_scale"]), f32(x["recv_bias"])
@@ -105,7 +106,7 @@ def main():
                    col_idx=torch.empty(cap, dtype=torch.int32, device=dev),
                    vals=torch.empty((cap, 64, 64), dtype=torch.bfloat16, device=dev),
                    nnz=torch.empty(1, dtype=torch.int32, device=dev), capacity=cap)
-    ws_c = cma.Workspace()
+    ws_c, ws_v = cma.Workspace(), cma.Workspace()
     O = torch.empty((Hr, P * n, 128), dtype=torch.bfloat16, device=dev)
     rows = torch.empty((Hs, vl_dec.maps_elems(cma.DENSE)), dtype=torch.float32, device=dev)
     od = torch.empty((Hr, P, 128), dtype=torch.bfloat16, device=dev)
@@ -119,12 +120,11 @@ def main():
         Mdec = cma.onehot_mix(arg, Hs)                                       # 3
         bsr = cma.block_compress(send_q, send_k, s_scale, s_bias, vl_pref, args.tau,
                                  workspace=ws_c, bsr=bsr_buf)                 # 4
-        cma.mapped_av(bsr, Hs, M, Hr, vt, vl_pref, out=O, q_rows=P * n,
-                      v_layout=cma.V_KEY_MAJOR)                               # 5
+        cma.mapped_av(bsr, Hs, M, Hr, v, vl_pref, out=O, q_rows=P * n,
+                      workspace=ws_v)                                         # 5
         cma.attn_maps(dec_q, send_k, s_scale, s_bias, vl_dec, layout=cma.DENSE,
                       out_dtype=torch.float32, out=rows)                      # 6
-        cma.mapped_av(("dense", rows, cma.DENSE), Hs, Mdec, Hr, vt, vl_dec, out=od, q_rows=P,
-                      v_layout=cma.V_KEY_MAJOR)
+        cma.mapped_av(("dense", rows, cma.DENSE), Hs, Mdec, Hr, v, vl_dec, out=od, q_rows=P)
         state.update(arg=arg, mar=mar, bsr=bsr, layers=layers)
 
     for _ in range(args.warmup):
@@ -176,6 +176,7 @@ def main():
         "k_block_stats": ("mfma", f_stats),
         "k_block_extract": ("hbm", b_ext),
         "k_attn_maps": ("hbm", b_maps / 3),
+        "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2),
         "k_gram_bf16": ("mfma", f_gram),
     }
     for name, (bound, work) in specs.items():

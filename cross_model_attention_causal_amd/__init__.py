@@ -23,7 +23,7 @@ CMA_OK, CMA_EINVAL, CMA_EUNSUPPORTED, CMA_ENOSPC, CMA_EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 DENSE, PACKED = 0, 1
 SRC_DENSE, SRC_BSR = 0, 1
-V_TOKEN_MAJOR, V_KEY_MAJOR = 0, 1
+V_TOKEN_MAJOR, V_KEY_MAJOR, V_TILED = 0, 1, 2
 BLOCK = 64
 
 EXPORTS = [
@@ -283,16 +283,24 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
 
 
 def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_stride=None,
-              workspace: Workspace | None = None, out=None, q_rows=None, v_layout=V_TOKEN_MAJOR):
+              workspace: Workspace | None = None, out=None, q_rows=None, v_layout=V_TOKEN_MAJOR,
+              k_rows=None):
     """O_h = (sum_j M[h, j] A_j) V_h. ``src`` is either a block_compress result
     (dict with row_ptr/col_idx/vals/n_block_rows) or ``("dense", maps, layout)``.
-    ``v`` is [n_recv, Tk, d] (V_TOKEN_MAJOR) or [n_recv, d, Tk] (V_KEY_MAJOR).
-    ``q_rows`` is the row count of the output tensor (default: Tk)."""
+    ``v`` is [n_recv, Tk, d] (V_TOKEN_MAJOR), [n_recv, d, Tk] (V_KEY_MAJOR) or
+    [n_recv, n_block_rows, 64 * 128] (V_TILED, block-sparse source only; then
+    ``k_rows`` gives Tk). ``q_rows`` is the row count of the output tensor
+    (default: Tk)."""
     torch = _torch()
     lib = load_library()
     dev = v.device
     if v_layout == V_KEY_MAJOR:
         H, d, Tk = v.shape
+    elif v_layout == V_TILED:
+        H, d = v.shape[0], 128
+        if k_rows is None:
+            raise ValueError("V_TILED needs k_rows (the key rows of the packed sequences)")
+        Tk = k_rows
     else:
         H, Tk, d = v.shape
     out_dtype = out_dtype or v.dtype

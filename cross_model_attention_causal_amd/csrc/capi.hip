@@ -352,10 +352,11 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
 
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k,
                                cma_v_layout v_layout) {
-  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_KEY_MAJOR || n_recv <= 0 || d <= 0 ||
-      total_k <= 0)
+  (void)total_k;
+  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || n_recv <= 0 || d <= 0 ||
+      src->n_block_rows <= 0)
     return 0;
-  return (size_t)n_recv * d * total_k * sizeof(uint16_t);
+  return (size_t)n_recv * src->n_block_rows * kBlock * d * sizeof(uint16_t);
 }
 
 int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
@@ -363,7 +364,8 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
                   const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
                   size_t workspace_bytes, void* stream) {
   if (!src) return fail(CMA_EINVAL, "NULL maps source");
-  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR) return fail(CMA_EINVAL, "bad V layout");
+  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR && v_layout != CMA_V_TILED)
+    return fail(CMA_EINVAL, "bad V layout");
   if (int e = check_varlen(vl, true)) return e;
   if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
   if (n_send < 0 || n_recv < 0 || M_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
@@ -380,6 +382,7 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   a.v = v;
   a.v_bf16 = v_dt == CMA_BF16;
   a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
+  a.v_tiled = v_layout == CMA_V_TILED;
   a.vl = to_varlen(vl);
   a.out = out;
   a.out_bf16 = out_dt == CMA_BF16;
@@ -394,6 +397,7 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
     a.maps_bf16 = src->maps_dt == CMA_BF16;
     a.packed = src->layout == CMA_MAP_PACKED;
     a.head_stride = src->head_stride;
+    if (a.v_tiled) return fail(CMA_EUNSUPPORTED, "the tiled V layout serves block-sparse sources only");
     return hip_status(launch_mapped_av_dense(a, st), "mapped_av (dense) launch");
   }
   if (src->kind != CMA_SRC_BSR) return fail(CMA_EINVAL, "bad source kind");
@@ -410,10 +414,14 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   a.col_idx = src->col_idx;
   a.vals = static_cast<const uint16_t*>(src->vals);
   a.n_block_rows = src->n_block_rows;
-  if (a.v_key_major) {
+  if (vl->max_seqlen_q > 0 && src->n_block_rows == 0)
+    return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
+  if (a.v_tiled) {
+    if (!aligned16(v)) return fail(CMA_EINVAL, "tiled V must be 16-byte aligned");
     a.vt = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
   } else {
-    const size_t need = (size_t)n_recv * d * vl->total_k * sizeof(uint16_t);
+    if (!a.v_key_major && !aligned16(v)) return fail(CMA_EINVAL, "token-major V must be 16-byte aligned");
+    const size_t need = (size_t)n_recv * src->n_block_rows * kBlock * d * sizeof(uint16_t);
     if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
     if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
     a.vt = static_cast<uint16_t*>(workspace);

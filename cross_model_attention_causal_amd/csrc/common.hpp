@@ -17,6 +17,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 lds_bf16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kXcds = 8;    // accelerator complex dies; workgroup i runs on XCD i % 8
 constexpr int kBlock = 64;  // block-sparse tile edge (rows and columns)
 constexpr int kPanel = 16;  // columns per panel of a stored block
 // Element (i, j) of a stored 64x64 block: blocks are kept as four panels of 16

@@ -23,6 +23,37 @@
 
 namespace cma {
 
+// Work item of workgroup `id`: (head h, sequence s, block-row r). The hardware
+// deals workgroup ids round-robin over the 8 XCDs (id i runs on XCD i % 8, as
+// that XCD's (i / 8)-th workgroup). With enough (head, sequence) pairs they are
+// dealt the same way: an XCD walks the block-rows of one pair at a time, longest
+// first, and its L2 keeps that pair's K, which every block-row of the pair
+// re-reads. With few pairs (fewer than 2 per XCD) that would idle XCDs, so ids
+// then go pair by pair. Grid: pair_grid() workgroups.
+__device__ __forceinline__ bool pair_item(int id, int nrb, int n_seqs, int n_heads, int& h, int& s, int& r) {
+  const int pairs = n_seqs * n_heads;
+  int pair, j;
+  if (pairs >= 2 * kXcds) {
+    const int xcd = id % kXcds;
+    j = id / kXcds;
+    pair = xcd + kXcds * (j / nrb);
+  } else {
+    j = id;
+    pair = id / nrb;
+  }
+  if (pair >= pairs) return false;
+  h = pair / n_seqs;
+  s = pair % n_seqs;
+  r = nrb - 1 - j % nrb;
+  return true;
+}
+
+inline unsigned pair_grid(int nrb, int n_seqs, int n_heads) {
+  const int64_t pairs = (int64_t)n_seqs * n_heads;
+  if (pairs < 2 * kXcds) return (unsigned)(pairs * nrb);
+  return (unsigned)(kXcds * ((pairs + kXcds - 1) / kXcds) * nrb);
+}
+
 // Per-sub-step K pipeline shared by both phases. A sub-step is one feature half
 // of a round of 4 key blocks. Two LDS stages alternate; the global loads of
 // sub-step u + 2 are in flight (in registers) while sub-step u is computed, and
@@ -88,8 +119,8 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   __shared__ int kcount;
   __shared__ float total_s;
 
-  const int h = blockIdx.z, s = blockIdx.y;
-  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;
+  int h, s, r;
+  if (!pair_item(blockIdx.x, a.nrb_max, a.vl.n_seqs, a.n_heads, h, s, r)) return;
   const int32_t n = seq_len_q(a.vl, s);
   if (!seq_ok(a.vl, s, n, n) || 64 * r >= n) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -275,8 +306,8 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   __shared__ int cols[kMaxBlockRows];
   __shared__ int ncols;
-  const int h = blockIdx.z, s = blockIdx.y;
-  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;
+  int h, s, r;
+  if (!pair_item(blockIdx.x, a.nrb_max, a.vl.n_seqs, a.n_heads, h, s, r)) return;
   const int32_t n = seq_len_q(a.vl, s);
   if (!seq_ok(a.vl, s, n, n) || 64 * r >= n) return;
   if ((int64_t)a.nnz[0] > a.capacity) return;
@@ -390,7 +421,7 @@ size_t compress_ws_bytes(int32_t n_heads, int32_t n_block_rows, int64_t total_q)
 
 template <int D>
 static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
-  dim3 grid(a.nrb_max, a.vl.n_seqs, a.n_heads);
+  dim3 grid(pair_grid(a.nrb_max, a.vl.n_seqs, a.n_heads));
   const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * a.nrb_max * sizeof(float);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

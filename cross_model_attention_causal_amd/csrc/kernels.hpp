@@ -93,10 +93,11 @@ struct MappedAvArgs {
   const void* v;
   bool v_bf16;
   bool v_key_major;  // v is [n_recv][d][total_k]
+  bool v_tiled;      // v is in the fused kernel's operand order (bsr path)
   Varlen vl;
   void* out;
   bool out_bf16;
-  uint16_t* vt;  // workspace: [n_recv][d][total_k] transposed V (bsr path)
+  uint16_t* vt;  // bsr path: tiled V [n_recv][n_block_rows][64 * d] (v itself or the workspace)
   int32_t max_q;
 };
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);

@@ -45,23 +45,54 @@ constexpr int kBHead = 2312;         // bf16 per mixed-map head (32 rows x 72 + 
 constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
 constexpr uint16_t kNoBlock = 0xffff;
 
-// Vt[h][e][t] = V[h][t][e]; grid (ceil(total_k / 64), n_heads), 256 threads.
-template <int D>
-__global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt,
-                                                     int64_t total_k) {
-  __shared__ uint16_t tile[64][D + 2];
-  const int h = blockIdx.y;
-  const int64_t t0 = (int64_t)blockIdx.x * 64;
-  const uint16_t* src = v + ((int64_t)h * total_k) * D;
-  for (int x = threadIdx.x; x < 64 * D; x += 256) {
-    const int tt = x / D, e = x % D;
-    tile[tt][e] = (t0 + tt < total_k) ? src[(t0 + tt) * D + e] : (uint16_t)0;
+// V in the fused kernel's operand order ("tiled"): for head h and 64-key block b
+// of the block grid (sequence s's blocks start at its block-row offset, as in
+// the block-sparse maps), 16 KB hold, for feature tile dt (32 features) and
+// k-step ks, 64 lanes x 8 keys: lane L, element e is
+//   V[key 64c + 32(L / 32) + 8ks + e][feature 32dt + L % 32],
+// zero past the sequence end. One 16-byte load per lane then reads a whole
+// contiguous 1 KB MFMA operand.
+__device__ __forceinline__ int64_t vtile_off(int dt, int ks, int lane) { return ((dt * 4 + ks) * 64 + lane) * 8; }
+
+// grid (nrb_max, n_seqs, n_recv), 256 threads: one 64-key block of one head.
+template <bool KEY_MAJOR>
+__global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, uint16_t* __restrict__ vtile,
+                                                Varlen vl, int32_t n_block_rows) {
+  constexpr int D = 128;
+  __shared__ uint16_t tile[64][D + 8];
+  const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int32_t n = seq_len_q(vl, s), nk = seq_len_k(vl, s);
+  if (!seq_ok(vl, s, n, nk) || 64 * c >= n) return;
+  int32_t roff;
+  int64_t tri;
+  block_offsets(vl, s, roff, tri);
+  const int64_t k0 = vl.cu_k[s] + 64 * c;
+  const int valid = min(64, n - 64 * c);
+  if (KEY_MAJOR) {
+    // rows of 64 keys per feature: 8 lanes x 16 B per feature row
+    for (int x = threadIdx.x; x < D * 8; x += 256) {
+      const int f = x >> 3, k8 = 8 * (x & 7);
+      const uint16_t* src = v + ((int64_t)h * D + f) * vl.total_k + k0 + k8;
+      for (int e = 0; e < 8; ++e) tile[k8 + e][f] = (k8 + e < valid) ? src[e] : (uint16_t)0;
+    }
+  } else {
+    // 64 contiguous key rows of 256 B
+    for (int x = threadIdx.x; x < 64 * (D / 8); x += 256) {
+      const int key = x / (D / 8), f8 = 8 * (x % (D / 8));
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (key < valid) w = ldg16(v + ((int64_t)h * vl.total_k + k0 + key) * D + f8);
+      *reinterpret_cast<u32x4*>(&tile[key][f8]) = w;
+    }
   }
   __syncthreads();
-  uint16_t* dst = vt + (int64_t)h * D * total_k;
-  for (int x = threadIdx.x; x < 64 * D; x += 256) {
-    const int e = x / 64, tt = x % 64;
-    if (t0 + tt < total_k) dst[(int64_t)e * total_k + t0 + tt] = tile[tt][e];
+  uint16_t* dst = vtile + ((int64_t)h * n_block_rows + roff + c) * (64 * D);
+  for (int x = threadIdx.x; x < 64 * D / 8; x += 256) {
+    // x = (dt * 4 + ks) * 64 + lane
+    const int lane = x & 63, dk = x >> 6, ks = dk & 3, dt = dk >> 2;
+    const int key0 = 32 * (lane >> 5) + 8 * ks, f = 32 * dt + (lane & 31);
+    uint32_t w[4];
+    for (int e = 0; e < 4; ++e) w[e] = tile[key0 + 2 * e][f] | ((uint32_t)tile[key0 + 2 * e + 1][f] << 16);
+    *reinterpret_cast<u32x4*>(dst + (int64_t)x * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -73,7 +104,6 @@ __global__ __launch_bounds__(256) void k_transpose_v(const uint16_t* __restrict_
 // descending, sequences interleaved) and unit u goes to XCD u % 8: with up to 8
 // sequences an XCD keeps to the same sequences, whose block-rows then sweep the
 // key blocks together and share V tiles in its L2.
-constexpr int kXcds = 8;
 
 __device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_hg, int& s, int& r, int& rh, int& hg) {
   const int per_unit = 2 * n_hg;
@@ -159,7 +189,6 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     for (int dt = 0; dt < 4; ++dt) acc[t][dt] = f32x16{};
   __syncthreads();
 
-  const int64_t k0 = a.vl.cu_k[s];
   const int row_base = 64 * r + kRowsPerWg * rh;
   const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
   const int n32 = lane & 31, q2 = lane >> 5;
@@ -169,16 +198,13 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     return cc <= r ? cc : -1;
   };
   int n_valid = 0;  // heads of this wave below n_recv (uniform)
-  const uint16_t* vrow[kHeadsPerWave];
+  const uint16_t* vblk[kHeadsPerWave];  // head's tiled V at block 0 of this sequence, + lane
 #pragma unroll
   for (int t = 0; t < kHeadsPerWave; ++t) {
     const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
     n_valid += h < a.n_recv;
-    vrow[t] = a.vt + ((int64_t)min(h, a.n_recv - 1) * D + n32) * a.vl.total_k + k0 + 32 * q2;
+    vblk[t] = a.vt + ((int64_t)min(h, a.n_recv - 1) * a.n_block_rows + roff) * (kBlock * D) + 8 * lane;
   }
-  const int64_t dstride = (int64_t)32 * a.vl.total_k;
-  const bool v_vec = ((a.vl.total_k & 7) == 0) && ((k0 & 7) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(a.vt) & 15) == 0);
   // Stage one 16-key panel of block (r, c) for all senders into stage buffer b:
   // each wave copies its senders' 1 KB pieces straight into LDS (16 B per lane)
   // or zero-fills a sender that did not keep the block.
@@ -198,25 +224,13 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       }
     }
   };
-  // V operand (head slot t, feature tile dt, k-step ks) of block c: in k-step ks,
-  // lane half q2 holds keys 32 q2 + 8 ks .. +8 (so a lane's four k-steps read 64
-  // contiguous bytes of one feature row); the mixed-map operand uses the same
-  // key order.
-  auto load_v = [&](int t, int dt, int64_t key0, bool fast, u32x4 vb[4]) {
-    const uint16_t* src = vrow[t] + dt * dstride + key0;
-    if (fast) {
+  // V operand (head slot t, feature tile dt, all four k-steps) of block c: four
+  // contiguous 1 KB runs of the tiled V. In k-step ks lane half q2 holds keys
+  // 32 q2 + 8 ks .. +8; the mixed-map operand uses the same key order.
+  auto load_v = [&](int t, int dt, int c, u32x4 vb[4]) {
+    const uint16_t* src = vblk[t] + (int64_t)c * (kBlock * D) + dt * 2048;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) vb[ks] = ldg16(src + 8 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        uint16_t e8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = (key0 + 32 * q2 + 8 * ks + e < n) ? src[8 * ks + e] : (uint16_t)0;
-        vb[ks] = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16),
-                       e8[4] | ((uint32_t)e8[5] << 16), e8[6] | ((uint32_t)e8[7] << 16)};
-      }
-    }
+    for (int ks = 0; ks < 4; ++ks) vb[ks] = ldg16(src + 512 * ks);
   };
 
   int c = anyc[0] ? 0 : next_col(0);
@@ -254,8 +268,6 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       buf ^= 1;
     }
     // ---- O += B_h V_h over the block's 64 keys
-    const int64_t key0 = 64 * c;
-    const bool fast = v_vec && (key0 + 64 <= n);
 #pragma unroll
     for (int t = 0; t < kHeadsPerWave; ++t) {
       if (t >= n_valid) break;
@@ -265,10 +277,10 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       for (int ks = 0; ks < 4; ++ks)
         av[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 32 * q2 + 8 * ks]));
       u32x4 vb[2][4];
-      load_v(t, 0, key0, fast, vb[0]);
+      load_v(t, 0, c, vb[0]);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        if (dt < 3) load_v(t, dt + 1, key0, fast, vb[(dt + 1) & 1]);
+        if (dt < 3) load_v(t, dt + 1, c, vb[(dt + 1) & 1]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) acc[t][dt] = mfma32(av[ks], as_bf16x8(vb[dt & 1][ks]), acc[t][dt]);
       }
@@ -457,15 +469,19 @@ hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
 
 hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
-  if (a.vl.total_k > 0 && !a.v_key_major) {
-    dim3 tg((unsigned)((a.vl.total_k + 63) / 64), a.n_recv);
-    KernelTimer kt_("k_transpose_v", st);
-    hipLaunchKernelGGL((k_transpose_v<128>), tg, dim3(256), 0, st,
-                       reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl.total_k);
+  const int nrb = (a.max_q + 63) / 64;
+  if (!a.v_tiled) {
+    dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_recv);
+    KernelTimer kt_("k_tile_v", st);
+    if (a.v_key_major)
+      hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
+                         a.vl, a.n_block_rows);
+    else
+      hipLaunchKernelGGL(k_tile_v<false>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
+                         a.vl, a.n_block_rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nrb = (a.max_q + 63) / 64;
   const int n_hg = (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg;
   const int64_t units = (int64_t)nrb * a.vl.n_seqs;
   const int64_t rounds = (units + kXcds - 1) / kXcds;

@@ -179,9 +179,15 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
 
 /* Layout of the receiver's V. TOKEN_MAJOR: [n_recv, total_k, d] (row t holds the
  * d values of key t). KEY_MAJOR: [n_recv, d, total_k] (row e holds feature e of
- * every key), the layout a V projection can write directly for a consumer that
- * contracts over keys. */
-typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1 } cma_v_layout;
+ * every key). TILED (block-sparse source, bf16, d = 128 only): the fused
+ * kernel's operand order, [n_recv, n_block_rows, 64 * 128]: sequence s's keys in
+ * 64-key blocks numbered like the block-sparse maps' block-rows (its first block
+ * at the sum of ceil(len/64) over earlier sequences); within block c, element
+ *   ((dt * 4 + ks) * 64 + L) * 8 + e  =  V[key 64c + 32(L/32) + 8ks + e][feature 32dt + L%32]
+ * for dt, ks in 0..3, L in 0..63, e in 0..7, zero past the sequence end. A V
+ * projection can write it directly; cma_mapped_av builds it from the other two
+ * layouts in its workspace. */
+typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1, CMA_V_TILED = 2 } cma_v_layout;
 
 /* Where cma_mapped_av reads the sender maps from. */
 typedef enum { CMA_SRC_DENSE = 0, CMA_SRC_BSR = 1 } cma_src_kind;
@@ -209,9 +215,10 @@ typedef struct {
  * (M_seq_stride = 0: one matrix for all). v in `v_layout` (see cma_v_layout) and
  * out [n_recv, total_q, d] in v_dt / out_dt (bf16 or f32); accumulation is fp32.
  * d in {64, 128}, 1 <= n_send <= 64 (dense) or <= 32 (BSR). A BSR source needs
- * bf16 V and d = 128; with TOKEN_MAJOR V it first writes a key-major copy of V
- * into `workspace` (cma_mapped_av_workspace(...) bytes), with KEY_MAJOR V it
- * needs no workspace and runs as a single kernel. A dense source needs no
+ * bf16 V and d = 128; with TOKEN_MAJOR or KEY_MAJOR V it first writes the TILED
+ * copy of V into `workspace` (cma_mapped_av_workspace(...) bytes: n_recv *
+ * n_block_rows * 64 * d * 2), with TILED V it needs no workspace and runs as a
+ * single kernel. A dense source takes TOKEN_MAJOR or KEY_MAJOR V and needs no
  * workspace.
  */
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k,

@@ -56,3 +56,27 @@ def blocks_from_panels(vals):
     """Inverse of blocks_to_panels."""
     v = np.asarray(vals)
     return np.ascontiguousarray(v.reshape(-1, 4, 64, 16).transpose(0, 2, 1, 3)).reshape(-1, 64, 64)
+
+
+def tile_v(V, lens, cu):
+    """Token-major V [H, T, 128] (uint16 bf16 bits) -> the tiled operand layout the
+    library documents: [H, sum ceil(len/64), 64 * 128], block c of sequence s at
+    block offset sum_{u<s} ceil(len_u/64); element ((dt*4+ks)*64 + L)*8 + e of a
+    block is V[key 64c + 32(L//32) + 8ks + e][feature 32dt + L%32], zero past the end."""
+    V = np.asarray(V)
+    H = V.shape[0]
+    nb = [(n + 63) // 64 for n in lens]
+    out = np.zeros((H, sum(nb), 64 * 128), dtype=V.dtype)
+    dt, ks, L, e = np.meshgrid(np.arange(4), np.arange(4), np.arange(64), np.arange(8), indexing="ij")
+    key = 32 * (L // 32) + 8 * ks + e
+    feat = 32 * dt + L % 32
+    pos = (((dt * 4 + ks) * 64 + L) * 8 + e).ravel()
+    b0 = 0
+    for s, n in enumerate(lens):
+        for c in range(nb[s]):
+            blk = np.zeros((H, 64, 128), dtype=V.dtype)
+            m = min(64, n - 64 * c)
+            blk[:, :m] = V[:, cu[s] + 64 * c: cu[s] + 64 * c + m]
+            out[:, b0 + c, pos] = blk[:, key.ravel(), feat.ravel()]
+        b0 += nb[s]
+    return out

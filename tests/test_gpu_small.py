@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from tests.gpu_util import (dev_bf16, dev_f32, dev_i32, f64, host64, rel_l2, bf16_bits_from_f64,
+from tests.gpu_util import (dev_bf16, dev_f32, dev_i32, f64, host64, rel_l2, bf16_bits_from_f64, tile_v,
                             blocks_to_panels, blocks_from_panels)
 
 pytestmark = pytest.mark.gpu
@@ -203,8 +203,8 @@ def test_block_compress_small(cma, tau):
 
 
 # ------------------------------------------------------------------ mapped_av block-sparse
-@pytest.mark.parametrize("n_recv,key_major", [(24, False), (7, False), (24, True)])
-def test_mapped_av_bsr_small(cma, n_recv, key_major):
+@pytest.mark.parametrize("n_recv,v_layout", [(24, "token"), (7, "token"), (24, "key"), (24, "tiled"), (7, "tiled")])
+def test_mapped_av_bsr_small(cma, n_recv, v_layout):
     lens = [200, 64, 130]
     n_send = 32
     say(f"mapped_av bsr lens={lens} n_send={n_send} n_recv={n_recv}")
@@ -216,9 +216,12 @@ def test_mapped_av_bsr_small(cma, n_recv, key_major):
     vl = cma.Varlen(x["cu_q"], x["cu_q"])
     src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
                vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
-    if key_major:
+    if v_layout == "key":
         O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))), vl,
                           out_dtype=torch.bfloat16, v_layout=cma.V_KEY_MAJOR)
+    elif v_layout == "tiled":
+        O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(tile_v(V, lens, x["cu_q"])), vl,
+                          out_dtype=torch.bfloat16, v_layout=cma.V_TILED, k_rows=T)
     else:
         O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
