@@ -88,6 +88,15 @@ __device__ __forceinline__ u32x4 ldg16_guard_any(const uint16_t* row, int64_t j0
 // ------------------------------------------------------------------ cross-lane
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Workgroup barrier that waits for this wave's LDS accesses but, unlike
+// __syncthreads, not for its global loads (prefetches stay in flight). The empty
+// asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ packed sequences
 struct Varlen {
   int32_t n_seqs;

@@ -26,6 +26,8 @@
 // receiver head) mixes the visible part of the row into LDS (only the nonzero
 // mixing weights are read, so a one-hot M reads one sender row) and streams V
 // with 16-byte loads. Used for decode rows and small dense problems.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace cma {
@@ -33,7 +35,6 @@ namespace cma {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHeadsPerWg = 16;
-constexpr int kHeadsPerWave = kHeadsPerWg / kWaves;
 constexpr int kRowsPerWg = 32;
 constexpr int kKeysPerStep = 16;
 constexpr int kSend = 32;            // senders per workgroup (n_send <= 32)
@@ -95,6 +96,10 @@ __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, 
     *reinterpret_cast<u32x4*>(dst + (int64_t)x * 8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
+
+// Zero source for senders that did not keep a block: their staged panel is
+// copied from here like any other (1 KB, read by every lane's 16-byte copy).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_panel[kBlock * kPanel];
 
 // Work items are (sequence, block-row r, row half, head group). Items of one
 // (sequence, r) "unit" share sender rows (head groups) and V tiles (row halves),
@@ -182,11 +187,6 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     mhi = as_bf16x8(hi);
     mlo = as_bf16x8(lo);
   }
-  f32x16 acc[kHeadsPerWave][4];
-#pragma unroll
-  for (int t = 0; t < kHeadsPerWave; ++t)
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[t][dt] = f32x16{};
   __syncthreads();
 
   const int row_base = 64 * r + kRowsPerWg * rh;
@@ -197,113 +197,193 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     while (cc <= r && !anyc[cc]) ++cc;
     return cc <= r ? cc : -1;
   };
-  int n_valid = 0;  // heads of this wave below n_recv (uniform)
-  const uint16_t* vblk[kHeadsPerWave];  // head's tiled V at block 0 of this sequence, + lane
-#pragma unroll
-  for (int t = 0; t < kHeadsPerWave; ++t) {
-    const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
-    n_valid += h < a.n_recv;
-    vblk[t] = a.vt + ((int64_t)min(h, a.n_recv - 1) * a.n_block_rows + roff) * (kBlock * D) + 8 * lane;
-  }
-  // Stage one 16-key panel of block (r, c) for all senders into stage buffer b:
-  // each wave copies its senders' 1 KB pieces straight into LDS (16 B per lane)
-  // or zero-fills a sender that did not keep the block.
-  auto issue_stage = [&](int c, int jq, int b) {
-    uint16_t* dst0 = &sbuf[b * kStageElems];
+  // Sources of this wave's senders (j = wave + 8u) for one block column: the
+  // stored block's rows of this row half, or a zero page for a sender that did
+  // not keep the block (then every panel reads the same zeros). Looked up once per
+  // column, before any copy is in flight.
+  struct SendSrc {
+    const uint16_t* p[kSend / kWaves];
+    int step[kSend / kWaves];
+  };
+  auto col_src = [&](int c, SendSrc& ss) {
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u) {
       const int j = wave + kWaves * u;
       const int bi = __builtin_amdgcn_readfirstlane((int)tbl[c * kSend + j]);
-      uint16_t* dst = dst0 + j * kSendStride;
+      const int sb = __builtin_amdgcn_readfirstlane(sbeg[j]);
       if (bi != kNoBlock) {
-        const uint16_t* src = a.vals + (int64_t)(sbeg[j] + bi) * (kBlock * kBlock) +
-                              jq * (kBlock * kPanel) + (kRowsPerWg * rh) * kPanel + 8 * lane;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        ss.p[u] = a.vals + (int64_t)(sb + bi) * (kBlock * kBlock) + (kRowsPerWg * rh) * kPanel;
+        ss.step[u] = kBlock * kPanel;
       } else {
-        *reinterpret_cast<u32x4*>(dst + 8 * lane) = u32x4{0u, 0u, 0u, 0u};
+        ss.p[u] = g_zero_panel;
+        ss.step[u] = 0;
       }
     }
   };
-  // V operand (head slot t, feature tile dt, all four k-steps) of block c: four
-  // contiguous 1 KB runs of the tiled V. In k-step ks lane half q2 holds keys
-  // 32 q2 + 8 ks .. +8; the mixed-map operand uses the same key order.
-  auto load_v = [&](int t, int dt, int c, u32x4 vb[4]) {
-    const uint16_t* src = vblk[t] + (int64_t)c * (kBlock * D) + dt * 2048;
+  // Copy panel jq (16 keys) of the column into stage buffer b: each sender's 1 KB
+  // piece goes straight to LDS, 16 B per lane.
+  auto issue_stage = [&](const SendSrc& ss, int jq, int b) {
+    uint16_t* dst0 = &sbuf[b * kStageElems];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) vb[ks] = ldg16(src + 512 * ks);
+    for (int u = 0; u < kSend / kWaves; ++u) {
+      const int j = wave + kWaves * u;
+      __builtin_amdgcn_global_load_lds(ss.p[u] + jq * ss.step[u] + 8 * lane,
+                                       (__attribute__((address_space(3))) void*)(dst0 + j * kSendStride), 16, 0, 0);
+    }
+  };
+  // Mix panel jq from stage buffer b into bbuf. The stage is read with the
+  // transposing LDS load written out in asm, all eight reads of the panel and
+  // their wait in one statement: the compiler cannot see which LDS bytes the
+  // in-flight direct-to-LDS copies of the next panel write, and would otherwise
+  // wait for them before any read.
+  auto mix_panel = [&](int jq, int b) {
+    const uint16_t* b0 = &sbuf[b * kStageElems] + (8 * q + e4) * kSendStride + wave * kKeysPerStep + 4 * cc4;
+    const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)b0);
+    // offsets: rows wave + 8u (u = 0..3) are 256 B apart; senders 8q + e4 + 4
+    // (the second k-half) are 4 * kSendStride * 2 = 4352 B further
+    static_assert(kRowsPerWg / kWaves == 4 && kKeysPerStep * kWaves * 2 == 256 && kSendStride * 8 == 4352,
+                  "the offsets below assume this stage geometry");
+    u32x2 tr[8];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:4352\n"
+        "ds_read_b64_tr_b16 %2, %8 offset:256\n"
+        "ds_read_b64_tr_b16 %3, %8 offset:4608\n"
+        "ds_read_b64_tr_b16 %4, %8 offset:512\n"
+        "ds_read_b64_tr_b16 %5, %8 offset:4864\n"
+        "ds_read_b64_tr_b16 %6, %8 offset:768\n"
+        "ds_read_b64_tr_b16 %7, %8 offset:5120\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(tr[0]), "=v"(tr[1]), "=v"(tr[2]), "=v"(tr[3]), "=v"(tr[4]), "=v"(tr[5]), "=v"(tr[6]), "=v"(tr[7])
+        : "v"(a0)
+        : "memory");
+    // The mixed values go to bbuf with stores written out in asm too (the
+    // compiler would otherwise also wait for the in-flight copies before them);
+    // the barrier that publishes bbuf waits for them (lgkmcnt).
+    const uint32_t w0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)&bbuf[
+                            (4 * q) * kBHead + wave * kBRow + kKeysPerStep * jq + p]);
+#pragma unroll
+    for (int u = 0; u < kRowsPerWg / kWaves; ++u) {
+      const u32x4 bv = {tr[2 * u][0], tr[2 * u][1], tr[2 * u + 1][0], tr[2 * u + 1][1]};
+      f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
+      d1 = mfma16(mhi, as_bf16x8(bv), d1);
+      d1 = mfma16(mlo, as_bf16x8(bv), d1);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        // element ((4q + v) * kBHead + (wave + 8u) * kBRow + 16 jq + p)
+        const uint32_t addr = w0 + 2 * (v * kBHead + kWaves * u * kBRow);
+        asm volatile("ds_write_b16 %0, %1" ::"v"(addr), "v"((uint32_t)f2bf(d1[v])) : "memory");
+      }
+    }
   };
 
-  int c = anyc[0] ? 0 : next_col(0);
-  int buf = 0;
-  if (c >= 0) issue_stage(c, 0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  while (c >= 0) {
-    const int cn = next_col(c);
-    // ---- mix the block's four 16-key panels into bbuf (bf16, 64 keys per row)
-    for (int jq = 0; jq < 4; ++jq) {
-      if (jq < 3) issue_stage(c, jq + 1, buf ^ 1);
-      else if (cn >= 0) issue_stage(cn, 0, buf ^ 1);
-      const uint16_t* sb = &sbuf[buf * kStageElems];
+  // Receiver heads of the workgroup: slot t of wave w is head hg * 16 + w + 8t.
+  // NH = 2 slots per wave when the group has more than 8 heads, else 1; slots
+  // past n_recv read head n_recv - 1's V and are computed but not stored, so
+  // that every wave runs the same straight-line schedule.
+  const int heads_here = min(kHeadsPerWg, a.n_recv - hg * kHeadsPerWg);
+  auto run = [&](auto nh) {
+    constexpr int NH = decltype(nh)::value;
+    constexpr int NI = 4 * NH;  // AV items per column: (slot t, feature tile dt)
+    f32x16 acc[NH][4];
 #pragma unroll
-      for (int u = 0; u < kRowsPerWg / kWaves; ++u) {
-        const int row = wave + kWaves * u;
-        const uint16_t* b0 = sb + (8 * q + e4) * kSendStride + row * kKeysPerStep + 4 * cc4;
-        const uint16_t* b1 = b0 + 4 * kSendStride;
-        lds_bf16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) lds_bf16x4*)(b0));
-        lds_bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (__attribute__((address_space(3))) lds_bf16x4*)(b1));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo4), h2 = __builtin_bit_cast(u32x2, hi4);
-        const u32x4 bv = {l2[0], l2[1], h2[0], h2[1]};
-        f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
-        d1 = mfma16(mhi, as_bf16x8(bv), d1);
-        d1 = mfma16(mlo, as_bf16x8(bv), d1);
+    for (int t = 0; t < NH; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          bbuf[(4 * q + v) * kBHead + row * kBRow + kKeysPerStep * jq + p] = f2bf(d1[v]);
+      for (int dt = 0; dt < 4; ++dt) acc[t][dt] = f32x16{};
+    const uint16_t* vblk[NH];  // slot's tiled V at block 0 of this sequence, + lane
+#pragma unroll
+    for (int t = 0; t < NH; ++t) {
+      const int h = min(hg * kHeadsPerWg + wave + kWaves * t, a.n_recv - 1);
+      vblk[t] = a.vt + ((int64_t)h * a.n_block_rows + roff) * (kBlock * D) + 8 * lane;
+    }
+    // V operand of item k (slot k / 4, feature tile k % 4) of block c: four
+    // contiguous 1 KB runs of the tiled V. In k-step ks lane half q2 holds keys
+    // 32 q2 + 8 ks .. +8; the mixed-map operand uses the same key order.
+    auto load_v = [&](int k, int c, u32x4 vb[4]) {
+      const uint16_t* src = vblk[k / 4] + (int64_t)c * (kBlock * D) + (k % 4) * 2048;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) vb[ks] = ldg16(src + 512 * ks);
+    };
+
+    // Per block column: four panels are mixed (panel jq + 1 in flight meanwhile),
+    // then O += B V over the block's 64 keys in NI items, each item's V loaded two
+    // items ahead into a ring of three; the first two items are issued during
+    // panel 2's mixing and the next column's panel 0 during panel 3's, so both
+    // stay in flight across the remaining mixing.
+    int c = anyc[0] ? 0 : next_col(0);
+    int buf = 0;
+    SendSrc cur, nxt;
+    if (c >= 0) {
+      col_src(c, cur);
+      issue_stage(cur, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    barrier_lds();
+    u32x4 vb[3][4];
+    while (c >= 0) {
+      const int cn = next_col(c);
+      if (cn >= 0) col_src(cn, nxt);
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        if (jq < 3) issue_stage(cur, jq + 1, buf ^ 1);
+        else if (cn >= 0) issue_stage(nxt, 0, buf ^ 1);
+        if (jq == 2) {
+          load_v(0, c, vb[0]);
+          load_v(1, c, vb[1]);
+        }
+        mix_panel(jq, buf);
+        // panel jq + 1 must have landed before the next pass reads it; the copy
+        // of the next column's panel 0 (issued at jq = 3) may stay in flight
+        // through the products below, as may the V items issued at jq = 2 (8
+        // loads, newer than panel 3's copies)
+        if (jq < 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        else if (jq == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        barrier_lds();
+        buf ^= 1;
       }
+      // ---- O += B_h V_h over the block's 64 keys
+#pragma unroll
+      for (int t = 0; t < NH; ++t) {
+        bf16x8 av[4];
+        const int hh = wave + kWaves * t;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          av[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 32 * q2 + 8 * ks]));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int k = 4 * t + dt;
+          if (k + 2 < NI) load_v(k + 2, c, vb[(k + 2) % 3]);
+          // keep the scheduler from sinking the prefetch next to its use
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc[t][dt] = mfma32(av[ks], as_bf16x8(vb[k % 3][ks]), acc[t][dt]);
+        }
+      }
+      // the next column's panel 0 is read next; bbuf is rewritten by its mixing
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      buf ^= 1;
+      barrier_lds();
+      c = cn;
+      cur = nxt;
     }
-    // ---- O += B_h V_h over the block's 64 keys
+    // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
-    for (int t = 0; t < kHeadsPerWave; ++t) {
-      if (t >= n_valid) break;
-      const int hh = kHeadsPerWave * wave + t;
-      bf16x8 av[4];
+    for (int t = 0; t < NH; ++t) {
+      const int h = hg * kHeadsPerWg + wave + kWaves * t;
+      if (h >= a.n_recv) continue;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        av[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 32 * q2 + 8 * ks]));
-      u32x4 vb[2][4];
-      load_v(t, 0, c, vb[0]);
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        if (dt < 3) load_v(t, dt + 1, c, vb[(dt + 1) & 1]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc[t][dt] = mfma32(av[ks], as_bf16x8(vb[dt & 1][ks]), acc[t][dt]);
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
+          if (row >= n) continue;
+          const int64_t o = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + row) * D + 32 * dt + n32;
+          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[t][dt][v]);
+          else reinterpret_cast<float*>(a.out)[o] = acc[t][dt][v];
+        }
     }
-    __syncthreads();  // bbuf is rewritten by the next block's mixing
-    c = cn;
-  }
-  // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
-#pragma unroll
-  for (int t = 0; t < kHeadsPerWave; ++t) {
-    const int h = hg * kHeadsPerWg + kHeadsPerWave * wave + t;
-    if (h >= a.n_recv) continue;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
-        if (row >= n) continue;
-        const int64_t o = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + row) * D + 32 * dt + n32;
-        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[t][dt][v]);
-        else reinterpret_cast<float*>(a.out)[o] = acc[t][dt][v];
-      }
-  }
+  };
+  if (heads_here > kWaves) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------- dense source

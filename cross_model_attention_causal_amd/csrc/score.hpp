@@ -153,15 +153,6 @@ __device__ __forceinline__ void kstage_mma(f32x16 acc[2], const uint8_t* blk, co
     for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32(as_bf16x8(x[ks][kt]), qop.v[4 * FH + ks], acc[kt]);
 }
 
-// Workgroup barrier that waits for this wave's LDS accesses but, unlike
-// __syncthreads, not for its global loads (prefetches stay in flight). The empty
-// asm statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Key index of element (kt, v) of a score block.
 __device__ __forceinline__ int tile_key(int key0, int kt, int v) {
   const int half = (threadIdx.x & 63) >> 5;
