@@ -48,7 +48,24 @@ def parse():
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB five times (for scaling hardware byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch.
+    Hardware counters of this run give the factor that turns counter readings into
+    bytes for the kernels measured with the same counters."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "launches": 5}), flush=True)
 
 
 def log(*a):
@@ -57,6 +74,8 @@ def log(*a):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        return calibrate_copy()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "

@@ -15,6 +15,7 @@ namespace cma {
 constexpr int kGramRows = 128;  // receiver maps per workgroup
 constexpr int kGramK = 64;      // K elements per step
 constexpr int kSbStride = 72;   // padded LDS row (bf16) of the staged sender slice
+constexpr int kMaxSteps = 64;   // K-steps of one split (4096 elements)
 
 template <int NT>  // sender tiles of 16 (n_send <= 16 * NT)
 __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
@@ -36,8 +37,13 @@ __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float rn[2] = {0.f, 0.f};
-  float sn[2] = {0.f, 0.f};  // sender norms: rows threadIdx.x and threadIdx.x + 256
+  // Squared norms in two levels: a step's squares are summed apart, added to an
+  // inner running sum that is folded into the outer one every 16 steps. A single
+  // long fp32 chain would drop the many tiny squares of a probability map's tail
+  // once the sum has grown (a systematic underestimate, which biases the cosine).
+  float rn[2] = {0.f, 0.f}, rn_in[2] = {0.f, 0.f};
+  float sn[2] = {0.f, 0.f}, sn_in[2] = {0.f, 0.f};  // sender rows threadIdx.x, threadIdx.x + 256
+  int step = 0;
 
   const uint16_t* arow[2];
   bool aok[2];
@@ -67,15 +73,18 @@ __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
         av[mt][ks] = x;
       }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      float t = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float lo = __uint_as_float(av[mt][ks][e] << 16);
           const float hi = __uint_as_float(av[mt][ks][e] & 0xffff0000u);
-          rn[mt] = fmaf(lo, lo, fmaf(hi, hi, rn[mt]));
+          t = fmaf(lo, lo, fmaf(hi, hi, t));
         }
+      rn_in[mt] += t;
+    }
     __syncthreads();
     if (rt == 0) {
 #pragma unroll
@@ -83,11 +92,21 @@ __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
         const int row = threadIdx.x + 256 * u;
         if (row < NT * 16) {
           const uint16_t* srow = &sb[row * kSbStride];
+          float t = 0.0f;
           for (int e = 0; e < kGramK; ++e) {
             const float x = bf2f(srow[e]);
-            sn[u] = fmaf(x, x, sn[u]);
+            t = fmaf(x, x, t);
           }
+          sn_in[u] += t;
         }
+      }
+    }
+    if ((++step & 15) == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        rn[u] += rn_in[u];
+        sn[u] += sn_in[u];
+        rn_in[u] = sn_in[u] = 0.0f;
       }
     }
 #pragma unroll
@@ -102,6 +121,11 @@ __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
     __syncthreads();
   }
 
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    rn[u] += rn_in[u];
+    sn[u] += sn_in[u];
+  }
   // partial dot products: D[m = 4qd + v][n = p]
   float* part = a.part + ((int64_t)sp * a.n_batch + b) * a.n_recv * a.n_send;
 #pragma unroll
@@ -216,7 +240,10 @@ CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t 
   } else {
     const int64_t kblocks = (len + kGramK - 1) / kGramK;
     const int64_t tiles = (int64_t)((n_recv + kGramRows - 1) / kGramRows) * n_batch;
+    // enough splits to fill the chip, and at most kMaxSteps K-steps per split so
+    // that each partial dot product is a short fp32 accumulation chain
     int64_t splits = (512 + tiles - 1) / tiles;
+    splits = std::max<int64_t>(splits, (kblocks + kMaxSteps - 1) / kMaxSteps);
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, kblocks));
     const int64_t per = (kblocks + splits - 1) / splits;
     pl.kchunk = std::max<int64_t>(1, per) * kGramK;

@@ -124,7 +124,7 @@ __device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_h
 }
 
 // grid (8 * ceil(units / 8) * 2 * n_hg), kThreads threads.
-__global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg) {
+__global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg, int hpg) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kStages * kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t bbuf[kHeadsPerWg * kBHead];
@@ -164,11 +164,15 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     }
   }
 
-  // ---- mixing weights, A operand of 16x16x32: lane (p, q) holds M[hg*16 + p][8q + e]
+  // Head group hg holds heads hg * hpg .. + hpg - 1 (hpg <= 16: the receiver
+  // heads split evenly over the groups, so that the groups of a block-row take
+  // the same time and read the shared sender rows together).
+  const int h_lo = hg * hpg, heads_here = min(hpg, a.n_recv - h_lo);
+  // ---- mixing weights, A operand of 16x16x32: lane (p, q) holds M[h_lo + p][8q + e]
   bf16x8 mhi, mlo;
   {
     const int p = lane & 15, q = lane >> 4;
-    const int h = hg * kHeadsPerWg + p;
+    const int h = h_lo + p;
     const float* Ms = a.M + (int64_t)s * a.M_stride;
     u32x4 hi, lo;
 #pragma unroll
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = 8 * q + 2 * e2 + u;
-        const float x = (h < a.n_recv && j < a.n_send) ? Ms[(int64_t)h * a.n_send + j] : 0.0f;
+        const float x = (p < heads_here && j < a.n_send) ? Ms[(int64_t)h * a.n_send + j] : 0.0f;
         xh[u] = bf2f(f2bf(x));
         xl[u] = x - xh[u];
       }
@@ -277,11 +281,10 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     }
   };
 
-  // Receiver heads of the workgroup: slot t of wave w is head hg * 16 + w + 8t.
+  // Receiver heads of the workgroup: slot t of wave w is head h_lo + w + 8t.
   // NH = 2 slots per wave when the group has more than 8 heads, else 1; slots
-  // past n_recv read head n_recv - 1's V and are computed but not stored, so
+  // past the group read its last head's V and are computed but not stored, so
   // that every wave runs the same straight-line schedule.
-  const int heads_here = min(kHeadsPerWg, a.n_recv - hg * kHeadsPerWg);
   auto run = [&](auto nh) {
     constexpr int NH = decltype(nh)::value;
     constexpr int NI = 4 * NH;  // AV items per column: (slot t, feature tile dt)
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     const uint16_t* vblk[NH];  // slot's tiled V at block 0 of this sequence, + lane
 #pragma unroll
     for (int t = 0; t < NH; ++t) {
-      const int h = min(hg * kHeadsPerWg + wave + kWaves * t, a.n_recv - 1);
+      const int h = h_lo + min(wave + kWaves * t, heads_here - 1);
       vblk[t] = a.vt + ((int64_t)h * a.n_block_rows + roff) * (kBlock * D) + 8 * lane;
     }
     // V operand of item k (slot k / 4, feature tile k % 4) of block c: four
@@ -368,8 +371,8 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
     for (int t = 0; t < NH; ++t) {
-      const int h = hg * kHeadsPerWg + wave + kWaves * t;
-      if (h >= a.n_recv) continue;
+      if (wave + kWaves * t >= heads_here) continue;
+      const int h = h_lo + wave + kWaves * t;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -563,12 +566,13 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const int n_hg = (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg;
+  const int hpg = (a.n_recv + n_hg - 1) / n_hg;
   const int64_t units = (int64_t)nrb * a.vl.n_seqs;
   const int64_t rounds = (units + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(rounds * kXcds * 2 * n_hg));
   {
     KernelTimer kt_("k_mapped_av_bsr", st);
-    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, nrb, n_hg);
+    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, nrb, n_hg, hpg);
   }
   return hipGetLastError();
 }

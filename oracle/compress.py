@@ -131,6 +131,39 @@ def compress_head(q, k, scale, bias, tau, block=BLOCK):
     return dict(masses=masses, kept=kept, margins=margins, blocks=blocks, m=m, l=l, n=n, R=R)
 
 
+def compress_block_row(q, k, scale, bias, r, tau, block=BLOCK):
+    """Both phases for block-row ``r`` of one head and one sequence, for sampled
+    checks of long sequences: the map rows of the block-row are the exact causal
+    softmax of those queries against keys ``0 .. 64 r + 63`` (so the same rows as
+    ``compress_head``'s map, without forming the rest of it).
+
+    Returns dict with ``masses`` [r + 1], ``kept`` (ascending columns), ``margin``,
+    ``blocks`` (float64 bf16-rounded ``[k, 64, 64]``, zero above the diagonal and
+    past the sequence) and the row statistics ``m``, ``l`` of the block-row's
+    queries (natural units).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    n = q.shape[0]
+    i0, i1 = r * block, min((r + 1) * block, n)
+    kend = i1  # keys 0 .. i1 - 1 are visible to some query of the block-row
+    A = causal_map(q[i0:i1], k[:kend], scale, bias)  # [i1 - i0, kend]; bottom-right alignment
+    rows = np.zeros((block, (r + 1) * block))
+    rows[: i1 - i0, :kend] = A
+    masses = rows.reshape(block, r + 1, block).sum(axis=(0, 2))
+    cols = select_blocks(masses, tau)
+    margin = selection_margin(masses, tau)
+    blocks = (round_bf16(np.stack([rows[:, c * block:(c + 1) * block] for c in cols]))
+              if cols else np.zeros((0, block, block)))
+    s = float(scale) * (q[i0:i1] @ k[:kend].T)
+    s[:, 0] += float(bias)
+    vis = np.arange(kend)[None, :] <= np.arange(i0, i1)[:, None]
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    l = np.exp(s - m[:, None]).sum(axis=1)
+    return dict(masses=masses, kept=cols, margin=margin, blocks=blocks, m=m, l=l)
+
+
 def block_compress(q, k, scale, bias, cu, tau, used=None, block=BLOCK, heads=None,
                    keep_values=True, cu_k=None):
     """Whole compression over heads and packed sequences, in the library's layout.

@@ -138,7 +138,9 @@ def synthetic_bsr(seed: int, n_heads: int, lengths, keep_frac: float = 0.93, blo
     (roughly the size of causal attention probabilities), zero above the diagonal
     and outside the sequence. Layout matches the library's block-sparse format:
     ``row_ptr[H * R_tot + 1]``, ``col_idx[nnz]``, ``vals[nnz, 64, 64]`` (uint16 bf16).
-    Stream order: [kept masks, values].
+    Stream order: [kept masks (one uniform per causal block, head-major, then
+    sequence, block-row, column), values (one 64 x 64 normal draw per kept block,
+    in storage order)].
     """
     ss = np.random.SeedSequence(seed)
     s_keep, s_val = ss.spawn(2)
@@ -146,38 +148,41 @@ def synthetic_bsr(seed: int, n_heads: int, lengths, keep_frac: float = 0.93, blo
     lengths = list(lengths)
     nblk = [(n + block - 1) // block for n in lengths]
     r_tot = sum(nblk)
-    counts = np.zeros(n_heads * r_tot, dtype=np.int64)
-    cols = []
-    g = 0
+    counts, cols, blk_r, blk_s = [], [], [], []
     for h in range(n_heads):
         for s, n in enumerate(lengths):
-            for r in range(nblk[s]):
-                keep = rk.uniform(size=r + 1) < keep_frac
-                keep[r] = True
-                c = np.nonzero(keep)[0].astype(np.int32)
-                cols.append(c)
-                counts[g] = len(c)
-                g += 1
+            R = nblk[s]
+            if R == 0:
+                continue
+            u = rk.uniform(size=R * (R + 1) // 2)
+            rr = np.repeat(np.arange(R), np.arange(1, R + 1))
+            cc = np.arange(R * (R + 1) // 2) - (rr * (rr + 1)) // 2
+            keep = (u < keep_frac) | (cc == rr)
+            counts.append(np.bincount(rr[keep], minlength=R))
+            cols.append(cc[keep].astype(np.int32))
+            blk_r.append(rr[keep])
+            blk_s.append(np.full(int(keep.sum()), s))
+    counts = np.concatenate(counts) if counts else np.zeros(0, np.int64)
+    assert counts.size == n_heads * r_tot
     row_ptr = np.zeros(n_heads * r_tot + 1, dtype=np.int64)
     row_ptr[1:] = np.cumsum(counts)
     nnz = int(row_ptr[-1])
     col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
+    blk_r = np.concatenate(blk_r) if blk_r else np.zeros(0, np.int64)
+    blk_s = np.concatenate(blk_s) if blk_s else np.zeros(0, np.int64)
+    lens = np.asarray(lengths, dtype=np.int64)
     vals = np.zeros((nnz, block, block), dtype=np.uint16)
-    g = 0
-    idx = 0
-    ii = np.arange(block)[:, None]
-    jj = np.arange(block)[None, :]
-    for h in range(n_heads):
-        for s, n in enumerate(lengths):
-            for r in range(nblk[s]):
-                for c in cols[g]:
-                    rows = r * block + ii
-                    colsj = c * block + jj
-                    ok = (colsj <= rows) & (rows < n) & (colsj < n)
-                    x = np.abs(rv.standard_normal(size=(block, block), dtype=np.float32)) / (rows + 1.0)
-                    vals[idx] = bf16_from_f32(np.where(ok, x, 0.0).astype(np.float32))
-                    idx += 1
-                g += 1
+    ii = np.arange(block)[None, :, None]
+    jj = np.arange(block)[None, None, :]
+    chunk = 4096
+    for a in range(0, nnz, chunk):
+        b = min(nnz, a + chunk)
+        rows = blk_r[a:b, None, None] * block + ii
+        colsj = col_idx[a:b, None, None].astype(np.int64) * block + jj
+        nn = lens[blk_s[a:b]][:, None, None]
+        ok = (colsj <= rows) & (rows < nn) & (colsj < nn)
+        x = np.abs(rv.standard_normal(size=(b - a, block, block), dtype=np.float32)) / (rows + 1.0)
+        vals[a:b] = bf16_from_f32(np.where(ok, x, 0.0).astype(np.float32))
     return dict(row_ptr=row_ptr.astype(np.int32), col_idx=col_idx, vals=vals, nnz=nnz,
                 lengths=lengths, n_heads=n_heads, block=block)
 

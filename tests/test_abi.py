@@ -1,0 +1,90 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/cma.h declares, and its host-only calls and argument validation work
+without touching a device (no compute call is made here)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cma.h")
+LIB = os.path.join(ROOT, "cross_model_attention_causal_amd", "libcma.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)  # drop comments
+    return sorted(set(re.findall(r"\b(cma_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from cross_model_attention_causal_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15, names
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_host_helpers(lib):
+    assert lib.cma_version() == 100
+    lib.cma_maps_elems.restype = ctypes.c_int64
+    lib.cma_maps_elems.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lq = np.array([5, 64, 3], dtype=np.int32)
+    lk = np.array([5, 70, 3], dtype=np.int32)
+    packed = lib.cma_maps_elems(3, lq.ctypes.data, lk.ctypes.data, 1)
+    dense = lib.cma_maps_elems(3, lq.ctypes.data, lk.ctypes.data, 0)
+    want_packed = sum(oracle.packed_size(int(a), int(b)) for a, b in zip(lq, lk))
+    assert packed == want_packed
+    assert dense == int(np.sum(lq.astype(np.int64) * lk))
+    bad = np.array([4], dtype=np.int32)  # nq > nk
+    assert lib.cma_maps_elems(1, np.array([5], dtype=np.int32).ctypes.data, bad.ctypes.data, 1) == -1
+    lib.cma_bsr_max_blocks.restype = ctypes.c_int64
+    lib.cma_bsr_max_blocks.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lens = np.array([200, 64, 5], dtype=np.int32)
+    R = (lens + 63) // 64
+    assert lib.cma_bsr_max_blocks(3, 3, lens.ctypes.data) == 3 * int(np.sum(R * (R + 1) // 2))
+
+
+@pytest.mark.parametrize("n_layers,ratio", [(80, 0.5), (24, 0.5), (40, 0.25), (10, 1.0), (80, 0.0)])
+def test_mapped_layers_match_oracle(lib, n_layers, ratio):
+    lib.cma_mapped_layers.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
+    out = np.zeros(n_layers, dtype=np.int32)
+    k = lib.cma_mapped_layers(n_layers, ratio, out.ctypes.data, n_layers)
+    assert list(out[:k]) == list(oracle.mapped_layers(n_layers, ratio))
+
+
+def test_validation_errors_without_device(lib):
+    """Bad arguments are rejected before any device work, with a message."""
+    lib.cma_last_error.restype = ctypes.c_char_p
+    # NULL varlen
+    rc = lib.cma_attn_maps(None, None, 1, 1, 128, None, None, None, None, 1, 1, ctypes.c_int64(0), None)
+    assert rc == -1
+    assert lib.cma_last_error()
+    # head map with zero problems is a no-op; negative sizes are rejected
+    rc = lib.cma_head_map_cosine(None, None, 1, -1, 1, 1, ctypes.c_int64(1), ctypes.c_int64(0), ctypes.c_int64(0),
+                                 ctypes.c_int64(0), ctypes.c_int64(0), None, None, None, None, ctypes.c_size_t(0),
+                                 None)
+    assert rc < 0
+    lib.cma_mapped_layers.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
+    assert lib.cma_mapped_layers(-1, 0.5, None, 0) == -1
+
+
+def test_golden_layer_order(lib):
+    """The 80-layer, 50% mapping order the IAM notes give (fixture with citation)."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "iam_mapped_layers.json")))
+    lib.cma_mapped_layers.argtypes = [ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_int32]
+    out = np.zeros(g["n_layers"], dtype=np.int32)
+    k = lib.cma_mapped_layers(g["n_layers"], g["ratio"], out.ctypes.data, g["n_layers"])
+    assert list(out[:k]) == g["layers"]

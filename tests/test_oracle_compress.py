@@ -145,3 +145,40 @@ def test_block_compress_layout_varlen():
                 g += 1
             off += Rs[s] * (Rs[s] + 1) // 2
             assert np.array_equal(out["row_stats"][h, cu[s]:cu[s + 1], 0], single["m"])
+
+
+@pytest.mark.parametrize("n,tau", [(200, 0.9), (256, 0.95), (130, 1.0)])
+def test_block_row_matches_whole_head(n, tau):
+    """The per-block-row oracle (used for sampled checks of long sequences) gives
+    exactly the whole-head oracle's masses, kept set, margin, blocks and row
+    statistics for every block-row, including a ragged last one."""
+    rng = np.random.default_rng(11 + n)
+    q = rng.standard_normal((n, 16))
+    k = rng.standard_normal((n, 16))
+    scale, bias = 0.6, 3.0
+    whole = oracle.compress_head(q, k, scale, bias, tau)
+    for r in range(whole["R"]):
+        one = oracle.compress_block_row(q, k, scale, bias, r, tau)
+        np.testing.assert_allclose(one["masses"], whole["masses"][r, : r + 1], rtol=1e-12, atol=1e-15)
+        assert one["kept"] == whole["kept"][r]
+        assert one["margin"] == pytest.approx(whole["margins"][r], rel=1e-9, abs=1e-12)
+        np.testing.assert_array_equal(one["blocks"], whole["blocks"][r])
+        rows = slice(64 * r, min(64 * (r + 1), n))
+        np.testing.assert_allclose(one["m"], whole["m"][rows], rtol=1e-12)
+        np.testing.assert_allclose(one["l"], whole["l"][rows], rtol=1e-12)
+
+
+def test_block_row_uniform_closed_form():
+    """Scale 0, no sink: every visible entry of row i is 1/(i+1), so an
+    off-diagonal block of block-row r has mass 64 * sum_{i in r} 1/(i+1) and the
+    diagonal block sum_{i in r} (i - 64r + 1)/(i+1)."""
+    n, r = 320, 3
+    q = np.ones((n, 8))
+    k = np.ones((n, 8))
+    one = oracle.compress_block_row(q, k, 0.0, 0.0, r, 1.0)
+    i = np.arange(64 * r, 64 * (r + 1))
+    off = 64 * np.sum(1.0 / (i + 1))
+    diag = np.sum((i - 64 * r + 1) / (i + 1))
+    np.testing.assert_allclose(one["masses"][:r], off, rtol=1e-13)
+    np.testing.assert_allclose(one["masses"][r], diag, rtol=1e-13)
+    assert one["kept"] == list(range(r + 1))
