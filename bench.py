@@ -215,14 +215,19 @@ def main():
     # dominant kernel among those with a roofline
     dom = max((k for k in stage if "bound" in stage[k]), key=lambda k: stage[k]["ms"] * stage[k]["launches"])
     d = stage[dom]
+    # HBM bytes per launch of the dominant kernel from the committed counter run
+    # (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size); null when
+    # the kernel's source or the shared headers changed since that run.
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tpath):
         try:
-            tj = json.load(open(tpath))
-            src = open(os.path.join(ROOT, "cross_model_attention_causal_amd", "csrc", tj[dom]["source"]), "rb").read()
-            if hashlib.sha256(src).hexdigest() == tj[dom]["sha256"]:
-                traffic = tj[dom]["bytes_per_launch"]
+            t = json.load(open(tpath))[dom]
+            h = hashlib.sha256()
+            for f in [t["source"]] + list(t.get("headers", [])):
+                h.update(open(os.path.join(ROOT, "cross_model_attention_causal_amd", "csrc", f), "rb").read())
+            if h.hexdigest() == t["sha256"]:
+                traffic = t["bytes_per_launch"]
         except (KeyError, OSError, ValueError):
             traffic = None
     roofline = dict(kernel=dom, bound=d["bound"], achieved=d["achieved"], peak=d["peak"], unit=d["unit"],
