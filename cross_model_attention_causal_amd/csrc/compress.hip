@@ -364,12 +364,11 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(fmaf(acc[kt][v], scale_l2, -lse));
         } else {
-          float t[32];
-          logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+          logits_inplace(acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(t[16 * kt + v] - lse);
+            for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(acc[kt][v] - lse);
         }
         if (!valid) {
 #pragma unroll

@@ -138,19 +138,18 @@ template <int D, int FH>
 __device__ __forceinline__ void kstage_mma(f32x16 acc[2], const uint8_t* blk, const QOperand<D>& qop) {
   const int lane = threadIdx.x & 63;
   const int hl = lane >> 5;
-  u32x4 x[4][2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 x[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int m = 32 * kt + (lane & 31);
       const int ch = 2 * ks + hl;
-      x[ks][kt] = *reinterpret_cast<const u32x4*>(blk + m * 128 + 16 * (ch ^ ((m >> 1) & 7)));
+      x[kt] = *reinterpret_cast<const u32x4*>(blk + m * 128 + 16 * (ch ^ ((m >> 1) & 7)));
     }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32(as_bf16x8(x[ks][kt]), qop.v[4 * FH + ks], acc[kt]);
+    for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32(as_bf16x8(x[kt]), qop.v[4 * FH + ks], acc[kt]);
+  }
 }
 
 // Key index of element (kt, v) of a score block.
@@ -171,6 +170,20 @@ __device__ __forceinline__ void logits_block(float t[32], const f32x16 acc[2], i
       float x = acc[kt][v] * scale_l2;
       if (key == 0) x += bias_l2;
       t[kt * 16 + v] = (key <= last) ? x : -INFINITY;
+    }
+  }
+}
+
+// As logits_block, in place in the accumulators.
+__device__ __forceinline__ void logits_inplace(f32x16 acc[2], int key0, int last, float scale_l2, float bias_l2) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = tile_key(key0, kt, v);
+      float x = acc[kt][v] * scale_l2;
+      if (key == 0) x += bias_l2;
+      acc[kt][v] = (key <= last) ? x : -INFINITY;
     }
   }
 }
