@@ -101,13 +101,15 @@ __device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* 
 }
 
 // Block statistics and selection for one (head, sequence, block-row).
-// Dynamic LDS: two K stages, then LP[64][R] = log2 of each (query, block)
+// Dynamic LDS: two K stages, then LP[64][R + 1] = log2 of each (query, block)
 // partial sum in absolute terms (running max + log2 of the partial), so that
 // mass_c = sum_i 2^(LP[i][c] - lse_i) once the row's lse is known.
 template <int D>
 __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn[];
-  const int R = a.nrb_max;
+  // row stride of LP: odd, so the 32 query rows written for one block fall in
+  // distinct LDS banks
+  const int LPS = a.nrb_max + 1;
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   float* LP = dyn + 2 * (kStageBytes / 4);
   __shared__ float sm[4][64], sl[4][64];
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
           logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
           part = online_update(t, m, l);
         }
-        if (lane < 32) LP[iloc * R + c] = m + log2f_fast(part);
+        if (lane < 32) LP[iloc * LPS + c] = m + log2f_fast(part);
       });
   if (lane < 32) {
     sm[kp][iloc] = m;
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   const int nb = r + 1;
   for (int c = tid; c < nb; c += 512) {
     float x = 0.0f;
-    for (int q = 0; q < nrows; ++q) x += exp2f_fast(LP[q * R + c] - lse_s[q]);
+    for (int q = 0; q < nrows; ++q) x += exp2f_fast(LP[q * LPS + c] - lse_s[q]);
     mass[c] = x;
   }
   __syncthreads();
@@ -421,7 +423,7 @@ size_t compress_ws_bytes(int32_t n_heads, int32_t n_block_rows, int64_t total_q)
 template <int D>
 static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   dim3 grid(pair_grid(a.nrb_max, a.vl.n_seqs, a.n_heads));
-  const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * a.nrb_max * sizeof(float);
+  const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * (a.nrb_max + 1) * sizeof(float);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

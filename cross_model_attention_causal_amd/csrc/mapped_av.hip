@@ -225,13 +225,15 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     }
   };
   // Copy panel jq (16 keys) of the column into stage buffer b: each sender's 1 KB
-  // piece goes straight to LDS, 16 B per lane.
+  // piece goes straight to LDS, 16 B per lane (lane L fills row L / 2, half L % 2).
+  // Senders j with bit 3 set store row r at row position r ^ 1: the transposing
+  // reads of senders j and j + 8 then fall in different LDS banks.
   auto issue_stage = [&](const SendSrc& ss, int jq, int b) {
     uint16_t* dst0 = &sbuf[b * kStageElems];
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u) {
-      const int j = wave + kWaves * u;
-      __builtin_amdgcn_global_load_lds(ss.p[u] + jq * ss.step[u] + 8 * lane,
+      const int j = wave + kWaves * u;  // (j >> 3) & 1 == u & 1
+      __builtin_amdgcn_global_load_lds(ss.p[u] + jq * ss.step[u] + 8 * (lane ^ (2 * (u & 1))),
                                        (__attribute__((address_space(3))) void*)(dst0 + j * kSendStride), 16, 0, 0);
     }
   };
@@ -241,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   // in-flight direct-to-LDS copies of the next panel write, and would otherwise
   // wait for them before any read.
   auto mix_panel = [&](int jq, int b) {
-    const uint16_t* b0 = &sbuf[b * kStageElems] + (8 * q + e4) * kSendStride + wave * kKeysPerStep + 4 * cc4;
+    // senders 8q + e4 (+ 4): row wave + 8u sits at row position (wave ^ (q & 1)) + 8u
+    const uint16_t* b0 = &sbuf[b * kStageElems] + (8 * q + e4) * kSendStride + (wave ^ (q & 1)) * kKeysPerStep + 4 * cc4;
     const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)b0);
     // offsets: rows wave + 8u (u = 0..3) are 256 B apart; senders 8q + e4 + 4
     // (the second k-half) are 4 * kSendStride * 2 = 4352 B further
@@ -261,23 +264,32 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
         : "=v"(tr[0]), "=v"(tr[1]), "=v"(tr[2]), "=v"(tr[3]), "=v"(tr[4]), "=v"(tr[5]), "=v"(tr[6]), "=v"(tr[7])
         : "v"(a0)
         : "memory");
-    // The mixed values go to bbuf with stores written out in asm too (the
-    // compiler would otherwise also wait for the in-flight copies before them);
-    // the barrier that publishes bbuf waits for them (lgkmcnt).
+    // Lane (p, q) holds heads 4q .. 4q + 3 at key p. Partner lanes p and p ^ 1
+    // swap half of their values (one DPP move) so that each writes two heads as
+    // whole dwords (keys p & ~1 and p | 1): the even lane heads 4q, 4q + 1, the
+    // odd lane heads 4q + 2, 4q + 3. Two lanes writing halves of one dword would
+    // conflict in the LDS banks. The stores are written out in asm too (the
+    // compiler would otherwise wait for the in-flight copies before them); the
+    // barrier that publishes bbuf waits for them (lgkmcnt).
+    const bool odd = p & 1;
     const uint32_t w0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)&bbuf[
-                            (4 * q) * kBHead + wave * kBRow + kKeysPerStep * jq + p]);
+                            (4 * q + 2 * odd) * kBHead + wave * kBRow + kKeysPerStep * jq + (p & ~1)]);
 #pragma unroll
     for (int u = 0; u < kRowsPerWg / kWaves; ++u) {
       const u32x4 bv = {tr[2 * u][0], tr[2 * u][1], tr[2 * u + 1][0], tr[2 * u + 1][1]};
       f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
       d1 = mfma16(mhi, as_bf16x8(bv), d1);
       d1 = mfma16(mlo, as_bf16x8(bv), d1);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        // element ((4q + v) * kBHead + (wave + 8u) * kBRow + 16 jq + p)
-        const uint32_t addr = w0 + 2 * (v * kBHead + kWaves * u * kBRow);
-        asm volatile("ds_write_b16 %0, %1" ::"v"(addr), "v"((uint32_t)f2bf(d1[v])) : "memory");
-      }
+      const uint32_t P = pack2bf(d1[0], d1[1]), Q = pack2bf(d1[2], d1[3]);
+      // quad_perm [1, 0, 3, 2]: the value of lane p ^ 1
+      const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? P : Q), 0xB1, 0xF, 0xF, false);
+      const uint32_t ev = odd ? recv : P, od = odd ? Q : recv;  // even-key and odd-key values
+      const uint32_t first = (ev & 0xffffu) | (od << 16), second = (ev >> 16) | (od & 0xffff0000u);
+      // elements ((4q + 2 odd + {0, 1}) * kBHead + (wave + 8u) * kBRow + 16 jq + (p & ~1))
+      const uint32_t addr = w0 + 2 * (kWaves * u * kBRow);
+      asm volatile("ds_write_b32 %0, %1\n"
+                   "ds_write_b32 %0, %2 offset:%3" ::"v"(addr), "v"(first), "v"(second), "i"(2 * kBHead)
+                   : "memory");
     }
   };
 
