@@ -193,15 +193,34 @@ class Varlen:
         return int(r)
 
 
+def _need(t, name, n):
+    """The C ABI takes raw pointers: check here that ``t`` holds at least ``n`` elements."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
+def _check_rows(vl, Tq, Tk):
+    """Every sequence's used rows must lie inside the packed tensors."""
+    if vl.n_seqs and (int(np.max(vl.cu_q_host[:-1] + vl.lens_q)) > Tq or
+                      int(np.max(vl.cu_k_host[:-1] + vl.lens_k)) > Tk):
+        raise ValueError("a sequence's rows run past the end of the packed q/k/v tensors")
+
+
 def attn_maps(q, k, scale, bias, vl: Varlen, layout=PACKED, out_dtype=None, out=None):
     """Causal maps of every (head, sequence); returns ``[H, head_stride]`` (see cma.h)."""
     torch = _torch()
     lib = load_library()
     H, Tq, d = q.shape
+    if k.dim() != 3 or k.shape[0] < H or k.shape[2] != d:
+        raise ValueError(f"k must be [>= {H}, Tk, {d}] (got {tuple(k.shape)})")
+    _need(scale, "scale", H)
+    _need(bias, "bias", H)
+    _check_rows(vl, Tq, k.shape[1])
     out_dtype = out_dtype or torch.bfloat16
     stride = vl.maps_elems(layout)
     if out is None:
         out = torch.empty((H, stride), dtype=out_dtype, device=q.device)
+    _need(out, "out", H * stride)
     cvl = vl.c(Tq, k.shape[1])
     _check(lib.cma_attn_maps(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dt(q), H, d, ctypes.byref(cvl),
                              _dev_ptr(scale, "scale"), _dev_ptr(bias, "bias"), _dev_ptr(out, "out"),
@@ -217,6 +236,9 @@ def head_map_cosine(recv, send, n_batch, n_recv, n_send, length, recv_hstride, r
     lib = load_library()
     dev = recv.device
     dt = _dt(recv)
+    if n_batch > 0 and n_recv > 0 and n_send > 0:
+        _need(recv, "recv", (n_recv - 1) * recv_hstride + (n_batch - 1) * recv_bstride + length)
+        _need(send, "send", (n_send - 1) * send_hstride + (n_batch - 1) * send_bstride + length)
     ws_bytes = lib.cma_head_map_cosine_workspace(n_batch, n_recv, n_send, length, dt)
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     cos = torch.empty((n_batch, n_recv, n_send), dtype=torch.float32, device=dev) if want_cos else None
@@ -257,7 +279,16 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
     lib = load_library()
     H, Tq, d = q.shape
     dev = q.device
+    if k.dim() != 3 or k.shape[0] < H or k.shape[2] != d:
+        raise ValueError(f"k must be [>= {H}, Tk, {d}] (got {tuple(k.shape)})")
+    _need(scale, "scale", H)
+    _need(bias, "bias", H)
+    _check_rows(vl, Tq, k.shape[1])
     nbr = vl.n_block_rows
+    if bsr is not None:
+        _need(bsr["row_ptr"], "row_ptr", H * nbr + 1)
+        _need(bsr["col_idx"], "col_idx", bsr["capacity"])
+        _need(bsr["vals"], "vals", bsr["capacity"] * BLOCK * BLOCK)
     if bsr is None:
         if capacity is None:
             capacity = bsr_max_blocks(H, vl.lens_q)
@@ -303,12 +334,19 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         Tk = k_rows
     else:
         H, Tk, d = v.shape
+    if H < n_recv:
+        raise ValueError(f"v holds {H} heads, n_recv is {n_recv}")
     out_dtype = out_dtype or v.dtype
     Tq = q_rows if q_rows is not None else Tk
+    _check_rows(vl, Tq, Tk)
     if out is None:
         out = torch.empty((n_recv, Tq, d), dtype=out_dtype, device=dev)
+    _need(out, "out", n_recv * Tq * d)
     s = _CMapsSrc()
     if isinstance(src, dict):
+        if v_layout == V_TILED:
+            _need(v, "v", n_recv * src["n_block_rows"] * BLOCK * 128)
+        _need(src["row_ptr"], "row_ptr", n_send * src["n_block_rows"] + 1)
         s.kind = SRC_BSR
         s.row_ptr = _dev_ptr(src["row_ptr"], "row_ptr")
         s.col_idx = _dev_ptr(src["col_idx"], "col_idx")
@@ -316,6 +354,8 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         s.n_block_rows = src["n_block_rows"]
     else:
         _, maps, layout = src
+        if maps.dim() != 2 or maps.shape[0] < n_send or maps.shape[1] < vl.maps_elems(layout):
+            raise ValueError(f"maps must be [>= {n_send}, >= {vl.maps_elems(layout)}] (got {tuple(maps.shape)})")
         s.kind = SRC_DENSE
         s.maps = _dev_ptr(maps, "maps")
         s.maps_dt = _dt(maps)
@@ -323,6 +363,7 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         s.head_stride = maps.shape[1]
     if M_seq_stride is None:
         M_seq_stride = 0 if M.shape[0] == 1 else n_recv * n_send
+    _need(M, "M", M_seq_stride * max(0, vl.n_seqs - 1) + n_recv * n_send)
     ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_recv, d, Tk, v_layout)
     ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
     cvl = vl.c(Tq, Tk)

@@ -88,3 +88,33 @@ def test_golden_layer_order(lib):
     out = np.zeros(g["n_layers"], dtype=np.int32)
     k = lib.cma_mapped_layers(g["n_layers"], g["ratio"], out.ctypes.data, g["n_layers"])
     assert list(out[:k]) == g["layers"]
+
+
+def test_binding_rejects_undersized_tensors():
+    """The binding checks tensor sizes before passing raw pointers (CPU tensors are
+    rejected too, but the size checks come first for the shapes tested here)."""
+    torch = pytest.importorskip("torch")
+    import cross_model_attention_causal_amd as cma
+    cma.load_library()
+
+    class VL:  # the host fields the checks read
+        n_seqs = 1
+        cu_q_host = np.array([0, 64])
+        cu_k_host = np.array([0, 64])
+        lens_q = np.array([64])
+        lens_k = np.array([64])
+        n_block_rows = 1
+
+        def maps_elems(self, layout):
+            return 64 * 65 // 2
+
+    q = torch.zeros(2, 64, 128)
+    with pytest.raises(ValueError):  # k has fewer heads than q
+        cma.attn_maps(q, torch.zeros(1, 64, 128), torch.zeros(2), None, VL())
+    with pytest.raises(ValueError):  # rows past the end of k
+        cma.attn_maps(q, torch.zeros(2, 32, 128), torch.zeros(2), None, VL())
+    with pytest.raises(ValueError):  # one scale for two heads
+        cma.attn_maps(q, torch.zeros(2, 64, 128), torch.zeros(1), None, VL())
+    with pytest.raises(ValueError):  # V with fewer heads than receivers
+        cma.mapped_av(("dense", torch.zeros(4, 2080), cma.PACKED), 4, torch.zeros(1, 3, 4), 3,
+                      torch.zeros(2, 64, 128), VL())
