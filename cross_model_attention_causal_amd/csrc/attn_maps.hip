@@ -145,6 +145,95 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   }
 }
 
+// Single query rows (decode: one new token per sequence), bf16 inputs. One
+// workgroup of 1024 threads per (sequence, head); the dot products are a GEMV, so
+// they run on VALU: D/8 lanes share one key row (one 16-byte load each, a wave
+// reads whole key rows), reduce across those lanes, and the logit goes to LDS.
+// Four keys per group are in flight at a time (256 key rows per workgroup). Max,
+// sum and the normalised row are then formed from LDS and written with coalesced
+// stores. K is read once.
+constexpr int kRowsThreads = 1024;
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kRowsThreads) void k_attn_rows(AttnMapsArgs a) {
+  extern __shared__ float lg[];  // logits (log2 units) of the row's keys
+  constexpr int NW = kRowsThreads / 64;
+  __shared__ float red[NW];
+  constexpr int LPK = D / 8, KPP = kRowsThreads / LPK;  // lanes per key, keys per pass
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  // rows longer than the LDS sized from max_seqlen_k are not computed (the
+  // lengths must not exceed the maxima the caller passes)
+  if (!seq_ok(a.vl, s, nq, nk) || nq != 1 || nk > a.rows_cap) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l = tid % LPK, g = tid / LPK;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s]) * D;
+  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
+  const float scale_l2 = a.scale[h] * kLog2e;
+  const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+  float qv[8];
+  {
+    const u32x4 w = ldg16(qrow + 8 * l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = __uint_as_float(w[e] << 16);
+      qv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  auto dot = [&](const u32x4& w) {
+    float d = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d = fmaf(qv[2 * e], __uint_as_float(w[e] << 16), d);
+      d = fmaf(qv[2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), d);
+    }
+#pragma unroll
+    for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off, 64);
+    return d;
+  };
+  float mx = -INFINITY;
+  int j = g;
+  for (; j + 3 * KPP < nk; j += 4 * KPP) {
+    u32x4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = ldg16(kseq + (int64_t)(j + u * KPP) * D + 8 * l);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = j + u * KPP;
+      const float t = dot(w[u]) * scale_l2 + (key == 0 ? bias_l2 : 0.0f);
+      mx = fmaxf(mx, t);
+      if (l == 0) lg[key] = t;
+    }
+  }
+  for (; j < nk; j += KPP) {
+    const float t = dot(ldg16(kseq + (int64_t)j * D + 8 * l)) * scale_l2 + (j == 0 ? bias_l2 : 0.0f);
+    mx = fmaxf(mx, t);
+    if (l == 0) lg[j] = t;
+  }
+  // workgroup max, then sum of 2^(t - max), in a fixed order
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
+  float sum = 0.0f;
+  for (int x = tid; x < nk; x += kRowsThreads) sum += exp2f_fast(lg[x] - M);
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  __syncthreads();
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  float L = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) L += red[w];
+  const float lse = M + log2f_fast(L);
+  const int64_t base = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, a.packed);
+  for (int x = tid; x < nk; x += kRowsThreads) {
+    const float p = exp2f_fast(lg[x] - lse);
+    if (OUT_BF16) reinterpret_cast<uint16_t*>(a.maps)[base + x] = f2bf(p);
+    else reinterpret_cast<float*>(a.maps)[base + x] = p;
+  }
+}
+
 // fp32 inputs: one workgroup per (query row, sequence, head), scores on VALU.
 // Used for small fp32 problems; three passes over the keys (max, sum, write).
 template <bool PACKED>
@@ -206,8 +295,28 @@ static hipError_t launch_bf16(const AttnMapsArgs& a, dim3 grid, hipStream_t st) 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, hipStream_t st) {
+constexpr int kRowsMaxKeys = 36 * 1024;  // keys of a single-row sequence held in LDS
+
+template <int D>
+static hipError_t launch_rows(AttnMapsArgs a, int max_k, hipStream_t st) {
+  a.rows_cap = max_k;
+  const size_t lds = (size_t)max_k * sizeof(float);
+  const void* f = a.out_bf16 ? reinterpret_cast<const void*>(&k_attn_rows<D, true>)
+                             : reinterpret_cast<const void*>(&k_attn_rows<D, false>);
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(a.vl.n_seqs, a.n_heads);
+  if (a.out_bf16) { KernelTimer kt_("k_attn_rows", st); hipLaunchKernelGGL((k_attn_rows<D, true>), grid, dim3(kRowsThreads), lds, st, a); }
+  else { KernelTimer kt_("k_attn_rows", st); hipLaunchKernelGGL((k_attn_rows<D, false>), grid, dim3(kRowsThreads), lds, st, a); }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, int max_k, hipStream_t st) {
   if (a.n_heads == 0 || a.vl.n_seqs == 0 || max_q == 0) return hipSuccess;
+  if (a.in_bf16 && max_q == 1 && max_k >= 1 && max_k <= kRowsMaxKeys) {
+    // every sequence has at most one query row (decode)
+    return d == 64 ? launch_rows<64>(a, max_k, st) : launch_rows<128>(a, max_k, st);
+  }
   if (a.in_bf16) {
     dim3 grid((max_q + 63) / 64, a.vl.n_seqs, a.n_heads);
     return d == 64 ? launch_bf16<64>(a, grid, st) : launch_bf16<128>(a, grid, st);

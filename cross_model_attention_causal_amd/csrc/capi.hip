@@ -220,7 +220,7 @@ int cma_attn_maps(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads
   a.in_bf16 = in_dt == CMA_BF16;
   a.out_bf16 = out_dt == CMA_BF16;
   a.packed = layout == CMA_MAP_PACKED;
-  return hip_status(launch_attn_maps(a, d, vl->max_seqlen_q, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_attn_maps(a, d, vl->max_seqlen_q, vl->max_seqlen_k, static_cast<hipStream_t>(stream)),
                     "attn_maps launch");
 }
 

@@ -25,8 +25,9 @@ struct AttnMapsArgs {
   int64_t head_stride;
   int32_t n_heads;
   bool in_bf16, out_bf16, packed;
+  int32_t rows_cap;  // single-row path: keys its LDS holds (set by the launcher)
 };
-hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, hipStream_t st);
+hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, int max_k, hipStream_t st);
 
 struct CosineArgs {
   const void* recv;

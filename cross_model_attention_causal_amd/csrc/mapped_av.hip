@@ -430,13 +430,16 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, int64_t lim, float
   }
 }
 
-template <int D, bool KEY_MAJOR, typename VT>
-__global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
+// NT threads: 1024 for token-major V (64 key rows in flight per pass, 8 passes
+// unrolled, so a single row streams V with enough loads outstanding), 256 for
+// key-major V.
+template <int D, bool KEY_MAJOR, typename VT, int NT>
+__global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
   extern __shared__ float bj[];  // mixed row window [kDenseWin]
   __shared__ int nzi[64];
   __shared__ float nzw[64];
   __shared__ int nnzm;
-  __shared__ float red[256 / (D / 8)][D];  // one row per key slot (token-major)
+  __shared__ float red[KEY_MAJOR ? 1 : NT / (D / 8)][D];  // one row per key slot (token-major)
   const int i = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
@@ -457,21 +460,29 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
   const int64_t row_off = map_seq_off(a.vl, s, a.packed) + map_row_off(i, nq, nk, a.packed);
   const int64_t k0 = a.vl.cu_k[s];
   constexpr int kChunks = D / 8;          // 8-feature chunks per key (token-major)
-  constexpr int kSlots = 256 / kChunks;   // keys per pass (token-major)
+  constexpr int kSlots = NT / kChunks;    // keys per pass (token-major)
   float accv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float acck[D / 16];
 #pragma unroll
   for (int u = 0; u < D / 16; ++u) acck[u] = 0.0f;
   for (int w0 = 0; w0 <= last; w0 += kDenseWin) {
     const int wlen = min(kDenseWin, last + 1 - w0);
-    for (int j = tid; j < wlen; j += 256) {
-      float b = 0.0f;
+    for (int j0 = tid; j0 < wlen; j0 += 4 * NT) {
+      // four window positions per thread at a time (independent loads)
+      float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int u = 0; u < nnzm; ++u) {
-        const int64_t idx = (int64_t)nzi[u] * a.head_stride + row_off + w0 + j;
-        b = fmaf(nzw[u], a.maps_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.maps)[idx])
-                                     : reinterpret_cast<const float*>(a.maps)[idx], b);
+        const int64_t base = (int64_t)nzi[u] * a.head_stride + row_off + w0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = j0 + NT * t;
+          if (j < wlen)
+            b[t] = fmaf(nzw[u], a.maps_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.maps)[base + j])
+                                            : reinterpret_cast<const float*>(a.maps)[base + j], b[t]);
+        }
       }
-      bj[j] = b;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (j0 + NT * t < wlen) bj[j0 + NT * t] = b[t];
     }
     __syncthreads();
     if constexpr (KEY_MAJOR) {
@@ -491,10 +502,24 @@ __global__ __launch_bounds__(256) void k_mapped_av_dense(MappedAvArgs a) {
         acck[rnd] += part;
       }
     } else {
+      // 8 independent 16-byte loads in flight per thread, then their products
       const int fc = tid % kChunks, ks = tid / kChunks;
-      for (int j = ks; j < wlen; j += kSlots) {
+      const int64_t vbase = ((int64_t)h * a.vl.total_k + k0 + w0) * D + 8 * fc;
+      int j = ks;
+      for (; j + 7 * kSlots < wlen; j += 8 * kSlots) {
+        float v[8][8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ld8<VT>(a.v, vbase + (int64_t)(j + u * kSlots) * D, 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float b = bj[j + u * kSlots];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) accv[e] = fmaf(b, v[u][e], accv[e]);
+        }
+      }
+      for (; j < wlen; j += kSlots) {
         float v[8];
-        ld8<VT>(a.v, ((int64_t)h * a.vl.total_k + k0 + w0 + j) * D + 8 * fc, 8, v);
+        ld8<VT>(a.v, vbase + (int64_t)j * D, 8, v);
         const float b = bj[j];
 #pragma unroll
         for (int e = 0; e < 8; ++e) accv[e] = fmaf(b, v[e], accv[e]);
@@ -539,13 +564,14 @@ __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, fl
 
 template <int D, bool KM>
 static void dense_launch(const MappedAvArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int NT = KM ? 256 : 1024;
   const size_t lds = kDenseWin * sizeof(float);
   if (a.v_bf16) {
     KernelTimer kt_("k_mapped_av_dense", st);
-    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t>), grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a);
   } else {
     KernelTimer kt_("k_mapped_av_dense", st);
-    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float>), grid, dim3(256), lds, st, a);
+    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a);
   }
 }
 

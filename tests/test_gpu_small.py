@@ -120,6 +120,29 @@ def test_attn_maps_decode_rows(cma):
             assert rel_l2(got[h], oracle.round_f32(ref)) <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_attn_maps_single_rows(cma, d, out_bf16):
+    """One query per sequence (decode): the single-row kernel, key counts from 1
+    (only the sink key) to several thousand, both layouts."""
+    lq, lk = [1, 1, 1, 1, 1], [1, 513, 64, 2001, 130]
+    say(f"attn_maps single rows d={d} out_bf16={out_bf16} lk={lk}")
+    x = synth.attention_inputs(17, 3, lq, d=d, k_lengths=lk)
+    vl = cma.Varlen(x["cu_q"], x["cu_k"])
+    om = oracle.attn_maps(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], x["cu_k"])
+    for lay in (cma.PACKED, cma.DENSE):
+        maps = cma.attn_maps(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_f32(x["scale"]), dev_f32(x["bias"]),
+                             vl, layout=lay, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+        torch.cuda.synchronize()
+        got = host64(maps)
+        for h in range(3):
+            ref = np.concatenate([A.ravel() for A in om[h]])
+            if out_bf16:
+                assert rel_l2(got[h], oracle.round_bf16(ref)) <= 1e-2
+            else:
+                assert rel_l2(got[h], oracle.round_f32(ref)) <= 1e-5
+
+
 # ------------------------------------------------------------------ cosine bf16
 def test_head_map_cosine_bf16(cma):
     n = 200
