@@ -1,26 +1,26 @@
 // Fused mapped attention x V (MapFlow, approach and storage-and-execution
 // sections; IAM Method 4 for decode rows):  O_h = (sum_j M[h, j] A_j) V_h.
 //
-// Block-sparse source (k_mapped_av_bsr). A workgroup (16 waves) owns 32 query
-// rows of one block-row and 16 receiver heads (one per wave). It first builds, in
-// LDS, the table block-column -> kept block of every sender (the union of their
-// kept columns), then walks the key axis in steps of 16 keys with a two-stage
-// software pipeline:
-//   - the 32 senders' 32 x 16 sub-blocks of the NEXT step (one contiguous 1 KB
-//     piece of a stored block's 16-column panel per sender) are loaded into
-//     registers while the current step computes, and written to the other half
-//     of a double-buffered LDS stage (zeros where a sender did not keep the
-//     block);
-//   - this step's V operands (16 keys x 128 features, from the key-major V)
-//     are loaded at the start of the step and consumed after the mixing;
-//   - mixing runs on the matrix cores: D1[h, pos] = sum_j M[h, j] A_j[pos] for
-//     16 positions is a 16x16x32 MFMA with M (split into bf16 high and low
-//     parts, so the mix is accurate to ~2^-16) as the A operand and the senders
-//     as the B operand, read with the transposing LDS load so that each lane
-//     gets 8 senders of one position; the mixed maps B_h go to LDS as bf16;
-//   - O += B_h V_h on 32x32x16 MFMAs, fp32 accumulators in registers.
-// The mixed map never leaves LDS. A token-major V is first copied key-major into
-// the workspace (k_transpose_v).
+// Block-sparse source (k_mapped_av_bsr). A workgroup (8 waves) owns 32 query
+// rows of one block-row and a group of at most 12 receiver heads. It first
+// lists, in LDS, the block columns that any sender kept (ascending) and, per
+// column and sender, which stored block holds it. It then walks the key axis in
+// 16-key panels (four per 64-key block column) with a three-stage software
+// pipeline; in step t
+//   - the 32 senders' 32 x 16 pieces of panel t + 3 (one contiguous 1 KB run of
+//     a stored block's 16-column panel per sender, or a zero page for a sender
+//     that did not keep the block) are copied straight to LDS;
+//   - the V operands of panel t + 2 are loaded into a ring of registers;
+//   - panel t + 1 is mixed on the matrix cores: D1[h, pos] = sum_j M[h, j]
+//     A_j[pos] for 16 positions is a 16x16x32 MFMA with M (split into bf16 high
+//     and low parts, so the mix is accurate to ~2^-16) as the A operand and the
+//     senders, read with the transposing LDS load so that each lane gets 8
+//     senders of one position, as the B operand; the mixed maps B_h go to LDS
+//     as bf16;
+//   - O += B_h V_h over panel t on 32x32x16 MFMAs, fp32 accumulators in
+//     registers; the group's (head, 32-feature tile) products are dealt evenly
+//     over the waves.
+// One barrier per step. The mixed map never leaves LDS.
 //
 // Dense source (k_mapped_av_dense): one workgroup per (query row, sequence,
 // receiver head) mixes the visible part of the row into LDS (only the nonzero
@@ -34,26 +34,26 @@ namespace cma {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kHeadsPerWg = 16;
+constexpr int kHeadsPerWg = 12;      // receiver heads per workgroup (M rows 12..15 of the mix are unused)
 constexpr int kRowsPerWg = 32;
-constexpr int kKeysPerStep = 16;
+constexpr int kKeysPerStep = 16;     // one panel
 constexpr int kSend = 32;            // senders per workgroup (n_send <= 32)
 constexpr int kSendStride = 544;     // bf16 per staged sender: 32 rows x 16 keys + 32 pad
 constexpr int kStageElems = kSend * kSendStride;
-constexpr int kStages = 2;           // sender stage ring: current panel + the next in flight
-constexpr int kBRow = 72;            // bf16 per mixed-map row (64 keys + 8 pad)
-constexpr int kBHead = 2312;         // bf16 per mixed-map head (32 rows x 72 + 8 pad)
+constexpr int kStages = 3;           // sender stage ring: panel t + 1 read, t + 2 and t + 3 in flight
+constexpr int kBH = 520;             // bf16 per head of a mixed panel: 32 rows x 16 keys + 8 pad
+constexpr int kBBuf = 16 * kBH;      // one mixed panel, 16 head slots (the mix's M rows)
 constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
 constexpr uint16_t kNoBlock = 0xffff;
 
 // V in the fused kernel's operand order ("tiled"): for head h and 64-key block b
 // of the block grid (sequence s's blocks start at its block-row offset, as in
-// the block-sparse maps), 16 KB hold, for feature tile dt (32 features) and
-// k-step ks, 64 lanes x 8 keys: lane L, element e is
-//   V[key 64c + 32(L / 32) + 8ks + e][feature 32dt + L % 32],
-// zero past the sequence end. One 16-byte load per lane then reads a whole
-// contiguous 1 KB MFMA operand.
-__device__ __forceinline__ int64_t vtile_off(int dt, int ks, int lane) { return ((dt * 4 + ks) * 64 + lane) * 8; }
+// the block-sparse maps), 16 KB hold, for panel ks (16 keys) and feature tile dt
+// (32 features), 64 lanes x 8 keys: lane L, element e is
+//   V[key 64c + 16ks + 8(L / 32) + e][feature 32dt + L % 32],
+// zero past the sequence end. One 16-byte load per lane reads a whole
+// contiguous 1 KB MFMA operand, and the four operands of a panel are adjacent.
+__device__ __forceinline__ int vtile_pos(int ks, int dt, int lane) { return ((ks * 4 + dt) * 64 + lane) * 8; }
 
 // grid (nrb_max, n_seqs, n_recv), 256 threads: one 64-key block of one head.
 template <bool KEY_MAJOR>
@@ -88,9 +88,9 @@ __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, 
   __syncthreads();
   uint16_t* dst = vtile + ((int64_t)h * n_block_rows + roff + c) * (64 * D);
   for (int x = threadIdx.x; x < 64 * D / 8; x += 256) {
-    // x = (dt * 4 + ks) * 64 + lane
-    const int lane = x & 63, dk = x >> 6, ks = dk & 3, dt = dk >> 2;
-    const int key0 = 32 * (lane >> 5) + 8 * ks, f = 32 * dt + (lane & 31);
+    // x = (ks * 4 + dt) * 64 + lane
+    const int lane = x & 63, kd = x >> 6, dt = kd & 3, ks = kd >> 2;
+    const int key0 = 16 * ks + 8 * (lane >> 5), f = 32 * dt + (lane & 31);
     uint32_t w[4];
     for (int e = 0; e < 4; ++e) w[e] = tile[key0 + 2 * e][f] | ((uint32_t)tile[key0 + 2 * e + 1][f] << 16);
     *reinterpret_cast<u32x4*>(dst + (int64_t)x * 8) = u32x4{w[0], w[1], w[2], w[3]};
@@ -123,13 +123,53 @@ __device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_h
   return true;
 }
 
+// LDS address of a shared-memory object, as the asm below takes it.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const T*)p);
+}
+
+// Inside the pipelined loop every LDS access is written in asm with its own
+// wait: the compiler cannot tell which LDS bytes the in-flight direct-to-LDS
+// copies write, and would otherwise wait for all of them before any LDS access.
+// An asm statement that issues several reads from one address register marks
+// its outputs early-clobber ("=&v"): otherwise the compiler may give the first
+// read's destination the address register, and a read that returns before the
+// next one issues would overwrite the address the later reads use.
+__device__ __forceinline__ int lds_u16(const uint16_t* p) {
+  uint32_t v;
+  asm volatile("ds_read_u16 %0, %1\n"
+               "s_waitcnt lgkmcnt(0)"
+               : "=v"(v)
+               : "v"(lds_addr(p))
+               : "memory");
+  return __builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Waits until at most N of this wave's global loads and copies are in flight.
+// Written with the builtin rather than asm so that the compiler's own wait
+// placement knows about it: otherwise, with direct-to-LDS copies and register
+// loads both outstanding, it cannot order them and waits for all of them before
+// the first use of any loaded register.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("" ::: "memory");
+  // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no
+  // wait), vmcnt[5:4] in bits 15:14
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+  asm volatile("" ::: "memory");
+}
+
 // grid (8 * ceil(units / 8) * 2 * n_hg), kThreads threads.
 __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg, int hpg) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kStages * kStageElems];
-  __shared__ __attribute__((aligned(16))) uint16_t bbuf[kHeadsPerWg * kBHead];
+  __shared__ __attribute__((aligned(16))) uint16_t bbuf[2 * kBBuf];
   __shared__ uint16_t tbl[kMaxCols * kSend];  // block index - sender's first block, or kNoBlock
+  __shared__ uint16_t ucol[kMaxCols];         // kept columns (any sender), ascending
   __shared__ int sbeg[kSend];
+  __shared__ int nu_s;
   __shared__ uint8_t anyc[kMaxCols];
 
   int s, r, rh, hg;
@@ -163,8 +203,21 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       }
     }
   }
+  __syncthreads();
+  // ---- the union of kept columns, in ascending order
+  if (wave == 0) {
+    int base = 0;
+    for (int c0 = 0; c0 <= r; c0 += 64) {
+      const int c = c0 + lane;
+      const bool f = c <= r && anyc[c];
+      const uint64_t m = __ballot(f);
+      if (f) ucol[base + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)c;
+      base += __popcll(m);
+    }
+    if (lane == 0) nu_s = base;
+  }
 
-  // Head group hg holds heads hg * hpg .. + hpg - 1 (hpg <= 16: the receiver
+  // Head group hg holds heads hg * hpg .. + hpg - 1 (hpg <= 12: the receiver
   // heads split evenly over the groups, so that the groups of a block-row take
   // the same time and read the shared sender rows together).
   const int h_lo = hg * hpg, heads_here = min(hpg, a.n_recv - h_lo);
@@ -191,32 +244,41 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     mhi = as_bf16x8(hi);
     mlo = as_bf16x8(lo);
   }
+  // start of this wave's senders (j = wave + 8u) in the block-sparse arrays
+  int sb[kSend / kWaves];
+#pragma unroll
+  for (int u = 0; u < kSend / kWaves; ++u) sb[u] = sbeg[wave + kWaves * u];
   __syncthreads();
+  const int nu = __builtin_amdgcn_readfirstlane(nu_s);
+  const int T = 4 * nu;  // panels
 
   const int row_base = 64 * r + kRowsPerWg * rh;
   const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
   const int n32 = lane & 31, q2 = lane >> 5;
-  auto next_col = [&](int c) {
-    int cc = c + 1;
-    while (cc <= r && !anyc[cc]) ++cc;
-    return cc <= r ? cc : -1;
-  };
-  // Sources of this wave's senders (j = wave + 8u) for one block column: the
-  // stored block's rows of this row half, or a zero page for a sender that did
-  // not keep the block (then every panel reads the same zeros). Looked up once per
-  // column, before any copy is in flight.
+  // Sources of this wave's senders for one block column: the stored block's rows
+  // of this row half, or a zero page for a sender that did not keep the block
+  // (then every panel reads the same zeros).
   struct SendSrc {
     const uint16_t* p[kSend / kWaves];
     int step[kSend / kWaves];
   };
-  auto col_src = [&](int c, SendSrc& ss) {
+  auto col_src = [&](int c, SendSrc& ss) __attribute__((always_inline)) {
+    // tbl entries of senders wave, wave + 8, wave + 16, wave + 24 are 16 B apart
+    uint32_t t4[4];
+    asm volatile("ds_read_u16 %0, %4\n"
+                 "ds_read_u16 %1, %4 offset:16\n"
+                 "ds_read_u16 %2, %4 offset:32\n"
+                 "ds_read_u16 %3, %4 offset:48\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(t4[0]), "=&v"(t4[1]), "=&v"(t4[2]), "=&v"(t4[3])
+                 : "v"(lds_addr(&tbl[c * kSend + wave]))
+                 : "memory");
+    static_assert(kSend / kWaves == 4 && kWaves * 2 == 16, "the offsets above assume this geometry");
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u) {
-      const int j = wave + kWaves * u;
-      const int bi = __builtin_amdgcn_readfirstlane((int)tbl[c * kSend + j]);
-      const int sb = __builtin_amdgcn_readfirstlane(sbeg[j]);
+      const int bi = __builtin_amdgcn_readfirstlane((int)t4[u]);
       if (bi != kNoBlock) {
-        ss.p[u] = a.vals + (int64_t)(sb + bi) * (kBlock * kBlock) + (kRowsPerWg * rh) * kPanel;
+        ss.p[u] = a.vals + (int64_t)(sb[u] + bi) * (kBlock * kBlock) + (kRowsPerWg * rh) * kPanel;
         ss.step[u] = kBlock * kPanel;
       } else {
         ss.p[u] = g_zero_panel;
@@ -228,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   // piece goes straight to LDS, 16 B per lane (lane L fills row L / 2, half L % 2).
   // Senders j with bit 3 set store row r at row position r ^ 1: the transposing
   // reads of senders j and j + 8 then fall in different LDS banks.
-  auto issue_stage = [&](const SendSrc& ss, int jq, int b) {
+  auto issue_stage = [&](const SendSrc& ss, int jq, int b) __attribute__((always_inline)) {
     uint16_t* dst0 = &sbuf[b * kStageElems];
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u) {
@@ -237,15 +299,11 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
                                        (__attribute__((address_space(3))) void*)(dst0 + j * kSendStride), 16, 0, 0);
     }
   };
-  // Mix panel jq from stage buffer b into bbuf. The stage is read with the
-  // transposing LDS load written out in asm, all eight reads of the panel and
-  // their wait in one statement: the compiler cannot see which LDS bytes the
-  // in-flight direct-to-LDS copies of the next panel write, and would otherwise
-  // wait for them before any read.
-  auto mix_panel = [&](int jq, int b) {
+  // Mix the panel in stage buffer b into mixed-panel buffer bb: head slot h,
+  // row i, key k at bbuf[bb * kBBuf + h * kBH + 16 i + k].
+  auto mix_panel = [&](int b, int bb) __attribute__((always_inline)) {
     // senders 8q + e4 (+ 4): row wave + 8u sits at row position (wave ^ (q & 1)) + 8u
     const uint16_t* b0 = &sbuf[b * kStageElems] + (8 * q + e4) * kSendStride + (wave ^ (q & 1)) * kKeysPerStep + 4 * cc4;
-    const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)b0);
     // offsets: rows wave + 8u (u = 0..3) are 256 B apart; senders 8q + e4 + 4
     // (the second k-half) are 4 * kSendStride * 2 = 4352 B further
     static_assert(kRowsPerWg / kWaves == 4 && kKeysPerStep * kWaves * 2 == 256 && kSendStride * 8 == 4352,
@@ -261,19 +319,19 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
         "ds_read_b64_tr_b16 %6, %8 offset:768\n"
         "ds_read_b64_tr_b16 %7, %8 offset:5120\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(tr[0]), "=v"(tr[1]), "=v"(tr[2]), "=v"(tr[3]), "=v"(tr[4]), "=v"(tr[5]), "=v"(tr[6]), "=v"(tr[7])
-        : "v"(a0)
+        : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]), "=&v"(tr[6]),
+          "=&v"(tr[7])
+        : "v"(lds_addr(b0))
         : "memory");
     // Lane (p, q) holds heads 4q .. 4q + 3 at key p. Partner lanes p and p ^ 1
     // swap half of their values (one DPP move) so that each writes two heads as
     // whole dwords (keys p & ~1 and p | 1): the even lane heads 4q, 4q + 1, the
     // odd lane heads 4q + 2, 4q + 3. Two lanes writing halves of one dword would
-    // conflict in the LDS banks. The stores are written out in asm too (the
-    // compiler would otherwise wait for the in-flight copies before them); the
-    // barrier that publishes bbuf waits for them (lgkmcnt).
+    // conflict in the LDS banks; the head stride of 1040 B puts the eight heads a
+    // store touches on distinct banks. The barrier that publishes bbuf waits for
+    // the stores (lgkmcnt).
     const bool odd = p & 1;
-    const uint32_t w0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint16_t*)&bbuf[
-                            (4 * q + 2 * odd) * kBHead + wave * kBRow + kKeysPerStep * jq + (p & ~1)]);
+    const uint32_t w0 = lds_addr(&bbuf[bb * kBBuf + (4 * q + 2 * odd) * kBH + wave * kKeysPerStep + (p & ~1)]);
 #pragma unroll
     for (int u = 0; u < kRowsPerWg / kWaves; ++u) {
       const u32x4 bv = {tr[2 * u][0], tr[2 * u][1], tr[2 * u + 1][0], tr[2 * u + 1][1]};
@@ -285,120 +343,152 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? P : Q), 0xB1, 0xF, 0xF, false);
       const uint32_t ev = odd ? recv : P, od = odd ? Q : recv;  // even-key and odd-key values
       const uint32_t first = (ev & 0xffffu) | (od << 16), second = (ev >> 16) | (od & 0xffff0000u);
-      // elements ((4q + 2 odd + {0, 1}) * kBHead + (wave + 8u) * kBRow + 16 jq + (p & ~1))
-      const uint32_t addr = w0 + 2 * (kWaves * u * kBRow);
+      // row wave + 8u: 8u rows of 16 keys further
+      const uint32_t addr = w0 + 2 * (kWaves * u * kKeysPerStep);
       asm volatile("ds_write_b32 %0, %1\n"
-                   "ds_write_b32 %0, %2 offset:%3" ::"v"(addr), "v"(first), "v"(second), "i"(2 * kBHead)
+                   "ds_write_b32 %0, %2 offset:%3" ::"v"(addr), "v"(first), "v"(second), "i"(2 * kBH)
                    : "memory");
     }
   };
 
-  // Receiver heads of the workgroup: slot t of wave w is head h_lo + w + 8t.
-  // NH = 2 slots per wave when the group has more than 8 heads, else 1; slots
-  // past the group read its last head's V and are computed but not stored, so
-  // that every wave runs the same straight-line schedule.
-  auto run = [&](auto nh) {
-    constexpr int NH = decltype(nh)::value;
-    constexpr int NI = 4 * NH;  // AV items per column: (slot t, feature tile dt)
-    f32x16 acc[NH][4];
+  // The group's products are items (head slot, feature tile dt), 4 per head,
+  // dealt NI to a wave: item g = NI * wave + k. With NI <= 6 a wave's items
+  // span at most two heads, hA and hA + 1. Items past the group's heads (only in
+  // groups of fewer than 2 NI heads) are computed on the last head's V and not
+  // stored, so that every wave runs the same branch-free schedule.
+  auto run = [&](auto ni) __attribute__((always_inline)) {
+    constexpr int NI = decltype(ni)::value;
+    const int g0 = NI * __builtin_amdgcn_readfirstlane(wave), n_items = 4 * heads_here;
+    const int hA = g0 >> 2, k_split = 4 - (g0 & 3);  // items k < k_split use head hA
+    f32x16 acc[NI];
 #pragma unroll
-    for (int t = 0; t < NH; ++t)
+    for (int k = 0; k < NI; ++k) acc[k] = f32x16{};
+    // tiled V of heads hA and hA + 1 (clamped to the group) at block 0 of this
+    // sequence; item k reads feature tile (g0 + k) % 4 of one of them
+    const uint16_t* vbA = a.vt + ((int64_t)(h_lo + min(hA, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D);
+    const uint16_t* vbB = a.vt + ((int64_t)(h_lo + min(hA + 1, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D);
+    SendSrc dsrc;   // sources of the column being copied
+    int v_off = 0;  // tiled-V offset of the column being loaded
+    u32x4 vr[3][NI];
+    auto load_v = [&](int jq, u32x4 (&dst)[NI]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[t][dt] = f32x16{};
-    const uint16_t* vblk[NH];  // slot's tiled V at block 0 of this sequence, + lane
+      for (int k = 0; k < NI; ++k) {
+        const uint16_t* base = ((k < k_split) ? vbA : vbB) + v_off + vtile_pos(jq, (g0 + k) & 3, 0);
+        dst[k] = ldg16(base + 8 * lane);
+      }
+    };
+    auto av = [&](int bb, const u32x4 (&v)[NI]) __attribute__((always_inline)) {
+      // A operands (mixed map, 32 rows x 16 keys) of heads hA and hA + 1: lane
+      // (row n32, half q2) holds keys 8 q2 .. + 7, one contiguous 1 KB read each
+      u32x4 oa, ob;
+      asm volatile("ds_read_b128 %0, %2\n"
+                   "ds_read_b128 %1, %2 offset:%3\n"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=&v"(oa), "=&v"(ob)
+                   : "v"(lds_addr(&bbuf[bb * kBBuf + hA * kBH + n32 * kKeysPerStep + 8 * q2])), "i"(2 * kBH)
+                   : "memory");
 #pragma unroll
-    for (int t = 0; t < NH; ++t) {
-      const int h = h_lo + min(wave + kWaves * t, heads_here - 1);
-      vblk[t] = a.vt + ((int64_t)h * a.n_block_rows + roff) * (kBlock * D) + 8 * lane;
-    }
-    // V operand of item k (slot k / 4, feature tile k % 4) of block c: four
-    // contiguous 1 KB runs of the tiled V. In k-step ks lane half q2 holds keys
-    // 32 q2 + 8 ks .. +8; the mixed-map operand uses the same key order.
-    auto load_v = [&](int k, int c, u32x4 vb[4]) {
-      const uint16_t* src = vblk[k / 4] + (int64_t)c * (kBlock * D) + (k % 4) * 2048;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) vb[ks] = ldg16(src + 512 * ks);
+      for (int k = 0; k < NI; ++k) {
+        const u32x4 o = (k < k_split) ? oa : ob;
+        acc[k] = mfma32(as_bf16x8(o), as_bf16x8(v[k]), acc[k]);
+      }
     };
 
-    // Per block column: four panels are mixed (panel jq + 1 in flight meanwhile),
-    // then O += B V over the block's 64 keys in NI items, each item's V loaded two
-    // items ahead into a ring of three; the first two items are issued during
-    // panel 2's mixing and the next column's panel 0 during panel 3's, so both
-    // stay in flight across the remaining mixing.
-    int c = anyc[0] ? 0 : next_col(0);
-    int buf = 0;
-    SendSrc cur, nxt;
-    if (c >= 0) {
-      col_src(c, cur);
-      issue_stage(cur, 0, 0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    barrier_lds();
-    u32x4 vb[3][4];
-    while (c >= 0) {
-      const int cn = next_col(c);
-      if (cn >= 0) col_src(cn, nxt);
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        if (jq < 3) issue_stage(cur, jq + 1, buf ^ 1);
-        else if (cn >= 0) issue_stage(nxt, 0, buf ^ 1);
-        if (jq == 2) {
-          load_v(0, c, vb[0]);
-          load_v(1, c, vb[1]);
-        }
-        mix_panel(jq, buf);
-        // panel jq + 1 must have landed before the next pass reads it; the copy
-        // of the next column's panel 0 (issued at jq = 3) may stay in flight
-        // through the products below, as may the V items issued at jq = 2 (8
-        // loads, newer than panel 3's copies)
-        if (jq < 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        else if (jq == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        barrier_lds();
-        buf ^= 1;
-      }
-      // ---- O += B_h V_h over the block's 64 keys
-#pragma unroll
-      for (int t = 0; t < NH; ++t) {
-        bf16x8 av[4];
-        const int hh = wave + kWaves * t;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          av[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(&bbuf[hh * kBHead + n32 * kBRow + 32 * q2 + 8 * ks]));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int k = 4 * t + dt;
-          if (k + 2 < NI) load_v(k + 2, c, vb[(k + 2) % 3]);
-          // keep the scheduler from sinking the prefetch next to its use
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) acc[t][dt] = mfma32(av[ks], as_bf16x8(vb[k % 3][ks]), acc[t][dt]);
-        }
-      }
-      // the next column's panel 0 is read next; bbuf is rewritten by its mixing
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Step t (R = t % 3): copy panel t + 3 into stage R (panel t's, mixed in the
+    // previous step), load V of panel t + 2 into ring slot (R + 2) % 3, mix panel
+    // t + 1, multiply panel t. A full step (t + 3 < T) issues 4 + NI global
+    // operations, so waiting until at most that many are in flight at its end
+    // completes every earlier step's: panel t + 2's copy before it is mixed,
+    // panel t + 1's V before it is multiplied.
+    //
+    // Main loop: 12 steps per trip, all full, with the column changes at fixed
+    // steps (panel t + 3 starts a column when t % 4 == 1, panel t + 2 when
+    // t % 4 == 2), so the body has no branches and the compiler's own waits for
+    // the V registers stay exact.
+    auto step_main = [&](int t0, auto ic) __attribute__((always_inline)) {
+      constexpr int I = decltype(ic)::value, R = I % 3;
+      const int t = t0 + I;
+      if constexpr (I % 4 == 1) col_src(lds_u16(&ucol[(t + 3) >> 2]), dsrc);
+      issue_stage(dsrc, (I + 3) % 4, R);
+      if constexpr (I % 4 == 2) v_off = lds_u16(&ucol[(t + 2) >> 2]) * (kBlock * D);
+      load_v((I + 2) % 4, vr[(R + 2) % 3]);
+      mix_panel((R + 1) % 3, (I + 1) & 1);
+      av(I & 1, vr[R]);
+      wait_vm<kSend / kWaves + NI>();
       barrier_lds();
-      c = cn;
-      cur = nxt;
+    };
+    // The last steps (fewer than 15 left): the same work under run-time tests.
+    auto step_tail = [&](int t, auto rc) __attribute__((always_inline)) {
+      constexpr int R = decltype(rc)::value;
+      const bool full = t + 3 < T;
+      if (full) {
+        if (((t + 3) & 3) == 0) col_src(lds_u16(&ucol[(t + 3) >> 2]), dsrc);
+        issue_stage(dsrc, (t + 3) & 3, R);
+      }
+      if (t + 2 < T) {
+        if (((t + 2) & 3) == 0) v_off = lds_u16(&ucol[(t + 2) >> 2]) * (kBlock * D);
+        load_v((t + 2) & 3, vr[(R + 2) % 3]);
+      }
+      if (t + 1 < T) mix_panel((R + 1) % 3, (t + 1) & 1);
+      av(t & 1, vr[R]);
+      if (full) wait_vm<kSend / kWaves + NI>();
+      else wait_vm<0>();
+      barrier_lds();
+    };
+
+    if (T > 0) {
+      // prologue (T >= 4): panels 0, 1, 2 of the first column copied, V of
+      // panels 0, 1 loaded, panel 0 mixed
+      col_src(lds_u16(&ucol[0]), dsrc);
+#pragma unroll
+      for (int b = 0; b < kStages; ++b) issue_stage(dsrc, b, b);
+      v_off = lds_u16(&ucol[0]) * (kBlock * D);
+      load_v(0, vr[0]);
+      load_v(1, vr[1]);
+      wait_vm<0>();
+      barrier_lds();
+      mix_panel(0, 0);
+      barrier_lds();
+    }
+    int t = 0;
+    for (; t + 14 < T; t += 12) {
+      step_main(t, std::integral_constant<int, 0>{});
+      step_main(t, std::integral_constant<int, 1>{});
+      step_main(t, std::integral_constant<int, 2>{});
+      step_main(t, std::integral_constant<int, 3>{});
+      step_main(t, std::integral_constant<int, 4>{});
+      step_main(t, std::integral_constant<int, 5>{});
+      step_main(t, std::integral_constant<int, 6>{});
+      step_main(t, std::integral_constant<int, 7>{});
+      step_main(t, std::integral_constant<int, 8>{});
+      step_main(t, std::integral_constant<int, 9>{});
+      step_main(t, std::integral_constant<int, 10>{});
+      step_main(t, std::integral_constant<int, 11>{});
+    }
+    for (; t < T; t += 3) {
+      step_tail(t, std::integral_constant<int, 0>{});
+      if (t + 1 < T) step_tail(t + 1, std::integral_constant<int, 1>{});
+      if (t + 2 < T) step_tail(t + 2, std::integral_constant<int, 2>{});
     }
     // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
-    for (int t = 0; t < NH; ++t) {
-      if (wave + kWaves * t >= heads_here) continue;
-      const int h = h_lo + wave + kWaves * t;
+    for (int k = 0; k < NI; ++k) {
+      const int g = g0 + k;
+      if (g >= n_items) continue;
+      const int h = h_lo + (g >> 2), dt = g & 3;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
-          if (row >= n) continue;
-          const int64_t o = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + row) * D + 32 * dt + n32;
-          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[t][dt][v]);
-          else reinterpret_cast<float*>(a.out)[o] = acc[t][dt][v];
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
+        if (row >= n) continue;
+        const int64_t o = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + row) * D + 32 * dt + n32;
+        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[k][v]);
+        else reinterpret_cast<float*>(a.out)[o] = acc[k][v];
+      }
     }
   };
-  if (heads_here > kWaves) run(std::integral_constant<int, 2>{});
-  else run(std::integral_constant<int, 1>{});
+  if (heads_here > 8) run(std::integral_constant<int, 6>{});
+  else if (heads_here > 4) run(std::integral_constant<int, 4>{});
+  else run(std::integral_constant<int, 2>{});
 }
 
 // ---------------------------------------------------------------- dense source

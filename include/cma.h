@@ -183,8 +183,8 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
  * kernel's operand order, [n_recv, n_block_rows, 64 * 128]: sequence s's keys in
  * 64-key blocks numbered like the block-sparse maps' block-rows (its first block
  * at the sum of ceil(len/64) over earlier sequences); within block c, element
- *   ((dt * 4 + ks) * 64 + L) * 8 + e  =  V[key 64c + 32(L/32) + 8ks + e][feature 32dt + L%32]
- * for dt, ks in 0..3, L in 0..63, e in 0..7, zero past the sequence end. A V
+ *   ((ks * 4 + dt) * 64 + L) * 8 + e  =  V[key 64c + 16ks + 8(L/32) + e][feature 32dt + L%32]
+ * for ks, dt in 0..3, L in 0..63, e in 0..7, zero past the sequence end. A V
  * projection can write it directly; cma_mapped_av builds it from the other two
  * layouts in its workspace. */
 typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1, CMA_V_TILED = 2 } cma_v_layout;

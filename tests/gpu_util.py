@@ -61,16 +61,16 @@ def blocks_from_panels(vals):
 def tile_v(V, lens, cu):
     """Token-major V [H, T, 128] (uint16 bf16 bits) -> the tiled operand layout the
     library documents: [H, sum ceil(len/64), 64 * 128], block c of sequence s at
-    block offset sum_{u<s} ceil(len_u/64); element ((dt*4+ks)*64 + L)*8 + e of a
-    block is V[key 64c + 32(L//32) + 8ks + e][feature 32dt + L%32], zero past the end."""
+    block offset sum_{u<s} ceil(len_u/64); element ((ks*4+dt)*64 + L)*8 + e of a
+    block is V[key 64c + 16ks + 8(L//32) + e][feature 32dt + L%32], zero past the end."""
     V = np.asarray(V)
     H = V.shape[0]
     nb = [(n + 63) // 64 for n in lens]
     out = np.zeros((H, sum(nb), 64 * 128), dtype=V.dtype)
     dt, ks, L, e = np.meshgrid(np.arange(4), np.arange(4), np.arange(64), np.arange(8), indexing="ij")
-    key = 32 * (L // 32) + 8 * ks + e
+    key = 16 * ks + 8 * (L // 32) + e
     feat = 32 * dt + L % 32
-    pos = (((dt * 4 + ks) * 64 + L) * 8 + e).ravel()
+    pos = (((ks * 4 + dt) * 64 + L) * 8 + e).ravel()
     b0 = 0
     for s, n in enumerate(lens):
         for c in range(nb[s]):
