@@ -45,6 +45,8 @@ constexpr int kBH = 520;             // bf16 per head of a mixed panel: 32 rows 
 constexpr int kBBuf = 16 * kBH;      // one mixed panel, 16 head slots (the mix's M rows)
 constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
 constexpr uint16_t kNoBlock = 0xffff;
+// buffer descriptor word 3 for raw (unformatted) 32-bit accesses on gfx9-family chips
+constexpr int kBufferFlags = 0x00020000;
 
 // V in the fused kernel's operand order ("tiled"): for head h and 64-key block b
 // of the block grid (sequence s's blocks start at its block-row offset, as in
@@ -176,7 +178,8 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   if (!decode_item(blockIdx.x, a.vl.n_seqs, nrb, n_hg, s, r, rh, hg)) return;
   const int32_t n = seq_len_q(a.vl, s);
   if (!seq_ok(a.vl, s, n, n) || 64 * r + kRowsPerWg * rh >= n) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform: keep it (and what is derived from it) in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   int32_t roff;
   int64_t tri;
   block_offsets(a.vl, s, roff, tri);
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   // start of this wave's senders (j = wave + 8u) in the block-sparse arrays
   int sb[kSend / kWaves];
 #pragma unroll
-  for (int u = 0; u < kSend / kWaves; ++u) sb[u] = sbeg[wave + kWaves * u];
+  for (int u = 0; u < kSend / kWaves; ++u) sb[u] = __builtin_amdgcn_readfirstlane(sbeg[wave + kWaves * u]);
   __syncthreads();
   const int nu = __builtin_amdgcn_readfirstlane(nu_s);
   const int T = 4 * nu;  // panels
@@ -258,9 +261,12 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   // Sources of this wave's senders for one block column: the stored block's rows
   // of this row half, or a zero page for a sender that did not keep the block
   // (then every panel reads the same zeros).
+  // Global reads go through buffer descriptors: the base and the per-step offset
+  // are scalar, the per-lane offset is one register, and a read past the
+  // descriptor's size returns zeros instead of touching memory.
   struct SendSrc {
-    const uint16_t* p[kSend / kWaves];
-    int step[kSend / kWaves];
+    __amdgpu_buffer_rsrc_t r[kSend / kWaves];
+    int step[kSend / kWaves];  // bytes per panel: 2 KB, or 0 for the zero page
   };
   auto col_src = [&](int c, SendSrc& ss) __attribute__((always_inline)) {
     // tbl entries of senders wave, wave + 8, wave + 16, wave + 24 are 16 B apart
@@ -277,38 +283,41 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u) {
       const int bi = __builtin_amdgcn_readfirstlane((int)t4[u]);
-      if (bi != kNoBlock) {
-        ss.p[u] = a.vals + (int64_t)(sb[u] + bi) * (kBlock * kBlock) + (kRowsPerWg * rh) * kPanel;
-        ss.step[u] = kBlock * kPanel;
-      } else {
-        ss.p[u] = g_zero_panel;
-        ss.step[u] = 0;
-      }
+      const bool kept = bi != kNoBlock;
+      // this row half's rows of the stored block: 3 panels x 2 KB + 1 KB reachable
+      const uint16_t* base =
+          kept ? a.vals + (int64_t)(sb[u] + bi) * (kBlock * kBlock) + (kRowsPerWg * rh) * kPanel : g_zero_panel;
+      ss.r[u] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0,
+                                                  kept ? 2 * (kBlock * kBlock - kRowsPerWg * rh * kPanel) : 2 * kBlock * kPanel,
+                                                  kBufferFlags);
+      ss.step[u] = kept ? 2 * kBlock * kPanel : 0;
     }
   };
   // Copy panel jq (16 keys) of the column into stage buffer b: each sender's 1 KB
   // piece goes straight to LDS, 16 B per lane (lane L fills row L / 2, half L % 2).
   // Senders j with bit 3 set store row r at row position r ^ 1: the transposing
-  // reads of senders j and j + 8 then fall in different LDS banks.
+  // reads of senders j and j + 8 then fall in different LDS banks. The source is a
+  // wave-uniform base plus a per-lane byte offset.
+  const uint32_t loff0 = 16u * lane, loff1 = 16u * (lane ^ 2);
   auto issue_stage = [&](const SendSrc& ss, int jq, int b) __attribute__((always_inline)) {
     uint16_t* dst0 = &sbuf[b * kStageElems];
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u) {
       const int j = wave + kWaves * u;  // (j >> 3) & 1 == u & 1
-      __builtin_amdgcn_global_load_lds(ss.p[u] + jq * ss.step[u] + 8 * (lane ^ (2 * (u & 1))),
-                                       (__attribute__((address_space(3))) void*)(dst0 + j * kSendStride), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.r[u], (__attribute__((address_space(3))) void*)(dst0 + j * kSendStride),
+                                               16, (u & 1) ? loff1 : loff0, jq * ss.step[u], 0, 0);
     }
   };
-  // Mix the panel in stage buffer b into mixed-panel buffer bb: head slot h,
-  // row i, key k at bbuf[bb * kBBuf + h * kBH + 16 i + k].
-  auto mix_panel = [&](int b, int bb) __attribute__((always_inline)) {
-    // senders 8q + e4 (+ 4): row wave + 8u sits at row position (wave ^ (q & 1)) + 8u
-    const uint16_t* b0 = &sbuf[b * kStageElems] + (8 * q + e4) * kSendStride + (wave ^ (q & 1)) * kKeysPerStep + 4 * cc4;
-    // offsets: rows wave + 8u (u = 0..3) are 256 B apart; senders 8q + e4 + 4
-    // (the second k-half) are 4 * kSendStride * 2 = 4352 B further
-    static_assert(kRowsPerWg / kWaves == 4 && kKeysPerStep * kWaves * 2 == 256 && kSendStride * 8 == 4352,
-                  "the offsets below assume this stage geometry");
-    u32x2 tr[8];
+  // LDS reads of one step, in one asm statement with one wait: the eight
+  // transposing reads of the panel to mix (lane (p, q) gets senders 8q .. 8q + 7
+  // at key p of rows wave + 8u; senders 8q + e4 (+ 4), row wave + 8u at row
+  // position (wave ^ (q & 1)) + 8u) and the two mixed-map operands of the
+  // products.
+  static_assert(kRowsPerWg / kWaves == 4 && kKeysPerStep * kWaves * 2 == 256 && kSendStride * 8 == 4352,
+                "the offsets below assume this stage geometry");
+  const uint32_t tr_lane = 2u * ((8 * q + e4) * kSendStride + (wave ^ (q & 1)) * kKeysPerStep + 4 * cc4);
+  auto read_mix_src = [&](int b, u32x2 (&tr)[8]) __attribute__((always_inline)) {
+    const uint32_t a0 = lds_addr(&sbuf[b * kStageElems]) + tr_lane;
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n"
         "ds_read_b64_tr_b16 %1, %8 offset:4352\n"
@@ -321,85 +330,122 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]), "=&v"(tr[6]),
           "=&v"(tr[7])
-        : "v"(lds_addr(b0))
+        : "v"(a0)
         : "memory");
-    // Lane (p, q) holds heads 4q .. 4q + 3 at key p. Partner lanes p and p ^ 1
-    // swap half of their values (one DPP move) so that each writes two heads as
-    // whole dwords (keys p & ~1 and p | 1): the even lane heads 4q, 4q + 1, the
-    // odd lane heads 4q + 2, 4q + 3. Two lanes writing halves of one dword would
-    // conflict in the LDS banks; the head stride of 1040 B puts the eight heads a
-    // store touches on distinct banks. The barrier that publishes bbuf waits for
-    // the stores (lgkmcnt).
-    const bool odd = p & 1;
-    const uint32_t w0 = lds_addr(&bbuf[bb * kBBuf + (4 * q + 2 * odd) * kBH + wave * kKeysPerStep + (p & ~1)]);
+  };
+  auto read_step = [&](int b, u32x2 (&tr)[8], uint32_t oa_addr, uint32_t ob_addr, u32x4& oa, u32x4& ob)
+                       __attribute__((always_inline)) {
+    const uint32_t a0 = lds_addr(&sbuf[b * kStageElems]) + tr_lane;
+    asm volatile(
+        "ds_read_b128 %8, %10\n"
+        "ds_read_b128 %9, %11\n"
+        "ds_read_b64_tr_b16 %0, %12\n"
+        "ds_read_b64_tr_b16 %1, %12 offset:4352\n"
+        "ds_read_b64_tr_b16 %2, %12 offset:256\n"
+        "ds_read_b64_tr_b16 %3, %12 offset:4608\n"
+        "ds_read_b64_tr_b16 %4, %12 offset:512\n"
+        "ds_read_b64_tr_b16 %5, %12 offset:4864\n"
+        "ds_read_b64_tr_b16 %6, %12 offset:768\n"
+        "ds_read_b64_tr_b16 %7, %12 offset:5120\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(tr[0]), "=&v"(tr[1]), "=&v"(tr[2]), "=&v"(tr[3]), "=&v"(tr[4]), "=&v"(tr[5]), "=&v"(tr[6]),
+          "=&v"(tr[7]), "=&v"(oa), "=&v"(ob)
+        : "v"(oa_addr), "v"(ob_addr), "v"(a0)
+        : "memory");
+  };
+  // Mix on 16x16x32 MFMAs with the senders as the A operand and M as the B
+  // operand: D[key 4q + v][head p] for row wave + 8u lands in lane (p, q), so a
+  // lane holds four consecutive keys of one head and writes them as one 8-byte
+  // store to bbuf[bb * kBBuf + p * kBH + 16 row + 4q] (head slot, row, key).
+  // With the head stride of 1040 B the 64 lanes of a store hit distinct banks.
+  const uint32_t mix_lane = 2u * (p * kBH + wave * kKeysPerStep + 4 * q);
+  auto mix_store = [&](int bb, const u32x2 (&tr)[8]) __attribute__((always_inline)) {
+    u32x2 w[4];
 #pragma unroll
     for (int u = 0; u < kRowsPerWg / kWaves; ++u) {
-      const u32x4 bv = {tr[2 * u][0], tr[2 * u][1], tr[2 * u + 1][0], tr[2 * u + 1][1]};
-      f32x4 d1 = {0.f, 0.f, 0.f, 0.f};
-      d1 = mfma16(mhi, as_bf16x8(bv), d1);
-      d1 = mfma16(mlo, as_bf16x8(bv), d1);
-      const uint32_t P = pack2bf(d1[0], d1[1]), Q = pack2bf(d1[2], d1[3]);
-      // quad_perm [1, 0, 3, 2]: the value of lane p ^ 1
-      const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? P : Q), 0xB1, 0xF, 0xF, false);
-      const uint32_t ev = odd ? recv : P, od = odd ? Q : recv;  // even-key and odd-key values
-      const uint32_t first = (ev & 0xffffu) | (od << 16), second = (ev >> 16) | (od & 0xffff0000u);
-      // row wave + 8u: 8u rows of 16 keys further
-      const uint32_t addr = w0 + 2 * (kWaves * u * kKeysPerStep);
-      asm volatile("ds_write_b32 %0, %1\n"
-                   "ds_write_b32 %0, %2 offset:%3" ::"v"(addr), "v"(first), "v"(second), "i"(2 * kBH)
-                   : "memory");
+      const u32x4 av = {tr[2 * u][0], tr[2 * u][1], tr[2 * u + 1][0], tr[2 * u + 1][1]};
+      f32x4 d = mfma16(as_bf16x8(av), mhi, f32x4{0.f, 0.f, 0.f, 0.f});
+      d = mfma16(as_bf16x8(av), mlo, d);
+      w[u] = u32x2{pack2bf(d[0], d[1]), pack2bf(d[2], d[3])};
     }
+    // rows wave + 8u are 8 x 32 B = 256 B apart
+    asm volatile(
+        "ds_write_b64 %0, %1\n"
+        "ds_write_b64 %0, %2 offset:256\n"
+        "ds_write_b64 %0, %3 offset:512\n"
+        "ds_write_b64 %0, %4 offset:768" ::"v"(lds_addr(&bbuf[bb * kBBuf]) + mix_lane),
+        "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3])
+        : "memory");
   };
 
   // The group's products are items (head slot, feature tile dt), 4 per head,
-  // dealt NI to a wave: item g = NI * wave + k. With NI <= 6 a wave's items
-  // span at most two heads, hA and hA + 1. Items past the group's heads (only in
-  // groups of fewer than 2 NI heads) are computed on the last head's V and not
+  // dealt NI to a wave with a fixed shape: items k < NA use head slot sA (tiles
+  // dA + k), the rest head slot sB (tiles dB + k - NA).
+  //   NI = 6 (up to 12 heads): sA = wave (all four tiles), sB = 8 + wave / 2
+  //                            (tiles 2 (wave % 2), + 1)
+  //   NI = 4 (up to 8 heads):  sA = wave (all four tiles)
+  //   NI = 2 (up to 4 heads):  sA = wave / 2 (tiles 2 (wave % 2), + 1)
+  // Slots past the group's heads compute on the last head's V and are not
   // stored, so that every wave runs the same branch-free schedule.
   auto run = [&](auto ni) __attribute__((always_inline)) {
     constexpr int NI = decltype(ni)::value;
-    const int g0 = NI * __builtin_amdgcn_readfirstlane(wave), n_items = 4 * heads_here;
-    const int hA = g0 >> 2, k_split = 4 - (g0 & 3);  // items k < k_split use head hA
+    constexpr int NA = NI == 2 ? 2 : 4;
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int sA = NI == 2 ? (w >> 1) : w, dA = NI == 2 ? 2 * (w & 1) : 0;
+    const int sB = NI == 6 ? 8 + (w >> 1) : sA, dB = NI == 6 ? 2 * (w & 1) : 0;
     f32x16 acc[NI];
 #pragma unroll
     for (int k = 0; k < NI; ++k) acc[k] = f32x16{};
-    // tiled V of heads hA and hA + 1 (clamped to the group) at block 0 of this
-    // sequence; item k reads feature tile (g0 + k) % 4 of one of them
-    const uint16_t* vbA = a.vt + ((int64_t)(h_lo + min(hA, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D);
-    const uint16_t* vbB = a.vt + ((int64_t)(h_lo + min(hA + 1, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D);
+    // tiled V of slots sA and sB (clamped to the group): this sequence's blocks
+    const int v_bytes = ((n + kBlock - 1) / kBlock) * (kBlock * D * 2);
+    const __amdgpu_buffer_rsrc_t vA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.vt + ((int64_t)(h_lo + min(sA, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D)),
+        (short)0, v_bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vB = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.vt + ((int64_t)(h_lo + min(sB, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D)),
+        (short)0, v_bytes, kBufferFlags);
+    // mixed-map operands of slots sA and sB: lane (row n32, half q2) holds keys
+    // 8 q2 .. + 7, one contiguous 1 KB read each
+    const uint32_t oA_lane = 2u * (sA * kBH + n32 * kKeysPerStep + 8 * q2);
+    const uint32_t oB_lane = 2u * (sB * kBH + n32 * kKeysPerStep + 8 * q2);
     SendSrc dsrc;   // sources of the column being copied
     int v_off = 0;  // tiled-V offset of the column being loaded
-    u32x4 vr[3][NI];
+    u32x4 vr[2][NI];
+    const uint32_t vlane = 16u * lane;
     auto load_v = [&](int jq, u32x4 (&dst)[NI]) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
-        const uint16_t* base = ((k < k_split) ? vbA : vbB) + v_off + vtile_pos(jq, (g0 + k) & 3, 0);
-        dst[k] = ldg16(base + 8 * lane);
+        const int soff = 2 * (v_off + (k < NA ? vtile_pos(jq, dA + k, 0) : vtile_pos(jq, dB + k - NA, 0)));
+        dst[k] = __builtin_amdgcn_raw_buffer_load_b128(k < NA ? vA : vB, vlane, soff, 0);
       }
     };
-    auto av = [&](int bb, const u32x4 (&v)[NI]) __attribute__((always_inline)) {
-      // A operands (mixed map, 32 rows x 16 keys) of heads hA and hA + 1: lane
-      // (row n32, half q2) holds keys 8 q2 .. + 7, one contiguous 1 KB read each
+    // Mix the panel in stage b into mixed buffer bbm (when do_mix), and
+    // O += B V over the mixed panel in buffer bba with V operands v.
+    auto compute = [&](int b, int bbm, bool do_mix, int bba, const u32x4 (&v)[NI]) __attribute__((always_inline)) {
+      u32x2 tr[8];
       u32x4 oa, ob;
-      asm volatile("ds_read_b128 %0, %2\n"
-                   "ds_read_b128 %1, %2 offset:%3\n"
-                   "s_waitcnt lgkmcnt(0)"
-                   : "=&v"(oa), "=&v"(ob)
-                   : "v"(lds_addr(&bbuf[bb * kBBuf + hA * kBH + n32 * kKeysPerStep + 8 * q2])), "i"(2 * kBH)
-                   : "memory");
-#pragma unroll
-      for (int k = 0; k < NI; ++k) {
-        const u32x4 o = (k < k_split) ? oa : ob;
-        acc[k] = mfma32(as_bf16x8(o), as_bf16x8(v[k]), acc[k]);
+      const uint32_t ob0 = lds_addr(&bbuf[bba * kBBuf]);
+      if (do_mix) {
+        read_step(b, tr, ob0 + oA_lane, ob0 + oB_lane, oa, ob);
+      } else {
+        asm volatile("ds_read_b128 %0, %2\n"
+                     "ds_read_b128 %1, %3\n"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(oa), "=&v"(ob)
+                     : "v"(ob0 + oA_lane), "v"(ob0 + oB_lane)
+                     : "memory");
       }
+#pragma unroll
+      for (int k = 0; k < NI; ++k) acc[k] = mfma32(as_bf16x8(k < NA ? oa : ob), as_bf16x8(v[k]), acc[k]);
+      if (do_mix) mix_store(bbm, tr);
     };
 
     // Step t (R = t % 3): copy panel t + 3 into stage R (panel t's, mixed in the
-    // previous step), load V of panel t + 2 into ring slot (R + 2) % 3, mix panel
-    // t + 1, multiply panel t. A full step (t + 3 < T) issues 4 + NI global
-    // operations, so waiting until at most that many are in flight at its end
-    // completes every earlier step's: panel t + 2's copy before it is mixed,
-    // panel t + 1's V before it is multiplied.
+    // previous step), mix panel t + 1, multiply panel t with the V operands in
+    // ring slot t % 2, then load V of panel t + 2 into that slot. A full step
+    // (t + 3 < T) issues 4 + NI global operations, so waiting until at most that
+    // many are in flight at its end completes every earlier step's: panel t + 2's
+    // copy before it is mixed, panel t + 1's V before it is multiplied.
     //
     // Main loop: 12 steps per trip, all full, with the column changes at fixed
     // steps (panel t + 3 starts a column when t % 4 == 1, panel t + 2 when
@@ -410,27 +456,26 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       const int t = t0 + I;
       if constexpr (I % 4 == 1) col_src(lds_u16(&ucol[(t + 3) >> 2]), dsrc);
       issue_stage(dsrc, (I + 3) % 4, R);
+      compute((R + 1) % 3, (I + 1) & 1, true, I & 1, vr[I & 1]);
       if constexpr (I % 4 == 2) v_off = lds_u16(&ucol[(t + 2) >> 2]) * (kBlock * D);
-      load_v((I + 2) % 4, vr[(R + 2) % 3]);
-      mix_panel((R + 1) % 3, (I + 1) & 1);
-      av(I & 1, vr[R]);
+      load_v((I + 2) % 4, vr[I & 1]);
       wait_vm<kSend / kWaves + NI>();
       barrier_lds();
     };
     // The last steps (fewer than 15 left): the same work under run-time tests.
-    auto step_tail = [&](int t, auto rc) __attribute__((always_inline)) {
-      constexpr int R = decltype(rc)::value;
+    // Stage, mixed buffer and V slot of step t follow t % 6 as in the main loop.
+    auto step_tail = [&](int t, auto ic) __attribute__((always_inline)) {
+      constexpr int I = decltype(ic)::value, R = I % 3;  // t % 6 == I
       const bool full = t + 3 < T;
       if (full) {
         if (((t + 3) & 3) == 0) col_src(lds_u16(&ucol[(t + 3) >> 2]), dsrc);
         issue_stage(dsrc, (t + 3) & 3, R);
       }
+      compute((R + 1) % 3, (I + 1) & 1, t + 1 < T, I & 1, vr[I & 1]);
       if (t + 2 < T) {
         if (((t + 2) & 3) == 0) v_off = lds_u16(&ucol[(t + 2) >> 2]) * (kBlock * D);
-        load_v((t + 2) & 3, vr[(R + 2) % 3]);
+        load_v((t + 2) & 3, vr[I & 1]);
       }
-      if (t + 1 < T) mix_panel((R + 1) % 3, (t + 1) & 1);
-      av(t & 1, vr[R]);
       if (full) wait_vm<kSend / kWaves + NI>();
       else wait_vm<0>();
       barrier_lds();
@@ -447,7 +492,9 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       load_v(1, vr[1]);
       wait_vm<0>();
       barrier_lds();
-      mix_panel(0, 0);
+      u32x2 tr[8];
+      read_mix_src(0, tr);
+      mix_store(0, tr);
       barrier_lds();
     }
     int t = 0;
@@ -465,17 +512,20 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       step_main(t, std::integral_constant<int, 10>{});
       step_main(t, std::integral_constant<int, 11>{});
     }
-    for (; t < T; t += 3) {
+    for (; t < T; t += 6) {  // t % 6 == 0 here
       step_tail(t, std::integral_constant<int, 0>{});
       if (t + 1 < T) step_tail(t + 1, std::integral_constant<int, 1>{});
       if (t + 2 < T) step_tail(t + 2, std::integral_constant<int, 2>{});
+      if (t + 3 < T) step_tail(t + 3, std::integral_constant<int, 3>{});
+      if (t + 4 < T) step_tail(t + 4, std::integral_constant<int, 4>{});
+      if (t + 5 < T) step_tail(t + 5, std::integral_constant<int, 5>{});
     }
     // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
     for (int k = 0; k < NI; ++k) {
-      const int g = g0 + k;
-      if (g >= n_items) continue;
-      const int h = h_lo + (g >> 2), dt = g & 3;
+      const int slot = k < NA ? sA : sB, dt = k < NA ? dA + k : dB + k - NA;
+      if (slot >= heads_here) continue;
+      const int h = h_lo + slot;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
