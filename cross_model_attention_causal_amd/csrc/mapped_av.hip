@@ -103,22 +103,27 @@ __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, 
 // copied from here like any other (1 KB, read by every lane's 16-byte copy).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_panel[kBlock * kPanel];
 
-// Work items are (sequence, block-row r, row half, head group). Items of one
-// (sequence, r) "unit" share sender rows (head groups) and V tiles (row halves),
-// so they are placed on the same XCD at the same time: the hardware deals
-// workgroup ids round-robin over the 8 XCDs, so id i runs on XCD i % 8 and is
-// that XCD's (i / 8)-th workgroup. Units are ordered longest first (r
-// descending, sequences interleaved) and unit u goes to XCD u % 8: with up to 8
-// sequences an XCD keeps to the same sequences, whose block-rows then sweep the
-// key blocks together and share V tiles in its L2.
-
-__device__ __forceinline__ bool decode_item(int id, int n_seqs, int nrb, int n_hg, int& s, int& r, int& rh, int& hg) {
+// Work items are (sequence, pair of block-rows, row half, head group). Pair pr
+// of a sequence with R block-rows holds rows R - 1 - pr and pr: the long row is
+// swept with its key columns ascending, then the short row with its columns
+// descending. Every pair then covers R + 1 columns, so the workgroups of a
+// launch wave start together and stay in step, and at any time they all work on
+// one of two columns (tau and R + 1 - tau): each V tile and each sender column is
+// fetched once per XCD and then served from its L2 to all of them. Items of one
+// (sequence, pair) "unit" share sender rows (head groups) and V tiles (row
+// halves) and sit on the same XCD: the hardware deals workgroup ids round-robin
+// over the 8 XCDs, so id i runs on XCD i % 8 and is that XCD's (i / 8)-th
+// workgroup, and unit u goes to XCD u % 8; units are numbered pair-major with
+// the sequences interleaved, so with up to 8 sequences an XCD keeps to the same
+// sequences.
+__device__ __forceinline__ bool decode_item(int id, int n_seqs, int n_pairs, int n_hg, int& s, int& pr, int& rh,
+                                            int& hg) {
   const int per_unit = 2 * n_hg;
   const int xcd = id % kXcds, m = id / kXcds;
   const int k = m / per_unit, item = m % per_unit;
   const int u = kXcds * k + xcd;
-  if (u >= n_seqs * nrb) return false;
-  r = nrb - 1 - u / n_seqs;
+  if (u >= n_seqs * n_pairs) return false;
+  pr = u / n_seqs;
   s = u % n_seqs;
   rh = item & 1;
   hg = item >> 1;
@@ -164,7 +169,7 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // grid (8 * ceil(units / 8) * 2 * n_hg), kThreads threads.
-__global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int nrb, int n_hg, int hpg) {
+__global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int n_pairs, int n_hg, int hpg) {
   constexpr int D = 128;
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kStages * kStageElems];
   __shared__ __attribute__((aligned(16))) uint16_t bbuf[2 * kBBuf];
@@ -174,51 +179,57 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   __shared__ int nu_s;
   __shared__ uint8_t anyc[kMaxCols];
 
-  int s, r, rh, hg;
-  if (!decode_item(blockIdx.x, a.vl.n_seqs, nrb, n_hg, s, r, rh, hg)) return;
+  int s, pr, rh, hg;
+  if (!decode_item(blockIdx.x, a.vl.n_seqs, n_pairs, n_hg, s, pr, rh, hg)) return;
   const int32_t n = seq_len_q(a.vl, s);
-  if (!seq_ok(a.vl, s, n, n) || 64 * r + kRowsPerWg * rh >= n) return;
+  if (!seq_ok(a.vl, s, n, n)) return;
+  const int r_long = (n + kBlock - 1) / kBlock - 1 - pr;  // swept first, columns ascending
+  if (r_long < pr) return;                                 // past this sequence's pairs
+  const int n_pass = r_long > pr ? 2 : 1;                  // then row pr, columns descending
   // the wave index is uniform: keep it (and what is derived from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   int32_t roff;
   int64_t tri;
   block_offsets(a.vl, s, roff, tri);
 
-  // ---- block table: tbl[c][j] = kept block of sender j at column c
-  for (int x = tid; x < (r + 1) * kSend; x += kThreads) tbl[x] = kNoBlock;
-  for (int c = tid; c <= r; c += kThreads) anyc[c] = 0;
-  if (tid < kSend) {
-    sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)tid * a.n_block_rows + roff + r] : 0;
-  }
-  __syncthreads();
-  {
-    constexpr int kPer = kThreads / kSend;  // threads per sender
-    const int j = tid / kPer, e0 = tid % kPer;
-    if (j < a.n_send) {
-      const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
-      const int beg = a.row_ptr[g], end = a.row_ptr[g + 1];
-      for (int e = beg + e0; e < end; e += kPer) {
-        const int c = a.col_idx[e];
-        if (c >= 0 && c <= r && e - beg < (int)kNoBlock) {
-          tbl[c * kSend + j] = (uint16_t)(e - beg);
-          anyc[c] = 1;
+  // Block table of block-row r: tbl[c][j] = kept block of sender j at column c,
+  // ucol = the union of kept columns in ascending order (nu_s of them), sbeg[j] =
+  // sender j's first block of the row.
+  auto build_table = [&](int r) __attribute__((always_inline)) {
+    __syncthreads();  // the previous row's readers are done with these arrays
+    for (int x = tid; x < (r + 1) * kSend; x += kThreads) tbl[x] = kNoBlock;
+    for (int c = tid; c <= r; c += kThreads) anyc[c] = 0;
+    if (tid < kSend) sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)tid * a.n_block_rows + roff + r] : 0;
+    __syncthreads();
+    {
+      constexpr int kPer = kThreads / kSend;  // threads per sender
+      const int j = tid / kPer, e0 = tid % kPer;
+      if (j < a.n_send) {
+        const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
+        const int beg = a.row_ptr[g], end = a.row_ptr[g + 1];
+        for (int e = beg + e0; e < end; e += kPer) {
+          const int c = a.col_idx[e];
+          if (c >= 0 && c <= r && e - beg < (int)kNoBlock) {
+            tbl[c * kSend + j] = (uint16_t)(e - beg);
+            anyc[c] = 1;
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  // ---- the union of kept columns, in ascending order
-  if (wave == 0) {
-    int base = 0;
-    for (int c0 = 0; c0 <= r; c0 += 64) {
-      const int c = c0 + lane;
-      const bool f = c <= r && anyc[c];
-      const uint64_t m = __ballot(f);
-      if (f) ucol[base + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)c;
-      base += __popcll(m);
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = 0; c0 <= r; c0 += 64) {
+        const int c = c0 + lane;
+        const bool f = c <= r && anyc[c];
+        const uint64_t m = __ballot(f);
+        if (f) ucol[base + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)c;
+        base += __popcll(m);
+      }
+      if (lane == 0) nu_s = base;
     }
-    if (lane == 0) nu_s = base;
-  }
+    __syncthreads();
+  };
 
   // Head group hg holds heads hg * hpg .. + hpg - 1 (hpg <= 12: the receiver
   // heads split evenly over the groups, so that the groups of a block-row take
@@ -247,15 +258,13 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     mhi = as_bf16x8(hi);
     mlo = as_bf16x8(lo);
   }
-  // start of this wave's senders (j = wave + 8u) in the block-sparse arrays
+  // per block-row: start of this wave's senders (j = wave + 8u) in the
+  // block-sparse arrays, and the row's panel count and sweep direction
   int sb[kSend / kWaves];
-#pragma unroll
-  for (int u = 0; u < kSend / kWaves; ++u) sb[u] = __builtin_amdgcn_readfirstlane(sbeg[wave + kWaves * u]);
-  __syncthreads();
-  const int nu = __builtin_amdgcn_readfirstlane(nu_s);
-  const int T = 4 * nu;  // panels
-
-  const int row_base = 64 * r + kRowsPerWg * rh;
+  int nu = 0, T = 0;
+  bool rev = false;
+  // k-th kept column of the row in sweep order
+  auto col_at = [&](int k) __attribute__((always_inline)) { return lds_u16(&ucol[rev ? nu - 1 - k : k]); };
   const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
   const int n32 = lane & 31, q2 = lane >> 5;
   // Sources of this wave's senders for one block column: the stored block's rows
@@ -394,8 +403,6 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     const int sA = NI == 2 ? (w >> 1) : w, dA = NI == 2 ? 2 * (w & 1) : 0;
     const int sB = NI == 6 ? 8 + (w >> 1) : sA, dB = NI == 6 ? 2 * (w & 1) : 0;
     f32x16 acc[NI];
-#pragma unroll
-    for (int k = 0; k < NI; ++k) acc[k] = f32x16{};
     // tiled V of slots sA and sB (clamped to the group): this sequence's blocks
     const int v_bytes = ((n + kBlock - 1) / kBlock) * (kBlock * D * 2);
     const __amdgpu_buffer_rsrc_t vA = __builtin_amdgcn_make_buffer_rsrc(
@@ -454,10 +461,10 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     auto step_main = [&](int t0, auto ic) __attribute__((always_inline)) {
       constexpr int I = decltype(ic)::value, R = I % 3;
       const int t = t0 + I;
-      if constexpr (I % 4 == 1) col_src(lds_u16(&ucol[(t + 3) >> 2]), dsrc);
+      if constexpr (I % 4 == 1) col_src(col_at((t + 3) >> 2), dsrc);
       issue_stage(dsrc, (I + 3) % 4, R);
       compute((R + 1) % 3, (I + 1) & 1, true, I & 1, vr[I & 1]);
-      if constexpr (I % 4 == 2) v_off = lds_u16(&ucol[(t + 2) >> 2]) * (kBlock * D);
+      if constexpr (I % 4 == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
       load_v((I + 2) % 4, vr[I & 1]);
       wait_vm<kSend / kWaves + NI>();
       barrier_lds();
@@ -468,12 +475,12 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       constexpr int I = decltype(ic)::value, R = I % 3;  // t % 6 == I
       const bool full = t + 3 < T;
       if (full) {
-        if (((t + 3) & 3) == 0) col_src(lds_u16(&ucol[(t + 3) >> 2]), dsrc);
+        if (((t + 3) & 3) == 0) col_src(col_at((t + 3) >> 2), dsrc);
         issue_stage(dsrc, (t + 3) & 3, R);
       }
       compute((R + 1) % 3, (I + 1) & 1, t + 1 < T, I & 1, vr[I & 1]);
       if (t + 2 < T) {
-        if (((t + 2) & 3) == 0) v_off = lds_u16(&ucol[(t + 2) >> 2]) * (kBlock * D);
+        if (((t + 2) & 3) == 0) v_off = col_at((t + 2) >> 2) * (kBlock * D);
         load_v((t + 2) & 3, vr[I & 1]);
       }
       if (full) wait_vm<kSend / kWaves + NI>();
@@ -481,13 +488,25 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       barrier_lds();
     };
 
+    for (int pass = 0; pass < n_pass; ++pass) {
+    const int r = pass ? pr : r_long;
+    if (64 * r + kRowsPerWg * rh >= n) continue;  // this row half lies past the sequence end
+    build_table(r);
+    rev = pass == 1;
+#pragma unroll
+    for (int u = 0; u < kSend / kWaves; ++u) sb[u] = __builtin_amdgcn_readfirstlane(sbeg[wave + kWaves * u]);
+    nu = __builtin_amdgcn_readfirstlane(nu_s);
+    T = 4 * nu;  // panels
+    const int row_base = 64 * r + kRowsPerWg * rh;
+#pragma unroll
+    for (int k = 0; k < NI; ++k) acc[k] = f32x16{};
     if (T > 0) {
       // prologue (T >= 4): panels 0, 1, 2 of the first column copied, V of
       // panels 0, 1 loaded, panel 0 mixed
-      col_src(lds_u16(&ucol[0]), dsrc);
+      col_src(col_at(0), dsrc);
 #pragma unroll
       for (int b = 0; b < kStages; ++b) issue_stage(dsrc, b, b);
-      v_off = lds_u16(&ucol[0]) * (kBlock * D);
+      v_off = col_at(0) * (kBlock * D);
       load_v(0, vr[0]);
       load_v(1, vr[1]);
       wait_vm<0>();
@@ -535,6 +554,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
         else reinterpret_cast<float*>(a.out)[o] = acc[k][v];
       }
     }
+    }  // pass
   };
   if (heads_here > 8) run(std::integral_constant<int, 6>{});
   else if (heads_here > 4) run(std::integral_constant<int, 4>{});
@@ -745,12 +765,13 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   }
   const int n_hg = (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg;
   const int hpg = (a.n_recv + n_hg - 1) / n_hg;
-  const int64_t units = (int64_t)nrb * a.vl.n_seqs;
+  const int n_pairs = (nrb + 1) / 2;  // block-rows R - 1 - p and p
+  const int64_t units = (int64_t)n_pairs * a.vl.n_seqs;
   const int64_t rounds = (units + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(rounds * kXcds * 2 * n_hg));
   {
     KernelTimer kt_("k_mapped_av_bsr", st);
-    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, nrb, n_hg, hpg);
+    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, n_pairs, n_hg, hpg);
   }
   return hipGetLastError();
 }
