@@ -5,11 +5,12 @@
 // rows of one block-row and a group of at most 12 receiver heads. It first
 // lists, in LDS, the block columns that any sender kept (ascending) and, per
 // column and sender, which stored block holds it. It then walks the key axis in
-// 16-key panels (four per 64-key block column) with a three-stage software
-// pipeline; in step t
-//   - the 32 senders' 32 x 16 pieces of panel t + 3 (one contiguous 1 KB run of
+// 16-key panels (four per 64-key block column) with a software pipeline; in
+// step t
+//   - the 32 senders' 32 x 16 pieces of panel t + 2 (one contiguous 1 KB run of
 //     a stored block's 16-column panel per sender, or a zero page for a sender
-//     that did not keep the block) are copied straight to LDS;
+//     that did not keep the block), loaded into registers in step t - 1, are
+//     written to LDS, and those of panel t + 3 are loaded;
 //   - the V operands of panel t + 2 are loaded into a ring of registers;
 //   - panel t + 1 is mixed on the matrix cores: D1[h, pos] = sum_j M[h, j]
 //     A_j[pos] for 16 positions is a 16x16x32 MFMA with M (split into bf16 high
@@ -40,7 +41,7 @@ constexpr int kKeysPerStep = 16;     // one panel
 constexpr int kSend = 32;            // senders per workgroup (n_send <= 32)
 constexpr int kSendStride = 544;     // bf16 per staged sender: 32 rows x 16 keys + 32 pad
 constexpr int kStageElems = kSend * kSendStride;
-constexpr int kStages = 3;           // sender stage ring: panel t + 1 read, t + 2 and t + 3 in flight
+constexpr int kStages = 2;           // sender stages: panel t + 1 read while panel t + 2 is written
 constexpr int kBH = 520;             // bf16 per head of a mixed panel: 32 rows x 16 keys + 8 pad
 constexpr int kBBuf = 16 * kBH;      // one mixed panel, 16 head slots (the mix's M rows)
 constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
@@ -136,13 +137,13 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
   return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const T*)p);
 }
 
-// Inside the pipelined loop every LDS access is written in asm with its own
-// wait: the compiler cannot tell which LDS bytes the in-flight direct-to-LDS
-// copies write, and would otherwise wait for all of them before any LDS access.
-// An asm statement that issues several reads from one address register marks
-// its outputs early-clobber ("=&v"): otherwise the compiler may give the first
-// read's destination the address register, and a read that returns before the
-// next one issues would overwrite the address the later reads use.
+// LDS accesses of the pipelined loop are written in asm, each statement issuing
+// its accesses and (for reads) waiting for them, so the LDS traffic of a step is
+// explicit. An asm statement that issues several reads from one address
+// register marks its outputs early-clobber ("=&v"): otherwise the compiler may
+// give the first read's destination the address register, and a read that
+// returns before the next one issues would overwrite the address the later
+// reads use.
 __device__ __forceinline__ int lds_u16(const uint16_t* p) {
   uint32_t v;
   asm volatile("ds_read_u16 %0, %1\n"
@@ -151,21 +152,6 @@ __device__ __forceinline__ int lds_u16(const uint16_t* p) {
                : "v"(lds_addr(p))
                : "memory");
   return __builtin_amdgcn_readfirstlane((int)v);
-}
-
-// Waits until at most N of this wave's global loads and copies are in flight.
-// Written with the builtin rather than asm so that the compiler's own wait
-// placement knows about it: otherwise, with direct-to-LDS copies and register
-// loads both outstanding, it cannot order them and waits for all of them before
-// the first use of any loaded register.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("" ::: "memory");
-  // s_waitcnt fields: vmcnt[3:0], expcnt[6:4] (7 = no wait), lgkmcnt[11:8] (15 = no
-  // wait), vmcnt[5:4] in bits 15:14
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-  asm volatile("" ::: "memory");
 }
 
 // grid (8 * ceil(units / 8) * 2 * n_hg), kThreads threads.
@@ -302,20 +288,26 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       ss.step[u] = kept ? 2 * kBlock * kPanel : 0;
     }
   };
-  // Copy panel jq (16 keys) of the column into stage buffer b: each sender's 1 KB
-  // piece goes straight to LDS, 16 B per lane (lane L fills row L / 2, half L % 2).
-  // Senders j with bit 3 set store row r at row position r ^ 1: the transposing
-  // reads of senders j and j + 8 then fall in different LDS banks. The source is a
-  // wave-uniform base plus a per-lane byte offset.
+  // Panel jq (16 keys) of the column: each sender's 1 KB piece is loaded into
+  // registers, 16 B per lane (lane L holds row L / 2, half L % 2), and written
+  // to a stage buffer. Senders j with bit 3 set store row r at row position
+  // r ^ 1: the transposing reads of senders j and j + 8 then fall in different
+  // LDS banks.
   const uint32_t loff0 = 16u * lane, loff1 = 16u * (lane ^ 2);
-  auto issue_stage = [&](const SendSrc& ss, int jq, int b) __attribute__((always_inline)) {
-    uint16_t* dst0 = &sbuf[b * kStageElems];
+  auto load_stage = [&](const SendSrc& ss, int jq, u32x4 (&S)[kSend / kWaves]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kSend / kWaves; ++u) {
-      const int j = wave + kWaves * u;  // (j >> 3) & 1 == u & 1
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ss.r[u], (__attribute__((address_space(3))) void*)(dst0 + j * kSendStride),
-                                               16, (u & 1) ? loff1 : loff0, jq * ss.step[u], 0, 0);
-    }
+    for (int u = 0; u < kSend / kWaves; ++u)  // sender wave + 8u: (j >> 3) & 1 == u & 1
+      S[u] = __builtin_amdgcn_raw_buffer_load_b128(ss.r[u], (u & 1) ? loff1 : loff0, jq * ss.step[u], 0);
+  };
+  static_assert(kSend / kWaves == 4 && kWaves * kSendStride * 2 == 8704, "the offsets below assume this geometry");
+  auto store_stage = [&](const u32x4 (&S)[kSend / kWaves], int b) __attribute__((always_inline)) {
+    asm volatile(
+        "ds_write_b128 %0, %1\n"
+        "ds_write_b128 %0, %2 offset:8704\n"
+        "ds_write_b128 %0, %3 offset:17408\n"
+        "ds_write_b128 %0, %4 offset:26112" ::"v"(lds_addr(&sbuf[b * kStageElems + wave * kSendStride]) + 16u * lane),
+        "v"(S[0]), "v"(S[1]), "v"(S[2]), "v"(S[3])
+        : "memory");
   };
   // LDS reads of one step, in one asm statement with one wait: the eight
   // transposing reads of the panel to mix (lane (p, q) gets senders 8q .. 8q + 7
@@ -447,44 +439,41 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       if (do_mix) mix_store(bbm, tr);
     };
 
-    // Step t (R = t % 3): copy panel t + 3 into stage R (panel t's, mixed in the
-    // previous step), mix panel t + 1, multiply panel t with the V operands in
-    // ring slot t % 2, then load V of panel t + 2 into that slot. A full step
-    // (t + 3 < T) issues 4 + NI global operations, so waiting until at most that
-    // many are in flight at its end completes every earlier step's: panel t + 2's
-    // copy before it is mixed, panel t + 1's V before it is multiplied.
+    u32x4 S[kSend / kWaves];  // the sender pieces of the next panel to stage
+
+    // Step t: write panel t + 2 (in S since step t - 1) to stage t % 2 (panel
+    // t's, mixed in step t - 1), load panel t + 3 into S, mix panel t + 1 (stage
+    // (t + 1) % 2) into mixed buffer (t + 1) % 2, multiply panel t (mixed buffer
+    // t % 2) with V slot t % 2, then load V of panel t + 2 into that slot. The
+    // compiler places the waits for the loaded registers itself.
     //
-    // Main loop: 12 steps per trip, all full, with the column changes at fixed
-    // steps (panel t + 3 starts a column when t % 4 == 1, panel t + 2 when
-    // t % 4 == 2), so the body has no branches and the compiler's own waits for
-    // the V registers stay exact.
+    // Main loop: 4 steps per trip, all full (t + 3 < T), with the column changes
+    // at fixed steps (panel t + 3 starts a column when t % 4 == 1, panel t + 2
+    // when t % 4 == 2).
     auto step_main = [&](int t0, auto ic) __attribute__((always_inline)) {
-      constexpr int I = decltype(ic)::value, R = I % 3;
+      constexpr int I = decltype(ic)::value;
       const int t = t0 + I;
-      if constexpr (I % 4 == 1) col_src(col_at((t + 3) >> 2), dsrc);
-      issue_stage(dsrc, (I + 3) % 4, R);
-      compute((R + 1) % 3, (I + 1) & 1, true, I & 1, vr[I & 1]);
-      if constexpr (I % 4 == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
-      load_v((I + 2) % 4, vr[I & 1]);
-      wait_vm<kSend / kWaves + NI>();
+      store_stage(S, I & 1);
+      if constexpr (I == 1) col_src(col_at((t + 3) >> 2), dsrc);
+      load_stage(dsrc, (I + 3) & 3, S);
+      compute((I + 1) & 1, (I + 1) & 1, true, I & 1, vr[I & 1]);
+      if constexpr (I == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
+      load_v((I + 2) & 3, vr[I & 1]);
       barrier_lds();
     };
-    // The last steps (fewer than 15 left): the same work under run-time tests.
-    // Stage, mixed buffer and V slot of step t follow t % 6 as in the main loop.
+    // The last steps (at most 6): the same work under run-time tests.
     auto step_tail = [&](int t, auto ic) __attribute__((always_inline)) {
-      constexpr int I = decltype(ic)::value, R = I % 3;  // t % 6 == I
-      const bool full = t + 3 < T;
-      if (full) {
-        if (((t + 3) & 3) == 0) col_src(col_at((t + 3) >> 2), dsrc);
-        issue_stage(dsrc, (t + 3) & 3, R);
+      constexpr int I = decltype(ic)::value;  // t % 4 == I
+      if (t + 2 < T) store_stage(S, I & 1);
+      if (t + 3 < T) {
+        if (I == 1) col_src(col_at((t + 3) >> 2), dsrc);
+        load_stage(dsrc, (I + 3) & 3, S);
       }
-      compute((R + 1) % 3, (I + 1) & 1, t + 1 < T, I & 1, vr[I & 1]);
+      compute((I + 1) & 1, (I + 1) & 1, t + 1 < T, I & 1, vr[I & 1]);
       if (t + 2 < T) {
-        if (((t + 2) & 3) == 0) v_off = col_at((t + 2) >> 2) * (kBlock * D);
-        load_v((t + 2) & 3, vr[I & 1]);
+        if (I == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
+        load_v((I + 2) & 3, vr[I & 1]);
       }
-      if (full) wait_vm<kSend / kWaves + NI>();
-      else wait_vm<0>();
       barrier_lds();
     };
 
@@ -501,43 +490,35 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
 #pragma unroll
     for (int k = 0; k < NI; ++k) acc[k] = f32x16{};
     if (T > 0) {
-      // prologue (T >= 4): panels 0, 1, 2 of the first column copied, V of
-      // panels 0, 1 loaded, panel 0 mixed
+      // prologue (T >= 4, one column at least): panels 0 and 1 staged, panel 2
+      // in S, V of panels 0 and 1 loaded, panel 0 mixed
       col_src(col_at(0), dsrc);
-#pragma unroll
-      for (int b = 0; b < kStages; ++b) issue_stage(dsrc, b, b);
       v_off = col_at(0) * (kBlock * D);
+      load_stage(dsrc, 0, S);
+      store_stage(S, 0);
+      load_stage(dsrc, 1, S);
       load_v(0, vr[0]);
       load_v(1, vr[1]);
-      wait_vm<0>();
       barrier_lds();
       u32x2 tr[8];
       read_mix_src(0, tr);
       mix_store(0, tr);
+      store_stage(S, 1);
+      load_stage(dsrc, 2, S);
       barrier_lds();
     }
     int t = 0;
-    for (; t + 14 < T; t += 12) {
+    for (; t + 6 < T; t += 4) {
       step_main(t, std::integral_constant<int, 0>{});
       step_main(t, std::integral_constant<int, 1>{});
       step_main(t, std::integral_constant<int, 2>{});
       step_main(t, std::integral_constant<int, 3>{});
-      step_main(t, std::integral_constant<int, 4>{});
-      step_main(t, std::integral_constant<int, 5>{});
-      step_main(t, std::integral_constant<int, 6>{});
-      step_main(t, std::integral_constant<int, 7>{});
-      step_main(t, std::integral_constant<int, 8>{});
-      step_main(t, std::integral_constant<int, 9>{});
-      step_main(t, std::integral_constant<int, 10>{});
-      step_main(t, std::integral_constant<int, 11>{});
     }
-    for (; t < T; t += 6) {  // t % 6 == 0 here
+    for (; t < T; t += 4) {  // t % 4 == 0 here
       step_tail(t, std::integral_constant<int, 0>{});
       if (t + 1 < T) step_tail(t + 1, std::integral_constant<int, 1>{});
       if (t + 2 < T) step_tail(t + 2, std::integral_constant<int, 2>{});
       if (t + 3 < T) step_tail(t + 3, std::integral_constant<int, 3>{});
-      if (t + 4 < T) step_tail(t + 4, std::integral_constant<int, 4>{});
-      if (t + 5 < T) step_tail(t + 5, std::integral_constant<int, 5>{});
     }
     // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
