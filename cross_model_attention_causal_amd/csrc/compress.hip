@@ -3,19 +3,28 @@
 // block-row and selects the blocks to keep; phase 2 recomputes only the kept
 // blocks and writes them. The dense map is never formed.
 //
-// Phase 1 (k_block_stats): per block-row, 8 waves sweep the key blocks (two
-// query tiles x four key phases). For every (query, key block) the online
-// softmax leaves a partial sum relative to the running max at that block; both
-// go to LDS. After the sweep the running statistics of the four key phases are
-// merged into each query's final (max, sum), and the mass of block c is
+// Both phases give a workgroup a group of G adjacent block-rows (G = 2, so 128
+// queries share every staged K block; phase 1 falls back to G = 1 when its
+// per-(query, block) table for two rows would not fit in LDS, above 128
+// block-rows). Its 8 waves are 2G query tiles of 32 queries x 8 / (2G) key
+// phases; each K round stages 4 key blocks and a wave takes 2G / 2 of them.
+//
+// Phase 1 (k_block_stats): for every (query, key block) the online softmax
+// leaves a partial sum relative to the running max at that block; log2 of the
+// absolute partial goes to LDS. After the sweep the running statistics of the
+// key phases are merged into each query's final (max, sum), and the mass of
+// block c is
 //   mass_c = sum_i partial_ic * 2^(max_ic - max_i) / sum_i
-// added over the 64 query rows in a fixed order. Selection (normalise by the
+// added over the 64 query rows of its block-row in a fixed order (four partial
+// sums of 16 rows, then combined pairwise). Selection (normalise by the
 // block-row total, order largest first with ties to the lower column, keep the
-// shortest prefix whose running sum reaches tau) runs in the same workgroup: a
-// bitonic sort in LDS and a sequential running sum.
+// shortest prefix whose running sum reaches tau) runs in the same workgroup:
+// every block's rank comes from wave-wide ballots over all weights, and one
+// wave scans the running sum.
 // Scan (k_bsr_scan): exclusive scan of kept counts -> row_ptr, nnz.
-// Phase 2 (k_block_extract): per block-row, recompute the kept blocks' scores,
-// p = 2^(t - lse2) and store bf16 blocks and their column indices.
+// Phase 2 (k_block_extract): the union of the group's kept columns is swept;
+// a wave recomputes the blocks its block-row kept, p = 2^(t - lse2), and
+// stores them as bf16 with their column indices.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -23,35 +32,36 @@
 
 namespace cma {
 
-// Work item of workgroup `id`: (head h, sequence s, block-row r). The hardware
-// deals workgroup ids round-robin over the 8 XCDs (id i runs on XCD i % 8, as
-// that XCD's (i / 8)-th workgroup). With enough (head, sequence) pairs they are
-// dealt the same way: an XCD walks the block-rows of one pair at a time, longest
-// first, and its L2 keeps that pair's K, which every block-row of the pair
-// re-reads. With few pairs (fewer than 2 per XCD) that would idle XCDs, so ids
-// then go pair by pair. Grid: pair_grid() workgroups.
-__device__ __forceinline__ bool pair_item(int id, int nrb, int n_seqs, int n_heads, int& h, int& s, int& r) {
+// Work item of workgroup `id`: (head h, sequence s, row group rg = block-rows
+// G rg .. G rg + G - 1). The hardware deals workgroup ids round-robin over the
+// 8 XCDs (id i runs on XCD i % 8, as that XCD's (i / 8)-th workgroup). With
+// enough (head, sequence) pairs they are dealt the same way: an XCD walks the
+// row groups of one pair at a time, longest first, and its L2 keeps that pair's
+// K, which every row group of the pair re-reads. With few pairs (fewer than 2
+// per XCD) that would idle XCDs, so ids then go pair by pair. Grid:
+// group_grid() workgroups.
+__device__ __forceinline__ bool group_item(int id, int ngr, int n_seqs, int n_heads, int& h, int& s, int& rg) {
   const int pairs = n_seqs * n_heads;
   int pair, j;
   if (pairs >= 2 * kXcds) {
     const int xcd = id % kXcds;
     j = id / kXcds;
-    pair = xcd + kXcds * (j / nrb);
+    pair = xcd + kXcds * (j / ngr);
   } else {
     j = id;
-    pair = id / nrb;
+    pair = id / ngr;
   }
   if (pair >= pairs) return false;
   h = pair / n_seqs;
   s = pair % n_seqs;
-  r = nrb - 1 - j % nrb;
+  rg = ngr - 1 - j % ngr;
   return true;
 }
 
-inline unsigned pair_grid(int nrb, int n_seqs, int n_heads) {
+inline unsigned group_grid(int ngr, int n_seqs, int n_heads) {
   const int64_t pairs = (int64_t)n_seqs * n_heads;
-  if (pairs < 2 * kXcds) return (unsigned)(pairs * nrb);
-  return (unsigned)(kXcds * ((pairs + kXcds - 1) / kXcds) * nrb);
+  if (pairs < 2 * kXcds) return (unsigned)(pairs * ngr);
+  return (unsigned)(kXcds * ((pairs + kXcds - 1) / kXcds) * ngr);
 }
 
 // Per-sub-step K pipeline shared by both phases. A sub-step is one feature half
@@ -100,20 +110,21 @@ __device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* 
   }
 }
 
-// Block statistics and selection for one (head, sequence, block-row).
-// Dynamic LDS: two K stages, then LP[64][R + 1] = log2 of each (query, block)
+// Block statistics and selection for one (head, sequence, row group).
+// Dynamic LDS: two K stages, then LP[64 G][LPS] = log2 of each (query, block)
 // partial sum in absolute terms (running max + log2 of the partial), so that
 // mass_c = sum_i 2^(LP[i][c] - lse_i) once the row's lse is known.
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
+  constexpr int QT = 2 * G, KP = 8 / QT, BPW = 4 / KP;  // query tiles, key phases, blocks per wave and round
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   // row stride of LP: odd, so the 32 query rows written for one block fall in
   // distinct LDS banks
-  const int LPS = a.nrb_max + 1;
+  const int LPS = (a.nrb_max + 1) | 1;
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   float* LP = dyn + 2 * (kStageBytes / 4);
-  __shared__ float sm[4][64], sl[4][64];
-  __shared__ float lse_s[64];
+  __shared__ float sm[KP][64 * G], sl[KP][64 * G];
+  __shared__ float lse_s[64 * G];
   __shared__ float mass[kMaxBlockRows];
   __shared__ float wts[kMaxBlockRows];
   __shared__ int order[kMaxBlockRows];
@@ -121,14 +132,18 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   __shared__ int kcount;
   __shared__ float total_s;
 
-  int h, s, r;
-  if (!pair_item(blockIdx.x, a.nrb_max, a.vl.n_seqs, a.n_heads, h, s, r)) return;
+  int h, s, rg;
+  if (!group_item(blockIdx.x, (a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads, h, s, rg)) return;
   const int32_t n = seq_len_q(a.vl, s);
-  if (!seq_ok(a.vl, s, n, n) || 64 * r >= n) return;
+  const int nrb = (n + kBlock - 1) / kBlock, r0 = G * rg;
+  if (!seq_ok(a.vl, s, n, n) || r0 >= nrb) return;
+  const int r_last = min(r0 + G - 1, nrb - 1);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int qt = wave & 1, kp = wave >> 1;
-  const int iloc = 32 * qt + (lane & 31);
-  const int i = 64 * r + iloc;
+  const int qt = wave % QT, kp = wave / QT;
+  const int rq = r0 + qt / 2;                             // the tile's block-row
+  const int cmax = rq <= r_last ? rq : -1;                // last key block the tile computes
+  const int qloc = 64 * (qt / 2) + 32 * (qt & 1) + (lane & 31);  // query within the group
+  const int i = 64 * r0 + qloc;
   const bool valid = i < n;
   const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, n - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
@@ -137,46 +152,58 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
 
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);
-  f32x16 acc[2];
+  f32x16 acc[BPW][2];
   float m = -INFINITY, l = 0.0f;
-  // Round k covers blocks 4k .. 4k + 3, wave (qt, kp) takes block 4k + kp.
   // Blocks strictly between column 0 (sink bias) and the diagonal (causal mask)
   // take the lean update on raw scores.
   const bool raw_ok = scale_l2 > 0.0f;
+  auto finish = [&](const f32x16 (&x)[2], int c) __attribute__((always_inline)) {
+    float part;
+    if (raw_ok && c != 0 && c != rq) {
+      part = online_update_raw(x, scale_l2, m, l);
+    } else {
+      float t[32];
+      logits_block(t, x, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+      part = online_update(t, m, l);
+    }
+    if (lane < 32) LP[qloc * LPS + c] = m + log2f_fast(part);
+  };
+  // Round k stages blocks 4k .. 4k + 3; the wave takes blocks 4k + kp + KP j.
+  // Both blocks' products are issued before either softmax update, so the
+  // matrix cores work on the second while the first one's update runs.
   kstage_pipeline<D>(
-      stage, kseq, n, (r + 4) / 4, [&](int c) { return 64 * min(c, r); },
+      stage, kseq, n, (r_last + 4) / 4, [&](int c) { return 64 * min(c, r_last); },
       [&](int k, const uint8_t* buf, auto fh) {
         constexpr int FH = decltype(fh)::value;
-        const int c = 4 * k + kp;
-        if (c > r) return;
-        if (FH == 0) acc[0] = acc[1] = f32x16{};
-        kstage_mma<D, FH>(acc, buf + kp * kStageBlockBytes, qop);
-        if (FH != D / 64 - 1) return;
-        float part;
-        if (raw_ok && c != 0 && c != r) {
-          part = online_update_raw(acc, scale_l2, m, l);
-        } else {
-          float t[32];
-          logits_block(t, acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
-          part = online_update(t, m, l);
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          if (4 * k + kp + KP * j > cmax) break;
+          if (FH == 0) acc[j][0] = acc[j][1] = f32x16{};
+          kstage_mma<D, FH>(acc[j], buf + (kp + KP * j) * kStageBlockBytes, qop);
         }
-        if (lane < 32) LP[iloc * LPS + c] = m + log2f_fast(part);
+        if (FH != D / 64 - 1) return;
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          const int c = 4 * k + kp + KP * j;
+          if (c > cmax) break;
+          finish(acc[j], c);
+        }
       });
   if (lane < 32) {
-    sm[kp][iloc] = m;
-    sl[kp][iloc] = l;
+    sm[kp][qloc] = m;
+    sl[kp][qloc] = l;
   }
   __syncthreads();
-  if (tid < 64) {
+  if (tid < 64 * G) {
     const int q = tid;
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][q]);
+    for (int w = 0; w < KP; ++w) M = fmaxf(M, sm[w][q]);
     float L = 0.0f;
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < KP; ++w)
       if (sm[w][q] != -INFINITY) L += sl[w][q] * exp2f_fast(sm[w][q] - M);
     const float lse = M + log2f_fast(L);
     lse_s[q] = lse;
-    const int iq = 64 * r + q;
+    const int iq = 64 * r0 + q;
     if (iq < n) {
       const int64_t tok = (int64_t)h * a.vl.total_q + a.vl.cu_q[s] + iq;
       a.lse2[tok] = lse;
@@ -186,89 +213,112 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
       }
     }
   }
-  if (tid < kWords) kept[tid] = 0u;
-  __syncthreads();
-  // mass_c over the valid rows, in row order
-  const int nrows = min(64, n - 64 * r);
-  const int nb = r + 1;
-  for (int c = tid; c < nb; c += 512) {
-    float x = 0.0f;
-    for (int q = 0; q < nrows; ++q) x += exp2f_fast(LP[q * LPS + c] - lse_s[q]);
-    mass[c] = x;
-  }
-  __syncthreads();
 
   int32_t roff;
   int64_t tri_off;
   block_offsets(a.vl, s, roff, tri_off);
-  const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
-  if (a.block_mass) {
-    int32_t r_all;
-    int64_t n_tri;  // blocks per head over all sequences
-    block_offsets(a.vl, a.vl.n_seqs, r_all, n_tri);
-    float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * (r + 1) / 2;
-    for (int c = tid; c < nb; c += 512) bm[c] = mass[c];
-  }
-  if (a.tau >= 1.0f) {
-    for (int c = tid; c < nb; c += 512) atomicOr(&kept[c >> 5], 1u << (c & 31));
-    if (tid == 0) kcount = nb;
-  } else {
-    // total mass: one wave, strided partial sums then a fixed butterfly
-    if (wave == 0) {
-      float x = 0.0f;
-      for (int c = lane; c < nb; c += 64) x += mass[c];
-      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-      if (lane == 0) total_s = x;
-    }
-    __syncthreads();
-    const float total = total_s;
-    for (int c = tid; c < nb; c += 512) wts[c] = mass[c] / total;
-    __syncthreads();
-    // rank of block c in the order weight descending, column ascending
-    for (int c = tid; c < nb; c += 512) {
-      const float wc = wts[c];
-      int rank = 0;
-      for (int c2 = 0; c2 < nb; ++c2) {
-        const float w2 = wts[c2];
-        rank += (w2 > wc) || (w2 == wc && c2 < c);
+  for (int gr = 0; gr < G; ++gr) {
+    const int r = r0 + gr;
+    if (r > r_last) break;
+    __syncthreads();  // lse_s is written; the previous row's readers of kept / kcount are done
+    if (tid < kWords) kept[tid] = 0u;
+    // mass_c over the valid rows: four consecutive threads take rows 16 part ..
+    // + 15 of block c, then add their partials in a fixed order
+    const int nrows = min(64, n - 64 * r);
+    const int nb = r + 1;
+    const float* LPr = LP + 64 * gr * LPS;
+    const float* lser = lse_s + 64 * gr;
+    for (int x0 = 0; x0 < 4 * nb; x0 += 512) {
+      const int x = x0 + tid, c = x >> 2, part = x & 3;
+      float y = 0.0f;
+      if (c < nb) {
+        const int q1 = min(16 * part + 16, nrows);
+        for (int q = 16 * part; q < q1; ++q) y += exp2f_fast(LPr[q * LPS + c] - lser[q]);
       }
-      order[rank] = c;
+      y += __shfl_xor(y, 1, 64);  // (p0 + p1), (p2 + p3)
+      y += __shfl_xor(y, 2, 64);  // (p0 + p1) + (p2 + p3)
+      if (c < nb && part == 0) mass[c] = y;
     }
     __syncthreads();
-    // running sum in that order (wave 0: 4 consecutive ranks per lane, then a
-    // wave-wide inclusive scan of the lane totals); keep the shortest prefix
-    // whose sum reaches tau
-    if (wave == 0) {
-      float cum[4];
-      float run = 0.0f;
+
+    const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
+    if (a.block_mass) {
+      int32_t r_all;
+      int64_t n_tri;  // blocks per head over all sequences
+      block_offsets(a.vl, a.vl.n_seqs, r_all, n_tri);
+      float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * (r + 1) / 2;
+      for (int c = tid; c < nb; c += 512) bm[c] = mass[c];
+    }
+    if (a.tau >= 1.0f) {
+      for (int c = tid; c < nb; c += 512) atomicOr(&kept[c >> 5], 1u << (c & 31));
+      if (tid == 0) kcount = nb;
+    } else {
+      // total mass: one wave, strided partial sums then a fixed butterfly
+      if (wave == 0) {
+        float x = 0.0f;
+        for (int c = lane; c < nb; c += 64) x += mass[c];
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+        if (lane == 0) total_s = x;
+      }
+      __syncthreads();
+      const float total = total_s;
+      for (int c = tid; c < nb; c += 512) wts[c] = mass[c] / total;
+      __syncthreads();
+      // rank of block c in the order weight descending, column ascending: wave w
+      // takes blocks w, w + 8, ...; lane L holds the weights of blocks L + 64 j and
+      // each comparison is one ballot over the wave
+      {
+        float w2[kMaxBlockRows / 64];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int x = 4 * lane + e;
-        run += x < nb ? wts[order[x]] : 0.0f;
-        cum[e] = run;
-      }
-      float pre = run;
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(pre, off, 64);
-        if (lane >= off) pre += y;
-      }
-      const float before = pre - run;
-      int first = 4 * 64;
+        for (int j = 0; j < kMaxBlockRows / 64; ++j) w2[j] = lane + 64 * j < nb ? wts[lane + 64 * j] : -INFINITY;
+        for (int c = wave; c < nb; c += 8) {
+          const float wc = wts[c];
+          int rank = 0;
 #pragma unroll
-      for (int e = 3; e >= 0; --e)
-        if (4 * lane + e < nb && before + cum[e] >= a.tau) first = 4 * lane + e;
-      for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
-      if (lane == 0) kcount = first < nb ? first + 1 : nb;
+          for (int j = 0; j < kMaxBlockRows / 64; ++j) {
+            const int c2 = lane + 64 * j;
+            const bool ahead = c2 < nb && (w2[j] > wc || (w2[j] == wc && c2 < c));
+            rank += __popcll(__ballot(ahead));
+          }
+          if (lane == 0) order[rank] = c;
+        }
+      }
+      __syncthreads();
+      // running sum in that order (wave 0: 4 consecutive ranks per lane, then a
+      // wave-wide inclusive scan of the lane totals); keep the shortest prefix
+      // whose sum reaches tau
+      if (wave == 0) {
+        float cum[4];
+        float run = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 4 * lane + e;
+          run += x < nb ? wts[order[x]] : 0.0f;
+          cum[e] = run;
+        }
+        float pre = run;
+        for (int off = 1; off < 64; off <<= 1) {
+          const float y = __shfl_up(pre, off, 64);
+          if (lane >= off) pre += y;
+        }
+        const float before = pre - run;
+        int first = 4 * 64;
+#pragma unroll
+        for (int e = 3; e >= 0; --e)
+          if (4 * lane + e < nb && before + cum[e] >= a.tau) first = 4 * lane + e;
+        for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+        if (lane == 0) kcount = first < nb ? first + 1 : nb;
+      }
+      __syncthreads();
+      for (int x = tid; x < kcount; x += 512) {
+        const int c = order[x];
+        atomicOr(&kept[c >> 5], 1u << (c & 31));
+      }
     }
     __syncthreads();
-    for (int x = tid; x < kcount; x += 512) {
-      const int c = order[x];
-      atomicOr(&kept[c >> 5], 1u << (c & 31));
-    }
+    if (tid < kWords) a.kept[g * kWords + tid] = kept[tid];
+    if (tid == 0) a.counts[g] = kcount;
   }
-  __syncthreads();
-  if (tid < kWords) a.kept[g * kWords + tid] = kept[tid];
-  if (tid == 0) a.counts[g] = kcount;
 }
 
 // Exclusive scan of the kept counts (one workgroup). Deterministic (integers).
@@ -299,106 +349,139 @@ __global__ __launch_bounds__(1024) void k_bsr_scan(const int32_t* counts, int64_
   }
 }
 
-// Extraction of the kept blocks of one (head, sequence, block-row): blocks are
-// taken 4 per round from the column list, wave (qt, kp) computing block 4k + kp
-// for its 32 query rows from the staged K.
+// Extraction of the kept blocks of one (head, sequence, row group of 2
+// block-rows): the union of the two rows' kept columns is swept 4 columns per
+// round; wave (qt, kp) recomputes, for its 32 query rows, the columns
+// 4k + kp and 4k + kp + 2 of round k that its block-row kept.
 template <int D>
 __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
+  constexpr int G = 2, QT = 4, KP = 2, BPW = 2;
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
-  __shared__ int cols[kMaxBlockRows];
-  __shared__ int ncols;
-  int h, s, r;
-  if (!pair_item(blockIdx.x, a.nrb_max, a.vl.n_seqs, a.n_heads, h, s, r)) return;
+  __shared__ int ucols[kMaxBlockRows];     // kept columns of either row, ascending
+  __shared__ int bidx[G][kMaxBlockRows];   // block index of union entry x in row gr, or -1
+  __shared__ int nu_s;
+  int h, s, rg;
+  if (!group_item(blockIdx.x, (a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads, h, s, rg)) return;
   const int32_t n = seq_len_q(a.vl, s);
-  if (!seq_ok(a.vl, s, n, n) || 64 * r >= n) return;
+  const int nrb = (n + kBlock - 1) / kBlock, r0 = G * rg;
+  if (!seq_ok(a.vl, s, n, n) || r0 >= nrb) return;
   if ((int64_t)a.nnz[0] > a.capacity) return;
+  const int r_last = min(r0 + G - 1, nrb - 1);
   int32_t roff;
   int64_t tri_off;
   block_offsets(a.vl, s, roff, tri_off);
-  const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    // column list in ascending order: one word of the kept mask per lane step
-    int k = 0;
-    for (int w = 0; w < kWords; ++w) {
-      const uint32_t bits = a.kept[g * kWords + w];
-      const int lane = tid;
-      if (lane < 32 && (bits >> lane) & 1u) cols[k + __builtin_popcount(bits & ((1u << lane) - 1u))] = 32 * w + lane;
-      k += __builtin_popcount(bits);
+  const int64_t g0 = (int64_t)h * a.n_block_rows + roff + r0;  // row r0; row r0 + 1 is g0 + 1
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (wave == 0) {
+    // union of the kept masks in ascending column order, each row's rank of a
+    // column among its own kept columns, and the rows' column indices
+    const bool has1 = r0 + 1 <= r_last;
+    const int64_t p0 = a.row_ptr[g0], p1 = has1 ? a.row_ptr[g0 + 1] : 0;
+    int nu = 0, k0 = 0, k1 = 0;
+    for (int c0 = 0; c0 < kMaxBlockRows; c0 += 64) {
+      const int c = c0 + lane, w = c >> 5;
+      const bool b0 = (a.kept[g0 * kWords + w] >> (c & 31)) & 1u;
+      const bool b1 = has1 && ((a.kept[(g0 + 1) * kWords + w] >> (c & 31)) & 1u);
+      const uint64_t below = (1ull << lane) - 1ull;
+      const uint64_t mu = __ballot(b0 || b1), m0 = __ballot(b0), m1 = __ballot(b1);
+      const int x = nu + __popcll(mu & below), i0 = k0 + __popcll(m0 & below), i1 = k1 + __popcll(m1 & below);
+      if (b0 || b1) {
+        ucols[x] = c;
+        bidx[0][x] = b0 ? i0 : -1;
+        bidx[1][x] = b1 ? i1 : -1;
+      }
+      if (b0) a.col_idx[p0 + i0] = c;
+      if (b1) a.col_idx[p1 + i1] = c;
+      nu += __popcll(mu);
+      k0 += __popcll(m0);
+      k1 += __popcll(m1);
     }
-    if (tid == 0) ncols = k;
+    if (lane == 0) nu_s = nu;
   }
   __syncthreads();
-  const int nc = ncols;
-  if (nc == 0) return;
-  for (int x = tid; x < nc; x += 512) a.col_idx[a.row_ptr[g] + x] = cols[x];
-  const int wave = tid >> 6, lane = tid & 63;
-  const int qt = wave & 1, kp = wave >> 1;
-  const int iloc = 32 * qt + (lane & 31);
-  const int i = 64 * r + iloc;
-  const bool valid = i < n;
+  const int nu = nu_s;
+  if (nu == 0) return;
+  const int qt = wave % QT, kp = wave / QT, gr = qt / 2;
+  const int rq = r0 + gr;                      // the tile's block-row
+  const bool tile_ok = rq <= r_last;
+  const int iloc = 32 * (qt & 1) + (lane & 31);
+  const int i = 64 * rq + iloc;
+  const bool valid = tile_ok && i < n;
   const int half = lane >> 5;
   const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, n - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
   const float scale_l2 = a.scale[h] * kLog2e;
   const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
   const float lse = valid ? a.lse2[(int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i] : 0.0f;
-  const int64_t base = a.row_ptr[g];
+  const int64_t base = tile_ok ? a.row_ptr[g0 + gr] : 0;
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);
-  f32x16 acc[2];
+  f32x16 acc[BPW][2];
   const bool raw_ok = scale_l2 > 0.0f;
+  // block index (in this tile's row) of union entry x, or -1 (not kept, or past the end)
+  auto blk_of = [&](int x) __attribute__((always_inline)) {
+    return (tile_ok && x < nu) ? __builtin_amdgcn_readfirstlane(bidx[gr][x]) : -1;
+  };
+  // p = 2^(logit - lse) in the accumulators (0 for rows past the end), stored as
+  // bf16 into block b of the row
+  auto finish = [&](f32x16 (&x)[2], int c, int b) __attribute__((always_inline)) {
+    if (raw_ok && c != 0 && c != rq) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[kt][v] = exp2f_fast(fmaf(x[kt][v], scale_l2, -lse));
+    } else {
+      logits_inplace(x, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) x[kt][v] = exp2f_fast(x[kt][v] - lse);
+    }
+    if (!valid) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) x[kt] = f32x16{};
+    }
+    // Lane (query, half) holds keys 32kt + 8g + 4half + 0..3 for g = 0..3. One
+    // exchange with the partner lane (lane ^ 32) per pair of groups leaves lane
+    // half h with the 8 consecutive keys 32kt + 16g2 + 8h .. +7, so that each
+    // store writes 16 bytes and one instruction fills a whole 1 KB run of a
+    // panel (32 rows x 16 keys).
+    uint16_t* blk = a.vals + (base + b) * (int64_t)(kBlock * kBlock);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int v0 = 8 * g2;  // elements v0..v0+3 (group 2g2), v0+4..v0+7 (group 2g2+1)
+        const uint32_t x0 = pack2bf(x[kt][v0], x[kt][v0 + 1]);
+        const uint32_t x1 = pack2bf(x[kt][v0 + 2], x[kt][v0 + 3]);
+        const uint32_t y0 = pack2bf(x[kt][v0 + 4], x[kt][v0 + 5]);
+        const uint32_t y1 = pack2bf(x[kt][v0 + 6], x[kt][v0 + 7]);
+        // lanes 0-31 keep x and receive the partner's x; lanes 32-63 receive
+        // the partner's y and keep their own y
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+        const int panel = 2 * kt + g2;
+        *reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half) = w;
+      }
+  };
   kstage_pipeline<D>(
-      stage, kseq, n, (nc + 3) / 4, [&](int x) { return 64 * cols[min(x, nc - 1)]; },
+      stage, kseq, n, (nu + 3) / 4, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
       [&](int k, const uint8_t* buf, auto fh) {
         constexpr int FH = decltype(fh)::value;
-        const int x = 4 * k + kp;
-        if (x >= nc) return;
-        if (FH == 0) acc[0] = acc[1] = f32x16{};
-        kstage_mma<D, FH>(acc, buf + kp * kStageBlockBytes, qop);
+        int b[BPW];
+#pragma unroll
+        for (int j = 0; j < BPW; ++j) {
+          b[j] = blk_of(4 * k + kp + KP * j);
+          if (b[j] < 0) continue;
+          if (FH == 0) acc[j][0] = acc[j][1] = f32x16{};
+          kstage_mma<D, FH>(acc[j], buf + (kp + KP * j) * kStageBlockBytes, qop);
+        }
         if (FH != D / 64 - 1) return;
-        const int c = cols[x];
-        // p = 2^(logit - lse) in the accumulator registers (0 for rows past the end)
-        if (raw_ok && c != 0 && c != r) {
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(fmaf(acc[kt][v], scale_l2, -lse));
-        } else {
-          logits_inplace(acc, 64 * c, valid ? i : -1, scale_l2, bias_l2);
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(acc[kt][v] - lse);
-        }
-        if (!valid) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) acc[kt] = f32x16{};
-        }
-        // Lane (query, half) holds keys 32kt + 8g + 4half + 0..3 for g = 0..3. One
-        // exchange with the partner lane (lane ^ 32) per pair of groups leaves lane
-        // half h with the 8 consecutive keys 32kt + 16g2 + 8h .. +7, so that each
-        // store writes 16 bytes and one instruction fills a whole 1 KB run of a
-        // panel (32 rows x 16 keys).
-        uint16_t* blk = a.vals + (base + x) * (int64_t)(kBlock * kBlock);
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2) {
-            const int v0 = 8 * g2;  // elements v0..v0+3 (group 2g2), v0+4..v0+7 (group 2g2+1)
-            const uint32_t x0 = pack2bf(acc[kt][v0], acc[kt][v0 + 1]);
-            const uint32_t x1 = pack2bf(acc[kt][v0 + 2], acc[kt][v0 + 3]);
-            const uint32_t y0 = pack2bf(acc[kt][v0 + 4], acc[kt][v0 + 5]);
-            const uint32_t y1 = pack2bf(acc[kt][v0 + 6], acc[kt][v0 + 7]);
-            // lanes 0-31 keep x and receive the partner's x; lanes 32-63 receive
-            // the partner's y and keep their own y
-            const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-            const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
-            const int panel = 2 * kt + g2;
-            *reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half) = w;
-          }
+        for (int j = 0; j < BPW; ++j)
+          if (b[j] >= 0) finish(acc[j], ucols[4 * k + kp + KP * j], b[j]);
       });
 }
 
@@ -422,12 +505,22 @@ size_t compress_ws_bytes(int32_t n_heads, int32_t n_block_rows, int64_t total_q)
 
 template <int D>
 static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
-  dim3 grid(pair_grid(a.nrb_max, a.vl.n_seqs, a.n_heads));
-  const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * (a.nrb_max + 1) * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_stats<D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // phase 1 takes two block-rows per workgroup when their per-(query, block)
+  // table fits in LDS next to the K stages, else one
+  const bool two = a.nrb_max <= 128;
+  const int G = two ? 2 : 1;
+  const int lps = (a.nrb_max + 1) | 1;
+  const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * G * lps * sizeof(float);
+  const dim3 grid(group_grid((a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads));
+  const void* fn = two ? reinterpret_cast<const void*>(&k_block_stats<D, 2>)
+                       : reinterpret_cast<const void*>(&k_block_stats<D, 1>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  { KernelTimer kt_("k_block_stats", st); hipLaunchKernelGGL((k_block_stats<D>), grid, dim3(512), lds, st, a); }
+  {
+    KernelTimer kt_("k_block_stats", st);
+    if (two) hipLaunchKernelGGL((k_block_stats<D, 2>), grid, dim3(512), lds, st, a);
+    else hipLaunchKernelGGL((k_block_stats<D, 1>), grid, dim3(512), lds, st, a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
@@ -441,7 +534,8 @@ static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_extract<D>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_x);
   if (e != hipSuccess) return e;
-  { KernelTimer kt_("k_block_extract", st); hipLaunchKernelGGL((k_block_extract<D>), grid, dim3(512), lds_x, st, a); }
+  const dim3 grid_x(group_grid((a.nrb_max + 1) / 2, a.vl.n_seqs, a.n_heads));
+  { KernelTimer kt_("k_block_extract", st); hipLaunchKernelGGL((k_block_extract<D>), grid_x, dim3(512), lds_x, st, a); }
   return hipGetLastError();
 }
 

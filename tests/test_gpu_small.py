@@ -225,6 +225,51 @@ def test_block_compress_small(cma, tau):
     say(f"  nnz={nnz} oracle={ref['nnz']} exempt rows differing={exempt}")
 
 
+def test_block_compress_longest_sequence(cma):
+    """A 16384-token sequence (256 block-rows, the longest the block table
+    holds) beside a short one: sampled block-rows against the oracle."""
+    lens = [16384, 300]
+    H, tau = 2, 0.95
+    say(f"block_compress lens={lens} H={H} tau={tau}")
+    x = synth.attention_inputs(311, H, lens, d=128)
+    vl = cma.Varlen(x["cu_q"], x["cu_k"])
+    out = cma.block_compress(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_f32(x["scale"]), dev_f32(x["bias"]),
+                             vl, tau, want_mass=True, want_stats=True)
+    torch.cuda.synchronize()
+    nnz = int(out["nnz"].item())
+    row_ptr = host64(out["row_ptr"]).astype(np.int64)
+    col = host64(out["col_idx"][:nnz]).astype(np.int64)
+    mass = host64(out["block_mass"])
+    stats = host64(out["row_stats"])
+    R = [(n + 63) // 64 for n in lens]
+    tri0 = lambda r: r * (r + 1) // 2
+    checked = exempt = 0
+    for h in range(H):
+        for s, rows in ((0, (0, 1, 127, 128, 200, 254, 255)), (1, range(R[1]))):
+            a, b = int(x["cu_q"][s]), int(x["cu_q"][s + 1])
+            q, k = f64(x["q"][h, a:b]), f64(x["k"][h, a:b])
+            g0 = h * sum(R) + sum(R[:s])
+            m0 = h * sum(tri0(r) for r in R) + sum(tri0(r) for r in R[:s])  # mass offset of this (h, s)
+            for r in rows:
+                ref = oracle.compress_block_row(q, k, x["scale"][h], x["bias"][h], r, tau)
+                mrow = mass.reshape(-1)[m0 + tri0(r): m0 + tri0(r) + r + 1]
+                assert rel_l2(mrow, ref["masses"]) <= 1e-5, (h, s, r)
+                rr = slice(a + 64 * r, min(a + 64 * r + 64, b))
+                assert np.max(np.abs(stats[h, rr, 0] - ref["m"])) <= 1e-4
+                assert rel_l2(stats[h, rr, 1], ref["l"]) <= 1e-5
+                g = g0 + r
+                cs = list(col[row_ptr[g]: row_ptr[g + 1]])
+                if ref["margin"] > 1e-4:
+                    assert cs == ref["kept"], (h, s, r)
+                if cs == ref["kept"]:
+                    v = blocks_from_panels(host64(out["vals"][row_ptr[g]: row_ptr[g + 1]]))
+                    assert rel_l2(v, ref["blocks"]) <= 1e-2
+                    checked += 1
+                else:
+                    exempt += 1
+    say(f"  {checked} sampled block-rows equal, {exempt} exempt (margin <= 1e-4)")
+
+
 # ------------------------------------------------------------------ mapped_av block-sparse
 @pytest.mark.parametrize("n_recv,v_layout", [(24, "token"), (7, "token"), (24, "key"), (24, "tiled"), (7, "tiled")])
 def test_mapped_av_bsr_small(cma, n_recv, v_layout):
