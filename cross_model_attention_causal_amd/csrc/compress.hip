@@ -110,6 +110,49 @@ __device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* 
   }
 }
 
+// Whole-block K pipeline: a sub-step stages two key blocks with all their
+// features (block j in slots j * D / 64 .. + D / 64 - 1, one 64-feature half per
+// slot; with D = 64 slots 2 and 3 repeat slots 0 and 1), so that a wave finishes
+// one block per sub-step. Depth 2, as kstage_pipeline: the loads of sub-step
+// u + 2 are in flight while sub-step u is computed.
+template <int D>
+__device__ __forceinline__ void kstage_load2(KStageRegs& rg, const uint16_t* __restrict__ kseq, int nk, int key0a,
+                                             int key0b) {
+  constexpr int FHN = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = 8 * wave + (lane >> 3), s = lane & 7;
+  const int ch = s ^ ((m >> 1) & 7);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int blk = FHN == 2 ? (b >> 1) : (b & 1), fh = FHN == 2 ? (b & 1) : 0;
+    const int key = min((blk ? key0b : key0a) + m, nk - 1);
+    rg.x[b] = ldg16(kseq + (int64_t)key * D + 64 * fh + 8 * ch);
+  }
+}
+
+template <int D, typename Key0, typename Body>
+__device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk, int nsub,
+                                                 Key0 key0_of, Body body) {
+  auto load = [&](KStageRegs& rg, int u) { kstage_load2<D>(rg, kseq, nk, key0_of(2 * u), key0_of(2 * u + 1)); };
+  auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
+    load(mine, min(u + 2, nsub - 1));  // clamped past the end: harmless, keeps the control flow straight
+    body(u, stage + (u & 1) * kStageBytes);
+    kstage_store(stage + ((u + 1) & 1) * kStageBytes, next);
+    barrier_lds();
+  };
+  if (nsub == 0) return;
+  KStageRegs r0, r1;
+  load(r0, 0);
+  load(r1, min(1, nsub - 1));
+  kstage_store(stage, r0);
+  barrier_lds();
+  for (int u = 0; u < nsub; u += 2) {
+    iter(r0, r1, u);
+    if (u + 1 >= nsub) break;
+    iter(r1, r0, u + 1);
+  }
+}
+
 // Block statistics and selection for one (head, sequence, row group).
 // Dynamic LDS: two K stages, then LP[64 G][LPS] = log2 of each (query, block)
 // partial sum in absolute terms (running max + log2 of the partial), so that
@@ -157,38 +200,57 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   // Blocks strictly between column 0 (sink bias) and the diagonal (causal mask)
   // take the lean update on raw scores.
   const bool raw_ok = scale_l2 > 0.0f;
-  auto finish = [&](const f32x16 (&x)[2], int c) __attribute__((always_inline)) {
+  auto finish = [&](f32x16 (&x)[2], int c) __attribute__((always_inline)) {
     float part;
     if (raw_ok && c != 0 && c != rq) {
       part = online_update_raw(x, scale_l2, m, l);
     } else {
-      float t[32];
-      logits_block(t, x, 64 * c, valid ? i : -1, scale_l2, bias_l2);
-      part = online_update(t, m, l);
+      logits_inplace(x, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+      part = online_update_acc(x, m, l);
     }
     if (lane < 32) LP[qloc * LPS + c] = m + log2f_fast(part);
   };
   // Round k stages blocks 4k .. 4k + 3; the wave takes blocks 4k + kp + KP j.
-  // Both blocks' products are issued before either softmax update, so the
-  // matrix cores work on the second while the first one's update runs.
-  kstage_pipeline<D>(
-      stage, kseq, n, (r_last + 4) / 4, [&](int c) { return 64 * min(c, r_last); },
-      [&](int k, const uint8_t* buf, auto fh) {
-        constexpr int FH = decltype(fh)::value;
-#pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-          if (4 * k + kp + KP * j > cmax) break;
-          if (FH == 0) acc[j][0] = acc[j][1] = f32x16{};
-          kstage_mma<D, FH>(acc[j], buf + (kp + KP * j) * kStageBlockBytes, qop);
-        }
-        if (FH != D / 64 - 1) return;
-#pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-          const int c = 4 * k + kp + KP * j;
-          if (c > cmax) break;
-          finish(acc[j], c);
-        }
-      });
+  if constexpr (BPW == 1) {
+    kstage_pipeline<D>(
+        stage, kseq, n, (r_last + 4) / 4, [&](int c) { return 64 * min(c, r_last); },
+        [&](int k, const uint8_t* buf, auto fh) {
+          constexpr int FH = decltype(fh)::value;
+          const int c = 4 * k + kp;
+          if (c > cmax) return;
+          if (FH == 0) acc[0][0] = acc[0][1] = f32x16{};
+          kstage_mma<D, FH>(acc[0], buf + kp * kStageBlockBytes, qop);
+          if (FH == D / 64 - 1) finish(acc[0], c);
+        });
+  } else {
+    // Two whole blocks per sub-step (kstage2_pipeline): the wave computes block
+    // 2u + kp of sub-step u and runs its softmax update in sub-step u + 1, beside
+    // that sub-step's products, so every sub-step has matrix and vector work.
+    // The two accumulator sets alternate with the sub-step's parity.
+    constexpr int FHN = D / 64;
+    int c_def = -1;  // block computed in the previous sub-step, or -1
+    auto sub = [&](int u, const uint8_t* buf, auto par) __attribute__((always_inline)) {
+      constexpr int P = decltype(par)::value;
+      const int c = 2 * u + kp;
+      if (c <= cmax) {
+        acc[P][0] = acc[P][1] = f32x16{};
+        kstage_mma<D, 0>(acc[P], buf + kp * FHN * kStageBlockBytes, qop);
+        if constexpr (FHN == 2) kstage_mma<D, 1>(acc[P], buf + (2 * kp + 1) * kStageBlockBytes, qop);
+      }
+      if (c_def >= 0) finish(acc[1 - P], c_def);
+      c_def = c <= cmax ? c : -1;
+    };
+    const int nsub = (r_last + 2) / 2;
+    kstage2_pipeline<D>(stage, kseq, n, nsub, [&](int c) { return 64 * min(c, r_last); },
+                        [&](int u, const uint8_t* buf) {
+                          if (u & 1) sub(u, buf, std::integral_constant<int, 1>{});
+                          else sub(u, buf, std::integral_constant<int, 0>{});
+                        });
+    if (c_def >= 0) {
+      if ((nsub - 1) & 1) finish(acc[1], c_def);
+      else finish(acc[0], c_def);
+    }
+  }
   if (lane < 32) {
     sm[kp][qloc] = m;
     sl[kp][qloc] = l;
@@ -262,7 +324,13 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
       }
       __syncthreads();
       const float total = total_s;
-      for (int c = tid; c < nb; c += 512) wts[c] = mass[c] / total;
+      // a NaN weight (only from non-finite inputs) ranks as 0, so that the order
+      // below stays a strict total order and the kept set a set of columns of
+      // this row with exactly kcount members
+      for (int c = tid; c < nb; c += 512) {
+        const float w = mass[c] / total;
+        wts[c] = w == w ? w : 0.0f;
+      }
       __syncthreads();
       // rank of block c in the order weight descending, column ascending: wave w
       // takes blocks w, w + 8, ...; lane L holds the weights of blocks L + 64 j and

@@ -210,6 +210,27 @@ __device__ __forceinline__ float online_update(const float t[32], float& m, floa
   return s;
 }
 
+// As online_update, on logits held in the accumulator registers.
+__device__ __forceinline__ float online_update_acc(const f32x16 t[2], float& m, float& l) {
+  float bm = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) bm = fmaxf(bm, t[kt][v]);
+  bm = fmaxf(bm, xor_lane(bm, 32));
+  const float mn = fmaxf(m, bm);
+  if (mn == -INFINITY) return 0.0f;
+  float s = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += exp2f_fast(t[kt][v] - mn);
+  s += xor_lane(s, 32);
+  l = l * exp2f_fast(m - mn) + s;
+  m = mn;
+  return s;
+}
+
 // Online update for a block that needs no mask and no sink bias (every key is
 // visible to every query of the wave and none is key 0), taking the raw scores.
 // Requires scale_l2 > 0, so that the largest raw score gives the largest logit;
