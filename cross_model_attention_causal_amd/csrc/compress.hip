@@ -418,12 +418,12 @@ __global__ __launch_bounds__(1024) void k_bsr_scan(const int32_t* counts, int64_
 }
 
 // Extraction of the kept blocks of one (head, sequence, row group of 2
-// block-rows): the union of the two rows' kept columns is swept 4 columns per
-// round; wave (qt, kp) recomputes, for its 32 query rows, the columns
-// 4k + kp and 4k + kp + 2 of round k that its block-row kept.
+// block-rows): the union of the two rows' kept columns is swept 2 columns per
+// sub-step; wave (qt, kp) recomputes, for its 32 query rows, column 2u + kp of
+// sub-step u if its block-row kept it.
 template <int D>
 __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
-  constexpr int G = 2, QT = 4, KP = 2, BPW = 2;
+  constexpr int G = 2, QT = 4;
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   __shared__ int ucols[kMaxBlockRows];     // kept columns of either row, ascending
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   const int64_t base = tile_ok ? a.row_ptr[g0 + gr] : 0;
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);
-  f32x16 acc[BPW][2];
+  f32x16 acc[2][2];
   const bool raw_ok = scale_l2 > 0.0f;
   // block index (in this tile's row) of union entry x, or -1 (not kept, or past the end)
   auto blk_of = [&](int x) __attribute__((always_inline)) {
@@ -534,23 +534,34 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
         *reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half) = w;
       }
   };
-  kstage_pipeline<D>(
-      stage, kseq, n, (nu + 3) / 4, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
-      [&](int k, const uint8_t* buf, auto fh) {
-        constexpr int FH = decltype(fh)::value;
-        int b[BPW];
-#pragma unroll
-        for (int j = 0; j < BPW; ++j) {
-          b[j] = blk_of(4 * k + kp + KP * j);
-          if (b[j] < 0) continue;
-          if (FH == 0) acc[j][0] = acc[j][1] = f32x16{};
-          kstage_mma<D, FH>(acc[j], buf + (kp + KP * j) * kStageBlockBytes, qop);
-        }
-        if (FH != D / 64 - 1) return;
-#pragma unroll
-        for (int j = 0; j < BPW; ++j)
-          if (b[j] >= 0) finish(acc[j], ucols[4 * k + kp + KP * j], b[j]);
-      });
+  // Whole-block sub-steps (kstage2_pipeline): the wave computes union entry
+  // 2u + kp of sub-step u if its block-row kept it, and exponentiates and stores
+  // it in sub-step u + 1, beside that sub-step's products. The two accumulator
+  // sets alternate with the sub-step's parity.
+  constexpr int FHN = D / 64;
+  int x_def = -1, b_def = -1;  // entry computed in the previous sub-step and its block index
+  auto sub = [&](int u, const uint8_t* buf, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    const int x = 2 * u + kp, b = blk_of(x);
+    if (b >= 0) {
+      acc[P][0] = acc[P][1] = f32x16{};
+      kstage_mma<D, 0>(acc[P], buf + kp * FHN * kStageBlockBytes, qop);
+      if constexpr (FHN == 2) kstage_mma<D, 1>(acc[P], buf + (2 * kp + 1) * kStageBlockBytes, qop);
+    }
+    if (b_def >= 0) finish(acc[1 - P], ucols[x_def], b_def);
+    x_def = x;
+    b_def = b;
+  };
+  const int nsub = (nu + 1) / 2;
+  kstage2_pipeline<D>(stage, kseq, n, nsub, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
+                      [&](int u, const uint8_t* buf) {
+                        if (u & 1) sub(u, buf, std::integral_constant<int, 1>{});
+                        else sub(u, buf, std::integral_constant<int, 0>{});
+                      });
+  if (b_def >= 0) {
+    if ((nsub - 1) & 1) finish(acc[1], ucols[x_def], b_def);
+    else finish(acc[0], ucols[x_def], b_def);
+  }
 }
 
 __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t value) {
