@@ -531,7 +531,9 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
         const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
         const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
         const int panel = 2 * kt + g2;
-        *reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half) = w;
+        // non-temporal: the blocks are not read again here, and 7.8 GB of them
+        // streaming through L2 would otherwise evict the K that is re-read
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half));
       }
   };
   // Whole-block sub-steps (kstage2_pipeline): the wave computes union entry
