@@ -168,12 +168,12 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   float* LP = dyn + 2 * (kStageBytes / 4);
   __shared__ float sm[KP][64 * G], sl[KP][64 * G];
   __shared__ float lse_s[64 * G];
-  __shared__ float mass[kMaxBlockRows];
-  __shared__ float wts[kMaxBlockRows];
-  __shared__ int order[kMaxBlockRows];
-  __shared__ uint32_t kept[kWords];
-  __shared__ int kcount;
-  __shared__ float total_s;
+  __shared__ float mass_a[G][kMaxBlockRows];
+  __shared__ float wts_a[G][kMaxBlockRows];
+  __shared__ int order_a[G][kMaxBlockRows];
+  __shared__ uint32_t kept_a[G][kWords];
+  __shared__ int kcount_a[G];
+  __shared__ float total_a[G];
 
   int h, s, rg;
   if (!group_item(blockIdx.x, (a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads, h, s, rg)) return;
@@ -276,116 +276,127 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     }
   }
 
+  // Selection, the group's rows side by side: waves 4 gr .. 4 gr + 3 (all 8
+  // waves when G = 1) take block-row r0 + gr.
+  constexpr int NTR = 512 / G, NWR = NTR / 64;  // threads and waves per row
+  const int gr = wave / NWR, tl = tid % NTR, wl = wave % NWR;
+  const int r = r0 + gr;
+  const bool act = r <= r_last;
+  float* mass = mass_a[gr];
+  float* wts = wts_a[gr];
+  int* order = order_a[gr];
+  uint32_t* kept = kept_a[gr];
   int32_t roff;
   int64_t tri_off;
   block_offsets(a.vl, s, roff, tri_off);
-  for (int gr = 0; gr < G; ++gr) {
-    const int r = r0 + gr;
-    if (r > r_last) break;
-    __syncthreads();  // lse_s is written; the previous row's readers of kept / kcount are done
-    if (tid < kWords) kept[tid] = 0u;
-    // mass_c over the valid rows: four consecutive threads take rows 16 part ..
-    // + 15 of block c, then add their partials in a fixed order
-    const int nrows = min(64, n - 64 * r);
-    const int nb = r + 1;
-    const float* LPr = LP + 64 * gr * LPS;
-    const float* lser = lse_s + 64 * gr;
-    for (int x0 = 0; x0 < 4 * nb; x0 += 512) {
-      const int x = x0 + tid, c = x >> 2, part = x & 3;
-      float y = 0.0f;
-      if (c < nb) {
-        const int q1 = min(16 * part + 16, nrows);
-        for (int q = 16 * part; q < q1; ++q) y += exp2f_fast(LPr[q * LPS + c] - lser[q]);
+  __syncthreads();  // lse_s is written
+  if (tl < kWords) kept[tl] = 0u;
+  // mass_c over the valid rows: four consecutive threads take rows 16 part ..
+  // + 15 of block c, then add their partials in a fixed order
+  const int nrows = act ? min(64, n - 64 * r) : 0;
+  const int nb = act ? r + 1 : 0;
+  const float* LPr = LP + 64 * gr * LPS;
+  const float* lser = lse_s + 64 * gr;
+  for (int x0 = 0; x0 < 4 * nb; x0 += NTR) {
+    const int x = x0 + tl, c = x >> 2, part = x & 3;
+    float y = 0.0f;
+    if (c < nb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int q = 16 * part + e;
+        if (q < nrows) y += exp2f_fast(LPr[q * LPS + c] - lser[q]);
       }
-      y += __shfl_xor(y, 1, 64);  // (p0 + p1), (p2 + p3)
-      y += __shfl_xor(y, 2, 64);  // (p0 + p1) + (p2 + p3)
-      if (c < nb && part == 0) mass[c] = y;
     }
-    __syncthreads();
+    y += __shfl_xor(y, 1, 64);  // (p0 + p1), (p2 + p3)
+    y += __shfl_xor(y, 2, 64);  // (p0 + p1) + (p2 + p3)
+    if (c < nb && part == 0) mass[c] = y;
+  }
+  __syncthreads();
 
-    const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
-    if (a.block_mass) {
-      int32_t r_all;
-      int64_t n_tri;  // blocks per head over all sequences
-      block_offsets(a.vl, a.vl.n_seqs, r_all, n_tri);
-      float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * (r + 1) / 2;
-      for (int c = tid; c < nb; c += 512) bm[c] = mass[c];
+  const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
+  if (act && a.block_mass) {
+    int32_t r_all;
+    int64_t n_tri;  // blocks per head over all sequences
+    block_offsets(a.vl, a.vl.n_seqs, r_all, n_tri);
+    float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * (r + 1) / 2;
+    for (int c = tl; c < nb; c += NTR) bm[c] = mass[c];
+  }
+  if (a.tau >= 1.0f) {
+    for (int c = tl; c < nb; c += NTR) atomicOr(&kept[c >> 5], 1u << (c & 31));
+    if (tl == 0) kcount_a[gr] = nb;
+  } else {
+    // total mass: one wave per row, strided partial sums then a fixed butterfly
+    if (wl == 0) {
+      float x = 0.0f;
+      for (int c = lane; c < nb; c += 64) x += mass[c];
+      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+      if (lane == 0) total_a[gr] = x;
     }
-    if (a.tau >= 1.0f) {
-      for (int c = tid; c < nb; c += 512) atomicOr(&kept[c >> 5], 1u << (c & 31));
-      if (tid == 0) kcount = nb;
-    } else {
-      // total mass: one wave, strided partial sums then a fixed butterfly
-      if (wave == 0) {
-        float x = 0.0f;
-        for (int c = lane; c < nb; c += 64) x += mass[c];
-        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-        if (lane == 0) total_s = x;
-      }
-      __syncthreads();
-      const float total = total_s;
-      // a NaN weight (only from non-finite inputs) ranks as 0, so that the order
-      // below stays a strict total order and the kept set a set of columns of
-      // this row with exactly kcount members
-      for (int c = tid; c < nb; c += 512) {
-        const float w = mass[c] / total;
-        wts[c] = w == w ? w : 0.0f;
-      }
-      __syncthreads();
-      // rank of block c in the order weight descending, column ascending: wave w
-      // takes blocks w, w + 8, ...; lane L holds the weights of blocks L + 64 j and
-      // each comparison is one ballot over the wave
-      {
-        float w2[kMaxBlockRows / 64];
+    __syncthreads();
+    const float total = total_a[gr];
+    // a NaN weight (only from non-finite inputs) ranks as 0, so that the order
+    // below stays a strict total order and the kept set a set of columns of
+    // this row with exactly kcount members
+    for (int c = tl; c < nb; c += NTR) {
+      const float w = mass[c] / total;
+      wts[c] = w == w ? w : 0.0f;
+    }
+    __syncthreads();
+    // rank of block c in the order weight descending, column ascending: wave wl
+    // of the row takes blocks wl, wl + NWR, ...; lane L holds the weights of
+    // blocks L + 64 j and each comparison is one ballot over the wave
+    {
+      float w2[kMaxBlockRows / 64];
 #pragma unroll
-        for (int j = 0; j < kMaxBlockRows / 64; ++j) w2[j] = lane + 64 * j < nb ? wts[lane + 64 * j] : -INFINITY;
-        for (int c = wave; c < nb; c += 8) {
-          const float wc = wts[c];
-          int rank = 0;
+      for (int j = 0; j < kMaxBlockRows / 64; ++j) w2[j] = lane + 64 * j < nb ? wts[lane + 64 * j] : -INFINITY;
+      for (int c = wl; c < nb; c += NWR) {
+        const float wc = wts[c];
+        int rank = 0;
 #pragma unroll
-          for (int j = 0; j < kMaxBlockRows / 64; ++j) {
-            const int c2 = lane + 64 * j;
-            const bool ahead = c2 < nb && (w2[j] > wc || (w2[j] == wc && c2 < c));
-            rank += __popcll(__ballot(ahead));
-          }
-          if (lane == 0) order[rank] = c;
+        for (int j = 0; j < kMaxBlockRows / 64; ++j) {
+          const int c2 = lane + 64 * j;
+          const bool ahead = c2 < nb && (w2[j] > wc || (w2[j] == wc && c2 < c));
+          rank += __popcll(__ballot(ahead));
         }
-      }
-      __syncthreads();
-      // running sum in that order (wave 0: 4 consecutive ranks per lane, then a
-      // wave-wide inclusive scan of the lane totals); keep the shortest prefix
-      // whose sum reaches tau
-      if (wave == 0) {
-        float cum[4];
-        float run = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int x = 4 * lane + e;
-          run += x < nb ? wts[order[x]] : 0.0f;
-          cum[e] = run;
-        }
-        float pre = run;
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(pre, off, 64);
-          if (lane >= off) pre += y;
-        }
-        const float before = pre - run;
-        int first = 4 * 64;
-#pragma unroll
-        for (int e = 3; e >= 0; --e)
-          if (4 * lane + e < nb && before + cum[e] >= a.tau) first = 4 * lane + e;
-        for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
-        if (lane == 0) kcount = first < nb ? first + 1 : nb;
-      }
-      __syncthreads();
-      for (int x = tid; x < kcount; x += 512) {
-        const int c = order[x];
-        atomicOr(&kept[c >> 5], 1u << (c & 31));
+        if (lane == 0) order[rank] = c;
       }
     }
     __syncthreads();
-    if (tid < kWords) a.kept[g * kWords + tid] = kept[tid];
-    if (tid == 0) a.counts[g] = kcount;
+    // running sum in that order (one wave per row: 4 consecutive ranks per lane,
+    // then a wave-wide inclusive scan of the lane totals); keep the shortest
+    // prefix whose sum reaches tau
+    if (wl == 0 && act) {
+      float cum[4];
+      float run = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int x = 4 * lane + e;
+        run += x < nb ? wts[order[x]] : 0.0f;
+        cum[e] = run;
+      }
+      float pre = run;
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(pre, off, 64);
+        if (lane >= off) pre += y;
+      }
+      const float before = pre - run;
+      int first = 4 * 64;
+#pragma unroll
+      for (int e = 3; e >= 0; --e)
+        if (4 * lane + e < nb && before + cum[e] >= a.tau) first = 4 * lane + e;
+      for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+      if (lane == 0) kcount_a[gr] = first < nb ? first + 1 : nb;
+    }
+    __syncthreads();
+    for (int x = tl; x < (act ? kcount_a[gr] : 0); x += NTR) {
+      const int c = order[x];
+      atomicOr(&kept[c >> 5], 1u << (c & 31));
+    }
+  }
+  __syncthreads();
+  if (act) {
+    if (tl < kWords) a.kept[g * kWords + tl] = kept[tl];
+    if (tl == 0) a.counts[g] = kcount_a[gr];
   }
 }
 
