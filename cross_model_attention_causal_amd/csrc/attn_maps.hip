@@ -32,8 +32,11 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, const float p[4],
 
 // grid (n_block_rows, n_seqs, n_heads), 512 threads = 8 waves:
 // wave w owns queries 32*(w&1) .. +31 of the block-row and key blocks c = (w>>1) mod 4.
+constexpr int kTileRow = 36;  // dwords per row of a wave's bf16 output tile (64 keys + pad)
+
 template <int D, bool PACKED, bool OUT_BF16>
 __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
+  __shared__ uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? 32 * kTileRow : 1];
   const int h = blockIdx.z, s = blockIdx.y;
   const int r = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest block-rows first
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
@@ -98,8 +101,8 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   }
   const float lse = M + log2f_fast(L);
 
-  const int64_t base = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED) +
-                       map_row_off(i, nq, nk, PACKED);
+  const int64_t base0 = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED);
+  const int64_t base = base0 + map_row_off(i, nq, nk, PACKED);
   const int wend = PACKED ? last + 1 : nk;  // entries of this row that exist in the layout
   const int cend = PACKED ? cmax : (nk - 1) >> 6;
   const int half = lane >> 5;
@@ -126,15 +129,45 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) acc[kt] = f32x16{};
     }
-    if (!valid) return;
+    if constexpr (OUT_BF16) {
+      // Through the wave's LDS tile, so that the global stores run along rows:
+      // lane (query q, half) puts its 4-key groups at tile row q, then each pass
+      // writes two rows (32 lanes per row) of the block's segment [64c, 64c + len)
+      // with 4-byte stores on the row's own element parity (a packed row may
+      // start at any element) and 2-byte stores for a leading or trailing odd
+      // entry.
+      uint32_t* tw = wtile[wave];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int key0 = 64 * c + 32 * kt + 8 * g + 4 * half;
-        const float p[4] = {acc[kt][4 * g], acc[kt][4 * g + 1], acc[kt][4 * g + 2], acc[kt][4 * g + 3]};
-        const int cnt = max(0, min(4, wend - key0));
-        if (cnt > 0) store4<OUT_BF16>(a.maps, base + key0, p, cnt);
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 w = {pack2bf(acc[kt][4 * g], acc[kt][4 * g + 1]), pack2bf(acc[kt][4 * g + 2], acc[kt][4 * g + 3])};
+          *reinterpret_cast<u32x2*>(&tw[(lane & 31) * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
+        }
+      const int k = lane & 31, rsel = lane >> 5;
+      for (int p2 = 0; p2 < 16; ++p2) {
+        const int qq = 2 * p2 + rsel;
+        const int iq = 64 * r + 32 * qt + qq;
+        const int len = iq < nq ? min(64, (PACKED ? nk - nq + iq + 1 : nk) - 64 * c) : 0;
+        if (len <= 0) continue;
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.maps) + base0 + map_row_off(iq, nq, nk, PACKED) + 64 * c;
+        const int sh = (int)((reinterpret_cast<uintptr_t>(out) >> 1) & 1), j0 = sh + 2 * k;  // 4-byte phase
+        const uint16_t* trow = reinterpret_cast<const uint16_t*>(&tw[qq * kTileRow]);
+        if (j0 + 1 < len) *reinterpret_cast<uint32_t*>(out + j0) = (uint32_t)trow[j0] | ((uint32_t)trow[j0 + 1] << 16);
+        else if (j0 < len) out[j0] = trow[j0];
+        if (sh && k == 0) out[0] = trow[0];
+      }
+    } else {
+      if (!valid) return;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int key0 = 64 * c + 32 * kt + 8 * g + 4 * half;
+          const float p[4] = {acc[kt][4 * g], acc[kt][4 * g + 1], acc[kt][4 * g + 2], acc[kt][4 * g + 3]};
+          const int cnt = max(0, min(4, wend - key0));
+          if (cnt > 0) store4<OUT_BF16>(a.maps, base + key0, p, cnt);
+        }
       }
     }
   };
@@ -271,8 +304,8 @@ __global__ __launch_bounds__(256) void k_attn_maps_f32(AttnMapsArgs a, int d) {
     __syncthreads();
   }
   const float inv = 1.0f / red[0];
-  const int64_t base = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED) +
-                       map_row_off(i, nq, nk, PACKED);
+  const int64_t base0 = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED);
+  const int64_t base = base0 + map_row_off(i, nq, nk, PACKED);
   const int wend = PACKED ? last + 1 : nk;
   for (int j = threadIdx.x; j < wend; j += 256) {
     const float p = j <= last ? expf(logit(j) - mx) * inv : 0.0f;
