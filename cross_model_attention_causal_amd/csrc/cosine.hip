@@ -1,49 +1,65 @@
 // Head mapping by cosine similarity of flattened maps (IAM Methods 1 and 4).
 //
 // The cosine matrix is a Gram product R S^T over the map length with the row
-// norms on the side. It runs as a split-K bf16 MFMA GEMM: a workgroup owns 128
-// receiver maps and one K-chunk, holds the partial dot products of its 128 maps
-// against all sender maps in registers, stages the sender slice through LDS
-// (shared by its 4 waves) and streams its own receiver rows straight from HBM,
-// so each receiver map is read once. Partial sums of each split go to a
-// workspace and a finalize kernel adds them in a fixed order (deterministic),
-// forms the cosines and takes argmax (lowest index on ties) and margin.
+// norms on the side. It runs as a split-K bf16 MFMA GEMM: a workgroup (8 waves)
+// owns 128 receiver maps and one K-chunk and holds the partial dot products of
+// its 128 maps against all sender maps in registers (wave = 32 receivers x one
+// half of the senders). Each 64-element K-step is software-pipelined: while the
+// step's products run, the next step's receiver operands (straight from HBM,
+// each receiver map read once) and sender slice (into registers, then into the
+// other half of a double-buffered LDS slice shared by all waves) are in flight.
+// Partial sums of each split go to a workspace and a finalize kernel adds them
+// in a fixed order (deterministic), forms the cosines and takes argmax (lowest
+// index on ties) and margin.
 #include "kernels.hpp"
 
 namespace cma {
 
-constexpr int kGramRows = 128;  // receiver maps per workgroup
-constexpr int kGramK = 64;      // K elements per step
-constexpr int kSbStride = 72;   // padded LDS row (bf16) of the staged sender slice
-constexpr int kMaxSteps = 64;   // K-steps of one split (4096 elements)
+constexpr int kGramRows = 128;     // receiver maps per workgroup
+constexpr int kGramK = 64;         // K elements per step
+constexpr int kGramThreads = 512;  // 8 waves = 4 groups of 32 receivers x 2 sender halves
+constexpr int kMaxSteps = 64;      // K-steps of one split (4096 elements)
 
-template <int NT>  // sender tiles of 16 (n_send <= 16 * NT)
-__global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sb[NT * 16 * kSbStride];
-  const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
+// The sender slice of a step in LDS: row j (a sender map) holds 64 elements as 8
+// chunks of 16 bytes, chunk ch in slot ch ^ ((j >> 1) & 7), so that the 16 rows
+// one operand read touches fall in distinct bank groups.
+__device__ __forceinline__ int sslot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
+
+template <int NTH>  // sender tiles of 16 per half (n_send <= 32 * NTH)
+__global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
+  constexpr int SROWS = 32 * NTH;                                  // staged sender rows
+  constexpr int SCH = SROWS * 8;                                   // 16-byte chunks per slice
+  constexpr int SPT = (SCH + kGramThreads - 1) / kGramThreads;     // chunks per thread
+  __shared__ __attribute__((aligned(16))) u32x4 sb[2][SCH];
   const int b = blockIdx.y;
   const int rt = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
-  (void)n_rtiles;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int p = lane & 15, qd = lane >> 4;
+  const int rg = wave & 3, sh = wave >> 2;  // receiver group, sender half
   const int64_t k_beg = (int64_t)sp * a.kchunk;
   const int64_t k_end = min(a.len, k_beg + a.kchunk);
+  const int nsteps = (int)((k_end - k_beg + kGramK - 1) / kGramK);
   const uint16_t* recv = reinterpret_cast<const uint16_t*>(a.recv) + (int64_t)b * a.rb;
   const uint16_t* send = reinterpret_cast<const uint16_t*>(a.send) + (int64_t)b * a.sb;
-  const int row0 = rt * kGramRows + 32 * wave;
+  const int row0 = rt * kGramRows + 32 * rg;
 
-  f32x4 acc[2][NT];
+  f32x4 acc[2][NTH];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NTH; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Squared norms in two levels: a step's squares are summed apart, added to an
   // inner running sum that is folded into the outer one every 16 steps. A single
   // long fp32 chain would drop the many tiny squares of a probability map's tail
   // once the sum has grown (a systematic underestimate, which biases the cosine).
   float rn[2] = {0.f, 0.f}, rn_in[2] = {0.f, 0.f};
-  float sn[2] = {0.f, 0.f}, sn_in[2] = {0.f, 0.f};  // sender rows threadIdx.x, threadIdx.x + 256
-  int step = 0;
+  float sn = 0.f, sn_in = 0.f;
+  // sender rows whose norms this workgroup accumulates (one per thread): the
+  // receiver tiles of a split share the rows out
+  const int s_per = (a.n_send + n_rtiles - 1) / n_rtiles;
+  const int srow = rt * s_per + tid;
+  const bool s_mine = tid < s_per && srow < a.n_send;
 
   const uint16_t* arow[2];
   bool aok[2];
@@ -53,17 +69,9 @@ __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
     aok[mt] = row < a.n_recv;
     arow[mt] = recv + (int64_t)(aok[mt] ? row : 0) * a.rh;
   }
-
-  for (int64_t k0 = k_beg; k0 < k_end; k0 += kGramK) {
-    // stage the sender slice [NT*16 rows][64]
-    for (int x = threadIdx.x; x < NT * 16 * 8; x += 256) {
-      const int row = x >> 3, ch = x & 7;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (row < a.n_send) val = ldg16_guard(send + (int64_t)row * a.sh, k0 + 8 * ch, k_end);
-      *reinterpret_cast<u32x4*>(&sb[row * kSbStride + 8 * ch]) = val;
-    }
-    // receiver operand straight from memory
-    u32x4 av[2][2];
+  // receiver operand of step st: lane (p, qd) holds k = 32 ks + 8 qd .. + 7 of its rows
+  auto load_a = [&](int st, u32x4 (&av)[2][2]) __attribute__((always_inline)) {
+    const int64_t k0 = k_beg + (int64_t)st * kGramK;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -72,86 +80,127 @@ __global__ __launch_bounds__(256) void k_gram_bf16(CosineArgs a) {
         if (aok[mt]) x = ldg16_guard(arow[mt], k0 + 32 * ks + 8 * qd, k_end);
         av[mt][ks] = x;
       }
+  };
+  // sender slice of step st: chunk x = tid + 512 i is (row x / 8, LDS slot x % 8)
+  auto load_s = [&](int st, u32x4 (&sv)[SPT]) __attribute__((always_inline)) {
+    const int64_t k0 = k_beg + (int64_t)st * kGramK;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      float t = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(av[mt][ks][e] << 16);
-          const float hi = __uint_as_float(av[mt][ks][e] & 0xffff0000u);
-          t = fmaf(lo, lo, fmaf(hi, hi, t));
-        }
-      rn_in[mt] += t;
+    for (int i = 0; i < SPT; ++i) {
+      const int x = tid + kGramThreads * i, row = x >> 3, slot = x & 7;
+      const int ch = slot ^ ((row >> 1) & 7);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (x < SCH && row < a.n_send) v = ldg16_guard(send + (int64_t)row * a.sh, k0 + 8 * ch, k_end);
+      sv[i] = v;
     }
-    __syncthreads();
-    if (rt == 0) {
+  };
+  auto store_s = [&](const u32x4 (&sv)[SPT], int buf) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int row = threadIdx.x + 256 * u;
-        if (row < NT * 16) {
-          const uint16_t* srow = &sb[row * kSbStride];
-          float t = 0.0f;
-          for (int e = 0; e < kGramK; ++e) {
-            const float x = bf2f(srow[e]);
-            t = fmaf(x, x, t);
+    for (int i = 0; i < SPT; ++i) {
+      const int x = tid + kGramThreads * i;
+      if (x < SCH) sb[buf][x] = sv[i];  // slot order: x = row * 8 + slot
+    }
+  };
+
+  u32x4 acur[2][2], anext[2][2], sv[SPT];
+  if (nsteps > 0) {
+    load_s(0, sv);
+    load_a(0, acur);
+    store_s(sv, 0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nsteps;
+    if (more) {
+      load_s(st + 1, sv);
+      load_a(st + 1, anext);
+    }
+    // receiver norms (one sender half does it)
+    if (sh == 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        float t = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = __uint_as_float(acur[mt][ks][e] << 16);
+            const float hi = __uint_as_float(acur[mt][ks][e] & 0xffff0000u);
+            t = fmaf(lo, lo, fmaf(hi, hi, t));
           }
-          sn_in[u] += t;
-        }
+        rn_in[mt] += t;
       }
     }
-    if ((++step & 15) == 0) {
+    // sender norms of this workgroup's share of the rows, in element order
+    if (s_mine) {
+      float t = 0.0f;
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) {
+        const u32x4 v = sb[buf][sslot(srow, ch)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __uint_as_float(v[e] << 16);
+          const float hi = __uint_as_float(v[e] & 0xffff0000u);
+          t = fmaf(hi, hi, fmaf(lo, lo, t));
+        }
+      }
+      sn_in += t;
+    }
+    if (((st + 1) & 15) == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         rn[u] += rn_in[u];
-        sn[u] += sn_in[u];
-        rn_in[u] = sn_in[u] = 0.0f;
+        rn_in[u] = 0.0f;
       }
+      sn += sn_in;
+      sn_in = 0.0f;
     }
+    // products: B operand lane (p, qd) = sender row 16 nt + p, k = 32 ks + 8 qd .. + 7
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NTH; ++nt) {
+      const int srow_b = 16 * (sh * NTH + nt) + p;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(&sb[(16 * nt + p) * kSbStride + 32 * ks + 8 * qd]);
+        const u32x4 bv = sb[buf][sslot(srow_b, 4 * ks + qd)];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(as_bf16x8(av[mt][ks]), as_bf16x8(bv), acc[mt][nt]);
+        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(as_bf16x8(acur[mt][ks]), as_bf16x8(bv), acc[mt][nt]);
       }
+    }
+    if (more) {
+      store_s(sv, buf ^ 1);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acur[mt][ks] = anext[mt][ks];
     }
     __syncthreads();
   }
 
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    rn[u] += rn_in[u];
-    sn[u] += sn_in[u];
-  }
+  for (int u = 0; u < 2; ++u) rn[u] += rn_in[u];
+  sn += sn_in;
   // partial dot products: D[m = 4qd + v][n = p]
   float* part = a.part + ((int64_t)sp * a.n_batch + b) * a.n_recv * a.n_send;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int nt = 0; nt < NTH; ++nt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = row0 + 16 * mt + 4 * qd + v, col = 16 * nt + p;
+        const int row = row0 + 16 * mt + 4 * qd + v, col = 16 * (sh * NTH + nt) + p;
         if (row < a.n_recv && col < a.n_send) part[(int64_t)row * a.n_send + col] = acc[mt][nt][v];
       }
+  if (sh == 0) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    float x = rn[mt];
-    x += xor_lane(x, 16);
-    x += xor_lane(x, 32);
-    const int row = row0 + 16 * mt + p;
-    if (qd == 0 && row < a.n_recv) a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + row] = x;
-  }
-  if (rt == 0) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int row = threadIdx.x + 256 * u;
-      if (row < a.n_send) a.snorm[((int64_t)sp * a.n_batch + b) * a.n_send + row] = sn[u];
+    for (int mt = 0; mt < 2; ++mt) {
+      float x = rn[mt];
+      x += xor_lane(x, 16);
+      x += xor_lane(x, 32);
+      const int row = row0 + 16 * mt + p;
+      if (qd == 0 && row < a.n_recv) a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + row] = x;
     }
   }
+  if (s_mine) a.snorm[((int64_t)sp * a.n_batch + b) * a.n_send + srow] = sn;
 }
 
 // fp32 maps: one workgroup per (sender, receiver, problem), VALU dot products.
@@ -192,16 +241,29 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
 __global__ __launch_bounds__(64) void k_cos_finalize(CosineArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   float rn = 0.f;
-  for (int sp = 0; sp < a.splits; ++sp) rn += a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + h];
+  for (int sp = 0; sp < a.splits; ++sp) rn += a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + h];  // one value per lane group, cheap
   const float rs = sqrtf(rn);
   float v1 = -INFINITY, v2 = -INFINITY;
   int i1 = 0x7fffffff, i2 = 0x7fffffff;
   for (int j = lane; j < a.n_send; j += 64) {
-    float dot = 0.f, sn = 0.f;
-    for (int sp = 0; sp < a.splits; ++sp) {
-      dot += a.part[(((int64_t)sp * a.n_batch + b) * a.n_recv + h) * a.n_send + j];
-      sn += a.snorm[((int64_t)sp * a.n_batch + b) * a.n_send + j];
+    // four interleaved partial sums over the splits, added in a fixed order
+    float d4[4] = {0.f, 0.f, 0.f, 0.f}, s4[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t pstride = (int64_t)a.n_batch * a.n_recv * a.n_send, sstride = (int64_t)a.n_batch * a.n_send;
+    const float* pp = a.part + ((int64_t)b * a.n_recv + h) * a.n_send + j;
+    const float* ps = a.snorm + (int64_t)b * a.n_send + j;
+    int sp = 0;
+    for (; sp + 3 < a.splits; sp += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        d4[u] += pp[(sp + u) * pstride];
+        s4[u] += ps[(sp + u) * sstride];
+      }
     }
+    for (int u = 0; sp < a.splits; ++sp, ++u) {
+      d4[u] += pp[sp * pstride];
+      s4[u] += ps[sp * sstride];
+    }
+    const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]), sn = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     const float den = rs * sqrtf(sn);
     const float c = den > 0.f ? dot / den : 0.f;
     if (a.cos) a.cos[((int64_t)b * a.n_recv + h) * a.n_send + j] = c;
@@ -240,38 +302,47 @@ CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t 
   } else {
     const int64_t kblocks = (len + kGramK - 1) / kGramK;
     const int64_t tiles = (int64_t)((n_recv + kGramRows - 1) / kGramRows) * n_batch;
-    // enough splits to fill the chip, and at most kMaxSteps K-steps per split so
-    // that each partial dot product is a short fp32 accumulation chain
-    int64_t splits = (512 + tiles - 1) / tiles;
-    splits = std::max<int64_t>(splits, (kblocks + kMaxSteps - 1) / kMaxSteps);
-    splits = std::max<int64_t>(1, std::min<int64_t>(splits, kblocks));
-    const int64_t per = (kblocks + splits - 1) / splits;
-    pl.kchunk = std::max<int64_t>(1, per) * kGramK;
+    // At most kMaxSteps K-steps per split, so that each partial dot product is a
+    // short fp32 accumulation chain, and at least one workgroup per CU (one fits
+    // at a time); among the step counts that allow, the one whose workgroups
+    // fill the last round of 256 best (then the fewest splits, which the
+    // finalize has to add).
+    constexpr int64_t kCus = 256;
+    const int64_t s_lo = std::max<int64_t>((kblocks + kMaxSteps - 1) / kMaxSteps, (kCus + tiles - 1) / tiles);
+    int64_t best_per = (kblocks + s_lo - 1) / s_lo;
+    double best_eff = -1.0;
+    for (int64_t per = std::max<int64_t>(1, best_per); per >= 1 && per >= best_per / 2; --per) {
+      const int64_t sp = (kblocks + per - 1) / per, wg = sp * tiles;
+      const double eff = (double)wg / (double)(((wg + kCus - 1) / kCus) * kCus);
+      if (eff > best_eff + 1e-9) {
+        best_eff = eff;
+        best_per = per;
+      }
+    }
+    pl.kchunk = std::max<int64_t>(1, best_per) * kGramK;
     pl.splits = (int32_t)std::max<int64_t>(1, (len + pl.kchunk - 1) / pl.kchunk);
   }
   pl.ws_bytes = (size_t)pl.splits * n_batch * ((size_t)n_recv * n_send + n_recv + n_send) * sizeof(float);
   return pl;
 }
 
-template <int NT>
+template <int NTH>
 static void gram_launch(const CosineArgs& a, hipStream_t st) {
   const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
   dim3 grid(n_rtiles * a.splits, a.n_batch);
-  { KernelTimer kt_("k_gram_bf16", st); hipLaunchKernelGGL((k_gram_bf16<NT>), grid, dim3(256), 0, st, a); }
+  { KernelTimer kt_("k_gram_bf16", st); hipLaunchKernelGGL((k_gram_bf16<NTH>), grid, dim3(kGramThreads), 0, st, a); }
 }
 
 hipError_t launch_cosine(const CosineArgs& a, hipStream_t st) {
   if (a.n_batch == 0 || a.n_recv == 0) return hipSuccess;
   if (a.bf16) {
-    const int nt = (a.n_send + 15) / 16;
-    if (nt <= 1) gram_launch<1>(a, st);
-    else if (nt <= 2) gram_launch<2>(a, st);
-    else if (nt <= 4) gram_launch<4>(a, st);
-    else if (nt <= 8) gram_launch<8>(a, st);
-    else if (nt <= 12) gram_launch<12>(a, st);
-    else if (nt <= 16) gram_launch<16>(a, st);
-    else if (nt <= 21) gram_launch<21>(a, st);
-    else gram_launch<24>(a, st);
+    const int nth = (a.n_send + 31) / 32;  // sender tiles of 16 per half
+    if (nth <= 1) gram_launch<1>(a, st);
+    else if (nth <= 2) gram_launch<2>(a, st);
+    else if (nth <= 4) gram_launch<4>(a, st);
+    else if (nth <= 8) gram_launch<8>(a, st);
+    else if (nth <= 11) gram_launch<11>(a, st);
+    else gram_launch<12>(a, st);
   } else {
     { KernelTimer kt_("k_gram_f32", st); hipLaunchKernelGGL(k_gram_f32, dim3(a.n_send, a.n_recv, a.n_batch), dim3(256), 0, st, a); }
   }
