@@ -25,6 +25,13 @@ constexpr int kMaxSteps = 64;      // K-steps of one split (4096 elements)
 // one operand read touches fall in distinct bank groups.
 __device__ __forceinline__ int sslot(int row, int ch) { return row * 8 + (ch ^ ((row >> 1) & 7)); }
 
+// t + lo^2 + hi^2 for the two bf16 values packed in w (one dot2 instruction; the
+// products of bf16 values are exact in fp32)
+__device__ __forceinline__ float sq2(uint32_t w, float t) {
+  const bf16x2 x = __builtin_bit_cast(bf16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, t, false);
+}
+
 template <int NTH>  // sender tiles of 16 per half (n_send <= 32 * NTH)
 __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   constexpr int SROWS = 32 * NTH;                                  // staged sender rows
@@ -32,8 +39,13 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   constexpr int SPT = (SCH + kGramThreads - 1) / kGramThreads;     // chunks per thread
   __shared__ __attribute__((aligned(16))) u32x4 sb[2][SCH];
   const int b = blockIdx.y;
-  const int rt = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
   const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
+  // Workgroup id i runs on XCD i % 8. Split sp goes to XCD sp % 8 with all its
+  // receiver tiles in consecutive slots there, so the tiles of a split run
+  // together and share its sender slice through that XCD's L2.
+  const int xcd = blockIdx.x % kXcds, m = blockIdx.x / kXcds;
+  const int sp = xcd + kXcds * (m / n_rtiles), rt = m % n_rtiles;
+  if (sp >= a.splits) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int p = lane & 15, qd = lane >> 4;
   const int rg = wave & 3, sh = wave >> 2;  // receiver group, sender half
@@ -69,28 +81,43 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
     aok[mt] = row < a.n_recv;
     arow[mt] = recv + (int64_t)(aok[mt] ? row : 0) * a.rh;
   }
+  // The loads of a full step carry no branch, so the compiler's waits for the
+  // prefetched registers stay exact: rows past the end read a valid row, and
+  // what they produce (products in rows or columns past the end, their norms)
+  // is never stored. A last, partial step uses element-guarded loads.
   // receiver operand of step st: lane (p, qd) holds k = 32 ks + 8 qd .. + 7 of its rows
-  auto load_a = [&](int st, u32x4 (&av)[2][2]) __attribute__((always_inline)) {
+  auto load_a = [&](int st, u32x4 (&av)[2][2], auto guarded) __attribute__((always_inline)) {
     const int64_t k0 = k_beg + (int64_t)st * kGramK;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (aok[mt]) x = ldg16_guard(arow[mt], k0 + 32 * ks + 8 * qd, k_end);
-        av[mt][ks] = x;
+        const int64_t j0 = k0 + 32 * ks + 8 * qd;
+        if constexpr (decltype(guarded)::value) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (aok[mt]) x = ldg16_guard(arow[mt], j0, k_end);
+          av[mt][ks] = x;
+        } else {
+          av[mt][ks] = ldg16(arow[mt] + j0);
+        }
       }
   };
   // sender slice of step st: chunk x = tid + 512 i is (row x / 8, LDS slot x % 8)
-  auto load_s = [&](int st, u32x4 (&sv)[SPT]) __attribute__((always_inline)) {
+  auto load_s = [&](int st, u32x4 (&sv)[SPT], auto guarded) __attribute__((always_inline)) {
     const int64_t k0 = k_beg + (int64_t)st * kGramK;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int x = tid + kGramThreads * i, row = x >> 3, slot = x & 7;
       const int ch = slot ^ ((row >> 1) & 7);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (x < SCH && row < a.n_send) v = ldg16_guard(send + (int64_t)row * a.sh, k0 + 8 * ch, k_end);
-      sv[i] = v;
+      const bool ok = x < SCH && row < a.n_send;
+      const uint16_t* srow_p = send + (int64_t)min(row, a.n_send - 1) * a.sh;
+      if constexpr (decltype(guarded)::value) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = ldg16_guard(srow_p, k0 + 8 * ch, k_end);
+        sv[i] = v;
+      } else {
+        sv[i] = ldg16(srow_p + k0 + 8 * ch);
+      }
     }
   };
   auto store_s = [&](const u32x4 (&sv)[SPT], int buf) __attribute__((always_inline)) {
@@ -100,21 +127,8 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
       if (x < SCH) sb[buf][x] = sv[i];  // slot order: x = row * 8 + slot
     }
   };
-
-  u32x4 acur[2][2], anext[2][2], sv[SPT];
-  if (nsteps > 0) {
-    load_s(0, sv);
-    load_a(0, acur);
-    store_s(sv, 0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < nsteps;
-    if (more) {
-      load_s(st + 1, sv);
-      load_a(st + 1, anext);
-    }
+  // one step's work on the slice in LDS buffer buf and the receiver operand av
+  auto compute = [&](int st, int buf, const u32x4 (&av)[2][2]) __attribute__((always_inline)) {
     // receiver norms (one sender half does it)
     if (sh == 0) {
 #pragma unroll
@@ -123,11 +137,7 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float lo = __uint_as_float(acur[mt][ks][e] << 16);
-            const float hi = __uint_as_float(acur[mt][ks][e] & 0xffff0000u);
-            t = fmaf(lo, lo, fmaf(hi, hi, t));
-          }
+          for (int e = 0; e < 4; ++e) t = sq2(av[mt][ks][e], t);
         rn_in[mt] += t;
       }
     }
@@ -138,11 +148,7 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
       for (int ch = 0; ch < 8; ++ch) {
         const u32x4 v = sb[buf][sslot(srow, ch)];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(v[e] << 16);
-          const float hi = __uint_as_float(v[e] & 0xffff0000u);
-          t = fmaf(hi, hi, fmaf(lo, lo, t));
-        }
+        for (int e = 0; e < 4; ++e) t = sq2(v[e], t);
       }
       sn_in += t;
     }
@@ -163,17 +169,43 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const u32x4 bv = sb[buf][sslot(srow_b, 4 * ks + qd)];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(as_bf16x8(acur[mt][ks]), as_bf16x8(bv), acc[mt][nt]);
+        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(as_bf16x8(av[mt][ks]), as_bf16x8(bv), acc[mt][nt]);
       }
     }
-    if (more) {
-      store_s(sv, buf ^ 1);
+  };
+
+  using Fast = std::integral_constant<bool, false>;
+  using Guarded = std::integral_constant<bool, true>;
+  const int nfull = (int)((k_end - k_beg) / kGramK);  // steps with all 64 elements inside the chunk
+  u32x4 acur[2][2], anext[2][2], sv[SPT];
+  if (nfull > 0) {
+    load_s(0, sv, Fast{});
+    load_a(0, acur, Fast{});
+    store_s(sv, 0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nfull; ++st) {
+    const int buf = st & 1;
+    // the next full step's operands (clamped at the end: a harmless reload)
+    const int nx = min(st + 1, nfull - 1);
+    load_s(nx, sv, Fast{});
+    load_a(nx, anext, Fast{});
+    compute(st, buf, acur);
+    store_s(sv, buf ^ 1);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acur[mt][ks] = anext[mt][ks];
-    }
+      for (int ks = 0; ks < 2; ++ks) acur[mt][ks] = anext[mt][ks];
     __syncthreads();
+  }
+  if (nfull < nsteps) {
+    // the partial last step
+    const int buf = nfull & 1;
+    load_s(nfull, sv, Guarded{});
+    load_a(nfull, acur, Guarded{});
+    store_s(sv, buf);
+    __syncthreads();
+    compute(nfull, buf, acur);
   }
 
 #pragma unroll
@@ -305,15 +337,16 @@ CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t 
     // At most kMaxSteps K-steps per split, so that each partial dot product is a
     // short fp32 accumulation chain, and at least one workgroup per CU (one fits
     // at a time); among the step counts that allow, the one whose workgroups
-    // fill the last round of 256 best (then the fewest splits, which the
-    // finalize has to add).
+    // fill the rounds of 256 best (then the fewest splits, which the finalize
+    // has to add).
     constexpr int64_t kCus = 256;
     const int64_t s_lo = std::max<int64_t>((kblocks + kMaxSteps - 1) / kMaxSteps, (kCus + tiles - 1) / tiles);
     int64_t best_per = (kblocks + s_lo - 1) / s_lo;
     double best_eff = -1.0;
     for (int64_t per = std::max<int64_t>(1, best_per); per >= 1 && per >= best_per / 2; --per) {
-      const int64_t sp = (kblocks + per - 1) / per, wg = sp * tiles;
-      const double eff = (double)wg / (double)(((wg + kCus - 1) / kCus) * kCus);
+      // the grid deals splits to the 8 XCDs (whole groups of 8 splits)
+      const int64_t sp = (kblocks + per - 1) / per, wg = sp * tiles, slots = ((sp + 7) / 8) * 8 * tiles;
+      const double eff = (double)wg / (double)(((slots + kCus - 1) / kCus) * kCus);
       if (eff > best_eff + 1e-9) {
         best_eff = eff;
         best_per = per;
@@ -329,7 +362,7 @@ CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t 
 template <int NTH>
 static void gram_launch(const CosineArgs& a, hipStream_t st) {
   const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
-  dim3 grid(n_rtiles * a.splits, a.n_batch);
+  dim3 grid(kXcds * ((a.splits + kXcds - 1) / kXcds) * n_rtiles, a.n_batch);
   { KernelTimer kt_("k_gram_bf16", st); hipLaunchKernelGGL((k_gram_bf16<NTH>), grid, dim3(kGramThreads), 0, st, a); }
 }
 
