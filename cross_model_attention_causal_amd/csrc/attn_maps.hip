@@ -30,12 +30,17 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, const float p[4],
   }
 }
 
-// grid (n_block_rows, n_seqs, n_heads), 512 threads = 8 waves:
-// wave w owns queries 32*(w&1) .. +31 of the block-row and key blocks c = (w>>1) mod 4.
+// grid (n_block_rows, n_seqs, n_heads), 512 threads = 8 waves: wave w owns
+// queries 32 (w & 1) .. + 31 of the block-row and key blocks 4k + (w >> 1) of
+// each round of the staged K (kstage_pipeline: 4 key blocks x one feature half
+// per sub-step, the loads of the sub-step after next in flight). Dynamic LDS:
+// the two K stages.
 constexpr int kTileRow = 36;  // dwords per row of a wave's bf16 output tile (64 keys + pad)
 
 template <int D, bool PACKED, bool OUT_BF16>
 __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   __shared__ uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? 32 * kTileRow : 1];
   const int h = blockIdx.z, s = blockIdx.y;
   const int r = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest block-rows first
@@ -47,15 +52,17 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   const bool valid = i < nq;
   const int last = nk - nq + i;  // last visible key of this query
   const int rowmax = min(64 * r + 63, nq - 1);
-  const int cmax = (nk - nq + rowmax) >> 6;
+  const int cmax = (nk - nq + rowmax) >> 6;  // last key block of the block-row
+  // last key block of the wave's queries (past it every key is masked for them)
+  const int cmax_t = (nk - nq + min(64 * r + 32 * qt + 31, nq - 1)) >> 6;
 
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, nq - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
   const float scale_l2 = a.scale[h] * kLog2e;
   const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
 
   QOperand<D> qop;
-  load_query<D>(qop, qrow, valid);
+  load_query_clamped<D>(qop, qrow, valid);
 
   f32x16 acc[2];
   float m = -INFINITY, l = 0.0f;
@@ -64,25 +71,22 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   const bool raw_ok = scale_l2 > 0.0f;
   const int first_last = nk - nq + 64 * r + 32 * qt;  // last key of the wave's first query
   auto lean = [&](int c) { return raw_ok && c != 0 && 64 * c + 63 <= first_last; };
-  // Sweep 1: running max and sum; the next block's K is in flight meanwhile.
-  auto step1 = [&](const KTile<D>& cur, KTile<D>& nxt, int c) {
-    if (c + 4 <= cmax) load_k<D>(nxt, kseq, 64 * (c + 4), nk);
-    mma_k<D>(acc, cur, qop);
+  auto key0_of = [&](int c) { return 64 * min(c, cmax); };
+  // Sweep 1: running max and sum.
+  kstage_pipeline<D>(stage, kseq, nk, (cmax + 4) / 4, key0_of, [&](int k, const uint8_t* buf, auto fh) {
+    constexpr int FH = decltype(fh)::value;
+    const int c = 4 * k + kp;
+    if (c > cmax_t) return;
+    if (FH == 0) acc[0] = acc[1] = f32x16{};
+    kstage_mma<D, FH>(acc, buf + kp * kStageBlockBytes, qop);
+    if (FH != D / 64 - 1) return;
     if (lean(c)) {
       online_update_raw(acc, scale_l2, m, l);
     } else {
-      float t[32];
-      logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
-      online_update(t, m, l);
+      logits_inplace(acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+      online_update_acc(acc, m, l);
     }
-  };
-  KTile<D> kb0, kb1;
-  if (kp <= cmax) load_k<D>(kb0, kseq, 64 * kp, nk);
-  for (int c = kp; c <= cmax; c += 8) {
-    step1(kb0, kb1, c);
-    if (c + 4 > cmax) break;
-    step1(kb1, kb0, c + 4);
-  }
+  });
 
   __shared__ float sm[4][64], sl[4][64];
   if (lane < 32) {
@@ -108,22 +112,28 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   const int half = lane >> 5;
   // Sweep 2: recompute and write p = 2^(logit - lse); dense rows also get the
   // zeros of blocks past the diagonal.
-  auto step2 = [&](const KTile<D>& cur, KTile<D>& nxt, int c) {
-    if (c <= cmax) {
-      load_k<D>(nxt, kseq, 64 * c, nk);
-      mma_k<D>(acc, nxt, qop);
+  kstage_pipeline<D>(stage, kseq, nk, (cend + 4) / 4, key0_of, [&](int k, const uint8_t* buf, auto fh) {
+    constexpr int FH = decltype(fh)::value;
+    const int c = 4 * k + kp;
+    if (c > cend) return;
+    const bool comp = c <= cmax_t;
+    if (comp) {
+      if (FH == 0) acc[0] = acc[1] = f32x16{};
+      kstage_mma<D, FH>(acc, buf + kp * kStageBlockBytes, qop);
+    }
+    if (FH != D / 64 - 1) return;
+    if (comp) {
       if (lean(c)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(fmaf(acc[kt][v], scale_l2, -lse));
       } else {
-        float t[32];
-        logits_block(t, acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
+        logits_inplace(acc, 64 * c, valid ? last : -1, scale_l2, bias_l2);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(t[16 * kt + v] - lse);
+          for (int v = 0; v < 16; ++v) acc[kt][v] = exp2f_fast(acc[kt][v] - lse);
       }
     } else {
 #pragma unroll
@@ -133,9 +143,8 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
       // Through the wave's LDS tile, so that the global stores run along rows:
       // lane (query q, half) puts its 4-key groups at tile row q, then each pass
       // writes two rows (32 lanes per row) of the block's segment [64c, 64c + len)
-      // with 4-byte stores on the row's own element parity (a packed row may
-      // start at any element) and 2-byte stores for a leading or trailing odd
-      // entry.
+      // with 4-byte stores on the row's own alignment (a packed row may start at
+      // any element) and 2-byte stores for a leading or trailing odd entry.
       uint32_t* tw = wtile[wave];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -144,18 +153,18 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
           const u32x2 w = {pack2bf(acc[kt][4 * g], acc[kt][4 * g + 1]), pack2bf(acc[kt][4 * g + 2], acc[kt][4 * g + 3])};
           *reinterpret_cast<u32x2*>(&tw[(lane & 31) * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
         }
-      const int k = lane & 31, rsel = lane >> 5;
+      const int kl = lane & 31, rsel = lane >> 5;
       for (int p2 = 0; p2 < 16; ++p2) {
         const int qq = 2 * p2 + rsel;
         const int iq = 64 * r + 32 * qt + qq;
         const int len = iq < nq ? min(64, (PACKED ? nk - nq + iq + 1 : nk) - 64 * c) : 0;
         if (len <= 0) continue;
         uint16_t* out = reinterpret_cast<uint16_t*>(a.maps) + base0 + map_row_off(iq, nq, nk, PACKED) + 64 * c;
-        const int sh = (int)((reinterpret_cast<uintptr_t>(out) >> 1) & 1), j0 = sh + 2 * k;  // 4-byte phase
+        const int sh = (int)((reinterpret_cast<uintptr_t>(out) >> 1) & 1), j0 = sh + 2 * kl;  // 4-byte phase
         const uint16_t* trow = reinterpret_cast<const uint16_t*>(&tw[qq * kTileRow]);
         if (j0 + 1 < len) *reinterpret_cast<uint32_t*>(out + j0) = (uint32_t)trow[j0] | ((uint32_t)trow[j0 + 1] << 16);
         else if (j0 < len) out[j0] = trow[j0];
-        if (sh && k == 0) out[0] = trow[0];
+        if (sh && kl == 0) out[0] = trow[0];
       }
     } else {
       if (!valid) return;
@@ -170,12 +179,7 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
         }
       }
     }
-  };
-  for (int c = kp; c <= cend; c += 8) {
-    step2(kb0, kb1, c);
-    if (c + 4 > cend) break;
-    step2(kb1, kb0, c + 4);
-  }
+  });
 }
 
 // Single query rows (decode: one new token per sequence), bf16 inputs. One
@@ -316,14 +320,23 @@ __global__ __launch_bounds__(256) void k_attn_maps_f32(AttnMapsArgs a, int d) {
   }
 }
 
+template <int D, bool PACKED, bool OUT_BF16>
+static void maps_launch(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
+  const size_t lds = 2 * (size_t)kStageBytes;  // the two K stages
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_maps<D, PACKED, OUT_BF16>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  KernelTimer kt_("k_attn_maps", st);
+  hipLaunchKernelGGL((k_attn_maps<D, PACKED, OUT_BF16>), grid, dim3(512), lds, st, a);
+}
+
 template <int D>
 static hipError_t launch_bf16(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
   if (a.packed) {
-    if (a.out_bf16) { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, true, true>), grid, dim3(512), 0, st, a); }
-    else { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, true, false>), grid, dim3(512), 0, st, a); }
+    if (a.out_bf16) maps_launch<D, true, true>(a, grid, st);
+    else maps_launch<D, true, false>(a, grid, st);
   } else {
-    if (a.out_bf16) { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, false, true>), grid, dim3(512), 0, st, a); }
-    else { KernelTimer kt_("k_attn_maps", st); hipLaunchKernelGGL((k_attn_maps<D, false, false>), grid, dim3(512), 0, st, a); }
+    if (a.out_bf16) maps_launch<D, false, true>(a, grid, st);
+    else maps_launch<D, false, false>(a, grid, st);
   }
   return hipGetLastError();
 }

@@ -8,6 +8,8 @@
 // in groups of 4 consecutive keys, and its partner lane (lane ^ 32) sees the rest:
 // row reductions need one cross-lane exchange.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace cma {
@@ -149,6 +151,96 @@ __device__ __forceinline__ void kstage_mma(f32x16 acc[2], const uint8_t* blk, co
     }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32(as_bf16x8(x[kt]), qop.v[4 * FH + ks], acc[kt]);
+  }
+}
+
+// Per-sub-step K pipeline (attention maps, block statistics and extraction). A
+// sub-step is one feature half
+// of a round of 4 key blocks. Two LDS stages alternate; the global loads of
+// sub-step u + 2 are in flight (in registers) while sub-step u is computed, and
+// sub-step u + 1 (loaded one iteration earlier) is written to the other stage at
+// the end of the iteration, before the barrier that publishes it.
+template <int D, typename Key0, typename Body>
+__device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk,
+                                                int rounds, Key0 key0_of, Body body) {
+  constexpr int FH = D / 64;
+  const int nsub = rounds * FH;
+  auto load = [&](KStageRegs& rg, int u) {
+    int key0[4];
+    const int k = u / FH;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) key0[b] = key0_of(4 * k + b);
+    if (FH == 1 || u % FH == 0) kstage_load<D, 0>(rg, kseq, nk, key0);
+    else kstage_load<D, FH - 1>(rg, kseq, nk, key0);
+  };
+  auto run = [&](int u) {
+    const uint8_t* buf = stage + (u & 1) * kStageBytes;
+    if (FH == 1 || u % FH == 0) body(u / FH, buf, std::integral_constant<int, 0>{});
+    else body(u / FH, buf, std::integral_constant<int, FH - 1>{});
+  };
+  // iteration u: regs `mine` held sub-step u (already in LDS) and now fetch u + 2;
+  // regs `next` hold sub-step u + 1. Past the end the indices are clamped: the
+  // extra loads are harmless and keep the control flow (and so the compiler's
+  // wait counting) straight.
+  auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
+    load(mine, min(u + 2, nsub - 1));
+    run(u);
+    kstage_store(stage + ((u + 1) & 1) * kStageBytes, next);
+    barrier_lds();
+  };
+  if (nsub == 0) return;
+  KStageRegs r0, r1;
+  load(r0, 0);
+  load(r1, min(1, nsub - 1));
+  kstage_store(stage, r0);
+  barrier_lds();
+  for (int u = 0; u < nsub; u += 2) {
+    iter(r0, r1, u);
+    if (u + 1 >= nsub) break;
+    iter(r1, r0, u + 1);
+  }
+}
+
+// Whole-block K pipeline: a sub-step stages two key blocks with all their
+// features (block j in slots j * D / 64 .. + D / 64 - 1, one 64-feature half per
+// slot; with D = 64 slots 2 and 3 repeat slots 0 and 1), so that a wave finishes
+// one block per sub-step. Depth 2, as kstage_pipeline: the loads of sub-step
+// u + 2 are in flight while sub-step u is computed.
+template <int D>
+__device__ __forceinline__ void kstage_load2(KStageRegs& rg, const uint16_t* __restrict__ kseq, int nk, int key0a,
+                                             int key0b) {
+  constexpr int FHN = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = 8 * wave + (lane >> 3), s = lane & 7;
+  const int ch = s ^ ((m >> 1) & 7);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int blk = FHN == 2 ? (b >> 1) : (b & 1), fh = FHN == 2 ? (b & 1) : 0;
+    const int key = min((blk ? key0b : key0a) + m, nk - 1);
+    rg.x[b] = ldg16(kseq + (int64_t)key * D + 64 * fh + 8 * ch);
+  }
+}
+
+template <int D, typename Key0, typename Body>
+__device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk, int nsub,
+                                                 Key0 key0_of, Body body) {
+  auto load = [&](KStageRegs& rg, int u) { kstage_load2<D>(rg, kseq, nk, key0_of(2 * u), key0_of(2 * u + 1)); };
+  auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
+    load(mine, min(u + 2, nsub - 1));  // clamped past the end: harmless, keeps the control flow straight
+    body(u, stage + (u & 1) * kStageBytes);
+    kstage_store(stage + ((u + 1) & 1) * kStageBytes, next);
+    barrier_lds();
+  };
+  if (nsub == 0) return;
+  KStageRegs r0, r1;
+  load(r0, 0);
+  load(r1, min(1, nsub - 1));
+  kstage_store(stage, r0);
+  barrier_lds();
+  for (int u = 0; u < nsub; u += 2) {
+    iter(r0, r1, u);
+    if (u + 1 >= nsub) break;
+    iter(r1, r0, u + 1);
   }
 }
 
