@@ -30,7 +30,11 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, const float p[4],
   }
 }
 
-// grid (n_block_rows, n_seqs, n_heads), 512 threads = 8 waves: wave w owns
+// 1-D grid of 8 * ceil(n_seqs * n_heads / 8) * n_rb workgroups, dealt to the 8
+// XCDs round robin: workgroup b runs on XCD b % 8 and takes slot b / 8 there; the
+// n_rb consecutive slots of a (sequence, head) unit are its block-rows, longest
+// first, so the block-rows that re-read one K run on one XCD and share its L2.
+// 512 threads = 8 waves: wave w owns
 // queries 32 (w & 1) .. + 31 of the block-row and key blocks 4k + (w >> 1) of
 // each round of the staged K (kstage_pipeline: 4 key blocks x one feature half
 // per sub-step, the loads of the sub-step after next in flight). Dynamic LDS:
@@ -42,8 +46,11 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   __shared__ uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? 32 * kTileRow : 1];
-  const int h = blockIdx.z, s = blockIdx.y;
-  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest block-rows first
+  const int slot = (int)(blockIdx.x >> 3);
+  const int unit = 8 * (slot / a.n_rb) + (int)(blockIdx.x & 7);
+  if (unit >= a.vl.n_seqs * a.n_heads) return;
+  const int s = unit % a.vl.n_seqs, h = unit / a.vl.n_seqs;
+  const int r = a.n_rb - 1 - slot % a.n_rb;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || 64 * r >= nq) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -180,6 +187,282 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
       }
     }
   });
+}
+
+// ---- Short sequences (every sequence has at most 512 keys): one pass.
+// A persistent workgroup (one per CU) takes (sequence, head) units round robin
+// and walks each unit's block-rows in order. The unit's K stays resident in LDS
+// (up to 8 blocks in the staged layout, block c in slots c * D / 64 ..): block c
+// goes in just before the first block-row that sees it, so K crosses HBM -> LDS
+// once per unit. Wave (qt, kp) scores its 32 queries against key blocks kp and
+// kp + 4 and keeps both score blocks in registers, so a single softmax pass
+// suffices (no second sweep over K). The next block-row's new K block is fetched
+// while the current one is scored, and its queries while it is normalised and
+// written.
+constexpr int kShortKeys = 512;
+constexpr int kShortTileRows = 16;  // query rows per pass of a wave's bf16 output tile
+
+// Block c of a unit's K (keys clamped to nk - 1) as 512 threads move it: wave w
+// keys 8w .. 8w + 7, one 16-byte chunk per lane and feature half.
+template <int D>
+__device__ __forceinline__ void kblock_load(u32x4 x[D / 64], const uint16_t* __restrict__ kseq, int nk, int c) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = 8 * wave + (lane >> 3), ch = (lane & 7) ^ ((m >> 1) & 7);
+  const int key = min(64 * c + m, nk - 1);
+#pragma unroll
+  for (int f = 0; f < D / 64; ++f) x[f] = ldg16(kseq + (int64_t)key * D + 64 * f + 8 * ch);
+}
+template <int D>
+__device__ __forceinline__ void kblock_store(uint8_t* kres, int c, const u32x4 x[D / 64]) {
+#pragma unroll
+  for (int f = 0; f < D / 64; ++f)
+    *reinterpret_cast<u32x4*>(kres + (c * (D / 64) + f) * kStageBlockBytes + 16 * threadIdx.x) = x[f];
+}
+
+// Largest logit of a score block: raw scores times `scl` (> 0; 1 for blocks
+// already turned into logits).
+__device__ __forceinline__ float block_max(const f32x16 acc[2], float scl) {
+  float b4[4] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3]};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = kt ? 0 : 4; v < 16; ++v) b4[v & 3] = fmaxf(b4[v & 3], acc[kt][v]);
+  return fmaxf(fmaxf(b4[0], b4[1]), fmaxf(b4[2], b4[3])) * scl;
+}
+// acc <- 2^(acc * scl - m) in place; returns this lane's sum of them.
+__device__ __forceinline__ float block_exp2(f32x16 acc[2], float scl, float m) {
+  float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc[kt][v] = exp2f_fast(fmaf(acc[kt][v], scl, -m));
+      s4[v & 3] += acc[kt][v];
+    }
+  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+template <int D, bool PACKED, bool OUT_BF16>
+__global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
+  constexpr int FHN = D / 64;
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  uint8_t* kres = reinterpret_cast<uint8_t*>(dyn);
+  __shared__ uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? kShortTileRows * kTileRow : 1];
+  __shared__ float sm[4][64], sl[4][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int qt = wave & 1, kp = wave >> 1, half = lane >> 5;
+  const int n_seqs = a.vl.n_seqs, n_units = n_seqs * a.n_heads, stride = gridDim.x;
+
+  // block-rows of unit u; a unit with more keys than the resident K holds is
+  // not computed (the lengths must not exceed the maxima the caller passes)
+  auto rows_of = [&](int u) {
+    const int sq = u % n_seqs;
+    const int32_t nq = seq_len_q(a.vl, sq), nk = seq_len_k(a.vl, sq);
+    return seq_ok(a.vl, sq, nq, nk) && nq > 0 && nk <= kShortKeys ? (nq + 63) >> 6 : 0;
+  };
+  // (u, r) -> the workgroup's next item; u = n_units when none is left
+  auto advance = [&](int& u, int& r) {
+    if (r + 1 < rows_of(u)) {
+      ++r;
+      return;
+    }
+    r = 0;
+    for (u += stride; u < n_units && rows_of(u) == 0; u += stride) {
+    }
+  };
+  // last key block seen by block-row r
+  auto cmax_of = [](int r, int nq, int nk) { return (nk - nq + min(64 * r + 63, nq - 1)) >> 6; };
+
+  int u = blockIdx.x, r = 0;
+  while (u < n_units && rows_of(u) == 0) u += stride;
+  if (u >= n_units) return;
+  QOperand<D> qop;
+  {
+    const int s = u % n_seqs, h = u / n_seqs;
+    const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+    const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
+    const int c_hi = cmax_of(0, nq, nk);
+    for (int c = 0; c <= c_hi; ++c) {
+      u32x4 x[FHN];
+      kblock_load<D>(x, kseq, nk, c);
+      kblock_store<D>(kres, c, x);
+    }
+    const int i = 32 * qt + (lane & 31);
+    load_query_clamped<D>(qop, a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, nq - 1)) * D, i < nq);
+  }
+  barrier_lds();
+
+  while (true) {
+    const int s = u % n_seqs, h = u / n_seqs;
+    const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+    const int i = 64 * r + 32 * qt + (lane & 31);
+    const bool valid = i < nq;
+    const int last = nk - nq + i;
+    const int cmax = cmax_of(r, nq, nk);
+    const int cmax_t = (nk - nq + min(64 * r + 32 * qt + 31, nq - 1)) >> 6;
+    const int cend = PACKED ? cmax : (nk - 1) >> 6;
+    const float scale_l2 = a.scale[h] * kLog2e;
+    const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+    const bool raw_ok = scale_l2 > 0.0f;
+    const int first_last = nk - nq + 64 * r + 32 * qt;
+    auto lean = [&](int c) { return raw_ok && c != 0 && 64 * c + 63 <= first_last; };
+
+    // next item and the K blocks it adds; its first new block is fetched now
+    int un = u, rn = r;
+    advance(un, rn);
+    const bool more = un < n_units;
+    const int sn = more ? un % n_seqs : s, hn = more ? un / n_seqs : h;
+    const int32_t nqn = seq_len_q(a.vl, sn), nkn = seq_len_k(a.vl, sn);
+    const uint16_t* kseq_n = a.k + ((int64_t)hn * a.vl.total_k + a.vl.cu_k[sn]) * D;
+    const int lo_n = !more ? 0 : (un == u ? cmax + 1 : 0);
+    const int hi_n = !more ? -1 : cmax_of(rn, nqn, nkn);
+    u32x4 kx[FHN];
+    kblock_load<D>(kx, kseq_n, nkn, lo_n);  // always a valid address (keys clamped)
+
+    // scores of blocks kp and kp + 4
+    f32x16 acc0[2], acc1[2];
+    const int c0 = kp, c1 = kp + 4;
+    const bool has0 = c0 <= cmax_t, has1 = c1 <= cmax_t;
+    acc0[0] = acc0[1] = acc1[0] = acc1[1] = f32x16{};
+    if (has0) {
+      kstage_mma<D, 0>(acc0, kres + (c0 * FHN) * kStageBlockBytes, qop);
+      if constexpr (FHN == 2) kstage_mma<D, 1>(acc0, kres + (c0 * FHN + 1) * kStageBlockBytes, qop);
+    }
+    if (has1) {
+      kstage_mma<D, 0>(acc1, kres + (c1 * FHN) * kStageBlockBytes, qop);
+      if constexpr (FHN == 2) kstage_mma<D, 1>(acc1, kres + (c1 * FHN + 1) * kStageBlockBytes, qop);
+    }
+    // queries of the next item (this item's are no longer needed)
+    {
+      const int in = 64 * rn + 32 * qt + (lane & 31);
+      load_query_clamped<D>(qop, a.q + ((int64_t)hn * a.vl.total_q + a.vl.cu_q[sn] + min(in, nqn - 1)) * D,
+                            more && in < nqn);
+    }
+
+    // softmax statistics of the wave's two blocks: one max over both, then the
+    // blocks become 2^(logit - m) in place and l is their sum
+    const bool lean0 = lean(c0), lean1 = lean(c1);
+    if (has0 && !lean0) logits_inplace(acc0, 64 * c0, valid ? last : -1, scale_l2, bias_l2);
+    if (has1 && !lean1) logits_inplace(acc1, 64 * c1, valid ? last : -1, scale_l2, bias_l2);
+    float m = -INFINITY;
+    if (has0) m = fmaxf(m, block_max(acc0, lean0 ? scale_l2 : 1.0f));
+    if (has1) m = fmaxf(m, block_max(acc1, lean1 ? scale_l2 : 1.0f));
+    m = fmaxf(m, xor_lane(m, 32));
+    const float ms = m == -INFINITY ? 0.0f : m;  // every logit -inf: the powers are 0
+    float l = 0.0f;
+    if (has0) l += block_exp2(acc0, lean0 ? scale_l2 : 1.0f, ms);
+    if (has1) l += block_exp2(acc1, lean1 ? scale_l2 : 1.0f, ms);
+    l += xor_lane(l, 32);
+    if (lane < 32) {
+      sm[kp][32 * qt + lane] = m;
+      sl[kp][32 * qt + lane] = l;
+    }
+    barrier_lds();
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][32 * qt + (lane & 31)]);
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = sm[w][32 * qt + (lane & 31)];
+      if (mw != -INFINITY) L += sl[w][32 * qt + (lane & 31)] * exp2f_fast(mw - M);
+    }
+    // p = 2^(logit - m) * 2^(m - M) / L
+    const float fac = m == -INFINITY ? 0.0f : exp2f_fast(m - M) * __builtin_amdgcn_rcpf(L);
+    // every wave is past its reads of the resident K: the next item's blocks go in
+    if (hi_n >= lo_n) {
+      kblock_store<D>(kres, lo_n, kx);
+      for (int c = lo_n + 1; c <= hi_n; ++c) {  // a unit whose first block-row sees several blocks
+        u32x4 x[FHN];
+        kblock_load<D>(x, kseq_n, nkn, c);
+        kblock_store<D>(kres, c, x);
+      }
+    }
+    barrier_lds();
+
+    // normalise and write blocks kp and kp + 4 (zeros past the diagonal of a dense row)
+    const int64_t base0 = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = kp + 4 * j;
+      if (c > cend) continue;
+      f32x16* acc = j ? acc1 : acc0;
+      const float f = c <= cmax_t ? fac : 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[kt][v] *= f;
+      if constexpr (OUT_BF16) {
+        // Through the wave's LDS tile, 16 query rows at a time: lane (query q,
+        // half) puts its 4-key groups at tile row q % 16, then each of 8 passes
+        // writes two rows (32 lanes per row) of the block's segment
+        // [64c, 64c + len) with 4-byte stores on the row's own alignment (a packed
+        // row may start at any element) and 2-byte stores for a leading or
+        // trailing odd entry. The stores go through a descriptor over this
+        // (head, sequence) map; lanes with nothing to write use an offset past it.
+        uint16_t* region = reinterpret_cast<uint16_t*>(a.maps) + base0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            region, (short)0, (int)(2 * map_elems(nq, nk, PACKED)), kBufferFlags);
+        const int pbase = (int)((reinterpret_cast<uintptr_t>(region) >> 1) & 1);
+        uint32_t* tw = wtile[wave];
+        const int kl = lane & 31, rsel = lane >> 5;
+        const uint8_t* trow0 = reinterpret_cast<const uint8_t*>(tw) + rsel * kTileRow * 4;
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          if (((lane & 31) >> 4) == qh) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const u32x2 w = {pack2bf(acc[kt][4 * g], acc[kt][4 * g + 1]),
+                                 pack2bf(acc[kt][4 * g + 2], acc[kt][4 * g + 3])};
+                *reinterpret_cast<u32x2*>(&tw[(lane & 15) * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
+              }
+          }
+          // row iq = iq0 + 2 p2: element offset e of its block segment and its
+          // entry count, both stepped two rows at a time
+          const int iq0 = 64 * r + 32 * qt + 16 * qh + rsel;
+          int e = (int)map_row_off(iq0, nq, nk, PACKED) + 64 * c;
+          int rl = (PACKED ? nk - nq + iq0 + 1 : nk) - 64 * c;
+          int de = PACKED ? 2 * (nk - nq) + 2 * iq0 + 3 : 2 * nk;
+#pragma unroll
+          for (int p2 = 0; p2 < kShortTileRows / 2; ++p2) {
+            const int len = iq0 + 2 * p2 < nq ? min(64, rl) : 0;
+            const int sh = (pbase + e) & 1, j0 = sh | (2 * kl);
+            const uint8_t* trow = trow0 + p2 * (2 * kTileRow * 4);
+            const uint32_t lo = *reinterpret_cast<const uint16_t*>(trow + 2 * j0);
+            const uint32_t hi = *reinterpret_cast<const uint16_t*>(trow + 2 * j0 + 2);
+            const uint32_t t0 = *reinterpret_cast<const uint16_t*>(trow);
+            const uint32_t ob = 2u * (uint32_t)(e + j0);
+            __builtin_amdgcn_raw_buffer_store_b32(lo | (hi << 16), rs, j0 + 1 < len ? ob : kBufferOff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)lo, rs, j0 < len && j0 + 1 >= len ? ob : kBufferOff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)t0, rs, sh && kl == 0 && len > 0 ? 2u * (uint32_t)e : kBufferOff,
+                                                  0, 0);
+            e += de;
+            de += PACKED ? 4 : 0;
+            rl += PACKED ? 2 : 0;
+          }
+        }
+      } else {
+        if (valid) {
+          const int wend = PACKED ? last + 1 : nk;
+          const int64_t base = base0 + map_row_off(i, nq, nk, PACKED);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int key0 = 64 * c + 32 * kt + 8 * g + 4 * half;
+              const float p[4] = {acc[kt][4 * g], acc[kt][4 * g + 1], acc[kt][4 * g + 2], acc[kt][4 * g + 3]};
+              const int cnt = max(0, min(4, wend - key0));
+              if (cnt > 0) store4<OUT_BF16>(a.maps, base + key0, p, cnt);
+            }
+        }
+      }
+    }
+    if (!more) break;
+    u = un;
+    r = rn;
+  }
 }
 
 // Single query rows (decode: one new token per sequence), bf16 inputs. One
@@ -329,8 +612,50 @@ static void maps_launch(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((k_attn_maps<D, PACKED, OUT_BF16>), grid, dim3(512), lds, st, a);
 }
 
+// Compute units of the current device (one persistent workgroup each).
+static int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int D, bool PACKED, bool OUT_BF16>
+static void short_launch(const AttnMapsArgs& a, int n_wg, hipStream_t st) {
+  const size_t lds = (size_t)8 * (D / 64) * kStageBlockBytes;  // the resident K
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_maps_short<D, PACKED, OUT_BF16>),
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  KernelTimer kt_("k_attn_maps_short", st);
+  hipLaunchKernelGGL((k_attn_maps_short<D, PACKED, OUT_BF16>), dim3(n_wg), dim3(512), lds, st, a);
+}
+
 template <int D>
-static hipError_t launch_bf16(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t launch_short(const AttnMapsArgs& a, hipStream_t st) {
+  const int64_t units = (int64_t)a.vl.n_seqs * a.n_heads;
+  if (units > INT32_MAX) return hipErrorInvalidValue;
+  const int n_wg = (int)std::min<int64_t>(units, cu_count());
+  if (a.packed) {
+    if (a.out_bf16) short_launch<D, true, true>(a, n_wg, st);
+    else short_launch<D, true, false>(a, n_wg, st);
+  } else {
+    if (a.out_bf16) short_launch<D, false, true>(a, n_wg, st);
+    else short_launch<D, false, false>(a, n_wg, st);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bf16(AttnMapsArgs a, int max_q, hipStream_t st) {
+  a.n_rb = (max_q + 63) / 64;
+  const int64_t units = (int64_t)a.vl.n_seqs * a.n_heads;
+  const int64_t n_wg = 8 * ((units + 7) / 8) * a.n_rb;
+  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg);
   if (a.packed) {
     if (a.out_bf16) maps_launch<D, true, true>(a, grid, st);
     else maps_launch<D, true, false>(a, grid, st);
@@ -363,9 +688,9 @@ hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, int max_k, 
     // every sequence has at most one query row (decode)
     return d == 64 ? launch_rows<64>(a, max_k, st) : launch_rows<128>(a, max_k, st);
   }
+  if (a.in_bf16 && max_k <= kShortKeys) return d == 64 ? launch_short<64>(a, st) : launch_short<128>(a, st);
   if (a.in_bf16) {
-    dim3 grid((max_q + 63) / 64, a.vl.n_seqs, a.n_heads);
-    return d == 64 ? launch_bf16<64>(a, grid, st) : launch_bf16<128>(a, grid, st);
+    return d == 64 ? launch_bf16<64>(a, max_q, st) : launch_bf16<128>(a, max_q, st);
   }
   dim3 grid(max_q, a.vl.n_seqs, a.n_heads);
   if (a.packed) { KernelTimer kt_("k_attn_maps_f32", st); hipLaunchKernelGGL((k_attn_maps_f32<true>), grid, dim3(256), 0, st, a, d); }

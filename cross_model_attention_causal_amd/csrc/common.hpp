@@ -85,6 +85,11 @@ __device__ __forceinline__ u32x4 ldg16_guard_any(const uint16_t* row, int64_t j0
   return r;
 }
 
+// Buffer descriptor word 3 for raw (unformatted) accesses on gfx9-family chips.
+// Accesses at or past num_records bytes read zero and drop their writes.
+constexpr int kBufferFlags = 0x00020000;
+constexpr uint32_t kBufferOff = 0x80000000u;  // an offset past any descriptor used here
+
 // ------------------------------------------------------------------ cross-lane
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 

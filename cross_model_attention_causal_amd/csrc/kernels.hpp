@@ -26,6 +26,7 @@ struct AttnMapsArgs {
   int32_t n_heads;
   bool in_bf16, out_bf16, packed;
   int32_t rows_cap;  // single-row path: keys its LDS holds (set by the launcher)
+  int32_t n_rb;      // block-row slots per (sequence, head) (set by the launcher)
 };
 hipError_t launch_attn_maps(const AttnMapsArgs& a, int d, int max_q, int max_k, hipStream_t st);
 

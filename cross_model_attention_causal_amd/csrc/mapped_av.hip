@@ -46,8 +46,6 @@ constexpr int kBH = 520;             // bf16 per head of a mixed panel: 32 rows 
 constexpr int kBBuf = 16 * kBH;      // one mixed panel, 16 head slots (the mix's M rows)
 constexpr int kMaxCols = 256;        // block columns per sequence (16384 tokens)
 constexpr uint16_t kNoBlock = 0xffff;
-// buffer descriptor word 3 for raw (unformatted) 32-bit accesses on gfx9-family chips
-constexpr int kBufferFlags = 0x00020000;
 
 // V in the fused kernel's operand order ("tiled"): for head h and 64-key block b
 // of the block grid (sequence s's blocks start at its block-row offset, as in

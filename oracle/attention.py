@@ -35,6 +35,8 @@ def causal_map(q, k, scale, bias=0.0):
     nq, nk = q.shape[0], k.shape[0]
     if nq > nk:
         raise ValueError("more queries than keys")
+    if nq == 0:  # a sequence with no query rows has an empty map
+        return np.zeros((0, nk))
     s = float(scale) * (q @ k.T)
     if nk > 0:
         s[:, 0] += float(bias)

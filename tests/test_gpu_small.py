@@ -73,12 +73,24 @@ def test_cfg1_tiny_fp32_all_stages(cma):
 
 
 # ------------------------------------------------------------------ attn_maps bf16
+# "short": every sequence has at most 512 keys (the one-pass kernel, K resident in
+# LDS), with an empty sequence; "long": one sequence past 512 keys (the two-sweep
+# kernel); "prefix": more keys than queries, so a unit's first block-row already
+# sees several key blocks.
+ATTN_CASES = {
+    "short": ([130, 64, 0, 7, 200], None),
+    "long": ([600, 64, 7, 200], None),
+    "prefix": ([130, 64, 7, 200], [300, 64, 100, 512]),
+}
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("layout", ["packed", "dense"])
-def test_attn_maps_bf16_varlen(cma, d, layout):
-    lens = [130, 64, 7, 200]
-    say(f"attn_maps bf16 d={d} layout={layout} lens={lens}")
-    x = synth.attention_inputs(101 + d, 5, lens, d=d)
+@pytest.mark.parametrize("case", list(ATTN_CASES))
+def test_attn_maps_bf16_varlen(cma, d, layout, case):
+    lens, klens = ATTN_CASES[case]
+    say(f"attn_maps bf16 d={d} layout={layout} case={case} lens={lens} k_lens={klens}")
+    x = synth.attention_inputs(101 + d, 5, lens, d=d, k_lengths=klens)
     vl = cma.Varlen(x["cu_q"], x["cu_k"])
     lay = cma.PACKED if layout == "packed" else cma.DENSE
     outs = {}

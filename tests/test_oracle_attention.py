@@ -81,6 +81,26 @@ def test_varlen_is_concatenation():
             assert np.array_equal(maps[h][s], oracle.causal_map(q[h, sl], k[h, sl], scale[h], bias[h]))
 
 
+def test_empty_sequences_in_batch():
+    """A sequence with no query rows has an empty map (0 rows, its key count wide),
+    packs to nothing and leaves the other sequences' maps unchanged."""
+    r = np.random.default_rng(4)
+    lq, lk = [5, 0, 0, 9], [5, 0, 4, 12]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    q = r.standard_normal((2, cq[-1], 8))
+    k = r.standard_normal((2, ck[-1], 8))
+    scale, bias = np.array([0.5, 1.0]), np.array([4.0, 0.0])
+    maps = oracle.attn_maps(q, k, scale, bias, cq, ck)
+    for h in range(2):
+        assert maps[h][1].shape == (0, 0) and maps[h][2].shape == (0, 4)
+        assert oracle.pack_rows(maps[h][2]).size == 0 == oracle.packed_size(0, 4)
+        for s in (0, 3):
+            want = oracle.causal_map(q[h, cq[s]:cq[s + 1]], k[h, ck[s]:ck[s + 1]], scale[h], bias[h])
+            assert np.array_equal(maps[h][s], want)
+            assert np.allclose(want.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+
+
 def test_identity_against_torch_sdpa():
     """Library special case: map @ V equals torch's scaled_dot_product_attention (float64, CPU)."""
     r = np.random.default_rng(11)
