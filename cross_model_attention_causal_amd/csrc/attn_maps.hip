@@ -45,7 +45,7 @@ template <int D, bool PACKED, bool OUT_BF16>
 __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
-  __shared__ uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? 32 * kTileRow : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? 32 * kTileRow : 1];
   const int slot = (int)(blockIdx.x >> 3);
   const int unit = 8 * (slot / a.n_rb) + (int)(blockIdx.x & 7);
   if (unit >= a.vl.n_seqs * a.n_heads) return;
@@ -153,6 +153,7 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
       // with 4-byte stores on the row's own alignment (a packed row may start at
       // any element) and 2-byte stores for a leading or trailing odd entry.
       uint32_t* tw = wtile[wave];
+      wave_lds_fence();  // the previous block's reads of the tile come first
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
           const u32x2 w = {pack2bf(acc[kt][4 * g], acc[kt][4 * g + 1]), pack2bf(acc[kt][4 * g + 2], acc[kt][4 * g + 3])};
           *reinterpret_cast<u32x2*>(&tw[(lane & 31) * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
         }
+      wave_lds_fence();  // rows are read by other lanes
       const int kl = lane & 31, rsel = lane >> 5;
       for (int p2 = 0; p2 < 16; ++p2) {
         const int qq = 2 * p2 + rsel;
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
   constexpr int FHN = D / 64;
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   uint8_t* kres = reinterpret_cast<uint8_t*>(dyn);
-  __shared__ uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? kShortTileRows * kTileRow : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? kShortTileRows * kTileRow : 1];
   __shared__ float sm[4][64], sl[4][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int qt = wave & 1, kp = wave >> 1, half = lane >> 5;
@@ -394,21 +396,24 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
         for (int v = 0; v < 16; ++v) acc[kt][v] *= f;
       if constexpr (OUT_BF16) {
         // Through the wave's LDS tile, 16 query rows at a time: lane (query q,
-        // half) puts its 4-key groups at tile row q % 16, then each of 8 passes
-        // writes two rows (32 lanes per row) of the block's segment
-        // [64c, 64c + len) with 4-byte stores on the row's own alignment (a packed
-        // row may start at any element) and 2-byte stores for a leading or
-        // trailing odd entry. The stores go through a descriptor over this
-        // (head, sequence) map; lanes with nothing to write use an offset past it.
+        // half) puts its 4-key groups at tile row q % 16; then each of 2 passes
+        // writes 8 rows, 8 lanes per row and 8 entries per lane, of the block's
+        // segment [64c, 64c + len). Stores need 4-byte alignment and a packed row
+        // may start at any element, so a lane's 8 entries start at j0 = sh + 8 k
+        // (sh: the row's 2-byte phase) and are cut from the tile with a byte
+        // shift; the leading entry of an odd-phase row and the partial end of a
+        // row go out in 2-, 4- and 8-byte pieces. The stores use a descriptor over
+        // this (head, sequence) map; lanes with nothing to write use an offset
+        // past it.
         uint16_t* region = reinterpret_cast<uint16_t*>(a.maps) + base0;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             region, (short)0, (int)(2 * map_elems(nq, nk, PACKED)), kBufferFlags);
         const int pbase = (int)((reinterpret_cast<uintptr_t>(region) >> 1) & 1);
         uint32_t* tw = wtile[wave];
-        const int kl = lane & 31, rsel = lane >> 5;
-        const uint8_t* trow0 = reinterpret_cast<const uint8_t*>(tw) + rsel * kTileRow * 4;
+        const int k8 = lane & 7, rr = lane >> 3;
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
+          wave_lds_fence();  // the previous half's reads of the tile come first
           if (((lane & 31) >> 4) == qh) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
@@ -419,28 +424,33 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
                 *reinterpret_cast<u32x2*>(&tw[(lane & 15) * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
               }
           }
-          // row iq = iq0 + 2 p2: element offset e of its block segment and its
-          // entry count, both stepped two rows at a time
-          const int iq0 = 64 * r + 32 * qt + 16 * qh + rsel;
-          int e = (int)map_row_off(iq0, nq, nk, PACKED) + 64 * c;
-          int rl = (PACKED ? nk - nq + iq0 + 1 : nk) - 64 * c;
-          int de = PACKED ? 2 * (nk - nq) + 2 * iq0 + 3 : 2 * nk;
+          wave_lds_fence();  // rows are read by other lanes
 #pragma unroll
-          for (int p2 = 0; p2 < kShortTileRows / 2; ++p2) {
-            const int len = iq0 + 2 * p2 < nq ? min(64, rl) : 0;
-            const int sh = (pbase + e) & 1, j0 = sh | (2 * kl);
-            const uint8_t* trow = trow0 + p2 * (2 * kTileRow * 4);
-            const uint32_t lo = *reinterpret_cast<const uint16_t*>(trow + 2 * j0);
-            const uint32_t hi = *reinterpret_cast<const uint16_t*>(trow + 2 * j0 + 2);
-            const uint32_t t0 = *reinterpret_cast<const uint16_t*>(trow);
+          for (int p = 0; p < kShortTileRows / 8; ++p) {
+            const int qq = 8 * p + rr;  // tile row
+            const int iq = 64 * r + 32 * qt + 16 * qh + qq;
+            const int e = (int)map_row_off(iq, nq, nk, PACKED) + 64 * c;  // segment start (element)
+            const int len = iq < nq ? min(64, (PACKED ? nk - nq + iq + 1 : nk) - 64 * c) : 0;
+            const int sh = (pbase + e) & 1, j0 = sh + 8 * k8;
+            const uint32_t* trow = tw + qq * kTileRow + 4 * k8;
+            const u32x4 w4 = *reinterpret_cast<const u32x4*>(trow);
+            const uint32_t w5 = trow[4];
+            // entries j0 + 2k, j0 + 2k + 1: the tile's dwords shifted down by sh entries
+            auto cut = [sh](uint32_t hi, uint32_t lo) { return sh ? (lo >> 16) | (hi << 16) : lo; };
+            const uint32_t d0 = cut(w4[1], w4[0]), d1 = cut(w4[2], w4[1]);
+            const uint32_t d2 = cut(w4[3], w4[2]), d3 = cut(w5, w4[3]);
             const uint32_t ob = 2u * (uint32_t)(e + j0);
-            __builtin_amdgcn_raw_buffer_store_b32(lo | (hi << 16), rs, j0 + 1 < len ? ob : kBufferOff, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)lo, rs, j0 < len && j0 + 1 >= len ? ob : kBufferOff, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)t0, rs, sh && kl == 0 && len > 0 ? 2u * (uint32_t)e : kBufferOff,
+            const int n = len - j0;  // entries of this lane's 8 inside the segment
+            const bool part = n > 0 && n < 8;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{d0, d1, d2, d3}, rs, n >= 8 ? ob : kBufferOff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{d0, d1}, rs, part && n >= 4 ? ob : kBufferOff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(n >= 4 ? d2 : d0, rs, part && (n & 2) ? ob + (n >= 4 ? 8u : 0u) : kBufferOff,
                                                   0, 0);
-            e += de;
-            de += PACKED ? 4 : 0;
-            rl += PACKED ? 2 : 0;
+            const uint32_t dt = n >= 6 ? d3 : n >= 4 ? d2 : n >= 2 ? d1 : d0;  // holds entry n - 1 in its low half
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)dt, rs, part && (n & 1) ? ob + 2u * (uint32_t)(n - 1) : kBufferOff,
+                                                  0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w4[0], rs, sh && k8 == 0 && len > 0 ? 2u * (uint32_t)e : kBufferOff,
+                                                  0, 0);
           }
         }
       } else {

@@ -102,6 +102,15 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
+// Point between LDS accesses of different lanes of one wave (one lane writes
+// what another reads). The hardware runs a wave's LDS instructions in issue
+// order, so only the compiler has to be kept from moving accesses across this
+// point or reusing values loaded before it.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ packed sequences
 struct Varlen {
   int32_t n_seqs;
