@@ -63,10 +63,10 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   // last key block of the wave's queries (past it every key is masked for them)
   const int cmax_t = (nk - nq + min(64 * r + 32 * qt + 31, nq - 1)) >> 6;
 
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, nq - 1)) * D;
-  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
-  const float scale_l2 = a.scale[h] * kLog2e;
-  const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + min(i, nq - 1)) * D;
+  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
+  const float scale_l2 = ld_const(a.scale + h) * kLog2e;
+  const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
 
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);
@@ -275,14 +275,32 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
   // last key block seen by block-row r
   auto cmax_of = [](int r, int nq, int nk) { return (nk - nq + min(64 * r + 63, nq - 1)) >> 6; };
 
-  int u = blockIdx.x, r = 0;
-  while (u < n_units && rows_of(u) == 0) u += stride;
-  if (u >= n_units) return;
-  QOperand<D> qop;
+  // Items of this workgroup: j (being computed) at (u0, r0), then (u1, r1) and
+  // (u2, r2); u == n_units: none. Item j computes with the queries fetched during
+  // item j - 1 and fetches those of item j + 1; it stores the K block of item
+  // j + 1 fetched during item j - 1 and fetches that of item j + 2. Two register
+  // sets alternate between consecutive items.
+  int u0 = blockIdx.x, r0 = 0;
+  while (u0 < n_units && rows_of(u0) == 0) u0 += stride;
+  if (u0 >= n_units) return;
+  int u1 = u0, r1 = r0;
+  advance(u1, r1);
+  int u2 = u1, r2 = r1;
+  if (u2 < n_units) advance(u2, r2);
+  auto kseq_of = [&](int u) {
+    return a.k + ((int64_t)(u / n_seqs) * a.vl.total_k + cu_k_of(a.vl, u % n_seqs)) * D;
+  };
+  // first K block that item (un, rn) adds after item (u, r) (both exist)
+  auto first_new = [&](int u, int r, int un, int rn) {
+    const int sq = u % n_seqs;
+    return un == u ? cmax_of(r, seq_len_q(a.vl, sq), seq_len_k(a.vl, sq)) + 1 : 0;
+  };
+  QOperand<D> qa, qb;
+  u32x4 ka[FHN], kb[FHN];
   {
-    const int s = u % n_seqs, h = u / n_seqs;
+    const int s = u0 % n_seqs, h = u0 / n_seqs;
     const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
-    const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
+    const uint16_t* kseq = kseq_of(u0);
     const int c_hi = cmax_of(0, nq, nk);
     for (int c = 0; c <= c_hi; ++c) {
       u32x4 x[FHN];
@@ -290,36 +308,39 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
       kblock_store<D>(kres, c, x);
     }
     const int i = 32 * qt + (lane & 31);
-    load_query_clamped<D>(qop, a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, nq - 1)) * D, i < nq);
+    load_query_rows<D>(qa, a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + min(i, nq - 1)) * D);
+    // item 1's first new block (a valid address in any case: keys clamped)
+    const int un = u1 < n_units ? u1 : u0;
+    const int sn = un % n_seqs;
+    kblock_load<D>(ka, kseq_of(un), seq_len_k(a.vl, sn), u1 < n_units ? first_new(u0, r0, u1, r1) : 0);
+    // Stores through a descriptor of zero bytes (they write nothing), as many as
+    // an item issues: the compiler sizes the waits at the loop head by the path
+    // into it with the fewest vector memory operations after a load, so without
+    // them the entry path would make every item wait for the previous item's
+    // stores before its first product.
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.maps, (short)0, 0, kBufferFlags);
+#pragma unroll
+    for (int t = 0; t < 48; ++t) __builtin_amdgcn_raw_buffer_store_b32(0u, none, kBufferOff + 4u * t, 0, 0);
   }
   barrier_lds();
 
-  while (true) {
+  // one item; returns whether another follows
+  auto item = [&](const QOperand<D>& qop, QOperand<D>& qnext, const u32x4* kcur, u32x4* knext) {
+    const int u = u0, r = r0;
     const int s = u % n_seqs, h = u / n_seqs;
     const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
     const int i = 64 * r + 32 * qt + (lane & 31);
-    const bool valid = i < nq;
+    const bool valid = i < nq;  // rows past the end score a copy of the last row; never stored
     const int last = nk - nq + i;
     const int cmax = cmax_of(r, nq, nk);
     const int cmax_t = (nk - nq + min(64 * r + 32 * qt + 31, nq - 1)) >> 6;
     const int cend = PACKED ? cmax : (nk - 1) >> 6;
-    const float scale_l2 = a.scale[h] * kLog2e;
-    const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+    const float scale_l2 = ld_const(a.scale + h) * kLog2e;
+    const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
     const bool raw_ok = scale_l2 > 0.0f;
     const int first_last = nk - nq + 64 * r + 32 * qt;
     auto lean = [&](int c) { return raw_ok && c != 0 && 64 * c + 63 <= first_last; };
-
-    // next item and the K blocks it adds; its first new block is fetched now
-    int un = u, rn = r;
-    advance(un, rn);
-    const bool more = un < n_units;
-    const int sn = more ? un % n_seqs : s, hn = more ? un / n_seqs : h;
-    const int32_t nqn = seq_len_q(a.vl, sn), nkn = seq_len_k(a.vl, sn);
-    const uint16_t* kseq_n = a.k + ((int64_t)hn * a.vl.total_k + a.vl.cu_k[sn]) * D;
-    const int lo_n = !more ? 0 : (un == u ? cmax + 1 : 0);
-    const int hi_n = !more ? -1 : cmax_of(rn, nqn, nkn);
-    u32x4 kx[FHN];
-    kblock_load<D>(kx, kseq_n, nkn, lo_n);  // always a valid address (keys clamped)
+    const bool more = u1 < n_units;
 
     // scores of blocks kp and kp + 4
     f32x16 acc0[2], acc1[2];
@@ -334,11 +355,17 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
       kstage_mma<D, 0>(acc1, kres + (c1 * FHN) * kStageBlockBytes, qop);
       if constexpr (FHN == 2) kstage_mma<D, 1>(acc1, kres + (c1 * FHN + 1) * kStageBlockBytes, qop);
     }
-    // queries of the next item (this item's are no longer needed)
+    // fetch item j + 1's queries and item j + 2's first new K block (dummy
+    // but valid addresses when an item does not exist)
     {
+      const int un = more ? u1 : u, rn = more ? r1 : r;
+      const int sn = un % n_seqs, hn = un / n_seqs;
+      const int32_t nqn = seq_len_q(a.vl, sn);
       const int in = 64 * rn + 32 * qt + (lane & 31);
-      load_query_clamped<D>(qop, a.q + ((int64_t)hn * a.vl.total_q + a.vl.cu_q[sn] + min(in, nqn - 1)) * D,
-                            more && in < nqn);
+      load_query_rows<D>(qnext, a.q + ((int64_t)hn * a.vl.total_q + cu_q_of(a.vl, sn) + min(in, nqn - 1)) * D);
+      const bool more2 = u2 < n_units;
+      const int uk = more2 ? u2 : u;
+      kblock_load<D>(knext, kseq_of(uk), seq_len_k(a.vl, uk % n_seqs), more2 ? first_new(u1, r1, u2, r2) : 0);
     }
 
     // softmax statistics of the wave's two blocks: one max over both, then the
@@ -371,13 +398,19 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
     }
     // p = 2^(logit - m) * 2^(m - M) / L
     const float fac = m == -INFINITY ? 0.0f : exp2f_fast(m - M) * __builtin_amdgcn_rcpf(L);
-    // every wave is past its reads of the resident K: the next item's blocks go in
-    if (hi_n >= lo_n) {
-      kblock_store<D>(kres, lo_n, kx);
-      for (int c = lo_n + 1; c <= hi_n; ++c) {  // a unit whose first block-row sees several blocks
-        u32x4 x[FHN];
-        kblock_load<D>(x, kseq_n, nkn, c);
-        kblock_store<D>(kres, c, x);
+    // every wave is past its reads of the resident K: item j + 1's blocks go in
+    if (more) {
+      const int sn = u1 % n_seqs;
+      const int lo = u1 == u ? cmax + 1 : 0, hi = cmax_of(r1, seq_len_q(a.vl, sn), seq_len_k(a.vl, sn));
+      if (hi >= lo) {
+        kblock_store<D>(kres, lo, kcur);
+        const uint16_t* kseq_n = kseq_of(u1);
+        const int32_t nkn = seq_len_k(a.vl, sn);
+        for (int c = lo + 1; c <= hi; ++c) {  // a unit whose first block-row sees several blocks
+          u32x4 x[FHN];
+          kblock_load<D>(x, kseq_n, nkn, c);
+          kblock_store<D>(kres, c, x);
+        }
       }
     }
     barrier_lds();
@@ -387,13 +420,16 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = kp + 4 * j;
-      if (c > cend) continue;
+      const bool live = c <= cend;  // the block exists in the row layout
       f32x16* acc = j ? acc1 : acc0;
-      const float f = c <= cmax_t ? fac : 0.0f;
+      if (!OUT_BF16 && !live) continue;
+      if (live) {
+        const float f = c <= cmax_t ? fac : 0.0f;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[kt][v] *= f;
+          for (int v = 0; v < 16; ++v) acc[kt][v] *= f;
+      }
       if constexpr (OUT_BF16) {
         // Through the wave's LDS tile, 16 query rows at a time: lane (query q,
         // half) puts its 4-key groups at tile row q % 16; then each of 2 passes
@@ -404,7 +440,10 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
         // shift; the leading entry of an odd-phase row and the partial end of a
         // row go out in 2-, 4- and 8-byte pieces. The stores use a descriptor over
         // this (head, sequence) map; lanes with nothing to write use an offset
-        // past it.
+        // past it. A block past the row layout issues the same stores, all with
+        // that offset: every path then has the same count of vector memory
+        // operations, so the compiler's wait for the next item's queries does not
+        // also wait for this item's stores.
         uint16_t* region = reinterpret_cast<uint16_t*>(a.maps) + base0;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             region, (short)0, (int)(2 * map_elems(nq, nk, PACKED)), kBufferFlags);
@@ -414,7 +453,7 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
           wave_lds_fence();  // the previous half's reads of the tile come first
-          if (((lane & 31) >> 4) == qh) {
+          if (live && ((lane & 31) >> 4) == qh) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -430,7 +469,7 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
             const int qq = 8 * p + rr;  // tile row
             const int iq = 64 * r + 32 * qt + 16 * qh + qq;
             const int e = (int)map_row_off(iq, nq, nk, PACKED) + 64 * c;  // segment start (element)
-            const int len = iq < nq ? min(64, (PACKED ? nk - nq + iq + 1 : nk) - 64 * c) : 0;
+            const int len = live && iq < nq ? min(64, (PACKED ? nk - nq + iq + 1 : nk) - 64 * c) : 0;
             const int sh = (pbase + e) & 1, j0 = sh + 8 * k8;
             const uint32_t* trow = tw + qq * kTileRow + 4 * k8;
             const u32x4 w4 = *reinterpret_cast<const u32x4*>(trow);
@@ -469,9 +508,14 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
         }
       }
     }
-    if (!more) break;
-    u = un;
-    r = rn;
+    u0 = u1;
+    r0 = r1;
+    u1 = u2;
+    r1 = r2;
+    if (u2 < n_units) advance(u2, r2);
+    return more;
+  };
+  while (item(qa, qb, ka, kb) && item(qb, qa, kb, ka)) {
   }
 }
 
@@ -496,10 +540,10 @@ __global__ __launch_bounds__(kRowsThreads) void k_attn_rows(AttnMapsArgs a) {
   if (!seq_ok(a.vl, s, nq, nk) || nq != 1 || nk > a.rows_cap) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l = tid % LPK, g = tid / LPK;
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s]) * D;
-  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
-  const float scale_l2 = a.scale[h] * kLog2e;
-  const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s)) * D;
+  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
+  const float scale_l2 = ld_const(a.scale + h) * kLog2e;
+  const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
   float qv[8];
   {
     const u32x4 w = ldg16(qrow + 8 * l);
@@ -571,9 +615,9 @@ __global__ __launch_bounds__(256) void k_attn_maps_f32(AttnMapsArgs a, int d) {
   const int h = blockIdx.z, s = blockIdx.y, i = blockIdx.x;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
-  const float* qrow = a.qf + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * d;
-  const float* kseq = a.kf + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * d;
-  const float scale = a.scale[h], bias = a.bias ? a.bias[h] : 0.0f;
+  const float* qrow = a.qf + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + i) * d;
+  const float* kseq = a.kf + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * d;
+  const float scale = ld_const(a.scale + h), bias = a.bias ? ld_const(a.bias + h) : 0.0f;
   const int last = nk - nq + i;
   __shared__ float red[256];
   auto logit = [&](int j) {

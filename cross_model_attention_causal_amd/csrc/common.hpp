@@ -122,11 +122,22 @@ struct Varlen {
   int64_t total_k;
 };
 
+// Read-only kernel input (sequence bounds, head scales): loaded through the
+// constant address space, so a wave-uniform address becomes a scalar load. Such
+// loads are counted apart from the vector memory queue, so waiting for them does
+// not also wait for a kernel's prefetches and stores in flight.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+__device__ __forceinline__ int32_t cu_q_of(const Varlen& v, int s) { return ld_const(v.cu_q + s); }
+__device__ __forceinline__ int32_t cu_k_of(const Varlen& v, int s) { return ld_const(v.cu_k + s); }
 __device__ __forceinline__ int32_t seq_len_q(const Varlen& v, int s) {
-  return v.used_q ? v.used_q[s] : v.cu_q[s + 1] - v.cu_q[s];
+  return v.used_q ? ld_const(v.used_q + s) : cu_q_of(v, s + 1) - cu_q_of(v, s);
 }
 __device__ __forceinline__ int32_t seq_len_k(const Varlen& v, int s) {
-  return v.used_k ? v.used_k[s] : v.cu_k[s + 1] - v.cu_k[s];
+  return v.used_k ? ld_const(v.used_k + s) : cu_k_of(v, s + 1) - cu_k_of(v, s);
 }
 
 // Elements of one (head, sequence) map in the given layout.
@@ -161,7 +172,7 @@ __device__ __forceinline__ void block_offsets(const Varlen& v, int s, int32_t& r
 // lengths within the reserved rows); these checks keep every access inside the
 // tensors even when they are not.
 __device__ __forceinline__ bool seq_ok(const Varlen& v, int s, int32_t nq, int32_t nk) {
-  int64_t q0 = v.cu_q[s], k0 = v.cu_k[s];
+  int64_t q0 = cu_q_of(v, s), k0 = cu_k_of(v, s);
   return nq >= 0 && nk >= 0 && nq <= nk && q0 >= 0 && k0 >= 0 && q0 + nq <= v.total_q &&
          k0 + nk <= v.total_k;
 }

@@ -99,10 +99,10 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   const int qloc = 64 * (qt / 2) + 32 * (qt & 1) + (lane & 31);  // query within the group
   const int i = 64 * r0 + qloc;
   const bool valid = i < n;
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, n - 1)) * D;
-  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
-  const float scale_l2 = a.scale[h] * kLog2e;
-  const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + min(i, n - 1)) * D;
+  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
+  const float scale_l2 = ld_const(a.scale + h) * kLog2e;
+  const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
 
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     lse_s[q] = lse;
     const int iq = 64 * r0 + q;
     if (iq < n) {
-      const int64_t tok = (int64_t)h * a.vl.total_q + a.vl.cu_q[s] + iq;
+      const int64_t tok = (int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + iq;
       a.lse2[tok] = lse;
       if (a.row_stats) {
         a.row_stats[2 * tok] = M * kLn2;
@@ -399,11 +399,11 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   const int i = 64 * rq + iloc;
   const bool valid = tile_ok && i < n;
   const int half = lane >> 5;
-  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + min(i, n - 1)) * D;
-  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + a.vl.cu_k[s]) * D;
-  const float scale_l2 = a.scale[h] * kLog2e;
-  const float bias_l2 = a.bias ? a.bias[h] * kLog2e : 0.0f;
-  const float lse = valid ? a.lse2[(int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i] : 0.0f;
+  const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + min(i, n - 1)) * D;
+  const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
+  const float scale_l2 = ld_const(a.scale + h) * kLog2e;
+  const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
+  const float lse = valid ? a.lse2[(int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + i] : 0.0f;
   const int64_t base = tile_ok ? a.row_ptr[g0 + gr] : 0;
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, 
   int32_t roff;
   int64_t tri;
   block_offsets(vl, s, roff, tri);
-  const int64_t k0 = vl.cu_k[s] + 64 * c;
+  const int64_t k0 = cu_k_of(vl, s) + 64 * c;
   const int valid = min(64, n - 64 * c);
   if (KEY_MAJOR) {
     // rows of 64 keys per feature: 8 lanes x 16 B per feature row
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       for (int v = 0; v < 16; ++v) {
         const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
         if (row >= n) continue;
-        const int64_t o = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + row) * D + 32 * dt + n32;
+        const int64_t o = ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + row) * D + 32 * dt + n32;
         if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[k][v]);
         else reinterpret_cast<float*>(a.out)[o] = acc[k][v];
       }
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
   __syncthreads();
   const int last = nk - nq + i;
   const int64_t row_off = map_seq_off(a.vl, s, a.packed) + map_row_off(i, nq, nk, a.packed);
-  const int64_t k0 = a.vl.cu_k[s];
+  const int64_t k0 = cu_k_of(a.vl, s);
   constexpr int kChunks = D / 8;          // 8-feature chunks per key (token-major)
   constexpr int kSlots = NT / kChunks;    // keys per pass (token-major)
   float accv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
     } else {
       for (int u = 0; u < kSlots; ++u) o += red[u][tid];
     }
-    const int64_t oi = ((int64_t)h * a.vl.total_q + a.vl.cu_q[s] + i) * D + tid;
+    const int64_t oi = ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + i) * D + tid;
     if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f2bf(o);
     else reinterpret_cast<float*>(a.out)[oi] = o;
   }

@@ -46,6 +46,17 @@ __device__ __forceinline__ void load_query_clamped(QOperand<D>& op, const uint16
   }
 }
 
+// As load_query_clamped without the zeroing: every lane takes the row it points
+// at (a row past the sequence end points at an existing row), for callers that
+// never use the results of such rows. Nothing consumes the loaded registers
+// here, so the loads stay in flight until the operand's first use.
+template <int D>
+__device__ __forceinline__ void load_query_rows(QOperand<D>& op, const uint16_t* qrow_safe) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) op.v[ks] = as_bf16x8(ldg16(qrow_safe + 16 * ks + 8 * half));
+}
+
 // One 64-key block of K as the A operand of 32x32x16 (lane holds key
 // key0 + 32kt + lane % 32, features 16ks + 8(lane/32) + e). Held in registers so
 // that the next block can be fetched while the current one is multiplied.
