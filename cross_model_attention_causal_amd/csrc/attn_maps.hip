@@ -249,7 +249,9 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
   constexpr int FHN = D / 64;
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   uint8_t* kres = reinterpret_cast<uint8_t*>(dyn);
-  __shared__ __attribute__((aligned(16))) uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? kShortTileRows * kTileRow : 1];
+  // 16 rows of a wave's output tile and a spare row that the lanes of the other
+  // half write to (their values are not read), so that the tile write needs no branch
+  __shared__ __attribute__((aligned(16))) uint32_t wtile[OUT_BF16 ? 8 : 1][OUT_BF16 ? (kShortTileRows + 1) * kTileRow : 1];
   __shared__ float sm[4][64], sl[4][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int qt = wave & 1, kp = wave >> 1, half = lane >> 5;
@@ -417,6 +419,10 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
 
     // normalise and write blocks kp and kp + 4 (zeros past the diagonal of a dense row)
     const int64_t base0 = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED);
+    uint16_t* region = reinterpret_cast<uint16_t*>(a.maps) + base0;  // this (head, sequence) map
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(region, (short)0, (int)(2 * map_elems(nq, nk, PACKED)), kBufferFlags);
+    const int pbase = (int)((reinterpret_cast<uintptr_t>(region) >> 1) & 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = kp + 4 * j;
@@ -444,23 +450,20 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
         // that offset: every path then has the same count of vector memory
         // operations, so the compiler's wait for the next item's queries does not
         // also wait for this item's stores.
-        uint16_t* region = reinterpret_cast<uint16_t*>(a.maps) + base0;
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            region, (short)0, (int)(2 * map_elems(nq, nk, PACKED)), kBufferFlags);
-        const int pbase = (int)((reinterpret_cast<uintptr_t>(region) >> 1) & 1);
         uint32_t* tw = wtile[wave];
         const int k8 = lane & 7, rr = lane >> 3;
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
           wave_lds_fence();  // the previous half's reads of the tile come first
-          if (live && ((lane & 31) >> 4) == qh) {
+          {
+            const int trw = ((lane & 31) >> 4) == qh ? (lane & 15) : kShortTileRows;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
                 const u32x2 w = {pack2bf(acc[kt][4 * g], acc[kt][4 * g + 1]),
                                  pack2bf(acc[kt][4 * g + 2], acc[kt][4 * g + 3])};
-                *reinterpret_cast<u32x2*>(&tw[(lane & 15) * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
+                *reinterpret_cast<u32x2*>(&tw[trw * kTileRow + 16 * kt + 4 * g + 2 * half]) = w;
               }
           }
           wave_lds_fence();  // rows are read by other lanes
