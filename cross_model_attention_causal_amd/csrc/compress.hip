@@ -362,7 +362,7 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   int64_t tri_off;
   block_offsets(a.vl, s, roff, tri_off);
   const int64_t g0 = (int64_t)h * a.n_block_rows + roff + r0;  // row r0; row r0 + 1 is g0 + 1
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if (wave == 0) {
     // union of the kept masks in ascending column order, each row's rank of a
     // column among its own kept columns, and the rows' column indices
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   const float scale_l2 = ld_const(a.scale + h) * kLog2e;
   const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
   const float lse = valid ? a.lse2[(int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + i] : 0.0f;
-  const int64_t base = tile_ok ? a.row_ptr[g0 + gr] : 0;
+  const int64_t base = tile_ok ? ld_const(a.row_ptr + g0 + gr) : 0;  // written by the scan before this kernel
   QOperand<D> qop;
   load_query_clamped<D>(qop, qrow, valid);
   f32x16 acc[2][2];
@@ -413,9 +413,8 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   auto blk_of = [&](int x) __attribute__((always_inline)) {
     return (tile_ok && x < nu) ? __builtin_amdgcn_readfirstlane(bidx[gr][x]) : -1;
   };
-  // p = 2^(logit - lse) in the accumulators (0 for rows past the end), stored as
-  // bf16 into block b of the row
-  auto finish = [&](f32x16 (&x)[2], int c, int b) __attribute__((always_inline)) {
+  // p = 2^(logit - lse) in the accumulators (0 for rows past the end)
+  auto finish = [&](f32x16 (&x)[2], int c) __attribute__((always_inline)) {
     if (raw_ok && c != 0 && c != rq) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -432,12 +431,20 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) x[kt] = f32x16{};
     }
+  };
+  // x as bf16 into block b of the row; b < 0: the same stores through a
+  // descriptor of zero bytes, which write nothing. Every sub-step thus issues the
+  // same stores, so the compiler's wait for the next stage's K (loaded before
+  // them) does not also wait for them.
+  auto store_block = [&](const f32x16 (&x)[2], int b) __attribute__((always_inline)) {
     // Lane (query, half) holds keys 32kt + 8g + 4half + 0..3 for g = 0..3. One
     // exchange with the partner lane (lane ^ 32) per pair of groups leaves lane
     // half h with the 8 consecutive keys 32kt + 16g2 + 8h .. +7, so that each
     // store writes 16 bytes and one instruction fills a whole 1 KB run of a
     // panel (32 rows x 16 keys).
-    uint16_t* blk = a.vals + (base + b) * (int64_t)(kBlock * kBlock);
+    uint16_t* blk = b >= 0 ? a.vals + (base + b) * (int64_t)(kBlock * kBlock) : a.vals;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(blk, (short)0, b >= 0 ? 2 * kBlock * kBlock : 0, kBufferFlags);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -453,9 +460,10 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
         const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
         const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
         const int panel = 2 * kt + g2;
-        // non-temporal: the blocks are not read again here, and 7.8 GB of them
-        // streaming through L2 would otherwise evict the K that is re-read
-        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(blk + panel * (kBlock * kPanel) + iloc * kPanel + 8 * half));
+        // non-temporal (cache policy nt): the blocks are not read again here, and
+        // 7.8 GB of them streaming through L2 would otherwise evict the K that is re-read
+        __builtin_amdgcn_raw_buffer_store_b128(w, rs, 2u * (uint32_t)(panel * (kBlock * kPanel) + iloc * kPanel + 8 * half), 0,
+                                               kCacheNT);
       }
   };
   // Whole-block sub-steps (kstage2_pipeline): the wave computes union entry
@@ -472,19 +480,27 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
       kstage_mma<D, 0>(acc[P], buf + kp * FHN * kStageBlockBytes, qop);
       if constexpr (FHN == 2) kstage_mma<D, 1>(acc[P], buf + (2 * kp + 1) * kStageBlockBytes, qop);
     }
-    if (b_def >= 0) finish(acc[1 - P], ucols[x_def], b_def);
+    if (b_def >= 0) finish(acc[1 - P], ucols[x_def]);
+    store_block(acc[1 - P], b_def);
     x_def = x;
     b_def = b;
   };
   const int nsub = (nu + 1) / 2;
-  kstage2_pipeline<D>(stage, kseq, n, nsub, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
-                      [&](int u, const uint8_t* buf) {
-                        if (u & 1) sub(u, buf, std::integral_constant<int, 1>{});
-                        else sub(u, buf, std::integral_constant<int, 0>{});
-                      });
+  kstage2_pipeline<D>(
+      stage, kseq, n, nsub, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
+      [&](int u, const uint8_t* buf) {
+        if (u & 1) sub(u, buf, std::integral_constant<int, 1>{});
+        else sub(u, buf, std::integral_constant<int, 0>{});
+      },
+      [&] { store_block(acc[0], -1); });
   if (b_def >= 0) {
-    if ((nsub - 1) & 1) finish(acc[1], ucols[x_def], b_def);
-    else finish(acc[0], ucols[x_def], b_def);
+    if ((nsub - 1) & 1) {
+      finish(acc[1], ucols[x_def]);
+      store_block(acc[1], b_def);
+    } else {
+      finish(acc[0], ucols[x_def]);
+      store_block(acc[0], b_def);
+    }
   }
 }
 

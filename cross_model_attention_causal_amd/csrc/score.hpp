@@ -232,9 +232,16 @@ __device__ __forceinline__ void kstage_load2(KStageRegs& rg, const uint16_t* __r
   }
 }
 
-template <int D, typename Key0, typename Body>
+struct NoPrologue {
+  __device__ void operator()() const {}
+};
+
+// `pro` runs once after the first loads are issued, before the loop (a body that
+// stores uses it to issue as many non-writing stores as one sub-step, so that the
+// compiler's waits at the loop head count an iteration's stores on every path).
+template <int D, typename Key0, typename Body, typename Pro = NoPrologue>
 __device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk, int nsub,
-                                                 Key0 key0_of, Body body) {
+                                                 Key0 key0_of, Body body, Pro pro = Pro{}) {
   auto load = [&](KStageRegs& rg, int u) { kstage_load2<D>(rg, kseq, nk, key0_of(2 * u), key0_of(2 * u + 1)); };
   auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
     load(mine, min(u + 2, nsub - 1));  // clamped past the end: harmless, keeps the control flow straight
@@ -246,6 +253,7 @@ __device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t*
   KStageRegs r0, r1;
   load(r0, 0);
   load(r1, min(1, nsub - 1));
+  pro();
   kstage_store(stage, r0);
   barrier_lds();
   for (int u = 0; u < nsub; u += 2) {
