@@ -170,12 +170,15 @@ __device__ __forceinline__ void kstage_mma(f32x16 acc[2], const uint8_t* blk, co
 // of a round of 4 key blocks. Two LDS stages alternate; the global loads of
 // sub-step u + 2 are in flight (in registers) while sub-step u is computed, and
 // sub-step u + 1 (loaded one iteration earlier) is written to the other stage at
-// the end of the iteration, before the barrier that publishes it.
+// the end of the iteration, before the barrier that publishes it. The count of
+// sub-steps run is rounded up to even, so a body can be called once for the round
+// just past the end: it must do nothing there (key0_of clamps its key blocks).
 template <int D, typename Key0, typename Body>
 __device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk,
                                                 int rounds, Key0 key0_of, Body body) {
   constexpr int FH = D / 64;
   const int nsub = rounds * FH;
+  const int ne = (nsub + 1) & ~1;  // sub-steps run (see below)
   auto load = [&](KStageRegs& rg, int u) {
     int key0[4];
     const int k = u / FH;
@@ -194,20 +197,23 @@ __device__ __forceinline__ void kstage_pipeline(uint8_t* stage, const uint16_t* 
   // extra loads are harmless and keep the control flow (and so the compiler's
   // wait counting) straight.
   auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
-    load(mine, min(u + 2, nsub - 1));
+    load(mine, min(u + 2, ne - 1));
     run(u);
     kstage_store(stage + ((u + 1) & 1) * kStageBytes, next);
     barrier_lds();
   };
   if (nsub == 0) return;
+  // An even count of sub-steps (the body takes one past the end as empty), so
+  // that the loop has a single exit: with an exit between the two copies of the
+  // step, the compiler's waits at the loop head assume the first copy's loads may
+  // still be in flight there and drain them.
   KStageRegs r0, r1;
   load(r0, 0);
-  load(r1, min(1, nsub - 1));
+  load(r1, 1);
   kstage_store(stage, r0);
   barrier_lds();
-  for (int u = 0; u < nsub; u += 2) {
+  for (int u = 0; u < ne; u += 2) {
     iter(r0, r1, u);
-    if (u + 1 >= nsub) break;
     iter(r1, r0, u + 1);
   }
 }
@@ -242,9 +248,10 @@ struct NoPrologue {
 template <int D, typename Key0, typename Body, typename Pro = NoPrologue>
 __device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t* __restrict__ kseq, int nk, int nsub,
                                                  Key0 key0_of, Body body, Pro pro = Pro{}) {
+  const int ne = (nsub + 1) & ~1;  // an even count, as in kstage_pipeline
   auto load = [&](KStageRegs& rg, int u) { kstage_load2<D>(rg, kseq, nk, key0_of(2 * u), key0_of(2 * u + 1)); };
   auto iter = [&](KStageRegs& mine, KStageRegs& next, int u) {
-    load(mine, min(u + 2, nsub - 1));  // clamped past the end: harmless, keeps the control flow straight
+    load(mine, min(u + 2, ne - 1));  // clamped past the end: harmless, keeps the control flow straight
     body(u, stage + (u & 1) * kStageBytes);
     kstage_store(stage + ((u + 1) & 1) * kStageBytes, next);
     barrier_lds();
@@ -252,13 +259,12 @@ __device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t*
   if (nsub == 0) return;
   KStageRegs r0, r1;
   load(r0, 0);
-  load(r1, min(1, nsub - 1));
+  load(r1, 1);
   pro();
   kstage_store(stage, r0);
   barrier_lds();
-  for (int u = 0; u < nsub; u += 2) {
+  for (int u = 0; u < ne; u += 2) {
     iter(r0, r1, u);
-    if (u + 1 >= nsub) break;
     iter(r1, r0, u + 1);
   }
 }
