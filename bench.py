@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--stage-figures", action="store_true",
+                    help="instead of the step: time each stage at its own workload (512-token head "
+                         "mapping; 32-head x 8192-token compression; the fused pass over it) and print "
+                         "one JSON line per workload with every kernel's roofline fraction")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (for scaling hardware byte counters)")
     return ap.parse_args()
@@ -72,10 +76,110 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def stage_figures(reps=5):
+    """Each stage at its own workload: the 512-token head mapping (maps of 336 small-
+    and 2560 large-model heads, the 2560 x 336 cosine), the 32-head x 8192-token
+    compression at tau 0.95, and the fused pass of 24 receiver heads over it.
+    Per kernel: average launch time from HIP events on the launch stream, the
+    algorithmic work per launch, and the fraction of the roofline that binds it."""
+    import torch
+    import cross_model_attention_causal_amd as cma
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cma.load_library()
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+
+    def timed(fn, work):
+        fn()
+        torch.cuda.synchronize()
+        cma.timing_reset()
+        cma.timing_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        cma.timing_enable(False)
+        kt = cma.timing_collect()
+        out = {}
+        for name, (ms, cnt) in kt.items():
+            e = dict(ms=round(ms / cnt, 4), launches_per_call=cnt // reps)
+            if name in work:
+                bound, amount = work[name]
+                sec = ms / cnt * 1e-3
+                if bound == "hbm":
+                    ach, peak, unit = amount / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+                else:
+                    ach, peak, unit = amount / sec / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+                e.update(bound=bound, work_per_launch=amount, achieved=round(ach, 1), peak=peak, unit=unit,
+                         frac=round(ach / peak, 4))
+            out[name] = e
+        return out
+
+    # 512-token head mapping
+    t0 = time.time()
+    x = synth.cfg2()
+    log(f"head-mapping inputs in {time.time() - t0:.1f}s")
+    Hs, Hr, n = x["n_send"], x["n_recv"], x["n"]
+    L = n * (n + 1) // 2
+    vl = cma.Varlen(x["cu"])
+    sq, sk, rq, rk = bf(x["send_q"]), bf(x["send_k"]), bf(x["recv_q"]), bf(x["recv_k"])
+    ss, sb, rs, rb = f32(x["send_scale"]), f32(x["send_bias"]), f32(x["recv_scale"]), f32(x["recv_bias"])
+    st = {}
+
+    def maps():
+        st["s"] = cma.attn_maps(sq, sk, ss, sb, vl)
+        st["r"] = cma.attn_maps(rq, rk, rs, rb, vl)
+    maps_bytes = (Hs + Hr) * (2 * n * 128 * 2 + L * 2) / 2  # per launch, average of the two
+    k_maps = timed(maps, {"k_attn_maps_short": ("hbm", maps_bytes), "k_attn_maps": ("hbm", maps_bytes)})
+    k_cos = timed(lambda: cma.head_map_cosine(st["r"], st["s"], 1, Hr, Hs, L, L, 0, L, 0),
+                  {"k_gram_bf16": ("mfma", 2 * Hr * Hs * L)})
+    print(json.dumps({"workload": f"head mapping: one {n}-token prompt, {Hs} small-model and {Hr} large-model "
+                                  "maps (d=128, bf16), packed causal, and the Hr x Hs cosine with argmax",
+                      "kernels": {**k_maps, **k_cos}}), flush=True)
+    del st, sq, sk, rq, rk
+
+    # 32-head x 8192-token compression, then the fused pass over it
+    t0 = time.time()
+    x = synth.cfg3()
+    y = synth.cfg4()
+    log(f"compression inputs in {time.time() - t0:.1f}s")
+    H, n, tau = x["n_heads"], x["n"], x["tau"]
+    vl = cma.Varlen(x["cu"])
+    q, k = bf(x["q"]), bf(x["k"])
+    sc, bi = f32(x["scale"]), f32(x["bias"])
+    ws = cma.Workspace()
+    res = {}
+
+    def comp():
+        res["bsr"] = cma.block_compress(q, k, sc, bi, vl, tau, workspace=ws)
+    comp()
+    torch.cuda.synchronize()
+    nnz = int(res["bsr"]["nnz"].item())
+    qk = 2 * H * n * 128 * 2
+    k_comp = timed(comp, {"k_block_stats": ("mfma", H * (n * (n + 1) // 2) * 128 * 2),
+                          "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + qk)})
+    causal = (n // 64) * (n // 64 + 1) // 2
+    print(json.dumps({"workload": f"block compression: {H} heads x {n} tokens (d=128, bf16), 64x64 blocks, "
+                                  f"tau={tau}", "kept_block_fraction": round(nnz / (H * causal), 4),
+                      "kernels": k_comp}), flush=True)
+    Hs, Hr = y["n_send"], y["n_recv"]
+    M, V = f32(y["M"]), bf(y["v"])
+    wsv = cma.Workspace()
+    r_tot = n // 64
+    k_mav = timed(lambda: cma.mapped_av(res["bsr"], Hs, M, Hr, V, vl, workspace=wsv),
+                  {"k_mapped_av_bsr": ("hbm", nnz * 8192 + 2 * Hr * n * 128 * 2 + (Hs * r_tot + 1 + nnz) * 4),
+                   "k_tile_v": ("hbm", 2 * Hr * n * 128 * 2)})
+    print(json.dumps({"workload": f"fused mapped x V: {Hr} receiver heads over the {Hs}-head compressed maps "
+                                  f"above, learned M, token-major bf16 V (d=128)", "kernels": k_mav}), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.stage_figures:
+        return stage_figures()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
@@ -184,17 +288,19 @@ def main():
     f_stats = Hs * P * (n * (n + 1) // 2) * 128 * 2
     # extraction: kept blocks written + Q and K read
     b_ext = nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2
-    # maps: sender and receiver prefix maps (Q, K read + packed bf16 written) and the
-    # decode rows (q row + 8193 keys read, fp32 row written); three launches per step
-    b_maps = ((Hs + Hr) * P * (2 * tau_t * 128 * 2 + L * 2)
-              + Hs * P * (128 * 2 + (n + 1) * (128 * 2 + 4)))
+    # maps: sender and receiver prefix maps, one launch each (Q, K read + packed bf16
+    # written; per launch the average of the two); the decode row (q row + 8193 keys
+    # read, fp32 row written), one launch
+    b_maps = (Hs + Hr) * P * (2 * tau_t * 128 * 2 + L * 2) / 2
+    b_rows = Hs * P * (128 * 2 + (n + 1) * (128 * 2 + 4))
     # cosine Gram: MFMA flops over all receiver x sender pairs
     f_gram = 2 * P * Hr * Hs * L
     specs = {
         "k_mapped_av_bsr": ("hbm", b_mav),
         "k_block_stats": ("mfma", f_stats),
         "k_block_extract": ("hbm", b_ext),
-        "k_attn_maps": ("hbm", b_maps / 3),
+        "k_attn_maps_short": ("hbm", b_maps),
+        "k_attn_rows": ("hbm", b_rows),
         "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2),
         "k_gram_bf16": ("mfma", f_gram),
     }
