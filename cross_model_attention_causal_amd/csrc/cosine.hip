@@ -269,31 +269,62 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// one wave per (receiver map, problem)
-__global__ __launch_bounds__(64) void k_cos_finalize(CosineArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+// Top-2 of (value, index) pairs under `better`, a strict total order (ties to
+// the lower index): merging partial lists in any order gives the same result.
+__device__ __forceinline__ void top2_merge(float& v1, int& i1, float& v2, int& i2, float ov1, int oi1, float ov2,
+                                           int oi2) {
+  float n1, n2;
+  int j1, j2;
+  if (better(v1, i1, ov1, oi1)) {
+    n1 = v1; j1 = i1;
+    if (better(v2, i2, ov1, oi1)) { n2 = v2; j2 = i2; } else { n2 = ov1; j2 = oi1; }
+  } else {
+    n1 = ov1; j1 = oi1;
+    if (better(v1, i1, ov2, oi2)) { n2 = v1; j2 = i1; } else { n2 = ov2; j2 = oi2; }
+  }
+  v1 = n1; i1 = j1; v2 = n2; i2 = j2;
+}
+
+// One workgroup of 256 threads per (receiver map, problem); thread t forms the
+// cosines of senders t, t + 256, ... Each cosine adds its splits' partial dot
+// products and sender norms in four interleaved sums (split sp into sum sp % 4,
+// in increasing sp), eight partials in flight; then the top two cosines per
+// wave, merged through LDS.
+constexpr int kFinThreads = 256;
+__global__ __launch_bounds__(kFinThreads) void k_cos_finalize(CosineArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float sv[2][kFinThreads / 64];
+  __shared__ int si[2][kFinThreads / 64];
+  // the receiver's norm: its splits' partial sums, added in split order (scalar
+  // loads of the Gram's output, issued back to back)
   float rn = 0.f;
-  for (int sp = 0; sp < a.splits; ++sp) rn += a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + h];  // one value per lane group, cheap
+#pragma unroll 8
+  for (int sp = 0; sp < a.splits; ++sp) rn += ld_const(a.rnorm + ((int64_t)sp * a.n_batch + b) * a.n_recv + h);
   const float rs = sqrtf(rn);
   float v1 = -INFINITY, v2 = -INFINITY;
   int i1 = 0x7fffffff, i2 = 0x7fffffff;
-  for (int j = lane; j < a.n_send; j += 64) {
-    // four interleaved partial sums over the splits, added in a fixed order
+  const int64_t pstride = (int64_t)a.n_batch * a.n_recv * a.n_send, sstride = (int64_t)a.n_batch * a.n_send;
+  for (int j = tid; j < a.n_send; j += kFinThreads) {
     float d4[4] = {0.f, 0.f, 0.f, 0.f}, s4[4] = {0.f, 0.f, 0.f, 0.f};
-    const int64_t pstride = (int64_t)a.n_batch * a.n_recv * a.n_send, sstride = (int64_t)a.n_batch * a.n_send;
     const float* pp = a.part + ((int64_t)b * a.n_recv + h) * a.n_send + j;
     const float* ps = a.snorm + (int64_t)b * a.n_send + j;
     int sp = 0;
-    for (; sp + 3 < a.splits; sp += 4) {
+    for (; sp + 7 < a.splits; sp += 8) {
+      float pd[8], pn[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        d4[u] += pp[(sp + u) * pstride];
-        s4[u] += ps[(sp + u) * sstride];
+      for (int u = 0; u < 8; ++u) {
+        pd[u] = pp[(sp + u) * pstride];
+        pn[u] = ps[(sp + u) * sstride];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        d4[u & 3] += pd[u];
+        s4[u & 3] += pn[u];
       }
     }
     for (int u = 0; sp < a.splits; ++sp, ++u) {
-      d4[u] += pp[sp * pstride];
-      s4[u] += ps[sp * sstride];
+      d4[u & 3] += pp[sp * pstride];
+      s4[u & 3] += ps[sp * sstride];
     }
     const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]), sn = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     const float den = rs * sqrtf(sn);
@@ -305,22 +336,16 @@ __global__ __launch_bounds__(64) void k_cos_finalize(CosineArgs a) {
       v2 = c; i2 = j;
     }
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov1 = __shfl_xor(v1, off, 64), ov2 = __shfl_xor(v2, off, 64);
-    const int oi1 = __shfl_xor(i1, off, 64), oi2 = __shfl_xor(i2, off, 64);
-    // merge the two top-2 lists
-    float n1, n2;
-    int j1, j2;
-    if (better(v1, i1, ov1, oi1)) {
-      n1 = v1; j1 = i1;
-      if (better(v2, i2, ov1, oi1)) { n2 = v2; j2 = i2; } else { n2 = ov1; j2 = oi1; }
-    } else {
-      n1 = ov1; j1 = oi1;
-      if (better(v1, i1, ov2, oi2)) { n2 = v1; j2 = i1; } else { n2 = ov2; j2 = oi2; }
-    }
-    v1 = n1; i1 = j1; v2 = n2; i2 = j2;
-  }
+  for (int off = 32; off > 0; off >>= 1)
+    top2_merge(v1, i1, v2, i2, __shfl_xor(v1, off, 64), __shfl_xor(i1, off, 64), __shfl_xor(v2, off, 64),
+               __shfl_xor(i2, off, 64));
   if (lane == 0) {
+    sv[0][wave] = v1; si[0][wave] = i1;
+    sv[1][wave] = v2; si[1][wave] = i2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kFinThreads / 64; ++w) top2_merge(v1, i1, v2, i2, sv[0][w], si[0][w], sv[1][w], si[1][w]);
     a.argmax[(int64_t)b * a.n_recv + h] = i1;
     if (a.margin) a.margin[(int64_t)b * a.n_recv + h] = a.n_send > 1 ? v1 - v2 : INFINITY;
   }
@@ -381,7 +406,7 @@ hipError_t launch_cosine(const CosineArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  { KernelTimer kt_("k_cos_finalize", st); hipLaunchKernelGGL(k_cos_finalize, dim3(a.n_recv, a.n_batch), dim3(64), 0, st, a); }
+  { KernelTimer kt_("k_cos_finalize", st); hipLaunchKernelGGL(k_cos_finalize, dim3(a.n_recv, a.n_batch), dim3(kFinThreads), 0, st, a); }
   return hipGetLastError();
 }
 
