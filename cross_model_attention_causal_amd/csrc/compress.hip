@@ -143,12 +143,18 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     auto sub = [&](int u, const uint8_t* buf, auto par) __attribute__((always_inline)) {
       constexpr int P = decltype(par)::value;
       const int c = 2 * u + kp;
-      if (c <= cmax) {
-        acc[P][0] = acc[P][1] = f32x16{};
-        kstage_mma<D, 0>(acc[P], buf + kp * FHN * kStageBlockBytes, qop);
-        if constexpr (FHN == 2) kstage_mma<D, 1>(acc[P], buf + (2 * kp + 1) * kStageBlockBytes, qop);
+      if (c <= cmax && c_def >= 0 && raw_ok && c_def != 0 && c_def != rq) {
+        // interior: this block's products beside the previous block's lean update
+        const float part = mma_beside_update<D>(acc[P], buf + kp * FHN * kStageBlockBytes, qop, acc[1 - P], scale_l2, m, l);
+        if (lane < 32) LP[qloc * LPS + c_def] = m + log2f_fast(part);
+      } else {
+        if (c <= cmax) {
+          acc[P][0] = acc[P][1] = f32x16{};
+          kstage_mma<D, 0>(acc[P], buf + kp * FHN * kStageBlockBytes, qop);
+          if constexpr (FHN == 2) kstage_mma<D, 1>(acc[P], buf + (2 * kp + 1) * kStageBlockBytes, qop);
+        }
+        if (c_def >= 0) finish(acc[1 - P], c_def);
       }
-      if (c_def >= 0) finish(acc[1 - P], c_def);
       c_def = c <= cmax ? c : -1;
     };
     const int nsub = (r_last + 2) / 2;

@@ -348,6 +348,11 @@ __device__ __forceinline__ float online_update_acc(const f32x16 t[2], float& m, 
   return s;
 }
 
+// Scheduling hints for one wave's instruction stream: `n` instructions of a kind
+// next (kinds as the compiler's scheduler numbers them).
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
+#define CMA_SCHED(kind, n) __builtin_amdgcn_sched_group_barrier((kind), (n), 0)
+
 // Online update for a block that needs no mask and no sink bias (every key is
 // visible to every query of the wave and none is key 0), taking the raw scores.
 // Requires scale_l2 > 0, so that the largest raw score gives the largest logit;
@@ -373,6 +378,29 @@ __device__ __forceinline__ float online_update_raw(const f32x16 acc[2], float sc
   l = l * exp2f_fast(m - mn) + s;
   m = mn;
   return s;
+}
+
+// The products of one block (K staged at blk, both feature halves for D = 128)
+// into acc_new, beside the lean online update of the previous block (acc_old),
+// in one straight stretch of code whose schedule alternates operand reads,
+// products and the update's vector instructions: the matrix core and the vector
+// unit then work at the same time within one wave. Returns the update's
+// partial sum.
+template <int D>
+__device__ __forceinline__ float mma_beside_update(f32x16 acc_new[2], const uint8_t* blk, const QOperand<D>& qop,
+                                                   const f32x16 acc_old[2], float scale_l2, float& m, float& l) {
+  acc_new[0] = acc_new[1] = f32x16{};
+  kstage_mma<D, 0>(acc_new, blk, qop);
+  if constexpr (D == 128) kstage_mma<D, 1>(acc_new, blk + kStageBlockBytes, qop);
+  const float part = online_update_raw(acc_old, scale_l2, m, l);
+  constexpr int NM = D / 8;  // products (32x32x16) per block
+#pragma unroll
+  for (int t = 0; t < NM; ++t) {
+    CMA_SCHED(kSchedDsRead, 1);
+    CMA_SCHED(kSchedMfma, 1);
+    CMA_SCHED(kSchedValu, 6);
+  }
+  return part;
 }
 
 }  // namespace cma
