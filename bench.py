@@ -235,19 +235,29 @@ def main():
     od = torch.empty((Hr, P, 128), dtype=torch.bfloat16, device=dev)
     state = {}
 
+    # The head mapping and the decode row (steps 1-3 and 6) do not depend on the
+    # compression and the fused pass (steps 4-5): they run on a second stream of
+    # the same (default) priority beside them. Each step starts both streams
+    # together and ends when both are done.
+    side = torch.cuda.Stream()
+
     def step():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
         layers = cma.mapped_layers(80, 0.5)                                  # host: layer order
-        cma.attn_maps(send_q, send_k, s_scale, s_bias, vl_map_s, out=sm)     # 1
-        cma.attn_maps(recv_q, recv_k, r_scale, r_bias, vl_map_r, out=rm)
-        cos, arg, mar = cma.head_map_cosine(rm, sm, P, Hr, Hs, L, P * L, L, P * L, L)  # 2
-        Mdec = cma.onehot_mix(arg, Hs)                                       # 3
+        with torch.cuda.stream(side):
+            cma.attn_maps(send_q, send_k, s_scale, s_bias, vl_map_s, out=sm)     # 1
+            cma.attn_maps(recv_q, recv_k, r_scale, r_bias, vl_map_r, out=rm)
+            cos, arg, mar = cma.head_map_cosine(rm, sm, P, Hr, Hs, L, P * L, L, P * L, L)  # 2
+            Mdec = cma.onehot_mix(arg, Hs)                                       # 3
+            cma.attn_maps(dec_q, send_k, s_scale, s_bias, vl_dec, layout=cma.DENSE,
+                          out_dtype=torch.float32, out=rows)                      # 6
+            cma.mapped_av(("dense", rows, cma.DENSE), Hs, Mdec, Hr, v, vl_dec, out=od, q_rows=P)
         bsr = cma.block_compress(send_q, send_k, s_scale, s_bias, vl_pref, args.tau,
                                  workspace=ws_c, bsr=bsr_buf)                 # 4
         cma.mapped_av(bsr, Hs, M, Hr, v, vl_pref, out=O, q_rows=P * n,
                       workspace=ws_v)                                         # 5
-        cma.attn_maps(dec_q, send_k, s_scale, s_bias, vl_dec, layout=cma.DENSE,
-                      out_dtype=torch.float32, out=rows)                      # 6
-        cma.mapped_av(("dense", rows, cma.DENSE), Hs, Mdec, Hr, v, vl_dec, out=od, q_rows=P)
+        main.wait_stream(side)
         state.update(arg=arg, mar=mar, bsr=bsr, layers=layers)
 
     for _ in range(args.warmup):
