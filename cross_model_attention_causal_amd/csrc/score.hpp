@@ -257,9 +257,13 @@ __device__ __forceinline__ void kstage2_pipeline(uint8_t* stage, const uint16_t*
     barrier_lds();
   };
   if (nsub == 0) return;
+  // sub-step 1 is fetched first: on the path into the loop, the operations after
+  // it (sub-step 0's loads, `pro`, the first iteration's own) then number at
+  // least those of an iteration, so the first wait for it leaves earlier stores
+  // in flight
   KStageRegs r0, r1;
-  load(r0, 0);
   load(r1, 1);
+  load(r0, 0);
   pro();
   kstage_store(stage, r0);
   barrier_lds();
