@@ -88,6 +88,7 @@ def load_library(path: str = LIB_PATH):
                                          P, ctypes.c_int, P, SZ, P]),
         "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
+        "cma_mapping_plan": (ctypes.c_int, [I32, P, I32, I32, P, P]),
         "cma_timing_enable": (ctypes.c_int, [ctypes.c_int]),
         "cma_timing_collect": (ctypes.c_int, []),
         "cma_timing_get": (D, [ctypes.c_char_p, ctypes.POINTER(I64)]),
@@ -391,6 +392,17 @@ def mapped_layers(n_layers, ratio):
     if n < 0:
         raise CmaError(n, lib.cma_last_error().decode())
     return [int(buf[i]) for i in range(n)]
+
+
+def mapping_plan(prompt_lens, tau_e, tau_t):
+    """IAM's tau_e / tau_t thresholds per request: (tokens to generate before the
+    head map is built, leading context tokens the similarity uses), as lists."""
+    lib = load_library()
+    p = np.ascontiguousarray(prompt_lens, dtype=np.int32)
+    gen = np.zeros(p.size, dtype=np.int32)
+    sim = np.zeros(p.size, dtype=np.int32)
+    _check(lib.cma_mapping_plan(p.size, p.ctypes.data, int(tau_e), int(tau_t), gen.ctypes.data, sim.ctypes.data))
+    return [int(v) for v in gen], [int(v) for v in sim]
 
 
 def timing_enable(on=True):

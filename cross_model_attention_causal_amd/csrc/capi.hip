@@ -453,4 +453,18 @@ int cma_mapped_layers(int32_t n_layers, double ratio, int32_t* out, int32_t cap)
   return want;
 }
 
+int cma_mapping_plan(int32_t n, const int32_t* prompt_len, int32_t tau_e, int32_t tau_t,
+                     int32_t* gen_before, int32_t* sim_len) {
+  if (n < 0 || (n > 0 && (!prompt_len || !gen_before || !sim_len)) || tau_e < 0 || tau_t < 1)
+    return fail(CMA_EINVAL, "bad arguments");
+  for (int32_t i = 0; i < n; ++i)
+    if (prompt_len[i] < 0) return fail(CMA_EINVAL, "negative prompt length at %d", i);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t gen = std::max(0, tau_e - prompt_len[i]);
+    gen_before[i] = gen;
+    sim_len[i] = std::min(prompt_len[i] + gen, tau_t);
+  }
+  return CMA_OK;
+}
+
 }  // extern "C"

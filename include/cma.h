@@ -247,6 +247,20 @@ int cma_onehot_mix(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32
  */
 int cma_mapped_layers(int32_t n_layers, double ratio, int32_t* out, int32_t cap);
 
+/*
+ * cma_mapping_plan -- the tau_e / tau_t thresholds of [IAM] Method 4 for a batch
+ * of n requests [host]. A prompt shorter than tau_e is first extended by ordinary
+ * generation to tau_e tokens, and only then is the head map built; the
+ * similarity is computed on the first tau_t tokens of a longer context:
+ *   gen_before[i] = max(0, tau_e - prompt_len[i])
+ *   sim_len[i]    = min(prompt_len[i] + gen_before[i], tau_t)
+ * prompt_len, gen_before, sim_len: [n] int32, host memory owned by the caller.
+ * Returns CMA_OK, or CMA_EINVAL (nothing written) for n < 0, a null array with
+ * n > 0, a negative prompt length, tau_e < 0 or tau_t < 1.
+ */
+int cma_mapping_plan(int32_t n, const int32_t* prompt_len, int32_t tau_e, int32_t tau_t,
+                     int32_t* gen_before, int32_t* sim_len);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,7 +12,11 @@ rounded half up); the forward run continues up to 0.8 L - 1 and the first 0.2 L
 layers are never mapped (more layers than that are not available).
 
 IAM Method 4: the head map fixed at prefill is a per-head argmax over sender
-heads; as a mixing matrix it is one-hot.
+heads; as a mixing matrix it is one-hot. Its thresholds: a prompt shorter than
+tau_e is first extended by ordinary generation to tau_e tokens, and only then is
+the mapping built; for a context longer than tau_t the similarity is computed on
+a truncated context. Readings: the generated tokens belong to the context the
+maps are taken over, and truncation keeps the first tau_t tokens.
 """
 import math
 
@@ -37,3 +41,13 @@ def onehot_mix(argmax, n_send):
     M = np.zeros(a.shape + (n_send,), dtype=np.float64)
     np.put_along_axis(M, a[..., None], 1.0, axis=-1)
     return M
+
+
+def mapping_plan(prompt_len, tau_e, tau_t):
+    """IAM Method 4 thresholds for one request: (tokens generated before the head
+    map is built, number of leading context tokens the similarity uses)."""
+    if prompt_len < 0 or tau_e < 0 or tau_t < 1:
+        raise ValueError("bad lengths")
+    gen = tau_e - prompt_len if prompt_len < tau_e else 0
+    context = prompt_len + gen
+    return gen, (context if context <= tau_t else tau_t)

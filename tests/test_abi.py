@@ -65,6 +65,60 @@ def test_mapped_layers_match_oracle(lib, n_layers, ratio):
     assert list(out[:k]) == list(oracle.mapped_layers(n_layers, ratio))
 
 
+# IAM Method 4 thresholds, worked by hand from the rule (extend a short prompt by
+# generation to tau_e, then take the similarity over at most the first tau_t tokens):
+# (prompt length, tau_e, tau_t) -> (tokens generated first, similarity prefix)
+PLAN_CASES = [
+    ((100, 256, 512), (156, 256)),   # short prompt: generate 156, map over 256
+    ((256, 256, 512), (0, 256)),     # exactly tau_e: map at prefill
+    ((300, 256, 512), (0, 300)),     # between the thresholds: the whole prompt
+    ((512, 256, 512), (0, 512)),
+    ((8192, 256, 512), (0, 512)),    # long prompt: truncated to the first 512 tokens
+    ((0, 256, 512), (256, 256)),     # empty prompt
+    ((100, 600, 512), (500, 512)),   # tau_e above tau_t: generate to 600, use 512
+    ((7, 0, 1), (0, 1)),
+]
+
+
+@pytest.mark.parametrize("args,want", PLAN_CASES)
+def test_mapping_plan_oracle_worked_cases(args, want):
+    assert oracle.mapping_plan(*args) == want
+
+
+def test_mapping_plan_matches_oracle(lib):
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    lib.cma_mapping_plan.argtypes = [I32, P, I32, I32, P, P]
+    lib.cma_mapping_plan.restype = ctypes.c_int
+    rng = np.random.default_rng(11)
+    for tau_e, tau_t in [(0, 1), (256, 512), (600, 512), (512, 512), (1, 8192)]:
+        p = np.concatenate([rng.integers(0, 9000, 200), [0, tau_e, tau_t, max(0, tau_e - 1), tau_t + 1]]).astype(np.int32)
+        gen = np.full(p.size, -7, dtype=np.int32)
+        sim = np.full(p.size, -7, dtype=np.int32)
+        assert lib.cma_mapping_plan(p.size, p.ctypes.data, tau_e, tau_t, gen.ctypes.data, sim.ctypes.data) == 0
+        want = [oracle.mapping_plan(int(x), tau_e, tau_t) for x in p]
+        assert list(zip(gen.tolist(), sim.tolist())) == want
+    # invalid arguments: an error and nothing written
+    bad = np.array([5, -1], dtype=np.int32)
+    gen = np.full(2, -7, dtype=np.int32)
+    sim = np.full(2, -7, dtype=np.int32)
+    assert lib.cma_mapping_plan(2, bad.ctypes.data, 10, 20, gen.ctypes.data, sim.ctypes.data) == -1
+    assert gen.tolist() == [-7, -7]
+    ok = np.array([5], dtype=np.int32)
+    assert lib.cma_mapping_plan(1, ok.ctypes.data, 10, 0, gen.ctypes.data, sim.ctypes.data) == -1
+    assert lib.cma_mapping_plan(1, ok.ctypes.data, -1, 20, gen.ctypes.data, sim.ctypes.data) == -1
+    assert lib.cma_mapping_plan(-1, None, 10, 20, None, None) == -1
+    assert lib.cma_mapping_plan(0, None, 10, 20, None, None) == 0
+
+
+def test_mapping_plan_binding():
+    import cross_model_attention_causal_amd as cma
+    lens = [100, 256, 8192, 0]
+    gen, sim = cma.mapping_plan(lens, 256, 512)
+    assert list(zip(gen, sim)) == [oracle.mapping_plan(p, 256, 512) for p in lens]
+    with pytest.raises(cma.CmaError):
+        cma.mapping_plan([-3], 256, 512)
+
+
 def test_validation_errors_without_device(lib):
     """Bad arguments are rejected before any device work, with a message."""
     lib.cma_last_error.restype = ctypes.c_char_p
