@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH):
         "cma_block_compress": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, F, I32, P, P,
                                               P, I64, P, P, P, P, SZ, P]),
         "cma_mapped_av_workspace": (SZ, [P, I32, I32, I64, ctypes.c_int]),
-        "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, P, ctypes.c_int, ctypes.c_int, I32, P,
+        "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, I32, P, ctypes.c_int, ctypes.c_int, I32, P,
                                          P, ctypes.c_int, P, SZ, P]),
         "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
@@ -316,11 +316,12 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
 
 def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_stride=None,
               workspace: Workspace | None = None, out=None, q_rows=None, v_layout=V_TOKEN_MAJOR,
-              k_rows=None):
-    """O_h = (sum_j M[h, j] A_j) V_h. ``src`` is either a block_compress result
+              k_rows=None, v_heads=None):
+    """O_h = (sum_j M[h, j] A_j) V_{h // g}, g = n_recv // v_heads (grouped V;
+    default v_heads = n_recv). ``src`` is either a block_compress result
     (dict with row_ptr/col_idx/vals/n_block_rows) or ``("dense", maps, layout)``.
-    ``v`` is [n_recv, Tk, d] (V_TOKEN_MAJOR), [n_recv, d, Tk] (V_KEY_MAJOR) or
-    [n_recv, n_block_rows, 64 * 128] (V_TILED, block-sparse source only; then
+    ``v`` is [v_heads, Tk, d] (V_TOKEN_MAJOR), [v_heads, d, Tk] (V_KEY_MAJOR) or
+    [v_heads, n_block_rows, 64 * 128] (V_TILED, block-sparse source only; then
     ``k_rows`` gives Tk). ``q_rows`` is the row count of the output tensor
     (default: Tk)."""
     torch = _torch()
@@ -335,8 +336,11 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         Tk = k_rows
     else:
         H, Tk, d = v.shape
-    if H < n_recv:
-        raise ValueError(f"v holds {H} heads, n_recv is {n_recv}")
+    n_v = n_recv if v_heads is None else int(v_heads)
+    if n_v < 1 or n_recv % n_v:
+        raise ValueError(f"v_heads ({n_v}) must be >= 1 and divide n_recv ({n_recv})")
+    if H < n_v:
+        raise ValueError(f"v holds {H} heads, {n_v} are needed")
     out_dtype = out_dtype or v.dtype
     Tq = q_rows if q_rows is not None else Tk
     _check_rows(vl, Tq, Tk)
@@ -346,7 +350,7 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
     s = _CMapsSrc()
     if isinstance(src, dict):
         if v_layout == V_TILED:
-            _need(v, "v", n_recv * src["n_block_rows"] * BLOCK * 128)
+            _need(v, "v", n_v * src["n_block_rows"] * BLOCK * 128)
         _need(src["row_ptr"], "row_ptr", n_send * src["n_block_rows"] + 1)
         s.kind = SRC_BSR
         s.row_ptr = _dev_ptr(src["row_ptr"], "row_ptr")
@@ -365,10 +369,10 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
     if M_seq_stride is None:
         M_seq_stride = 0 if M.shape[0] == 1 else n_recv * n_send
     _need(M, "M", M_seq_stride * max(0, vl.n_seqs - 1) + n_recv * n_send)
-    ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_recv, d, Tk, v_layout)
+    ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_v, d, Tk, v_layout)
     ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
     cvl = vl.c(Tq, Tk)
-    _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv,
+    _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv, n_v,
                              _dev_ptr(v, "v"), _dt(v), v_layout, d, ctypes.byref(cvl),
                              _dev_ptr(out, "out"), _dt(out),
                              ws.data_ptr() if ws is not None else None,

@@ -350,18 +350,18 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
   return hip_status(launch_compress(a, d, st), "block_compress launch");
 }
 
-size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k,
+size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout) {
   (void)total_k;
-  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || n_recv <= 0 || d <= 0 ||
+  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || n_v_heads <= 0 || d <= 0 ||
       src->n_block_rows <= 0)
     return 0;
-  return (size_t)n_recv * src->n_block_rows * kBlock * d * sizeof(uint16_t);
+  return (size_t)n_v_heads * src->n_block_rows * kBlock * d * sizeof(uint16_t);
 }
 
 int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
-                  int32_t n_recv, const void* v, cma_dtype v_dt, cma_v_layout v_layout, int32_t d,
-                  const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
+                  int32_t n_recv, int32_t n_v_heads, const void* v, cma_dtype v_dt, cma_v_layout v_layout,
+                  int32_t d, const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
                   size_t workspace_bytes, void* stream) {
   if (!src) return fail(CMA_EINVAL, "NULL maps source");
   if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR && v_layout != CMA_V_TILED)
@@ -369,6 +369,8 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   if (int e = check_varlen(vl, true)) return e;
   if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
   if (n_send < 0 || n_recv < 0 || M_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
+  if (n_v_heads < 1 || (n_recv > 0 && n_recv % n_v_heads != 0))
+    return fail(CMA_EINVAL, "n_v_heads (%d) must be >= 1 and divide n_recv (%d)", n_v_heads, n_recv);
   if (d != 64 && d != 128) return fail(CMA_EUNSUPPORTED, "mapped_av supports d = 64 or 128 (got %d)", d);
   if (n_recv == 0 || vl->n_seqs == 0) return CMA_OK;
   if (n_send == 0 || n_send > 64) return fail(CMA_EUNSUPPORTED, "mapped_av supports 1 <= n_send <= 64");
@@ -376,6 +378,8 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   MappedAvArgs a{};
   a.n_send = n_send;
   a.n_recv = n_recv;
+  a.n_v = n_v_heads;
+  a.v_group = n_recv / n_v_heads;
   a.d = d;
   a.M = M;
   a.M_stride = M_seq_stride;
@@ -421,7 +425,7 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
     a.vt = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
   } else {
     if (!a.v_key_major && !aligned16(v)) return fail(CMA_EINVAL, "token-major V must be 16-byte aligned");
-    const size_t need = (size_t)n_recv * src->n_block_rows * kBlock * d * sizeof(uint16_t);
+    const size_t need = (size_t)n_v_heads * src->n_block_rows * kBlock * d * sizeof(uint16_t);
     if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
     if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
     a.vt = static_cast<uint16_t*>(workspace);

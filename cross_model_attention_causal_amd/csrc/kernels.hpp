@@ -90,16 +90,17 @@ struct MappedAvArgs {
   const uint16_t* vals;
   int32_t n_block_rows;
   int32_t n_send, n_recv, d;
+  int32_t n_v, v_group;  // V heads; receiver head h reads V head h / v_group
   const float* M;
   int64_t M_stride;
   const void* v;
   bool v_bf16;
-  bool v_key_major;  // v is [n_recv][d][total_k]
+  bool v_key_major;  // v is [n_v][d][total_k] (else [n_v][total_k][d])
   bool v_tiled;      // v is in the fused kernel's operand order (bsr path)
   Varlen vl;
   void* out;
   bool out_bf16;
-  uint16_t* vt;  // bsr path: tiled V [n_recv][n_block_rows][64 * d] (v itself or the workspace)
+  uint16_t* vt;  // bsr path: tiled V [n_v][n_block_rows][64 * d] (v itself or the workspace)
   int32_t max_q;
 };
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);

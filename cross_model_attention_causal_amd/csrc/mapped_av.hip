@@ -56,7 +56,7 @@ constexpr uint16_t kNoBlock = 0xffff;
 // contiguous 1 KB MFMA operand, and the four operands of a panel are adjacent.
 __device__ __forceinline__ int vtile_pos(int ks, int dt, int lane) { return ((ks * 4 + dt) * 64 + lane) * 8; }
 
-// grid (nrb_max, n_seqs, n_recv), 256 threads: one 64-key block of one head.
+// grid (nrb_max, n_seqs, n_v), 256 threads: one 64-key block of one V head.
 template <bool KEY_MAJOR>
 __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, uint16_t* __restrict__ vtile,
                                                 Varlen vl, int32_t n_block_rows) {
@@ -396,10 +396,12 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     // tiled V of slots sA and sB (clamped to the group): this sequence's blocks
     const int v_bytes = ((n + kBlock - 1) / kBlock) * (kBlock * D * 2);
     const __amdgpu_buffer_rsrc_t vA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.vt + ((int64_t)(h_lo + min(sA, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D)),
+        const_cast<uint16_t*>(a.vt + ((int64_t)((h_lo + min(sA, heads_here - 1)) / a.v_group) * a.n_block_rows + roff) *
+                                         (kBlock * D)),
         (short)0, v_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vB = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.vt + ((int64_t)(h_lo + min(sB, heads_here - 1)) * a.n_block_rows + roff) * (kBlock * D)),
+        const_cast<uint16_t*>(a.vt + ((int64_t)((h_lo + min(sB, heads_here - 1)) / a.v_group) * a.n_block_rows + roff) *
+                                         (kBlock * D)),
         (short)0, v_bytes, kBufferFlags);
     // mixed-map operands of slots sA and sB: lane (row n32, half q2) holds keys
     // 8 q2 .. + 7, one contiguous 1 KB read each
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
 #pragma unroll
       for (int rnd = 0; rnd < D / 16; ++rnd) {
         const int f = 16 * rnd + fs;
-        const int64_t vrow = ((int64_t)h * D + f) * a.vl.total_k + k0 + w0;
+        const int64_t vrow = ((int64_t)(h / a.v_group) * D + f) * a.vl.total_k + k0 + w0;
         float part = 0.0f;
         for (int j = 8 * lf; j < wlen; j += 128) {
           float v[8];
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
     } else {
       // 8 independent 16-byte loads in flight per thread, then their products
       const int fc = tid % kChunks, ks = tid / kChunks;
-      const int64_t vbase = ((int64_t)h * a.vl.total_k + k0 + w0) * D + 8 * fc;
+      const int64_t vbase = ((int64_t)(h / a.v_group) * a.vl.total_k + k0 + w0) * D + 8 * fc;
       int j = ks;
       for (; j + 7 * kSlots < wlen; j += 8 * kSlots) {
         float v[8][8];
@@ -731,7 +733,7 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
   const int nrb = (a.max_q + 63) / 64;
   if (!a.v_tiled) {
-    dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_recv);
+    dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_v);  // each V head once
     KernelTimer kt_("k_tile_v", st);
     if (a.v_key_major)
       hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,

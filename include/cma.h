@@ -208,24 +208,27 @@ typedef struct {
 /*
  * cma_mapped_av -- fused mapped attention x V ([MapFlow] approach and fused
  * kernel; [IAM] Method 4 decode with a one-hot M):
- *   O_h = ( sum_j M[s][h][j] * A_j ) @ V_h     for every sequence s,
+ *   O_h = ( sum_j M[s][h][j] * A_j ) @ V_{h / g}     for every sequence s,
  * where A_j is sender head j's map as stored (zeros off the kept blocks for a
- * BSR source). The mixed map is formed on chip and never written to memory.
+ * BSR source) and g = n_recv / n_v_heads receiver heads share one V head
+ * (grouped V; n_v_heads = n_recv: one V per receiver head). The mixed map is
+ * formed on chip and never written to memory.
  * M: fp32 [*, n_recv, n_send], sequence s uses M + s * M_seq_stride
- * (M_seq_stride = 0: one matrix for all). v in `v_layout` (see cma_v_layout) and
- * out [n_recv, total_q, d] in v_dt / out_dt (bf16 or f32); accumulation is fp32.
- * d in {64, 128}, 1 <= n_send <= 64 (dense) or <= 32 (BSR). A BSR source needs
- * bf16 V and d = 128; with TOKEN_MAJOR or KEY_MAJOR V it first writes the TILED
- * copy of V into `workspace` (cma_mapped_av_workspace(...) bytes: n_recv *
- * n_block_rows * 64 * d * 2), with TILED V it needs no workspace and runs as a
- * single kernel. A dense source takes TOKEN_MAJOR or KEY_MAJOR V and needs no
- * workspace.
+ * (M_seq_stride = 0: one matrix for all). v (n_v_heads heads) in `v_layout` (see
+ * cma_v_layout, with n_v_heads in place of n_recv) and out [n_recv, total_q, d]
+ * in v_dt / out_dt (bf16 or f32); accumulation is fp32. n_v_heads >= 1 must
+ * divide n_recv. d in {64, 128}, 1 <= n_send <= 64 (dense) or <= 32 (BSR). A BSR
+ * source needs bf16 V and d = 128; with TOKEN_MAJOR or KEY_MAJOR V it first
+ * writes the TILED copy of V into `workspace` (cma_mapped_av_workspace(...)
+ * bytes: n_v_heads * n_block_rows * 64 * d * 2), with TILED V it needs no
+ * workspace and runs as a single kernel. A dense source takes TOKEN_MAJOR or
+ * KEY_MAJOR V and needs no workspace.
  */
-size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_recv, int32_t d, int64_t total_k,
+size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout);
 int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
-                  int32_t n_recv, const void* v, cma_dtype v_dt, cma_v_layout v_layout, int32_t d,
-                  const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
+                  int32_t n_recv, int32_t n_v_heads, const void* v, cma_dtype v_dt, cma_v_layout v_layout,
+                  int32_t d, const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
                   size_t workspace_bytes, void* stream);
 
 /*

@@ -283,31 +283,38 @@ def test_block_compress_longest_sequence(cma):
 
 
 # ------------------------------------------------------------------ mapped_av block-sparse
-@pytest.mark.parametrize("n_recv,v_layout", [(24, "token"), (7, "token"), (24, "key"), (24, "tiled"), (7, "tiled")])
-def test_mapped_av_bsr_small(cma, n_recv, v_layout):
+# v_heads: grouped V (receiver head h reads V head h // (n_recv // v_heads));
+# None = one V per receiver head. The oracle gets V repeated per group.
+@pytest.mark.parametrize("n_recv,v_layout,v_heads", [(24, "token", None), (7, "token", None), (24, "key", None),
+                                                     (24, "tiled", None), (7, "tiled", None), (24, "token", 6),
+                                                     (24, "tiled", 8), (24, "key", 3)])
+def test_mapped_av_bsr_small(cma, n_recv, v_layout, v_heads):
     lens = [200, 64, 130]
     n_send = 32
-    say(f"mapped_av bsr lens={lens} n_send={n_send} n_recv={n_recv}")
+    n_v = v_heads or n_recv
+    say(f"mapped_av bsr lens={lens} n_send={n_send} n_recv={n_recv} v_heads={n_v} v_layout={v_layout}")
     x = synth.attention_inputs(401, n_send, lens, d=128)
     ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9)
     M = synth.mix_matrix_learned(402, n_recv, n_send)
     T = int(x["cu_q"][-1])
-    V = synth.values(403, n_recv, T, 128)
+    V = synth.values(403, n_v, T, 128)
     vl = cma.Varlen(x["cu_q"], x["cu_q"])
     src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
                vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
     if v_layout == "key":
         O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))), vl,
-                          out_dtype=torch.bfloat16, v_layout=cma.V_KEY_MAJOR)
+                          out_dtype=torch.bfloat16, v_layout=cma.V_KEY_MAJOR, v_heads=v_heads)
     elif v_layout == "tiled":
         O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(tile_v(V, lens, x["cu_q"])), vl,
-                          out_dtype=torch.bfloat16, v_layout=cma.V_TILED, k_rows=T)
+                          out_dtype=torch.bfloat16, v_layout=cma.V_TILED, k_rows=T, v_heads=v_heads)
     else:
-        O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl, out_dtype=torch.bfloat16)
+        O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl, out_dtype=torch.bfloat16,
+                          v_heads=v_heads)
     torch.cuda.synchronize()
     got = host64(O)
     rows = [(s, r) for s in range(len(lens)) for r in range((lens[s] + 63) // 64)]
-    oo = oracle.mapped_av_bsr_rows(ref["row_ptr"], ref["col_idx"], ref["vals"], n_send, lens, M, f64(V),
+    Vr = np.repeat(f64(V), n_recv // n_v, axis=0)
+    oo = oracle.mapped_av_bsr_rows(ref["row_ptr"], ref["col_idx"], ref["vals"], n_send, lens, M, Vr,
                                    x["cu_q"], rows)
     refO = np.zeros_like(got)
     for (s, r), o in oo.items():
@@ -316,18 +323,21 @@ def test_mapped_av_bsr_small(cma, n_recv, v_layout):
     assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
 
 
-@pytest.mark.parametrize("key_major", [False, True])
-def test_mapped_av_dense_decode_rows(cma, key_major):
-    """Decode rows: one query per sequence over long contexts, one-hot and learned M."""
+@pytest.mark.parametrize("key_major,v_heads", [(False, None), (True, None), (False, 3), (True, 2)])
+def test_mapped_av_dense_decode_rows(cma, key_major, v_heads):
+    """Decode rows: one query per sequence over long contexts, one-hot and learned M;
+    optionally grouped V (the oracle gets V repeated per group)."""
     lq, lk = [1, 1, 2], [1000, 513, 300]
     n_send, n_recv = 28, 6
-    say(f"mapped_av dense decode rows lq={lq} lk={lk} key_major={key_major}")
+    n_v = v_heads or n_recv
+    say(f"mapped_av dense decode rows lq={lq} lk={lk} key_major={key_major} v_heads={n_v}")
     x = synth.attention_inputs(501, n_send, lq, d=128, k_lengths=lk)
     om = oracle.attn_maps(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], x["cu_k"])
     maps = np.stack([np.concatenate([A.ravel() for A in om[j]]) for j in range(n_send)])
     mapsr = oracle.round_f32(maps)
     Tk = int(x["cu_k"][-1])
-    V = synth.values(502, n_recv, Tk, 128)
+    V = synth.values(502, n_v, Tk, 128)
+    Vr = np.repeat(f64(V), n_recv // n_v, axis=0)
     vl = cma.Varlen(x["cu_q"], x["cu_k"])
     Ml = synth.mix_matrix_learned(503, n_recv, n_send, n_batch=3)
     Moh = oracle.onehot_mix(np.array([[5, 0, 27, 3, 3, 9], [1, 2, 3, 4, 5, 6], [0, 0, 0, 0, 0, 0]]), n_send).astype(np.float32)
@@ -335,14 +345,14 @@ def test_mapped_av_dense_decode_rows(cma, key_major):
         vd = dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))) if key_major else dev_bf16(V)
         O = cma.mapped_av(("dense", dev_f32(mapsr), cma.DENSE), n_send, dev_f32(M), n_recv, vd, vl,
                           out_dtype=torch.float32, q_rows=int(x["cu_q"][-1]),
-                          v_layout=cma.V_KEY_MAJOR if key_major else cma.V_TOKEN_MAJOR)
+                          v_layout=cma.V_KEY_MAJOR if key_major else cma.V_TOKEN_MAJOR, v_heads=v_heads)
         torch.cuda.synchronize()
         got = host64(O)
         off = 0
         for s_ in range(3):
             A = mapsr[:, off: off + lq[s_] * lk[s_]].reshape(n_send, lq[s_], lk[s_])
             off += lq[s_] * lk[s_]
-            ref = oracle.mapped_av_dense(A, M[s_].astype(np.float64), f64(V)[:, x["cu_k"][s_]: x["cu_k"][s_] + lk[s_]])
+            ref = oracle.mapped_av_dense(A, M[s_].astype(np.float64), Vr[:, x["cu_k"][s_]: x["cu_k"][s_] + lk[s_]])
             assert rel_l2(got[:, x["cu_q"][s_]: x["cu_q"][s_] + lq[s_]], oracle.round_f32(ref)) <= 1e-5
 
 
