@@ -172,6 +172,14 @@ def stage_figures(reps=5):
                    "k_tile_v": ("hbm", 2 * Hr * n * 128 * 2)})
     print(json.dumps({"workload": f"fused mapped x V: {Hr} receiver heads over the {Hs}-head compressed maps "
                                   f"above, learned M, token-major bf16 V (d=128)", "kernels": k_mav}), flush=True)
+    # the same with grouped V: 8 V heads, each shared by 3 receiver heads
+    Hv = 8
+    Vg = V[:Hv].contiguous()
+    k_gqa = timed(lambda: cma.mapped_av(res["bsr"], Hs, M, Hr, Vg, vl, workspace=wsv, v_heads=Hv),
+                  {"k_mapped_av_bsr": ("hbm", nnz * 8192 + (Hv + Hr) * n * 128 * 2 + (Hs * r_tot + 1 + nnz) * 4),
+                   "k_tile_v": ("hbm", 2 * Hv * n * 128 * 2)})
+    print(json.dumps({"workload": f"fused mapped x V with grouped V: {Hr} receiver heads reading {Hv} V heads "
+                                  f"({Hr // Hv} per V head), otherwise as above", "kernels": k_gqa}), flush=True)
 
 
 def main():
