@@ -180,6 +180,19 @@ def stage_figures(reps=5):
                    "k_tile_v": ("hbm", 2 * Hv * n * 128 * 2)})
     print(json.dumps({"workload": f"fused mapped x V with grouped V: {Hr} receiver heads reading {Hv} V heads "
                                   f"({Hr // Hv} per V head), otherwise as above", "kernels": k_gqa}), flush=True)
+    # two such receivers served from the one sender state: separate calls, then one
+    # call with their heads stacked (each sender column read once per XCD)
+    M2 = torch.cat([M, M.flip(1)], dim=1).contiguous()
+    V2 = torch.cat([Vg, Vg.flip(0)]).contiguous()
+    k_two = timed(lambda: (cma.mapped_av(res["bsr"], Hs, M, Hr, Vg, vl, workspace=wsv, v_heads=Hv),
+                           cma.mapped_av(res["bsr"], Hs, M2[:, Hr:].contiguous(), Hr, V2[Hv:], vl, workspace=wsv,
+                                         v_heads=Hv)), {})
+    k_stack = timed(lambda: cma.mapped_av(res["bsr"], Hs, M2, 2 * Hr, V2, vl, workspace=wsv, v_heads=2 * Hv), {})
+    print(json.dumps({"workload": f"two receivers of {Hr} heads ({Hv} V heads each) on the one sender state: two "
+                                  "calls against one call with the heads stacked",
+                      "two_calls_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_two.values()), 4),
+                      "stacked_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_stack.values()), 4),
+                      "kernels_two_calls": k_two, "kernels_stacked": k_stack}), flush=True)
 
 
 def main():

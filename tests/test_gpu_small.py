@@ -323,6 +323,39 @@ def test_mapped_av_bsr_small(cma, n_recv, v_layout, v_heads):
     assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
 
 
+def test_mapped_av_two_receivers_stacked(cma):
+    """Two receivers served from one sender state: their heads stacked in one call
+    (M rows and V heads concatenated, each with its own grouped V) give exactly the
+    outputs of two separate calls, and match the oracle."""
+    lens = [200, 64, 130]
+    n_send = 32
+    say(f"mapped_av two receivers stacked lens={lens}")
+    x = synth.attention_inputs(411, n_send, lens, d=128)
+    ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9)
+    T = int(x["cu_q"][-1])
+    vl = cma.Varlen(x["cu_q"], x["cu_q"])
+    src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
+               vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
+    # receiver 1: 24 heads, 8 V heads; receiver 2: 12 heads, 4 V heads (group 3 in both)
+    M1, M2 = synth.mix_matrix_learned(412, 24, n_send), synth.mix_matrix_learned(413, 12, n_send)
+    V1, V2 = synth.values(414, 8, T, 128), synth.values(415, 4, T, 128)
+    O1 = cma.mapped_av(src, n_send, dev_f32(M1), 24, dev_bf16(V1), vl, v_heads=8)
+    O2 = cma.mapped_av(src, n_send, dev_f32(M2), 12, dev_bf16(V2), vl, v_heads=4)
+    Ms = np.concatenate([M1, M2], axis=1)  # [1, 36, n_send]
+    Os = cma.mapped_av(src, n_send, dev_f32(Ms), 36, dev_bf16(np.concatenate([V1, V2])), vl, v_heads=12)
+    torch.cuda.synchronize()
+    assert torch.equal(Os[:24], O1) and torch.equal(Os[24:], O2)
+    rows = [(s_, r) for s_ in range(len(lens)) for r in range((lens[s_] + 63) // 64)]
+    Vr = np.repeat(f64(np.concatenate([V1, V2])), 3, axis=0)
+    oo = oracle.mapped_av_bsr_rows(ref["row_ptr"], ref["col_idx"], ref["vals"], n_send, lens, Ms, Vr, x["cu_q"], rows)
+    got = host64(Os)
+    refO = np.zeros_like(got)
+    for (s_, r), o in oo.items():
+        a0 = x["cu_q"][s_] + 64 * r
+        refO[:, a0: a0 + o.shape[1]] = o
+    assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
+
+
 @pytest.mark.parametrize("key_major,v_heads", [(False, None), (True, None), (False, 3), (True, 2)])
 def test_mapped_av_dense_decode_rows(cma, key_major, v_heads):
     """Decode rows: one query per sequence over long contexts, one-hot and learned M;
