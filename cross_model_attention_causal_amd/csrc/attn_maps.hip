@@ -1,8 +1,14 @@
 // Causal attention probability maps (GLIDE II-B; materialised as IAM Method 4
-// requires). Two sweeps per 64-query block-row: the first finds each query's
-// softmax max and normaliser with an online update, the second recomputes the
-// scores and writes exp(s - max) / sum. Recomputing QK^T is cheaper than a
-// round trip of the map: writing the map is the HBM cost of this stage.
+// requires). Writing the map is the HBM cost of this stage. Four kernels, chosen
+// per launch:
+//  * k_attn_rows: one query row per sequence (decode), keys read once;
+//  * k_attn_maps_short: every sequence has at most 512 keys; a persistent
+//    workgroup keeps a (sequence, head)'s K in LDS and forms each block-row's
+//    softmax in one pass from scores held in registers;
+//  * k_attn_maps: longer sequences, two sweeps per 64-query block-row (online
+//    max and normaliser, then recompute and write exp(s - max) / sum);
+//    recomputing QK^T is cheaper than a round trip of the map;
+//  * k_attn_maps_f32: fp32 inputs (the reference path), one row per workgroup.
 #include "kernels.hpp"
 #include "score.hpp"
 
