@@ -317,31 +317,67 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   }
 }
 
-// Exclusive scan of the kept counts (one workgroup). Deterministic (integers).
-__global__ __launch_bounds__(1024) void k_bsr_scan(const int32_t* counts, int64_t n, int32_t* row_ptr,
-                                                   int32_t* nnz) {
-  __shared__ int64_t part[1024];
-  const int t = threadIdx.x;
-  const int64_t chunk = (n + 1023) / 1024;
-  const int64_t b0 = t * chunk, b1 = min(n, b0 + chunk);
-  int64_t sum = 0;
-  for (int64_t x = b0; x < b1; ++x) sum += counts[x];
-  part[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t v = t >= off ? part[t - off] : 0;
+// Exclusive scan of the kept counts (one workgroup). The counts go through LDS
+// in tiles of kScanTile with coalesced loads and stores; each thread scans 8
+// consecutive counts, a wave scan and the 16 wave totals give its offset, and a
+// carry runs across tiles. Deterministic (integers).
+constexpr int kScanThreads = 1024, kScanPer = 8, kScanTile = kScanThreads * kScanPer;
+
+__global__ __launch_bounds__(kScanThreads) void k_bsr_scan(const int32_t* counts, int64_t n,
+                                                           int32_t* row_ptr, int32_t* nnz) {
+  __shared__ __attribute__((aligned(16))) int32_t buf[kScanTile];
+  __shared__ int64_t wsum[kScanThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < n; base += kScanTile) {
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int64_t x = base + i * kScanThreads + t;
+      buf[i * kScanThreads + t] = x < n ? counts[x] : 0;
+    }
     __syncthreads();
-    part[t] += v;
+    const int4 c0 = reinterpret_cast<const int4*>(buf)[2 * t];
+    const int4 c1 = reinterpret_cast<const int4*>(buf)[2 * t + 1];
+    const int32_t v[kScanPer] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    int64_t own = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) own += v[i];
+    int64_t pre = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t y = __shfl_up(pre, off, 64);
+      if (lane >= off) pre += y;
+    }
+    if (lane == 63) wsum[w] = pre;
     __syncthreads();
+    int64_t before = 0, total = 0;
+#pragma unroll
+    for (int j = 0; j < kScanThreads / 64; ++j) {
+      const int64_t sj = wsum[j];
+      before += j < w ? sj : 0;
+      total += sj;
+    }
+    int64_t run = carry + before + pre - own;
+    int32_t o[kScanPer];
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      o[i] = (int32_t)run;
+      run += v[i];
+    }
+    reinterpret_cast<int4*>(buf)[2 * t] = make_int4(o[0], o[1], o[2], o[3]);
+    reinterpret_cast<int4*>(buf)[2 * t + 1] = make_int4(o[4], o[5], o[6], o[7]);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int64_t x = base + i * kScanThreads + t;
+      if (x < n) row_ptr[x] = buf[i * kScanThreads + t];
+    }
+    carry += total;
+    __syncthreads();  // buf and wsum are rewritten by the next tile
   }
-  int64_t run = part[t] - sum;  // exclusive prefix of this chunk
-  for (int64_t x = b0; x < b1; ++x) {
-    row_ptr[x] = (int32_t)run;
-    run += counts[x];
-  }
-  if (t == 1023) {
-    row_ptr[n] = (int32_t)part[1023];
-    nnz[0] = (int32_t)part[1023];
+  if (t == 0) {
+    row_ptr[n] = (int32_t)carry;
+    nnz[0] = (int32_t)carry;
   }
 }
 
@@ -550,7 +586,7 @@ static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   {
     KernelTimer kt_("k_bsr_scan", st);
-    hipLaunchKernelGGL(k_bsr_scan, dim3(1), dim3(1024), 0, st, a.counts,
+    hipLaunchKernelGGL(k_bsr_scan, dim3(1), dim3(kScanThreads), 0, st, a.counts,
                        (int64_t)a.n_heads * a.n_block_rows, a.row_ptr, a.nnz);
   }
   e = hipGetLastError();
