@@ -9,8 +9,9 @@
 // step t
 //   - the 32 senders' 32 x 16 pieces of panel t + 2 (one contiguous 1 KB run of
 //     a stored block's 16-column panel per sender, or a zero page for a sender
-//     that did not keep the block), loaded into registers in step t - 1, are
-//     written to LDS, and those of panel t + 3 are loaded;
+//     that did not keep the block), loaded into registers in step t - 2, are
+//     written to LDS, and those of panel t + 4 are loaded (two register sets,
+//     so that every global read has two steps to arrive);
 //   - the V operands of panel t + 2 are loaded into a ring of registers;
 //   - panel t + 1 is mixed on the matrix cores: D1[h, pos] = sum_j M[h, j]
 //     A_j[pos] for 16 positions is a 16x16x32 MFMA with M (split into bf16 high
@@ -439,35 +440,38 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       if (do_mix) mix_store(bbm, tr);
     };
 
-    u32x4 S[kSend / kWaves];  // the sender pieces of the next panel to stage
+    u32x4 S[2][kSend / kWaves];  // sender pieces of the next two panels to stage
 
-    // Step t: write panel t + 2 (in S since step t - 1) to stage t % 2 (panel
-    // t's, mixed in step t - 1), load panel t + 3 into S, mix panel t + 1 (stage
-    // (t + 1) % 2) into mixed buffer (t + 1) % 2, multiply panel t (mixed buffer
-    // t % 2) with V slot t % 2, then load V of panel t + 2 into that slot. The
-    // compiler places the waits for the loaded registers itself.
+    // Step t: write panel t + 2 (in S[t % 2] since step t - 2) to stage t % 2
+    // (panel t's, mixed in step t - 1), load panel t + 4 into S[t % 2], mix
+    // panel t + 1 (stage (t + 1) % 2) into mixed buffer (t + 1) % 2, multiply
+    // panel t (mixed buffer t % 2) with V slot t % 2, then load V of panel t + 2
+    // into that slot. The compiler places the waits for the loaded registers
+    // itself; in the main loop a step waits only for loads issued two steps
+    // before it (the two later steps' loads stay in flight), because the
+    // prologue issues its loads in the loop's order.
     //
-    // Main loop: 4 steps per trip, all full (t + 3 < T), with the column changes
-    // at fixed steps (panel t + 3 starts a column when t % 4 == 1, panel t + 2
+    // Main loop: 4 steps per trip, all full (t + 4 < T), with the column changes
+    // at fixed steps (panel t + 4 starts a column when t % 4 == 0, panel t + 2
     // when t % 4 == 2).
     auto step_main = [&](int t0, auto ic) __attribute__((always_inline)) {
       constexpr int I = decltype(ic)::value;
       const int t = t0 + I;
-      store_stage(S, I & 1);
-      if constexpr (I == 1) col_src(col_at((t + 3) >> 2), dsrc);
-      load_stage(dsrc, (I + 3) & 3, S);
+      store_stage(S[I & 1], I & 1);
+      if constexpr (I == 0) col_src(col_at((t + 4) >> 2), dsrc);
+      load_stage(dsrc, I, S[I & 1]);
       compute((I + 1) & 1, (I + 1) & 1, true, I & 1, vr[I & 1]);
       if constexpr (I == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
       load_v((I + 2) & 3, vr[I & 1]);
       barrier_lds();
     };
-    // The last steps (at most 6): the same work under run-time tests.
+    // The last steps (at most 7): the same work under run-time tests.
     auto step_tail = [&](int t, auto ic) __attribute__((always_inline)) {
       constexpr int I = decltype(ic)::value;  // t % 4 == I
-      if (t + 2 < T) store_stage(S, I & 1);
-      if (t + 3 < T) {
-        if (I == 1) col_src(col_at((t + 3) >> 2), dsrc);
-        load_stage(dsrc, (I + 3) & 3, S);
+      if (t + 2 < T) store_stage(S[I & 1], I & 1);
+      if (t + 4 < T) {
+        if (I == 0) col_src(col_at((t + 4) >> 2), dsrc);
+        load_stage(dsrc, I, S[I & 1]);
       }
       compute((I + 1) & 1, (I + 1) & 1, t + 1 < T, I & 1, vr[I & 1]);
       if (t + 2 < T) {
@@ -490,35 +494,42 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
 #pragma unroll
     for (int k = 0; k < NI; ++k) acc[k] = f32x16{};
     if (T > 0) {
-      // prologue (T >= 4, one column at least): panels 0 and 1 staged, panel 2
-      // in S, V of panels 0 and 1 loaded, panel 0 mixed
+      // prologue (T >= 4, one column at least): panels 0 and 1 staged, panel 0
+      // mixed, panels 2 and 3 in S[0] and S[1], V of panels 0 and 1 loaded
       col_src(col_at(0), dsrc);
       v_off = col_at(0) * (kBlock * D);
-      load_stage(dsrc, 0, S);
-      store_stage(S, 0);
-      load_stage(dsrc, 1, S);
-      load_v(0, vr[0]);
-      load_v(1, vr[1]);
+      load_stage(dsrc, 0, S[0]);
+      load_stage(dsrc, 1, S[1]);
+      store_stage(S[0], 0);
+      store_stage(S[1], 1);
       barrier_lds();
       u32x2 tr[8];
       read_mix_src(0, tr);
       mix_store(0, tr);
-      store_stage(S, 1);
-      load_stage(dsrc, 2, S);
+      // the loop's loads in its own order (sender panel, V panel, sender panel,
+      // V panel), so that the waits the compiler places at the loop head are
+      // the loop's own
+      load_stage(dsrc, 2, S[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(0, vr[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(dsrc, 3, S[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(1, vr[1]);
       barrier_lds();
-    }
-    int t = 0;
-    for (; t + 6 < T; t += 4) {
-      step_main(t, std::integral_constant<int, 0>{});
-      step_main(t, std::integral_constant<int, 1>{});
-      step_main(t, std::integral_constant<int, 2>{});
-      step_main(t, std::integral_constant<int, 3>{});
-    }
-    for (; t < T; t += 4) {  // t % 4 == 0 here
-      step_tail(t, std::integral_constant<int, 0>{});
-      if (t + 1 < T) step_tail(t + 1, std::integral_constant<int, 1>{});
-      if (t + 2 < T) step_tail(t + 2, std::integral_constant<int, 2>{});
-      if (t + 3 < T) step_tail(t + 3, std::integral_constant<int, 3>{});
+      int t = 0;
+      for (; t + 7 < T; t += 4) {
+        step_main(t, std::integral_constant<int, 0>{});
+        step_main(t, std::integral_constant<int, 1>{});
+        step_main(t, std::integral_constant<int, 2>{});
+        step_main(t, std::integral_constant<int, 3>{});
+      }
+      for (; t < T; t += 4) {  // t % 4 == 0 here
+        step_tail(t, std::integral_constant<int, 0>{});
+        if (t + 1 < T) step_tail(t + 1, std::integral_constant<int, 1>{});
+        if (t + 2 < T) step_tail(t + 2, std::integral_constant<int, 2>{});
+        if (t + 3 < T) step_tail(t + 3, std::integral_constant<int, 3>{});
+      }
     }
     // epilogue: D[m = row][n = feature]: row = 8(v/4) + 4 q2 + (v%4), feature = 32 dt + n32
 #pragma unroll
