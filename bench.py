@@ -79,8 +79,9 @@ def log(*a):
 def stage_figures(reps=5):
     """Each stage at its own workload: the 512-token head mapping (maps of 336 small-
     and 2560 large-model heads, the 2560 x 336 cosine), the 32-head x 8192-token
-    compression at tau 0.95, and the fused pass of 24 receiver heads over it.
-    Per kernel: average launch time from HIP events on the launch stream, the
+    compression at tau 0.95, the fused pass of 24 receiver heads over it, and
+    one mapped layer of the varlen serving mix (its prefill chain and one decode
+    step). Per kernel: average launch time from HIP events on the launch stream, the
     algorithmic work per launch, and the fraction of the roofline that binds it."""
     import torch
     import cross_model_attention_causal_amd as cma
@@ -193,6 +194,80 @@ def stage_figures(reps=5):
                       "two_calls_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_two.values()), 4),
                       "stacked_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_stack.values()), 4),
                       "kernels_two_calls": k_two, "kernels_stacked": k_stack}), flush=True)
+    del res, q, k, M, V, Vg, M2, V2, ws, wsv
+
+    # the varlen serving mix, one mapped layer: the prefill chain over all 68
+    # prompts, then one decode step of the 64 short prompts at the longest context
+    t0 = time.time()
+    x = synth.cfg5_layer(0)
+    log(f"serving-mix inputs in {time.time() - t0:.1f}s")
+    Hs, Hr, tt, nsh, dec = x["n_send"], x["n_recv"], x["tau_t"], x["n_short"], x["decode"]
+    pl, cp, cs = x["prompt_lengths"], x["cu_prompt"], x["cu_store"]
+    P, L = len(pl), tt * (tt + 1) // 2
+    sq, sk = bf(x["send_q"]), bf(x["send_k"])
+    ss, sb = f32(x["send_scale"]), f32(x["send_bias"])
+    rq, rk, rs, rb = bf(x["recv_q"]), bf(x["recv_k"]), f32(x["recv_scale"]), f32(x["recv_bias"])
+    v = bf(x["v"])
+    vl_s = cma.Varlen(cp, cs, used_q=[tt] * P, used_k=[tt] * P)
+    vl_r = cma.Varlen(np.arange(P + 1) * tt)
+    vl_p = cma.Varlen(cp, cs, used_q=pl, used_k=pl)
+    ws, wsv = cma.Workspace(), cma.Workspace()
+    st = {}
+
+    def prefill():
+        sm = cma.attn_maps(sq, sk, ss, sb, vl_s)
+        rm = cma.attn_maps(rq, rk, rs, rb, vl_r)
+        _, st["arg"], _ = cma.head_map_cosine(rm, sm, P, Hr, Hs, L, P * L, L, P * L, L)
+        st["bsr"] = cma.block_compress(sq, sk, ss, sb, vl_p, 0.95, workspace=ws)
+        # one sender per receiver head: the argmax itself selects the maps
+        st["O"] = cma.mapped_av(st["bsr"], Hs, st["arg"], Hr, v, vl_p, q_rows=int(cp[-1]), workspace=wsv)
+    prefill()
+    torch.cuda.synchronize()
+    nnz = int(st["bsr"]["nnz"].item())
+    tri = sum(n * (n + 1) // 2 for n in pl)
+    r_tot = sum((n + 63) // 64 for n in pl)
+    tokens = int(cp[-1])
+    # blocks of the senders in use: each prompt's kept blocks of the senders its heads map to
+    rp = st["bsr"]["row_ptr"].cpu().numpy().astype(np.int64)
+    argh = st["arg"].cpu().numpy()
+    roff = np.concatenate([[0], np.cumsum([(n + 63) // 64 for n in pl])])
+    used_blocks = sum(int(rp[j * r_tot + roff[p_ + 1]] - rp[j * r_tot + roff[p_]])
+                      for p_ in range(P) for j in set(argh[p_].tolist()))
+    maps_bytes = P * (Hs + Hr) * (2 * tt * 128 * 2 + L * 2) / 2
+    idx_bytes = used_blocks * 8192 + 2 * Hr * tokens * 128 * 2 + (Hs * r_tot + 1 + nnz) * 4
+    k_pre = timed(prefill, {"k_attn_maps_short": ("hbm", maps_bytes),
+                            "k_gram_bf16": ("mfma", 2 * Hr * Hs * L * P),
+                            "k_block_stats": ("mfma", Hs * tri * 128 * 2),
+                            "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2),
+                            "k_mapped_av_idx": ("hbm", idx_bytes),
+                            "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2)})
+    pre_ms = sum(e["ms"] * e["launches_per_call"] for e in k_pre.values())
+    # the general fused pass on the same problem, with the argmax as a one-hot M
+    st["M"] = cma.onehot_mix(st["arg"], Hs)
+    k_gen = timed(lambda: cma.mapped_av(st["bsr"], Hs, st["M"], Hr, v, vl_p, q_rows=tokens, workspace=wsv),
+                  {"k_mapped_av_bsr": ("hbm", idx_bytes)})
+    print(json.dumps({"workload": f"serving mix, one mapped layer, prefill: {P} prompts ({nsh} x {pl[0]} + "
+                                  f"{P - nsh} x {pl[-1]} tokens) packed varlen, {Hs} sender / {Hr} receiver heads "
+                                  f"(d=128, bf16): prefix maps (tau_t={tt}), per-prompt cosine head maps, one-hot "
+                                  "M, block compression at tau 0.95, fused mapped x V",
+                      "kernel_ms_per_layer": round(pre_ms, 4), "kept_block_fraction":
+                      round(nnz / (Hs * sum((n // 64) * (n // 64 + 1) // 2 for n in pl)), 4),
+                      "kernels": k_pre, "general_path_one_hot_M": k_gen}), flush=True)
+    t = dec - 1
+    ctx = tt + t + 1
+    vl_d = cma.Varlen(np.arange(nsh + 1), cs[: nsh + 1], used_q=[1] * nsh, used_k=[ctx] * nsh)
+    qd = bf(x["send_dec_q"][t])
+    Md = st["M"][:nsh].contiguous()
+
+    def decode():
+        rows = cma.attn_maps(qd, sk, ss, sb, vl_d, layout=cma.DENSE, out_dtype=torch.float32)
+        st["od"] = cma.mapped_av(("dense", rows, cma.DENSE), Hs, Md, Hr, v, vl_d, q_rows=nsh)
+    k_dec = timed(decode, {"k_attn_rows": ("hbm", Hs * nsh * ctx * (128 * 2 + 4)),
+                           "k_mapped_av_dense": ("hbm", Hr * nsh * ctx * (128 * 2 + 4))})
+    dec_ms = sum(e["ms"] * e["launches_per_call"] for e in k_dec.values())
+    print(json.dumps({"workload": f"serving mix, one mapped layer, one decode step: {nsh} prompts at context "
+                                  f"{ctx}, sender rows over {Hs} heads and the one-hot mapped x V of {Hr} receiver "
+                                  "heads", "kernel_ms_per_step": round(dec_ms, 4), "kernels": k_dec}), flush=True)
 
 
 def main():

@@ -30,7 +30,7 @@ EXPORTS = [
     "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
     "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks",
     "cma_block_compress_workspace", "cma_block_compress", "cma_mapped_av_workspace",
-    "cma_mapped_av", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
+    "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
     "cma_timing_collect", "cma_timing_get", "cma_timing_name", "cma_timing_reset",
 ]
 
@@ -86,6 +86,9 @@ def load_library(path: str = LIB_PATH):
         "cma_mapped_av_workspace": (SZ, [P, I32, I32, I64, ctypes.c_int]),
         "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, I32, P, ctypes.c_int, ctypes.c_int, I32, P,
                                          P, ctypes.c_int, P, SZ, P]),
+        "cma_mapped_av_indexed_workspace": (SZ, [P, I32, I32, I32, I32, ctypes.c_int]),
+        "cma_mapped_av_indexed": (ctypes.c_int, [P, I32, P, I64, I32, I32, P, ctypes.c_int, ctypes.c_int, I32,
+                                                 P, P, ctypes.c_int, P, SZ, P]),
         "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
         "cma_mapping_plan": (ctypes.c_int, [I32, P, I32, I32, P, P]),
@@ -318,7 +321,10 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
               workspace: Workspace | None = None, out=None, q_rows=None, v_layout=V_TOKEN_MAJOR,
               k_rows=None, v_heads=None):
     """O_h = (sum_j M[h, j] A_j) V_{h // g}, g = n_recv // v_heads (grouped V;
-    default v_heads = n_recv). ``src`` is either a block_compress result
+    default v_heads = n_recv). ``M`` is fp32 mixing weights [B, n_recv, n_send],
+    or int32 sender indices [B, n_recv] (one sender per receiver head, e.g. the
+    cosine argmax: O_h = A_{M[h]} V_{h // g}, block-sparse source only; then
+    ``M_seq_stride`` counts int32 entries). ``src`` is either a block_compress result
     (dict with row_ptr/col_idx/vals/n_block_rows) or ``("dense", maps, layout)``.
     ``v`` is [v_heads, Tk, d] (V_TOKEN_MAJOR), [v_heads, d, Tk] (V_KEY_MAJOR) or
     [v_heads, n_block_rows, 64 * 128] (V_TILED, block-sparse source only; then
@@ -366,12 +372,26 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         s.maps_dt = _dt(maps)
         s.layout = layout
         s.head_stride = maps.shape[1]
+    cvl = vl.c(Tq, Tk)
+    if M.dtype == torch.int32:
+        if s.kind != SRC_BSR:
+            raise ValueError("sender indices need a block-sparse source")
+        if M_seq_stride is None:
+            M_seq_stride = 0 if M.shape[0] == 1 else n_recv
+        _need(M, "sender", M_seq_stride * max(0, vl.n_seqs - 1) + n_recv)
+        ws_bytes = lib.cma_mapped_av_indexed_workspace(ctypes.byref(s), n_recv, n_v, d, vl.n_seqs, v_layout)
+        ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
+        _check(lib.cma_mapped_av_indexed(ctypes.byref(s), n_send, _dev_ptr(M, "sender"), M_seq_stride, n_recv,
+                                         n_v, _dev_ptr(v, "v"), _dt(v), v_layout, d, ctypes.byref(cvl),
+                                         _dev_ptr(out, "out"), _dt(out),
+                                         ws.data_ptr() if ws is not None else None,
+                                         ws.numel() if ws is not None else 0, _stream()))
+        return out
     if M_seq_stride is None:
         M_seq_stride = 0 if M.shape[0] == 1 else n_recv * n_send
     _need(M, "M", M_seq_stride * max(0, vl.n_seqs - 1) + n_recv * n_send)
     ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_v, d, Tk, v_layout)
     ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
-    cvl = vl.c(Tq, Tk)
     _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv, n_v,
                              _dev_ptr(v, "v"), _dt(v), v_layout, d, ctypes.byref(cvl),
                              _dev_ptr(out, "out"), _dt(out),

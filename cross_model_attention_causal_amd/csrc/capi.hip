@@ -433,6 +433,98 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   return hip_status(launch_mapped_av_bsr(a, st), "mapped_av (block-sparse) launch");
 }
 
+// Workspace of the indexed path: [tiled V (unless V is tiled)][roff][order][pairs],
+// each part on a 256-byte boundary. The pair table holds at most
+// sum_s ceil(R_s / 2) <= (n_block_rows + n_seqs) / 2 items.
+namespace {
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+struct IdxLayout {  // byte offsets into the workspace; the tiled V (if any) starts at 0
+  size_t roff, order, pairs, total;
+  int64_t cap;
+};
+IdxLayout idx_layout(int32_t n_block_rows, int32_t n_recv, int32_t n_v_heads, int32_t d, int32_t n_seqs,
+                     bool tiled) {
+  IdxLayout l{};
+  l.cap = ((int64_t)n_block_rows + n_seqs) / 2 + 1;
+  l.roff = tiled ? 0 : round256((size_t)n_v_heads * n_block_rows * kBlock * d * sizeof(uint16_t));
+  l.order = l.roff + round256((size_t)n_seqs * sizeof(int32_t));
+  l.pairs = l.order + round256((size_t)n_seqs * n_recv * sizeof(int32_t));
+  l.total = l.pairs + round256((size_t)l.cap * sizeof(int32_t));
+  return l;
+}
+}  // namespace
+
+size_t cma_mapped_av_indexed_workspace(const cma_maps_src* src, int32_t n_recv, int32_t n_v_heads, int32_t d,
+                                       int32_t n_seqs, cma_v_layout v_layout) {
+  if (!src || src->kind != CMA_SRC_BSR || n_recv <= 0 || n_v_heads <= 0 || d <= 0 || n_seqs <= 0 ||
+      src->n_block_rows < 0)
+    return 0;
+  return idx_layout(src->n_block_rows, n_recv, n_v_heads, d, n_seqs, v_layout == CMA_V_TILED).total;
+}
+
+int cma_mapped_av_indexed(const cma_maps_src* src, int32_t n_send, const int32_t* sender,
+                          int64_t sender_seq_stride, int32_t n_recv, int32_t n_v_heads, const void* v,
+                          cma_dtype v_dt, cma_v_layout v_layout, int32_t d, const cma_varlen* vl, void* out,
+                          cma_dtype out_dt, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!src) return fail(CMA_EINVAL, "NULL maps source");
+  if (src->kind != CMA_SRC_BSR) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed reads block-sparse maps only");
+  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR && v_layout != CMA_V_TILED)
+    return fail(CMA_EINVAL, "bad V layout");
+  if (int e = check_varlen(vl, true)) return e;
+  if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
+  if (n_send < 0 || n_recv < 0 || sender_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
+  if (n_v_heads < 1 || (n_recv > 0 && n_recv % n_v_heads != 0))
+    return fail(CMA_EINVAL, "n_v_heads (%d) must be >= 1 and divide n_recv (%d)", n_v_heads, n_recv);
+  if (n_recv == 0 || vl->n_seqs == 0) return CMA_OK;
+  if (v_dt != CMA_BF16 || d != 128) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed needs bf16 V and d = 128");
+  if (n_send < 1 || n_send > 256) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports 1 <= n_send <= 256");
+  if (n_recv > 256) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports n_recv <= 256");
+  if (vl->n_seqs >= (1 << 24)) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports fewer than 2^24 sequences");
+  if (!sender || !v || !out) return fail(CMA_EINVAL, "NULL sender, v or out");
+  if (!src->row_ptr || !src->col_idx || !src->vals) return fail(CMA_EINVAL, "NULL block-sparse arrays");
+  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
+    return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports sequences up to %d tokens", kMaxBlockRows * kBlock);
+  if (!aligned16(src->vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
+  if (src->n_block_rows < 0) return fail(CMA_EINVAL, "negative n_block_rows");
+  if (vl->max_seqlen_q > 0 && src->n_block_rows == 0)
+    return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
+  if (vl->max_seqlen_q > vl->max_seqlen_k && vl->max_seqlen_k > 0)
+    return fail(CMA_EINVAL, "block-sparse maps are square: max_seqlen_q must not exceed max_seqlen_k");
+  const bool tiled = v_layout == CMA_V_TILED;
+  const IdxLayout l = idx_layout(src->n_block_rows, n_recv, n_v_heads, d, vl->n_seqs, tiled);
+  if (!workspace || workspace_bytes < l.total) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", l.total);
+  if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
+  if (tiled ? !aligned16(v) : (v_layout == CMA_V_TOKEN_MAJOR && !aligned16(v)))
+    return fail(CMA_EINVAL, "V must be 16-byte aligned");
+  MappedAvArgs a{};
+  a.n_send = n_send;
+  a.n_recv = n_recv;
+  a.n_v = n_v_heads;
+  a.v_group = n_recv / n_v_heads;
+  a.d = d;
+  a.v = v;
+  a.v_bf16 = true;
+  a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
+  a.v_tiled = tiled;
+  a.vl = to_varlen(vl);
+  a.out = out;
+  a.out_bf16 = out_dt == CMA_BF16;
+  a.max_q = vl->max_seqlen_q;
+  a.row_ptr = src->row_ptr;
+  a.col_idx = src->col_idx;
+  a.vals = static_cast<const uint16_t*>(src->vals);
+  a.n_block_rows = src->n_block_rows;
+  char* ws = static_cast<char*>(workspace);
+  a.vt = tiled ? const_cast<uint16_t*>(static_cast<const uint16_t*>(v)) : reinterpret_cast<uint16_t*>(ws);
+  a.sender = sender;
+  a.sender_stride = sender_seq_stride;
+  a.plan_roff = reinterpret_cast<int32_t*>(ws + l.roff);
+  a.plan_order = reinterpret_cast<int32_t*>(ws + l.order);
+  a.plan_pairs = reinterpret_cast<int32_t*>(ws + l.pairs);
+  a.plan_cap = l.cap;
+  return hip_status(launch_mapped_av_indexed(a, static_cast<hipStream_t>(stream)), "mapped_av_indexed launch");
+}
+
 int cma_onehot_mix(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32_t n_send, float* M,
                    void* stream) {
   if (n_batch < 0 || n_recv < 0 || n_send < 0) return fail(CMA_EINVAL, "negative size");

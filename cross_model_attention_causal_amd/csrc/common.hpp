@@ -90,6 +90,7 @@ __device__ __forceinline__ u32x4 ldg16_guard_any(const uint16_t* row, int64_t j0
 constexpr int kBufferFlags = 0x00020000;
 constexpr uint32_t kBufferOff = 0x80000000u;  // an offset past any descriptor used here
 constexpr int kCacheNT = 2;                   // cache-policy bit of a buffer access: non-temporal
+constexpr int kWaitVmcnt0 = 0x0f70;           // s_waitcnt immediate: vmcnt(0), other counters free
 
 // ------------------------------------------------------------------ cross-lane
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }

@@ -102,9 +102,17 @@ struct MappedAvArgs {
   bool out_bf16;
   uint16_t* vt;  // bsr path: tiled V [n_v][n_block_rows][64 * d] (v itself or the workspace)
   int32_t max_q;
+  // indexed path (one sender per receiver head): sender[s * sender_stride + h]
+  const int32_t* sender;
+  int64_t sender_stride;
+  int32_t* plan_roff;   // [n_seqs]: first block-row of each sequence
+  int32_t* plan_order;  // [n_seqs * n_recv]: receiver heads of each sequence, ordered by sender
+  int32_t* plan_pairs;  // [plan_cap]: (sequence << 7 | pair) of every work item, -1 past the end
+  int64_t plan_cap;
 };
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st);
+hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_onehot(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32_t n_send,
                          float* M, hipStream_t st);
 

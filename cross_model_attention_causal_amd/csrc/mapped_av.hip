@@ -553,6 +553,221 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   else run(std::integral_constant<int, 2>{});
 }
 
+// ------------------------------------------------------------ indexed source
+// One sender per receiver head, the head map of IAM Method 4 (the argmax of the
+// cosine): O_h = A_{j(h)} V_h. No mix is formed; each wave owns one receiver head
+// and 64 query rows (one block-row) and walks only its own sender's kept blocks
+// of that row. The stored block's 16-key panel already holds, for 32 rows, the
+// A operand of a 32x32x16 MFMA as one contiguous 1 KB run (lane L: row L % 32,
+// keys 8 (L / 32) .. + 7), and the tiled V holds the B operand, so both go from
+// memory straight to registers: no LDS, no barrier. Per 16-key panel a wave
+// issues 6 loads (2 row halves of A, 4 feature tiles of V) and 8 MFMAs; loads run
+// three panels ahead in a ring of four register sets.
+//
+// Work items are (sequence, pair of block-rows, octet of heads): the long row of
+// the pair with its columns ascending, then the short row descending (every pair
+// covers R + 1 columns). A workgroup is one item, its 8 waves the octet's heads
+// in the order of their senders, so heads that share a sender read its blocks
+// together. Workgroup id = item * n_oct + octet: with 8 octets (64 heads) every
+// item of octet o runs on XCD o, whose L2 then holds that octet's V columns and
+// sender blocks for all the pairs in flight there.
+
+// Receiver heads of each sequence ordered by sender (ties by head; heads whose
+// sender index is out of range last). grid (n_seqs), 256 threads.
+__global__ __launch_bounds__(256) void k_idx_order(MappedAvArgs a) {
+  __shared__ int32_t key[256];
+  const int s = blockIdx.x, h = threadIdx.x, H = a.n_recv;
+  if (h < H) {
+    const int j = a.sender[(int64_t)s * a.sender_stride + h];
+    key[h] = (j >= 0 && j < a.n_send ? j : a.n_send) * 256 + h;
+  }
+  __syncthreads();
+  if (h < H) {
+    const int kh = key[h];
+    int rank = 0;
+    for (int x = 0; x < H; ++x) rank += key[x] < kh;
+    a.plan_order[(int64_t)s * H + rank] = h;
+  }
+}
+
+// Block-row offsets of the sequences and the work-item table. One workgroup.
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void k_idx_plan(MappedAvArgs a) {
+  __shared__ int64_t wsum[kPlanThreads / 64][2];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int64_t x = t; x < a.plan_cap; x += kPlanThreads) a.plan_pairs[x] = -1;
+  // exclusive scans of block-rows and pairs over the sequences, in chunks of
+  // consecutive sequences per thread
+  const int ns = a.vl.n_seqs;
+  const int chunk = (ns + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(ns, t * chunk), s1 = min(ns, s0 + chunk);
+  int64_t rows = 0, pairs = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int32_t n = seq_len_q(a.vl, s);
+    const int nrb = seq_ok(a.vl, s, n, n) ? (n + kBlock - 1) / kBlock : 0;
+    rows += nrb;
+    pairs += (nrb + 1) / 2;
+  }
+  int64_t pr = rows, pp = pairs;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t yr = __shfl_up(pr, off, 64), yp = __shfl_up(pp, off, 64);
+    if (lane >= off) {
+      pr += yr;
+      pp += yp;
+    }
+  }
+  if (lane == 63) {
+    wsum[w][0] = pr;
+    wsum[w][1] = pp;
+  }
+  __syncthreads();  // also orders the -1 fill before the writes below
+  int64_t br = 0, bp = 0;
+  for (int x = 0; x < w; ++x) {
+    br += wsum[x][0];
+    bp += wsum[x][1];
+  }
+  int64_t roff = br + pr - rows, poff = bp + pp - pairs;
+  for (int s = s0; s < s1; ++s) {
+    const int32_t n = seq_len_q(a.vl, s);
+    const int nrb = seq_ok(a.vl, s, n, n) ? (n + kBlock - 1) / kBlock : 0;
+    a.plan_roff[s] = (int32_t)roff;
+    for (int p = 0; p < (nrb + 1) / 2; ++p)
+      if (poff + p < a.plan_cap) a.plan_pairs[poff + p] = (s << 7) | p;
+    roff += nrb;
+    poff += (nrb + 1) / 2;
+  }
+}
+
+// grid (plan_cap * n_oct), 512 threads (8 waves, one receiver head each).
+__global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct) {
+  constexpr int D = 128;
+  const int item = blockIdx.x / n_oct, oct = blockIdx.x % n_oct;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int hs = 8 * oct + wave;
+  if (hs >= a.n_recv) return;
+  const int code = ld_const(a.plan_pairs + item);
+  if (code < 0) return;
+  const int s = code >> 7, pr = code & 127;
+  const int32_t n = seq_len_q(a.vl, s);
+  if (!seq_ok(a.vl, s, n, n)) return;
+  const int nrb = (n + kBlock - 1) / kBlock;
+  const int r_long = nrb - 1 - pr;
+  if (r_long < pr) return;
+  const int n_pass = r_long > pr ? 2 : 1;
+  const int h = ld_const(a.plan_order + (int64_t)s * a.n_recv + hs);
+  const int j = ld_const(a.sender + (int64_t)s * a.sender_stride + h);
+  const bool j_ok = j >= 0 && j < a.n_send;
+  const int roff = ld_const(a.plan_roff + s);
+  const int64_t q0 = cu_q_of(a.vl, s);
+  // tiled V of this head's V head over this sequence's blocks
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      a.vt + ((int64_t)(h / a.v_group) * a.n_block_rows + roff) * (kBlock * D), (short)0,
+      nrb * (kBlock * D * 2), kBufferFlags);
+  const uint32_t a_lane = 32u * (lane & 31) + 16u * (lane >> 5);  // A operand: row L % 32, keys 8 (L / 32) ..
+  const uint32_t v_lane = 16u * lane;
+
+  struct Set {
+    u32x4 x[2];  // A of row halves 0 and 1
+    u32x4 v[4];  // V of feature tiles 0..3
+  };
+  for (int pass = 0; pass < n_pass; ++pass) {
+    const int r = pass ? pr : r_long;
+    const int rdir = pass;  // 1: columns descending
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[u][dt] = f32x16{};
+    int beg = 0, nb = 0;
+    if (j_ok) {
+      const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
+      beg = ld_const(a.row_ptr + g);
+      nb = ld_const(a.row_ptr + g + 1) - beg;
+    }
+    if (nb > 0) {
+      // Block k of the sweep (k = nb - 1 past the end): its stored index e and
+      // column c. (Integer arithmetic rather than selects: the compiler turns
+      // uniform selects into branches, and a branch in the loop makes it wait
+      // for every load in flight.)
+      auto blk = [&](int k) __attribute__((always_inline)) {
+        const int kk = min(k, nb - 1);
+        return beg + kk + rdir * (nb - 1 - 2 * kk);
+      };
+      // Issue the loads of panel ks of block e (column c) into set S; okv = 0
+      // past the last block: the descriptors then hold no bytes and the loads
+      // return zeros without touching memory.
+      auto issue = [&](int ks, int e, int c, int okv, Set& S) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(a.vals + (int64_t)e * (kBlock * kBlock)), (short)0, okv * (kBlock * kBlock * 2),
+            kBufferFlags);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) S.x[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane + 1024u * u, 2048 * ks, 0);
+        const int vo = (int)((uint32_t)(c * (kBlock * D * 2) + ks * 4096) | ((uint32_t)(1 - okv) << 31));
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) S.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_lane + 1024u * dt, vo, 0);
+      };
+      auto compute = [&](const Set& S) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) acc[u][dt] = mfma32(as_bf16x8(S.x[u]), as_bf16x8(S.v[dt]), acc[u][dt]);
+      };
+      Set S0, S1, S2, S3;
+      int e_cur = blk(0), c_cur = ld_const(a.col_idx + e_cur);
+      issue(0, e_cur, c_cur, 1, S0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(1, e_cur, c_cur, 1, S1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(2, e_cur, c_cur, 1, S2);
+      __builtin_amdgcn_sched_barrier(0);
+      // One block (4 panels) per trip; panel t + 3 is issued before panel t is
+      // used. The scheduling barriers keep the loads in this order, so that a
+      // step waits only for its own set (three later sets stay in flight). The
+      // next block's column is read at the top of the trip, a step before use.
+      for (int k = 0; k < nb; ++k) {
+        const int e_nx = blk(k + 1), ok_nx = k + 1 < nb;
+        const int c_nx = ld_const(a.col_idx + e_nx);
+        issue(3, e_cur, c_cur, 1, S3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(S0);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(0, e_nx, c_nx, ok_nx, S0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(S1);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(1, e_nx, c_nx, ok_nx, S1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(S2);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(2, e_nx, c_nx, ok_nx, S2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(S3);
+        __builtin_amdgcn_sched_barrier(0);
+        e_cur = e_nx;
+        c_cur = c_nx;
+      }
+    }
+    // D[m = row][n = feature]: row = 32 u + 8 (v / 4) + 4 (L / 32) + v % 4, feature = 32 dt + L % 32
+    const int row0 = kBlock * r;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = row0 + 32 * u + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (row >= n) continue;
+          const int64_t o = ((int64_t)h * a.vl.total_q + q0 + row) * D + 32 * dt + (lane & 31);
+          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[u][dt][v]);
+          else reinterpret_cast<float*>(a.out)[o] = acc[u][dt][v];
+        }
+    // drain the stores before the next row's loads: with stores still counted,
+    // the compiler could not size the loop's waits and would drain every step
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  }
+}
+
 // ---------------------------------------------------------------- dense source
 // grid (max_q, n_seqs, n_recv), 256 threads; dynamic LDS holds the mixed row
 // (up to kDenseWin keys at a time).
@@ -764,6 +979,41 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   {
     KernelTimer kt_("k_mapped_av_bsr", st);
     hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, n_pairs, n_hg, hpg);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st) {
+  if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
+  const int nrb = (a.max_q + 63) / 64;
+  if (!a.v_tiled) {
+    dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_v);
+    KernelTimer kt_("k_tile_v", st);
+    if (a.v_key_major)
+      hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
+                         a.vl, a.n_block_rows);
+    else
+      hipLaunchKernelGGL(k_tile_v<false>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
+                         a.vl, a.n_block_rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    KernelTimer kt_("k_idx_order", st);
+    hipLaunchKernelGGL(k_idx_order, dim3((unsigned)a.vl.n_seqs), dim3(256), 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    KernelTimer kt_("k_idx_plan", st);
+    hipLaunchKernelGGL(k_idx_plan, dim3(1), dim3(kPlanThreads), 0, st, a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_oct = (a.n_recv + 7) / 8;
+  {
+    KernelTimer kt_("k_mapped_av_idx", st);
+    hipLaunchKernelGGL(k_mapped_av_idx, dim3((unsigned)(a.plan_cap * n_oct)), dim3(512), 0, st, a, n_oct);
   }
   return hipGetLastError();
 }

@@ -232,6 +232,32 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
                   size_t workspace_bytes, void* stream);
 
 /*
+ * cma_mapped_av_indexed -- mapped attention x V with one sender per receiver head,
+ * the head map of [IAM] Methods 1 and 4 (each receiver head reuses the map of its
+ * most similar sender head):
+ *   O_h = A_{sender[s][h]} @ V_{h / g}          for every sequence s,
+ * the same result as cma_mapped_av with the one-hot M of cma_onehot_mix, without
+ * reading the other senders' maps. sender: int32 [*, n_recv] (device), sequence s
+ * uses sender + s * sender_seq_stride (0: one row for all sequences), e.g. the
+ * argmax of cma_head_map_cosine; an index outside [0, n_send) gives zero rows.
+ * Source: BSR only (output of cma_block_compress); V bf16, d = 128, any
+ * cma_v_layout (n_v_heads heads, n_v_heads >= 1 dividing n_recv); out
+ * [n_recv, total_q, 128] bf16 or f32, fp32 accumulation. n_recv <= 256,
+ * 1 <= n_send <= 256, max_seqlen_q <= 16384, n_seqs < 2^24. Each receiver head
+ * reads only its sender's kept blocks. Workspace (device, 16-byte aligned):
+ * cma_mapped_av_indexed_workspace(...) bytes, which hold the tiled copy of V
+ * (unless v_layout is TILED), the heads ordered by sender per sequence and the
+ * work-item table; n_block_rows must equal sum_s ceil(len_s / 64), as for every
+ * BSR call.
+ */
+size_t cma_mapped_av_indexed_workspace(const cma_maps_src* src, int32_t n_recv, int32_t n_v_heads, int32_t d,
+                                       int32_t n_seqs, cma_v_layout v_layout);
+int cma_mapped_av_indexed(const cma_maps_src* src, int32_t n_send, const int32_t* sender,
+                          int64_t sender_seq_stride, int32_t n_recv, int32_t n_v_heads, const void* v,
+                          cma_dtype v_dt, cma_v_layout v_layout, int32_t d, const cma_varlen* vl, void* out,
+                          cma_dtype out_dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * cma_onehot_mix -- IAM head map as a mixing matrix ([IAM] Method 4):
  * M[b][h][j] = (j == argmax[b][h]) for argmax [n_batch, n_recv] (device);
  * M [n_batch, n_recv, n_send] fp32 (device). Indices outside [0, n_send) give

@@ -211,6 +211,8 @@ def test_cfg5_serving_layer_full(cma):
     bsr = cma.block_compress(sq, sk, ss, sb, vl_p, 0.95, workspace=cma.Workspace())
     v = dev_bf16(x["v"])
     O = cma.mapped_av(bsr, Hs, Mo, Hr, v, vl_p, q_rows=int(cp[-1]), workspace=cma.Workspace())
+    # the same with the argmax as sender indices (each head reads only its sender)
+    Oi = cma.mapped_av(bsr, Hs, arg, Hr, v, vl_p, q_rows=int(cp[-1]), workspace=cma.Workspace())
     # decode rows at steps 0 and dec - 1 for the short prompts
     dec_out = {}
     for t in (0, dec - 1):
@@ -221,6 +223,8 @@ def test_cfg5_serving_layer_full(cma):
         dec_out[t] = (host64(rows), host64(od))
     torch.cuda.synchronize()
     say(f"cfg5: GPU done at {time.time() - t0:.1f}s")
+    assert arg.dtype == torch.int32 and torch.equal(Oi, O)
+    del Oi
     garg, gcos = host64(arg).astype(int), host64(cos)
     nnz = int(bsr["nnz"].item())
     row_ptr = host64(bsr["row_ptr"]).astype(np.int64)

@@ -323,6 +323,66 @@ def test_mapped_av_bsr_small(cma, n_recv, v_layout, v_heads):
     assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
 
 
+# ------------------------------------------------------------------ mapped_av, one sender per head
+# Sender indices per (sequence, receiver head) as the cosine argmax gives them:
+# O_h = A_{idx[h]} V_{h // g}. The oracle gets the one-hot M; the general path
+# with that M must give the same bits (its mix of a one-hot row is exact).
+@pytest.mark.parametrize("lens,n_recv,v_layout,v_heads,shared,out_f32", [
+    ([200, 64, 130], 64, "token", None, False, False),
+    ([130, 0, 64, 257], 13, "key", None, False, True),
+    ([200, 64, 130], 64, "tiled", 16, True, False),
+    ([64 * 9 + 5], 24, "token", 8, False, True),
+])
+def test_mapped_av_indexed_small(cma, lens, n_recv, v_layout, v_heads, shared, out_f32):
+    n_send = 28
+    n_v = v_heads or n_recv
+    say(f"mapped_av indexed lens={lens} n_send={n_send} n_recv={n_recv} v_heads={n_v} v_layout={v_layout} "
+        f"shared={shared} out_f32={out_f32}")
+    x = synth.attention_inputs(431, n_send, lens, d=128)
+    ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9)
+    S = len(lens)
+    rng = np.random.default_rng(432)
+    idx = rng.integers(0, n_send, size=(1 if shared else S, n_recv)).astype(np.int32)
+    if n_recv == 13:
+        idx[:, 3], idx[:, 7] = -1, n_send  # out of range: zero rows
+    M = np.zeros((idx.shape[0], n_recv, n_send))
+    for b in range(idx.shape[0]):
+        for h in range(n_recv):
+            if 0 <= idx[b, h] < n_send:
+                M[b, h, idx[b, h]] = 1.0
+    T = int(x["cu_q"][-1])
+    V = synth.values(433, n_v, T, 128)
+    vl = cma.Varlen(x["cu_q"], x["cu_q"])
+    src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
+               vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
+    od = torch.float32 if out_f32 else torch.bfloat16
+    if v_layout == "key":
+        vv, kw = dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))), dict(v_layout=cma.V_KEY_MAJOR)
+    elif v_layout == "tiled":
+        vv, kw = dev_bf16(tile_v(V, lens, x["cu_q"])), dict(v_layout=cma.V_TILED, k_rows=T)
+    else:
+        vv, kw = dev_bf16(V), {}
+    O = cma.mapped_av(src, n_send, dev_i32(idx), n_recv, vv, vl, out_dtype=od, v_heads=v_heads, **kw)
+    Og = cma.mapped_av(src, n_send, dev_f32(M), n_recv, vv, vl, out_dtype=od, v_heads=v_heads, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Og)
+    got = host64(O)
+    rows = [(s_, r) for s_ in range(S) for r in range((lens[s_] + 63) // 64)]
+    Vr = np.repeat(f64(V), n_recv // n_v, axis=0)
+    oo = oracle.mapped_av_bsr_rows(ref["row_ptr"], ref["col_idx"], ref["vals"], n_send, lens, M, Vr,
+                                   x["cu_q"], rows)
+    refO = np.zeros_like(got)
+    for (s_, r), o in oo.items():
+        a = x["cu_q"][s_] + 64 * r
+        refO[:, a: a + o.shape[1]] = o
+    if out_f32:
+        assert rel_l2(got, refO) <= 1e-5
+    else:
+        assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
+    if n_recv == 13:
+        assert not got[[3, 7]].any()
+
+
 def test_mapped_av_two_receivers_stacked(cma):
     """Two receivers served from one sender state: their heads stacked in one call
     (M rows and V heads concatenated, each with its own grouped V) give exactly the

@@ -147,6 +147,22 @@ def test_block_compress_layout_varlen():
             assert np.array_equal(out["row_stats"][h, cu[s]:cu[s + 1], 0], single["m"])
 
 
+def test_block_compress_empty_sequence():
+    """A zero-length sequence in the batch has no block-rows: the block-sparse
+    output equals that of the batch without it."""
+    r = np.random.default_rng(11)
+    lens = [70, 0, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = r.standard_normal((2, cu[-1], 8))
+    k = r.standard_normal((2, cu[-1], 8))
+    scale, bias = np.array([0.9, 1.2]), np.array([4.0, 0.0])
+    a = oracle.block_compress(q, k, scale, bias, cu, 0.8)
+    b = oracle.block_compress(q, k, scale, bias, np.array([0, 70, 75]), 0.8)
+    assert a["r_tot"] == b["r_tot"] == 3
+    for key in ("row_ptr", "col_idx", "vals", "masses", "row_stats"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 @pytest.mark.parametrize("n,tau", [(200, 0.9), (256, 0.95), (130, 1.0)])
 def test_block_row_matches_whole_head(n, tau):
     """The per-block-row oracle (used for sampled checks of long sequences) gives
