@@ -93,9 +93,10 @@ def row_stats(q, k, scale, bias):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     n = q.shape[0]
+    if n == 0:  # an empty sequence has no rows
+        return np.zeros(0), np.zeros(0)
     s = float(scale) * (q @ k.T)
-    if n:
-        s[:, 0] += float(bias)
+    s[:, 0] += float(bias)
     vis = np.tril(np.ones((n, n), dtype=bool))
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)
