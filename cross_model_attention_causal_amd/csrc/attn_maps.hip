@@ -332,6 +332,11 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
   }
   barrier_lds();
 
+  // offset of the current unit's sequence in the map layout, recomputed only when
+  // the unit changes (a unit's block-rows are consecutive items)
+  int off_u = -1;
+  int64_t off_seq = 0;
+
   // one item; returns whether another follows
   auto item = [&](const QOperand<D>& qop, QOperand<D>& qnext, const u32x4* kcur, u32x4* knext) {
     const int u = u0, r = r0;
@@ -424,7 +429,11 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
     barrier_lds();
 
     // normalise and write blocks kp and kp + 4 (zeros past the diagonal of a dense row)
-    const int64_t base0 = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, PACKED);
+    if (u != off_u) {
+      off_seq = map_seq_off(a.vl, s, PACKED);
+      off_u = u;
+    }
+    const int64_t base0 = (int64_t)h * a.head_stride + off_seq;
     uint16_t* region = reinterpret_cast<uint16_t*>(a.maps) + base0;  // this (head, sequence) map
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(region, (short)0, (int)(2 * map_elems(nq, nk, PACKED)), kBufferFlags);

@@ -151,9 +151,35 @@ __device__ __forceinline__ int64_t map_row_off(int64_t i, int64_t nq, int64_t nk
   return packed ? i * (nk - nq) + i * (i + 1) / 2 : i * nk;
 }
 // Offset of sequence s's map inside a head's map area (sum over earlier sequences).
+// The per-sequence sums below read the sequence table 16 entries at a time, all
+// loads of a group issued before the first use (one uniform branch per group for
+// the used-length arrays), so that a batch of many sequences costs a few scalar
+// round trips rather than one per sequence.
+constexpr int kSeqGroup = 16;
+// lengths of sequences t .. t + 15 from the used lengths, else the cu differences
+__device__ __forceinline__ void seq_lens16(const int32_t* used, const int32_t* cu, int t, int32_t (&n)[kSeqGroup]) {
+  if (used) {
+#pragma unroll
+    for (int e = 0; e < kSeqGroup; ++e) n[e] = ld_const(used + t + e);
+  } else {
+    int32_t c[kSeqGroup + 1];
+#pragma unroll
+    for (int e = 0; e <= kSeqGroup; ++e) c[e] = ld_const(cu + t + e);
+#pragma unroll
+    for (int e = 0; e < kSeqGroup; ++e) n[e] = c[e + 1] - c[e];
+  }
+}
 __device__ __forceinline__ int64_t map_seq_off(const Varlen& v, int s, bool packed) {
   int64_t off = 0;
-  for (int t = 0; t < s; ++t) off += map_elems(seq_len_q(v, t), seq_len_k(v, t), packed);
+  int t = 0;
+  for (; t + kSeqGroup <= s; t += kSeqGroup) {
+    int32_t nq[kSeqGroup], nk[kSeqGroup];
+    seq_lens16(v.used_q, v.cu_q, t, nq);
+    seq_lens16(v.used_k, v.cu_k, t, nk);
+#pragma unroll
+    for (int e = 0; e < kSeqGroup; ++e) off += map_elems(nq[e], nk[e], packed);
+  }
+  for (; t < s; ++t) off += map_elems(seq_len_q(v, t), seq_len_k(v, t), packed);
   return off;
 }
 // Block-rows of earlier sequences, and packed lower-triangular block counts of
@@ -161,7 +187,18 @@ __device__ __forceinline__ int64_t map_seq_off(const Varlen& v, int s, bool pack
 __device__ __forceinline__ void block_offsets(const Varlen& v, int s, int32_t& roff, int64_t& tri_off) {
   int32_t r = 0;
   int64_t t = 0;
-  for (int u = 0; u < s; ++u) {
+  int u = 0;
+  for (; u + kSeqGroup <= s; u += kSeqGroup) {
+    int32_t nq[kSeqGroup];
+    seq_lens16(v.used_q, v.cu_q, u, nq);
+#pragma unroll
+    for (int e = 0; e < kSeqGroup; ++e) {
+      const int32_t R = (nq[e] + kBlock - 1) / kBlock;
+      r += R;
+      t += (int64_t)R * (R + 1) / 2;
+    }
+  }
+  for (; u < s; ++u) {
     int32_t R = (seq_len_q(v, u) + kBlock - 1) / kBlock;
     r += R;
     t += (int64_t)R * (R + 1) / 2;
