@@ -236,7 +236,9 @@ def stage_figures(reps=5):
     maps_bytes = P * (Hs + Hr) * (2 * tt * 128 * 2 + L * 2) / 2
     idx_bytes = used_blocks * 8192 + 2 * Hr * tokens * 128 * 2 + (Hs * r_tot + 1 + nnz) * 4
     k_pre = timed(prefill, {"k_attn_maps_short": ("hbm", maps_bytes),
-                            "k_gram_bf16": ("mfma", 2 * Hr * Hs * L * P),
+                            # 68 small problems (64 x 28): ~20 flop per byte, far below
+                            # the ridge, so the maps' bytes bound the Gram here
+                            "k_gram_bf16": ("hbm", P * (Hr + Hs) * L * 2),
                             "k_block_stats": ("mfma", Hs * tri * 128 * 2),
                             "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2),
                             "k_mapped_av_idx": ("hbm", idx_bytes),
