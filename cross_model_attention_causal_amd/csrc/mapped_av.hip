@@ -812,15 +812,17 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
   if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
   const int tid = threadIdx.x;
   const float* Ms = a.M + (int64_t)s * a.M_stride + (int64_t)h * a.n_send;
-  if (tid == 0) {
-    int k = 0;
-    for (int j = 0; j < a.n_send; ++j)
-      if (Ms[j] != 0.0f) {
-        nzi[k] = j;
-        nzw[k] = Ms[j];
-        ++k;
-      }
-    nnzm = k;
+  // the nonzero mixing weights of this head in ascending sender order (n_send <= 64:
+  // one wave loads them together and compacts them with a ballot)
+  if (tid < 64) {
+    const float w = tid < a.n_send ? Ms[tid] : 0.0f;
+    const uint64_t nz = __ballot(w != 0.0f);
+    if (w != 0.0f) {
+      const int k = __popcll(nz & ((1ull << tid) - 1ull));
+      nzi[k] = tid;
+      nzw[k] = w;
+    }
+    if (tid == 0) nnzm = __popcll(nz);
   }
   __syncthreads();
   const int last = nk - nq + i;
