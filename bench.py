@@ -329,21 +329,25 @@ def main():
                    nnz=torch.empty(1, dtype=torch.int32, device=dev), capacity=cap)
     ws_c, ws_v = cma.Workspace(), cma.Workspace()
     O = torch.empty((Hr, P * n, 128), dtype=torch.bfloat16, device=dev)
+    vt = torch.empty((Hr, vl_pref.n_block_rows, 64 * 128), dtype=torch.bfloat16, device=dev)
     rows = torch.empty((Hs, vl_dec.maps_elems(cma.DENSE)), dtype=torch.float32, device=dev)
     od = torch.empty((Hr, P, 128), dtype=torch.bfloat16, device=dev)
     state = {}
 
-    # The head mapping and the decode row (steps 1-3 and 6) do not depend on the
-    # compression and the fused pass (steps 4-5): they run on a second stream of
-    # the same (default) priority beside them. Each step starts both streams
-    # together and ends when both are done.
+    # The head mapping and the decode row (steps 1-3 and 6) and the tiling of V do
+    # not depend on the compression (step 4): they run on a second stream of the
+    # same (default) priority beside it; the fused pass (step 5) waits for the
+    # tiled V. Each step starts both streams together and ends when both are done.
     side = torch.cuda.Stream()
+    v_ready = torch.cuda.Event()
 
     def step():
         main = torch.cuda.current_stream()
         side.wait_stream(main)
         layers = cma.mapped_layers(80, 0.5)                                  # host: layer order
         with torch.cuda.stream(side):
+            cma.tile_v(v, vl_pref, vl_pref.n_block_rows, out=vt)                 # 5a
+            v_ready.record(side)
             cma.attn_maps(send_q, send_k, s_scale, s_bias, vl_map_s, out=sm)     # 1
             cma.attn_maps(recv_q, recv_k, r_scale, r_bias, vl_map_r, out=rm)
             cos, arg, mar = cma.head_map_cosine(rm, sm, P, Hr, Hs, L, P * L, L, P * L, L)  # 2
@@ -353,8 +357,9 @@ def main():
             cma.mapped_av(("dense", rows, cma.DENSE), Hs, Mdec, Hr, v, vl_dec, out=od, q_rows=P)
         bsr = cma.block_compress(send_q, send_k, s_scale, s_bias, vl_pref, args.tau,
                                  workspace=ws_c, bsr=bsr_buf)                 # 4
-        cma.mapped_av(bsr, Hs, M, Hr, v, vl_pref, out=O, q_rows=P * n,
-                      workspace=ws_v)                                         # 5
+        main.wait_event(v_ready)
+        cma.mapped_av(bsr, Hs, M, Hr, vt, vl_pref, out=O, q_rows=P * n, v_layout=cma.V_TILED,
+                      k_rows=v.shape[1], workspace=ws_v)                      # 5
         main.wait_stream(side)
         state.update(arg=arg, mar=mar, bsr=bsr, layers=layers)
 

@@ -30,7 +30,7 @@ EXPORTS = [
     "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
     "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks",
     "cma_block_compress_workspace", "cma_block_compress", "cma_mapped_av_workspace",
-    "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
+    "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_tile_v", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
     "cma_timing_collect", "cma_timing_get", "cma_timing_name", "cma_timing_reset",
 ]
 
@@ -89,6 +89,7 @@ def load_library(path: str = LIB_PATH):
         "cma_mapped_av_indexed_workspace": (SZ, [P, I32, I32, I32, I32, ctypes.c_int]),
         "cma_mapped_av_indexed": (ctypes.c_int, [P, I32, P, I64, I32, I32, P, ctypes.c_int, ctypes.c_int, I32,
                                                  P, P, ctypes.c_int, P, SZ, P]),
+        "cma_tile_v": (ctypes.c_int, [P, ctypes.c_int, I32, I32, P, I32, P, P]),
         "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
         "cma_mapping_plan": (ctypes.c_int, [I32, P, I32, I32, P, P]),
@@ -397,6 +398,26 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
                              _dev_ptr(out, "out"), _dt(out),
                              ws.data_ptr() if ws is not None else None,
                              ws.numel() if ws is not None else 0, _stream()))
+    return out
+
+
+def tile_v(v, vl: Varlen, n_block_rows, v_layout=V_TOKEN_MAJOR, out=None):
+    """V ([H, Tk, 128] token-major or [H, 128, Tk] key-major, bf16) in the tiled
+    operand order [H, n_block_rows, 64 * 128] that ``mapped_av`` takes with
+    ``v_layout=V_TILED`` (then also pass ``k_rows`` = Tk)."""
+    torch = _torch()
+    lib = load_library()
+    if v_layout == V_KEY_MAJOR:
+        H, d, Tk = v.shape
+    else:
+        H, Tk, d = v.shape
+    if out is None:
+        out = torch.empty((H, n_block_rows, BLOCK * d), dtype=v.dtype, device=v.device)
+    _need(out, "out", H * n_block_rows * BLOCK * d)
+    _check_rows(vl, Tk, Tk)
+    cvl = vl.c(Tk, Tk)
+    _check(lib.cma_tile_v(_dev_ptr(v, "v"), v_layout, H, d, ctypes.byref(cvl), n_block_rows,
+                          _dev_ptr(out, "out"), _stream()))
     return out
 
 

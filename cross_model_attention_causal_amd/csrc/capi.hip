@@ -433,6 +433,33 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   return hip_status(launch_mapped_av_bsr(a, st), "mapped_av (block-sparse) launch");
 }
 
+int cma_tile_v(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
+               int32_t n_block_rows, void* vt, void* stream) {
+  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR)
+    return fail(CMA_EINVAL, "tile_v reads token-major or key-major V");
+  if (int e = check_varlen(vl, true)) return e;
+  if (n_v_heads < 0 || n_block_rows < 0) return fail(CMA_EINVAL, "negative size");
+  if (d != 128) return fail(CMA_EUNSUPPORTED, "tile_v supports d = 128");
+  if (n_v_heads == 0 || vl->n_seqs == 0 || vl->max_seqlen_q == 0) return CMA_OK;
+  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
+    return fail(CMA_EUNSUPPORTED, "tile_v supports sequences up to %d tokens", kMaxBlockRows * kBlock);
+  if (n_block_rows == 0) return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
+  if (!v || !vt) return fail(CMA_EINVAL, "NULL v or vt");
+  if (!aligned16(vt) || (v_layout == CMA_V_TOKEN_MAJOR && !aligned16(v)))
+    return fail(CMA_EINVAL, "v (token-major) and vt must be 16-byte aligned");
+  MappedAvArgs a{};
+  a.n_v = n_v_heads;
+  a.d = d;
+  a.v = v;
+  a.v_bf16 = true;
+  a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
+  a.vl = to_varlen(vl);
+  a.vt = static_cast<uint16_t*>(vt);
+  a.n_block_rows = n_block_rows;
+  a.max_q = vl->max_seqlen_q;
+  return hip_status(launch_tile_v(a, static_cast<hipStream_t>(stream)), "tile_v launch");
+}
+
 // Workspace of the indexed path: [tiled V (unless V is tiled)][roff][order][pairs],
 // each part on a 256-byte boundary. The pair table holds at most
 // sum_s ceil(R_s / 2) <= (n_block_rows + n_seqs) / 2 items.

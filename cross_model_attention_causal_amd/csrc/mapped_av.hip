@@ -957,19 +957,25 @@ hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_tile_v(const MappedAvArgs& a, hipStream_t st) {
+  if (a.n_v == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
+  const int nrb = (a.max_q + 63) / 64;
+  dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_v);  // each V head once
+  KernelTimer kt_("k_tile_v", st);
+  if (a.v_key_major)
+    hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl,
+                       a.n_block_rows);
+  else
+    hipLaunchKernelGGL(k_tile_v<false>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl,
+                       a.n_block_rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
   const int nrb = (a.max_q + 63) / 64;
   if (!a.v_tiled) {
-    dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_v);  // each V head once
-    KernelTimer kt_("k_tile_v", st);
-    if (a.v_key_major)
-      hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
-                         a.vl, a.n_block_rows);
-    else
-      hipLaunchKernelGGL(k_tile_v<false>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
-                         a.vl, a.n_block_rows);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_tile_v(a, st);
     if (e != hipSuccess) return e;
   }
   const int n_hg = (a.n_recv + kHeadsPerWg - 1) / kHeadsPerWg;
@@ -987,17 +993,8 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
 
 hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
-  const int nrb = (a.max_q + 63) / 64;
   if (!a.v_tiled) {
-    dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_v);
-    KernelTimer kt_("k_tile_v", st);
-    if (a.v_key_major)
-      hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
-                         a.vl, a.n_block_rows);
-    else
-      hipLaunchKernelGGL(k_tile_v<false>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt,
-                         a.vl, a.n_block_rows);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_tile_v(a, st);
     if (e != hipSuccess) return e;
   }
   {

@@ -189,6 +189,18 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
  * layouts in its workspace. */
 typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1, CMA_V_TILED = 2 } cma_v_layout;
 
+/*
+ * cma_tile_v -- V in the TILED layout (see cma_v_layout) from TOKEN_MAJOR or
+ * KEY_MAJOR V, bf16, d = 128: what cma_mapped_av does in its workspace, as a call of
+ * its own, so that a caller can tile V once (e.g. on another stream, or for several
+ * calls) and pass CMA_V_TILED. v: n_v_heads heads; vt [n_v_heads, n_block_rows,
+ * 64 * 128] bf16 (device, 16-byte aligned), every block of every sequence written
+ * (zeros past the sequence's end); n_block_rows = sum_s ceil(len_s / 64) as for the block-sparse maps.
+ * The varlen's used query lengths are the sequence lengths (square sequences).
+ */
+int cma_tile_v(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
+               int32_t n_block_rows, void* vt, void* stream);
+
 /* Where cma_mapped_av reads the sender maps from. */
 typedef enum { CMA_SRC_DENSE = 0, CMA_SRC_BSR = 1 } cma_src_kind;
 typedef struct {

@@ -383,6 +383,37 @@ def test_mapped_av_indexed_small(cma, lens, n_recv, v_layout, v_heads, shared, o
         assert not got[[3, 7]].any()
 
 
+@pytest.mark.parametrize("key_major", [False, True])
+def test_tile_v(cma, key_major):
+    """cma.tile_v writes the documented tiled layout (bit for bit, zeros past each
+    sequence's end), and the fused pass on the tiled copy equals the one that tiles
+    V itself."""
+    lens = [200, 64, 130, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, R = int(cu[-1]), sum((n + 63) // 64 for n in lens)
+    say(f"tile_v lens={lens} key_major={key_major}")
+    V = synth.values(441, 6, T, 128)
+    vl = cma.Varlen(cu, cu)
+    if key_major:
+        vv, lay = dev_bf16(np.ascontiguousarray(V.transpose(0, 2, 1))), cma.V_KEY_MAJOR
+    else:
+        vv, lay = dev_bf16(V), cma.V_TOKEN_MAJOR
+    got = cma.tile_v(vv, vl, R, v_layout=lay)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(got), f64(tile_v(V, lens, cu)))
+    # the fused pass: tiled by the caller vs tiled inside the call
+    n_send = 8
+    x = synth.attention_inputs(442, n_send, lens, d=128)
+    ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9)
+    src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
+               vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
+    M = dev_f32(synth.mix_matrix_learned(443, 6, n_send))
+    O1 = cma.mapped_av(src, n_send, M, 6, vv, vl, v_layout=lay)
+    O2 = cma.mapped_av(src, n_send, M, 6, got, vl, v_layout=cma.V_TILED, k_rows=T)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+
+
 def test_mapped_av_two_receivers_stacked(cma):
     """Two receivers served from one sender state: their heads stacked in one call
     (M rows and V heads concatenated, each with its own grouped V) give exactly the
