@@ -389,7 +389,7 @@ def main():
     causal_blocks = P * (n // 64) * (n // 64 + 1) // 2
     kept_frac = nnz / (Hs * causal_blocks)
 
-    # algorithmic work per launch (the design doc gives the derivations)
+    # algorithmic work per launch: work per unit (bytes or flops) times the units of one launch
     def per_launch(name):
         ms, cnt = kt.get(name, (0.0, 0))
         return (ms / cnt if cnt else float("nan")), cnt
