@@ -172,3 +172,56 @@ def test_binding_rejects_undersized_tensors():
     with pytest.raises(ValueError):  # V with fewer heads than receivers
         cma.mapped_av(("dense", torch.zeros(4, 2080), cma.PACKED), 4, torch.zeros(1, 3, 4), 3,
                       torch.zeros(2, 64, 128), VL())
+
+
+def test_indexed_workspace_and_validation(lib):
+    """cma_mapped_av_indexed: the workspace size follows its layout (tiled V, then
+    the per-sequence block-row offsets, the head order and the pair table, each
+    on a 256-byte boundary), and bad arguments are rejected before any device
+    work (the pointers below are never dereferenced)."""
+    from cross_model_attention_causal_amd import _CMapsSrc, _CVarlen, SRC_BSR, SRC_DENSE, V_TILED, V_TOKEN_MAJOR
+    P, I32, I64, SZ, INT = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+    lib.cma_last_error.restype = ctypes.c_char_p
+    ws = lib.cma_mapped_av_indexed_workspace
+    ws.restype, ws.argtypes = SZ, [P, I32, I32, I32, I32, INT]
+    r256 = lambda x: (x + 255) // 256 * 256
+    src = _CMapsSrc()
+    src.kind, src.n_block_rows = SRC_BSR, 37
+    for layout in (V_TOKEN_MAJOR, V_TILED):
+        n_recv, n_v, n_seqs = 64, 16, 5
+        vt = 0 if layout == V_TILED else r256(n_v * 37 * 64 * 128 * 2)
+        want = vt + r256(4 * n_seqs) + r256(4 * n_seqs * n_recv) + r256(4 * ((37 + n_seqs) // 2 + 1))
+        assert ws(ctypes.byref(src), n_recv, n_v, 128, n_seqs, layout) == want
+    dense = _CMapsSrc()
+    dense.kind = SRC_DENSE
+    assert ws(ctypes.byref(dense), 64, 16, 128, 5, V_TOKEN_MAJOR) == 0
+
+    call = lib.cma_mapped_av_indexed
+    call.argtypes = [P, I32, P, I64, I32, I32, P, INT, INT, I32, P, P, INT, P, SZ, P]
+    fake = 0x1000
+    src.row_ptr = src.col_idx = src.vals = fake
+    vl = _CVarlen()
+    vl.n_seqs, vl.cu_seqlens_q, vl.cu_seqlens_k = 2, fake, fake
+    vl.max_seqlen_q = vl.max_seqlen_k = 128
+    vl.total_q = vl.total_k = 256
+
+    def run(s=src, n_send=8, n_recv=16, n_v=16, v_dt=1, d=128, ws_bytes=1 << 30):
+        return call(ctypes.byref(s) if s is not None else None, n_send, fake, 0, n_recv, n_v, fake, v_dt,
+                    V_TOKEN_MAJOR, d, ctypes.byref(vl), fake, 1, fake, ws_bytes, None)
+
+    assert run(s=None) == -1                  # no source
+    assert run(s=dense) == -2                 # dense maps have no indexed form
+    assert run(n_v=5) == -1                   # V heads must divide receiver heads
+    assert run(v_dt=0) == -2                  # fp32 V
+    assert run(d=64) == -2
+    assert run(n_recv=300, n_v=300) == -2     # more receiver heads than the head sort holds
+    assert run(n_send=0) == -2
+    assert run(ws_bytes=64) == -3             # workspace too small
+    assert lib.cma_last_error()
+
+    tile = lib.cma_tile_v
+    tile.argtypes = [P, INT, I32, I32, P, I32, P, P]
+    assert tile(fake, V_TILED, 4, 128, ctypes.byref(vl), 4, fake, None) == -1   # input must be untiled
+    assert tile(fake, V_TOKEN_MAJOR, 4, 64, ctypes.byref(vl), 4, fake, None) == -2
+    assert tile(fake, V_TOKEN_MAJOR, 4, 128, ctypes.byref(vl), 4, None, None) == -1
+    assert tile(fake, V_TOKEN_MAJOR, 4, 128, ctypes.byref(vl), 0, fake, None) == -1
