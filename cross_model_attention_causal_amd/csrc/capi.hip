@@ -391,6 +391,7 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   a.out = out;
   a.out_bf16 = out_dt == CMA_BF16;
   a.max_q = vl->max_seqlen_q;
+  a.max_k = vl->max_seqlen_k;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (src->kind == CMA_SRC_DENSE) {
     if (!src->maps) return fail(CMA_EINVAL, "NULL maps");

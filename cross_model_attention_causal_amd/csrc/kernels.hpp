@@ -101,7 +101,7 @@ struct MappedAvArgs {
   void* out;
   bool out_bf16;
   uint16_t* vt;  // bsr path: tiled V [n_v][n_block_rows][64 * d] (v itself or the workspace)
-  int32_t max_q;
+  int32_t max_q, max_k;  // longest query / key sequence (host maxima)
   // indexed path (one sender per receiver head): sender[s * sender_stride + h]
   const int32_t* sender;
   int64_t sender_stride;

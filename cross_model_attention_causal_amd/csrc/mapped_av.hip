@@ -769,8 +769,8 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
 }
 
 // ---------------------------------------------------------------- dense source
-// grid (max_q, n_seqs, n_recv), 256 threads; dynamic LDS holds the mixed row
-// (up to kDenseWin keys at a time).
+// grid (max_q, n_seqs, n_recv); dynamic LDS holds the mixed row, `win` keys at a
+// time (the longest key sequence, at most kDenseWin).
 constexpr int kDenseWin = 8192;
 
 // 8 consecutive V values starting at element index i as floats; entries at or
@@ -797,12 +797,12 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, int64_t lim, float
   }
 }
 
-// NT threads: 1024 for token-major V (64 key rows in flight per pass, 8 passes
-// unrolled, so a single row streams V with enough loads outstanding), 256 for
-// key-major V.
+// NT threads: 512 for token-major V (32 key rows per pass, 8 passes unrolled, so a
+// single row streams V with 128 KB of loads outstanding, and with a short window
+// four workgroups share a CU), 256 for key-major V.
 template <int D, bool KEY_MAJOR, typename VT, int NT>
-__global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
-  extern __shared__ float bj[];  // mixed row window [kDenseWin]
+__global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win) {
+  extern __shared__ float bj[];  // mixed row window [win]
   __shared__ int nzi[64];
   __shared__ float nzw[64];
   __shared__ int nnzm;
@@ -834,8 +834,8 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a) {
   float acck[D / 16];
 #pragma unroll
   for (int u = 0; u < D / 16; ++u) acck[u] = 0.0f;
-  for (int w0 = 0; w0 <= last; w0 += kDenseWin) {
-    const int wlen = min(kDenseWin, last + 1 - w0);
+  for (int w0 = 0; w0 <= last; w0 += win) {
+    const int wlen = min(win, last + 1 - w0);
     for (int j0 = tid; j0 < wlen; j0 += 4 * NT) {
       // four window positions per thread at a time (independent loads)
       float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -933,14 +933,17 @@ __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, fl
 
 template <int D, bool KM>
 static void dense_launch(const MappedAvArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int NT = KM ? 256 : 1024;
-  const size_t lds = kDenseWin * sizeof(float);
+  constexpr int NT = KM ? 256 : 512;
+  // the mixed-row window: the longest key sequence (in 64s), at most kDenseWin keys,
+  // so that short contexts leave LDS for more workgroups per CU
+  const int win = (int)std::min<int64_t>(kDenseWin, std::max<int64_t>(64, ((int64_t)a.max_k + 63) / 64 * 64));
+  const size_t lds = (size_t)win * sizeof(float);
   if (a.v_bf16) {
     KernelTimer kt_("k_mapped_av_dense", st);
-    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a);
+    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a, win);
   } else {
     KernelTimer kt_("k_mapped_av_dense", st);
-    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a);
+    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a, win);
   }
 }
 
