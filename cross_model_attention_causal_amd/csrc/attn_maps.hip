@@ -685,7 +685,7 @@ static void maps_launch(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
 }
 
 // Compute units of the current device (one persistent workgroup each).
-static int cu_count() {
+int cu_count() {
   static int cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -114,6 +114,7 @@ hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_tile_v(const MappedAvArgs& a, hipStream_t st);  // v -> vt (bf16, d = 128)
+int cu_count();  // compute units of the current device (cached per device)
 hipError_t launch_onehot(const int32_t* argmax, int32_t n_batch, int32_t n_recv, int32_t n_send,
                          float* M, hipStream_t st);
 

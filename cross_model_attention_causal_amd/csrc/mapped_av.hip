@@ -797,9 +797,9 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, int64_t lim, float
   }
 }
 
-// NT threads: 512 for token-major V (32 key rows per pass, 8 passes unrolled, so a
-// single row streams V with 128 KB of loads outstanding, and with a short window
-// four workgroups share a CU), 256 for key-major V.
+// NT threads, token-major V: 512 (32 key rows per pass, 8 passes unrolled: a row
+// streams V with 128 KB of loads outstanding, and two workgroups share a CU) or,
+// for launches of few rows, 1024 (64 key rows per pass); key-major V: 256.
 template <int D, bool KEY_MAJOR, typename VT, int NT>
 __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win) {
   extern __shared__ float bj[];  // mixed row window [win]
@@ -933,18 +933,25 @@ __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, fl
 
 template <int D, bool KM>
 static void dense_launch(const MappedAvArgs& a, dim3 grid, hipStream_t st) {
-  constexpr int NT = KM ? 256 : 512;
   // the mixed-row window: the longest key sequence (in 64s), at most kDenseWin keys,
   // so that short contexts leave LDS for more workgroups per CU
   const int win = (int)std::min<int64_t>(kDenseWin, std::max<int64_t>(64, ((int64_t)a.max_k + 63) / 64 * 64));
   const size_t lds = (size_t)win * sizeof(float);
-  if (a.v_bf16) {
-    KernelTimer kt_("k_mapped_av_dense", st);
-    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a, win);
-  } else {
-    KernelTimer kt_("k_mapped_av_dense", st);
-    hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a, win);
+  // token-major V: with few rows (a long-context decode of a small batch) 1024
+  // threads keep more loads in flight per row; with many rows 512 threads let two
+  // workgroups share a CU
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  KernelTimer kt_("k_mapped_av_dense", st);
+  if constexpr (!KM) {
+    if (wgs < 2 * (int64_t)cu_count()) {
+      if (a.v_bf16) hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, 1024>), grid, dim3(1024), lds, st, a, win);
+      else hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, 1024>), grid, dim3(1024), lds, st, a, win);
+      return;
+    }
   }
+  constexpr int NT = KM ? 256 : 512;
+  if (a.v_bf16) hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a, win);
+  else hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a, win);
 }
 
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
