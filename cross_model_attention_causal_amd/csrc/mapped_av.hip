@@ -383,8 +383,9 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   //                            (tiles 2 (wave % 2), + 1)
   //   NI = 4 (up to 8 heads):  sA = wave (all four tiles)
   //   NI = 2 (up to 4 heads):  sA = wave / 2 (tiles 2 (wave % 2), + 1)
-  // Slots past the group's heads compute on the last head's V and are not
-  // stored, so that every wave runs the same branch-free schedule.
+  // Slots past the group's heads run the same branch-free schedule on a V
+  // descriptor of no bytes (their loads return zeros without a memory access)
+  // and are not stored.
   auto run = [&](auto ni) __attribute__((always_inline)) {
     constexpr int NI = decltype(ni)::value;
     constexpr int NA = NI == 2 ? 2 : 4;
@@ -397,11 +398,11 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     const __amdgpu_buffer_rsrc_t vA = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.vt + ((int64_t)((h_lo + min(sA, heads_here - 1)) / a.v_group) * a.n_block_rows + roff) *
                                          (kBlock * D)),
-        (short)0, v_bytes, kBufferFlags);
+        (short)0, sA < heads_here ? v_bytes : 0, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vB = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.vt + ((int64_t)((h_lo + min(sB, heads_here - 1)) / a.v_group) * a.n_block_rows + roff) *
                                          (kBlock * D)),
-        (short)0, v_bytes, kBufferFlags);
+        (short)0, sB < heads_here ? v_bytes : 0, kBufferFlags);
     // mixed-map operands of slots sA and sB: lane (row n32, half q2) holds keys
     // 8 q2 .. + 7, one contiguous 1 KB read each
     const uint32_t oA_lane = 2u * (sA * kBH + n32 * kKeysPerStep + 8 * q2);
