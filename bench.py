@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the check of the last step's outputs (sampled fused-pass rows, the decode "
+                         "rows and prompt 0's head map) against the oracle")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--stage-figures", action="store_true",
                     help="instead of the step: time each stage at its own workload (512-token head "
@@ -361,7 +364,7 @@ def main():
         cma.mapped_av(bsr, Hs, M, Hr, vt, vl_pref, out=O, q_rows=P * n, v_layout=cma.V_TILED,
                       k_rows=v.shape[1], workspace=ws_v)                      # 5
         main.wait_stream(side)
-        state.update(arg=arg, mar=mar, bsr=bsr, layers=layers)
+        state.update(arg=arg, mar=mar, cos=cos, bsr=bsr, layers=layers)
 
     for _ in range(args.warmup):
         step()
@@ -478,10 +481,92 @@ def main():
         "wall_s_timed_region": round(wall, 3),
     }
 
+    check_ok = True
+    if not args.no_check:
+        result["check"] = check_outputs(x, state, O, od, P, n, args.tau)
+        check_ok = result["check"]["ok"]
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, P, n, tokens, args.tau)
 
     print(json.dumps(result), flush=True)
+    if not check_ok:
+        sys.exit(1)
+
+
+def check_outputs(x, state, O, od, P, n, tau):
+    """The last timed step's own outputs against the oracle, on a sample: prompt 0's
+    cosine head map (argmax equal wherever the oracle's margin exceeds 1e-4, cosines
+    at 1e-5), every prompt's decode row through the one-hot mapped x V (bf16, 1e-2),
+    and four block-rows of the fused pass (prompts 0 and P-1): every sender whose
+    oracle selection margin exceeds 1e-4 keeps exactly the oracle's columns, and O
+    equals the oracle's product over the kept columns (bf16, relative L2 1e-2)."""
+    import oracle
+
+    t0 = time.perf_counter()
+    f64 = lambda b: (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+    rel = lambda a, b: float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
+    Hs, Hr, tau_t, slot = x["n_send"], x["n_recv"], x["tau_t"], x["slot"]
+    arg = state["arg"].cpu().numpy().astype(np.int64)
+    cos_g = state["cos"].cpu().numpy().astype(np.float64) if state.get("cos") is not None else None
+    out = dict(ok=True)
+    # head map of prompt 0
+    S = np.stack([oracle.round_bf16(oracle.pack_rows(oracle.causal_map(
+        f64(x["send_q"][j, :tau_t]), f64(x["send_k"][j, :tau_t]), x["send_scale"][j], x["send_bias"][j])))
+        for j in range(Hs)])
+    R = np.stack([oracle.round_bf16(oracle.pack_rows(oracle.causal_map(
+        f64(x["recv_q"][h, :tau_t]), f64(x["recv_k"][h, :tau_t]), x["recv_scale"][h], x["recv_bias"][h])))
+        for h in range(Hr)])
+    ocos, oarg, omar = oracle.head_map(R, S)
+    big = omar > 1e-4
+    out["head_map_decided"] = int(big.sum())
+    out["head_map_ok"] = bool(np.array_equal(arg[0][big], oarg[big]) and
+                              (cos_g is None or rel(cos_g[0], ocos) <= 1e-5))
+    # decode rows: oracle rows over n + 1 keys, one-hot by the library's argmax
+    odg = od.float().cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for p in range(P):
+        ks = slice(p * slot, p * slot + n + 1)
+        A = np.stack([oracle.causal_map(f64(x["dec_q"][j, p][None, :]), f64(x["send_k"][j, ks]),
+                                        x["send_scale"][j], x["send_bias"][j])[0] for j in range(Hs)])
+        ref = np.stack([A[arg[p, h]] @ f64(x["v"][h, ks]) for h in range(Hr)])
+        worst = max(worst, rel(odg[:, p], oracle.round_bf16(ref)))
+    out["decode_rel_l2"] = round(worst, 6)
+    # fused pass: sampled block-rows, reference on the library's kept columns
+    bsr = state["bsr"]
+    nnz = int(bsr["nnz"].item())
+    row_ptr = bsr["row_ptr"].cpu().numpy().astype(np.int64)
+    col = bsr["col_idx"][:nnz].cpu().numpy().astype(np.int64)
+    Rb = n // 64
+    r_tot = P * Rb
+    M = x["M"][0].astype(np.float64)
+    worst_o, decided, sel_ok = 0.0, 0, True
+    for p, r in sorted({(0, 0), (0, min(64, Rb - 1)), (0, Rb - 1), (P - 1, Rb // 2)}):
+        qs, ks = slice(p * n, p * n + n), slice(p * slot, p * slot + n)
+        mixed = np.zeros((Hr, 64, 64 * (r + 1)))
+        for j in range(Hs):
+            ref = oracle.compress_block_row(f64(x["send_q"][j, qs]), f64(x["send_k"][j, ks]), x["send_scale"][j],
+                                            x["send_bias"][j], r, tau)
+            g = j * r_tot + p * Rb + r
+            kept = [int(c) for c in col[row_ptr[g]: row_ptr[g + 1]]]
+            if ref["margin"] > 1e-4:
+                decided += 1
+                sel_ok &= kept == ref["kept"]
+            A = np.zeros((64, 64 * (r + 1)))
+            for c in kept:
+                A[:, 64 * c: 64 * c + 64] = oracle.round_bf16(ref["rows"][:, 64 * c: 64 * c + 64])
+            mixed += M[:, j, None, None] * A[None]
+        Vp = f64(x["v"][:, p * slot: p * slot + 64 * (r + 1)])
+        ref_o = np.stack([mixed[h] @ Vp[h] for h in range(Hr)])
+        got = O[:, p * n + 64 * r: p * n + 64 * r + 64].float().cpu().numpy().astype(np.float64)
+        worst_o = max(worst_o, rel(got, oracle.round_bf16(ref_o)))
+    out["fused_rel_l2"] = round(worst_o, 6)
+    out["fused_decided_selections"] = decided
+    out["selections_ok"] = bool(sel_ok)
+    out["ok"] = bool(out["head_map_ok"] and sel_ok and worst <= 1e-2 and worst_o <= 1e-2)
+    out["seconds"] = round(time.perf_counter() - t0, 1)
+    return out
 
 
 def cpu_baseline(x, P, n, tokens, tau):

@@ -543,25 +543,27 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
 // reads whole key rows), reduce across those lanes, and the logit goes to LDS.
 // Four keys per group are in flight at a time (256 key rows per workgroup). Max,
 // sum and the normalised row are then formed from LDS and written with coalesced
-// stores. K is read once.
+// stores. K is read once when the row fits the LDS window (rows_cap keys, sized
+// from the longest key sequence); a longer row (lengths above the maxima the
+// caller passed) is still computed, window by window: an online max and sum
+// over all windows, then each window's logits again for the write.
 constexpr int kRowsThreads = 1024;
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kRowsThreads) void k_attn_rows(AttnMapsArgs a) {
-  extern __shared__ float lg[];  // logits (log2 units) of the row's keys
+  extern __shared__ float lg[];  // logits (log2 units) of the current window's keys
   constexpr int NW = kRowsThreads / 64;
   __shared__ float red[NW];
   constexpr int LPK = D / 8, KPP = kRowsThreads / LPK;  // lanes per key, keys per pass
   const int s = blockIdx.x, h = blockIdx.y;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
-  // rows longer than the LDS sized from max_seqlen_k are not computed (the
-  // lengths must not exceed the maxima the caller passes)
-  if (!seq_ok(a.vl, s, nq, nk) || nq != 1 || nk > a.rows_cap) return;
+  if (!seq_ok(a.vl, s, nq, nk) || nq != 1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l = tid % LPK, g = tid / LPK;
   const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
   const float scale_l2 = ld_const(a.scale + h) * kLog2e;
   const float bias_l2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
+  const int cap = a.rows_cap;
   float qv[8];
   {
     const u32x4 w = ldg16(qrow + 8 * l);
@@ -582,47 +584,76 @@ __global__ __launch_bounds__(kRowsThreads) void k_attn_rows(AttnMapsArgs a) {
     for (int off = 1; off < LPK; off <<= 1) d += __shfl_xor(d, off, 64);
     return d;
   };
-  float mx = -INFINITY;
-  int j = g;
-  for (; j + 3 * KPP < nk; j += 4 * KPP) {
-    u32x4 w[4];
+  // logits of keys w0 .. w0 + wn - 1 into lg[0 .. wn); returns this thread's max
+  auto logits = [&](int w0, int wn) {
+    float mx = -INFINITY;
+    int j = g;
+    for (; j + 3 * KPP < wn; j += 4 * KPP) {
+      u32x4 w[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = ldg16(kseq + (int64_t)(j + u * KPP) * D + 8 * l);
+      for (int u = 0; u < 4; ++u) w[u] = ldg16(kseq + (int64_t)(w0 + j + u * KPP) * D + 8 * l);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = j + u * KPP;
-      const float t = dot(w[u]) * scale_l2 + (key == 0 ? bias_l2 : 0.0f);
-      mx = fmaxf(mx, t);
-      if (l == 0) lg[key] = t;
+      for (int u = 0; u < 4; ++u) {
+        const int key = w0 + j + u * KPP;
+        const float t = dot(w[u]) * scale_l2 + (key == 0 ? bias_l2 : 0.0f);
+        mx = fmaxf(mx, t);
+        if (l == 0) lg[j + u * KPP] = t;
+      }
     }
-  }
-  for (; j < nk; j += KPP) {
-    const float t = dot(ldg16(kseq + (int64_t)j * D + 8 * l)) * scale_l2 + (j == 0 ? bias_l2 : 0.0f);
-    mx = fmaxf(mx, t);
-    if (l == 0) lg[j] = t;
-  }
-  // workgroup max, then sum of 2^(t - max), in a fixed order
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float M = red[0];
+    for (; j < wn; j += KPP) {
+      const float t = dot(ldg16(kseq + (int64_t)(w0 + j) * D + 8 * l)) * scale_l2 + (w0 + j == 0 ? bias_l2 : 0.0f);
+      mx = fmaxf(mx, t);
+      if (l == 0) lg[j] = t;
+    }
+    return mx;
+  };
+  // workgroup reductions in a fixed order (the leading barrier also orders the
+  // previous use of red and of lg)
+  auto wg_max = [&](float x) {
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    __syncthreads();
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    float m = red[0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w]);
-  float sum = 0.0f;
-  for (int x = tid; x < nk; x += kRowsThreads) sum += exp2f_fast(lg[x] - M);
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  __syncthreads();
-  if (lane == 0) red[wave] = sum;
-  __syncthreads();
-  float L = 0.0f;
+    for (int w = 1; w < NW; ++w) m = fmaxf(m, red[w]);
+    return m;
+  };
+  auto wg_sum = [&](float x) {
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    __syncthreads();
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    float t = 0.0f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) L += red[w];
+    for (int w = 0; w < NW; ++w) t += red[w];
+    return t;
+  };
+  // online max / sum over the windows (one window when nk <= cap)
+  float M = -INFINITY, L = 0.0f;
+  for (int w0 = 0; w0 < nk; w0 += cap) {
+    const int wn = min(cap, nk - w0);
+    const float wm = wg_max(logits(w0, wn));
+    const float Mn = fmaxf(M, wm);
+    float part = 0.0f;
+    for (int x = tid; x < wn; x += kRowsThreads) part += exp2f_fast(lg[x] - Mn);
+    L = L * exp2f_fast(M - Mn) + wg_sum(part);
+    M = Mn;
+  }
   const float lse = M + log2f_fast(L);
   const int64_t base = (int64_t)h * a.head_stride + map_seq_off(a.vl, s, a.packed);
-  for (int x = tid; x < nk; x += kRowsThreads) {
-    const float p = exp2f_fast(lg[x] - lse);
-    if (OUT_BF16) reinterpret_cast<uint16_t*>(a.maps)[base + x] = f2bf(p);
-    else reinterpret_cast<float*>(a.maps)[base + x] = p;
+  for (int w0 = 0; w0 < nk; w0 += cap) {
+    const int wn = min(cap, nk - w0);
+    if (nk > cap) {  // the window's logits again (lg holds the last window's)
+      __syncthreads();
+      logits(w0, wn);
+      __syncthreads();
+    }
+    for (int x = tid; x < wn; x += kRowsThreads) {
+      const float p = exp2f_fast(lg[x] - lse);
+      if (OUT_BF16) reinterpret_cast<uint16_t*>(a.maps)[base + w0 + x] = f2bf(p);
+      else reinterpret_cast<float*>(a.maps)[base + w0 + x] = p;
+    }
   }
 }
 
@@ -742,7 +773,7 @@ constexpr int kRowsMaxKeys = 36 * 1024;  // keys of a single-row sequence held i
 
 template <int D>
 static hipError_t launch_rows(AttnMapsArgs a, int max_k, hipStream_t st) {
-  a.rows_cap = max_k;
+  a.rows_cap = max_k;  // >= 1 (checked by the caller of launch_rows)
   const size_t lds = (size_t)max_k * sizeof(float);
   const void* f = a.out_bf16 ? reinterpret_cast<const void*>(&k_attn_rows<D, true>)
                              : reinterpret_cast<const void*>(&k_attn_rows<D, false>);

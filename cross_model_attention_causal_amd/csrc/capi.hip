@@ -91,6 +91,44 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// CMA_CHECK_LENGTHS=1: every call copies the device sequence tables to the host
+// (synchronously) and checks them against the host maxima and tensor sizes.
+bool check_lengths_enabled() {
+  static const bool on = [] {
+    const char* s = getenv("CMA_CHECK_LENGTHS");
+    return s && s[0] == '1';
+  }();
+  return on;
+}
+
+int check_lengths_on_device(const cma_varlen* vl, bool need_k) {
+  const int n = vl->n_seqs;
+  if (n == 0) return CMA_OK;
+  std::vector<int32_t> cq(n + 1), ck(n + 1), uq, uk;
+  auto get = [&](const int32_t* p, std::vector<int32_t>& v, size_t cnt) {
+    v.resize(cnt);
+    return hipMemcpy(v.data(), p, cnt * sizeof(int32_t), hipMemcpyDeviceToHost);
+  };
+  if (get(vl->cu_seqlens_q, cq, n + 1) != hipSuccess) return fail(CMA_EHIP, "copying cu_seqlens_q failed");
+  const int32_t* cuk = vl->cu_seqlens_k ? vl->cu_seqlens_k : vl->cu_seqlens_q;
+  if (get(cuk, ck, n + 1) != hipSuccess) return fail(CMA_EHIP, "copying cu_seqlens_k failed");
+  if (vl->seqused_q && get(vl->seqused_q, uq, n) != hipSuccess) return fail(CMA_EHIP, "copying seqused_q failed");
+  if (vl->seqused_k && get(vl->seqused_k, uk, n) != hipSuccess) return fail(CMA_EHIP, "copying seqused_k failed");
+  const int64_t tk = vl->cu_seqlens_k ? vl->total_k : vl->total_q;
+  for (int s = 0; s < n; ++s) {
+    const int64_t lq = vl->seqused_q ? uq[s] : (int64_t)cq[s + 1] - cq[s];
+    const int64_t lk = vl->seqused_k ? uk[s] : (int64_t)ck[s + 1] - ck[s];
+    if (cq[s] < 0 || ck[s] < 0 || cq[s + 1] < cq[s] || ck[s + 1] < ck[s])
+      return fail(CMA_EINVAL, "cu_seqlens must be nonnegative and nondecreasing (sequence %d)", s);
+    if (lq < 0 || lk < 0 || cq[s] + lq > vl->total_q || (need_k && ck[s] + lk > tk))
+      return fail(CMA_EINVAL, "sequence %d runs past the tensor rows", s);
+    if (lq > vl->max_seqlen_q || (need_k && lk > vl->max_seqlen_k))
+      return fail(CMA_EINVAL, "sequence %d is longer (%lld / %lld) than max_seqlen_q / _k (%d / %d)", s,
+                  (long long)lq, (long long)lk, vl->max_seqlen_q, vl->max_seqlen_k);
+  }
+  return CMA_OK;
+}
+
 int check_varlen(const cma_varlen* vl, bool need_k) {
   if (!vl) return fail(CMA_EINVAL, "varlen descriptor is NULL");
   if (vl->n_seqs < 0) return fail(CMA_EINVAL, "n_seqs < 0");
@@ -100,6 +138,7 @@ int check_varlen(const cma_varlen* vl, bool need_k) {
   if (vl->total_q < 0 || vl->total_k < 0) return fail(CMA_EINVAL, "negative total rows");
   if (vl->max_seqlen_q > vl->total_q || (need_k && vl->max_seqlen_k > vl->total_k))
     return fail(CMA_EINVAL, "max_seqlen exceeds the tensor rows");
+  if (check_lengths_enabled()) return check_lengths_on_device(vl, need_k);
   return CMA_OK;
 }
 

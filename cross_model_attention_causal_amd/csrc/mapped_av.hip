@@ -694,17 +694,20 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
         return beg + kk + rdir * (nb - 1 - 2 * kk);
       };
       // Issue the loads of panel ks of block e (column c) into set S; okv = 0
-      // past the last block: the descriptors then hold no bytes and the loads
-      // return zeros without touching memory.
+      // past the last block, where no load may touch memory: the A descriptor then
+      // holds no bytes, and the V loads take a lane offset of 2^31, past the end of
+      // the V descriptor (the range check of a raw buffer access covers the lane
+      // offset, not the scalar one), so both return zeros.
       auto issue = [&](int ks, int e, int c, int okv, Set& S) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(a.vals + (int64_t)e * (kBlock * kBlock)), (short)0, okv * (kBlock * kBlock * 2),
             kBufferFlags);
 #pragma unroll
         for (int u = 0; u < 2; ++u) S.x[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane + 1024u * u, 2048 * ks, 0);
-        const int vo = (int)((uint32_t)(c * (kBlock * D * 2) + ks * 4096) | ((uint32_t)(1 - okv) << 31));
+        const int vo = c * (kBlock * D * 2) + ks * 4096;
+        const uint32_t vlo = v_lane | ((uint32_t)(1 - okv) << 31);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) S.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_lane + 1024u * dt, vo, 0);
+        for (int dt = 0; dt < 4; ++dt) S.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlo + 1024u * dt, vo, 0);
       };
       auto compute = [&](const Set& S) __attribute__((always_inline)) {
 #pragma unroll

@@ -25,7 +25,7 @@ Readings where the pages are silent are stated in the functions' docstrings.
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, invariants, library special cases or brute force.
 """
-from .numerics import round_bf16, round_f32, round_to
+from .numerics import round_bf16, round_f32
 from .attention import causal_map, attn_maps, pack_rows, packed_size, seq_lengths
 from .cosine import cosine_matrix, head_map
 from .compress import (BLOCK, block_masses, select_blocks, selection_margin, compress_head,
@@ -34,7 +34,7 @@ from .mapped_av import dense_from_bsr_rows, mapped_av_dense, mapped_av_bsr_rows,
 from .layers import mapped_layers, mapping_plan, onehot_mix
 
 __all__ = [
-    "round_bf16", "round_f32", "round_to", "causal_map", "attn_maps", "pack_rows", "packed_size",
+    "round_bf16", "round_f32", "causal_map", "attn_maps", "pack_rows", "packed_size",
     "seq_lengths", "cosine_matrix", "head_map", "BLOCK", "block_masses", "select_blocks",
     "selection_margin", "compress_head", "compress_block_row", "block_compress", "row_stats", "dense_from_bsr_rows",
     "mapped_av_dense", "mapped_av_bsr_rows", "mix_maps", "mapped_layers", "mapping_plan", "onehot_mix",

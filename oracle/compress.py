@@ -140,8 +140,9 @@ def compress_block_row(q, k, scale, bias, r, tau, block=BLOCK):
 
     Returns dict with ``masses`` [r + 1], ``kept`` (ascending columns), ``margin``,
     ``blocks`` (float64 bf16-rounded ``[k, 64, 64]``, zero above the diagonal and
-    past the sequence) and the row statistics ``m``, ``l`` of the block-row's
-    queries (natural units).
+    past the sequence), ``rows`` (the exact float64 map rows of the block-row,
+    ``[64, 64 (r + 1)]``, zero-padded likewise) and the row statistics ``m``, ``l``
+    of the block-row's queries (natural units).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -162,7 +163,7 @@ def compress_block_row(q, k, scale, bias, r, tau, block=BLOCK):
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)
     l = np.exp(s - m[:, None]).sum(axis=1)
-    return dict(masses=masses, kept=cols, margin=margin, blocks=blocks, m=m, l=l)
+    return dict(masses=masses, kept=cols, margin=margin, blocks=blocks, rows=rows, m=m, l=l)
 
 
 def block_compress(q, k, scale, bias, cu, tau, used=None, block=BLOCK, heads=None,

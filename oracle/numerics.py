@@ -25,13 +25,9 @@ def round_bf16(x):
 
 
 def round_f32(x):
-    """Round float64 values to the nearest float32 value (ties to even), as float64."""
+    """Round float64 values to the nearest float32 value (ties to even), as float64.
+
+    numpy's float64 -> float32 conversion is the IEEE 754 one: round to nearest,
+    ties to even, with float32 subnormals below 2**-126 and overflow to infinity.
+    """
     return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
-
-
-def round_to(x, dtype: str):
-    if dtype == "bf16":
-        return round_bf16(x)
-    if dtype == "f32":
-        return round_f32(x)
-    raise ValueError(dtype)

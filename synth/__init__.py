@@ -119,74 +119,6 @@ def mix_matrix_learned(seed: int, n_recv: int, n_send: int, n_batch: int = 1, si
     return m.astype(np.float32)
 
 
-def mix_matrix_stochastic(seed: int, n_recv: int, n_send: int, n_batch: int = 1):
-    """Nonnegative mixing weights with unit row sums (U[0, 1) rows divided by their sum)."""
-    rng = _rng(np.random.SeedSequence(seed))
-    m = rng.uniform(0.0, 1.0, size=(n_batch, n_recv, n_send))
-    m = m / m.sum(axis=2, keepdims=True)
-    return m.astype(np.float32)
-
-
-def synthetic_bsr(seed: int, n_heads: int, lengths, keep_frac: float = 0.93, block: int = 64):
-    """A structurally valid block-sparse causal map set drawn at random.
-
-    Stands in for a compressor's output when only the consumer (the fused
-    mapped x V pass) is under test at full size. For every head and block-row a
-    random subset of the causal blocks is kept (each independently with
-    probability ``keep_frac``; the diagonal block always, so no row is empty); the
-    kept blocks hold bf16 values ``|N(0,1)| / (i + 1)`` for row position ``i``
-    (roughly the size of causal attention probabilities), zero above the diagonal
-    and outside the sequence. Layout matches the library's block-sparse format:
-    ``row_ptr[H * R_tot + 1]``, ``col_idx[nnz]``, ``vals[nnz, 64, 64]`` (uint16 bf16).
-    Stream order: [kept masks (one uniform per causal block, head-major, then
-    sequence, block-row, column), values (one 64 x 64 normal draw per kept block,
-    in storage order)].
-    """
-    ss = np.random.SeedSequence(seed)
-    s_keep, s_val = ss.spawn(2)
-    rk, rv = _rng(s_keep), _rng(s_val)
-    lengths = list(lengths)
-    nblk = [(n + block - 1) // block for n in lengths]
-    r_tot = sum(nblk)
-    counts, cols, blk_r, blk_s = [], [], [], []
-    for h in range(n_heads):
-        for s, n in enumerate(lengths):
-            R = nblk[s]
-            if R == 0:
-                continue
-            u = rk.uniform(size=R * (R + 1) // 2)
-            rr = np.repeat(np.arange(R), np.arange(1, R + 1))
-            cc = np.arange(R * (R + 1) // 2) - (rr * (rr + 1)) // 2
-            keep = (u < keep_frac) | (cc == rr)
-            counts.append(np.bincount(rr[keep], minlength=R))
-            cols.append(cc[keep].astype(np.int32))
-            blk_r.append(rr[keep])
-            blk_s.append(np.full(int(keep.sum()), s))
-    counts = np.concatenate(counts) if counts else np.zeros(0, np.int64)
-    assert counts.size == n_heads * r_tot
-    row_ptr = np.zeros(n_heads * r_tot + 1, dtype=np.int64)
-    row_ptr[1:] = np.cumsum(counts)
-    nnz = int(row_ptr[-1])
-    col_idx = np.concatenate(cols).astype(np.int32) if cols else np.zeros(0, np.int32)
-    blk_r = np.concatenate(blk_r) if blk_r else np.zeros(0, np.int64)
-    blk_s = np.concatenate(blk_s) if blk_s else np.zeros(0, np.int64)
-    lens = np.asarray(lengths, dtype=np.int64)
-    vals = np.zeros((nnz, block, block), dtype=np.uint16)
-    ii = np.arange(block)[None, :, None]
-    jj = np.arange(block)[None, None, :]
-    chunk = 4096
-    for a in range(0, nnz, chunk):
-        b = min(nnz, a + chunk)
-        rows = blk_r[a:b, None, None] * block + ii
-        colsj = col_idx[a:b, None, None].astype(np.int64) * block + jj
-        nn = lens[blk_s[a:b]][:, None, None]
-        ok = (colsj <= rows) & (rows < nn) & (colsj < nn)
-        x = np.abs(rv.standard_normal(size=(b - a, block, block), dtype=np.float32)) / (rows + 1.0)
-        vals[a:b] = bf16_from_f32(np.where(ok, x, 0.0).astype(np.float32))
-    return dict(row_ptr=row_ptr.astype(np.int32), col_idx=col_idx, vals=vals, nnz=nnz,
-                lengths=lengths, n_heads=n_heads, block=block)
-
-
 # ----------------------------------------------------------------------------- named workloads
 D = 128
 
@@ -354,4 +286,32 @@ def prefill_batch(n_prompts: int = 4, n: int = 8192, n_send: int = 32, n_recv: i
     out.update(n_prompts=n_prompts, n=n, slot=slot, tau_t=tau_t, n_send=n_send, n_recv=n_recv, d=D,
                cu_q=cu_from_lengths([n] * n_prompts), cu_k=cu_from_lengths([slot] * n_prompts),
                cu_t=cu_from_lengths([tau_t] * n_prompts))
+    return out
+
+
+def long_decode(n_prompts: int = 4, n: int = 8192, decode: int = 512, n_send: int = 32, n_recv: int = 24):
+    """IAM's long-context decode: ``n_prompts`` prompts of ``n`` tokens, each followed
+    by ``decode`` generated tokens whose mapped layers reuse the sender's attention
+    row over the growing context (8192 + 512 at batch 4 in the IAM efficiency setting).
+
+    * ``send_k`` [32, P*(n+decode), 128]: sender keys of the prompt and generated tokens
+    * ``dec_q`` [decode, 32, P, 128]: sender query of each generated token (step-major)
+    * ``v`` [24, P*(n+decode), 128]: receiver values of the same positions
+    * ``M`` [1, 24, 32]: learned-style mixing weights (N(0, 0.2) + 1 on the diagonal)
+    Stream order: [send k, send heads, dec q, v, M].
+    """
+    ss = np.random.SeedSequence([BASE_SEED + 45, n_prompts, n, decode])
+    s = ss.spawn(5)
+    ctx = n + decode
+    out = dict(send_k=_normal_bf16(_rng(s[0]), (n_send, n_prompts * ctx, D)))
+    out["send_scale"], out["send_bias"] = head_scales(_rng(s[1]), 1, n_send, D)
+    out["dec_q"] = _normal_bf16(_rng(s[2]), (decode, n_send, n_prompts, D))
+    out["v"] = _normal_bf16(_rng(s[3]), (n_recv, n_prompts * ctx, D))
+    r = _rng(s[4])
+    m = r.normal(0.0, 0.2, size=(1, n_recv, n_send))
+    for h in range(min(n_recv, n_send)):
+        m[0, h, h] += 1.0
+    out["M"] = m.astype(np.float32)
+    out.update(n_prompts=n_prompts, n=n, decode=decode, ctx=ctx, n_send=n_send, n_recv=n_recv, d=D,
+               cu_k=cu_from_lengths([ctx] * n_prompts))
     return out

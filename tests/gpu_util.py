@@ -80,3 +80,35 @@ def tile_v(V, lens, cu):
             out[:, b0 + c, pos] = blk[:, key.ravel(), feat.ravel()]
         b0 += nb[s]
     return out
+
+
+def greedy_mismatches(mass_packed, row_ptr, col, R_list, tau, head_off=0, min_margin=1e-6):
+    """Selection validity on every block-row, from the library's own masses.
+
+    ``mass_packed``: one head's masses over its sequences, each packed
+    lower-triangular (offset + r(r+1)/2 + c); ``R_list``: block-rows per sequence;
+    ``head_off``: index of the head's first block-row in ``row_ptr``. For every
+    block-row the greedy shortest prefix (weight descending, ties to the lower
+    column, running sum >= tau) is recomputed in float64 from those masses and
+    compared with the kept columns the library returned. Returns (rows compared,
+    list of mismatching rows whose margin under the library's masses exceeds
+    ``min_margin``, rows skipped for a smaller margin).
+    """
+    import oracle
+    bad, skipped, n = [], 0, 0
+    off, g = 0, head_off
+    for R in R_list:
+        for r in range(R):
+            mrow = np.asarray(mass_packed[off + r * (r + 1) // 2: off + r * (r + 1) // 2 + r + 1], dtype=np.float64)
+            kept = [int(c) for c in col[row_ptr[g]: row_ptr[g + 1]]]
+            n += 1
+            if mrow.sum() > 0:
+                want = oracle.select_blocks(mrow, tau)
+                if kept != want:
+                    if oracle.selection_margin(mrow, tau) > min_margin:
+                        bad.append(g)
+                    else:
+                        skipped += 1
+            g += 1
+        off += R * (R + 1) // 2
+    return n, bad, skipped

@@ -225,3 +225,60 @@ def test_indexed_workspace_and_validation(lib):
     assert tile(fake, V_TOKEN_MAJOR, 4, 64, ctypes.byref(vl), 4, fake, None) == -2
     assert tile(fake, V_TOKEN_MAJOR, 4, 128, ctypes.byref(vl), 4, None, None) == -1
     assert tile(fake, V_TOKEN_MAJOR, 4, 128, ctypes.byref(vl), 0, fake, None) == -1
+
+
+def test_workspace_too_small_is_enospc(lib):
+    """Each call that takes a workspace rejects a short one with CMA_ENOSPC before
+    any device work (the fake pointers below are never dereferenced)."""
+    from cross_model_attention_causal_amd import _CMapsSrc, _CVarlen, SRC_BSR, V_TOKEN_MAJOR
+    P, I32, I64, SZ, INT, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int,
+                               ctypes.c_float)
+    lib.cma_last_error.restype = ctypes.c_char_p
+    fake = 0x1000
+    vl = _CVarlen()
+    vl.n_seqs, vl.cu_seqlens_q, vl.cu_seqlens_k = 2, fake, fake
+    vl.max_seqlen_q = vl.max_seqlen_k = 128
+    vl.total_q = vl.total_k = 256
+
+    # head_map_cosine
+    cws = lib.cma_head_map_cosine_workspace
+    cws.restype, cws.argtypes = SZ, [I32, I32, I32, I64, INT]
+    need = cws(1, 24, 32, 131328, 1)
+    assert need > 0
+    cos = lib.cma_head_map_cosine
+    cos.argtypes = [P, P, INT, I32, I32, I32, I64, I64, I64, I64, I64, P, P, P, P, SZ, P]
+    args = (fake, fake, 1, 1, 24, 32, 131328, 131328, 0, 131328, 0, fake, fake, fake)
+    assert cos(*args, fake, need - 1, None) == -3
+    assert b"workspace" in lib.cma_last_error()
+    assert cos(*args, None, need, None) == -3
+
+    # block_compress
+    bws = lib.cma_block_compress_workspace
+    bws.restype, bws.argtypes = SZ, [I32, I32, I32, I64]
+    need = bws(4, 4, 128, 256)
+    assert need >= 4 * 4 * (4 + 32) + 4 * 256 * 4
+    comp = lib.cma_block_compress
+    comp.argtypes = [P, P, INT, I32, I32, P, P, P, F, I32, P, P, P, I64, P, P, P, P, SZ, P]
+    head = (fake, fake, 1, 4, 128, ctypes.byref(vl), fake, None, 0.95, 4, fake, fake, fake, 40, fake, None, None)
+    assert comp(*head, fake, need - 1, None) == -3
+    assert comp(*head, None, need, None) == -3
+    bad_tau = head[:8] + (0.0,) + head[9:]
+    assert comp(*bad_tau, fake, need, None) == -1                  # tau must be > 0
+    d96 = head[:4] + (96,) + head[5:]
+    assert comp(*d96, fake, need, None) == -2                      # head dim 96 is not built
+
+    # mapped_av, block-sparse source with token-major V (V is tiled in the workspace)
+    src = _CMapsSrc()
+    src.kind, src.n_block_rows = SRC_BSR, 4
+    src.row_ptr = src.col_idx = src.vals = fake
+    mws = lib.cma_mapped_av_workspace
+    mws.restype, mws.argtypes = SZ, [P, I32, I32, I64, INT]
+    need = mws(ctypes.byref(src), 24, 128, 256, V_TOKEN_MAJOR)
+    assert need == 24 * 4 * 64 * 128 * 2
+    mav = lib.cma_mapped_av
+    mav.argtypes = [P, I32, P, I64, I32, I32, P, INT, INT, I32, P, P, INT, P, SZ, P]
+    run = lambda ws, nb: mav(ctypes.byref(src), 32, fake, 0, 24, 24, fake, 1, V_TOKEN_MAJOR, 128, ctypes.byref(vl),
+                             fake, 1, ws, nb, None)
+    assert run(fake, need - 1) == -3
+    assert run(None, need) == -3
+    assert run(fake + 8, need) == -1                               # workspace must be 16-byte aligned

@@ -14,7 +14,7 @@ import torch
 import oracle
 import synth
 from tests.gpu_util import (dev_bf16, dev_f32, dev_i32, f64, host64, rel_l2, bf16_bits_from_f64, tile_v,
-                            blocks_to_panels, blocks_from_panels)
+                            blocks_to_panels, blocks_from_panels, greedy_mismatches)
 
 pytestmark = pytest.mark.gpu
 
@@ -234,6 +234,13 @@ def test_block_compress_small(cma, tau):
         if gk == ref["kept"][g] and gk:
             a, b = row_ptr[g], ref["row_ptr"][g]
             assert rel_l2(vals[a: a + len(gk)], ref["vals"][b: b + len(gk)]) <= 1e-2
+    # every block-row, exempt or not: the kept set is the greedy prefix of the
+    # library's own masses (where those masses decide it by more than 1e-6)
+    R_list = [(n + 63) // 64 for n in lens]
+    mass = host64(out["block_mass"])
+    for h in range(H):
+        _, bad, _ = greedy_mismatches(mass[h], row_ptr, col, R_list, tau, head_off=h * sum(R_list))
+        assert not bad, (h, bad)
     say(f"  nnz={nnz} oracle={ref['nnz']} exempt rows differing={exempt}")
 
 
@@ -279,7 +286,11 @@ def test_block_compress_longest_sequence(cma):
                     checked += 1
                 else:
                     exempt += 1
-    say(f"  {checked} sampled block-rows equal, {exempt} exempt (margin <= 1e-4)")
+    for h in range(H):
+        n_rows, bad, _ = greedy_mismatches(mass[h], row_ptr, col, R, tau, head_off=h * sum(R))
+        assert not bad, (h, bad)
+    say(f"  {checked} sampled block-rows equal, {exempt} exempt (margin <= 1e-4); greedy prefix of the "
+        f"library's masses on all {H * sum(R)} block-rows")
 
 
 # ------------------------------------------------------------------ mapped_av block-sparse
