@@ -29,7 +29,7 @@ BLOCK = 64
 EXPORTS = [
     "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
     "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks",
-    "cma_block_compress_workspace", "cma_block_compress", "cma_mapped_av_workspace",
+    "cma_block_compress_workspace", "cma_block_compress", "cma_block_compress_noalloc", "cma_mapped_av_workspace",
     "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_tile_v", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
     "cma_timing_collect", "cma_timing_get", "cma_timing_name", "cma_timing_reset",
 ]
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH):
         "cma_block_compress_workspace": (SZ, [I32, I32, I32, I64]),
         "cma_block_compress": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, F, I32, P, P,
                                               P, I64, P, P, P, P, SZ, P]),
+        "cma_block_compress_noalloc": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, F, I32, P, P,
+                                                      P, I64, P, P, P, P]),
         "cma_mapped_av_workspace": (SZ, [P, I32, I32, I64, ctypes.c_int]),
         "cma_mapped_av": (ctypes.c_int, [P, I32, P, I64, I32, I32, P, ctypes.c_int, ctypes.c_int, I32, P,
                                          P, ctypes.c_int, P, SZ, P]),
@@ -276,10 +278,11 @@ class Workspace:
 
 
 def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=False,
-                   want_stats=False, workspace: Workspace | None = None, bsr=None):
+                   want_stats=False, workspace: Workspace | None = None, bsr=None, no_alloc=False):
     """Two-phase block-sparse compression. Returns a dict with row_ptr, col_idx,
     vals (bf16 [capacity, 64, 64]), nnz (device int32[1]) and optional masses/stats.
-    ``bsr`` may pass preallocated output arrays to reuse."""
+    ``bsr`` may pass preallocated output arrays to reuse. ``no_alloc`` calls
+    ``cma_block_compress_noalloc`` (the library's static scratch, no workspace)."""
     torch = _torch()
     lib = load_library()
     H, Tq, d = q.shape
@@ -304,15 +307,17 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
     n_tri = int(sum(((int(n) + BLOCK - 1) // BLOCK) * ((int(n) + BLOCK - 1) // BLOCK + 1) // 2 for n in vl.lens_q))
     mass = torch.empty((H, n_tri), dtype=torch.float32, device=dev) if want_mass else None
     stats = torch.empty((H, Tq, 2), dtype=torch.float32, device=dev) if want_stats else None
-    ws_bytes = lib.cma_block_compress_workspace(H, nbr, vl.max_q, Tq)
-    ws = (workspace or Workspace()).get(ws_bytes, dev)
     cvl = vl.c(Tq, k.shape[1])
-    _check(lib.cma_block_compress(_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dt(q), H, d, ctypes.byref(cvl),
-                                  _dev_ptr(scale, "scale"), _dev_ptr(bias, "bias"), float(tau), nbr,
-                                  _dev_ptr(bsr["row_ptr"], "row_ptr"), _dev_ptr(bsr["col_idx"], "col_idx"),
-                                  _dev_ptr(bsr["vals"], "vals"), bsr["capacity"],
-                                  _dev_ptr(bsr["nnz"], "nnz"), _dev_ptr(mass, "block_mass"),
-                                  _dev_ptr(stats, "row_stats"), ws.data_ptr(), ws.numel(), _stream()))
+    head = (_dev_ptr(q, "q"), _dev_ptr(k, "k"), _dt(q), H, d, ctypes.byref(cvl), _dev_ptr(scale, "scale"),
+            _dev_ptr(bias, "bias"), float(tau), nbr, _dev_ptr(bsr["row_ptr"], "row_ptr"),
+            _dev_ptr(bsr["col_idx"], "col_idx"), _dev_ptr(bsr["vals"], "vals"), bsr["capacity"],
+            _dev_ptr(bsr["nnz"], "nnz"), _dev_ptr(mass, "block_mass"), _dev_ptr(stats, "row_stats"))
+    if no_alloc:
+        _check(lib.cma_block_compress_noalloc(*head, _stream()))
+    else:
+        ws_bytes = lib.cma_block_compress_workspace(H, nbr, vl.max_q, Tq)
+        ws = (workspace or Workspace()).get(ws_bytes, dev)
+        _check(lib.cma_block_compress(*head, ws.data_ptr(), ws.numel(), _stream()))
     out = dict(bsr)
     out.update(block_mass=mass, row_stats=stats, n_block_rows=nbr, n_heads=H)
     return out

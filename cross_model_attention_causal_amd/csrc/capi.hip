@@ -333,11 +333,69 @@ size_t cma_block_compress_workspace(int32_t n_heads, int32_t n_block_rows, int32
   return compress_ws_bytes(n_heads, n_block_rows, total_q);
 }
 
+}  // extern "C"
+
+// Scratch of the allocation-free compression entry point: one array per GPU the
+// library runs on (part of the library's code object, held until the process
+// ends). Host code never passes the array's name to a kernel: on the host it is
+// a stand-in, not a device address. The device address is taken once per device
+// with hipGetSymbolAddress (that device current) and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[CMA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(CMA_EHIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(CMA_EUNSUPPORTED, "device index %d beyond 63", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(CMA_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CMA_OK;
+}
+
+int block_compress_impl(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                        const cma_varlen* vl, const float* logit_scale, const float* key0_bias, float tau,
+                        int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx, void* vals, int64_t capacity,
+                        int32_t* nnz, float* block_mass, float* row_stats, void* workspace, size_t workspace_bytes,
+                        void* stream, bool static_scratch);
+}  // namespace
+
+extern "C" {
+
 int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
                        const cma_varlen* vl, const float* logit_scale, const float* key0_bias,
                        float tau, int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx,
                        void* vals, int64_t capacity, int32_t* nnz, float* block_mass,
                        float* row_stats, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_compress_impl(q, k, in_dt, n_heads, d, vl, logit_scale, key0_bias, tau, n_block_rows, row_ptr,
+                             col_idx, vals, capacity, nnz, block_mass, row_stats, workspace, workspace_bytes, stream,
+                             false);
+}
+
+int cma_block_compress_noalloc(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                               const cma_varlen* vl, const float* logit_scale, const float* key0_bias, float tau,
+                               int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx, void* vals,
+                               int64_t capacity, int32_t* nnz, float* block_mass, float* row_stats, void* stream) {
+  return block_compress_impl(q, k, in_dt, n_heads, d, vl, logit_scale, key0_bias, tau, n_block_rows, row_ptr,
+                             col_idx, vals, capacity, nnz, block_mass, row_stats, nullptr, 0, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+int block_compress_impl(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                        const cma_varlen* vl, const float* logit_scale, const float* key0_bias, float tau,
+                        int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx, void* vals, int64_t capacity,
+                        int32_t* nnz, float* block_mass, float* row_stats, void* workspace, size_t workspace_bytes,
+                        void* stream, bool static_scratch) {
   if (int e = check_varlen(vl, true)) return e;
   if (in_dt != CMA_BF16) return fail(CMA_EUNSUPPORTED, "block_compress needs bf16 q and k");
   if (d != 64 && d != 128) return fail(CMA_EUNSUPPORTED, "block_compress supports d = 64 or 128 (got %d)", d);
@@ -353,6 +411,13 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
     if (!aligned16(q) || !aligned16(k)) return fail(CMA_EINVAL, "q and k must be 16-byte aligned");
   }
   const size_t need = compress_ws_bytes(n_heads, n_block_rows, vl->total_q);
+  if (static_scratch) {
+    if (need > (size_t)CMA_NOALLOC_SCRATCH_BYTES)
+      return fail(CMA_ENOSPC, "the call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                  (size_t)CMA_NOALLOC_SCRATCH_BYTES);
+    if (int e = scratch_address(&workspace)) return e;
+    workspace_bytes = CMA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
   CompressArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -386,8 +451,17 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
     if (e == hipSuccess) e = launch_fill_i32(nnz, 1, 0, st);
     return hip_status(e, "block_compress (empty)");
   }
+  if (static_scratch) {
+    // the shared scratch keeps the previous call's counts: clear them (a fill
+    // kernel) so that a block-row this call does not reach cannot inherit one
+    hipError_t e = launch_fill_i32(a.counts, (int64_t)n_heads * n_block_rows, 0, st);
+    if (e != hipSuccess) return hip_status(e, "block_compress_noalloc (clear)");
+  }
   return hip_status(launch_compress(a, d, st), "block_compress launch");
 }
+}  // namespace
+
+extern "C" {
 
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout) {

@@ -177,6 +177,25 @@ int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_
                        void* vals, int64_t capacity, int32_t* nnz, float* block_mass,
                        float* row_stats, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * cma_block_compress_noalloc -- cma_block_compress for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, results and kernels, without the
+ * workspace. Its scratch (per-block-row counts, kept-column masks and per-query
+ * log-sum-exp: cma_block_compress_workspace(...) bytes) lives in one static
+ * device array of CMA_NOALLOC_SCRATCH_BYTES per GPU, part of the library's code
+ * object. Returns CMA_ENOSPC (nothing launched) when the call needs more; calls
+ * no hipMalloc, hipFree or allocating routine. Every call on one GPU uses that
+ * GPU's one array: calls that overlap on a GPU (other streams, other threads)
+ * race and must be serialised by the caller. The first call on a device takes
+ * the array's device address (hipGetSymbolAddress) and keeps it.
+ */
+#define CMA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int cma_block_compress_noalloc(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
+                               const cma_varlen* vl, const float* logit_scale, const float* key0_bias, float tau,
+                               int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx, void* vals,
+                               int64_t capacity, int32_t* nnz, float* block_mass, float* row_stats, void* stream);
+
 /* Layout of the receiver's V. TOKEN_MAJOR: [n_recv, total_k, d] (row t holds the
  * d values of key t). KEY_MAJOR: [n_recv, d, total_k] (row e holds feature e of
  * every key). TILED (block-sparse source, bf16, d = 128 only): the fused

@@ -282,3 +282,27 @@ def test_workspace_too_small_is_enospc(lib):
     assert run(fake, need - 1) == -3
     assert run(None, need) == -3
     assert run(fake + 8, need) == -1                               # workspace must be 16-byte aligned
+
+
+def test_noalloc_compress_rejects_oversized_scratch(lib):
+    """cma_block_compress_noalloc refuses (CMA_ENOSPC, before any device work) a
+    problem whose scratch would exceed its static array of 16 MiB."""
+    from cross_model_attention_causal_amd import _CVarlen
+    P, I32, I64, SZ, INT, F = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int,
+                               ctypes.c_float)
+    lib.cma_last_error.restype = ctypes.c_char_p
+    ws = lib.cma_block_compress_workspace
+    ws.restype, ws.argtypes = SZ, [I32, I32, I32, I64]
+    fn = lib.cma_block_compress_noalloc
+    fn.argtypes = [P, P, INT, I32, I32, P, P, P, F, I32, P, P, P, I64, P, P, P, P]
+    fake = 0x1000
+    big_T = 1 << 22
+    assert ws(2, big_T // 64, 64, big_T) > (16 << 20)
+    vl = _CVarlen()
+    vl.n_seqs, vl.cu_seqlens_q, vl.cu_seqlens_k = 1, fake, fake
+    vl.max_seqlen_q = vl.max_seqlen_k = 64
+    vl.total_q = vl.total_k = big_T
+    rc = fn(fake, fake, 1, 2, 128, ctypes.byref(vl), fake, None, 0.9, big_T // 64, fake, fake, fake, 0, fake,
+            None, None, None)
+    assert rc == -3
+    assert b"scratch" in lib.cma_last_error()
