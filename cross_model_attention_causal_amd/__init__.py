@@ -23,15 +23,18 @@ CMA_OK, CMA_EINVAL, CMA_EUNSUPPORTED, CMA_ENOSPC, CMA_EHIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 DENSE, PACKED = 0, 1
 SRC_DENSE, SRC_BSR = 0, 1
-V_TOKEN_MAJOR, V_KEY_MAJOR, V_TILED = 0, 1, 2
+V_TOKEN_MAJOR, V_KEY_MAJOR, V_TILED, V_PAGED = 0, 1, 2, 3
 BLOCK = 64
 
 EXPORTS = [
     "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
-    "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks",
+    "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks", "cma_bsr_capacity",
     "cma_block_compress_workspace", "cma_block_compress", "cma_block_compress_noalloc", "cma_mapped_av_workspace",
-    "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_tile_v", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
+    "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_tile_v", "cma_tile_v_paged", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
     "cma_timing_collect", "cma_timing_get", "cma_timing_name", "cma_timing_reset",
+    "cma_prefix_hashes", "cma_fnv1a64", "cma_prefix_index_create", "cma_prefix_index_destroy",
+    "cma_prefix_index_insert", "cma_prefix_index_lookup", "cma_prefix_index_erase", "cma_prefix_index_evict_lru",
+    "cma_prefix_index_size",
 ]
 
 
@@ -53,7 +56,13 @@ class _CMapsSrc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("maps", ctypes.c_void_p), ("maps_dt", ctypes.c_int),
                 ("layout", ctypes.c_int), ("head_stride", ctypes.c_int64),
                 ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
-                ("vals", ctypes.c_void_p), ("n_block_rows", ctypes.c_int32)]
+                ("vals", ctypes.c_void_p), ("n_block_rows", ctypes.c_int32),
+                ("row_end", ctypes.c_void_p), ("n_key_blocks", ctypes.c_int32)]
+
+
+class _CPagedV(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("page_stride", ctypes.c_int32),
+                ("n_pages", ctypes.c_int32)]
 
 
 _lib = None
@@ -80,6 +89,7 @@ def load_library(path: str = LIB_PATH):
         "cma_head_map_cosine": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, I32, I64, I64, I64,
                                                I64, I64, P, P, P, P, SZ, P]),
         "cma_bsr_max_blocks": (I64, [I32, I32, P]),
+        "cma_bsr_capacity": (I64, [I32, I32, P, P]),
         "cma_block_compress_workspace": (SZ, [I32, I32, I32, I64]),
         "cma_block_compress": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, P, P, P, F, I32, P, P,
                                               P, I64, P, P, P, P, SZ, P]),
@@ -92,6 +102,7 @@ def load_library(path: str = LIB_PATH):
         "cma_mapped_av_indexed": (ctypes.c_int, [P, I32, P, I64, I32, I32, P, ctypes.c_int, ctypes.c_int, I32,
                                                  P, P, ctypes.c_int, P, SZ, P]),
         "cma_tile_v": (ctypes.c_int, [P, ctypes.c_int, I32, I32, P, I32, P, P]),
+        "cma_tile_v_paged": (ctypes.c_int, [P, ctypes.c_int, I32, I32, P, P, P]),
         "cma_onehot_mix": (ctypes.c_int, [P, I32, I32, I32, P, P]),
         "cma_mapped_layers": (ctypes.c_int, [I32, D, P, I32]),
         "cma_mapping_plan": (ctypes.c_int, [I32, P, I32, I32, P, P]),
@@ -100,6 +111,15 @@ def load_library(path: str = LIB_PATH):
         "cma_timing_get": (D, [ctypes.c_char_p, ctypes.POINTER(I64)]),
         "cma_timing_name": (ctypes.c_char_p, [ctypes.c_int]),
         "cma_timing_reset": (None, []),
+        "cma_prefix_hashes": (ctypes.c_int, [P, I64, ctypes.c_uint64, P]),
+        "cma_fnv1a64": (ctypes.c_uint64, [P, SZ]),
+        "cma_prefix_index_create": (P, [I32, I64]),
+        "cma_prefix_index_destroy": (None, [P]),
+        "cma_prefix_index_insert": (ctypes.c_int, [P, I32, ctypes.c_uint64, P, P]),
+        "cma_prefix_index_lookup": (I64, [P, I32, P, I64, P, P]),
+        "cma_prefix_index_erase": (ctypes.c_int, [P, I32, ctypes.c_uint64]),
+        "cma_prefix_index_evict_lru": (ctypes.c_int, [P, P, P, P, P]),
+        "cma_prefix_index_size": (I64, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +190,7 @@ class Varlen:
         self.max_q = int(self.lens_q.max()) if n else 0
         self.max_k = int(self.lens_k.max()) if n else 0
         self.n_block_rows = int(sum((int(x) + BLOCK - 1) // BLOCK for x in self.lens_q))
+        self.n_key_blocks = int(sum((int(x) + BLOCK - 1) // BLOCK for x in self.lens_k))
 
     @staticmethod
     def from_lengths(lens_q, lens_k=None, device="cuda"):
@@ -258,10 +279,17 @@ def head_map_cosine(recv, send, n_batch, n_recv, n_send, length, recv_hstride, r
     return cos, arg, mar
 
 
-def bsr_max_blocks(n_heads, lens):
+def bsr_max_blocks(n_heads, lens, lens_k=None):
+    """Most blocks a compression can keep (``lens_k``: key lengths of prefill chunks)."""
     lib = load_library()
     a = np.ascontiguousarray(lens, dtype=np.int32)
-    return int(lib.cma_bsr_max_blocks(n_heads, len(a), a.ctypes.data))
+    if lens_k is None:
+        return int(lib.cma_bsr_max_blocks(n_heads, len(a), a.ctypes.data))
+    b = np.ascontiguousarray(lens_k, dtype=np.int32)
+    r = int(lib.cma_bsr_capacity(n_heads, len(a), a.ctypes.data, b.ctypes.data))
+    if r < 0:
+        raise ValueError("inconsistent lengths")
+    return r
 
 
 class Workspace:
@@ -299,12 +327,16 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
         _need(bsr["vals"], "vals", bsr["capacity"] * BLOCK * BLOCK)
     if bsr is None:
         if capacity is None:
-            capacity = bsr_max_blocks(H, vl.lens_q)
+            capacity = bsr_max_blocks(H, vl.lens_q, vl.lens_k)
         bsr = dict(row_ptr=torch.empty(H * nbr + 1, dtype=torch.int32, device=dev),
                    col_idx=torch.empty(max(1, capacity), dtype=torch.int32, device=dev),
                    vals=torch.empty((max(1, capacity), BLOCK, BLOCK), dtype=torch.bfloat16, device=dev),
                    nnz=torch.empty(1, dtype=torch.int32, device=dev), capacity=capacity)
-    n_tri = int(sum(((int(n) + BLOCK - 1) // BLOCK) * ((int(n) + BLOCK - 1) // BLOCK + 1) // 2 for n in vl.lens_q))
+    # block masses: block-row r of a sequence with kb0 = (nk - nq) / 64 holds kb0 + r + 1
+    n_tri = 0
+    for nq_, nk_ in zip(vl.lens_q, vl.lens_k):
+        R = (int(nq_) + BLOCK - 1) // BLOCK
+        n_tri += R * max(0, (int(nk_) - int(nq_)) // BLOCK) + R * (R + 1) // 2
     mass = torch.empty((H, n_tri), dtype=torch.float32, device=dev) if want_mass else None
     stats = torch.empty((H, Tq, 2), dtype=torch.float32, device=dev) if want_stats else None
     cvl = vl.c(Tq, k.shape[1])
@@ -319,7 +351,7 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
         ws = (workspace or Workspace()).get(ws_bytes, dev)
         _check(lib.cma_block_compress(*head, ws.data_ptr(), ws.numel(), _stream()))
     out = dict(bsr)
-    out.update(block_mass=mass, row_stats=stats, n_block_rows=nbr, n_heads=H)
+    out.update(block_mass=mass, row_stats=stats, n_block_rows=nbr, n_key_blocks=vl.n_key_blocks, n_heads=H)
     return out
 
 
@@ -331,15 +363,31 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
     or int32 sender indices [B, n_recv] (one sender per receiver head, e.g. the
     cosine argmax: O_h = A_{M[h]} V_{h // g}, block-sparse source only; then
     ``M_seq_stride`` counts int32 entries). ``src`` is either a block_compress result
-    (dict with row_ptr/col_idx/vals/n_block_rows) or ``("dense", maps, layout)``.
-    ``v`` is [v_heads, Tk, d] (V_TOKEN_MAJOR), [v_heads, d, Tk] (V_KEY_MAJOR) or
-    [v_heads, n_block_rows, 64 * 128] (V_TILED, block-sparse source only; then
-    ``k_rows`` gives Tk). ``q_rows`` is the row count of the output tensor
-    (default: Tk)."""
+    (dict with row_ptr/col_idx/vals/n_block_rows, optionally row_end and
+    n_key_blocks) or ``("dense", maps, layout)``.
+    ``v`` is [v_heads, Tk, d] (V_TOKEN_MAJOR), [v_heads, d, Tk] (V_KEY_MAJOR),
+    [v_heads, n_key_blocks, 64 * 128] (V_TILED) or a dict ``{"pages": [v_heads,
+    n_pages, 64 * 128], "table": int32 [n_seqs, stride]}`` (V_PAGED); the last two
+    serve block-sparse sources only and need ``k_rows`` (Tk). ``q_rows`` is the
+    row count of the output tensor (default: Tk)."""
     torch = _torch()
     lib = load_library()
-    dev = v.device
-    if v_layout == V_KEY_MAJOR:
+    pv = None
+    dev = v["pages"].device if v_layout == V_PAGED else v.device
+    if v_layout == V_PAGED:
+        pages, table = v["pages"], v["table"]
+        if k_rows is None:
+            raise ValueError("V_PAGED needs k_rows (the key rows of the packed sequences)")
+        if table.dim() != 2 or table.dtype != torch.int32 or table.shape[0] < vl.n_seqs:
+            raise ValueError("the page table must be int32 [n_seqs, stride]")
+        H, d, Tk = pages.shape[0], 128, k_rows
+        pv = _CPagedV()
+        pv.pages = _dev_ptr(pages, "pages")
+        pv.page_table = _dev_ptr(table, "page table")
+        pv.page_stride = table.shape[1]
+        pv.n_pages = pages.shape[1]
+        vdt, vptr = _dt(pages), ctypes.addressof(pv)
+    elif v_layout == V_KEY_MAJOR:
         H, d, Tk = v.shape
     elif v_layout == V_TILED:
         H, d = v.shape[0], 128
@@ -348,12 +396,14 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         Tk = k_rows
     else:
         H, Tk, d = v.shape
+    if pv is None:
+        vdt, vptr = _dt(v), _dev_ptr(v, "v")
     n_v = n_recv if v_heads is None else int(v_heads)
     if n_v < 1 or n_recv % n_v:
         raise ValueError(f"v_heads ({n_v}) must be >= 1 and divide n_recv ({n_recv})")
     if H < n_v:
         raise ValueError(f"v holds {H} heads, {n_v} are needed")
-    out_dtype = out_dtype or v.dtype
+    out_dtype = out_dtype or (torch.bfloat16 if pv is not None else v.dtype)
     Tq = q_rows if q_rows is not None else Tk
     _check_rows(vl, Tq, Tk)
     if out is None:
@@ -361,14 +411,19 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
     _need(out, "out", n_recv * Tq * d)
     s = _CMapsSrc()
     if isinstance(src, dict):
+        nkb = int(src.get("n_key_blocks") or vl.n_key_blocks)
         if v_layout == V_TILED:
-            _need(v, "v", n_v * src["n_block_rows"] * BLOCK * 128)
-        _need(src["row_ptr"], "row_ptr", n_send * src["n_block_rows"] + 1)
+            _need(v, "v", n_v * nkb * BLOCK * 128)
+        row_end = src.get("row_end")
+        _need(src["row_ptr"], "row_ptr", n_send * src["n_block_rows"] + (0 if row_end is not None else 1))
+        _need(row_end, "row_end", n_send * src["n_block_rows"])
         s.kind = SRC_BSR
         s.row_ptr = _dev_ptr(src["row_ptr"], "row_ptr")
         s.col_idx = _dev_ptr(src["col_idx"], "col_idx")
         s.vals = _dev_ptr(src["vals"], "vals")
         s.n_block_rows = src["n_block_rows"]
+        s.row_end = _dev_ptr(row_end, "row_end")
+        s.n_key_blocks = nkb
     else:
         _, maps, layout = src
         if maps.dim() != 2 or maps.shape[0] < n_send or maps.shape[1] < vl.maps_elems(layout):
@@ -388,7 +443,7 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         ws_bytes = lib.cma_mapped_av_indexed_workspace(ctypes.byref(s), n_recv, n_v, d, vl.n_seqs, v_layout)
         ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
         _check(lib.cma_mapped_av_indexed(ctypes.byref(s), n_send, _dev_ptr(M, "sender"), M_seq_stride, n_recv,
-                                         n_v, _dev_ptr(v, "v"), _dt(v), v_layout, d, ctypes.byref(cvl),
+                                         n_v, vptr, vdt, v_layout, d, ctypes.byref(cvl),
                                          _dev_ptr(out, "out"), _dt(out),
                                          ws.data_ptr() if ws is not None else None,
                                          ws.numel() if ws is not None else 0, _stream()))
@@ -399,7 +454,7 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
     ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_v, d, Tk, v_layout)
     ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
     _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv, n_v,
-                             _dev_ptr(v, "v"), _dt(v), v_layout, d, ctypes.byref(cvl),
+                             vptr, vdt, v_layout, d, ctypes.byref(cvl),
                              _dev_ptr(out, "out"), _dt(out),
                              ws.data_ptr() if ws is not None else None,
                              ws.numel() if ws is not None else 0, _stream()))
@@ -408,8 +463,9 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
 
 def tile_v(v, vl: Varlen, n_block_rows, v_layout=V_TOKEN_MAJOR, out=None):
     """V ([H, Tk, 128] token-major or [H, 128, Tk] key-major, bf16) in the tiled
-    operand order [H, n_block_rows, 64 * 128] that ``mapped_av`` takes with
-    ``v_layout=V_TILED`` (then also pass ``k_rows`` = Tk)."""
+    operand order [H, n_key_blocks, 64 * 128] that ``mapped_av`` takes with
+    ``v_layout=V_TILED`` (then also pass ``k_rows`` = Tk). ``n_block_rows``: the
+    key blocks (``vl.n_key_blocks``; for whole prompts the block-rows)."""
     torch = _torch()
     lib = load_library()
     if v_layout == V_KEY_MAJOR:
@@ -424,6 +480,93 @@ def tile_v(v, vl: Varlen, n_block_rows, v_layout=V_TOKEN_MAJOR, out=None):
     _check(lib.cma_tile_v(_dev_ptr(v, "v"), v_layout, H, d, ctypes.byref(cvl), n_block_rows,
                           _dev_ptr(out, "out"), _stream()))
     return out
+
+
+def tile_v_paged(v, vl: Varlen, pages, table, v_layout=V_TOKEN_MAJOR):
+    """Write V's 64-key blocks into the pages of a paged V cache: key block c of
+    sequence s goes to page ``table[s, c]`` of ``pages`` ([H, n_pages, 64 * 128]
+    bf16), as ``mapped_av`` reads it with ``v_layout=V_PAGED``."""
+    lib = load_library()
+    if v_layout == V_KEY_MAJOR:
+        H, d, Tk = v.shape
+    else:
+        H, Tk, d = v.shape
+    torch = _torch()
+    if table.dim() != 2 or table.dtype != torch.int32 or table.shape[0] < vl.n_seqs:
+        raise ValueError("the page table must be int32 [n_seqs, stride]")
+    if pages.shape[0] < H or pages.shape[2] != BLOCK * d:
+        raise ValueError("pages must be [>= H, n_pages, 64 * d]")
+    _check_rows(vl, Tk, Tk)
+    pv = _CPagedV()
+    pv.pages = _dev_ptr(pages, "pages")
+    pv.page_table = _dev_ptr(table, "page table")
+    pv.page_stride = table.shape[1]
+    pv.n_pages = pages.shape[1]
+    cvl = vl.c(Tk, Tk)
+    _check(lib.cma_tile_v_paged(_dev_ptr(v, "v"), v_layout, H, d, ctypes.byref(cvl), ctypes.byref(pv), _stream()))
+    return pages
+
+
+def prefix_hashes(tokens, seed=0):
+    """Chain hashes (uint64) of the whole 64-token blocks of a token sequence."""
+    lib = load_library()
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = np.zeros(max(1, t.size // 64), dtype=np.uint64)
+    _check(lib.cma_prefix_hashes(t.ctypes.data, t.size, ctypes.c_uint64(seed & (2 ** 64 - 1)), out.ctypes.data))
+    return out[: t.size // 64]
+
+
+class PrefixIndex:
+    """Host-side prefix-hash index of cached block-rows (see cma.h): per (layer,
+    prefix hash), every sender head's (first block in the pool, block count)."""
+
+    def __init__(self, n_heads, capacity):
+        self.lib = load_library()
+        self.n_heads = int(n_heads)
+        self.h = self.lib.cma_prefix_index_create(self.n_heads, int(capacity))
+        if not self.h:
+            raise CmaError(CMA_EINVAL, "cma_prefix_index_create failed")
+
+    def close(self):
+        if self.h:
+            self.lib.cma_prefix_index_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.close()
+
+    def __len__(self):
+        return int(self.lib.cma_prefix_index_size(self.h))
+
+    def insert(self, layer, h, begin, count):
+        b = np.ascontiguousarray(begin, dtype=np.int32)
+        c = np.ascontiguousarray(count, dtype=np.int32)
+        if b.size != self.n_heads or c.size != self.n_heads:
+            raise ValueError(f"begin and count need {self.n_heads} entries")
+        return self.lib.cma_prefix_index_insert(self.h, int(layer), ctypes.c_uint64(int(h)), b.ctypes.data,
+                                                c.ctypes.data)
+
+    def lookup(self, layer, hashes):
+        """(hits, begin [hits, n_heads], count [hits, n_heads]) for the leading run of hits."""
+        hs = np.ascontiguousarray(hashes, dtype=np.uint64)
+        b = np.zeros((max(1, hs.size), self.n_heads), dtype=np.int32)
+        c = np.zeros_like(b)
+        n = self.lib.cma_prefix_index_lookup(self.h, int(layer), hs.ctypes.data, hs.size, b.ctypes.data, c.ctypes.data)
+        if n < 0:
+            raise CmaError(int(n), "cma_prefix_index_lookup failed")
+        return int(n), b[:n], c[:n]
+
+    def erase(self, layer, h):
+        return self.lib.cma_prefix_index_erase(self.h, int(layer), ctypes.c_uint64(int(h)))
+
+    def evict_lru(self):
+        """((layer, hash), begin, count) of the evicted entry, or None if empty."""
+        layer, h = ctypes.c_int32(0), ctypes.c_uint64(0)
+        b = np.zeros(self.n_heads, dtype=np.int32)
+        c = np.zeros_like(b)
+        r = self.lib.cma_prefix_index_evict_lru(self.h, ctypes.byref(layer), ctypes.byref(h), b.ctypes.data,
+                                                c.ctypes.data)
+        return ((int(layer.value), int(h.value)), b, c) if r == 1 else None
 
 
 def onehot_mix(argmax, n_send):

@@ -101,7 +101,7 @@ bool check_lengths_enabled() {
   return on;
 }
 
-int check_lengths_on_device(const cma_varlen* vl, bool need_k) {
+int check_lengths_on_device(const cma_varlen* vl, bool need_k, bool chunks) {
   const int n = vl->n_seqs;
   if (n == 0) return CMA_OK;
   std::vector<int32_t> cq(n + 1), ck(n + 1), uq, uk;
@@ -125,11 +125,16 @@ int check_lengths_on_device(const cma_varlen* vl, bool need_k) {
     if (lq > vl->max_seqlen_q || (need_k && lk > vl->max_seqlen_k))
       return fail(CMA_EINVAL, "sequence %d is longer (%lld / %lld) than max_seqlen_q / _k (%d / %d)", s,
                   (long long)lq, (long long)lk, vl->max_seqlen_q, vl->max_seqlen_k);
+    if (chunks && (lk < lq || (lk - lq) % kBlock))
+      return fail(CMA_EINVAL, "sequence %d: a block-sparse query chunk needs nk >= nq with nk - nq a multiple of %d",
+                  s, kBlock);
   }
   return CMA_OK;
 }
 
-int check_varlen(const cma_varlen* vl, bool need_k) {
+// chunks: block-sparse calls, whose sequences are whole prompts or prefill chunks
+// (nk >= nq, nk - nq a multiple of 64).
+int check_varlen(const cma_varlen* vl, bool need_k, bool chunks = false) {
   if (!vl) return fail(CMA_EINVAL, "varlen descriptor is NULL");
   if (vl->n_seqs < 0) return fail(CMA_EINVAL, "n_seqs < 0");
   if (vl->n_seqs > 0 && (!vl->cu_seqlens_q || (need_k && !vl->cu_seqlens_k)))
@@ -138,7 +143,7 @@ int check_varlen(const cma_varlen* vl, bool need_k) {
   if (vl->total_q < 0 || vl->total_k < 0) return fail(CMA_EINVAL, "negative total rows");
   if (vl->max_seqlen_q > vl->total_q || (need_k && vl->max_seqlen_k > vl->total_k))
     return fail(CMA_EINVAL, "max_seqlen exceeds the tensor rows");
-  if (check_lengths_enabled()) return check_lengths_on_device(vl, need_k);
+  if (check_lengths_enabled()) return check_lengths_on_device(vl, need_k, chunks);
   return CMA_OK;
 }
 
@@ -326,6 +331,18 @@ int64_t cma_bsr_max_blocks(int32_t n_heads, int32_t n_seqs, const int32_t* len_h
   return tot * n_heads;
 }
 
+int64_t cma_bsr_capacity(int32_t n_heads, int32_t n_seqs, const int32_t* len_q, const int32_t* len_k) {
+  if (n_heads < 0 || n_seqs < 0 || (n_seqs > 0 && !len_q)) return -1;
+  int64_t tot = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    const int64_t nq = len_q[s], nk = len_k ? len_k[s] : len_q[s];
+    if (nq < 0 || nk < nq) return -1;
+    const int64_t R = (nq + kBlock - 1) / kBlock, kb0 = (nk - nq) / kBlock;
+    tot += R * kb0 + R * (R + 1) / 2;
+  }
+  return tot * n_heads;
+}
+
 size_t cma_block_compress_workspace(int32_t n_heads, int32_t n_block_rows, int32_t max_seqlen,
                                     int64_t total_q) {
   (void)max_seqlen;
@@ -396,13 +413,13 @@ int block_compress_impl(const void* q, const void* k, cma_dtype in_dt, int32_t n
                         int32_t n_block_rows, int32_t* row_ptr, int32_t* col_idx, void* vals, int64_t capacity,
                         int32_t* nnz, float* block_mass, float* row_stats, void* workspace, size_t workspace_bytes,
                         void* stream, bool static_scratch) {
-  if (int e = check_varlen(vl, true)) return e;
+  if (int e = check_varlen(vl, true, true)) return e;
   if (in_dt != CMA_BF16) return fail(CMA_EUNSUPPORTED, "block_compress needs bf16 q and k");
   if (d != 64 && d != 128) return fail(CMA_EUNSUPPORTED, "block_compress supports d = 64 or 128 (got %d)", d);
   if (!(tau > 0.0f) || std::isnan(tau)) return fail(CMA_EINVAL, "tau must be > 0");
   if (n_heads < 0 || n_block_rows < 0 || capacity < 0) return fail(CMA_EINVAL, "negative size");
-  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
-    return fail(CMA_EUNSUPPORTED, "max_seqlen_q > %d", kMaxBlockRows * kBlock);
+  if (vl->max_seqlen_q > kMaxBlockRows * kBlock || vl->max_seqlen_k > kMaxBlockRows * kBlock)
+    return fail(CMA_EUNSUPPORTED, "sequences (queries and keys) are limited to %d tokens", kMaxBlockRows * kBlock);
   if (!row_ptr || !nnz) return fail(CMA_EINVAL, "NULL row_ptr or nnz");
   if (capacity > 0 && (!col_idx || !vals)) return fail(CMA_EINVAL, "NULL col_idx or vals");
   if (vals && !aligned16(vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
@@ -429,6 +446,7 @@ int block_compress_impl(const void* q, const void* k, cma_dtype in_dt, int32_t n
   a.n_heads = n_heads;
   a.n_block_rows = n_block_rows;
   a.nrb_max = (vl->max_seqlen_q + kBlock - 1) / kBlock;
+  a.ncb_max = (std::max(vl->max_seqlen_q, vl->max_seqlen_k) + kBlock - 1) / kBlock;
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.vals = static_cast<uint16_t*>(vals);
@@ -463,13 +481,73 @@ int block_compress_impl(const void* q, const void* k, cma_dtype in_dt, int32_t n
 
 extern "C" {
 
+}  // extern "C"
+
+namespace {
+int32_t key_blocks_of(const cma_maps_src* src) { return src->n_key_blocks > 0 ? src->n_key_blocks : src->n_block_rows; }
+
+// Checks shared by the block-sparse passes, and the source and V fields of `a`.
+// Needs a.n_v and a.vl set. For TOKEN_MAJOR / KEY_MAJOR V the tiled copy goes to
+// the workspace at `vt_ws` (the caller checks its size).
+int setup_bsr(MappedAvArgs& a, const cma_maps_src* src, const void* v, cma_v_layout v_layout, const cma_varlen* vl,
+              uint16_t* vt_ws) {
+  if (!src->row_ptr || !src->col_idx || !src->vals) return fail(CMA_EINVAL, "NULL block-sparse arrays");
+  if (vl->max_seqlen_q > kMaxBlockRows * kBlock || vl->max_seqlen_k > kMaxBlockRows * kBlock)
+    return fail(CMA_EUNSUPPORTED, "block-sparse passes support sequences up to %d tokens", kMaxBlockRows * kBlock);
+  if (!aligned16(src->vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
+  if (src->n_block_rows < 0 || src->n_key_blocks < 0) return fail(CMA_EINVAL, "negative n_block_rows or n_key_blocks");
+  if (vl->max_seqlen_q > 0 && src->n_block_rows == 0)
+    return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
+  if (vl->max_seqlen_q > vl->max_seqlen_k)
+    return fail(CMA_EINVAL, "block-sparse sequences have at least as many keys as queries (max_seqlen_q > max_seqlen_k)");
+  a.row_ptr = src->row_ptr;
+  a.row_end = src->row_end;
+  a.col_idx = src->col_idx;
+  a.vals = static_cast<const uint16_t*>(src->vals);
+  a.n_block_rows = src->n_block_rows;
+  a.n_key_blocks = key_blocks_of(src);
+  a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
+  if (v_layout == CMA_V_PAGED) {
+    const cma_paged_v* pv = static_cast<const cma_paged_v*>(v);
+    if (!pv->pages || !pv->page_table) return fail(CMA_EINVAL, "NULL pages or page_table in the paged V");
+    if (!aligned16(pv->pages)) return fail(CMA_EINVAL, "V pages must be 16-byte aligned");
+    if (pv->n_pages < 1 || pv->n_pages > kMaxVPages)
+      return fail(CMA_EUNSUPPORTED, "paged V supports 1 .. %d pages", kMaxVPages);
+    if ((int64_t)pv->page_stride * kBlock < vl->max_seqlen_k)
+      return fail(CMA_EINVAL, "page_stride (%d) holds fewer key blocks than the longest sequence", pv->page_stride);
+    a.vt = const_cast<uint16_t*>(static_cast<const uint16_t*>(pv->pages));
+    a.v_pages = pv->page_table;
+    a.v_page_stride = pv->page_stride;
+    a.v_n_pages = pv->n_pages;
+    a.v_tiled = true;
+  } else if (v_layout == CMA_V_TILED) {
+    if (!aligned16(v)) return fail(CMA_EINVAL, "tiled V must be 16-byte aligned");
+    a.vt = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
+    a.v_tiled = true;
+  } else {
+    if (!a.v_key_major && !aligned16(v)) return fail(CMA_EINVAL, "token-major V must be 16-byte aligned");
+    a.vt = vt_ws;
+  }
+  return CMA_OK;
+}
+
+bool v_layout_ok(cma_v_layout l) {
+  return l == CMA_V_TOKEN_MAJOR || l == CMA_V_KEY_MAJOR || l == CMA_V_TILED || l == CMA_V_PAGED;
+}
+size_t tiled_v_bytes(const cma_maps_src* src, int32_t n_v_heads, int32_t d) {
+  return (size_t)n_v_heads * key_blocks_of(src) * kBlock * d * sizeof(uint16_t);
+}
+}  // namespace
+
+extern "C" {
+
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout) {
   (void)total_k;
-  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || n_v_heads <= 0 || d <= 0 ||
-      src->n_block_rows <= 0)
+  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || v_layout == CMA_V_PAGED || n_v_heads <= 0 ||
+      d <= 0 || src->n_block_rows <= 0)
     return 0;
-  return (size_t)n_v_heads * src->n_block_rows * kBlock * d * sizeof(uint16_t);
+  return tiled_v_bytes(src, n_v_heads, d);
 }
 
 int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64_t M_seq_stride,
@@ -477,9 +555,8 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
                   int32_t d, const cma_varlen* vl, void* out, cma_dtype out_dt, void* workspace,
                   size_t workspace_bytes, void* stream) {
   if (!src) return fail(CMA_EINVAL, "NULL maps source");
-  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR && v_layout != CMA_V_TILED)
-    return fail(CMA_EINVAL, "bad V layout");
-  if (int e = check_varlen(vl, true)) return e;
+  if (!v_layout_ok(v_layout)) return fail(CMA_EINVAL, "bad V layout");
+  if (int e = check_varlen(vl, true, src->kind == CMA_SRC_BSR)) return e;
   if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
   if (n_send < 0 || n_recv < 0 || M_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
   if (n_v_heads < 1 || (n_recv > 0 && n_recv % n_v_heads != 0))
@@ -515,52 +592,38 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
     a.maps_bf16 = src->maps_dt == CMA_BF16;
     a.packed = src->layout == CMA_MAP_PACKED;
     a.head_stride = src->head_stride;
-    if (a.v_tiled) return fail(CMA_EUNSUPPORTED, "the tiled V layout serves block-sparse sources only");
+    if (a.v_tiled || v_layout == CMA_V_PAGED)
+      return fail(CMA_EUNSUPPORTED, "tiled and paged V serve block-sparse sources only");
     return hip_status(launch_mapped_av_dense(a, st), "mapped_av (dense) launch");
   }
   if (src->kind != CMA_SRC_BSR) return fail(CMA_EINVAL, "bad source kind");
   if (v_dt != CMA_BF16 || d != 128) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av needs bf16 V and d = 128");
   if (n_send > 32) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av supports n_send <= 32");
-  if (!src->row_ptr || !src->col_idx || !src->vals) return fail(CMA_EINVAL, "NULL block-sparse arrays");
-  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
-    return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av supports sequences up to %d tokens", kMaxBlockRows * kBlock);
-  if (!aligned16(src->vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
-  if (src->n_block_rows < 0) return fail(CMA_EINVAL, "negative n_block_rows");
-  if (vl->max_seqlen_q > vl->max_seqlen_k && vl->max_seqlen_k > 0)
-    return fail(CMA_EINVAL, "block-sparse maps are square: max_seqlen_q must not exceed max_seqlen_k");
-  a.row_ptr = src->row_ptr;
-  a.col_idx = src->col_idx;
-  a.vals = static_cast<const uint16_t*>(src->vals);
-  a.n_block_rows = src->n_block_rows;
-  if (vl->max_seqlen_q > 0 && src->n_block_rows == 0)
-    return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
-  if (a.v_tiled) {
-    if (!aligned16(v)) return fail(CMA_EINVAL, "tiled V must be 16-byte aligned");
-    a.vt = const_cast<uint16_t*>(static_cast<const uint16_t*>(v));
-  } else {
-    if (!a.v_key_major && !aligned16(v)) return fail(CMA_EINVAL, "token-major V must be 16-byte aligned");
-    const size_t need = (size_t)n_v_heads * src->n_block_rows * kBlock * d * sizeof(uint16_t);
+  const bool tiles = v_layout == CMA_V_TOKEN_MAJOR || v_layout == CMA_V_KEY_MAJOR;
+  if (tiles) {
+    const size_t need = tiled_v_bytes(src, n_v_heads, d);
     if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
     if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
-    a.vt = static_cast<uint16_t*>(workspace);
   }
+  if (int e = setup_bsr(a, src, v, v_layout, vl, static_cast<uint16_t*>(workspace))) return e;
   return hip_status(launch_mapped_av_bsr(a, st), "mapped_av (block-sparse) launch");
 }
 
-int cma_tile_v(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
-               int32_t n_block_rows, void* vt, void* stream) {
+namespace {
+int tile_v_common(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
+                  int32_t n_key_blocks, void* vt, const cma_paged_v* pv, void* stream) {
   if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR)
     return fail(CMA_EINVAL, "tile_v reads token-major or key-major V");
   if (int e = check_varlen(vl, true)) return e;
-  if (n_v_heads < 0 || n_block_rows < 0) return fail(CMA_EINVAL, "negative size");
+  if (n_v_heads < 0 || n_key_blocks < 0) return fail(CMA_EINVAL, "negative size");
   if (d != 128) return fail(CMA_EUNSUPPORTED, "tile_v supports d = 128");
-  if (n_v_heads == 0 || vl->n_seqs == 0 || vl->max_seqlen_q == 0) return CMA_OK;
-  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
+  if (n_v_heads == 0 || vl->n_seqs == 0 || vl->max_seqlen_k == 0) return CMA_OK;
+  if (vl->max_seqlen_k > kMaxBlockRows * kBlock)
     return fail(CMA_EUNSUPPORTED, "tile_v supports sequences up to %d tokens", kMaxBlockRows * kBlock);
-  if (n_block_rows == 0) return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
-  if (!v || !vt) return fail(CMA_EINVAL, "NULL v or vt");
+  if (!pv && n_key_blocks == 0) return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-key blocks");
+  if (!v || !vt) return fail(CMA_EINVAL, "NULL v or destination");
   if (!aligned16(vt) || (v_layout == CMA_V_TOKEN_MAJOR && !aligned16(v)))
-    return fail(CMA_EINVAL, "v (token-major) and vt must be 16-byte aligned");
+    return fail(CMA_EINVAL, "v (token-major) and the destination must be 16-byte aligned");
   MappedAvArgs a{};
   a.n_v = n_v_heads;
   a.d = d;
@@ -569,38 +632,64 @@ int cma_tile_v(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t 
   a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
   a.vl = to_varlen(vl);
   a.vt = static_cast<uint16_t*>(vt);
-  a.n_block_rows = n_block_rows;
+  a.n_key_blocks = n_key_blocks;
   a.max_q = vl->max_seqlen_q;
+  a.max_k = vl->max_seqlen_k;
+  if (pv) {
+    if (!pv->page_table) return fail(CMA_EINVAL, "NULL page_table");
+    if (pv->n_pages < 1 || pv->n_pages > kMaxVPages)
+      return fail(CMA_EUNSUPPORTED, "paged V supports 1 .. %d pages", kMaxVPages);
+    if ((int64_t)pv->page_stride * kBlock < vl->max_seqlen_k)
+      return fail(CMA_EINVAL, "page_stride (%d) holds fewer key blocks than the longest sequence", pv->page_stride);
+    a.v_pages = pv->page_table;
+    a.v_page_stride = pv->page_stride;
+    a.v_n_pages = pv->n_pages;
+  }
   return hip_status(launch_tile_v(a, static_cast<hipStream_t>(stream)), "tile_v launch");
 }
+}  // namespace
 
-// Workspace of the indexed path: [tiled V (unless V is tiled)][roff][order][pairs],
-// each part on a 256-byte boundary. The pair table holds at most
-// sum_s ceil(R_s / 2) <= (n_block_rows + n_seqs) / 2 items.
+int cma_tile_v(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
+               int32_t n_block_rows, void* vt, void* stream) {
+  return tile_v_common(v, v_layout, n_v_heads, d, vl, n_block_rows, vt, nullptr, stream);
+}
+
+int cma_tile_v_paged(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
+                     const cma_paged_v* dst, void* stream) {
+  if (!dst) return fail(CMA_EINVAL, "NULL paged V descriptor");
+  return tile_v_common(v, v_layout, n_v_heads, d, vl, 0, const_cast<void*>(dst->pages), dst, stream);
+}
+
+// Workspace of the indexed path: [tiled V (unless V is tiled or paged)][block-row
+// and key-block offsets][order][pairs], each part on a 256-byte boundary. The
+// pair table holds at most sum_s ceil(R_s / 2) <= (n_block_rows + n_seqs) / 2 items.
+}  // extern "C"
 namespace {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct IdxLayout {  // byte offsets into the workspace; the tiled V (if any) starts at 0
   size_t roff, order, pairs, total;
   int64_t cap;
 };
-IdxLayout idx_layout(int32_t n_block_rows, int32_t n_recv, int32_t n_v_heads, int32_t d, int32_t n_seqs,
-                     bool tiled) {
+IdxLayout idx_layout(const cma_maps_src* src, int32_t n_recv, int32_t n_v_heads, int32_t d, int32_t n_seqs,
+                     bool own_v) {
   IdxLayout l{};
-  l.cap = ((int64_t)n_block_rows + n_seqs) / 2 + 1;
-  l.roff = tiled ? 0 : round256((size_t)n_v_heads * n_block_rows * kBlock * d * sizeof(uint16_t));
-  l.order = l.roff + round256((size_t)n_seqs * sizeof(int32_t));
+  l.cap = ((int64_t)src->n_block_rows + n_seqs) / 2 + 1;
+  l.roff = own_v ? round256(tiled_v_bytes(src, n_v_heads, d)) : 0;
+  l.order = l.roff + round256((size_t)2 * n_seqs * sizeof(int32_t));
   l.pairs = l.order + round256((size_t)n_seqs * n_recv * sizeof(int32_t));
   l.total = l.pairs + round256((size_t)l.cap * sizeof(int32_t));
   return l;
 }
 }  // namespace
+extern "C" {
 
 size_t cma_mapped_av_indexed_workspace(const cma_maps_src* src, int32_t n_recv, int32_t n_v_heads, int32_t d,
                                        int32_t n_seqs, cma_v_layout v_layout) {
   if (!src || src->kind != CMA_SRC_BSR || n_recv <= 0 || n_v_heads <= 0 || d <= 0 || n_seqs <= 0 ||
-      src->n_block_rows < 0)
+      src->n_block_rows < 0 || src->n_key_blocks < 0)
     return 0;
-  return idx_layout(src->n_block_rows, n_recv, n_v_heads, d, n_seqs, v_layout == CMA_V_TILED).total;
+  const bool own_v = v_layout == CMA_V_TOKEN_MAJOR || v_layout == CMA_V_KEY_MAJOR;
+  return idx_layout(src, n_recv, n_v_heads, d, n_seqs, own_v).total;
 }
 
 int cma_mapped_av_indexed(const cma_maps_src* src, int32_t n_send, const int32_t* sender,
@@ -609,9 +698,8 @@ int cma_mapped_av_indexed(const cma_maps_src* src, int32_t n_send, const int32_t
                           cma_dtype out_dt, void* workspace, size_t workspace_bytes, void* stream) {
   if (!src) return fail(CMA_EINVAL, "NULL maps source");
   if (src->kind != CMA_SRC_BSR) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed reads block-sparse maps only");
-  if (v_layout != CMA_V_TOKEN_MAJOR && v_layout != CMA_V_KEY_MAJOR && v_layout != CMA_V_TILED)
-    return fail(CMA_EINVAL, "bad V layout");
-  if (int e = check_varlen(vl, true)) return e;
+  if (!v_layout_ok(v_layout)) return fail(CMA_EINVAL, "bad V layout");
+  if (int e = check_varlen(vl, true, true)) return e;
   if (!dtype_ok(v_dt) || !dtype_ok(out_dt)) return fail(CMA_EINVAL, "bad dtype");
   if (n_send < 0 || n_recv < 0 || sender_seq_stride < 0) return fail(CMA_EINVAL, "negative size");
   if (n_v_heads < 1 || (n_recv > 0 && n_recv % n_v_heads != 0))
@@ -622,21 +710,10 @@ int cma_mapped_av_indexed(const cma_maps_src* src, int32_t n_send, const int32_t
   if (n_recv > 256) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports n_recv <= 256");
   if (vl->n_seqs >= (1 << 24)) return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports fewer than 2^24 sequences");
   if (!sender || !v || !out) return fail(CMA_EINVAL, "NULL sender, v or out");
-  if (!src->row_ptr || !src->col_idx || !src->vals) return fail(CMA_EINVAL, "NULL block-sparse arrays");
-  if (vl->max_seqlen_q > kMaxBlockRows * kBlock)
-    return fail(CMA_EUNSUPPORTED, "mapped_av_indexed supports sequences up to %d tokens", kMaxBlockRows * kBlock);
-  if (!aligned16(src->vals)) return fail(CMA_EINVAL, "vals must be 16-byte aligned");
-  if (src->n_block_rows < 0) return fail(CMA_EINVAL, "negative n_block_rows");
-  if (vl->max_seqlen_q > 0 && src->n_block_rows == 0)
-    return fail(CMA_EINVAL, "n_block_rows must cover the sequences' 64-row blocks");
-  if (vl->max_seqlen_q > vl->max_seqlen_k && vl->max_seqlen_k > 0)
-    return fail(CMA_EINVAL, "block-sparse maps are square: max_seqlen_q must not exceed max_seqlen_k");
-  const bool tiled = v_layout == CMA_V_TILED;
-  const IdxLayout l = idx_layout(src->n_block_rows, n_recv, n_v_heads, d, vl->n_seqs, tiled);
+  const bool own_v = v_layout == CMA_V_TOKEN_MAJOR || v_layout == CMA_V_KEY_MAJOR;
+  const IdxLayout l = idx_layout(src, n_recv, n_v_heads, d, vl->n_seqs, own_v);
   if (!workspace || workspace_bytes < l.total) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", l.total);
   if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
-  if (tiled ? !aligned16(v) : (v_layout == CMA_V_TOKEN_MAJOR && !aligned16(v)))
-    return fail(CMA_EINVAL, "V must be 16-byte aligned");
   MappedAvArgs a{};
   a.n_send = n_send;
   a.n_recv = n_recv;
@@ -645,18 +722,13 @@ int cma_mapped_av_indexed(const cma_maps_src* src, int32_t n_send, const int32_t
   a.d = d;
   a.v = v;
   a.v_bf16 = true;
-  a.v_key_major = v_layout == CMA_V_KEY_MAJOR;
-  a.v_tiled = tiled;
   a.vl = to_varlen(vl);
   a.out = out;
   a.out_bf16 = out_dt == CMA_BF16;
   a.max_q = vl->max_seqlen_q;
-  a.row_ptr = src->row_ptr;
-  a.col_idx = src->col_idx;
-  a.vals = static_cast<const uint16_t*>(src->vals);
-  a.n_block_rows = src->n_block_rows;
+  a.max_k = vl->max_seqlen_k;
   char* ws = static_cast<char*>(workspace);
-  a.vt = tiled ? const_cast<uint16_t*>(static_cast<const uint16_t*>(v)) : reinterpret_cast<uint16_t*>(ws);
+  if (int e = setup_bsr(a, src, v, v_layout, vl, reinterpret_cast<uint16_t*>(ws))) return e;
   a.sender = sender;
   a.sender_stride = sender_seq_stride;
   a.plan_roff = reinterpret_cast<int32_t*>(ws + l.roff);

@@ -182,28 +182,38 @@ __device__ __forceinline__ int64_t map_seq_off(const Varlen& v, int s, bool pack
   for (; t < s; ++t) off += map_elems(seq_len_q(v, t), seq_len_k(v, t), packed);
   return off;
 }
-// Block-rows of earlier sequences, and packed lower-triangular block counts of
-// earlier sequences (for block statistics).
-__device__ __forceinline__ void block_offsets(const Varlen& v, int s, int32_t& roff, int64_t& tri_off) {
-  int32_t r = 0;
+// Block-sparse sequences may be prefill chunks: nq query rows at the end of nk
+// keys (bottom-right), with the block grid starting at the sequence's first
+// token, so nk - nq must be a multiple of 64; the chunk's block-row r is then
+// block-row kb0 + r of the grid and sees key blocks 0 .. kb0 + r. Returns kb0,
+// or -1 for a sequence that is not such a chunk (it then has no block-rows).
+__device__ __forceinline__ int chunk_kb0(int32_t nq, int32_t nk) {
+  return (nk >= nq && ((nk - nq) & (kBlock - 1)) == 0) ? (nk - nq) / kBlock : -1;
+}
+
+// Offsets of sequence s in the block-sparse arrays: query block-rows (roff) and
+// key blocks (kroff) of earlier sequences, and their block-mass entries (tri_off:
+// ceil(nq/64) kb0 + R(R+1)/2 each, the lower triangle for whole prompts).
+__device__ __forceinline__ void bsr_offsets(const Varlen& v, int s, int32_t& roff, int32_t& kroff, int64_t& tri_off) {
+  int32_t r = 0, kr = 0;
   int64_t t = 0;
   int u = 0;
-  for (; u + kSeqGroup <= s; u += kSeqGroup) {
-    int32_t nq[kSeqGroup];
-    seq_lens16(v.used_q, v.cu_q, u, nq);
-#pragma unroll
-    for (int e = 0; e < kSeqGroup; ++e) {
-      const int32_t R = (nq[e] + kBlock - 1) / kBlock;
-      r += R;
-      t += (int64_t)R * (R + 1) / 2;
-    }
-  }
-  for (; u < s; ++u) {
-    int32_t R = (seq_len_q(v, u) + kBlock - 1) / kBlock;
+  auto add = [&](int32_t nq, int32_t nk) {
+    const int32_t R = (nq + kBlock - 1) / kBlock, kb = max(chunk_kb0(nq, nk), 0);
     r += R;
-    t += (int64_t)R * (R + 1) / 2;
+    kr += (nk + kBlock - 1) / kBlock;
+    t += (int64_t)R * kb + (int64_t)R * (R + 1) / 2;
+  };
+  for (; u + kSeqGroup <= s; u += kSeqGroup) {
+    int32_t nq[kSeqGroup], nk[kSeqGroup];
+    seq_lens16(v.used_q, v.cu_q, u, nq);
+    seq_lens16(v.used_k, v.cu_k, u, nk);
+#pragma unroll
+    for (int e = 0; e < kSeqGroup; ++e) add(nq[e], nk[e]);
   }
+  for (; u < s; ++u) add(seq_len_q(v, u), seq_len_k(v, u));
   roff = r;
+  kroff = kr;
   tri_off = t;
 }
 

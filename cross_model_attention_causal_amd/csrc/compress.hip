@@ -74,7 +74,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   extern __shared__ __attribute__((aligned(16))) float dyn[];
   // row stride of LP: odd, so the 32 query rows written for one block fall in
   // distinct LDS banks
-  const int LPS = (a.nrb_max + 1) | 1;
+  const int LPS = (a.ncb_max + 1) | 1;
   uint8_t* stage = reinterpret_cast<uint8_t*>(dyn);
   float* LP = dyn + 2 * (kStageBytes / 4);
   __shared__ float sm[KP][64 * G], sl[KP][64 * G];
@@ -88,17 +88,22 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
 
   int h, s, rg;
   if (!group_item(blockIdx.x, (a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads, h, s, rg)) return;
-  const int32_t n = seq_len_q(a.vl, s);
+  // n query rows at the end of nk keys (a chunk; n = nk for a whole prompt):
+  // block-row r of the chunk is block-row kb0 + r of the sequence's grid
+  const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  const int kb0 = chunk_kb0(n, nk);
   const int nrb = (n + kBlock - 1) / kBlock, r0 = G * rg;
-  if (!seq_ok(a.vl, s, n, n) || r0 >= nrb) return;
+  if (!seq_ok(a.vl, s, n, nk) || kb0 < 0 || r0 >= nrb) return;
   const int r_last = min(r0 + G - 1, nrb - 1);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int qt = wave % QT, kp = wave / QT;
-  const int rq = r0 + qt / 2;                             // the tile's block-row
-  const int cmax = rq <= r_last ? rq : -1;                // last key block the tile computes
+  const int rq = kb0 + r0 + qt / 2;                       // the tile's block-row in the sequence's grid
+  const int c_last = kb0 + r_last;                        // last key block of the group
+  const int cmax = rq <= c_last ? rq : -1;                // last key block the tile computes
   const int qloc = 64 * (qt / 2) + 32 * (qt & 1) + (lane & 31);  // query within the group
-  const int i = 64 * r0 + qloc;
+  const int i = 64 * r0 + qloc;                           // query row within the chunk
   const bool valid = i < n;
+  const int ipos = 64 * kb0 + i;                          // its key position
   const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + min(i, n - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
   const float scale_l2 = ld_const(a.scale + h) * kLog2e;
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     if (raw_ok && c != 0 && c != rq) {
       part = online_update_raw(x, scale_l2, m, l);
     } else {
-      logits_inplace(x, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+      logits_inplace(x, 64 * c, valid ? ipos : -1, scale_l2, bias_l2);
       part = online_update_acc(x, m, l);
     }
     if (lane < 32) LP[qloc * LPS + c] = m + log2f_fast(part);
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   // Round k stages blocks 4k .. 4k + 3; the wave takes blocks 4k + kp + KP j.
   if constexpr (BPW == 1) {
     kstage_pipeline<D>(
-        stage, kseq, n, (r_last + 4) / 4, [&](int c) { return 64 * min(c, r_last); },
+        stage, kseq, nk, (c_last + 4) / 4, [&](int c) { return 64 * min(c, c_last); },
         [&](int k, const uint8_t* buf, auto fh) {
           constexpr int FH = decltype(fh)::value;
           const int c = 4 * k + kp;
@@ -157,8 +162,8 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
       }
       c_def = c <= cmax ? c : -1;
     };
-    const int nsub = (r_last + 2) / 2;
-    kstage2_pipeline<D>(stage, kseq, n, nsub, [&](int c) { return 64 * min(c, r_last); },
+    const int nsub = (c_last + 2) / 2;
+    kstage2_pipeline<D>(stage, kseq, nk, nsub, [&](int c) { return 64 * min(c, c_last); },
                         [&](int u, const uint8_t* buf) {
                           if (u & 1) sub(u, buf, std::integral_constant<int, 1>{});
                           else sub(u, buf, std::integral_constant<int, 0>{});
@@ -203,15 +208,15 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   float* wts = wts_a[gr];
   int* order = order_a[gr];
   uint32_t* kept = kept_a[gr];
-  int32_t roff;
+  int32_t roff, kroff;
   int64_t tri_off;
-  block_offsets(a.vl, s, roff, tri_off);
+  bsr_offsets(a.vl, s, roff, kroff, tri_off);
   __syncthreads();  // lse_s is written
   if (tl < kWords) kept[tl] = 0u;
   // mass_c over the valid rows: four consecutive threads take rows 16 part ..
   // + 15 of block c, then add their partials in a fixed order
   const int nrows = act ? min(64, n - 64 * r) : 0;
-  const int nb = act ? r + 1 : 0;
+  const int nb = act ? kb0 + r + 1 : 0;
   const float* LPr = LP + 64 * gr * LPS;
   const float* lser = lse_s + 64 * gr;
   for (int x0 = 0; x0 < 4 * nb; x0 += NTR) {
@@ -232,10 +237,10 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
 
   const int64_t g = (int64_t)h * a.n_block_rows + roff + r;
   if (act && a.block_mass) {
-    int32_t r_all;
+    int32_t r_all, kr_all;
     int64_t n_tri;  // blocks per head over all sequences
-    block_offsets(a.vl, a.vl.n_seqs, r_all, n_tri);
-    float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * (r + 1) / 2;
+    bsr_offsets(a.vl, a.vl.n_seqs, r_all, kr_all, n_tri);
+    float* bm = a.block_mass + (int64_t)h * n_tri + tri_off + (int64_t)r * kb0 + (int64_t)r * (r + 1) / 2;
     for (int c = tl; c < nb; c += NTR) bm[c] = mass[c];
   }
   if (a.tau >= 1.0f) {
@@ -395,14 +400,15 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   __shared__ int nu_s;
   int h, s, rg;
   if (!group_item(blockIdx.x, (a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads, h, s, rg)) return;
-  const int32_t n = seq_len_q(a.vl, s);
+  const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  const int kb0 = chunk_kb0(n, nk);  // the chunk's first block-row in the sequence's grid
   const int nrb = (n + kBlock - 1) / kBlock, r0 = G * rg;
-  if (!seq_ok(a.vl, s, n, n) || r0 >= nrb) return;
+  if (!seq_ok(a.vl, s, n, nk) || kb0 < 0 || r0 >= nrb) return;
   if ((int64_t)a.nnz[0] > a.capacity) return;
   const int r_last = min(r0 + G - 1, nrb - 1);
-  int32_t roff;
+  int32_t roff, kroff;
   int64_t tri_off;
-  block_offsets(a.vl, s, roff, tri_off);
+  bsr_offsets(a.vl, s, roff, kroff, tri_off);
   const int64_t g0 = (int64_t)h * a.n_block_rows + roff + r0;  // row r0; row r0 + 1 is g0 + 1
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   if (wave == 0) {
@@ -435,11 +441,13 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   const int nu = nu_s;
   if (nu == 0) return;
   const int qt = wave % QT, kp = wave / QT, gr = qt / 2;
-  const int rq = r0 + gr;                      // the tile's block-row
+  const int rq = r0 + gr;                      // the tile's block-row (in the chunk)
+  const int rq_abs = kb0 + rq;                 // and in the sequence's grid
   const bool tile_ok = rq <= r_last;
   const int iloc = 32 * (qt & 1) + (lane & 31);
   const int i = 64 * rq + iloc;
   const bool valid = tile_ok && i < n;
+  const int ipos = 64 * kb0 + i;               // the query's key position
   const int half = lane >> 5;
   const uint16_t* qrow = a.q + ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + min(i, n - 1)) * D;
   const uint16_t* kseq = a.k + ((int64_t)h * a.vl.total_k + cu_k_of(a.vl, s)) * D;
@@ -457,13 +465,13 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   };
   // p = 2^(logit - lse) in the accumulators (0 for rows past the end)
   auto finish = [&](f32x16 (&x)[2], int c) __attribute__((always_inline)) {
-    if (raw_ok && c != 0 && c != rq) {
+    if (raw_ok && c != 0 && c != rq_abs) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) x[kt][v] = exp2f_fast(fmaf(x[kt][v], scale_l2, -lse));
     } else {
-      logits_inplace(x, 64 * c, valid ? i : -1, scale_l2, bias_l2);
+      logits_inplace(x, 64 * c, valid ? ipos : -1, scale_l2, bias_l2);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(512) void k_block_extract(CompressArgs a) {
   };
   const int nsub = (nu + 1) / 2;
   kstage2_pipeline<D>(
-      stage, kseq, n, nsub, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
+      stage, kseq, nk, nsub, [&](int x) { return 64 * ucols[min(x, nu - 1)]; },
       [&](int u, const uint8_t* buf) {
         if (u & 1) sub(u, buf, std::integral_constant<int, 1>{});
         else sub(u, buf, std::integral_constant<int, 0>{});
@@ -568,9 +576,9 @@ template <int D>
 static hipError_t compress_impl(const CompressArgs& a, hipStream_t st) {
   // phase 1 takes two block-rows per workgroup when their per-(query, block)
   // table fits in LDS next to the K stages, else one
-  const bool two = a.nrb_max <= 128;
+  const bool two = a.ncb_max <= 128;
   const int G = two ? 2 : 1;
-  const int lps = (a.nrb_max + 1) | 1;
+  const int lps = (a.ncb_max + 1) | 1;
   const size_t lds = 2 * (size_t)kStageBytes + (size_t)64 * G * lps * sizeof(float);
   const dim3 grid(group_grid((a.nrb_max + G - 1) / G, a.vl.n_seqs, a.n_heads));
   const void* fn = two ? reinterpret_cast<const void*>(&k_block_stats<D, 2>)

@@ -60,7 +60,9 @@ struct CompressArgs {
   const float* scale;
   const float* bias;
   float tau;
-  int32_t n_heads, n_block_rows, nrb_max;
+  int32_t n_heads, n_block_rows;
+  int32_t nrb_max;  // block-rows of the longest query sequence (grid)
+  int32_t ncb_max;  // key blocks of the longest key sequence (<= kMaxBlockRows)
   int32_t* row_ptr;
   int32_t* col_idx;
   uint16_t* vals;
@@ -74,6 +76,7 @@ struct CompressArgs {
   float* lse2;         // [n_heads * total_q] log2-domain log-sum-exp per query row
 };
 constexpr int kMaxBlockRows = 256;  // sequences up to 16384 tokens
+constexpr int kMaxVPages = 65536;   // pages of a paged V head (byte offsets stay below 2^31)
 constexpr int kWords = kMaxBlockRows / 32;
 size_t compress_ws_bytes(int32_t n_heads, int32_t n_block_rows, int64_t total_q);
 hipError_t launch_compress(const CompressArgs& a, int d, hipStream_t st);
@@ -89,6 +92,12 @@ struct MappedAvArgs {
   const int32_t* col_idx;
   const uint16_t* vals;
   int32_t n_block_rows;
+  const int32_t* row_end;  // block-row g's blocks end at row_end[g] (NULL: row_ptr[g + 1])
+  int32_t n_key_blocks;    // tiled V blocks per head: sum over sequences of ceil(nk / 64)
+  // paged V: vt is the page pool [n_v][v_n_pages][64 * 128]; key block c of
+  // sequence s is page v_pages[s * v_page_stride + c]
+  const int32_t* v_pages;
+  int32_t v_page_stride, v_n_pages;
   int32_t n_send, n_recv, d;
   int32_t n_v, v_group;  // V heads; receiver head h reads V head h / v_group
   const float* M;
@@ -100,12 +109,12 @@ struct MappedAvArgs {
   Varlen vl;
   void* out;
   bool out_bf16;
-  uint16_t* vt;  // bsr path: tiled V [n_v][n_block_rows][64 * d] (v itself or the workspace)
+  uint16_t* vt;  // bsr path: tiled V [n_v][n_key_blocks][64 * d] (v itself or the workspace), or the page pool
   int32_t max_q, max_k;  // longest query / key sequence (host maxima)
   // indexed path (one sender per receiver head): sender[s * sender_stride + h]
   const int32_t* sender;
   int64_t sender_stride;
-  int32_t* plan_roff;   // [n_seqs]: first block-row of each sequence
+  int32_t* plan_roff;   // [2 n_seqs]: first block-row of each sequence, then its first key block
   int32_t* plan_order;  // [n_seqs * n_recv]: receiver heads of each sequence, ordered by sender
   int32_t* plan_pairs;  // [plan_cap]: (sequence << 7 | pair) of every work item, -1 past the end
   int64_t plan_cap;

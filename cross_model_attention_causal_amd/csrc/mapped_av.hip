@@ -57,19 +57,31 @@ constexpr uint16_t kNoBlock = 0xffff;
 // contiguous 1 KB MFMA operand, and the four operands of a panel are adjacent.
 __device__ __forceinline__ int vtile_pos(int ks, int dt, int lane) { return ((ks * 4 + dt) * 64 + lane) * 8; }
 
-// grid (nrb_max, n_seqs, n_v), 256 threads: one 64-key block of one V head.
+// grid (key blocks of the longest sequence, n_seqs, n_v), 256 threads: one 64-key
+// block of one V head, written to the sequence's tiled blocks (starting at its
+// key-block offset) or, with a page table, to the page the table names.
 template <bool KEY_MAJOR>
 __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, uint16_t* __restrict__ vtile,
-                                                Varlen vl, int32_t n_block_rows) {
+                                                Varlen vl, int32_t n_key_blocks, const int32_t* __restrict__ pages,
+                                                int32_t page_stride, int32_t n_pages) {
   constexpr int D = 128;
   __shared__ uint16_t tile[64][D + 8];
   const int c = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
-  const int32_t n = seq_len_q(vl, s), nk = seq_len_k(vl, s);
-  if (!seq_ok(vl, s, n, nk) || 64 * c >= n) return;
-  int32_t roff;
-  int64_t tri;
-  block_offsets(vl, s, roff, tri);
-  const int64_t k0 = cu_k_of(vl, s) + 64 * c;
+  const int32_t n = seq_len_k(vl, s);
+  const int64_t kbase = cu_k_of(vl, s);
+  if (n < 0 || kbase < 0 || kbase + n > vl.total_k || 64 * c >= n) return;
+  uint16_t* dst;
+  if (pages) {
+    const int32_t pg = ld_const(pages + (int64_t)s * page_stride + c);
+    if (pg < 0 || pg >= n_pages) return;
+    dst = vtile + ((int64_t)h * n_pages + pg) * (64 * D);
+  } else {
+    int32_t roff, kroff;
+    int64_t tri;
+    bsr_offsets(vl, s, roff, kroff, tri);
+    dst = vtile + ((int64_t)h * n_key_blocks + kroff + c) * (64 * D);
+  }
+  const int64_t k0 = kbase + 64 * c;
   const int valid = min(64, n - 64 * c);
   if (KEY_MAJOR) {
     // rows of 64 keys per feature: 8 lanes x 16 B per feature row
@@ -88,7 +100,6 @@ __global__ __launch_bounds__(256) void k_tile_v(const uint16_t* __restrict__ v, 
     }
   }
   __syncthreads();
-  uint16_t* dst = vtile + ((int64_t)h * n_block_rows + roff + c) * (64 * D);
   for (int x = threadIdx.x; x < 64 * D / 8; x += 256) {
     // x = (ks * 4 + dt) * 64 + lane
     const int lane = x & 63, kd = x >> 6, dt = kd & 3, ks = kd >> 2;
@@ -149,6 +160,15 @@ __device__ __forceinline__ int lds_u16(const uint16_t* p) {
                : "memory");
   return __builtin_amdgcn_readfirstlane((int)v);
 }
+__device__ __forceinline__ int lds_i32(const int* p) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n"
+               "s_waitcnt lgkmcnt(0)"
+               : "=v"(v)
+               : "v"(lds_addr(p))
+               : "memory");
+  return __builtin_amdgcn_readfirstlane((int)v);
+}
 
 // grid (8 * ceil(units / 8) * 2 * n_hg), kThreads threads.
 __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int n_pairs, int n_hg, int hpg) {
@@ -157,30 +177,37 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   __shared__ __attribute__((aligned(16))) uint16_t bbuf[2 * kBBuf];
   __shared__ uint16_t tbl[kMaxCols * kSend];  // block index - sender's first block, or kNoBlock
   __shared__ uint16_t ucol[kMaxCols];         // kept columns (any sender), ascending
+  __shared__ int upage[kMaxCols];             // V block (tiled or paged) of each kept column
   __shared__ int sbeg[kSend];
   __shared__ int nu_s;
   __shared__ uint8_t anyc[kMaxCols];
 
   int s, pr, rh, hg;
   if (!decode_item(blockIdx.x, a.vl.n_seqs, n_pairs, n_hg, s, pr, rh, hg)) return;
-  const int32_t n = seq_len_q(a.vl, s);
-  if (!seq_ok(a.vl, s, n, n)) return;
+  // n query rows at the end of nk keys (a prefill chunk; n = nk for a whole
+  // prompt): block-row r of the queries is block-row kb0 + r of the sequence
+  const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  const int kb0 = chunk_kb0(n, nk);
+  if (!seq_ok(a.vl, s, n, nk) || kb0 < 0) return;
   const int r_long = (n + kBlock - 1) / kBlock - 1 - pr;  // swept first, columns ascending
   if (r_long < pr) return;                                 // past this sequence's pairs
   const int n_pass = r_long > pr ? 2 : 1;                  // then row pr, columns descending
   // the wave index is uniform: keep it (and what is derived from it) in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  int32_t roff;
+  int32_t roff, kroff;
   int64_t tri;
-  block_offsets(a.vl, s, roff, tri);
+  bsr_offsets(a.vl, s, roff, kroff, tri);
+  const bool paged = a.v_pages != nullptr;
 
-  // Block table of block-row r: tbl[c][j] = kept block of sender j at column c,
-  // ucol = the union of kept columns in ascending order (nu_s of them), sbeg[j] =
-  // sender j's first block of the row.
+  // Block table of block-row r (key blocks 0 .. kb0 + r): tbl[c][j] = kept block
+  // of sender j at column c, ucol = the union of kept columns in ascending order
+  // (nu_s of them), upage = the V block of each, sbeg[j] = sender j's first block
+  // of the row.
   auto build_table = [&](int r) __attribute__((always_inline)) {
+    const int ra = kb0 + r;
     __syncthreads();  // the previous row's readers are done with these arrays
-    for (int x = tid; x < (r + 1) * kSend; x += kThreads) tbl[x] = kNoBlock;
-    for (int c = tid; c <= r; c += kThreads) anyc[c] = 0;
+    for (int x = tid; x < (ra + 1) * kSend; x += kThreads) tbl[x] = kNoBlock;
+    for (int c = tid; c <= ra; c += kThreads) anyc[c] = 0;
     if (tid < kSend) sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)tid * a.n_block_rows + roff + r] : 0;
     __syncthreads();
     {
@@ -188,10 +215,10 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       const int j = tid / kPer, e0 = tid % kPer;
       if (j < a.n_send) {
         const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
-        const int beg = a.row_ptr[g], end = a.row_ptr[g + 1];
+        const int beg = a.row_ptr[g], end = a.row_end ? a.row_end[g] : a.row_ptr[g + 1];
         for (int e = beg + e0; e < end; e += kPer) {
           const int c = a.col_idx[e];
-          if (c >= 0 && c <= r && e - beg < (int)kNoBlock) {
+          if (c >= 0 && c <= ra && e - beg < (int)kNoBlock) {
             tbl[c * kSend + j] = (uint16_t)(e - beg);
             anyc[c] = 1;
           }
@@ -201,14 +228,20 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     __syncthreads();
     if (wave == 0) {
       int base = 0;
-      for (int c0 = 0; c0 <= r; c0 += 64) {
+      for (int c0 = 0; c0 <= ra; c0 += 64) {
         const int c = c0 + lane;
-        const bool f = c <= r && anyc[c];
+        const bool f = c <= ra && anyc[c];
         const uint64_t m = __ballot(f);
         if (f) ucol[base + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)c;
         base += __popcll(m);
       }
       if (lane == 0) nu_s = base;
+    }
+    __syncthreads();
+    for (int x = tid; x < nu_s; x += kThreads) {
+      const int c = ucol[x];
+      // a page outside the pool (a broken table) is clamped into it: memory-safe
+      upage[x] = paged ? min(max(a.v_pages[(int64_t)s * a.v_page_stride + c], 0), a.v_n_pages - 1) : c;
     }
     __syncthreads();
   };
@@ -247,6 +280,8 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   bool rev = false;
   // k-th kept column of the row in sweep order
   auto col_at = [&](int k) __attribute__((always_inline)) { return lds_u16(&ucol[rev ? nu - 1 - k : k]); };
+  // its V block (offset in 64-key blocks from the V descriptor's base)
+  auto page_at = [&](int k) __attribute__((always_inline)) { return lds_i32(&upage[rev ? nu - 1 - k : k]); };
   const int q = lane >> 4, p = lane & 15, e4 = (lane >> 2) & 3, cc4 = lane & 3;
   const int n32 = lane & 31, q2 = lane >> 5;
   // Sources of this wave's senders for one block column: the stored block's rows
@@ -393,16 +428,17 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     const int sA = NI == 2 ? (w >> 1) : w, dA = NI == 2 ? 2 * (w & 1) : 0;
     const int sB = NI == 6 ? 8 + (w >> 1) : sA, dB = NI == 6 ? 2 * (w & 1) : 0;
     f32x16 acc[NI];
-    // tiled V of slots sA and sB (clamped to the group): this sequence's blocks
-    const int v_bytes = ((n + kBlock - 1) / kBlock) * (kBlock * D * 2);
-    const __amdgpu_buffer_rsrc_t vA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.vt + ((int64_t)((h_lo + min(sA, heads_here - 1)) / a.v_group) * a.n_block_rows + roff) *
-                                         (kBlock * D)),
-        (short)0, sA < heads_here ? v_bytes : 0, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vB = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(a.vt + ((int64_t)((h_lo + min(sB, heads_here - 1)) / a.v_group) * a.n_block_rows + roff) *
-                                         (kBlock * D)),
-        (short)0, sB < heads_here ? v_bytes : 0, kBufferFlags);
+    // V of slots sA and sB (clamped to the group): this sequence's tiled key
+    // blocks, or the V head's whole page pool (the column's page is the offset)
+    const int v_bytes = (paged ? a.v_n_pages : (nk + kBlock - 1) / kBlock) * (kBlock * D * 2);
+    auto v_base = [&](int slot) __attribute__((always_inline)) {
+      const int64_t g = (h_lo + min(slot, heads_here - 1)) / a.v_group;
+      return const_cast<uint16_t*>(a.vt + (paged ? g * a.v_n_pages : g * a.n_key_blocks + kroff) * (kBlock * D));
+    };
+    const __amdgpu_buffer_rsrc_t vA =
+        __builtin_amdgcn_make_buffer_rsrc(v_base(sA), (short)0, sA < heads_here ? v_bytes : 0, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vB =
+        __builtin_amdgcn_make_buffer_rsrc(v_base(sB), (short)0, sB < heads_here ? v_bytes : 0, kBufferFlags);
     // mixed-map operands of slots sA and sB: lane (row n32, half q2) holds keys
     // 8 q2 .. + 7, one contiguous 1 KB read each
     const uint32_t oA_lane = 2u * (sA * kBH + n32 * kKeysPerStep + 8 * q2);
@@ -460,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       if constexpr (I == 0) col_src(col_at((t + 4) >> 2), dsrc);
       load_stage(dsrc, I, S[I & 1]);
       compute((I + 1) & 1, (I + 1) & 1, true, I & 1, vr[I & 1]);
-      if constexpr (I == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
+      if constexpr (I == 2) v_off = page_at((t + 2) >> 2) * (kBlock * D);
       load_v((I + 2) & 3, vr[I & 1]);
       barrier_lds();
     };
@@ -474,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       }
       compute((I + 1) & 1, (I + 1) & 1, t + 1 < T, I & 1, vr[I & 1]);
       if (t + 2 < T) {
-        if (I == 2) v_off = col_at((t + 2) >> 2) * (kBlock * D);
+        if (I == 2) v_off = page_at((t + 2) >> 2) * (kBlock * D);
         load_v((I + 2) & 3, vr[I & 1]);
       }
       barrier_lds();
@@ -496,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
       // prologue (T >= 4, one column at least): panels 0 and 1 staged, panel 0
       // mixed, panels 2 and 3 in S[0] and S[1], V of panels 0 and 1 loaded
       col_src(col_at(0), dsrc);
-      v_off = col_at(0) * (kBlock * D);
+      v_off = page_at(0) * (kBlock * D);
       load_stage(dsrc, 0, S[0]);
       load_stage(dsrc, 1, S[1]);
       store_stage(S[0], 0);
@@ -592,7 +628,7 @@ __global__ __launch_bounds__(256) void k_idx_order(MappedAvArgs a) {
 // Block-row offsets of the sequences and the work-item table. One workgroup.
 constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void k_idx_plan(MappedAvArgs a) {
-  __shared__ int64_t wsum[kPlanThreads / 64][2];
+  __shared__ int64_t wsum[kPlanThreads / 64][3];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   for (int64_t x = t; x < a.plan_cap; x += kPlanThreads) a.plan_pairs[x] = -1;
   // exclusive scans of block-rows and pairs over the sequences, in chunks of
@@ -600,41 +636,55 @@ __global__ __launch_bounds__(kPlanThreads) void k_idx_plan(MappedAvArgs a) {
   const int ns = a.vl.n_seqs;
   const int chunk = (ns + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(ns, t * chunk), s1 = min(ns, s0 + chunk);
-  int64_t rows = 0, pairs = 0;
+  // block-rows (every sequence's, as the block-sparse layout counts them), key
+  // blocks, and work pairs (sequences that are whole prompts or valid chunks)
+  auto counts = [&](int s, int& nrb, int& nkb, int& np) {
+    const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+    nrb = (max(n, 0) + kBlock - 1) / kBlock;
+    nkb = (max(nk, 0) + kBlock - 1) / kBlock;
+    np = seq_ok(a.vl, s, n, nk) && chunk_kb0(n, nk) >= 0 ? (nrb + 1) / 2 : 0;
+  };
+  int64_t rows = 0, kblk = 0, pairs = 0;
   for (int s = s0; s < s1; ++s) {
-    const int32_t n = seq_len_q(a.vl, s);
-    const int nrb = seq_ok(a.vl, s, n, n) ? (n + kBlock - 1) / kBlock : 0;
+    int nrb, nkb, np;
+    counts(s, nrb, nkb, np);
     rows += nrb;
-    pairs += (nrb + 1) / 2;
+    kblk += nkb;
+    pairs += np;
   }
-  int64_t pr = rows, pp = pairs;
+  int64_t pr = rows, pk = kblk, pp = pairs;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int64_t yr = __shfl_up(pr, off, 64), yp = __shfl_up(pp, off, 64);
+    const int64_t yr = __shfl_up(pr, off, 64), yk = __shfl_up(pk, off, 64), yp = __shfl_up(pp, off, 64);
     if (lane >= off) {
       pr += yr;
+      pk += yk;
       pp += yp;
     }
   }
   if (lane == 63) {
     wsum[w][0] = pr;
-    wsum[w][1] = pp;
+    wsum[w][1] = pk;
+    wsum[w][2] = pp;
   }
   __syncthreads();  // also orders the -1 fill before the writes below
-  int64_t br = 0, bp = 0;
+  int64_t br = 0, bk = 0, bp = 0;
   for (int x = 0; x < w; ++x) {
     br += wsum[x][0];
-    bp += wsum[x][1];
+    bk += wsum[x][1];
+    bp += wsum[x][2];
   }
-  int64_t roff = br + pr - rows, poff = bp + pp - pairs;
+  int64_t roff = br + pr - rows, koff = bk + pk - kblk, poff = bp + pp - pairs;
   for (int s = s0; s < s1; ++s) {
-    const int32_t n = seq_len_q(a.vl, s);
-    const int nrb = seq_ok(a.vl, s, n, n) ? (n + kBlock - 1) / kBlock : 0;
+    int nrb, nkb, np;
+    counts(s, nrb, nkb, np);
     a.plan_roff[s] = (int32_t)roff;
-    for (int p = 0; p < (nrb + 1) / 2; ++p)
+    a.plan_roff[ns + s] = (int32_t)koff;
+    for (int p = 0; p < np; ++p)
       if (poff + p < a.plan_cap) a.plan_pairs[poff + p] = (s << 7) | p;
     roff += nrb;
-    poff += (nrb + 1) / 2;
+    koff += nkb;
+    poff += np;
   }
 }
 
@@ -648,8 +698,9 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
   const int code = ld_const(a.plan_pairs + item);
   if (code < 0) return;
   const int s = code >> 7, pr = code & 127;
-  const int32_t n = seq_len_q(a.vl, s);
-  if (!seq_ok(a.vl, s, n, n)) return;
+  const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  const int kb0 = chunk_kb0(n, nk);  // block-row r of the queries is block-row kb0 + r of the sequence
+  if (!seq_ok(a.vl, s, n, nk) || kb0 < 0) return;
   const int nrb = (n + kBlock - 1) / kBlock;
   const int r_long = nrb - 1 - pr;
   if (r_long < pr) return;
@@ -657,12 +708,16 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
   const int h = ld_const(a.plan_order + (int64_t)s * a.n_recv + hs);
   const int j = ld_const(a.sender + (int64_t)s * a.sender_stride + h);
   const bool j_ok = j >= 0 && j < a.n_send;
-  const int roff = ld_const(a.plan_roff + s);
+  const int roff = ld_const(a.plan_roff + s), kroff = ld_const(a.plan_roff + a.vl.n_seqs + s);
   const int64_t q0 = cu_q_of(a.vl, s);
-  // tiled V of this head's V head over this sequence's blocks
+  // V of this head's V head: the sequence's tiled key blocks, or the head's page
+  // pool (then a block's page is its offset)
+  const bool paged = a.v_pages != nullptr;
+  const int64_t vg = h / a.v_group;
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      a.vt + ((int64_t)(h / a.v_group) * a.n_block_rows + roff) * (kBlock * D), (short)0,
-      nrb * (kBlock * D * 2), kBufferFlags);
+      a.vt + (paged ? vg * a.v_n_pages : vg * a.n_key_blocks + kroff) * (kBlock * D), (short)0,
+      (paged ? a.v_n_pages : (nk + kBlock - 1) / kBlock) * (kBlock * D * 2), kBufferFlags);
+  const int32_t* vpg = paged ? a.v_pages + (int64_t)s * a.v_page_stride : nullptr;
   const uint32_t a_lane = 32u * (lane & 31) + 16u * (lane >> 5);  // A operand: row L % 32, keys 8 (L / 32) ..
   const uint32_t v_lane = 16u * lane;
 
@@ -682,7 +737,7 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
     if (j_ok) {
       const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
       beg = ld_const(a.row_ptr + g);
-      nb = ld_const(a.row_ptr + g + 1) - beg;
+      nb = (a.row_end ? ld_const(a.row_end + g) : ld_const(a.row_ptr + g + 1)) - beg;
     }
     if (nb > 0) {
       // Block k of the sweep (k = nb - 1 past the end): its stored index e and
@@ -704,7 +759,7 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
             kBufferFlags);
 #pragma unroll
         for (int u = 0; u < 2; ++u) S.x[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane + 1024u * u, 2048 * ks, 0);
-        const int vo = c * (kBlock * D * 2) + ks * 4096;
+        const int vo = c * (kBlock * D * 2) + ks * 4096;  // c: the column's V block (see vblk)
         const uint32_t vlo = v_lane | ((uint32_t)(1 - okv) << 31);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) S.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlo + 1024u * dt, vo, 0);
@@ -715,8 +770,14 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) acc[u][dt] = mfma32(as_bf16x8(S.x[u]), as_bf16x8(S.v[dt]), acc[u][dt]);
       };
+      // V block of column c: its page (clamped into the pool: memory-safe for a
+      // broken table), or c itself
+      const int nkb = (nk + kBlock - 1) / kBlock;
+      auto vblk = [&](int c) __attribute__((always_inline)) {
+        return paged ? min(max(ld_const(vpg + c), 0), a.v_n_pages - 1) : min(max(c, 0), nkb - 1);
+      };
       Set S0, S1, S2, S3;
-      int e_cur = blk(0), c_cur = ld_const(a.col_idx + e_cur);
+      int e_cur = blk(0), c_cur = vblk(ld_const(a.col_idx + e_cur));
       issue(0, e_cur, c_cur, 1, S0);
       __builtin_amdgcn_sched_barrier(0);
       issue(1, e_cur, c_cur, 1, S1);
@@ -729,7 +790,7 @@ __global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct
       // next block's column is read at the top of the trip, a step before use.
       for (int k = 0; k < nb; ++k) {
         const int e_nx = blk(k + 1), ok_nx = k + 1 < nb;
-        const int c_nx = ld_const(a.col_idx + e_nx);
+        const int c_nx = vblk(ld_const(a.col_idx + e_nx));
         issue(3, e_cur, c_cur, 1, S3);
         __builtin_amdgcn_sched_barrier(0);
         compute(S0);
@@ -970,16 +1031,16 @@ hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tile_v(const MappedAvArgs& a, hipStream_t st) {
-  if (a.n_v == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
-  const int nrb = (a.max_q + 63) / 64;
-  dim3 tg((unsigned)nrb, a.vl.n_seqs, a.n_v);  // each V head once
+  if (a.n_v == 0 || a.vl.n_seqs == 0 || a.max_k == 0) return hipSuccess;
+  const int nkb = (a.max_k + 63) / 64;
+  dim3 tg((unsigned)nkb, a.vl.n_seqs, a.n_v);  // each V head once
   KernelTimer kt_("k_tile_v", st);
   if (a.v_key_major)
     hipLaunchKernelGGL(k_tile_v<true>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl,
-                       a.n_block_rows);
+                       a.n_key_blocks, a.v_pages, a.v_page_stride, a.v_n_pages);
   else
     hipLaunchKernelGGL(k_tile_v<false>, tg, dim3(256), 0, st, reinterpret_cast<const uint16_t*>(a.v), a.vt, a.vl,
-                       a.n_block_rows);
+                       a.n_key_blocks, a.v_pages, a.v_page_stride, a.v_n_pages);
   return hipGetLastError();
 }
 

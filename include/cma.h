@@ -147,11 +147,18 @@ int cma_head_map_cosine(const void* recv, const void* send, cma_dtype dt, int32_
  * normalised by their sum, ordered largest first (ties: lower column) and the
  * shortest prefix whose running sum reaches `tau` is kept (tau >= 1 keeps all).
  * Phase 2 recomputes only the kept blocks and writes them as bf16.
- * Sequences are square (prefill): sequence s has n_s = used query rows; its
- * keys are rows cu_seqlens_k[s] .. + n_s. Blocks are laid out per sequence from
- * its first token; edge blocks are zero-padded.
+ * Sequence s has nq = used query rows and nk = used key rows (keys at rows
+ * cu_seqlens_k[s] ..). nq = nk is a whole prompt; nq < nk is a prefill chunk
+ * ([MapFlow] storage and execution, closing paragraph: chunked prefill): the
+ * nq queries are the last nq positions of the nk-token sequence (bottom-right
+ * alignment). Blocks are laid out per sequence from its first token, so nk - nq
+ * must be a multiple of 64: block-row r of the chunk is block-row kb0 + r of
+ * the sequence (kb0 = (nk - nq) / 64) and has blocks 0 .. kb0 + r; it equals
+ * that block-row of the whole prompt's compression. A sequence that breaks this
+ * rule gets no output rows (CMA_CHECK_LENGTHS=1 turns it into CMA_EINVAL). Edge
+ * blocks are zero-padded.
  * Outputs (block-sparse row format, BSR):
- *   row_ptr [n_heads * n_block_rows + 1] int32, n_block_rows = sum_s ceil(n_s/64);
+ *   row_ptr [n_heads * n_block_rows + 1] int32, n_block_rows = sum_s ceil(nq_s/64);
  *     global block-row g = h * n_block_rows + (block-rows of earlier sequences) + r;
  *   col_idx [capacity] int32, kept block columns (sequence-local), ascending per row;
  *   vals [capacity, 64, 64] bf16 blocks, zeros above the diagonal, each stored as
@@ -160,15 +167,21 @@ int cma_head_map_cosine(const void* recv, const void* send, cma_dtype dt, int32_
  *     is contiguous, which is how the fused pass reads it);
  *   nnz [1] int32: number of kept blocks. If nnz > capacity nothing is written to
  *     col_idx / vals (row_ptr and nnz still are): allocate nnz and call again.
- *     cma_bsr_max_blocks() is always enough.
- *   block_mass (optional) [n_heads, sum_s R_s(R_s+1)/2] fp32 masses, per sequence
- *     packed lower-triangular (offset + r(r+1)/2 + c);
+ *     cma_bsr_capacity() is always enough.
+ *   block_mass (optional) [n_heads, sum_s (R_s kb0_s + R_s(R_s+1)/2)] fp32 masses,
+ *     R_s = ceil(nq_s/64); block-row r of sequence s holds kb0_s + r + 1 masses from
+ *     offset_s + r kb0_s + r(r+1)/2 (packed lower-triangular for whole prompts);
  *   row_stats (optional) [n_heads, total_q, 2] fp32 (row max of the logits,
  *     sum of exp(logit - max)) at each query row.
- * Requires d in {64, 128}, max_seqlen_q <= 16384, tau > 0. Workspace:
+ * Requires d in {64, 128}, max_seqlen_q and max_seqlen_k <= 16384, tau > 0. Workspace:
  * cma_block_compress_workspace(...) bytes.
  */
 int64_t cma_bsr_max_blocks(int32_t n_heads, int32_t n_seqs, const int32_t* len_host);
+/* Blocks a compression can keep at most, prefill chunks included: n_heads * sum_s
+ * (R_s kb0_s + R_s(R_s+1)/2), R_s = ceil(nq_s/64), kb0_s = (nk_s - nq_s) / 64
+ * (len_q, len_k [host]; len_k NULL: whole prompts, as cma_bsr_max_blocks); -1 on
+ * bad arguments. */
+int64_t cma_bsr_capacity(int32_t n_heads, int32_t n_seqs, const int32_t* len_q, const int32_t* len_k);
 size_t cma_block_compress_workspace(int32_t n_heads, int32_t n_block_rows, int32_t max_seqlen,
                                     int64_t total_q);
 int cma_block_compress(const void* q, const void* k, cma_dtype in_dt, int32_t n_heads, int32_t d,
@@ -199,14 +212,33 @@ int cma_block_compress_noalloc(const void* q, const void* k, cma_dtype in_dt, in
 /* Layout of the receiver's V. TOKEN_MAJOR: [n_recv, total_k, d] (row t holds the
  * d values of key t). KEY_MAJOR: [n_recv, d, total_k] (row e holds feature e of
  * every key). TILED (block-sparse source, bf16, d = 128 only): the fused
- * kernel's operand order, [n_recv, n_block_rows, 64 * 128]: sequence s's keys in
- * 64-key blocks numbered like the block-sparse maps' block-rows (its first block
- * at the sum of ceil(len/64) over earlier sequences); within block c, element
+ * kernel's operand order, [n_recv, n_key_blocks, 64 * 128]: sequence s's nk_s
+ * keys in 64-key blocks, its first block at the sum of ceil(nk/64) over earlier
+ * sequences (n_key_blocks = that sum over all sequences; for whole prompts the
+ * same numbering as the block-sparse maps' block-rows); within block c, element
  *   ((ks * 4 + dt) * 64 + L) * 8 + e  =  V[key 64c + 16ks + 8(L/32) + e][feature 32dt + L%32]
  * for ks, dt in 0..3, L in 0..63, e in 0..7, zero past the sequence end. A V
  * projection can write it directly; cma_mapped_av builds it from the other two
- * layouts in its workspace. */
-typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1, CMA_V_TILED = 2 } cma_v_layout;
+ * layouts in its workspace.
+ * PAGED (block-sparse source, bf16, d = 128): V in a paged cache ([MapFlow]
+ * storage and execution, closing paragraph: PagedAttention): the `v` argument
+ * then points to a cma_paged_v descriptor in HOST memory. Each page holds one
+ * 64-key block of one V head in the TILED block order; the page table maps key
+ * block c of sequence s to a page. */
+typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1, CMA_V_TILED = 2, CMA_V_PAGED = 3 } cma_v_layout;
+
+/* Paged V (CMA_V_PAGED). pages: device [n_v_heads, n_pages, 64 * 128] bf16,
+ * 16-byte aligned (page p of V head g at (g * n_pages + p) * 8192 elements);
+ * page_table: device int32, key block c of sequence s in page
+ * page_table[s * page_stride + c] (c < ceil(nk_s / 64) <= page_stride), every
+ * entry in [0, n_pages); 1 <= n_pages <= 65536. Keys past a sequence's end
+ * inside its last page must be zero (cma_tile_v_paged writes them so). */
+typedef struct {
+  const void* pages;
+  const int32_t* page_table;
+  int32_t page_stride;
+  int32_t n_pages;
+} cma_paged_v;
 
 /*
  * cma_tile_v -- V in the TILED layout (see cma_v_layout) from TOKEN_MAJOR or
@@ -220,6 +252,17 @@ typedef enum { CMA_V_TOKEN_MAJOR = 0, CMA_V_KEY_MAJOR = 1, CMA_V_TILED = 2 } cma
 int cma_tile_v(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
                int32_t n_block_rows, void* vt, void* stream);
 
+/*
+ * cma_tile_v_paged -- as cma_tile_v, into the pages of a paged V cache: key
+ * block c of sequence s (its nk_s used keys) goes to page
+ * dst->page_table[s * dst->page_stride + c] of every V head (zeros past the
+ * sequence's end); pages the table does not name are left as they are. dst is a
+ * host descriptor whose `pages` the call writes. Returns EINVAL for a bad
+ * descriptor (the table's entries are trusted to lie in [0, n_pages)).
+ */
+int cma_tile_v_paged(const void* v, cma_v_layout v_layout, int32_t n_v_heads, int32_t d, const cma_varlen* vl,
+                     const cma_paged_v* dst, void* stream);
+
 /* Where cma_mapped_av reads the sender maps from. */
 typedef enum { CMA_SRC_DENSE = 0, CMA_SRC_BSR = 1 } cma_src_kind;
 typedef struct {
@@ -229,11 +272,20 @@ typedef struct {
   cma_dtype maps_dt;
   cma_map_layout layout;
   int64_t head_stride;
-  /* CMA_SRC_BSR: output of cma_block_compress (square sequences) */
+  /* CMA_SRC_BSR: output of cma_block_compress (whole prompts or prefill chunks).
+   * Block-row g's blocks are entries row_ptr[g] .. row_end[g] - 1 of col_idx and
+   * vals; row_end = NULL means row_ptr[g + 1] (the packed form cma_block_compress
+   * writes). With row_end, rows may sit anywhere in (and share) a pool of blocks,
+   * e.g. block-rows looked up in a prefix cache (cma_prefix_index_*) next to
+   * freshly compressed ones. */
   const int32_t* row_ptr;
   const int32_t* col_idx;
   const void* vals;
   int32_t n_block_rows;
+  const int32_t* row_end;
+  /* key blocks of all sequences, sum_s ceil(nk_s / 64) (the TILED V's block
+   * count); 0 means n_block_rows (whole prompts) */
+  int32_t n_key_blocks;
 } cma_maps_src;
 
 /*
@@ -249,11 +301,13 @@ typedef struct {
  * cma_v_layout, with n_v_heads in place of n_recv) and out [n_recv, total_q, d]
  * in v_dt / out_dt (bf16 or f32); accumulation is fp32. n_v_heads >= 1 must
  * divide n_recv. d in {64, 128}, 1 <= n_send <= 64 (dense) or <= 32 (BSR). A BSR
- * source needs bf16 V and d = 128; with TOKEN_MAJOR or KEY_MAJOR V it first
- * writes the TILED copy of V into `workspace` (cma_mapped_av_workspace(...)
- * bytes: n_v_heads * n_block_rows * 64 * d * 2), with TILED V it needs no
- * workspace and runs as a single kernel. A dense source takes TOKEN_MAJOR or
- * KEY_MAJOR V and needs no workspace.
+ * source needs bf16 V and d = 128; its sequences are whole prompts or prefill
+ * chunks as in cma_block_compress (out holds the chunk's nq rows; V its nk keys,
+ * nk <= 16384); with TOKEN_MAJOR or KEY_MAJOR V it first writes the TILED copy
+ * of V into `workspace` (cma_mapped_av_workspace(...) bytes: n_v_heads *
+ * n_key_blocks * 64 * d * 2), with TILED or PAGED V it needs no workspace and
+ * runs as a single kernel. A dense source takes TOKEN_MAJOR or KEY_MAJOR V and
+ * needs no workspace.
  */
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout);
@@ -271,15 +325,16 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
  * reading the other senders' maps. sender: int32 [*, n_recv] (device), sequence s
  * uses sender + s * sender_seq_stride (0: one row for all sequences), e.g. the
  * argmax of cma_head_map_cosine; an index outside [0, n_send) gives zero rows.
- * Source: BSR only (output of cma_block_compress); V bf16, d = 128, any
- * cma_v_layout (n_v_heads heads, n_v_heads >= 1 dividing n_recv); out
- * [n_recv, total_q, 128] bf16 or f32, fp32 accumulation. n_recv <= 256,
- * 1 <= n_send <= 256, max_seqlen_q <= 16384, n_seqs < 2^24. Each receiver head
- * reads only its sender's kept blocks. Workspace (device, 16-byte aligned):
+ * Source: BSR only (output of cma_block_compress; whole prompts or prefill
+ * chunks, optional row_end); V bf16, d = 128, any cma_v_layout (n_v_heads
+ * heads, n_v_heads >= 1 dividing n_recv); out [n_recv, total_q, 128] bf16 or
+ * f32, fp32 accumulation. n_recv <= 256, 1 <= n_send <= 256, max_seqlen_q and
+ * max_seqlen_k <= 16384, n_seqs < 2^24. Each receiver head reads only its
+ * sender's kept blocks. Workspace (device, 16-byte aligned):
  * cma_mapped_av_indexed_workspace(...) bytes, which hold the tiled copy of V
- * (unless v_layout is TILED), the heads ordered by sender per sequence and the
- * work-item table; n_block_rows must equal sum_s ceil(len_s / 64), as for every
- * BSR call.
+ * (unless v_layout is TILED or PAGED), each sequence's block-row and key-block
+ * offsets, the heads ordered by sender per sequence and the work-item table;
+ * n_block_rows must equal sum_s ceil(nq_s / 64), as for every BSR call.
  */
 size_t cma_mapped_av_indexed_workspace(const cma_maps_src* src, int32_t n_recv, int32_t n_v_heads, int32_t d,
                                        int32_t n_seqs, cma_v_layout v_layout);
@@ -320,6 +375,51 @@ int cma_mapped_layers(int32_t n_layers, double ratio, int32_t* out, int32_t cap)
  */
 int cma_mapping_plan(int32_t n, const int32_t* prompt_len, int32_t tau_e, int32_t tau_t,
                      int32_t* gen_before, int32_t* sim_len);
+
+/*
+ * Prefix-hash index of compressed sender states ([MapFlow] storage and execution,
+ * second component: the sender's block-sparse rows differ in number per layer and
+ * position; a prefix-hash index that carries the preceding context lets a
+ * receiver find the cached blocks it can reuse, and one sender state serves
+ * several downstream models). Host memory only; the block pool it points into
+ * (col_idx / vals of a block-sparse source) is the caller's.
+ *
+ * cma_prefix_hashes: chained hashes of the n_tokens / 64 whole 64-token blocks of
+ * a token sequence [host]: hash b = FNV-1a-64 over (hash b-1 as 8 little-endian
+ * bytes; `seed` for b = 0) followed by tokens 64b .. 64b + 63 (4 little-endian
+ * bytes each). Equal hashes b mean equal tokens 0 .. 64b + 63 (up to 64-bit
+ * collisions), i.e. the same causal context for block-row b. `seed` names what
+ * else the rows depend on (sender model and layer weights).
+ * cma_fnv1a64: the plain FNV-1a-64 of a byte string.
+ *
+ * cma_prefix_index_create(n_heads, capacity): an empty index of at most
+ * `capacity` entries, each holding n_heads (begin, count) pairs; NULL on bad
+ * arguments or allocation failure. destroy frees it.
+ * insert(layer, hash, begin[n_heads], count[n_heads]): caches one block-row (for
+ * every sender head, its blocks begin[h] .. begin[h] + count[h] - 1 of the pool);
+ * re-inserting a key replaces its entry; CMA_ENOSPC when full (evict first),
+ * CMA_EINVAL for a negative begin or count.
+ * lookup(layer, hashes[n], begin[n][n_heads], count[n][n_heads]): the number of
+ * leading hashes found (a request reuses block-rows 0 .. hits - 1), their entries
+ * copied out (begin / count may be NULL); refreshes their recency.
+ * erase: 1 if the key was present, 0 if not. evict_lru: removes the least
+ * recently used entry and returns 1 with its key and pairs (the caller frees that
+ * pool space), 0 if empty. size: entries held. All calls are thread-safe; a
+ * negative return is a status.
+ */
+typedef struct cma_prefix_index cma_prefix_index;
+int cma_prefix_hashes(const int32_t* tokens, int64_t n_tokens, uint64_t seed, uint64_t* hashes);
+uint64_t cma_fnv1a64(const void* data, size_t n_bytes);
+cma_prefix_index* cma_prefix_index_create(int32_t n_heads, int64_t capacity);
+void cma_prefix_index_destroy(cma_prefix_index* index);
+int cma_prefix_index_insert(cma_prefix_index* index, int32_t layer, uint64_t hash, const int32_t* begin,
+                            const int32_t* count);
+int64_t cma_prefix_index_lookup(cma_prefix_index* index, int32_t layer, const uint64_t* hashes, int64_t n,
+                                int32_t* begin, int32_t* count);
+int cma_prefix_index_erase(cma_prefix_index* index, int32_t layer, uint64_t hash);
+int cma_prefix_index_evict_lru(cma_prefix_index* index, int32_t* layer, uint64_t* hash, int32_t* begin,
+                               int32_t* count);
+int64_t cma_prefix_index_size(cma_prefix_index* index);
 
 #ifdef __cplusplus
 }

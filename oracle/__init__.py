@@ -32,10 +32,12 @@ from .compress import (BLOCK, block_masses, select_blocks, selection_margin, com
                        compress_block_row, block_compress, row_stats)
 from .mapped_av import dense_from_bsr_rows, mapped_av_dense, mapped_av_bsr_rows, mix_maps
 from .layers import mapped_layers, mapping_plan, onehot_mix
+from .prefix import fnv1a64, prefix_hashes, PrefixIndexModel
 
 __all__ = [
     "round_bf16", "round_f32", "causal_map", "attn_maps", "pack_rows", "packed_size",
     "seq_lengths", "cosine_matrix", "head_map", "BLOCK", "block_masses", "select_blocks",
     "selection_margin", "compress_head", "compress_block_row", "block_compress", "row_stats", "dense_from_bsr_rows",
     "mapped_av_dense", "mapped_av_bsr_rows", "mix_maps", "mapped_layers", "mapping_plan", "onehot_mix",
+    "fnv1a64", "prefix_hashes", "PrefixIndexModel",
 ]

@@ -89,15 +89,19 @@ def selection_margin(mass_row, tau):
 
 
 def row_stats(q, k, scale, bias):
-    """(m_i, l_i): row maximum of the logits and sum of exp(logit - m_i) (natural units)."""
+    """(m_i, l_i): row maximum of the logits and sum of exp(logit - m_i) (natural units).
+
+    Query row i sits at key position nk - nq + i (bottom-right alignment) and sees
+    keys 0 .. nk - nq + i.
+    """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
-    n = q.shape[0]
-    if n == 0:  # an empty sequence has no rows
+    nq, nk = q.shape[0], k.shape[0]
+    if nq == 0:  # an empty sequence has no rows
         return np.zeros(0), np.zeros(0)
     s = float(scale) * (q @ k.T)
     s[:, 0] += float(bias)
-    vis = np.tril(np.ones((n, n), dtype=bool))
+    vis = np.arange(nk)[None, :] <= (nk - nq + np.arange(nq))[:, None]
     s = np.where(vis, s, -np.inf)
     m = s.max(axis=1)
     l = np.exp(s - m[:, None]).sum(axis=1)
@@ -105,21 +109,32 @@ def row_stats(q, k, scale, bias):
 
 
 def compress_head(q, k, scale, bias, tau, block=BLOCK):
-    """Both phases for one head and one sequence (square causal map).
+    """Both phases for one head and one sequence.
 
-    Returns dict with ``masses`` [R, R], ``kept`` (list of column lists),
-    ``margins`` [R], ``blocks`` (list over rows of float64 bf16-rounded
-    ``[k_r, 64, 64]`` arrays) and ``m``, ``l`` row statistics.
+    The sequence has nk = len(k) keys and nq = len(q) <= nk query rows, the last
+    nq positions (a prefill chunk at the end of its context; nq = nk for a whole
+    prompt). The block grid starts at the sequence's first token, so nk - nq must
+    be a multiple of the block size: block-row r of the chunk is block-row
+    kb0 + r of the sequence (kb0 = (nk - nq) / 64) and has blocks c = 0 .. kb0 + r.
+
+    Returns dict with ``masses`` [R, C] (R = ceil(nq / 64) block-rows, C = ceil(nk
+    / 64) block columns; row r is meaningful up to column kb0 + r, zero after),
+    ``kept`` (list of column lists), ``margins`` [R], ``blocks`` (list over rows of
+    float64 bf16-rounded ``[k_r, 64, 64]`` arrays), ``m``, ``l`` row statistics and
+    ``kb0``.
     """
     A = causal_map(q, k, scale, bias)
-    n = A.shape[0]
-    R = (n + block - 1) // block
-    masses = block_masses(A, block)
+    nq, nk = A.shape
+    if (nk - nq) % block:
+        raise ValueError("a query chunk must start on a block boundary of its sequence")
+    kb0 = (nk - nq) // block
+    R = (nq + block - 1) // block
+    C = (nk + block - 1) // block
+    Ap = np.pad(A, ((0, R * block - nq), (0, C * block - nk)))
+    masses = Ap.reshape(R, block, C, block).sum(axis=(1, 3))
     kept, margins, blocks = [], np.zeros(R), []
-    pad = R * block - n
-    Ap = np.pad(A, ((0, pad), (0, pad)))
     for r in range(R):
-        row = masses[r, : r + 1]
+        row = masses[r, : kb0 + r + 1]
         cols = select_blocks(row, tau)
         kept.append(cols)
         margins[r] = selection_margin(row, tau)
@@ -129,7 +144,7 @@ def compress_head(q, k, scale, bias, tau, block=BLOCK):
         else:
             blocks.append(np.zeros((0, block, block)))
     m, l = row_stats(q, k, scale, bias)
-    return dict(masses=masses, kept=kept, margins=margins, blocks=blocks, m=m, l=l, n=n, R=R)
+    return dict(masses=masses, kept=kept, margins=margins, blocks=blocks, m=m, l=l, n=nq, R=R, kb0=kb0)
 
 
 def compress_block_row(q, k, scale, bias, r, tau, block=BLOCK):
@@ -167,27 +182,32 @@ def compress_block_row(q, k, scale, bias, r, tau, block=BLOCK):
 
 
 def block_compress(q, k, scale, bias, cu, tau, used=None, block=BLOCK, heads=None,
-                   keep_values=True, cu_k=None):
+                   keep_values=True, cu_k=None, used_k=None):
     """Whole compression over heads and packed sequences, in the library's layout.
 
     Sequence s uses query rows ``cu[s] ..`` and key rows ``cu_k[s] ..`` (``cu_k``
-    defaults to ``cu``), ``used[s]`` tokens of each (default: the ``cu`` spacing).
+    defaults to ``cu``), ``used[s]`` queries (default: the ``cu`` spacing) and
+    ``used_k[s]`` keys (default: as many as queries); with more keys than queries
+    the queries are a chunk at the end of the sequence (``compress_head``).
 
     Returns dict with:
     * ``row_ptr`` [H * R_tot + 1] int64, ``col_idx`` [nnz], ``vals`` [nnz, 64, 64]
       float64 (bf16-rounded) when ``keep_values``;
-    * ``masses`` [H, NB_tot] packed lower-triangular per sequence (index
-      offset_s + r(r+1)/2 + c), ``row_stats`` [H, T, 2] (m, l) at each token;
+    * ``masses`` [H, NB_tot]: per sequence, block-row r's kb0 + r + 1 masses at
+      offset_s + r kb0 + r(r+1)/2 (lower-triangular for whole prompts),
+      ``row_stats`` [H, T, 2] (m, l) at each query row;
     * ``margins`` [H * R_tot] selection margins; ``kept`` flat list of column lists.
     """
     lens = seq_lengths(cu, used)
+    lens_k = list(lens) if used_k is None else [int(x) for x in used_k]
     cu = np.asarray(cu, dtype=np.int64)
     cu_k = cu if cu_k is None else np.asarray(cu_k, dtype=np.int64)
     hs = list(range(q.shape[0])) if heads is None else list(heads)
     bias = np.zeros(q.shape[0]) if bias is None else bias
     Rs = [(n + block - 1) // block for n in lens]
+    kb0s = [(nk - n) // block for n, nk in zip(lens, lens_k)]
     r_tot = sum(Rs)
-    nb_tot = sum(R * (R + 1) // 2 for R in Rs)
+    nb_tot = sum(R * kb + R * (R + 1) // 2 for R, kb in zip(Rs, kb0s))
     T = int(q.shape[1])
     masses = np.zeros((len(hs), nb_tot))
     stats = np.zeros((len(hs), T, 2))
@@ -196,17 +216,18 @@ def block_compress(q, k, scale, bias, cu, tau, used=None, block=BLOCK, heads=Non
         off = 0
         for s, n in enumerate(lens):
             qs = q[h, cu[s]: cu[s] + n]
-            ks = k[h, cu_k[s]: cu_k[s] + n]
+            ks = k[h, cu_k[s]: cu_k[s] + lens_k[s]]
             res = compress_head(qs, ks, scale[h], bias[h], tau, block)
-            R = Rs[s]
+            R, kb = Rs[s], kb0s[s]
             for r in range(R):
-                masses[hi, off + r * (r + 1) // 2: off + r * (r + 1) // 2 + r + 1] = res["masses"][r, : r + 1]
+                o = off + r * kb + r * (r + 1) // 2
+                masses[hi, o: o + kb + r + 1] = res["masses"][r, : kb + r + 1]
                 counts.append(len(res["kept"][r]))
                 kept_all.append(res["kept"][r])
                 margins.append(res["margins"][r])
                 if keep_values and len(res["kept"][r]):
                     vals.append(res["blocks"][r])
-            off += R * (R + 1) // 2
+            off += R * kb + R * (R + 1) // 2
             stats[hi, cu[s]: cu[s] + n, 0] = res["m"]
             stats[hi, cu[s]: cu[s] + n, 1] = res["l"]
     row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
@@ -214,7 +235,7 @@ def block_compress(q, k, scale, bias, cu, tau, used=None, block=BLOCK, heads=Non
     col_idx = np.array([c for cols in kept_all for c in cols], dtype=np.int64)
     out = dict(row_ptr=row_ptr, col_idx=col_idx, masses=masses, row_stats=stats,
                margins=np.array(margins), kept=kept_all, r_tot=r_tot, nb_tot=nb_tot,
-               lengths=lens, nnz=int(row_ptr[-1]))
+               lengths=lens, lengths_k=lens_k, nnz=int(row_ptr[-1]))
     if keep_values:
         out["vals"] = np.concatenate(vals) if vals else np.zeros((0, block, block))
     return out

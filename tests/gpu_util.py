@@ -82,12 +82,14 @@ def tile_v(V, lens, cu):
     return out
 
 
-def greedy_mismatches(mass_packed, row_ptr, col, R_list, tau, head_off=0, min_margin=1e-6):
+def greedy_mismatches(mass_packed, row_ptr, col, R_list, tau, head_off=0, min_margin=1e-6, kb0_list=None):
     """Selection validity on every block-row, from the library's own masses.
 
     ``mass_packed``: one head's masses over its sequences, each packed
     lower-triangular (offset + r(r+1)/2 + c); ``R_list``: block-rows per sequence;
-    ``head_off``: index of the head's first block-row in ``row_ptr``. For every
+    ``head_off``: index of the head's first block-row in ``row_ptr``; ``kb0_list``:
+    per sequence, the first block-row of a prefill chunk (its block-row r holds
+    kb0 + r + 1 masses from r kb0 + r(r+1)/2; default 0, whole prompts). For every
     block-row the greedy shortest prefix (weight descending, ties to the lower
     column, running sum >= tau) is recomputed in float64 from those masses and
     compared with the kept columns the library returned. Returns (rows compared,
@@ -97,9 +99,11 @@ def greedy_mismatches(mass_packed, row_ptr, col, R_list, tau, head_off=0, min_ma
     import oracle
     bad, skipped, n = [], 0, 0
     off, g = 0, head_off
-    for R in R_list:
+    kb0_list = kb0_list or [0] * len(R_list)
+    for R, kb in zip(R_list, kb0_list):
         for r in range(R):
-            mrow = np.asarray(mass_packed[off + r * (r + 1) // 2: off + r * (r + 1) // 2 + r + 1], dtype=np.float64)
+            o = off + r * kb + r * (r + 1) // 2
+            mrow = np.asarray(mass_packed[o: o + kb + r + 1], dtype=np.float64)
             kept = [int(c) for c in col[row_ptr[g]: row_ptr[g + 1]]]
             n += 1
             if mrow.sum() > 0:
@@ -110,5 +114,5 @@ def greedy_mismatches(mass_packed, row_ptr, col, R_list, tau, head_off=0, min_ma
                     else:
                         skipped += 1
             g += 1
-        off += R * (R + 1) // 2
+        off += R * kb + R * (R + 1) // 2
     return n, bad, skipped

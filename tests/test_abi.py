@@ -306,3 +306,19 @@ def test_noalloc_compress_rejects_oversized_scratch(lib):
             None, None, None)
     assert rc == -3
     assert b"scratch" in lib.cma_last_error()
+
+
+def test_bsr_capacity_counts_chunk_blocks(lib):
+    """cma_bsr_capacity: every block a compression can keep, prefill chunks included
+    (block-row r of a chunk starting at block-row kb0 has kb0 + r + 1 blocks)."""
+    lib.cma_bsr_capacity.restype = ctypes.c_int64
+    lib.cma_bsr_capacity.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lq = np.array([448, 70, 128, 0], dtype=np.int32)
+    lk = np.array([576, 198, 128, 64], dtype=np.int32)
+    want = sum(len(oracle.select_blocks(np.ones(((b - a) // 64) + r + 1), 1.0))
+               for a, b in zip(lq, lk) for r in range((int(a) + 63) // 64))
+    assert lib.cma_bsr_capacity(3, 4, lq.ctypes.data, lk.ctypes.data) == 3 * want
+    lib.cma_bsr_max_blocks.restype = ctypes.c_int64
+    lib.cma_bsr_max_blocks.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.cma_bsr_capacity(2, 4, lq.ctypes.data, None) == lib.cma_bsr_max_blocks(2, 4, lq.ctypes.data)
+    assert lib.cma_bsr_capacity(2, 1, lk.ctypes.data, lq.ctypes.data) == -1  # fewer keys than queries

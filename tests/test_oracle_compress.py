@@ -198,3 +198,59 @@ def test_block_row_uniform_closed_form():
     np.testing.assert_allclose(one["masses"][:r], off, rtol=1e-13)
     np.testing.assert_allclose(one["masses"][r], diag, rtol=1e-13)
     assert one["kept"] == list(range(r + 1))
+
+
+@pytest.mark.parametrize("n,kb0,tau", [(300, 2, 0.9), (256, 3, 0.95), (70, 1, 1.0)])
+def test_chunk_equals_rows_of_whole_prompt(n, kb0, tau):
+    """A prefill chunk (the last n - 64 kb0 queries against all n keys) compresses to
+    exactly the block-rows kb0 .. of the whole prompt's compression: the same
+    masses, kept sets, blocks and row statistics (the map rows are the same rows of
+    one causal softmax)."""
+    rng = np.random.default_rng(n + kb0)
+    q = rng.standard_normal((n, 16))
+    k = rng.standard_normal((n, 16))
+    whole = oracle.compress_head(q, k, 0.6, 3.0, tau)
+    chunk = oracle.compress_head(q[64 * kb0:], k, 0.6, 3.0, tau)
+    assert chunk["kb0"] == kb0 and chunk["R"] == whole["R"] - kb0
+    for r in range(chunk["R"]):
+        ra = kb0 + r
+        np.testing.assert_allclose(chunk["masses"][r, : ra + 1], whole["masses"][ra, : ra + 1], rtol=1e-12,
+                                   atol=1e-15)
+        assert not chunk["masses"][r, ra + 1:].any()
+        if whole["margins"][ra] > 1e-9:
+            assert chunk["kept"][r] == whole["kept"][ra]
+            np.testing.assert_allclose(chunk["blocks"][r], whole["blocks"][ra], rtol=2 ** -8, atol=0)
+    np.testing.assert_allclose(chunk["m"], whole["m"][64 * kb0:], rtol=1e-12)
+    np.testing.assert_allclose(chunk["l"], whole["l"][64 * kb0:], rtol=1e-12)
+    with pytest.raises(ValueError):  # a chunk must start on a block boundary
+        oracle.compress_head(q[64 * kb0 + 1:], k, 0.6, 3.0, tau)
+
+
+def test_block_compress_layout_with_chunks():
+    """Varlen layout with chunked sequences: row pointers, masses at offset
+    r kb0 + r(r+1)/2 per sequence, and per-sequence results equal to compress_head."""
+    rng = np.random.default_rng(3)
+    lq, lk = [70, 128, 5], [198, 128, 69]
+    H = 2
+    cu_q = np.concatenate([[0], np.cumsum(lq)])
+    cu_k = np.concatenate([[0], np.cumsum(lk)])
+    q = rng.standard_normal((H, int(cu_q[-1]), 16))
+    k = rng.standard_normal((H, int(cu_k[-1]), 16))
+    scale, bias = np.array([0.5, 0.8]), np.array([2.0, 0.0])
+    out = oracle.block_compress(q, k, scale, bias, cu_q, 0.85, cu_k=cu_k, used_k=lk)
+    R = [(n + 63) // 64 for n in lq]
+    kb = [(b - a) // 64 for a, b in zip(lq, lk)]
+    assert out["nb_tot"] == sum(r * x + r * (r + 1) // 2 for r, x in zip(R, kb))
+    g = 0
+    for h in range(H):
+        off = 0
+        for s in range(3):
+            res = oracle.compress_head(q[h, cu_q[s]: cu_q[s + 1]], k[h, cu_k[s]: cu_k[s + 1]], scale[h], bias[h], 0.85)
+            for r in range(R[s]):
+                o = off + r * kb[s] + r * (r + 1) // 2
+                assert np.array_equal(out["masses"][h, o: o + kb[s] + r + 1], res["masses"][r, : kb[s] + r + 1])
+                assert out["kept"][g] == res["kept"][r]
+                assert list(out["col_idx"][out["row_ptr"][g]: out["row_ptr"][g + 1]]) == res["kept"][r]
+                g += 1
+            off += R[s] * kb[s] + R[s] * (R[s] + 1) // 2
+    assert g == H * sum(R)

@@ -124,3 +124,42 @@ def test_layer_order_properties():
     assert len(full) == 64 and min(full) == 16 and len(set(full)) == 64
     assert oracle.mapped_layers(80, 0.0) == []
     assert oracle.mapped_layers(40, 0.5) == list(range(39, 31, -1)) + list(range(8, 20))
+
+
+def test_chunk_rows_equal_whole_prompt_rows():
+    """mapped_av over a chunk's block-rows (queries at the end of a longer key span)
+    equals the same rows of the whole prompt's pass; a BSR whose rows are listed by
+    (begin, end) pairs out of order gives the same result as the packed one."""
+    rng = np.random.default_rng(11)
+    n, kb0, Hs, Hr = 200, 2, 3, 2
+    q = rng.standard_normal((Hs, n, 16))
+    k = rng.standard_normal((Hs, n, 16))
+    sc, bi = np.array([0.5, 0.7, 0.9]), np.zeros(Hs)
+    whole = oracle.block_compress(q, k, sc, bi, np.array([0, n]), 0.9)
+    chunk = oracle.block_compress(q[:, 64 * kb0:], k, sc, bi, np.array([0, n - 64 * kb0]), 0.9,
+                                  cu_k=np.array([0, n]), used_k=[n])
+    M = rng.standard_normal((1, Hr, Hs))
+    V = rng.standard_normal((Hr, n, 8))
+    R = (n + 63) // 64
+    ow = oracle.mapped_av_bsr_rows(whole["row_ptr"], whole["col_idx"], whole["vals"], Hs, [n], M, V,
+                                   np.array([0]), [(0, r) for r in range(R)])
+    oc = oracle.mapped_av_bsr_rows(chunk["row_ptr"], chunk["col_idx"], chunk["vals"], Hs, [n - 64 * kb0], M, V,
+                                   np.array([0]), [(0, r) for r in range(R - kb0)], lengths_k=[n])
+    for r in range(R - kb0):
+        if all(whole["margins"][j * R + kb0 + r] > 1e-9 for j in range(Hs)):
+            np.testing.assert_allclose(oc[(0, r)], ow[(0, kb0 + r)], rtol=1e-12, atol=1e-12)
+    # rows given by (begin, end), stored in reverse order
+    rp = chunk["row_ptr"]
+    order = list(range(len(rp) - 1))[::-1]
+    beg, end, cols, vals = np.zeros(len(order), np.int64), np.zeros(len(order), np.int64), [], []
+    pos = 0
+    for g in order:
+        a, b = int(rp[g]), int(rp[g + 1])
+        beg[g], end[g] = pos, pos + b - a
+        cols.extend(chunk["col_idx"][a:b])
+        vals.append(chunk["vals"][a:b])
+        pos += b - a
+    ob = oracle.mapped_av_bsr_rows(np.append(beg, 0), np.array(cols), np.concatenate(vals), Hs, [n - 64 * kb0], M,
+                                   V, np.array([0]), [(0, r) for r in range(R - kb0)], lengths_k=[n], row_end=end)
+    for key in oc:
+        assert np.array_equal(ob[key], oc[key])
