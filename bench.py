@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--ctx", type=int, default=8192)
     ap.add_argument("--tau", type=float, default=0.95)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the single-sequence headline figures (H1: fused mapped x V, H2: block "
+                         "compression, each on one 8192-token sequence)")
     ap.add_argument("--no-check", action="store_true",
                     help="skip the check of the last step's outputs (sampled fused-pass rows, the decode "
                          "rows and prompt 0's head map) against the oracle")
@@ -55,6 +58,9 @@ def parse():
                     help="instead of the step: time each stage at its own workload (512-token head "
                          "mapping; 32-head x 8192-token compression; the fused pass over it) and print "
                          "one JSON line per workload with every kernel's roofline fraction")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only run the ceiling probes (HBM read and copy, 32x32x16 bf16 MFMA rate, L2 -> CU "
+                         "read bandwidth) and print one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (for scaling hardware byte counters)")
     return ap.parse_args()
@@ -73,6 +79,60 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                       "launches": 5}), flush=True)
+
+
+def peaks(reps=5):
+    """The chip's ceilings as the library's probes measure them (cma_probe.h): median
+    of ``reps`` launches each, timed with HIP events on the current stream."""
+    import ctypes
+    import torch
+    import cross_model_attention_causal_amd as cma
+
+    lib = cma.load_library()
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.cma_probe_read.argtypes = [P, I64, I32, P, P]
+    lib.cma_probe_copy.argtypes = [P, P, I64, I32, P]
+    lib.cma_probe_mfma.argtypes = [I32, I32, P, P]
+    lib.cma_probe_l2.argtypes = [P, I32, I32, I32, P, P]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert fn() == 0
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    out = {"probe": "ceilings", "compute_units": cus, "reps": reps}
+    big = 4 << 30
+    a = torch.ones(big // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(cus * 8 * 512, dtype=torch.int32, device="cuda")
+    t = med(lambda: lib.cma_probe_read(a.data_ptr(), big, cus * 8, sink.data_ptr(), st))
+    out["hbm_read_GBps"] = round(big / (t * 1e-3) / 1e9, 1)
+    half = big // 2
+    b = torch.empty(half // 4, dtype=torch.float32, device="cuda")
+    t = med(lambda: lib.cma_probe_copy(a.data_ptr(), b.data_ptr(), half, cus * 8, st))
+    out["hbm_copy_GBps_read_plus_write"] = round(2 * half / (t * 1e-3) / 1e9, 1)
+    del a, b
+    n_wg, iters = cus * 4, 20000
+    o = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    t = med(lambda: lib.cma_probe_mfma(n_wg, iters, o.data_ptr(), st))
+    flops = n_wg * 4 * iters * 8 * 2 * 32 * 32 * 16
+    out["mfma_32x32x16_bf16_TFLOPs"] = round(flops / (t * 1e-3) / 1e12, 1)
+    l2b, l2it = 2 << 20, 200
+    buf = torch.ones(l2b // 2, dtype=torch.bfloat16, device="cuda")
+    t = med(lambda: lib.cma_probe_l2(buf.data_ptr(), l2b, l2it, cus * 2, sink.data_ptr(), st))
+    moved = cus * 2 * l2it * l2b
+    out["l2_to_cu_GBps"] = round(moved / (t * 1e-3) / 1e9, 1)
+    out["l2_to_cu_B_per_clk_per_cu_at_2p4GHz"] = round(moved / (t * 1e-3) / 2.4e9 / cus, 1)
+    print(json.dumps(out), flush=True)
 
 
 def log(*a):
@@ -184,6 +244,37 @@ def stage_figures(reps=5):
                    "k_tile_v": ("hbm", 2 * Hv * n * 128 * 2)})
     print(json.dumps({"workload": f"fused mapped x V with grouped V: {Hr} receiver heads reading {Hv} V heads "
                                   f"({Hr // Hv} per V head), otherwise as above", "kernels": k_gqa}), flush=True)
+    # a prefill chunk: the last 4096 queries of the 8192-token prompt over all its
+    # keys (compression of the chunk, then the fused pass with V read through a
+    # shuffled page table)
+    ch = n // 2
+    vl_c = cma.Varlen([0, ch], [0, n], used_q=[ch], used_k=[n])
+    qc = q[:, n - ch:].contiguous()
+    res_c = {}
+
+    def comp_chunk():
+        res_c["bsr"] = cma.block_compress(qc, k, sc, bi, vl_c, tau, workspace=ws)
+    comp_chunk()
+    torch.cuda.synchronize()
+    nnz_c = int(res_c["bsr"]["nnz"].item())
+    n_pages = n // 64 + 16
+    table = torch.from_numpy(np.random.default_rng(5).permutation(n_pages)[: n // 64].astype(np.int32)).view(
+        1, -1).to("cuda")
+    pages = torch.zeros((Hr, n_pages, 64 * 128), dtype=torch.bfloat16, device="cuda")
+    cma.tile_v_paged(V, cma.Varlen([0, n]), pages, table)
+    pv = dict(pages=pages, table=table)
+    chunk_flops = H * sum((n - ch + i + 1) for i in range(ch)) * 128 * 2
+    k_cc = timed(comp_chunk, {"k_block_stats": ("mfma", chunk_flops),
+                              "k_block_extract": ("hbm", nnz_c * 8192 + nnz_c * 4 + H * (ch + n) * 128 * 2)})
+    k_cm = timed(lambda: cma.mapped_av(res_c["bsr"], Hs, M, Hr, pv, vl_c, q_rows=ch, v_layout=cma.V_PAGED,
+                                       k_rows=n),
+                 {"k_mapped_av_bsr": ("hbm", nnz_c * 8192 + Hr * (ch + n) * 128 * 2
+                                      + (Hs * (ch // 64) + 1 + nnz_c) * 4)})
+    print(json.dumps({"workload": f"prefill chunk: the last {ch} queries of the {n}-token prompt over its {n} keys, "
+                                  f"{H} sender heads compressed at tau={tau}, then {Hr} receiver heads with V read "
+                                  "through a page table of 64-key pages", "kernels_compress": k_cc,
+                      "kernels_mapped_av": k_cm}), flush=True)
+    del res_c, pages, pv, qc
     # two such receivers served from the one sender state: separate calls, then one
     # call with their heads stacked (each sender column read once per XCD)
     M2 = torch.cat([M, M.flip(1)], dim=1).contiguous()
@@ -275,12 +366,64 @@ def stage_figures(reps=5):
                                   "heads", "kernel_ms_per_step": round(dec_ms, 4), "kernels": k_dec}), flush=True)
 
 
+def long_decode_figures(reps=5):
+    """IAM's long-context decode (8192 + 512 at batch 4), one generation step at its
+    longest context (8704 keys): the sender rows over 32 heads, then the mapped x V
+    of 24 receiver heads with a one-hot head map."""
+    import torch
+    import cross_model_attention_causal_amd as cma
+    import synth
+
+    x = synth.long_decode()
+    P, n, dec, Hs, Hr = x["n_prompts"], x["n"], x["decode"], x["n_send"], x["n_recv"]
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    t = dec - 1
+    ctx = n + 1 + t
+    vl = cma.Varlen(np.arange(P + 1), x["cu_k"], used_q=[1] * P, used_k=[ctx] * P)
+    k, sc, bi, v = bf(x["send_k"]), f32(x["send_scale"]), f32(x["send_bias"]), bf(x["v"])
+    qd = bf(x["dec_q"][t])
+    Mo = torch.zeros((P, Hr, Hs), dtype=torch.float32, device="cuda")
+    Mo[:, torch.arange(Hr), torch.arange(Hr) * 7 % Hs] = 1.0
+    st = {}
+
+    def step():
+        st["rows"] = cma.attn_maps(qd, k, sc, bi, vl, layout=cma.DENSE, out_dtype=torch.float32)
+        st["o"] = cma.mapped_av(("dense", st["rows"], cma.DENSE), Hs, Mo, Hr, v, vl, q_rows=P)
+    step()
+    torch.cuda.synchronize()
+    cma.timing_reset()
+    cma.timing_enable(True)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    cma.timing_enable(False)
+    kt = cma.timing_collect()
+    work = {"k_attn_rows": Hs * P * (128 * 2 + ctx * (128 * 2 + 4)), "k_mapped_av_dense": Hr * P * ctx * (128 * 2 + 4)}
+    kern = {}
+    for name, (ms, cnt) in kt.items():
+        e = dict(ms=round(ms / cnt, 4), launches_per_step=cnt // reps)
+        if name in work:
+            ach = work[name] / (ms / cnt * 1e-3) / 1e9
+            e.update(bound="hbm", work_per_launch=work[name], achieved=round(ach, 1), peak=HBM_PEAK_GBS,
+                     unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4))
+        kern[name] = e
+    step_ms = sum(e["ms"] * e["launches_per_step"] for e in kern.values())
+    print(json.dumps({"workload": f"IAM long-context decode, one step at context {ctx}: {P} prompts, sender rows "
+                                  f"over {Hs} heads, one-hot mapped x V of {Hr} receiver heads (bf16, d=128)",
+                      "kernel_ms_per_step": round(step_ms, 4), "tokens_per_s": round(P / (step_ms * 1e-3), 1),
+                      "kernels": kern}), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.peaks:
+        return peaks()
     if args.stage_figures:
-        return stage_figures()
+        stage_figures()
+        return long_decode_figures()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
@@ -374,16 +517,19 @@ def main():
     cma.timing_enable(True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(args.steps):
+    # one event between consecutive steps (each step ends with the main stream
+    # waiting for the side stream), so every step's own time is known too
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     cma.timing_enable(False)
     kt = cma.timing_collect()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     tokens = P * n
     value = tokens / (ms_step / 1e3)
 
@@ -479,12 +625,19 @@ def main():
         "kept_block_fraction": round(kept_frac, 4),
         "stages": stage,
         "wall_s_timed_region": round(wall, 3),
+        "step_ms_percentiles": {"p10": round(float(np.percentile(step_ms, 10)), 4),
+                                "median": round(float(np.median(step_ms)), 4),
+                                "p90": round(float(np.percentile(step_ms, 90)), 4)},
     }
-
     check_ok = True
     if not args.no_check:
         result["check"] = check_outputs(x, state, O, od, P, n, args.tau)
         check_ok = result["check"]["ok"]
+
+    if not args.no_headline:
+        del state, bsr_buf, O, vt, rows
+        torch.cuda.empty_cache()
+        result["headline"] = headline_figures()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, P, n, tokens, args.tau)
@@ -492,6 +645,60 @@ def main():
     print(json.dumps(result), flush=True)
     if not check_ok:
         sys.exit(1)
+
+
+def headline_figures(reps=10):
+    """Single-sequence headline figures on one 8192-token prompt (32 sender heads,
+    tau = 0.95; 24 receiver heads, learned M, token-major V): H2 = 8192 / t(block
+    compression: statistics, scan, extraction) and H1 = 8192 / t(mapped x V: V
+    tiling and the fused pass), each time the median over ``reps`` calls from HIP
+    events on the launch stream around the whole call, with the per-kernel averages
+    beside them."""
+    import torch
+    import cross_model_attention_causal_amd as cma
+    import synth
+
+    x, y = synth.cfg3(), synth.cfg4()
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
+    H, n, tau = x["n_heads"], x["n"], x["tau"]
+    vl = cma.Varlen(x["cu"])
+    q, k, sc, bi = bf(x["q"]), bf(x["k"]), f32(x["scale"]), f32(x["bias"])
+    M, V = f32(y["M"]), bf(y["v"])
+    ws, wsv, res = cma.Workspace(), cma.Workspace(), {}
+
+    def comp():
+        res["bsr"] = cma.block_compress(q, k, sc, bi, vl, tau, workspace=ws)
+
+    def mav():
+        res["O"] = cma.mapped_av(res["bsr"], y["n_send"], M, y["n_recv"], V, vl, workspace=wsv)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        cma.timing_reset()
+        cma.timing_enable(True)
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        cma.timing_enable(False)
+        kt = cma.timing_collect()
+        return float(np.median(ms)), {kname: round(t / c, 4) for kname, (t, c) in kt.items()}
+
+    t_c, k_c = timed(comp)
+    t_m, k_m = timed(mav)
+    nnz = int(res["bsr"]["nnz"].item())
+    return {"workload": f"one {n}-token prompt: block compression of {H} sender heads (tau={tau}), then "
+                        f"mapped x V of {y['n_recv']} receiver heads (learned M, token-major bf16 V, d=128)",
+            "H1_tokens_per_s": round(n / (t_m * 1e-3), 1), "H1_ms": round(t_m, 4),
+            "H2_tokens_per_s": round(n / (t_c * 1e-3), 1), "H2_ms": round(t_c, 4),
+            "kept_block_fraction": round(nnz / (H * (n // 64) * (n // 64 + 1) // 2), 4),
+            "kernel_ms": {**k_c, **k_m}}
 
 
 def check_outputs(x, state, O, od, P, n, tau):

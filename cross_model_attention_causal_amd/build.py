@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcma.so")
 OBJ = os.path.join(ROOT, "_build")
-SOURCES = ["capi.hip", "attn_maps.hip", "cosine.hip", "compress.hip", "mapped_av.hip", "prefix_index.hip"]
+SOURCES = ["capi.hip", "attn_maps.hip", "cosine.hip", "compress.hip", "mapped_av.hip", "prefix_index.hip", "probes.hip"]
 
 
 def _hipcc():

@@ -1,0 +1,112 @@
+// Microbenchmarks of the chip's ceilings that the kernels are measured against:
+// streaming HBM read and copy bandwidth, the sustained rate of the 32x32x16 bf16
+// matrix instruction, and the bandwidth from the L2 caches into the compute units
+// (every workgroup re-reads one small buffer, so after the first pass the bytes
+// come from each XCD's L2, in the 1 KB-per-instruction shape the fused pass
+// uses). Each entry point enqueues one launch on `stream`; the caller times it.
+// Not part of the method's path.
+#include "common.hpp"
+
+#include "cma_probe.h"
+
+namespace cma {
+
+// grid-stride 16-byte reads of n16 chunks; the xor of what was read goes to
+// sink[thread] only if it equals `never` (it does not), so the loads stay.
+__global__ __launch_bounds__(512) void k_probe_read(const u32x4* __restrict__ src, int64_t n16, uint32_t never,
+                                                     uint32_t* sink) {
+  uint32_t x = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i + u * stride < n16 ? src[i + u * stride] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (x == never) sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
+__global__ __launch_bounds__(512) void k_probe_copy(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                     int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// Every wave runs `iters` rounds of 8 independent 32x32x16 bf16 products.
+__global__ __launch_bounds__(256) void k_probe_mfma(int iters, float* out) {
+  const int lane = threadIdx.x & 63;
+  u32x4 av = {0x3f803f80u ^ (uint32_t)lane, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  u32x4 bv = {0x3c003c00u, 0x3c003c00u ^ (uint32_t)lane, 0x3c003c00u, 0x3c003c00u};
+  f32x16 acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = mfma32(as_bf16x8(av), as_bf16x8(bv), acc[k]);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[k][v];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// Every workgroup reads the same `bytes` (a multiple of 16 KB) `iters` times, one
+// 1 KB-per-wave buffer load per instruction, 8 loads in flight per wave.
+__global__ __launch_bounds__(512) void k_probe_l2(const uint16_t* __restrict__ buf, int bytes, int iters,
+                                                   uint32_t never, uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(buf), (short)0, bytes, kBufferFlags);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t x = 0;
+  const int per_round = 8 * 1024 * 8;  // 8 waves x 8 loads x 1 KB
+  for (int it = 0; it < iters; ++it) {
+    for (int off = 0; off < bytes; off += per_round) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, 16u * lane, off + (wave * 8 + u) * 1024, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][3];
+    }
+  }
+  if (x == never) sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
+}  // namespace cma
+
+using namespace cma;
+
+extern "C" {
+
+int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, void* sink, void* stream) {
+  if (!src || !sink || bytes < 16 || n_wg < 1 || (reinterpret_cast<uintptr_t>(src) & 15)) return CMA_EINVAL;
+  hipLaunchKernelGGL(k_probe_read, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), bytes / 16, 0x9e3779b9u, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void* stream) {
+  if (!src || !dst || bytes < 16 || n_wg < 1 || ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15))
+    return CMA_EINVAL;
+  hipLaunchKernelGGL(k_probe_copy, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+int cma_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* stream) {
+  if (!out || n_wg < 1 || iters < 1) return CMA_EINVAL;
+  hipLaunchKernelGGL(k_probe_mfma, dim3(n_wg), dim3(256), 0, static_cast<hipStream_t>(stream), iters, out);
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+int cma_probe_l2(const void* buf, int32_t bytes, int32_t iters, int32_t n_wg, void* sink, void* stream) {
+  if (!buf || !sink || n_wg < 1 || iters < 1 || bytes < 65536 || bytes % 65536) return CMA_EINVAL;
+  hipLaunchKernelGGL(k_probe_l2, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(buf), bytes, iters, 0x9e3779b9u, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+}  // extern "C"

@@ -17,9 +17,12 @@ LIB = os.path.join(ROOT, "cross_model_attention_causal_amd", "libcma.so")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)  # drop comments
-    return sorted(set(re.findall(r"\b(cma_[a-z0-9_]+)\s*\(", text)))
+    import glob
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)  # drop comments
+        names |= set(re.findall(r"\b(cma_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
