@@ -201,7 +201,23 @@ def stage_figures(reps=5):
     print(json.dumps({"workload": f"head mapping: one {n}-token prompt, {Hs} small-model and {Hr} large-model "
                                   "maps (d=128, bf16), packed causal, and the Hr x Hs cosine with argmax",
                       "kernels": {**k_maps, **k_cos}}), flush=True)
-    del st, sq, sk, rq, rk
+    del st
+    # the same head mapping with the large model's maps formed inside the Gram
+    # producer (never stored): the small model's maps stored dense, then the fused pass
+    fz = {}
+
+    def fused():
+        fz["s"] = cma.attn_maps(sq, sk, ss, sb, vl, layout=cma.DENSE)
+        fz["r"] = cma.head_map_fused(rq, rk, rs, rb, fz["s"], Hs, vl, workspace=fz.setdefault("ws", cma.Workspace()))
+    s_bytes = Hs * (2 * n * 128 * 2 + n * n * 2)
+    k_fused = timed(fused, {"k_attn_maps_short": ("hbm", s_bytes),
+                            "k_head_map_fused": ("mfma", 2 * Hr * Hs * L + 2 * Hr * L * 128)})
+    tot = sum(e["ms"] * e["launches_per_call"] for e in k_fused.values())
+    print(json.dumps({"workload": f"fused head mapping: the same {Hr} x {Hs} problem, {Hs} small-model maps stored "
+                                  f"(dense bf16), the {Hr} large-model maps formed on chip inside the Gram "
+                                  "(work: Gram products + one QK^T pass over the causal entries)",
+                      "total_ms": round(tot, 4), "kernels": k_fused}), flush=True)
+    del fz, sq, sk, rq, rk
 
     # 32-head x 8192-token compression, then the fused pass over it
     t0 = time.time()

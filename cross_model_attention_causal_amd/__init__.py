@@ -28,7 +28,7 @@ BLOCK = 64
 
 EXPORTS = [
     "cma_version", "cma_last_error", "cma_maps_elems", "cma_attn_maps",
-    "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_bsr_max_blocks", "cma_bsr_capacity",
+    "cma_head_map_cosine_workspace", "cma_head_map_cosine", "cma_head_map_fused_workspace", "cma_head_map_fused", "cma_bsr_max_blocks", "cma_bsr_capacity",
     "cma_block_compress_workspace", "cma_block_compress", "cma_block_compress_noalloc", "cma_mapped_av_workspace",
     "cma_mapped_av", "cma_mapped_av_indexed_workspace", "cma_mapped_av_indexed", "cma_tile_v", "cma_tile_v_paged", "cma_onehot_mix", "cma_mapped_layers", "cma_timing_enable",
     "cma_timing_collect", "cma_timing_get", "cma_timing_name", "cma_timing_reset",
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH):
         "cma_head_map_cosine_workspace": (SZ, [I32, I32, I32, I64, ctypes.c_int]),
         "cma_head_map_cosine": (ctypes.c_int, [P, P, ctypes.c_int, I32, I32, I32, I64, I64, I64,
                                                I64, I64, P, P, P, P, SZ, P]),
+        "cma_head_map_fused_workspace": (SZ, [I32, I32, I32, I32]),
+        "cma_head_map_fused": (ctypes.c_int, [P, P, I32, I32, P, P, P, I64, I32, P, P, P, P, P, SZ, P]),
         "cma_bsr_max_blocks": (I64, [I32, I32, P]),
         "cma_bsr_capacity": (I64, [I32, I32, P, P]),
         "cma_block_compress_workspace": (SZ, [I32, I32, I32, I64]),
@@ -276,6 +278,39 @@ def head_map_cosine(recv, send, n_batch, n_recv, n_send, length, recv_hstride, r
                                    length, recv_hstride, recv_bstride, send_hstride, send_bstride,
                                    _dev_ptr(cos, "cos"), _dev_ptr(arg, "argmax"),
                                    _dev_ptr(mar, "margin"), ws.data_ptr(), ws_bytes, _stream()))
+    return cos, arg, mar
+
+
+def head_map_fused(recv_q, recv_k, recv_scale, recv_bias, send_maps, n_send, vl: Varlen, want_cos=True,
+                   want_margin=True, workspace: Workspace | None = None):
+    """Cosine head map with the receivers' maps formed on chip (never stored): one
+    problem per sequence of ``vl``; ``send_maps`` as ``attn_maps(..., layout=DENSE)``
+    wrote them (bf16 [>= n_send, head_stride]). Returns (cos or None, argmax, margin
+    or None), each with a leading sequence dimension."""
+    torch = _torch()
+    lib = load_library()
+    H, Tq, d = recv_q.shape
+    if recv_k.dim() != 3 or recv_k.shape[0] < H or recv_k.shape[2] != d:
+        raise ValueError(f"recv_k must be [>= {H}, Tk, {d}]")
+    _need(recv_scale, "recv_scale", H)
+    _need(recv_bias, "recv_bias", H)
+    _check_rows(vl, Tq, recv_k.shape[1])
+    stride = vl.maps_elems(DENSE)
+    if send_maps.dim() != 2 or send_maps.shape[0] < n_send or send_maps.shape[1] < stride:
+        raise ValueError(f"send_maps must be [>= {n_send}, >= {stride}] (dense maps)")
+    dev = recv_q.device
+    B = vl.n_seqs
+    ws_bytes = lib.cma_head_map_fused_workspace(B, H, n_send, vl.max_q)
+    ws = (workspace or Workspace()).get(max(1, ws_bytes), dev)
+    cos = torch.empty((B, H, n_send), dtype=torch.float32, device=dev) if want_cos else None
+    arg = torch.empty((B, H), dtype=torch.int32, device=dev)
+    mar = torch.empty((B, H), dtype=torch.float32, device=dev) if want_margin else None
+    cvl = vl.c(Tq, recv_k.shape[1])
+    _check(lib.cma_head_map_fused(_dev_ptr(recv_q, "recv_q"), _dev_ptr(recv_k, "recv_k"), H, d,
+                                  _dev_ptr(recv_scale, "recv_scale"), _dev_ptr(recv_bias, "recv_bias"),
+                                  _dev_ptr(send_maps, "send_maps"), send_maps.shape[1], n_send, ctypes.byref(cvl),
+                                  _dev_ptr(cos, "cos"), _dev_ptr(arg, "argmax"), _dev_ptr(mar, "margin"),
+                                  ws.data_ptr(), ws.numel(), _stream()))
     return cos, arg, mar
 
 

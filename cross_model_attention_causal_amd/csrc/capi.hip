@@ -331,6 +331,55 @@ int64_t cma_bsr_max_blocks(int32_t n_heads, int32_t n_seqs, const int32_t* len_h
   return tot * n_heads;
 }
 
+size_t cma_head_map_fused_workspace(int32_t n_batch, int32_t n_recv, int32_t n_send, int32_t max_seqlen) {
+  if (n_batch <= 0 || n_recv <= 0 || n_send <= 0 || max_seqlen <= 0) return 0;
+  return fused_map_ws_bytes(n_batch, n_recv, n_send, max_seqlen);
+}
+
+int cma_head_map_fused(const void* recv_q, const void* recv_k, int32_t n_recv, int32_t d, const float* recv_scale,
+                       const float* recv_bias, const void* send_maps, int64_t send_head_stride, int32_t n_send,
+                       const cma_varlen* vl, float* cos, int32_t* argmax, float* margin, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (int e = check_varlen(vl, true)) return e;
+  if (n_recv < 0 || n_send < 0 || send_head_stride < 0) return fail(CMA_EINVAL, "negative size");
+  if (d != 128) return fail(CMA_EUNSUPPORTED, "head_map_fused supports d = 128 (got %d)", d);
+  if (n_recv == 0 || vl->n_seqs == 0) return CMA_OK;
+  if (n_send == 0) return fail(CMA_EINVAL, "n_send must be positive");
+  if (vl->max_seqlen_q != vl->max_seqlen_k)
+    return fail(CMA_EINVAL, "head_map_fused maps square sequences (max_seqlen_q == max_seqlen_k)");
+  if (vl->max_seqlen_q > kFusedMaxLen) return fail(CMA_EUNSUPPORTED, "head_map_fused supports sequences up to %d", kFusedMaxLen);
+  if (!recv_q || !recv_k || !recv_scale || !send_maps || !argmax)
+    return fail(CMA_EINVAL, "NULL recv_q, recv_k, recv_scale, send_maps or argmax");
+  if (!aligned16(recv_q) || !aligned16(recv_k) || !aligned16(send_maps))
+    return fail(CMA_EINVAL, "recv_q, recv_k and send_maps must be 16-byte aligned");
+  const size_t need = fused_map_ws_bytes(vl->n_seqs, n_recv, n_send, vl->max_seqlen_q);
+  if (!workspace || workspace_bytes < need) return fail(CMA_ENOSPC, "workspace of %zu bytes needed", need);
+  FusedMapArgs a{};
+  a.q = static_cast<const uint16_t*>(recv_q);
+  a.k = static_cast<const uint16_t*>(recv_k);
+  a.vl = to_varlen(vl);
+  a.scale = recv_scale;
+  a.bias = recv_bias;
+  a.send = static_cast<const uint16_t*>(send_maps);
+  a.send_hs = send_head_stride;
+  a.n_recv = n_recv;
+  a.n_send = n_send;
+  a.n_qt = (vl->max_seqlen_q + kFusedRows - 1) / kFusedRows;
+  a.fin.bf16 = true;
+  a.fin.n_batch = vl->n_seqs;
+  a.fin.n_recv = n_recv;
+  a.fin.n_send = n_send;
+  a.fin.cos = cos;
+  a.fin.argmax = argmax;
+  a.fin.margin = margin;
+  float* ws = static_cast<float*>(workspace);
+  a.fin.part = ws;
+  a.fin.rnorm = a.fin.part + (size_t)a.n_qt * vl->n_seqs * n_recv * n_send;
+  a.fin.snorm = a.fin.rnorm + (size_t)a.n_qt * vl->n_seqs * n_recv;
+  a.fin.splits = a.n_qt;
+  return hip_status(launch_head_map_fused(a, static_cast<hipStream_t>(stream)), "head_map_fused launch");
+}
+
 int64_t cma_bsr_capacity(int32_t n_heads, int32_t n_seqs, const int32_t* len_q, const int32_t* len_k) {
   if (n_heads < 0 || n_seqs < 0 || (n_seqs > 0 && !len_q)) return -1;
   int64_t tot = 0;

@@ -12,6 +12,7 @@
 // in a fixed order (deterministic), forms the cosines and takes argmax (lowest
 // index on ties) and margin.
 #include "kernels.hpp"
+#include "score.hpp"
 
 namespace cma {
 
@@ -349,6 +350,313 @@ __global__ __launch_bounds__(kFinThreads) void k_cos_finalize(CosineArgs a) {
     a.argmax[(int64_t)b * a.n_recv + h] = i1;
     if (a.margin) a.margin[(int64_t)b * a.n_recv + h] = a.n_send > 1 ? v1 - v2 : INFINITY;
   }
+}
+
+// ------------------------------------------------------------ fused maps -> cosine
+// Head mapping without storing the receivers' maps (IAM Methods 1 and 4: the
+// cosine of flattened causal maps; the maps are explicit softmax outputs, so no
+// flash-style kernel can produce them): a workgroup owns 32 query rows of one
+// sequence (one split of the Gram's K), 32 receiver heads and up to 128 sender
+// heads. It first sweeps the keys once per head for the rows' softmax statistics
+// (online max and sum, 32x32x16 bf16 MFMA), then walks the rows' keys in blocks
+// of 32: the waves recompute their heads' score tiles, form the probabilities,
+// round them to bf16 (the values a stored map would hold) and write them to an
+// LDS buffer ordered (row, head, key), double-buffered; the same waves then take
+// rows of the buffer as the A operand (32 heads x 16 keys) of 32x32x16 MFMAs
+// whose B operand is the sender maps' same row and keys (dense bf16 maps, read
+// straight into registers). Per split the Gram partial, the receivers' squared
+// norms (from the rounded values) and the senders' squared norms go to the
+// workspace; k_cos_finalize adds the splits in a fixed order.
+constexpr int kFusedRS = kFusedHeads * 64 + 16;   // LDS bytes per query row of a buffer
+constexpr int kFusedBuf = kFusedRows * kFusedRS;  // one buffer
+
+__global__ __launch_bounds__(512) void k_head_map_fused(FusedMapArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ float lse_s[kFusedHeads][kFusedRows];
+  __shared__ float sn_s[24][32];  // senders' squared norms per Gram item
+  const int n_rt = (a.n_recv + kFusedHeads - 1) / kFusedHeads, n_sg = (a.n_send + kFusedSend - 1) / kFusedSend;
+  const int per_qt = n_rt * n_sg;
+  const int qt = a.n_qt - 1 - (int)(blockIdx.x / per_qt);  // the longest splits first
+  const int rem = (int)(blockIdx.x % per_qt), sg = rem / n_rt, rt = rem % n_rt;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nl = lane & 31, hl = lane >> 5;
+  const int32_t n = seq_len_q(a.vl, b), nk = seq_len_k(a.vl, b);
+  const int i0 = kFusedRows * qt;
+  const int64_t split_row = (int64_t)qt * a.fin.n_batch + b;
+  float* part = a.fin.part + split_row * a.n_recv * a.n_send;
+  if (!seq_ok(a.vl, b, n, nk) || n != nk || i0 >= n) {
+    // no rows of this problem in this split: its partials are zero
+    for (int x = tid; x < kFusedHeads * kFusedSend; x += 512) {
+      const int h = kFusedHeads * rt + x / kFusedSend, j = kFusedSend * sg + x % kFusedSend;
+      if (h < a.n_recv && j < a.n_send) part[(int64_t)h * a.n_send + j] = 0.f;
+    }
+    if (sg == 0 && tid < kFusedHeads && kFusedHeads * rt + tid < a.n_recv)
+      a.fin.rnorm[split_row * a.n_recv + kFusedHeads * rt + tid] = 0.f;
+    if (rt == 0 && tid < kFusedSend && kFusedSend * sg + tid < a.n_send)
+      a.fin.snorm[split_row * a.n_send + kFusedSend * sg + tid] = 0.f;
+    return;
+  }
+  const int64_t q0 = cu_q_of(a.vl, b), k0 = cu_k_of(a.vl, b);
+  const int64_t map_off = map_seq_off(a.vl, b, false);  // the sequence's dense sender maps
+  const int n_kb = qt + 1;                               // key blocks of 32: keys 0 .. i0 + 31
+  const int qpos = i0 + nl;                              // the lane's query row
+  const bool qvalid = qpos < n;
+  const bool do_snorm = rt == 0;
+
+  // this lane's Q operand of head h (B of 32x32x16: query nl, features 16 ks + 8 hl ..)
+  auto load_q = [&](int h, QOperand<128>& qop) __attribute__((always_inline)) {
+    load_query_clamped<128>(qop, a.q + ((int64_t)h * a.vl.total_q + q0 + min(qpos, n - 1)) * 128, qvalid);
+  };
+  // the K operand of key block kb (32 keys; A of 32x32x16: key nl, features 16 ks + 8 hl ..)
+  auto load_kt = [&](int h, int kb, u32x4 (&kx)[8]) __attribute__((always_inline)) {
+    const int key = min(32 * kb + nl, n - 1);
+    const uint16_t* krow = a.k + ((int64_t)h * a.vl.total_k + k0 + key) * 128 + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kx[ks] = ldg16(krow + 16 * ks);
+  };
+  // scores of a key block x the 32 queries: D[key 8(v/4) + 4 hl + v%4][query nl]
+  auto mma_kt = [&](const u32x4 (&kx)[8], const QOperand<128>& qop) __attribute__((always_inline)) {
+    f32x16 c = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) c = mfma32(as_bf16x8(kx[ks]), qop.v[ks], c);
+    return c;
+  };
+  auto key_of = [&](int kb, int v) __attribute__((always_inline)) { return 32 * kb + 8 * (v >> 2) + 4 * hl + (v & 3); };
+
+  // ---- softmax statistics of the 32 rows, per head (wave w: heads 4w .. 4w + 3)
+#pragma unroll 1
+  for (int u = 0; u < 4; ++u) {
+    const int hh = 4 * wave + u, h = kFusedHeads * rt + hh;
+    float lse = -INFINITY;
+    if (h < a.n_recv) {
+      QOperand<128> qop;
+      load_q(h, qop);
+      const float sl2 = ld_const(a.scale + h) * kLog2e, bl2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
+      float m = -INFINITY, l = 0.0f;
+      // key blocks two at a time, the next block's K in flight during a block's products
+      u32x4 kxa[8], kxb[8];
+      load_kt(h, 0, kxa);
+      auto step = [&](int kb, const u32x4 (&kx)[8]) __attribute__((always_inline)) {
+        f32x16 c = mma_kt(kx, qop);
+        float bm = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key_of(kb, v);
+          const float t = (key <= qpos && key < n) ? c[v] * sl2 + (key == 0 ? bl2 : 0.0f) : -INFINITY;
+          c[v] = t;
+          bm = fmaxf(bm, t);
+        }
+        bm = fmaxf(bm, xor_lane(bm, 32));
+        const float mn = fmaxf(m, bm);
+        float s = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += mn == -INFINITY ? 0.0f : exp2f_fast(c[v] - mn);
+        s += xor_lane(s, 32);
+        l = mn == -INFINITY ? 0.0f : l * exp2f_fast(m - mn) + s;
+        m = mn;
+      };
+      for (int kb = 0; kb < n_kb; kb += 2) {
+        if (kb + 1 < n_kb) load_kt(h, kb + 1, kxb);
+        step(kb, kxa);
+        if (kb + 1 < n_kb) {
+          if (kb + 2 < n_kb) load_kt(h, kb + 2, kxa);
+          step(kb + 1, kxb);
+        }
+      }
+      lse = m + log2f_fast(l);
+    }
+    if (lane < 32) lse_s[hh][lane] = lse;
+  }
+  __syncthreads();
+
+  // ---- probabilities into the LDS buffer, then the Gram
+  // The Gram of a key block is split into items (32-sender tile t, group g of
+  // 32 / G rows), dealt round robin to the waves (at most 3 per wave): G rows
+  // groups per tile so that there are at least 8 items however few senders.
+  const int n_tiles = (min(kFusedSend, a.n_send - kFusedSend * sg) + 31) / 32;
+  const int G = n_tiles >= 6 ? 2 : (n_tiles >= 3 ? 4 : 8), RG = kFusedRows / G;
+  const int n_items = n_tiles * G;
+  f32x16 acc[3];
+#pragma unroll
+  for (int it = 0; it < 3; ++it) acc[it] = f32x16{};
+  float rn[4] = {0.f, 0.f, 0.f, 0.f}, sn[3] = {0.f, 0.f, 0.f};
+  // Produce key block kb into buffer buf: lane (query nl, half hl) writes its 16
+  // probabilities of each head as four 8-byte pieces at row nl, head slot hh,
+  // 8-key chunk g placed at slot g ^ ((hh >> 1) & 3) (the reads of 32 heads then
+  // spread over the bank groups); the row stride's extra 16 bytes spread the 32
+  // rows a write touches.
+  auto produce = [&](int kb, int buf) __attribute__((always_inline)) {
+    uint8_t* B = smem + buf * kFusedBuf;
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) {
+      const int hh = 4 * wave + u, h = kFusedHeads * rt + hh;
+      uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      if (h < a.n_recv) {
+        QOperand<128> qop;
+        u32x4 kx[8];
+        load_q(h, qop);
+        load_kt(h, kb, kx);
+        const f32x16 c = mma_kt(kx, qop);
+        const float sl2 = ld_const(a.scale + h) * kLog2e, bl2 = a.bias ? ld_const(a.bias + h) * kLog2e : 0.0f;
+        const float lse = lse_s[hh][nl];
+        float p[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key_of(kb, v);
+          const float t = c[v] * sl2 + (key == 0 ? bl2 : 0.0f);
+          p[v] = (qvalid && key <= qpos) ? exp2f_fast(t - lse) : 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          w[2 * g] = pack2bf(p[4 * g], p[4 * g + 1]);
+          w[2 * g + 1] = pack2bf(p[4 * g + 2], p[4 * g + 3]);
+        }
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t = sq2(w[e], t);
+        rn[u] += t;  // one tile's squares at a time (a short chain per lane)
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<u32x2*>(B + nl * kFusedRS + hh * 64 + 16 * (g ^ ((hh >> 1) & 3)) + 8 * hl) =
+            u32x2{w[2 * g], w[2 * g + 1]};
+    }
+  };
+  // sender operands (B of 32x32x16: sender 32 t + nl, keys key0 + 8 hl ..) of row
+  // i: FAST (every row starts on 16 bytes and the sequence fills whole key blocks)
+  // takes plain 16-byte loads with no branch, else each load checks alignment and
+  // the row's end
+  auto load_b = [&](int t, int i, int kb, u32x4 (&bv)[2], auto fast) __attribute__((always_inline)) {
+    const int jr = kFusedSend * sg + 32 * t + nl;
+    const int64_t so = (int64_t)min(jr, a.n_send - 1) * a.send_hs + map_off + (int64_t)min(i, n - 1) * n;
+    const uint16_t* srow = a.send + so;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int key0 = 32 * kb + 16 * ks + 8 * hl;
+      if constexpr (decltype(fast)::value) {
+        bv[ks] = ldg16(srow + key0);
+      } else {
+        bv[ks] = (((so + key0) & 7) == 0 && key0 + 8 <= n) ? ldg16(srow + key0) : ldg16_guard_any(srow, key0, n);
+      }
+    }
+  };
+  const bool fast = (n % 32) == 0 && (map_off % 8) == 0 && (a.send_hs % 8) == 0 &&
+                    (reinterpret_cast<uintptr_t>(a.send) & 15) == 0;
+  // Gram of key block kb from buffer buf: this wave's items, rows two at a time
+  // with the sender operands of the next two rows in flight (rows past the
+  // sequence end read the last row; their probabilities in the buffer are zero)
+  auto consume = [&](int kb, int buf, auto fastc) __attribute__((always_inline)) {
+    const uint8_t* B = smem + buf * kFusedBuf;
+#pragma unroll
+    for (int it = 0; it < 3; ++it) {
+      const int item = wave + 8 * it;
+      if (item >= n_items) break;
+      const int t = item / G, r0 = (item % G) * RG;
+      if (i0 + r0 >= n) continue;
+      u32x4 bc[2][2], bn[2][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) load_b(t, i0 + r0 + e, kb, bc[e], fastc);
+      for (int r = r0; r < r0 + RG; r += 2) {
+        if (r + 2 < r0 + RG) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) load_b(t, i0 + r + 2 + e, kb, bn[e], fastc);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int c8 = 2 * ks + hl;
+            const u32x4 av =
+                *reinterpret_cast<const u32x4*>(B + (r + e) * kFusedRS + nl * 64 + 16 * (c8 ^ ((nl >> 1) & 3)));
+            acc[it] = mfma32(as_bf16x8(av), as_bf16x8(bc[e][ks]), acc[it]);
+            if (do_snorm && i0 + r + e < n) {
+              float q2 = 0.0f;
+#pragma unroll
+              for (int x = 0; x < 4; ++x) q2 = sq2(bc[e][ks][x], q2);
+              sn[it] += q2;
+            }
+          }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          bc[e][0] = bn[e][0];
+          bc[e][1] = bn[e][1];
+        }
+      }
+    }
+  };
+  produce(0, 0);
+  __syncthreads();
+  for (int kb = 0; kb < n_kb; ++kb) {
+    if (kb + 1 < n_kb) produce(kb + 1, (kb + 1) & 1);
+    if (fast) consume(kb, kb & 1, std::true_type{});
+    else consume(kb, kb & 1, std::false_type{});
+    __syncthreads();
+  }
+
+  // ---- partial Gram: per tile, the row groups' sums added in group order
+  float* red = reinterpret_cast<float*>(smem);  // [item][32 heads][32 senders]
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const int item = wave + 8 * it;
+    if (item < n_items) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 8 * (v >> 2) + 4 * hl + (v & 3);
+        red[(item * kFusedHeads + m) * 32 + nl] = acc[it][v];
+      }
+      if (do_snorm) {
+        const float x = sn[it] + xor_lane(sn[it], 32);
+        if (lane < 32) sn_s[item][nl] = x;
+      }
+    }
+  }
+  // receivers' squared norms: wave w's heads, over its lanes
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float x = rn[u];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += xor_lane(x, off);
+    const int h = kFusedHeads * rt + 4 * wave + u;
+    if (sg == 0 && lane == 0 && h < a.n_recv) a.fin.rnorm[split_row * a.n_recv + h] = x;
+  }
+  __syncthreads();
+  for (int x = tid; x < kFusedHeads * 32 * n_tiles; x += 512) {
+    const int t = x / (kFusedHeads * 32), y = x % (kFusedHeads * 32), m = y / 32, jj = y % 32;
+    float s = 0.0f;
+    for (int g = 0; g < G; ++g) s += red[((t * G + g) * kFusedHeads + m) * 32 + jj];
+    const int h = kFusedHeads * rt + m, j = kFusedSend * sg + 32 * t + jj;
+    if (h < a.n_recv && j < a.n_send) part[(int64_t)h * a.n_send + j] = s;
+  }
+  if (do_snorm && tid < 32 * n_tiles && kFusedSend * sg + tid < a.n_send) {
+    const int t = tid / 32, jj = tid % 32;
+    float s = 0.0f;
+    for (int g = 0; g < G; ++g) s += sn_s[t * G + g][jj];
+    a.fin.snorm[split_row * a.n_send + kFusedSend * sg + tid] = s;
+  }
+}
+
+size_t fused_map_ws_bytes(int32_t n_batch, int32_t n_recv, int32_t n_send, int32_t max_seqlen) {
+  const int64_t n_qt = (max_seqlen + kFusedRows - 1) / kFusedRows;
+  return (size_t)n_qt * n_batch * ((size_t)n_recv * n_send + n_recv + n_send) * sizeof(float);
+}
+
+hipError_t launch_head_map_fused(const FusedMapArgs& a, hipStream_t st) {
+  if (a.fin.n_batch == 0 || a.n_recv == 0 || a.n_qt == 0) return hipSuccess;
+  const int n_rt = (a.n_recv + kFusedHeads - 1) / kFusedHeads, n_sg = (a.n_send + kFusedSend - 1) / kFusedSend;
+  const size_t lds = 2 * (size_t)kFusedBuf;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_head_map_fused),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  {
+    KernelTimer kt_("k_head_map_fused", st);
+    hipLaunchKernelGGL(k_head_map_fused, dim3((unsigned)(a.n_qt * n_rt * n_sg), a.fin.n_batch), dim3(512), lds, st,
+                       a);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  { KernelTimer kt_("k_cos_finalize", st); hipLaunchKernelGGL(k_cos_finalize, dim3(a.n_recv, a.fin.n_batch), dim3(kFinThreads), 0, st, a.fin); }
+  return hipGetLastError();
 }
 
 CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t len, bool bf16) {

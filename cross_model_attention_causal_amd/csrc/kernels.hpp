@@ -53,6 +53,26 @@ struct CosinePlan {
 CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t len, bool bf16);
 hipError_t launch_cosine(const CosineArgs& a, hipStream_t st);
 
+// Fused head mapping: receiver maps scored inside the Gram producer (never stored).
+struct FusedMapArgs {
+  const uint16_t* q;  // receiver queries / keys [n_recv, total, 128] bf16
+  const uint16_t* k;
+  Varlen vl;          // one problem per sequence (square: nq == nk)
+  const float* scale;
+  const float* bias;
+  const uint16_t* send;  // sender maps, dense bf16, as cma_attn_maps writes them
+  int64_t send_hs;       // elements per sender head
+  int32_t n_recv, n_send;
+  int32_t n_qt;          // query tiles of 32 rows of the longest sequence (the split count)
+  CosineArgs fin;        // finalize: part / rnorm / snorm with splits = n_qt, outputs
+};
+constexpr int kFusedRows = 32;    // query rows per workgroup (one split)
+constexpr int kFusedHeads = 32;   // receiver heads per workgroup
+constexpr int kFusedSend = 384;   // senders per workgroup (up to twelve 32-wide tiles)
+constexpr int kFusedMaxLen = 4096;  // longest mapped prefix
+size_t fused_map_ws_bytes(int32_t n_batch, int32_t n_recv, int32_t n_send, int32_t max_seqlen);
+hipError_t launch_head_map_fused(const FusedMapArgs& a, hipStream_t st);
+
 struct CompressArgs {
   const uint16_t* q;
   const uint16_t* k;

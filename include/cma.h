@@ -140,6 +140,32 @@ int cma_head_map_cosine(const void* recv, const void* send, cma_dtype dt, int32_
                         size_t workspace_bytes, void* stream);
 
 /*
+ * cma_head_map_fused -- the head mapping of cma_head_map_cosine without storing the
+ * receivers' maps ([IAM] Methods 1 and 4; the maps must be explicit softmax
+ * outputs, which is why the pages rule out a flash-style kernel, so here they
+ * are formed tile by tile on chip and consumed by the Gram product at once).
+ * One problem per sequence b of `vl` (square: nq == nk, max_seqlen <= 4096):
+ *   R_bh = the causal map of receiver head h on sequence b, computed from
+ *          recv_q / recv_k [n_recv, total, d] bf16 with recv_scale / recv_bias
+ *          [n_recv] as in cma_attn_maps, each value rounded to bf16 (the values a
+ *          stored map would hold);
+ *   S_bj = sender head j's map of sequence b as stored by cma_attn_maps with
+ *          CMA_MAP_DENSE, bf16: send_maps + j * send_head_stride, sequence b at the
+ *          sum of n_u^2 over earlier sequences (rows starting on 16 bytes are read
+ *          16 bytes at a time, others element by element);
+ * cos [n_seqs, n_recv, n_send] (or NULL), argmax [n_seqs, n_recv], margin (or
+ * NULL) as cma_head_map_cosine defines them (the zeros above the diagonal add
+ * nothing, so the value equals the cosine of the flattened causal entries).
+ * d = 128. Workspace: cma_head_map_fused_workspace(n_seqs, n_recv, n_send,
+ * max_seqlen) bytes (per 32-row split, the partial Gram and norms).
+ */
+size_t cma_head_map_fused_workspace(int32_t n_batch, int32_t n_recv, int32_t n_send, int32_t max_seqlen);
+int cma_head_map_fused(const void* recv_q, const void* recv_k, int32_t n_recv, int32_t d, const float* recv_scale,
+                       const float* recv_bias, const void* send_maps, int64_t send_head_stride, int32_t n_send,
+                       const cma_varlen* vl, float* cos, int32_t* argmax, float* margin, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * cma_block_compress -- two-phase block-sparse compression of causal maps
  * ([MapFlow] storage and execution), never forming the dense map.
  * Phase 1 sweeps QK^T once per block-row with an online softmax and keeps, per
