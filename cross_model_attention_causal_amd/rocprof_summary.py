@@ -90,8 +90,9 @@ def traffic(args):
     fetch, write = counter_means(args.fetch), counter_means(args.write)
     cf, cw = counter_means(args.cal_fetch), counter_means(args.cal_write)
     n = 1 << 30  # the calibration copy reads and writes 1 GiB per launch
-    cal_f = next(v["FETCH_SIZE"] for v in cf.values() if "FETCH_SIZE" in v)
-    cal_w = next(v["WRITE_SIZE"] for v in cw.values() if "WRITE_SIZE" in v)
+    # the copy is the calibration run's largest kernel (the run also fills the source)
+    cal_f = max(v["FETCH_SIZE"] for k, v in cf.items() if "FETCH_SIZE" in v and "copy" in k.lower())
+    cal_w = max(v["WRITE_SIZE"] for k, v in cw.items() if "WRITE_SIZE" in v and "copy" in k.lower())
     ff, fw = n / 1024 / cal_f, n / 1024 / cal_w
     md = [f"# HBM traffic per launch, {args.workload} (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)", "",
           f"Each counter in its own run. Calibration: a plain device copy of 1 GiB reads {cal_f:.0f} KiB by "
@@ -122,9 +123,33 @@ def counters(args):
         for k, cs in counter_means(d, args.kernel).items():
             merged.setdefault(k, {}).update(cs)
     md = [f"# {args.title}", "", "Commands (one counter group per run):", "", "```", args.cmd, "```", ""]
+    md += ["Derived (per launch; GRBM_GUI_ACTIVE counts cycles on each of the 8 XCDs, the SQ_ counters add",
+           "over the 256 CUs, and SQ_VALU_MFMA_BUSY_CYCLES over their 4 SIMDs each):", "",
+           "* cycles = GRBM_GUI_ACTIVE / 8;",
+           "* MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles);",
+           "* CU busy = SQ_BUSY_CU_CYCLES / (256 x cycles);",
+           "* VALU share = 4 x SQ_INSTS_VALU / (1024 SIMDs x cycles) (a wave64 vector instruction issues over 4 cycles",
+           "  on a 16-lane SIMD; transcendental ones take longer, so this is a lower bound);",
+           "* LDS conflict share = SQ_LDS_BANK_CONFLICT / (256 x cycles);",
+           "* address unit busy = TA_BUSY_avr / cycles.", ""]
     for k, cs in merged.items():
         md += [f"Kernel `{k[:80]}`, per launch:", "", "| counter | value |", "|---|---|"]
         md += [f"| `{c}` | {v:.4g} |" for c, v in sorted(cs.items())]
+        g = cs.get("GRBM_GUI_ACTIVE")
+        if g:
+            cyc = g / 8
+            der = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+                der.append(("MFMA busy", cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cyc)))
+            if "SQ_BUSY_CU_CYCLES" in cs:
+                der.append(("CU busy", cs["SQ_BUSY_CU_CYCLES"] / (256 * cyc)))
+            if "SQ_INSTS_VALU" in cs:
+                der.append(("VALU share", 4 * cs["SQ_INSTS_VALU"] / (1024 * cyc)))
+            if "SQ_LDS_BANK_CONFLICT" in cs:
+                der.append(("LDS conflict share", cs["SQ_LDS_BANK_CONFLICT"] / (256 * cyc)))
+            if "TA_BUSY_avr" in cs:
+                der.append(("address unit busy", cs["TA_BUSY_avr"] / cyc))
+            md += [f"| {name} | {val:.3f} |" for name, val in der]
         md.append("")
     open(args.out, "w").write("\n".join(md) + "\n")
 
