@@ -94,6 +94,8 @@ def peaks(reps=5):
     lib.cma_probe_copy.argtypes = [P, P, I64, I32, P]
     lib.cma_probe_mfma.argtypes = [I32, I32, P, P]
     lib.cma_probe_l2.argtypes = [P, I32, I32, I32, P, P]
+    lib.cma_probe_write.argtypes = [P, I64, I32, P]
+    lib.cma_probe_valu.argtypes = [I32, I32, I32, P, P]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     st = torch.cuda.current_stream().cuda_stream
 
@@ -120,7 +122,16 @@ def peaks(reps=5):
     b = torch.empty(half // 4, dtype=torch.float32, device="cuda")
     t = med(lambda: lib.cma_probe_copy(a.data_ptr(), b.data_ptr(), half, cus * 8, st))
     out["hbm_copy_GBps_read_plus_write"] = round(2 * half / (t * 1e-3) / 1e9, 1)
+    t = med(lambda: lib.cma_probe_write(a.data_ptr(), big, cus * 8, st))
+    out["hbm_write_GBps"] = round(big / (t * 1e-3) / 1e9, 1)
     del a, b
+    # vector-unit rates: lane-operations per clock per SIMD (4 SIMDs per CU) at 2.4 GHz
+    n_wg, iters = cus * 8, 4096
+    o = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    for kind, name in ((0, "exp2"), (1, "fma")):
+        t = med(lambda: lib.cma_probe_valu(kind, n_wg, iters, o.data_ptr(), st))
+        out[f"valu_{name}_lane_ops_per_clk_per_simd_at_2p4GHz"] = round(
+            n_wg * 256 * iters * 8 / (t * 1e-3) / (4 * cus) / 2.4e9, 2)
     n_wg, iters = cus * 4, 20000
     o = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
     t = med(lambda: lib.cma_probe_mfma(n_wg, iters, o.data_ptr(), st))
@@ -343,15 +354,21 @@ def stage_figures(reps=5):
     roff = np.concatenate([[0], np.cumsum([(n + 63) // 64 for n in pl])])
     used_blocks = sum(int(rp[j * r_tot + roff[p_ + 1]] - rp[j * r_tot + roff[p_]])
                       for p_ in range(P) for j in set(argh[p_].tolist()))
+    # blocks multiplied by the indexed pass: each receiver head's sender's kept blocks
+    head_blocks = sum(int(rp[j * r_tot + roff[p_ + 1]] - rp[j * r_tot + roff[p_]])
+                      for p_ in range(P) for j in argh[p_].tolist())
     maps_bytes = P * (Hs + Hr) * (2 * tt * 128 * 2 + L * 2) / 2
     idx_bytes = used_blocks * 8192 + 2 * Hr * tokens * 128 * 2 + (Hs * r_tot + 1 + nnz) * 4
+    # 64 x 64 x 128 multiply-adds per (receiver head, block): ~2 TFLOP against ~3 GB,
+    # so the matrix cores, not HBM, bound the indexed pass
+    idx_flops = head_blocks * 64 * 64 * 128 * 2
     k_pre = timed(prefill, {"k_attn_maps_short": ("hbm", maps_bytes),
                             # 68 small problems (64 x 28): ~20 flop per byte, far below
                             # the ridge, so the maps' bytes bound the Gram here
                             "k_gram_bf16": ("hbm", P * (Hr + Hs) * L * 2),
                             "k_block_stats": ("mfma", Hs * tri * 128 * 2),
                             "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2),
-                            "k_mapped_av_idx": ("hbm", idx_bytes),
+                            "k_mapped_av_idx": ("mfma", idx_flops),
                             "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2)})
     pre_ms = sum(e["ms"] * e["launches_per_call"] for e in k_pre.values())
     # the general fused pass on the same problem, with the argmax as a one-hot M

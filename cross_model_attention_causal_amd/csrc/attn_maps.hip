@@ -59,7 +59,7 @@ __global__ __launch_bounds__(512) void k_attn_maps(AttnMapsArgs a) {
   const int r = a.n_rb - 1 - slot % a.n_rb;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || 64 * r >= nq) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int qt = wave & 1, kp = wave >> 1;
   const int i = 64 * r + 32 * qt + (lane & 31);
   const bool valid = i < nq;
@@ -214,7 +214,7 @@ constexpr int kShortTileRows = 16;  // query rows per pass of a wave's bf16 outp
 // keys 8w .. 8w + 7, one 16-byte chunk per lane and feature half.
 template <int D>
 __device__ __forceinline__ void kblock_load(u32x4 x[D / 64], const uint16_t* __restrict__ kseq, int nk, int c) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = 8 * wave + (lane >> 3), ch = (lane & 7) ^ ((m >> 1) & 7);
   const int key = min(64 * c + m, nk - 1);
 #pragma unroll
@@ -389,12 +389,12 @@ __global__ __launch_bounds__(512) void k_attn_maps_short(AttnMapsArgs a) {
     float m = -INFINITY;
     if (has0) m = fmaxf(m, block_max(acc0, lean0 ? scale_l2 : 1.0f));
     if (has1) m = fmaxf(m, block_max(acc1, lean1 ? scale_l2 : 1.0f));
-    m = fmaxf(m, xor_lane(m, 32));
+    m = pair32_max(m);
     const float ms = m == -INFINITY ? 0.0f : m;  // every logit -inf: the powers are 0
     float l = 0.0f;
     if (has0) l += block_exp2(acc0, lean0 ? scale_l2 : 1.0f, ms);
     if (has1) l += block_exp2(acc1, lean1 ? scale_l2 : 1.0f, ms);
-    l += xor_lane(l, 32);
+    l = pair32_add(l);
     if (lane < 32) {
       sm[kp][32 * qt + lane] = m;
       sl[kp][32 * qt + lane] = l;

@@ -95,6 +95,25 @@ constexpr int kWaitVmcnt0 = 0x0f70;           // s_waitcnt immediate: vmcnt(0), 
 // ------------------------------------------------------------------ cross-lane
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// IEEE 754-2019 maximum: a NaN operand gives NaN. Unlike fmaxf it needs no
+// quieting of its operands, and chains of it fuse into v_maximum3_f32.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Max and sum of a value over the lane pair (l, l ^ 32), both lanes ending with
+// the same bits: one v_permlane32_swap (a vector instruction) instead of an LDS
+// permute. The swap of (v, v) leaves lanes 0-31 with (own, partner) and lanes
+// 32-63 with (partner, own); max and + are commutative.
+__device__ __forceinline__ float pair32_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float pair32_add(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 // Workgroup barrier that waits for this wave's LDS accesses but, unlike
 // __syncthreads, not for its global loads (prefetches stay in flight). The empty
 // asm statements keep the compiler from moving memory accesses across it.

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   const int nrb = (n + kBlock - 1) / kBlock, r0 = G * rg;
   if (!seq_ok(a.vl, s, n, nk) || kb0 < 0 || r0 >= nrb) return;
   const int r_last = min(r0 + G - 1, nrb - 1);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int qt = wave % QT, kp = wave / QT;
   const int rq = kb0 + r0 + qt / 2;                       // the tile's block-row in the sequence's grid
   const int c_last = kb0 + r_last;                        // last key block of the group

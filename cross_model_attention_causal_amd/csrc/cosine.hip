@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   const int xcd = blockIdx.x % kXcds, m = blockIdx.x / kXcds;
   const int sp = xcd + kXcds * (m / n_rtiles), rt = m % n_rtiles;
   if (sp >= a.splits) return;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int p = lane & 15, qd = lane >> 4;
   const int rg = wave & 3, sh = wave >> 2;  // receiver group, sender half
   const int64_t k_beg = (int64_t)sp * a.kchunk;
@@ -447,12 +447,12 @@ __global__ __launch_bounds__(512) void k_head_map_fused(FusedMapArgs a) {
           c[v] = t;
           bm = fmaxf(bm, t);
         }
-        bm = fmaxf(bm, xor_lane(bm, 32));
+        bm = pair32_max(bm);
         const float mn = fmaxf(m, bm);
         float s = 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) s += mn == -INFINITY ? 0.0f : exp2f_fast(c[v] - mn);
-        s += xor_lane(s, 32);
+        s = pair32_add(s);
         l = mn == -INFINITY ? 0.0f : l * exp2f_fast(m - mn) + s;
         m = mn;
       };
@@ -606,7 +606,7 @@ __global__ __launch_bounds__(512) void k_head_map_fused(FusedMapArgs a) {
         red[(item * kFusedHeads + m) * 32 + nl] = acc[it][v];
       }
       if (do_snorm) {
-        const float x = sn[it] + xor_lane(sn[it], 32);
+        const float x = pair32_add(sn[it]);
         if (lane < 32) sn_s[item][nl] = x;
       }
     }

@@ -590,22 +590,27 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
 
 // ------------------------------------------------------------ indexed source
 // One sender per receiver head, the head map of IAM Method 4 (the argmax of the
-// cosine): O_h = A_{j(h)} V_h. No mix is formed; each wave owns one receiver head
-// and 64 query rows (one block-row) and walks only its own sender's kept blocks
-// of that row. The stored block's 16-key panel already holds, for 32 rows, the
-// A operand of a 32x32x16 MFMA as one contiguous 1 KB run (lane L: row L % 32,
-// keys 8 (L / 32) .. + 7), and the tiled V holds the B operand, so both go from
-// memory straight to registers: no LDS, no barrier. Per 16-key panel a wave
-// issues 6 loads (2 row halves of A, 4 feature tiles of V) and 8 MFMAs; loads run
-// three panels ahead in a ring of four register sets.
+// cosine): O_h = A_{j(h)} V_h. Nothing is mixed. A workgroup owns one receiver
+// head and a group of 8 consecutive block-rows of one sequence, one row per
+// wave, and sweeps the union of the columns that the head's sender kept in those
+// rows. The V block of each column (16 KB in the tiled operand order) is staged
+// in LDS once for the 8 rows, so V crosses L2 -> CU once per 8 block-rows
+// instead of once per row. A stored block's 16-key panel already holds, for 32
+// rows, the A operand of a 32x32x16 MFMA as one contiguous 1 KB run, which the
+// wave reads straight into registers three panels ahead (a ring of four sets);
+// the V operands come from the stage. Per panel a wave issues 2 global and 4
+// LDS reads and 8 MFMAs; a row that did not keep a column skips its products.
 //
-// Work items are (sequence, pair of block-rows, octet of heads): the long row of
-// the pair with its columns ascending, then the short row descending (every pair
-// covers R + 1 columns). A workgroup is one item, its 8 waves the octet's heads
-// in the order of their senders, so heads that share a sender read its blocks
-// together. Workgroup id = item * n_oct + octet: with 8 octets (64 heads) every
-// item of octet o runs on XCD o, whose L2 then holds that octet's V columns and
-// sender blocks for all the pairs in flight there.
+// Work items are (sequence, pair of row groups, head). Block-rows in the upper
+// half of a sequence (2r >= R - 1 for R rows) are swept with their columns
+// ascending and the lower ones descending, as the general pass sweeps them, so
+// that with a one-hot M both passes add the same terms in the same order (the
+// results are bit-identical). Item p takes the upper group of rows R - 8p - 8 ..
+// R - 8p - 1 (not below the middle), then the lower group 8p .. 8p + 7 (not
+// above it): every item of a sequence covers about R + 8 columns. The heads of a
+// sequence are taken in the order of their senders and dealt to XCDs in runs
+// (XCD x takes heads x * hpx .. + hpx - 1 of every item), so that heads sharing a
+// sender read its blocks from one L2, and each head's V stays in one L2.
 
 // Receiver heads of each sequence ordered by sender (ties by head; heads whose
 // sender index is out of range last). grid (n_seqs), 256 threads.
@@ -625,6 +630,8 @@ __global__ __launch_bounds__(256) void k_idx_order(MappedAvArgs a) {
   }
 }
 
+constexpr int kIdxRows = 8;  // block-rows per workgroup of the indexed pass (one per wave)
+
 // Block-row offsets of the sequences and the work-item table. One workgroup.
 constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void k_idx_plan(MappedAvArgs a) {
@@ -642,7 +649,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_idx_plan(MappedAvArgs a) {
     const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
     nrb = (max(n, 0) + kBlock - 1) / kBlock;
     nkb = (max(nk, 0) + kBlock - 1) / kBlock;
-    np = seq_ok(a.vl, s, n, nk) && chunk_kb0(n, nk) >= 0 ? (nrb + 1) / 2 : 0;
+    // items: groups of kIdxRows of the upper ceil(nrb / 2) block-rows (see k_mapped_av_idx)
+    np = seq_ok(a.vl, s, n, nk) && chunk_kb0(n, nk) >= 0 ? (nrb - nrb / 2 + kIdxRows - 1) / kIdxRows : 0;
   };
   int64_t rows = 0, kblk = 0, pairs = 0;
   for (int s = s0; s < s1; ++s) {
@@ -688,144 +696,188 @@ __global__ __launch_bounds__(kPlanThreads) void k_idx_plan(MappedAvArgs a) {
   }
 }
 
-// grid (plan_cap * n_oct), 512 threads (8 waves, one receiver head each).
-__global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int n_oct) {
+// grid (8 * hpx * plan_cap), 512 threads (8 waves, one block-row each).
+__global__ __launch_bounds__(512) void k_mapped_av_idx(MappedAvArgs a, int hpx) {
   constexpr int D = 128;
-  const int item = blockIdx.x / n_oct, oct = blockIdx.x % n_oct;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const int hs = 8 * oct + wave;
-  if (hs >= a.n_recv) return;
+  constexpr int kVBytes = kBlock * D * 2;  // one V block: 16 KB
+  __shared__ __attribute__((aligned(16))) uint16_t vst[2][kBlock * D];  // V stages of two columns
+  __shared__ int tbl[kIdxRows][kMaxCols];  // stored block of union column x in wave w's row, or -1
+  __shared__ int upage[kMaxCols];          // V block (tiled index or page) of union column x
+  __shared__ int16_t posu[kMaxCols];       // union index of column c
+  __shared__ uint16_t ucol[kMaxCols];      // union columns, ascending
+  __shared__ uint8_t anyc[kMaxCols];
+  __shared__ int nu_s;
+  const int xcd = blockIdx.x % kXcds, m = blockIdx.x / kXcds;
+  const int item = m / hpx, hs = xcd * hpx + m % hpx;
+  if (hs >= a.n_recv || item >= a.plan_cap) return;
   const int code = ld_const(a.plan_pairs + item);
   if (code < 0) return;
-  const int s = code >> 7, pr = code & 127;
+  const int s = code >> 7, pg = code & 127;
   const int32_t n = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   const int kb0 = chunk_kb0(n, nk);  // block-row r of the queries is block-row kb0 + r of the sequence
   if (!seq_ok(a.vl, s, n, nk) || kb0 < 0) return;
-  const int nrb = (n + kBlock - 1) / kBlock;
-  const int r_long = nrb - 1 - pr;
-  if (r_long < pr) return;
-  const int n_pass = r_long > pr ? 2 : 1;
+  const int nrb = (n + kBlock - 1) / kBlock, mid = nrb / 2;  // rows mid.. ascending, 0..mid - 1 descending
+  const int up_hi = nrb - kIdxRows * pg, up_lo = max(mid, up_hi - kIdxRows);
+  if (up_lo >= up_hi) return;
+  const int n_pass = kIdxRows * pg < mid ? 2 : 1;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = ld_const(a.plan_order + (int64_t)s * a.n_recv + hs);
   const int j = ld_const(a.sender + (int64_t)s * a.sender_stride + h);
   const bool j_ok = j >= 0 && j < a.n_send;
   const int roff = ld_const(a.plan_roff + s), kroff = ld_const(a.plan_roff + a.vl.n_seqs + s);
   const int64_t q0 = cu_q_of(a.vl, s);
   // V of this head's V head: the sequence's tiled key blocks, or the head's page
-  // pool (then a block's page is its offset)
+  // pool (a column's V block is then its page)
   const bool paged = a.v_pages != nullptr;
   const int64_t vg = h / a.v_group;
+  const int nkb = (nk + kBlock - 1) / kBlock;
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
       a.vt + (paged ? vg * a.v_n_pages : vg * a.n_key_blocks + kroff) * (kBlock * D), (short)0,
-      (paged ? a.v_n_pages : (nk + kBlock - 1) / kBlock) * (kBlock * D * 2), kBufferFlags);
-  const int32_t* vpg = paged ? a.v_pages + (int64_t)s * a.v_page_stride : nullptr;
+      (paged ? a.v_n_pages : nkb) * kVBytes, kBufferFlags);
   const uint32_t a_lane = 32u * (lane & 31) + 16u * (lane >> 5);  // A operand: row L % 32, keys 8 (L / 32) ..
   const uint32_t v_lane = 16u * lane;
 
-  struct Set {
-    u32x4 x[2];  // A of row halves 0 and 1
-    u32x4 v[4];  // V of feature tiles 0..3
-  };
   for (int pass = 0; pass < n_pass; ++pass) {
-    const int r = pass ? pr : r_long;
-    const int rdir = pass;  // 1: columns descending
+    const bool rev = pass == 1;  // columns descending
+    const int lo = rev ? kIdxRows * pg : up_lo, hi = rev ? min(kIdxRows * pg + kIdxRows, mid) : up_hi;
+    const int R = lo + wave;  // this wave's block-row (of the queries)
+    const bool row_ok = R < hi;
+    const int ra_max = kb0 + hi - 1;  // last column of the union
+    // this wave's row: stored blocks beg .. end - 1 of its sender
+    int beg = 0, end = 0;
+    if (j_ok && row_ok) {
+      const int64_t gi = (int64_t)j * a.n_block_rows + roff + R;
+      beg = ld_const(a.row_ptr + gi);
+      end = a.row_end ? ld_const(a.row_end + gi) : ld_const(a.row_ptr + gi + 1);
+    }
+    // table: union of the rows' kept columns (ascending), and per wave the stored
+    // block of each union column
+    __syncthreads();  // the previous pass is done with the arrays
+    for (int c = tid; c <= ra_max; c += 512) anyc[c] = 0;
+    for (int x = lane; x <= ra_max; x += 64) tbl[wave][x] = -1;
+    __syncthreads();
+    for (int e = beg + lane; e < end; e += 64) {
+      const int c = a.col_idx[e];
+      if (c >= 0 && c <= kb0 + R) anyc[c] = 1;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int c0 = 0; c0 <= ra_max; c0 += 64) {
+        const int c = c0 + lane;
+        const bool f = c <= ra_max && anyc[c];
+        const uint64_t mk = __ballot(f);
+        if (f) {
+          const int x = base + __popcll(mk & ((1ull << lane) - 1ull));
+          ucol[x] = (uint16_t)c;
+          posu[c] = (int16_t)x;
+        }
+        base += __popcll(mk);
+      }
+      if (lane == 0) nu_s = base;
+    }
+    __syncthreads();
+    const int nu = __builtin_amdgcn_readfirstlane(nu_s);
+    for (int e = beg + lane; e < end; e += 64) {
+      const int c = a.col_idx[e];
+      if (c >= 0 && c <= kb0 + R) tbl[wave][posu[c]] = e;
+    }
+    for (int x = tid; x < nu; x += 512) {
+      const int c = ucol[x];
+      // a page outside the pool (a broken table) is clamped into it: memory-safe
+      upage[x] = paged ? min(max(a.v_pages[(int64_t)s * a.v_page_stride + c], 0), a.v_n_pages - 1)
+                       : min(c, nkb - 1);
+    }
+    __syncthreads();
+
     f32x16 acc[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) acc[u][dt] = f32x16{};
-    int beg = 0, nb = 0;
-    if (j_ok) {
-      const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
-      beg = ld_const(a.row_ptr + g);
-      nb = (a.row_end ? ld_const(a.row_end + g) : ld_const(a.row_ptr + g + 1)) - beg;
-    }
-    if (nb > 0) {
-      // Block k of the sweep (k = nb - 1 past the end): its stored index e and
-      // column c. (Integer arithmetic rather than selects: the compiler turns
-      // uniform selects into branches, and a branch in the loop makes it wait
-      // for every load in flight.)
-      auto blk = [&](int k) __attribute__((always_inline)) {
-        const int kk = min(k, nb - 1);
-        return beg + kk + rdir * (nb - 1 - 2 * kk);
+    if (nu > 0) {
+      // union index of sweep step x
+      auto xi = [&](int x) __attribute__((always_inline)) { return rev ? nu - 1 - x : x; };
+      // stored block of sweep step x in this wave's row (-1: not kept, or x past the end)
+      auto blk = [&](int x) __attribute__((always_inline)) { return x < nu ? lds_i32(&tbl[wave][xi(x)]) : -1; };
+      // V block of sweep step x into registers: 512 threads x 2 x 16 B; past the
+      // end the lane offset lies beyond the descriptor (zeros, no memory access)
+      auto load_v = [&](int x, u32x4 (&vr)[2]) __attribute__((always_inline)) {
+        const int pgx = x < nu ? lds_i32(&upage[xi(x)]) : 0;
+        const uint32_t lo = x < nu ? 16u * tid : kBufferOff;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) vr[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, lo + 8192u * i, pgx * kVBytes, 0);
       };
-      // Issue the loads of panel ks of block e (column c) into set S; okv = 0
-      // past the last block, where no load may touch memory: the A descriptor then
-      // holds no bytes, and the V loads take a lane offset of 2^31, past the end of
-      // the V descriptor (the range check of a raw buffer access covers the lane
-      // offset, not the scalar one), so both return zeros.
-      auto issue = [&](int ks, int e, int c, int okv, Set& S) __attribute__((always_inline)) {
+      auto store_v = [&](int b, const u32x4 (&vr)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&vst[b][8 * tid + 4096 * i]) = vr[i];
+      };
+      // A of panel ks of stored block e (e < 0: a descriptor of no bytes, zeros)
+      auto load_a = [&](int e, int ks, u32x4 (&x)[2]) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(a.vals + (int64_t)e * (kBlock * kBlock)), (short)0, okv * (kBlock * kBlock * 2),
-            kBufferFlags);
+            const_cast<uint16_t*>(a.vals + (int64_t)max(e, 0) * (kBlock * kBlock)), (short)0,
+            e >= 0 ? kBlock * kBlock * 2 : 0, kBufferFlags);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) S.x[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane + 1024u * u, 2048 * ks, 0);
-        const int vo = c * (kBlock * D * 2) + ks * 4096;  // c: the column's V block (see vblk)
-        const uint32_t vlo = v_lane | ((uint32_t)(1 - okv) << 31);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) S.v[dt] = __builtin_amdgcn_raw_buffer_load_b128(rv, vlo + 1024u * dt, vo, 0);
+        for (int u = 0; u < 2; ++u) x[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_lane + 1024u * u, 2048 * ks, 0);
       };
-      auto compute = [&](const Set& S) __attribute__((always_inline)) {
+      u32x4 A[4][2];  // panel ks of the current column in set ks (ring of four: three panels ahead)
+      u32x4 vr[2];
+      // prologue: V of step 0 staged, A of its panels 0..2 in flight
+      int e_cur = blk(0);
+      load_v(0, vr);
+      store_v(0, vr);
+      load_a(e_cur, 0, A[0]);
+      load_a(e_cur, 1, A[1]);
+      load_a(e_cur, 2, A[2]);
+      barrier_lds();
+      for (int x = 0; x < nu; ++x) {
+        const int e_nx = blk(x + 1);
+        load_v(x + 1, vr);
+        const uint32_t vb = lds_addr(&vst[x & 1][0]) + v_lane;
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int ks = 0; ks < 4; ++ks) {
+          // panel 4x + ks + 3: panel 3 of this column, or panels 0..2 of the next
+          if (ks == 0) load_a(e_cur, 3, A[3]);
+          else load_a(e_nx, ks - 1, A[ks - 1]);
+          if (e_cur >= 0) {
+            u32x4 vo[4];
+            asm volatile(
+                "ds_read_b128 %0, %4\n"
+                "ds_read_b128 %1, %4 offset:1024\n"
+                "ds_read_b128 %2, %4 offset:2048\n"
+                "ds_read_b128 %3, %4 offset:3072\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(vo[0]), "=&v"(vo[1]), "=&v"(vo[2]), "=&v"(vo[3])
+                : "v"(vb + 4096u * ks)
+                : "memory");
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[u][dt] = mfma32(as_bf16x8(S.x[u]), as_bf16x8(S.v[dt]), acc[u][dt]);
-      };
-      // V block of column c: its page (clamped into the pool: memory-safe for a
-      // broken table), or c itself
-      const int nkb = (nk + kBlock - 1) / kBlock;
-      auto vblk = [&](int c) __attribute__((always_inline)) {
-        return paged ? min(max(ld_const(vpg + c), 0), a.v_n_pages - 1) : min(max(c, 0), nkb - 1);
-      };
-      Set S0, S1, S2, S3;
-      int e_cur = blk(0), c_cur = vblk(ld_const(a.col_idx + e_cur));
-      issue(0, e_cur, c_cur, 1, S0);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(1, e_cur, c_cur, 1, S1);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(2, e_cur, c_cur, 1, S2);
-      __builtin_amdgcn_sched_barrier(0);
-      // One block (4 panels) per trip; panel t + 3 is issued before panel t is
-      // used. The scheduling barriers keep the loads in this order, so that a
-      // step waits only for its own set (three later sets stay in flight). The
-      // next block's column is read at the top of the trip, a step before use.
-      for (int k = 0; k < nb; ++k) {
-        const int e_nx = blk(k + 1), ok_nx = k + 1 < nb;
-        const int c_nx = vblk(ld_const(a.col_idx + e_nx));
-        issue(3, e_cur, c_cur, 1, S3);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(S0);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(0, e_nx, c_nx, ok_nx, S0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(S1);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(1, e_nx, c_nx, ok_nx, S1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(S2);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(2, e_nx, c_nx, ok_nx, S2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(S3);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) acc[u][dt] = mfma32(as_bf16x8(A[ks][u]), as_bf16x8(vo[dt]), acc[u][dt]);
+          }
+        }
+        store_v((x + 1) & 1, vr);
+        barrier_lds();
         e_cur = e_nx;
-        c_cur = c_nx;
       }
     }
     // D[m = row][n = feature]: row = 32 u + 8 (v / 4) + 4 (L / 32) + v % 4, feature = 32 dt + L % 32
-    const int row0 = kBlock * r;
+    if (row_ok) {
+      const int row0 = kBlock * R;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = row0 + 32 * u + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (row >= n) continue;
-          const int64_t o = ((int64_t)h * a.vl.total_q + q0 + row) * D + 32 * dt + (lane & 31);
-          if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[u][dt][v]);
-          else reinterpret_cast<float*>(a.out)[o] = acc[u][dt][v];
-        }
-    // drain the stores before the next row's loads: with stores still counted,
+          for (int v = 0; v < 16; ++v) {
+            const int row = row0 + 32 * u + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row >= n) continue;
+            const int64_t o = ((int64_t)h * a.vl.total_q + q0 + row) * D + 32 * dt + (lane & 31);
+            if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[u][dt][v]);
+            else reinterpret_cast<float*>(a.out)[o] = acc[u][dt][v];
+          }
+    }
+    // drain the stores before the next pass's loads: with stores still counted,
     // the compiler could not size the loop's waits and would drain every step
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   }
@@ -891,6 +943,11 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win)
   const int last = nk - nq + i;
   const int64_t row_off = map_seq_off(a.vl, s, a.packed) + map_row_off(i, nq, nk, a.packed);
   const int64_t k0 = cu_k_of(a.vl, s);
+  // bf16 token-major V whose rows start on 16-byte boundaries takes the
+  // pipelined loop in the 1024-thread form (batches of kPipe loads per thread;
+  // two batches' registers fit the 128 that 1024 threads allow)
+  constexpr int kPipe = (!KEY_MAJOR && NT == 1024 && std::is_same<VT, uint16_t>::value) ? 6 : 0;
+  const bool v_al16 = (reinterpret_cast<uintptr_t>(a.v) & 15) == 0;
   constexpr int kChunks = D / 8;          // 8-feature chunks per key (token-major)
   constexpr int kSlots = NT / kChunks;    // keys per pass (token-major)
   float accv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -932,6 +989,56 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win)
           for (int e = 0; e < 8; ++e) part = fmaf(j + e < wlen ? bj[j + e] : 0.0f, v[e], part);
         }
         acck[rnd] += part;
+      }
+    } else if (kPipe > 0 && v_al16) {
+      // bf16 V with 1024 threads (a launch of few rows), software-pipelined: a
+      // thread's keys are ks, ks + kSlots, ...; they go in batches of kPipe
+      // 16-byte loads (kept raw), and the next batch is in flight while the
+      // current one is multiplied. Loads past the thread's keys
+      // take a lane offset past the descriptor (zeros, no memory access) and
+      // weight 0, so the sums equal the unpipelined loop's term for term.
+      const int fc = tid % kChunks, ks = tid / kChunks;
+      // the window's V rows (uniform: the descriptor lives in scalar registers)
+      const uint64_t vaddr = reinterpret_cast<uint64_t>(reinterpret_cast<const uint16_t*>(a.v) +
+                                                        ((int64_t)(h / a.v_group) * a.vl.total_k + k0 + w0) * D);
+      uint16_t* vwin = reinterpret_cast<uint16_t*>(
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(vaddr >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)vaddr));
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          vwin, (short)0, __builtin_amdgcn_readfirstlane(wlen * D * 2), kBufferFlags);
+      const int nt = wlen > ks ? (wlen - ks + kSlots - 1) / kSlots : 0;  // this thread's keys
+      const int nb = (nt + kPipe - 1) / kPipe;
+      // the lane's byte offset in the window; key t of the thread adds the uniform
+      // t * kSlots rows as the scalar offset (the range check covers the lane offset)
+      const uint32_t vlane = (uint32_t)((ks * D + 8 * fc) * 2);
+      u32x4 x0[kPipe > 0 ? kPipe : 1], x1[kPipe > 0 ? kPipe : 1];
+      auto load = [&](int b, auto& x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kPipe; ++u) {
+          const int t = kPipe * b + u;
+          x[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, t < nt ? vlane : kBufferOff, t * (kSlots * D * 2), 0);
+        }
+      };
+      auto use = [&](int b, const auto& x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kPipe; ++u) {
+          const int t = kPipe * b + u;
+          const float bw = t < nt ? bj[min(ks + t * kSlots, wlen - 1)] : 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            accv[2 * e] = fmaf(bw, __uint_as_float(x[u][e] << 16), accv[2 * e]);
+            accv[2 * e + 1] = fmaf(bw, __uint_as_float(x[u][e] & 0xffff0000u), accv[2 * e + 1]);
+          }
+        }
+      };
+      if (nb > 0) load(0, x0);
+      for (int b = 0; b < nb; b += 2) {
+        load(b + 1, x1);  // past the thread's keys: zeros, no memory access
+        use(b, x0);
+        if (b + 1 < nb) {
+          load(b + 2, x0);
+          use(b + 1, x1);
+        }
       }
     } else {
       // 8 independent 16-byte loads in flight per thread, then their products
@@ -1082,10 +1189,10 @@ hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_oct = (a.n_recv + 7) / 8;
+  const int hpx = (a.n_recv + kXcds - 1) / kXcds;  // heads per XCD
   {
     KernelTimer kt_("k_mapped_av_idx", st);
-    hipLaunchKernelGGL(k_mapped_av_idx, dim3((unsigned)(a.plan_cap * n_oct)), dim3(512), 0, st, a, n_oct);
+    hipLaunchKernelGGL(k_mapped_av_idx, dim3((unsigned)(kXcds * hpx * a.plan_cap)), dim3(512), 0, st, a, hpx);
   }
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // Microbenchmarks of the chip's ceilings that the kernels are measured against:
-// streaming HBM read and copy bandwidth, the sustained rate of the 32x32x16 bf16
-// matrix instruction, and the bandwidth from the L2 caches into the compute units
+// streaming HBM read, write and copy bandwidth, the rate of the vector unit's
+// exp2 and fused multiply-add, the sustained rate of the 32x32x16 bf16 matrix
+// instruction, and the bandwidth from the L2 caches into the compute units
 // (every workgroup re-reads one small buffer, so after the first pass the bytes
 // come from each XCD's L2, in the 1 KB-per-instruction shape the fused pass
 // uses). Each entry point enqueues one launch on `stream`; the caller times it.
@@ -31,6 +32,30 @@ __global__ __launch_bounds__(512) void k_probe_copy(const u32x4* __restrict__ sr
                                                      int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// grid-stride 16-byte stores of n16 chunks (a streaming write).
+__global__ __launch_bounds__(512) void k_probe_write(u32x4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const uint32_t v = threadIdx.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = u32x4{v, v, v, v};
+}
+
+// Every lane runs `iters` rounds of 8 independent chains of one vector operation
+// (kind 0: exp2, the hardware transcendental; kind 1: fused multiply-add).
+template <int KIND>
+__global__ __launch_bounds__(256) void k_probe_valu(int iters, float* out) {
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)(threadIdx.x + i) * 1e-3f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = KIND == 0 ? __builtin_amdgcn_exp2f(x[i]) : fmaf(x[i], 0.999f, 0.5f);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r += x[i];
+  out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
 
 // Every wave runs `iters` rounds of 8 independent 32x32x16 bf16 products.
@@ -93,6 +118,22 @@ int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void
     return CMA_EINVAL;
   hipLaunchKernelGGL(k_probe_copy, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, void* stream) {
+  if (!dst || bytes < 16 || n_wg < 1 || (reinterpret_cast<uintptr_t>(dst) & 15)) return CMA_EINVAL;
+  hipLaunchKernelGGL(k_probe_write, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<u32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+int cma_probe_valu(int32_t kind, int32_t n_wg, int32_t iters, float* out, void* stream) {
+  if (!out || n_wg < 1 || iters < 1 || (kind != 0 && kind != 1)) return CMA_EINVAL;
+  if (kind == 0)
+    hipLaunchKernelGGL(k_probe_valu<0>, dim3(n_wg), dim3(256), 0, static_cast<hipStream_t>(stream), iters, out);
+  else
+    hipLaunchKernelGGL(k_probe_valu<1>, dim3(n_wg), dim3(256), 0, static_cast<hipStream_t>(stream), iters, out);
   return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
 }
 

@@ -319,13 +319,13 @@ __device__ __forceinline__ float online_update(const float t[32], float& m, floa
   float bm = -INFINITY;
 #pragma unroll
   for (int e = 0; e < 32; ++e) bm = fmaxf(bm, t[e]);
-  bm = fmaxf(bm, xor_lane(bm, 32));
+  bm = pair32_max(bm);
   const float mn = fmaxf(m, bm);
   if (mn == -INFINITY) return 0.0f;
   float s = 0.0f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) s += exp2f_fast(t[e] - mn);
-  s += xor_lane(s, 32);
+  s = pair32_add(s);
   l = l * exp2f_fast(m - mn) + s;
   m = mn;
   return s;
@@ -337,8 +337,8 @@ __device__ __forceinline__ float online_update_acc(const f32x16 t[2], float& m, 
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) bm = fmaxf(bm, t[kt][v]);
-  bm = fmaxf(bm, xor_lane(bm, 32));
+    for (int v = 0; v < 16; ++v) bm = vmax(bm, t[kt][v]);
+  bm = pair32_max(bm);
   const float mn = fmaxf(m, bm);
   if (mn == -INFINITY) return 0.0f;
   float s = 0.0f;
@@ -346,7 +346,7 @@ __device__ __forceinline__ float online_update_acc(const f32x16 t[2], float& m, 
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) s += exp2f_fast(t[kt][v] - mn);
-  s += xor_lane(s, 32);
+  s = pair32_add(s);
   l = l * exp2f_fast(m - mn) + s;
   m = mn;
   return s;
@@ -362,23 +362,27 @@ constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100;
 // Requires scale_l2 > 0, so that the largest raw score gives the largest logit;
 // the exponent is one fused multiply-add, 2^(s * scale_l2 - max).
 __device__ __forceinline__ float online_update_raw(const f32x16 acc[2], float scale_l2, float& m, float& l) {
+  // IEEE maximum (NaN-propagating) needs no quieting of the matrix products'
+  // results and fuses into three-operand instructions
   float b4[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) b4[u] = fmaxf(acc[0][u], acc[0][u + 4]);
+  for (int u = 0; u < 4; ++u) b4[u] = vmax(acc[0][u], acc[0][u + 4]);
 #pragma unroll
-  for (int v = 8; v < 16; ++v) b4[v & 3] = fmaxf(b4[v & 3], acc[0][v]);
+  for (int v = 8; v < 16; ++v) b4[v & 3] = vmax(b4[v & 3], acc[0][v]);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) b4[v & 3] = fmaxf(b4[v & 3], acc[1][v]);
-  float bm = fmaxf(fmaxf(b4[0], b4[1]), fmaxf(b4[2], b4[3]));
-  bm = fmaxf(bm, xor_lane(bm, 32)) * scale_l2;
+  for (int v = 0; v < 16; ++v) b4[v & 3] = vmax(b4[v & 3], acc[1][v]);
+  float bm = vmax(vmax(b4[0], b4[1]), vmax(b4[2], b4[3]));
+  bm = pair32_max(bm) * scale_l2;
   const float mn = fmaxf(m, bm);
-  float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float s4[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s4[v] = exp2f_fast(fmaf(acc[0][v], scale_l2, -mn));
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s4[v & 3] += exp2f_fast(fmaf(acc[kt][v], scale_l2, -mn));
+    for (int v = 4 * (1 - kt); v < 16; ++v) s4[v & 3] += exp2f_fast(fmaf(acc[kt][v], scale_l2, -mn));
   float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-  s += xor_lane(s, 32);
+  s = pair32_add(s);
   l = l * exp2f_fast(m - mn) + s;
   m = mn;
   return s;

@@ -11,6 +11,13 @@
  *                  uint32 (written only in a case that does not occur).
  * cma_probe_copy:  the same grid copies `bytes` from src to dst (16-byte aligned):
  *                  read + write bandwidth.
+ * cma_probe_write: the same grid writes `bytes` to dst (16-byte aligned) with
+ *                  16-byte stores: HBM write bandwidth.
+ * cma_probe_valu:  n_wg workgroups of 256 threads; every lane runs `iters` rounds
+ *                  of 8 independent chains of one vector operation (kind 0: the
+ *                  hardware exp2, kind 1: fused multiply-add); out: device,
+ *                  n_wg * 256 floats. Lane-operations per clock per SIMD give the
+ *                  operation's issue rate.
  * cma_probe_mfma:  n_wg workgroups of 4 waves; every wave runs `iters` rounds of 8
  *                  independent 32x32x16 bf16 matrix products (2 * 32 * 32 * 16
  *                  flops each); out: device, n_wg * 256 floats.
@@ -33,6 +40,8 @@ extern "C" {
 
 int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, void* sink, void* stream);
 int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void* stream);
+int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, void* stream);
+int cma_probe_valu(int32_t kind, int32_t n_wg, int32_t iters, float* out, void* stream);
 int cma_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* stream);
 int cma_probe_l2(const void* buf, int32_t bytes, int32_t iters, int32_t n_wg, void* sink, void* stream);
 
