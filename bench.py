@@ -96,6 +96,7 @@ def peaks(reps=5):
     lib.cma_probe_l2.argtypes = [P, I32, I32, I32, P, P]
     lib.cma_probe_write.argtypes = [P, I64, I32, P]
     lib.cma_probe_valu.argtypes = [I32, I32, I32, P, P]
+    lib.cma_probe_lds.argtypes = [I32, I32, P, P]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     st = torch.cuda.current_stream().cuda_stream
 
@@ -112,7 +113,7 @@ def peaks(reps=5):
             ms.append(e0.elapsed_time(e1))
         return float(np.median(ms))
 
-    out = {"probe": "ceilings", "compute_units": cus, "reps": reps}
+    out = {"probe": "ceilings", "compute_units": cus, "reps": reps, "clocks_before": clocks()}
     big = 4 << 30
     a = torch.ones(big // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(cus * 8 * 512, dtype=torch.int32, device="cuda")
@@ -143,7 +144,30 @@ def peaks(reps=5):
     moved = cus * 2 * l2it * l2b
     out["l2_to_cu_GBps"] = round(moved / (t * 1e-3) / 1e9, 1)
     out["l2_to_cu_B_per_clk_per_cu_at_2p4GHz"] = round(moved / (t * 1e-3) / 2.4e9 / cus, 1)
+    # LDS: one 512-thread workgroup per CU (64 KB each), 16-byte reads
+    lds_it = 4096
+    t = med(lambda: lib.cma_probe_lds(cus, lds_it, sink.data_ptr(), st))
+    lds_bytes = cus * 512 * lds_it * 8 * 16
+    out["lds_read_B_per_clk_per_cu_at_2p4GHz"] = round(lds_bytes / (t * 1e-3) / 2.4e9 / cus, 1)
+    out["clocks_after"] = clocks()
     print(json.dumps(out), flush=True)
+
+
+def clocks():
+    """The current shader and memory clocks as rocm-smi reports them (a child
+    process; None where the tool is missing or says nothing)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    got = {}
+    for line in r.stdout.splitlines():
+        low = line.lower()
+        for key in ("sclk", "mclk", "fclk"):
+            if key in low and "mhz" in low and key not in got:
+                got[key] = line.split(":", 2)[-1].strip()
+    return got or None
 
 
 def log(*a):
@@ -681,12 +705,13 @@ def main():
 
 
 def headline_figures(reps=10):
-    """Single-sequence headline figures on one 8192-token prompt (32 sender heads,
-    tau = 0.95; 24 receiver heads, learned M, token-major V): H2 = 8192 / t(block
-    compression: statistics, scan, extraction) and H1 = 8192 / t(mapped x V: V
-    tiling and the fused pass), each time the median over ``reps`` calls from HIP
-    events on the launch stream around the whole call, with the per-kernel averages
-    beside them."""
+    """Headline figures. On one 8192-token prompt (32 sender heads, tau = 0.95; 24
+    receiver heads, learned M, token-major V): H2 = 8192 / t(block compression:
+    statistics, scan, extraction) and H1 = 8192 / t(mapped x V: V tiling and the
+    fused pass). On four 8192-token prompts (28 sender heads, 64 receiver heads with
+    one sender each): H3 = 4 * 8192 / (t(block compression) + t(indexed mapped x
+    V)). Each time is the median over ``reps`` calls from HIP events on the launch
+    stream around the whole call, with the per-kernel averages beside them."""
     import torch
     import cross_model_attention_causal_amd as cma
     import synth
@@ -726,12 +751,38 @@ def headline_figures(reps=10):
     t_c, k_c = timed(comp)
     t_m, k_m = timed(mav)
     nnz = int(res["bsr"]["nnz"].item())
+    del res["bsr"], res["O"]
+    # H3: the serving mix's four 8192-token prompts, one mapped layer: 28 sender
+    # heads compressed, then 64 receiver heads through the indexed pass (one sender
+    # per head; seeded random senders stand in for the cosine argmax)
+    P3, Hs3, Hr3 = 4, 28, 64
+    x3 = synth.attention_inputs(20260035, Hs3, [n] * P3, d=128)
+    vl3 = cma.Varlen(x3["cu_q"])
+    q3, k3, sc3, bi3 = bf(x3["q"]), bf(x3["k"]), f32(x3["scale"]), f32(x3["bias"])
+    v3 = bf(synth.values(20260036, Hr3, P3 * n, 128))
+    snd = np.random.Generator(np.random.PCG64(np.random.SeedSequence(20260037))).integers(0, Hs3, (P3, Hr3))
+    snd3 = torch.from_numpy(snd.astype(np.int32)).to("cuda")
+    ws3, wsv3 = cma.Workspace(), cma.Workspace()
+
+    def comp3():
+        res["bsr3"] = cma.block_compress(q3, k3, sc3, bi3, vl3, tau, workspace=ws3)
+
+    def mav3():
+        res["O3"] = cma.mapped_av(res["bsr3"], Hs3, snd3, Hr3, v3, vl3, workspace=wsv3)
+
+    t_c3, k_c3 = timed(comp3)
+    t_m3, k_m3 = timed(mav3)
     return {"workload": f"one {n}-token prompt: block compression of {H} sender heads (tau={tau}), then "
                         f"mapped x V of {y['n_recv']} receiver heads (learned M, token-major bf16 V, d=128)",
             "H1_tokens_per_s": round(n / (t_m * 1e-3), 1), "H1_ms": round(t_m, 4),
             "H2_tokens_per_s": round(n / (t_c * 1e-3), 1), "H2_ms": round(t_c, 4),
             "kept_block_fraction": round(nnz / (H * (n // 64) * (n // 64 + 1) // 2), 4),
-            "kernel_ms": {**k_c, **k_m}}
+            "kernel_ms": {**k_c, **k_m},
+            "H3_workload": f"{P3} prompts of {n} tokens, one mapped layer: block compression of {Hs3} sender "
+                           f"heads (tau={tau}), then {Hr3} receiver heads with one sender each (indexed pass, "
+                           "token-major bf16 V)",
+            "H3_tokens_per_s": round(P3 * n / ((t_c3 + t_m3) * 1e-3), 1), "H3_ms": round(t_c3 + t_m3, 4),
+            "H3_kernel_ms": {**k_c3, **k_m3}}
 
 
 def check_outputs(x, state, O, od, P, n, tau):

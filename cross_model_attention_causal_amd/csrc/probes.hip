@@ -58,6 +58,28 @@ __global__ __launch_bounds__(256) void k_probe_valu(int iters, float* out) {
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = r;
 }
 
+// Every lane reads 16 bytes per instruction from LDS, 8 reads in flight, lane L
+// of a wave at byte 16 L of a 1 KB run (the pattern the kernels' operand reads
+// use, free of bank conflicts), `iters` rounds over a 64 KB buffer.
+__global__ __launch_bounds__(512) void k_probe_lds(int iters, uint32_t never, uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[16384];  // 64 KB
+  for (int i = threadIdx.x; i < 16384; i += 512) buf[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t x = 0;
+  for (int it = 0; it < iters; ++it) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int run = (it * 8 + u + wave * 8) & 63;  // 64 runs of 1 KB
+      v[u] = *reinterpret_cast<const u32x4*>(&buf[run * 256 + 4 * lane]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][3];
+  }
+  if (x == never) sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
 // Every wave runs `iters` rounds of 8 independent 32x32x16 bf16 products.
 __global__ __launch_bounds__(256) void k_probe_mfma(int iters, float* out) {
   const int lane = threadIdx.x & 63;
@@ -140,6 +162,13 @@ int cma_probe_valu(int32_t kind, int32_t n_wg, int32_t iters, float* out, void* 
 int cma_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* stream) {
   if (!out || n_wg < 1 || iters < 1) return CMA_EINVAL;
   hipLaunchKernelGGL(k_probe_mfma, dim3(n_wg), dim3(256), 0, static_cast<hipStream_t>(stream), iters, out);
+  return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
+}
+
+int cma_probe_lds(int32_t n_wg, int32_t iters, void* sink, void* stream) {
+  if (!sink || n_wg < 1 || iters < 1) return CMA_EINVAL;
+  hipLaunchKernelGGL(k_probe_lds, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream), iters, 0x9e3779b9u,
+                     static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
 }
 

@@ -21,6 +21,10 @@
  * cma_probe_mfma:  n_wg workgroups of 4 waves; every wave runs `iters` rounds of 8
  *                  independent 32x32x16 bf16 matrix products (2 * 32 * 32 * 16
  *                  flops each); out: device, n_wg * 256 floats.
+ * cma_probe_lds:   n_wg workgroups of 512 threads (one per CU at a time) read a
+ *                  64 KB LDS buffer `iters` times per lane in 16-byte reads, 8 in
+ *                  flight, each wave instruction one conflict-free 1 KB run: the
+ *                  LDS read bandwidth of a CU. sink: device, n_wg * 512 uint32.
  * cma_probe_l2:    n_wg workgroups of 8 waves each read the same `bytes` (a
  *                  multiple of 64 KB, small enough to stay in an XCD's 4 MB L2)
  *                  `iters` times with 1 KB-per-wave buffer loads, 8 in flight per
@@ -43,6 +47,7 @@ int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void
 int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, void* stream);
 int cma_probe_valu(int32_t kind, int32_t n_wg, int32_t iters, float* out, void* stream);
 int cma_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* stream);
+int cma_probe_lds(int32_t n_wg, int32_t iters, void* sink, void* stream);
 int cma_probe_l2(const void* buf, int32_t bytes, int32_t iters, int32_t n_wg, void* sink, void* stream);
 
 #ifdef __cplusplus
