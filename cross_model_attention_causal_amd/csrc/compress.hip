@@ -80,8 +80,9 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   __shared__ float sm[KP][64 * G], sl[KP][64 * G];
   __shared__ float lse_s[64 * G];
   __shared__ float mass_a[G][kMaxBlockRows];
-  __shared__ float wts_a[G][kMaxBlockRows];
+  __shared__ float wts_a[G][kMaxBlockRows];  // weights in column order, then in rank order
   __shared__ int order_a[G][kMaxBlockRows];
+  __shared__ __attribute__((aligned(16))) uint64_t key_a[G][kMaxBlockRows];
   __shared__ uint32_t kept_a[G][kWords];
   __shared__ int kcount_a[G];
   __shared__ float total_a[G];
@@ -207,6 +208,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   float* mass = mass_a[gr];
   float* wts = wts_a[gr];
   int* order = order_a[gr];
+  uint64_t* key = key_a[gr];
   uint32_t* kept = kept_a[gr];
   int32_t roff, kroff;
   int64_t tri_off;
@@ -256,32 +258,36 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     }
     __syncthreads();
     const float total = total_a[gr];
-    // a NaN weight (only from non-finite inputs) ranks as 0, so that the order
-    // below stays a strict total order and the kept set a set of columns of
-    // this row with exactly kcount members
-    for (int c = tl; c < nb; c += NTR) {
-      const float w = mass[c] / total;
-      wts[c] = w == w ? w : 0.0f;
+    // Weights, and sort keys: a weight's bits (nonnegative floats order as
+    // unsigned integers) above the complemented column, so that one unsigned
+    // comparison orders blocks weight descending, column ascending. A NaN weight
+    // (only from non-finite inputs) ranks as 0, so that the order stays a strict
+    // total order and the kept set a set of columns of this row with exactly
+    // kcount members. Slots from nb up to the next multiple of 16 get key 0,
+    // which no block's key is below.
+    const int nb16 = (nb + 15) & ~15;
+    for (int c = tl; c < nb16; c += NTR) {
+      const float w = c < nb ? mass[c] / total : 0.0f;
+      const float wv = w == w ? w : 0.0f;
+      key[c] = c < nb ? ((uint64_t)__float_as_uint(wv) << 32) | (uint64_t)(0xffffffffu - (uint32_t)c) : 0ull;
     }
     __syncthreads();
-    // rank of block c in the order weight descending, column ascending: wave wl
-    // of the row takes blocks wl, wl + NWR, ...; lane L holds the weights of
-    // blocks L + 64 j and each comparison is one ballot over the wave
-    {
-      float w2[kMaxBlockRows / 64];
+    // rank of block c = the number of blocks ahead of it: each thread of the row
+    // takes its blocks and compares their keys with every key of the row (16 per
+    // step, eight broadcast reads in flight); the block's weight goes to its
+    // rank's slot
+    for (int c = tl; c < nb; c += NTR) {
+      const uint64_t kc = key[c];
+      int rank = 0;
+      for (int c2 = 0; c2 < nb16; c2 += 16) {
+        uint64_t k16[16];
 #pragma unroll
-      for (int j = 0; j < kMaxBlockRows / 64; ++j) w2[j] = lane + 64 * j < nb ? wts[lane + 64 * j] : -INFINITY;
-      for (int c = wl; c < nb; c += NWR) {
-        const float wc = wts[c];
-        int rank = 0;
+        for (int e = 0; e < 16; ++e) k16[e] = key[c2 + e];
 #pragma unroll
-        for (int j = 0; j < kMaxBlockRows / 64; ++j) {
-          const int c2 = lane + 64 * j;
-          const bool ahead = c2 < nb && (w2[j] > wc || (w2[j] == wc && c2 < c));
-          rank += __popcll(__ballot(ahead));
-        }
-        if (lane == 0) order[rank] = c;
+        for (int e = 0; e < 16; ++e) rank += (int)(k16[e] > kc);
       }
+      order[rank] = c;
+      wts[rank] = __uint_as_float((uint32_t)(kc >> 32));
     }
     __syncthreads();
     // running sum in that order (one wave per row: 4 consecutive ranks per lane,
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int x = 4 * lane + e;
-        run += x < nb ? wts[order[x]] : 0.0f;
+        run += x < nb ? wts[x] : 0.0f;
         cum[e] = run;
       }
       float pre = run;
