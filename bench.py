@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-check", action="store_true",
                     help="skip the check of the last step's outputs (sampled fused-pass rows, the decode "
                          "rows and prompt 0's head map) against the oracle")
+    ap.add_argument("--no-measured-ceilings", dest="measured_ceilings", action="store_false",
+                    help="skip the probes run after the timed steps (the stages' fractions of the "
+                         "measured ceilings)")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--stage-figures", action="store_true",
                     help="instead of the step: time each stage at its own workload (512-token head "
@@ -82,6 +85,11 @@ def calibrate_copy():
 
 
 def peaks(reps=5):
+    """Print the chip's ceilings as the library's probes measure them (one JSON line)."""
+    print(json.dumps(measure_ceilings(reps)), flush=True)
+
+
+def measure_ceilings(reps=5):
     """The chip's ceilings as the library's probes measure them (cma_probe.h): median
     of ``reps`` launches each, timed with HIP events on the current stream."""
     import ctypes
@@ -150,7 +158,9 @@ def peaks(reps=5):
     lds_bytes = cus * 512 * lds_it * 8 * 16
     out["lds_read_B_per_clk_per_cu_at_2p4GHz"] = round(lds_bytes / (t * 1e-3) / 2.4e9 / cus, 1)
     out["clocks_after"] = clocks()
-    print(json.dumps(out), flush=True)
+    del buf, sink, o
+    torch.cuda.empty_cache()
+    return out
 
 
 def clocks():
@@ -174,13 +184,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def stage_figures(reps=5):
+def stage_figures(reps=20, warmup=3):
     """Each stage at its own workload: the 512-token head mapping (maps of 336 small-
     and 2560 large-model heads, the 2560 x 336 cosine), the 32-head x 8192-token
     compression at tau 0.95, the fused pass of 24 receiver heads over it, and
     one mapped layer of the varlen serving mix (its prefill chain and one decode
     step). Per kernel: average launch time from HIP events on the launch stream, the
-    algorithmic work per launch, and the fraction of the roofline that binds it."""
+    algorithmic work per launch, and the fraction of the roofline that binds it; per
+    workload call: p10, median and p90 of ``reps`` timed calls after ``warmup``."""
     import torch
     import cross_model_attention_causal_amd as cma
     import synth
@@ -191,16 +202,22 @@ def stage_figures(reps=5):
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
 
     def timed(fn, work):
-        fn()
+        for _ in range(warmup):
+            fn()
         torch.cuda.synchronize()
         cma.timing_reset()
         cma.timing_enable(True)
-        for _ in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record()
+        for i in range(reps):
             fn()
+            evs[i + 1].record()
         torch.cuda.synchronize()
         cma.timing_enable(False)
         kt = cma.timing_collect()
-        out = {}
+        call = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)])
+        out = {"call_ms": {"p10": round(float(np.percentile(call, 10)), 4), "median": round(float(np.median(call)), 4),
+                           "p90": round(float(np.percentile(call, 90)), 4), "reps": reps}}
         for name, (ms, cnt) in kt.items():
             e = dict(ms=round(ms / cnt, 4), launches_per_call=cnt // reps)
             if name in work:
@@ -235,6 +252,7 @@ def stage_figures(reps=5):
                   {"k_gram_bf16": ("mfma", 2 * Hr * Hs * L)})
     print(json.dumps({"workload": f"head mapping: one {n}-token prompt, {Hs} small-model and {Hr} large-model "
                                   "maps (d=128, bf16), packed causal, and the Hr x Hs cosine with argmax",
+                      "call_ms": {"maps": k_maps.pop("call_ms"), "cosine": k_cos.pop("call_ms")},
                       "kernels": {**k_maps, **k_cos}}), flush=True)
     del st
     # the same head mapping with the large model's maps formed inside the Gram
@@ -247,7 +265,7 @@ def stage_figures(reps=5):
     s_bytes = Hs * (2 * n * 128 * 2 + n * n * 2)
     k_fused = timed(fused, {"k_attn_maps_short": ("hbm", s_bytes),
                             "k_head_map_fused": ("mfma", 2 * Hr * Hs * L + 2 * Hr * L * 128)})
-    tot = sum(e["ms"] * e["launches_per_call"] for e in k_fused.values())
+    tot = sum(e["ms"] * e["launches_per_call"] for e in k_fused.values() if "launches_per_call" in e)
     print(json.dumps({"workload": f"fused head mapping: the same {Hr} x {Hs} problem, {Hs} small-model maps stored "
                                   f"(dense bf16), the {Hr} large-model maps formed on chip inside the Gram "
                                   "(work: Gram products + one QK^T pass over the causal entries)",
@@ -336,8 +354,8 @@ def stage_figures(reps=5):
     k_stack = timed(lambda: cma.mapped_av(res["bsr"], Hs, M2, 2 * Hr, V2, vl, workspace=wsv, v_heads=2 * Hv), {})
     print(json.dumps({"workload": f"two receivers of {Hr} heads ({Hv} V heads each) on the one sender state: two "
                                   "calls against one call with the heads stacked",
-                      "two_calls_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_two.values()), 4),
-                      "stacked_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_stack.values()), 4),
+                      "two_calls_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_two.values() if "launches_per_call" in v), 4),
+                      "stacked_ms": round(sum(v["ms"] * v["launches_per_call"] for v in k_stack.values() if "launches_per_call" in v), 4),
                       "kernels_two_calls": k_two, "kernels_stacked": k_stack}), flush=True)
     del res, q, k, M, V, Vg, M2, V2, ws, wsv
 
@@ -394,7 +412,7 @@ def stage_figures(reps=5):
                             "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2),
                             "k_mapped_av_idx": ("mfma", idx_flops),
                             "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2)})
-    pre_ms = sum(e["ms"] * e["launches_per_call"] for e in k_pre.values())
+    pre_ms = sum(e["ms"] * e["launches_per_call"] for e in k_pre.values() if "launches_per_call" in e)
     # the general fused pass on the same problem, with the argmax as a one-hot M
     st["M"] = cma.onehot_mix(st["arg"], Hs)
     k_gen = timed(lambda: cma.mapped_av(st["bsr"], Hs, st["M"], Hr, v, vl_p, q_rows=tokens, workspace=wsv),
@@ -417,7 +435,7 @@ def stage_figures(reps=5):
         st["od"] = cma.mapped_av(("dense", rows, cma.DENSE), Hs, Md, Hr, v, vl_d, q_rows=nsh)
     k_dec = timed(decode, {"k_attn_rows": ("hbm", Hs * nsh * ctx * (128 * 2 + 4)),
                            "k_mapped_av_dense": ("hbm", Hr * nsh * ctx * (128 * 2 + 4))})
-    dec_ms = sum(e["ms"] * e["launches_per_call"] for e in k_dec.values())
+    dec_ms = sum(e["ms"] * e["launches_per_call"] for e in k_dec.values() if "launches_per_call" in e)
     print(json.dumps({"workload": f"serving mix, one mapped layer, one decode step: {nsh} prompts at context "
                                   f"{ctx}, sender rows over {Hs} heads and the one-hot mapped x V of {Hr} receiver "
                                   "heads", "kernel_ms_per_step": round(dec_ms, 4), "kernels": k_dec}), flush=True)
@@ -614,25 +632,34 @@ def main():
     b_rows = Hs * P * (128 * 2 + (n + 1) * (128 * 2 + 4))
     # cosine Gram: MFMA flops over all receiver x sender pairs
     f_gram = 2 * P * Hr * Hs * L
+    # (bound, work per launch, share of the bytes that are written)
     specs = {
-        "k_mapped_av_bsr": ("hbm", b_mav),
-        "k_block_stats": ("mfma", f_stats),
-        "k_block_extract": ("hbm", b_ext),
-        "k_attn_maps_short": ("hbm", b_maps),
-        "k_attn_rows": ("hbm", b_rows),
-        "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2),
-        "k_gram_bf16": ("mfma", f_gram),
+        "k_mapped_av_bsr": ("hbm", b_mav, Hr * tokens * 128 * 2 / b_mav),
+        "k_block_stats": ("mfma", f_stats, 0.0),
+        "k_block_extract": ("hbm", b_ext, nnz * 8196 / b_ext),
+        "k_attn_maps_short": ("hbm", b_maps, L * 2 / (2 * tau_t * 128 * 2 + L * 2)),
+        "k_attn_rows": ("hbm", b_rows, 4 / (128 * 2 + 4)),
+        "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2, 0.5),
+        "k_gram_bf16": ("mfma", f_gram, 0.0),
     }
-    for name, (bound, work) in specs.items():
+    # the probes' ceilings, measured after the timed steps (the measured-ceiling
+    # fraction of an HBM kernel prices its reads at the read probe's rate and its
+    # writes at the write probe's)
+    cei = measure_ceilings(3) if args.measured_ceilings else None
+    for name, (bound, work, wf) in specs.items():
         ms, cnt = per_launch(name)
         if not cnt:
             continue
         if bound == "hbm":
             ach, peak, unit = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+            mpeak = 1.0 / ((1.0 - wf) / cei["hbm_read_GBps"] + wf / cei["hbm_write_GBps"]) if cei else None
         else:
             ach, peak, unit = work / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+            mpeak = cei["mfma_32x32x16_bf16_TFLOPs"] if cei else None
         stage[name] = dict(ms=round(ms, 4), launches=cnt, bound=bound, achieved=round(ach, 1),
                            peak=peak, unit=unit, frac=round(ach / peak, 4))
+        if mpeak:
+            stage[name].update(measured_peak=round(mpeak, 1), frac_of_measured=round(ach / mpeak, 4))
     for name, (ms, cnt) in kt.items():
         if name not in stage:
             stage[name] = dict(ms=round(ms / cnt, 4), launches=cnt)
@@ -679,6 +706,14 @@ def main():
             "tau_t": tau_t, "global_batch": P, "seq_len": n, "parallelism": "none (1 GPU)",
         },
         "roofline": roofline,
+        # the same kernel against the ceilings the probes measured on this GPU after
+        # the timed steps (cma_probe.h), beside the vendor peak above
+        "roofline_measured": (dict(kernel=dom, ceiling=d.get("measured_peak"), unit=d["unit"],
+                                   frac=d.get("frac_of_measured"),
+                                   probes={k: cei[k] for k in ("hbm_read_GBps", "hbm_write_GBps",
+                                                               "hbm_copy_GBps_read_plus_write",
+                                                               "mfma_32x32x16_bf16_TFLOPs")})
+                              if cei else None),
         "kept_block_fraction": round(kept_frac, 4),
         "stages": stage,
         "wall_s_timed_region": round(wall, 3),
