@@ -593,8 +593,11 @@ extern "C" {
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout) {
   (void)total_k;
-  if (!src || src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || v_layout == CMA_V_PAGED || n_v_heads <= 0 ||
-      d <= 0 || src->n_block_rows <= 0)
+  if (!src || n_v_heads <= 0 || d <= 0) return 0;
+  // dense: partial rows of a launch of fewer rows than twice the CUs, split
+  // kDenseSplitMax ways at most
+  if (src->kind == CMA_SRC_DENSE) return (size_t)kDenseSplitMax * 2 * cu_count() * d * sizeof(float);
+  if (src->kind != CMA_SRC_BSR || v_layout == CMA_V_TILED || v_layout == CMA_V_PAGED || src->n_block_rows <= 0)
     return 0;
   return tiled_v_bytes(src, n_v_heads, d);
 }
@@ -643,6 +646,11 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
     a.head_stride = src->head_stride;
     if (a.v_tiled || v_layout == CMA_V_PAGED)
       return fail(CMA_EUNSUPPORTED, "tiled and paged V serve block-sparse sources only");
+    if (workspace) {  // optional: room to split the rows of a launch of few rows
+      if (!aligned16(workspace)) return fail(CMA_EINVAL, "workspace must be 16-byte aligned");
+      a.part = static_cast<float*>(workspace);
+      a.part_bytes = workspace_bytes;
+    }
     return hip_status(launch_mapped_av_dense(a, st), "mapped_av (dense) launch");
   }
   if (src->kind != CMA_SRC_BSR) return fail(CMA_EINVAL, "bad source kind");

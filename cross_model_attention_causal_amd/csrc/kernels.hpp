@@ -138,7 +138,11 @@ struct MappedAvArgs {
   int32_t* plan_order;  // [n_seqs * n_recv]: receiver heads of each sequence, ordered by sender
   int32_t* plan_pairs;  // [plan_cap]: (sequence << 7 | pair) of every work item, -1 past the end
   int64_t plan_cap;
+  // dense path: partial rows of split rows (workspace; NULL: rows are not split)
+  float* part;
+  size_t part_bytes;
 };
+constexpr int kDenseSplitMax = 8;  // workgroups per row of a dense launch of few rows
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st);
 hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st);

@@ -916,13 +916,16 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, int64_t lim, float
 // streams V with 128 KB of loads outstanding, and two workgroups share a CU) or,
 // for launches of few rows, 1024 (64 key rows per pass); key-major V: 256.
 template <int D, bool KEY_MAJOR, typename VT, int NT>
-__global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win) {
+// With n_split > 1 (launches of few rows), workgroup x of a row takes the
+// split x % n_split of its keys (64-key aligned pieces) and writes its partial
+// row to part[split][out element] (fp32); k_dense_split_sum adds the splits.
+__global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win, int n_split, float* part) {
   extern __shared__ float bj[];  // mixed row window [win]
   __shared__ int nzi[64];
   __shared__ float nzw[64];
   __shared__ int nnzm;
   __shared__ float red[KEY_MAJOR ? 1 : NT / (D / 8)][D];  // one row per key slot (token-major)
-  const int i = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int i = blockIdx.x / n_split, sp = blockIdx.x % n_split, s = blockIdx.y, h = blockIdx.z;
   const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
   if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
   const int tid = threadIdx.x;
@@ -941,6 +944,13 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win)
   }
   __syncthreads();
   const int last = nk - nq + i;
+  // this workgroup's keys: the whole row, or its split
+  int kbeg = 0, kend = last + 1;
+  if (n_split > 1) {
+    const int chunk = ((last + n_split) / n_split + 63) & ~63;
+    kbeg = min(last + 1, sp * chunk);
+    kend = min(last + 1, kbeg + chunk);
+  }
   const int64_t row_off = map_seq_off(a.vl, s, a.packed) + map_row_off(i, nq, nk, a.packed);
   const int64_t k0 = cu_k_of(a.vl, s);
   // bf16 token-major V whose rows start on 16-byte boundaries takes the
@@ -954,8 +964,8 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win)
   float acck[D / 16];
 #pragma unroll
   for (int u = 0; u < D / 16; ++u) acck[u] = 0.0f;
-  for (int w0 = 0; w0 <= last; w0 += win) {
-    const int wlen = min(win, last + 1 - w0);
+  for (int w0 = kbeg; w0 < kend; w0 += win) {
+    const int wlen = min(win, kend - w0);
     for (int j0 = tid; j0 < wlen; j0 += 4 * NT) {
       // four window positions per thread at a time (independent loads)
       float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1088,9 +1098,25 @@ __global__ __launch_bounds__(NT) void k_mapped_av_dense(MappedAvArgs a, int win)
       for (int u = 0; u < kSlots; ++u) o += red[u][tid];
     }
     const int64_t oi = ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + i) * D + tid;
-    if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f2bf(o);
+    if (n_split > 1) part[(int64_t)sp * a.n_recv * a.vl.total_q * D + oi] = o;
+    else if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f2bf(o);
     else reinterpret_cast<float*>(a.out)[oi] = o;
   }
+}
+
+// The splits of each row added in split order (deterministic). grid (max_q,
+// n_seqs, n_recv), D threads.
+template <int D>
+__global__ __launch_bounds__(D) void k_dense_split_sum(MappedAvArgs a, int n_split, const float* __restrict__ part) {
+  const int i = blockIdx.x, s = blockIdx.y, h = blockIdx.z;
+  const int32_t nq = seq_len_q(a.vl, s), nk = seq_len_k(a.vl, s);
+  if (!seq_ok(a.vl, s, nq, nk) || i >= nq) return;
+  const int64_t oi = ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + i) * D + threadIdx.x;
+  const int64_t stride = (int64_t)a.n_recv * a.vl.total_q * D;
+  float o = 0.0f;
+  for (int sp = 0; sp < n_split; ++sp) o += part[sp * stride + oi];
+  if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f2bf(o);
+  else reinterpret_cast<float*>(a.out)[oi] = o;
 }
 
 __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, float* M) {
@@ -1102,39 +1128,53 @@ __global__ void k_onehot(const int32_t* argmax, int64_t rows, int32_t n_send, fl
 }
 
 template <int D, bool KM>
-static void dense_launch(const MappedAvArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t dense_launch(const MappedAvArgs& a, hipStream_t st) {
   // the mixed-row window: the longest key sequence (in 64s), at most kDenseWin keys,
   // so that short contexts leave LDS for more workgroups per CU
   const int win = (int)std::min<int64_t>(kDenseWin, std::max<int64_t>(64, ((int64_t)a.max_k + 63) / 64 * 64));
   const size_t lds = (size_t)win * sizeof(float);
-  // token-major V: with few rows (a long-context decode of a small batch) 1024
-  // threads keep more loads in flight per row; with many rows 512 threads let two
-  // workgroups share a CU
-  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
-  KernelTimer kt_("k_mapped_av_dense", st);
-  if constexpr (!KM) {
-    if (wgs < 2 * (int64_t)cu_count()) {
-      if (a.v_bf16) hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, 1024>), grid, dim3(1024), lds, st, a, win);
-      else hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, 1024>), grid, dim3(1024), lds, st, a, win);
-      return;
+  const int64_t rows = (int64_t)a.max_q * a.vl.n_seqs * a.n_recv;
+  const int cus = cu_count();
+  // A launch of fewer rows than twice the CUs (a long-context decode of a small
+  // batch) splits each row's keys over up to kDenseSplitMax workgroups (at least
+  // 1024 keys each, at most two workgroups per CU in all) when the workspace
+  // holds the partial rows.
+  int n_split = 1;
+  if (rows < 2 * (int64_t)cus && a.part) {
+    n_split = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)kDenseSplitMax, 2 * (int64_t)cus / rows,
+                                                           (int64_t)a.max_k / 1024}));
+    if ((size_t)n_split * a.n_recv * a.vl.total_q * D * sizeof(float) > a.part_bytes) n_split = 1;
+  }
+  dim3 grid((unsigned)(a.max_q * n_split), (unsigned)a.vl.n_seqs, (unsigned)a.n_recv);
+  {
+    KernelTimer kt_("k_mapped_av_dense", st);
+    // token-major V, unsplit: with few rows 1024 threads keep more loads in
+    // flight per row; otherwise 512 threads let two workgroups share a CU
+    bool big = false;
+    if constexpr (!KM) big = n_split == 1 && rows < 2 * (int64_t)cus;
+    if (big) {
+      if (a.v_bf16) hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, 1024>), grid, dim3(1024), lds, st, a, win, n_split, a.part);
+      else hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, 1024>), grid, dim3(1024), lds, st, a, win, n_split, a.part);
+    } else {
+      constexpr int NT = KM ? 256 : 512;
+      if (a.v_bf16) hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a, win, n_split, a.part);
+      else hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a, win, n_split, a.part);
     }
   }
-  constexpr int NT = KM ? 256 : 512;
-  if (a.v_bf16) hipLaunchKernelGGL((k_mapped_av_dense<D, KM, uint16_t, NT>), grid, dim3(NT), lds, st, a, win);
-  else hipLaunchKernelGGL((k_mapped_av_dense<D, KM, float, NT>), grid, dim3(NT), lds, st, a, win);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_split == 1) return e;
+  {
+    KernelTimer kt_("k_dense_split_sum", st);
+    hipLaunchKernelGGL((k_dense_split_sum<D>), dim3((unsigned)a.max_q, (unsigned)a.vl.n_seqs, (unsigned)a.n_recv),
+                       dim3(D), 0, st, a, n_split, a.part);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st) {
   if (a.n_recv == 0 || a.vl.n_seqs == 0 || a.max_q == 0) return hipSuccess;
-  dim3 grid(a.max_q, a.vl.n_seqs, a.n_recv);
-  if (a.v_key_major) {
-    if (a.d == 64) dense_launch<64, true>(a, grid, st);
-    else dense_launch<128, true>(a, grid, st);
-  } else {
-    if (a.d == 64) dense_launch<64, false>(a, grid, st);
-    else dense_launch<128, false>(a, grid, st);
-  }
-  return hipGetLastError();
+  if (a.v_key_major) return a.d == 64 ? dense_launch<64, true>(a, st) : dense_launch<128, true>(a, st);
+  return a.d == 64 ? dense_launch<64, false>(a, st) : dense_launch<128, false>(a, st);
 }
 
 hipError_t launch_tile_v(const MappedAvArgs& a, hipStream_t st) {

@@ -333,7 +333,11 @@ typedef struct {
  * of V into `workspace` (cma_mapped_av_workspace(...) bytes: n_v_heads *
  * n_key_blocks * 64 * d * 2), with TILED or PAGED V it needs no workspace and
  * runs as a single kernel. A dense source takes TOKEN_MAJOR or KEY_MAJOR V and
- * needs no workspace.
+ * needs no workspace; given one of cma_mapped_av_workspace(...) bytes (2 MiB for
+ * 256 CUs at d = 128), a launch of fewer rows than twice the CUs (a long-context
+ * decode of a small batch) splits each row's keys over up to 8 workgroups and
+ * adds the partial rows in a fixed order (deterministic; the sums may differ in
+ * the last bits from an unsplit launch).
  */
 size_t cma_mapped_av_workspace(const cma_maps_src* src, int32_t n_v_heads, int32_t d, int64_t total_k,
                                cma_v_layout v_layout);
