@@ -19,7 +19,7 @@ heads, d = 128, bf16. One step runs every stage of the path once:
 plus the host-side mapped-layer order. Inputs are resident in HBM before timing;
 the receiver's V is token-major [heads, tokens, d].
 
-Prints one JSON line. ``--gpus N`` with N > 1 is not supported: this build runs
+Prints one JSON line. ``--gpus N`` with N > 1 is not supported: the benchmark runs
 on one GPU.
 """
 import argparse
@@ -501,7 +501,7 @@ def main():
         return long_decode_figures()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design "
+        print(json.dumps({"error": "the benchmark runs on one GPU only; sharding over several GPUs is a design "
                           "note, not a supported run (use --gpus 1)", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
