@@ -392,7 +392,7 @@ def block_compress(q, k, scale, bias, vl: Varlen, tau, capacity=None, want_mass=
 
 def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_stride=None,
               workspace: Workspace | None = None, out=None, q_rows=None, v_layout=V_TOKEN_MAJOR,
-              k_rows=None, v_heads=None):
+              k_rows=None, v_heads=None, split_rows=True):
     """O_h = (sum_j M[h, j] A_j) V_{h // g}, g = n_recv // v_heads (grouped V;
     default v_heads = n_recv). ``M`` is fp32 mixing weights [B, n_recv, n_send],
     or int32 sender indices [B, n_recv] (one sender per receiver head, e.g. the
@@ -404,7 +404,9 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
     [v_heads, n_key_blocks, 64 * 128] (V_TILED) or a dict ``{"pages": [v_heads,
     n_pages, 64 * 128], "table": int32 [n_seqs, stride]}`` (V_PAGED); the last two
     serve block-sparse sources only and need ``k_rows`` (Tk). ``q_rows`` is the
-    row count of the output tensor (default: Tk)."""
+    row count of the output tensor (default: Tk). With a dense source the call
+    passes the library a workspace in which a launch of few rows splits each row's
+    keys over several workgroups; ``split_rows=False`` passes none."""
     torch = _torch()
     lib = load_library()
     pv = None
@@ -487,6 +489,8 @@ def mapped_av(src, n_send, M, n_recv, v, vl: Varlen, out_dtype=None, M_seq_strid
         M_seq_stride = 0 if M.shape[0] == 1 else n_recv * n_send
     _need(M, "M", M_seq_stride * max(0, vl.n_seqs - 1) + n_recv * n_send)
     ws_bytes = lib.cma_mapped_av_workspace(ctypes.byref(s), n_v, d, Tk, v_layout)
+    if s.kind == SRC_DENSE and not split_rows:
+        ws_bytes = 0
     ws = (workspace or Workspace()).get(ws_bytes, dev) if ws_bytes else None
     _check(lib.cma_mapped_av(ctypes.byref(s), n_send, _dev_ptr(M, "M"), M_seq_stride, n_recv, n_v,
                              vptr, vdt, v_layout, d, ctypes.byref(cvl),

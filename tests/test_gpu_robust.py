@@ -188,9 +188,16 @@ def test_long_context_decode_rows(cma, long_dec, step):
     O_l = cma.mapped_av(("dense", rows, cma.DENSE), Hs, dev_f32(x["M"]), Hr, v, vl, q_rows=P)
     O_o = cma.mapped_av(("dense", rows, cma.DENSE), Hs, dev_f32(Mo), Hr, v, vl, q_rows=P,
                         out_dtype=torch.float32)
+    # the same launches without a workspace: each row in one workgroup
+    O_l1 = cma.mapped_av(("dense", rows, cma.DENSE), Hs, dev_f32(x["M"]), Hr, v, vl, q_rows=P, split_rows=False)
+    O_o1 = cma.mapped_av(("dense", rows, cma.DENSE), Hs, dev_f32(Mo), Hr, v, vl, q_rows=P,
+                         out_dtype=torch.float32, split_rows=False)
     torch.cuda.synchronize()
     R = host64(rows).reshape(Hs, P, nk)
     Ol, Oo = host64(O_l), host64(O_o)
+    # split and unsplit rows add the same terms in different orders
+    assert rel_l2(host64(O_o1), Oo) <= 1e-6
+    assert rel_l2(host64(O_l1), Ol) <= 1e-2
     M = x["M"][0].astype(np.float64)
     for p in (0, P - 1):
         ks = slice(int(x["cu_k"][p]), int(x["cu_k"][p]) + nk)
