@@ -84,6 +84,12 @@ def calibrate_copy():
                       "launches": 5}), flush=True)
 
 
+# share of an HBM-bound kernel's algorithmic bytes that are written (the rest read),
+# for its fraction of the probes' read and write ceilings
+WRITE_SHARE = {"k_attn_maps_short": 0.5, "k_attn_maps": 0.5, "k_tile_v": 0.5, "k_attn_rows": 4 / 260,
+               "k_block_extract": 0.94}
+
+
 def peaks(reps=5):
     """Print the chip's ceilings as the library's probes measure them (one JSON line)."""
     print(json.dumps(measure_ceilings(reps)), flush=True)
@@ -201,34 +207,49 @@ def stage_figures(reps=20, warmup=3):
     bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to("cuda")
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
 
+    # the probes' ceilings, for fractions of what this GPU measurably sustains
+    cei = measure_ceilings(3)
+    log("ceilings: " + json.dumps({k: v for k, v in cei.items() if k.startswith(("hbm", "mfma"))}))
+    # Every timed call starts with the last-level cache (the 256 MB MALL) flushed by
+    # writing a 512 MB buffer, outside the timed interval, so that no stage is timed
+    # on inputs left in the cache by its previous call.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
     def timed(fn, work):
+        """work: kernel -> (bound, work per launch[, share of the bytes written])."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         cma.timing_reset()
         cma.timing_enable(True)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        evs[0].record()
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         for i in range(reps):
+            flush.fill_(i & 0xff)
+            e0[i].record()
             fn()
-            evs[i + 1].record()
+            e1[i].record()
         torch.cuda.synchronize()
         cma.timing_enable(False)
         kt = cma.timing_collect()
-        call = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)])
+        call = np.array([e0[i].elapsed_time(e1[i]) for i in range(reps)])
         out = {"call_ms": {"p10": round(float(np.percentile(call, 10)), 4), "median": round(float(np.median(call)), 4),
                            "p90": round(float(np.percentile(call, 90)), 4), "reps": reps}}
         for name, (ms, cnt) in kt.items():
             e = dict(ms=round(ms / cnt, 4), launches_per_call=cnt // reps)
             if name in work:
-                bound, amount = work[name]
+                bound, amount = work[name][:2]
+                wf = work[name][2] if len(work[name]) > 2 else WRITE_SHARE.get(name, 0.0)
                 sec = ms / cnt * 1e-3
                 if bound == "hbm":
                     ach, peak, unit = amount / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+                    mpeak = 1.0 / ((1.0 - wf) / cei["hbm_read_GBps"] + wf / cei["hbm_write_GBps"])
                 else:
                     ach, peak, unit = amount / sec / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+                    mpeak = cei["mfma_32x32x16_bf16_TFLOPs"]
                 e.update(bound=bound, work_per_launch=amount, achieved=round(ach, 1), peak=peak, unit=unit,
-                         frac=round(ach / peak, 4))
+                         frac=round(ach / peak, 4), measured_peak=round(mpeak, 1),
+                         frac_of_measured=round(ach / mpeak, 4))
             out[name] = e
         return out
 
@@ -291,7 +312,8 @@ def stage_figures(reps=20, warmup=3):
     nnz = int(res["bsr"]["nnz"].item())
     qk = 2 * H * n * 128 * 2
     k_comp = timed(comp, {"k_block_stats": ("mfma", H * (n * (n + 1) // 2) * 128 * 2),
-                          "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + qk)})
+                          "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + qk,
+                                              nnz * 8196 / (nnz * 8196 + qk))})
     causal = (n // 64) * (n // 64 + 1) // 2
     print(json.dumps({"workload": f"block compression: {H} heads x {n} tokens (d=128, bf16), 64x64 blocks, "
                                   f"tau={tau}", "kept_block_fraction": round(nnz / (H * causal), 4),
@@ -334,7 +356,8 @@ def stage_figures(reps=20, warmup=3):
     pv = dict(pages=pages, table=table)
     chunk_flops = H * sum((n - ch + i + 1) for i in range(ch)) * 128 * 2
     k_cc = timed(comp_chunk, {"k_block_stats": ("mfma", chunk_flops),
-                              "k_block_extract": ("hbm", nnz_c * 8192 + nnz_c * 4 + H * (ch + n) * 128 * 2)})
+                              "k_block_extract": ("hbm", nnz_c * 8192 + nnz_c * 4 + H * (ch + n) * 128 * 2,
+                                                  nnz_c * 8196 / (nnz_c * 8196 + H * (ch + n) * 128 * 2))})
     k_cm = timed(lambda: cma.mapped_av(res_c["bsr"], Hs, M, Hr, pv, vl_c, q_rows=ch, v_layout=cma.V_PAGED,
                                        k_rows=n),
                  {"k_mapped_av_bsr": ("hbm", nnz_c * 8192 + Hr * (ch + n) * 128 * 2
@@ -409,7 +432,8 @@ def stage_figures(reps=20, warmup=3):
                             # the ridge, so the maps' bytes bound the Gram here
                             "k_gram_bf16": ("hbm", P * (Hr + Hs) * L * 2),
                             "k_block_stats": ("mfma", Hs * tri * 128 * 2),
-                            "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2),
+                            "k_block_extract": ("hbm", nnz * 8192 + nnz * 4 + 2 * Hs * tokens * 128 * 2,
+                                                nnz * 8196 / (nnz * 8196 + 2 * Hs * tokens * 128 * 2)),
                             "k_mapped_av_idx": ("mfma", idx_flops),
                             "k_tile_v": ("hbm", 2 * Hr * tokens * 128 * 2)})
     pre_ms = sum(e["ms"] * e["launches_per_call"] for e in k_pre.values() if "launches_per_call" in e)
@@ -441,7 +465,7 @@ def stage_figures(reps=20, warmup=3):
                                   "heads", "kernel_ms_per_step": round(dec_ms, 4), "kernels": k_dec}), flush=True)
 
 
-def long_decode_figures(reps=5):
+def long_decode_figures(reps=20):
     """IAM's long-context decode (8192 + 512 at batch 4), one generation step at its
     longest context (8704 keys): the sender rows over 32 heads, then the mapped x V
     of 24 receiver heads with a one-hot head map."""
@@ -465,11 +489,17 @@ def long_decode_figures(reps=5):
     def step():
         st["rows"] = cma.attn_maps(qd, k, sc, bi, vl, layout=cma.DENSE, out_dtype=torch.float32)
         st["o"] = cma.mapped_av(("dense", st["rows"], cma.DENSE), Hs, Mo, Hr, v, vl, q_rows=P)
-    step()
+    cei = measure_ceilings(3)
+    # the step's K and V (~0.5 GB) would fit the 256 MB last-level cache in part:
+    # it is flushed (a 512 MB write) before every timed step
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        step()
     torch.cuda.synchronize()
     cma.timing_reset()
     cma.timing_enable(True)
-    for _ in range(reps):
+    for i in range(reps):
+        flush.fill_(i & 0xff)
         step()
     torch.cuda.synchronize()
     cma.timing_enable(False)
@@ -480,8 +510,11 @@ def long_decode_figures(reps=5):
         e = dict(ms=round(ms / cnt, 4), launches_per_step=cnt // reps)
         if name in work:
             ach = work[name] / (ms / cnt * 1e-3) / 1e9
+            wf = WRITE_SHARE.get(name, 0.0)
+            mpeak = 1.0 / ((1.0 - wf) / cei["hbm_read_GBps"] + wf / cei["hbm_write_GBps"])
             e.update(bound="hbm", work_per_launch=work[name], achieved=round(ach, 1), peak=HBM_PEAK_GBS,
-                     unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4))
+                     unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), measured_peak=round(mpeak, 1),
+                     frac_of_measured=round(ach / mpeak, 4))
         kern[name] = e
     step_ms = sum(e["ms"] * e["launches_per_step"] for e in kern.values())
     print(json.dumps({"workload": f"IAM long-context decode, one step at context {ctx}: {P} prompts, sender rows "

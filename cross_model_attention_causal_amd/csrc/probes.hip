@@ -34,11 +34,13 @@ __global__ __launch_bounds__(512) void k_probe_copy(const u32x4* __restrict__ sr
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
-// grid-stride 16-byte stores of n16 chunks (a streaming write).
+// grid-stride 16-byte non-temporal stores of n16 chunks (a streaming write, with
+// the cache policy the block extraction's stores use).
 __global__ __launch_bounds__(512) void k_probe_write(u32x4* __restrict__ dst, int64_t n16) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const uint32_t v = threadIdx.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = u32x4{v, v, v, v};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(u32x4{v, v, v, v}, dst + i);
 }
 
 // Every lane runs `iters` rounds of 8 independent chains of one vector operation

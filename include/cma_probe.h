@@ -12,7 +12,7 @@
  * cma_probe_copy:  the same grid copies `bytes` from src to dst (16-byte aligned):
  *                  read + write bandwidth.
  * cma_probe_write: the same grid writes `bytes` to dst (16-byte aligned) with
- *                  16-byte stores: HBM write bandwidth.
+ *                  16-byte non-temporal stores: HBM write bandwidth.
  * cma_probe_valu:  n_wg workgroups of 256 threads; every lane runs `iters` rounds
  *                  of 8 independent chains of one vector operation (kind 0: the
  *                  hardware exp2, kind 1: fused multiply-add); out: device,
