@@ -108,7 +108,7 @@ def measure_ceilings(reps=5):
     lib.cma_probe_copy.argtypes = [P, P, I64, I32, P]
     lib.cma_probe_mfma.argtypes = [I32, I32, P, P]
     lib.cma_probe_l2.argtypes = [P, I32, I32, I32, P, P]
-    lib.cma_probe_write.argtypes = [P, I64, I32, P]
+    lib.cma_probe_write.argtypes = [P, I64, I32, I32, P]
     lib.cma_probe_valu.argtypes = [I32, I32, I32, P, P]
     lib.cma_probe_lds.argtypes = [I32, I32, P, P]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -137,8 +137,14 @@ def measure_ceilings(reps=5):
     b = torch.empty(half // 4, dtype=torch.float32, device="cuda")
     t = med(lambda: lib.cma_probe_copy(a.data_ptr(), b.data_ptr(), half, cus * 8, st))
     out["hbm_copy_GBps_read_plus_write"] = round(2 * half / (t * 1e-3) / 1e9, 1)
-    t = med(lambda: lib.cma_probe_write(a.data_ptr(), big, cus * 8, st))
-    out["hbm_write_GBps"] = round(big / (t * 1e-3) / 1e9, 1)
+    # writes: plain and non-temporal stores, grid-stride and per-workgroup
+    # contiguous; the ceiling is the best of the four
+    wr = {}
+    for mode, name in ((0, "plain_stride"), (1, "nt_stride"), (2, "plain_contig"), (3, "nt_contig")):
+        t = med(lambda: lib.cma_probe_write(a.data_ptr(), big, cus * 8, mode, st))
+        wr[name] = round(big / (t * 1e-3) / 1e9, 1)
+    out["hbm_write_GBps_by_pattern"] = wr
+    out["hbm_write_GBps"] = max(wr.values())
     del a, b
     # vector-unit rates: lane-operations per clock per SIMD (4 SIMDs per CU) at 2.4 GHz
     n_wg, iters = cus * 8, 4096
@@ -170,19 +176,24 @@ def measure_ceilings(reps=5):
 
 
 def clocks():
-    """The current shader and memory clocks as rocm-smi reports them (a child
-    process; None where the tool is missing or says nothing)."""
-    import subprocess
+    """The current shader and memory clocks of device 0 as the amdgpu driver's sysfs
+    files list them (the entry marked '*'); None where they cannot be read. Read from
+    files, with no child process, so it also works under a profiler."""
+    import torch
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
-    except (OSError, subprocess.SubprocessError):
+        p = torch.cuda.get_device_properties(0)
+        dev = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    except (AttributeError, RuntimeError):
         return None
     got = {}
-    for line in r.stdout.splitlines():
-        low = line.lower()
-        for key in ("sclk", "mclk", "fclk"):
-            if key in low and "mhz" in low and key not in got:
-                got[key] = line.split(":", 2)[-1].strip()
+    for key in ("sclk", "mclk", "fclk"):
+        try:
+            with open(f"{dev}/pp_dpm_{key}") as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        got[key] = line.split(":", 1)[-1].strip(" *\n")
+        except OSError:
+            pass
     return got or None
 
 

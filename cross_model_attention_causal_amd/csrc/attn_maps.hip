@@ -707,12 +707,14 @@ __global__ __launch_bounds__(256) void k_attn_maps_f32(AttnMapsArgs a, int d) {
 }
 
 template <int D, bool PACKED, bool OUT_BF16>
-static void maps_launch(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
+static hipError_t maps_launch(const AttnMapsArgs& a, dim3 grid, hipStream_t st) {
   const size_t lds = 2 * (size_t)kStageBytes;  // the two K stages
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_maps<D, PACKED, OUT_BF16>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_maps<D, PACKED, OUT_BF16>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   KernelTimer kt_("k_attn_maps", st);
   hipLaunchKernelGGL((k_attn_maps<D, PACKED, OUT_BF16>), grid, dim3(512), lds, st, a);
+  return hipGetLastError();
 }
 
 // Compute units of the current device (one persistent workgroup each).
@@ -729,12 +731,14 @@ int cu_count() {
 }
 
 template <int D, bool PACKED, bool OUT_BF16>
-static void short_launch(const AttnMapsArgs& a, int n_wg, hipStream_t st) {
+static hipError_t short_launch(const AttnMapsArgs& a, int n_wg, hipStream_t st) {
   const size_t lds = (size_t)8 * (D / 64) * kStageBlockBytes;  // the resident K
-  hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_maps_short<D, PACKED, OUT_BF16>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_maps_short<D, PACKED, OUT_BF16>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   KernelTimer kt_("k_attn_maps_short", st);
   hipLaunchKernelGGL((k_attn_maps_short<D, PACKED, OUT_BF16>), dim3(n_wg), dim3(512), lds, st, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -742,14 +746,8 @@ static hipError_t launch_short(const AttnMapsArgs& a, hipStream_t st) {
   const int64_t units = (int64_t)a.vl.n_seqs * a.n_heads;
   if (units > INT32_MAX) return hipErrorInvalidValue;
   const int n_wg = (int)std::min<int64_t>(units, cu_count());
-  if (a.packed) {
-    if (a.out_bf16) short_launch<D, true, true>(a, n_wg, st);
-    else short_launch<D, true, false>(a, n_wg, st);
-  } else {
-    if (a.out_bf16) short_launch<D, false, true>(a, n_wg, st);
-    else short_launch<D, false, false>(a, n_wg, st);
-  }
-  return hipGetLastError();
+  if (a.packed) return a.out_bf16 ? short_launch<D, true, true>(a, n_wg, st) : short_launch<D, true, false>(a, n_wg, st);
+  return a.out_bf16 ? short_launch<D, false, true>(a, n_wg, st) : short_launch<D, false, false>(a, n_wg, st);
 }
 
 template <int D>
@@ -759,14 +757,8 @@ static hipError_t launch_bf16(AttnMapsArgs a, int max_q, hipStream_t st) {
   const int64_t n_wg = 8 * ((units + 7) / 8) * a.n_rb;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg);
-  if (a.packed) {
-    if (a.out_bf16) maps_launch<D, true, true>(a, grid, st);
-    else maps_launch<D, true, false>(a, grid, st);
-  } else {
-    if (a.out_bf16) maps_launch<D, false, true>(a, grid, st);
-    else maps_launch<D, false, false>(a, grid, st);
-  }
-  return hipGetLastError();
+  if (a.packed) return a.out_bf16 ? maps_launch<D, true, true>(a, grid, st) : maps_launch<D, true, false>(a, grid, st);
+  return a.out_bf16 ? maps_launch<D, false, true>(a, grid, st) : maps_launch<D, false, false>(a, grid, st);
 }
 
 constexpr int kRowsMaxKeys = 36 * 1024;  // keys of a single-row sequence held in LDS

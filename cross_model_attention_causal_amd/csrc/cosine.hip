@@ -1,16 +1,16 @@
 // Head mapping by cosine similarity of flattened maps (IAM Methods 1 and 4).
 //
 // The cosine matrix is a Gram product R S^T over the map length with the row
-// norms on the side. It runs as a split-K bf16 MFMA GEMM: a workgroup (8 waves)
-// owns 128 receiver maps and one K-chunk and holds the partial dot products of
-// its 128 maps against all sender maps in registers (wave = 32 receivers x one
-// half of the senders). Each 64-element K-step is software-pipelined: while the
-// step's products run, the next step's receiver operands (straight from HBM,
-// each receiver map read once) and sender slice (into registers, then into the
-// other half of a double-buffered LDS slice shared by all waves) are in flight.
-// Partial sums of each split go to a workspace and a finalize kernel adds them
-// in a fixed order (deterministic), forms the cosines and takes argmax (lowest
-// index on ties) and margin.
+// norms on the side. It runs as a split-K bf16 MFMA GEMM (32x32x16): a
+// workgroup (8 waves) owns 128 receiver maps and one K-chunk and holds the
+// partial dot products of its 128 maps against all sender maps in registers
+// (wave = 32 receivers x one half of the 32-sender tiles). Each 64-element K-step
+// of the tile's receiver maps and of the sender maps is staged in LDS (each map
+// read once per workgroup) by a depth-2 pipeline: while a step's products run,
+// the loads of the step after next are in flight into registers and the next
+// step goes to the other LDS buffer. Partial sums of each split go to a
+// workspace and a finalize kernel adds them in a fixed order (deterministic),
+// forms the cosines and takes argmax (lowest index on ties) and margin.
 #include "kernels.hpp"
 #include "score.hpp"
 
@@ -18,7 +18,7 @@ namespace cma {
 
 constexpr int kGramRows = 128;     // receiver maps per workgroup
 constexpr int kGramK = 64;         // K elements per step
-constexpr int kGramThreads = 512;  // 8 waves = 4 groups of 32 receivers x 2 sender halves
+constexpr int kGramThreads = 512;  // 8 waves = 4 groups of 32 receivers x 2 halves of the sender tiles
 constexpr int kMaxSteps = 64;      // K-steps of one split (4096 elements)
 
 // The sender slice of a step in LDS: row j (a sender map) holds 64 elements as 8
@@ -33,12 +33,16 @@ __device__ __forceinline__ float sq2(uint32_t w, float t) {
   return __builtin_amdgcn_fdot2_f32_bf16(x, x, t, false);
 }
 
-template <int NTH>  // sender tiles of 16 per half (n_send <= 32 * NTH)
+// NTH: staged sender tiles of 32 (n_send <= 32 * NTH); DEPTH: steps whose loads
+// are in flight while a step is computed (2 needs a second register set).
+template <int NTH, int DEPTH>
 __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   constexpr int SROWS = 32 * NTH;                                  // staged sender rows
-  constexpr int SCH = SROWS * 8;                                   // 16-byte chunks per slice
-  constexpr int SPT = (SCH + kGramThreads - 1) / kGramThreads;     // chunks per thread
-  __shared__ __attribute__((aligned(16))) u32x4 sb[2][SCH];
+  constexpr int T2 = (NTH + 1) / 2;                                // sender tiles per wave
+  constexpr int ROWS = kGramRows + SROWS;                          // staged rows: receivers, then senders
+  constexpr int CH = ROWS * 8;                                     // 16-byte chunks per stage
+  constexpr int PT = (CH + kGramThreads - 1) / kGramThreads;       // chunks per thread
+  __shared__ __attribute__((aligned(16))) u32x4 sb[2][CH];
   const int b = blockIdx.y;
   const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
   // Workgroup id i runs on XCD i % 8. Split sp goes to XCD sp % 8 with all its
@@ -48,25 +52,24 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   const int sp = xcd + kXcds * (m / n_rtiles), rt = m % n_rtiles;
   if (sp >= a.splits) return;
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int p = lane & 15, qd = lane >> 4;
-  const int rg = wave & 3, sh = wave >> 2;  // receiver group, sender half
+  const int nl = lane & 31, hl = lane >> 5;
+  const int rg = wave & 3, sh = wave >> 2;  // receiver group, half of the sender tiles
   const int64_t k_beg = (int64_t)sp * a.kchunk;
   const int64_t k_end = min(a.len, k_beg + a.kchunk);
   const int nsteps = (int)((k_end - k_beg + kGramK - 1) / kGramK);
   const uint16_t* recv = reinterpret_cast<const uint16_t*>(a.recv) + (int64_t)b * a.rb;
   const uint16_t* send = reinterpret_cast<const uint16_t*>(a.send) + (int64_t)b * a.sb;
-  const int row0 = rt * kGramRows + 32 * rg;
+  const int rbase = rt * kGramRows;
+  const int row0 = rbase + 32 * rg;
 
-  f32x4 acc[2][NTH];
+  f32x16 acc[T2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NTH; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T2; ++t) acc[t] = f32x16{};
   // Squared norms in two levels: a step's squares are summed apart, added to an
   // inner running sum that is folded into the outer one every 16 steps. A single
   // long fp32 chain would drop the many tiny squares of a probability map's tail
   // once the sum has grown (a systematic underestimate, which biases the cosine).
-  float rn[2] = {0.f, 0.f}, rn_in[2] = {0.f, 0.f};
+  float rn = 0.f, rn_in = 0.f;
   float sn = 0.f, sn_in = 0.f;
   // sender rows whose norms this workgroup accumulates (one per thread): the
   // receiver tiles of a split share the rows out
@@ -74,103 +77,86 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   const int srow = rt * s_per + tid;
   const bool s_mine = tid < s_per && srow < a.n_send;
 
-  const uint16_t* arow[2];
-  bool aok[2];
+  // A step's stage: the 64 elements of the tile's 128 receiver maps, then those
+  // of the staged sender maps; staged row j holds 8 chunks of 16 bytes, chunk ch
+  // in slot ch ^ ((j >> 1) & 7). Thread chunk i is x = tid + 512 i = (row x / 8,
+  // slot x % 8), read from a fixed map row: rows past the last map read a valid
+  // row, whose products and norms are never stored. Each map is read once per
+  // workgroup and both sender halves take their receiver operands from LDS.
+  const uint16_t* cptr[PT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int row = row0 + 16 * mt + p;
-    aok[mt] = row < a.n_recv;
-    arow[mt] = recv + (int64_t)(aok[mt] ? row : 0) * a.rh;
+  for (int i = 0; i < PT; ++i) {
+    const int x = min(tid + kGramThreads * i, CH - 1), row = x >> 3, slot = x & 7;
+    const int ch = slot ^ ((row >> 1) & 7);
+    const uint16_t* base = row < kGramRows ? recv + (int64_t)min(rbase + row, a.n_recv - 1) * a.rh
+                                           : send + (int64_t)min(row - kGramRows, a.n_send - 1) * a.sh;
+    cptr[i] = base + 8 * ch;
   }
-  // The loads of a full step carry no branch, so the compiler's waits for the
-  // prefetched registers stay exact: rows past the end read a valid row, and
-  // what they produce (products in rows or columns past the end, their norms)
-  // is never stored. A last, partial step uses element-guarded loads.
-  // receiver operand of step st: lane (p, qd) holds k = 32 ks + 8 qd .. + 7 of its rows
-  auto load_a = [&](int st, u32x4 (&av)[2][2], auto guarded) __attribute__((always_inline)) {
+  auto load = [&](int st, u32x4 (&v)[PT], auto guarded) __attribute__((always_inline)) {
     const int64_t k0 = k_beg + (int64_t)st * kGramK;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int64_t j0 = k0 + 32 * ks + 8 * qd;
-        if constexpr (decltype(guarded)::value) {
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (aok[mt]) x = ldg16_guard(arow[mt], j0, k_end);
-          av[mt][ks] = x;
-        } else {
-          av[mt][ks] = ldg16(arow[mt] + j0);
-        }
-      }
-  };
-  // sender slice of step st: chunk x = tid + 512 i is (row x / 8, LDS slot x % 8)
-  auto load_s = [&](int st, u32x4 (&sv)[SPT], auto guarded) __attribute__((always_inline)) {
-    const int64_t k0 = k_beg + (int64_t)st * kGramK;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int x = tid + kGramThreads * i, row = x >> 3, slot = x & 7;
-      const int ch = slot ^ ((row >> 1) & 7);
-      const bool ok = x < SCH && row < a.n_send;
-      const uint16_t* srow_p = send + (int64_t)min(row, a.n_send - 1) * a.sh;
+    for (int i = 0; i < PT; ++i) {
       if constexpr (decltype(guarded)::value) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok) v = ldg16_guard(srow_p, k0 + 8 * ch, k_end);
-        sv[i] = v;
+        // element-guarded: chunk offset of the row pointer within the 64 elements
+        const int x = min(tid + kGramThreads * i, CH - 1), row = x >> 3, slot = x & 7;
+        const int ch = slot ^ ((row >> 1) & 7);
+        v[i] = ldg16_guard(cptr[i] - 8 * ch, k0 + 8 * ch, k_end);
       } else {
-        sv[i] = ldg16(srow_p + k0 + 8 * ch);
+        v[i] = ldg16(cptr[i] + k0);
       }
     }
   };
-  auto store_s = [&](const u32x4 (&sv)[SPT], int buf) __attribute__((always_inline)) {
+  auto store = [&](const u32x4 (&v)[PT], int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
+    for (int i = 0; i < PT; ++i) {
       const int x = tid + kGramThreads * i;
-      if (x < SCH) sb[buf][x] = sv[i];  // slot order: x = row * 8 + slot
+      if (CH % kGramThreads == 0 || x < CH) sb[buf][x] = v[i];  // slot order: x = row * 8 + slot
     }
   };
-  // one step's work on the slice in LDS buffer buf and the receiver operand av
-  auto compute = [&](int st, int buf, const u32x4 (&av)[2][2]) __attribute__((always_inline)) {
-    // receiver norms (one sender half does it)
+  // one step's work on the stage in LDS buffer buf. Operands of 32x32x16: lane
+  // (nl, hl) holds elements 16 ks + 8 hl .. + 7 of map row nl of the tile (A:
+  // receivers, B: senders), so that D[m][n] = sum_k R[m][k] S[n][k].
+  auto compute = [&](int st, int buf) __attribute__((always_inline)) {
+    u32x4 av[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) av[ks] = sb[buf][sslot(32 * rg + nl, 2 * ks + hl)];
+    // receiver norms (one sender half does it; the partner lane holds the other
+    // half of the row's elements)
     if (sh == 0) {
+      float t = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float t = 0.0f;
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) t = sq2(av[mt][ks][e], t);
-        rn_in[mt] += t;
-      }
+        for (int e = 0; e < 4; ++e) t = sq2(av[ks][e], t);
+      rn_in += t;
     }
     // sender norms of this workgroup's share of the rows, in element order
     if (s_mine) {
       float t = 0.0f;
 #pragma unroll
       for (int ch = 0; ch < 8; ++ch) {
-        const u32x4 v = sb[buf][sslot(srow, ch)];
+        const u32x4 v = sb[buf][sslot(kGramRows + srow, ch)];
 #pragma unroll
         for (int e = 0; e < 4; ++e) t = sq2(v[e], t);
       }
       sn_in += t;
     }
     if (((st + 1) & 15) == 0) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        rn[u] += rn_in[u];
-        rn_in[u] = 0.0f;
-      }
+      rn += rn_in;
+      rn_in = 0.0f;
       sn += sn_in;
       sn_in = 0.0f;
     }
-    // products: B operand lane (p, qd) = sender row 16 nt + p, k = 32 ks + 8 qd .. + 7
 #pragma unroll
-    for (int nt = 0; nt < NTH; ++nt) {
-      const int srow_b = 16 * (sh * NTH + nt) + p;
+    for (int t = 0; t < T2; ++t) {
+      const int tile = sh * T2 + t;
+      if (tile < NTH) {
+        const int srow_b = kGramRows + 32 * tile + nl;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 bv = sb[buf][sslot(srow_b, 4 * ks + qd)];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma16(as_bf16x8(av[mt][ks]), as_bf16x8(bv), acc[mt][nt]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 bv = sb[buf][sslot(srow_b, 2 * ks + hl)];
+          acc[t] = mfma32(as_bf16x8(av[ks]), as_bf16x8(bv), acc[t]);
+        }
       }
     }
   };
@@ -178,60 +164,70 @@ __global__ __launch_bounds__(kGramThreads) void k_gram_bf16(CosineArgs a) {
   using Fast = std::integral_constant<bool, false>;
   using Guarded = std::integral_constant<bool, true>;
   const int nfull = (int)((k_end - k_beg) / kGramK);  // steps with all 64 elements inside the chunk
-  u32x4 acur[2][2], anext[2][2], sv[SPT];
-  if (nfull > 0) {
-    load_s(0, sv, Fast{});
-    load_a(0, acur, Fast{});
-    store_s(sv, 0);
-  }
-  __syncthreads();
-  for (int st = 0; st < nfull; ++st) {
-    const int buf = st & 1;
-    // the next full step's operands (clamped at the end: a harmless reload)
-    const int nx = min(st + 1, nfull - 1);
-    load_s(nx, sv, Fast{});
-    load_a(nx, anext, Fast{});
-    compute(st, buf, acur);
-    store_s(sv, buf ^ 1);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) acur[mt][ks] = anext[mt][ks];
+  // Pipeline of depth 2: while step st is computed from one LDS buffer, the
+  // loads of step st + 2 are in flight into registers and step st + 1 (loaded
+  // one iteration earlier) goes to the other buffer. Past the last full step the
+  // loads are clamped (harmless reloads) and nothing is computed, so that both
+  // register sets see the same operations on every path and the compiler's
+  // waits for the older set never include the newer one. Depth 1: the loads of
+  // step st + 1 are in flight while step st is computed.
+  u32x4 r0[PT];
+  if constexpr (DEPTH == 2) {
+    u32x4 r1[PT];
+    if (nfull > 0) {
+      load(0, r0, Fast{});
+      load(min(1, nfull - 1), r1, Fast{});
+      store(r0, 0);
+    }
     __syncthreads();
+    auto iter = [&](u32x4 (&mine)[PT], const u32x4 (&next)[PT], int st) __attribute__((always_inline)) {
+      load(min(st + 2, nfull - 1), mine, Fast{});
+      if (st < nfull) compute(st, st & 1);
+      store(next, (st + 1) & 1);
+      __syncthreads();
+    };
+    for (int st = 0; st < nfull; st += 2) {
+      iter(r0, r1, st);
+      iter(r1, r0, st + 1);
+    }
+  } else {
+    if (nfull > 0) {
+      load(0, r0, Fast{});
+      store(r0, 0);
+    }
+    __syncthreads();
+    for (int st = 0; st < nfull; ++st) {
+      load(min(st + 1, nfull - 1), r0, Fast{});
+      compute(st, st & 1);
+      store(r0, (st + 1) & 1);
+      __syncthreads();
+    }
   }
   if (nfull < nsteps) {
     // the partial last step
-    const int buf = nfull & 1;
-    load_s(nfull, sv, Guarded{});
-    load_a(nfull, acur, Guarded{});
-    store_s(sv, buf);
+    load(nfull, r0, Guarded{});
+    store(r0, 0);
     __syncthreads();
-    compute(nfull, buf, acur);
+    compute(nfull, 0);
   }
 
-#pragma unroll
-  for (int u = 0; u < 2; ++u) rn[u] += rn_in[u];
+  rn += rn_in;
   sn += sn_in;
-  // partial dot products: D[m = 4qd + v][n = p]
+  // partial dot products: D[m = 8 (v / 4) + 4 hl + v % 4][n = nl]
   float* part = a.part + ((int64_t)sp * a.n_batch + b) * a.n_recv * a.n_send;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int t = 0; t < T2; ++t) {
+    const int col = 32 * (sh * T2 + t) + nl;
 #pragma unroll
-    for (int nt = 0; nt < NTH; ++nt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = row0 + 16 * mt + 4 * qd + v, col = 16 * (sh * NTH + nt) + p;
-        if (row < a.n_recv && col < a.n_send) part[(int64_t)row * a.n_send + col] = acc[mt][nt][v];
-      }
-  if (sh == 0) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      float x = rn[mt];
-      x += xor_lane(x, 16);
-      x += xor_lane(x, 32);
-      const int row = row0 + 16 * mt + p;
-      if (qd == 0 && row < a.n_recv) a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + row] = x;
+    for (int v = 0; v < 16; ++v) {
+      const int row = row0 + 8 * (v >> 2) + 4 * hl + (v & 3);
+      if (row < a.n_recv && col < a.n_send) part[(int64_t)row * a.n_send + col] = acc[t][v];
     }
+  }
+  if (sh == 0) {
+    const float x = rn + xor_lane(rn, 32);
+    const int row = row0 + nl;
+    if (hl == 0 && row < a.n_recv) a.rnorm[((int64_t)sp * a.n_batch + b) * a.n_recv + row] = x;
   }
   if (s_mine) a.snorm[((int64_t)sp * a.n_batch + b) * a.n_send + srow] = sn;
 }
@@ -694,15 +690,20 @@ CosinePlan plan_cosine(int32_t n_batch, int32_t n_recv, int32_t n_send, int64_t 
 
 template <int NTH>
 static void gram_launch(const CosineArgs& a, hipStream_t st) {
+  // two steps in flight where the second register set fits beside the accumulators
+  constexpr int DEPTH = NTH <= 8 ? 2 : 1;
   const int n_rtiles = (a.n_recv + kGramRows - 1) / kGramRows;
   dim3 grid(kXcds * ((a.splits + kXcds - 1) / kXcds) * n_rtiles, a.n_batch);
-  { KernelTimer kt_("k_gram_bf16", st); hipLaunchKernelGGL((k_gram_bf16<NTH>), grid, dim3(kGramThreads), 0, st, a); }
+  {
+    KernelTimer kt_("k_gram_bf16", st);
+    hipLaunchKernelGGL((k_gram_bf16<NTH, DEPTH>), grid, dim3(kGramThreads), 0, st, a);
+  }
 }
 
 hipError_t launch_cosine(const CosineArgs& a, hipStream_t st) {
   if (a.n_batch == 0 || a.n_recv == 0) return hipSuccess;
   if (a.bf16) {
-    const int nth = (a.n_send + 31) / 32;  // sender tiles of 16 per half
+    const int nth = (a.n_send + 31) / 32;  // sender tiles of 32
     if (nth <= 1) gram_launch<1>(a, st);
     else if (nth <= 2) gram_launch<2>(a, st);
     else if (nth <= 4) gram_launch<4>(a, st);

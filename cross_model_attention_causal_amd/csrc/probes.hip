@@ -34,13 +34,28 @@ __global__ __launch_bounds__(512) void k_probe_copy(const u32x4* __restrict__ sr
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
-// grid-stride 16-byte non-temporal stores of n16 chunks (a streaming write, with
-// the cache policy the block extraction's stores use).
+// 16-byte stores of n16 chunks. NT: non-temporal (the cache policy the block
+// extraction's stores use), else plain. CONTIG: workgroup b writes chunks
+// [b * per, (b + 1) * per) in runs of 8 KB (one chunk per thread), else a
+// grid-stride loop over all chunks.
+template <bool NT, bool CONTIG>
 __global__ __launch_bounds__(512) void k_probe_write(u32x4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const uint32_t v = threadIdx.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    __builtin_nontemporal_store(u32x4{v, v, v, v}, dst + i);
+  int64_t i, end, step;
+  if (CONTIG) {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    i = (int64_t)blockIdx.x * per + threadIdx.x;
+    end = min(n16, ((int64_t)blockIdx.x + 1) * per);
+    step = blockDim.x;
+  } else {
+    i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    end = n16;
+    step = (int64_t)gridDim.x * blockDim.x;
+  }
+  for (; i < end; i += step) {
+    if (NT) __builtin_nontemporal_store(u32x4{v, v, v, v}, dst + i);
+    else dst[i] = u32x4{v, v, v, v};
+  }
 }
 
 // Every lane runs `iters` rounds of 8 independent chains of one vector operation
@@ -145,10 +160,18 @@ int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void
   return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
 }
 
-int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, void* stream) {
-  if (!dst || bytes < 16 || n_wg < 1 || (reinterpret_cast<uintptr_t>(dst) & 15)) return CMA_EINVAL;
-  hipLaunchKernelGGL(k_probe_write, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
-                     static_cast<u32x4*>(dst), bytes / 16);
+int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, int32_t mode, void* stream) {
+  if (!dst || bytes < 16 || n_wg < 1 || mode < 0 || mode > 3 || (reinterpret_cast<uintptr_t>(dst) & 15))
+    return CMA_EINVAL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  u32x4* d = static_cast<u32x4*>(dst);
+  const int64_t n16 = bytes / 16;
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((k_probe_write<false, false>), dim3(n_wg), dim3(512), 0, st, d, n16); break;
+    case 1: hipLaunchKernelGGL((k_probe_write<true, false>), dim3(n_wg), dim3(512), 0, st, d, n16); break;
+    case 2: hipLaunchKernelGGL((k_probe_write<false, true>), dim3(n_wg), dim3(512), 0, st, d, n16); break;
+    default: hipLaunchKernelGGL((k_probe_write<true, true>), dim3(n_wg), dim3(512), 0, st, d, n16); break;
+  }
   return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
 }
 

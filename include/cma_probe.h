@@ -12,7 +12,9 @@
  * cma_probe_copy:  the same grid copies `bytes` from src to dst (16-byte aligned):
  *                  read + write bandwidth.
  * cma_probe_write: the same grid writes `bytes` to dst (16-byte aligned) with
- *                  16-byte non-temporal stores: HBM write bandwidth.
+ *                  16-byte stores: HBM write bandwidth. mode bit 0: non-temporal
+ *                  stores (else plain); bit 1: each workgroup writes one
+ *                  contiguous share in 8 KB runs (else a grid-stride loop).
  * cma_probe_valu:  n_wg workgroups of 256 threads; every lane runs `iters` rounds
  *                  of 8 independent chains of one vector operation (kind 0: the
  *                  hardware exp2, kind 1: fused multiply-add); out: device,
@@ -44,7 +46,7 @@ extern "C" {
 
 int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, void* sink, void* stream);
 int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void* stream);
-int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, void* stream);
+int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, int32_t mode, void* stream);
 int cma_probe_valu(int32_t kind, int32_t n_wg, int32_t iters, float* out, void* stream);
 int cma_probe_mfma(int32_t n_wg, int32_t iters, float* out, void* stream);
 int cma_probe_lds(int32_t n_wg, int32_t iters, void* sink, void* stream);

@@ -204,6 +204,28 @@ def test_head_map_cosine_batched_strided(cma):
         assert np.array_equal(host64(arg)[b][big].astype(int), oarg[big])
 
 
+@pytest.mark.parametrize("Hs,L", [(100, 1000), (200, 24676), (384, 50001)])
+def test_head_map_cosine_sender_tiles(cma, Hs, L):
+    """Sender counts that take the 4-, 8- and 12-tile forms of the Gram, with a
+    ragged receiver tile, splits of one and of several full K-steps and a
+    partial last step."""
+    Hr = 150
+    say(f"head_map_cosine Hr={Hr} Hs={Hs} L={L}")
+    r = np.random.default_rng(Hs + L)
+    Lp = (L + 7) // 8 * 8
+    R = np.zeros((Hr, Lp)); R[:, :L] = r.uniform(0, 1, (Hr, L)) ** 4
+    S = np.zeros((Hs, Lp)); S[:, :L] = r.uniform(0, 1, (Hs, L)) ** 4
+    Rb, Sb = oracle.round_bf16(R), oracle.round_bf16(S)
+    cos, arg, mar = cma.head_map_cosine(dev_bf16(bf16_bits_from_f64(Rb)), dev_bf16(bf16_bits_from_f64(Sb)),
+                                        1, Hr, Hs, L, Lp, 0, Lp, 0)
+    torch.cuda.synchronize()
+    ocos, oarg, omar = oracle.head_map(Rb[:, :L], Sb[:, :L])
+    assert rel_l2(host64(cos)[0], ocos) <= 1e-5
+    big = omar > 1e-4
+    assert np.array_equal(host64(arg)[0][big].astype(int), oarg[big])
+    assert np.allclose(host64(mar)[0], omar, atol=1e-5)
+
+
 # ------------------------------------------------------------------ block compress
 @pytest.mark.parametrize("tau", [0.9, 1.0])
 def test_block_compress_small(cma, tau):
