@@ -114,6 +114,25 @@ __device__ __forceinline__ float pair32_add(float v) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Inclusive prefix sum of a float over the 64 lanes in lane order, on data-parallel
+// (DPP) lane moves, no LDS: Hillis-Steele steps of 1, 2, 4 and 8 lanes inside each
+// row of 16, then each row's total broadcast into the rows after it (lane 15 into
+// rows 1 and 3, lane 31 into rows 2 and 3). A fixed tree, so the result is the same
+// on every run. Lanes with no source lane add 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_from(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_scan_add(float x) {
+  x += dpp_from<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_from<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_from<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_from<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_from<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_from<0x143, 0xc>(x);  // row_bcast:31
+  return x;
+}
+
 // Workgroup barrier that waits for this wave's LDS accesses but, unlike
 // __syncthreads, not for its global loads (prefetches stay in flight). The empty
 // asm statements keep the compiler from moving memory accesses across it.

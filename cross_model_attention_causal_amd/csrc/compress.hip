@@ -221,16 +221,18 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
   const int nb = act ? kb0 + r + 1 : 0;
   const float* LPr = LP + 64 * gr * LPS;
   const float* lser = lse_s + 64 * gr;
+  // (every thread reads its 16 entries, those of a column past the row's last
+  // read a valid one, so that the reads are all in flight at once; rows past the
+  // sequence end then add nothing)
   for (int x0 = 0; x0 < 4 * nb; x0 += NTR) {
     const int x = x0 + tl, c = x >> 2, part = x & 3;
-    float y = 0.0f;
-    if (c < nb) {
+    const int cc = min(c, nb - 1);
+    float t[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int q = 16 * part + e;
-        if (q < nrows) y += exp2f_fast(LPr[q * LPS + c] - lser[q]);
-      }
-    }
+    for (int e = 0; e < 16; ++e) t[e] = LPr[(16 * part + e) * LPS + cc] - lser[16 * part + e];
+    float y = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) y += 16 * part + e < nrows ? exp2f_fast(t[e]) : 0.0f;
     y += __shfl_xor(y, 1, 64);  // (p0 + p1), (p2 + p3)
     y += __shfl_xor(y, 2, 64);  // (p0 + p1) + (p2 + p3)
     if (c < nb && part == 0) mass[c] = y;
@@ -249,12 +251,12 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     for (int c = tl; c < nb; c += NTR) atomicOr(&kept[c >> 5], 1u << (c & 31));
     if (tl == 0) kcount_a[gr] = nb;
   } else {
-    // total mass: one wave per row, strided partial sums then a fixed butterfly
+    // total mass: one wave per row, strided partial sums then a fixed lane tree
     if (wl == 0) {
       float x = 0.0f;
       for (int c = lane; c < nb; c += 64) x += mass[c];
-      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-      if (lane == 0) total_a[gr] = x;
+      x = wave_scan_add(x);
+      if (lane == 63) total_a[gr] = x;
     }
     __syncthreads();
     const float total = total_a[gr];
@@ -274,8 +276,8 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
     __syncthreads();
     // rank of block c = the number of blocks ahead of it: each thread of the row
     // takes its blocks and compares their keys with every key of the row (16 per
-    // step, eight broadcast reads in flight); the block's weight goes to its
-    // rank's slot
+    // step, all lanes reading the same key: broadcast reads); the block's weight
+    // goes to its rank's slot
     for (int c = tl; c < nb; c += NTR) {
       const uint64_t kc = key[c];
       int rank = 0;
@@ -302,17 +304,15 @@ __global__ __launch_bounds__(512) void k_block_stats(CompressArgs a) {
         run += x < nb ? wts[x] : 0.0f;
         cum[e] = run;
       }
-      float pre = run;
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(pre, off, 64);
-        if (lane >= off) pre += y;
-      }
-      const float before = pre - run;
-      int first = 4 * 64;
+      const float before = wave_scan_add(run) - run;
+      int mine = 4 * 64;
 #pragma unroll
       for (int e = 3; e >= 0; --e)
-        if (4 * lane + e < nb && before + cum[e] >= a.tau) first = 4 * lane + e;
-      for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+        if (4 * lane + e < nb && before + cum[e] >= a.tau) mine = 4 * lane + e;
+      // the running sum only grows: the first rank that reaches tau is the
+      // lowest lane's hit
+      const uint64_t hit = __ballot(mine < 4 * 64);
+      const int first = hit ? __builtin_amdgcn_readlane(mine, (int)__builtin_ctzll(hit)) : 4 * 64;
       if (lane == 0) kcount_a[gr] = first < nb ? first + 1 : nb;
     }
     __syncthreads();
