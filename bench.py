@@ -104,7 +104,7 @@ def measure_ceilings(reps=5):
 
     lib = cma.load_library()
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-    lib.cma_probe_read.argtypes = [P, I64, I32, P, P]
+    lib.cma_probe_read.argtypes = [P, I64, I32, I32, P, P]
     lib.cma_probe_copy.argtypes = [P, P, I64, I32, P]
     lib.cma_probe_mfma.argtypes = [I32, I32, P, P]
     lib.cma_probe_l2.argtypes = [P, I32, I32, I32, P, P]
@@ -131,8 +131,13 @@ def measure_ceilings(reps=5):
     big = 4 << 30
     a = torch.ones(big // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(cus * 8 * 512, dtype=torch.int32, device="cuda")
-    t = med(lambda: lib.cma_probe_read(a.data_ptr(), big, cus * 8, sink.data_ptr(), st))
-    out["hbm_read_GBps"] = round(big / (t * 1e-3) / 1e9, 1)
+    # reads: grid-stride and per-workgroup contiguous; the ceiling is the better
+    rd = {}
+    for mode, name in ((0, "stride"), (1, "contig")):
+        t = med(lambda: lib.cma_probe_read(a.data_ptr(), big, cus * 8, mode, sink.data_ptr(), st))
+        rd[name] = round(big / (t * 1e-3) / 1e9, 1)
+    out["hbm_read_GBps_by_pattern"] = rd
+    out["hbm_read_GBps"] = max(rd.values())
     half = big // 2
     b = torch.empty(half // 4, dtype=torch.float32, device="cuda")
     t = med(lambda: lib.cma_probe_copy(a.data_ptr(), b.data_ptr(), half, cus * 8, st))

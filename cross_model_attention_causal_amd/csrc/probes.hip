@@ -14,14 +14,27 @@ namespace cma {
 
 // grid-stride 16-byte reads of n16 chunks; the xor of what was read goes to
 // sink[thread] only if it equals `never` (it does not), so the loads stay.
+// CONTIG: workgroup b reads chunks [b * per, (b + 1) * per) in runs of 8 KB (one
+// 16-byte chunk per thread, four runs in flight), else a grid-stride loop.
+template <bool CONTIG>
 __global__ __launch_bounds__(512) void k_probe_read(const u32x4* __restrict__ src, int64_t n16, uint32_t never,
                                                      uint32_t* sink) {
   uint32_t x = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += 4 * stride) {
+  int64_t i, end, step;
+  if (CONTIG) {
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    i = (int64_t)blockIdx.x * per + threadIdx.x;
+    end = min(n16, ((int64_t)blockIdx.x + 1) * per);
+    step = blockDim.x;
+  } else {
+    i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    end = n16;
+    step = (int64_t)gridDim.x * blockDim.x;
+  }
+  for (; i < end; i += 4 * step) {
     u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = i + u * stride < n16 ? src[i + u * stride] : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < 4; ++u) v[u] = i + u * step < end ? src[i + u * step] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < 4; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
@@ -145,10 +158,16 @@ using namespace cma;
 
 extern "C" {
 
-int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, void* sink, void* stream) {
-  if (!src || !sink || bytes < 16 || n_wg < 1 || (reinterpret_cast<uintptr_t>(src) & 15)) return CMA_EINVAL;
-  hipLaunchKernelGGL(k_probe_read, dim3(n_wg), dim3(512), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), bytes / 16, 0x9e3779b9u, static_cast<uint32_t*>(sink));
+int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, int32_t mode, void* sink, void* stream) {
+  if (!src || !sink || bytes < 16 || n_wg < 1 || (mode != 0 && mode != 1) || (reinterpret_cast<uintptr_t>(src) & 15))
+    return CMA_EINVAL;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mode == 0)
+    hipLaunchKernelGGL((k_probe_read<false>), dim3(n_wg), dim3(512), 0, st, static_cast<const u32x4*>(src), bytes / 16,
+                       0x9e3779b9u, static_cast<uint32_t*>(sink));
+  else
+    hipLaunchKernelGGL((k_probe_read<true>), dim3(n_wg), dim3(512), 0, st, static_cast<const u32x4*>(src), bytes / 16,
+                       0x9e3779b9u, static_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? CMA_OK : CMA_EHIP;
 }
 

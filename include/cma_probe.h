@@ -6,8 +6,10 @@
  * caller times the launch (HIP events) and owns every buffer.
  *
  * cma_probe_read:  n_wg workgroups of 512 threads stream `bytes` (device, 16-byte
- *                  aligned) once with 16-byte loads: HBM read bandwidth for
- *                  bytes >> the 256 MB last-level cache. sink: device, n_wg * 512
+ *                  aligned) once with 16-byte loads, four in flight per thread:
+ *                  HBM read bandwidth for bytes >> the 256 MB last-level cache.
+ *                  mode 0: a grid-stride loop; 1: each workgroup reads one
+ *                  contiguous share in 8 KB runs. sink: device, n_wg * 512
  *                  uint32 (written only in a case that does not occur).
  * cma_probe_copy:  the same grid copies `bytes` from src to dst (16-byte aligned):
  *                  read + write bandwidth.
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, void* sink, void* stream);
+int cma_probe_read(const void* src, int64_t bytes, int32_t n_wg, int32_t mode, void* sink, void* stream);
 int cma_probe_copy(const void* src, void* dst, int64_t bytes, int32_t n_wg, void* stream);
 int cma_probe_write(void* dst, int64_t bytes, int32_t n_wg, int32_t mode, void* stream);
 int cma_probe_valu(int32_t kind, int32_t n_wg, int32_t iters, float* out, void* stream);
