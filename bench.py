@@ -202,6 +202,31 @@ def clocks():
     return got or None
 
 
+def cache_flush():
+    """A function that evicts the 256 MB last-level cache (MALL) by reading a 512 MB
+    buffer with the read probe on the current stream. A read leaves clean lines
+    behind: a write flush would leave up to 256 MB of dirty lines that the next
+    kernel's reads must first write back, slowing it for reasons of the flush's own."""
+    import ctypes
+    import torch
+    import cross_model_attention_causal_amd as cma
+
+    lib = cma.load_library()
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.cma_probe_read.argtypes = [P, I64, I32, I32, P, P]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(cus * 8 * 512, dtype=torch.int32, device="cuda")
+
+    def flush():
+        st = torch.cuda.current_stream().cuda_stream
+        assert lib.cma_probe_read(buf.data_ptr(), buf.numel(), cus * 8, 1, sink.data_ptr(), st) == 0
+
+    flush()
+    torch.cuda.synchronize()
+    return flush
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -227,9 +252,9 @@ def stage_figures(reps=20, warmup=3):
     cei = measure_ceilings(3)
     log("ceilings: " + json.dumps({k: v for k, v in cei.items() if k.startswith(("hbm", "mfma"))}))
     # Every timed call starts with the last-level cache (the 256 MB MALL) flushed by
-    # writing a 512 MB buffer, outside the timed interval, so that no stage is timed
+    # reading a 512 MB buffer, outside the timed interval, so that no stage is timed
     # on inputs left in the cache by its previous call.
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = cache_flush()
 
     def timed(fn, work):
         """work: kernel -> (bound, work per launch[, share of the bytes written])."""
@@ -241,7 +266,7 @@ def stage_figures(reps=20, warmup=3):
         e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         for i in range(reps):
-            flush.fill_(i & 0xff)
+            flush()
             e0[i].record()
             fn()
             e1[i].record()
@@ -507,15 +532,15 @@ def long_decode_figures(reps=20):
         st["o"] = cma.mapped_av(("dense", st["rows"], cma.DENSE), Hs, Mo, Hr, v, vl, q_rows=P)
     cei = measure_ceilings(3)
     # the step's K and V (~0.5 GB) would fit the 256 MB last-level cache in part:
-    # it is flushed (a 512 MB write) before every timed step
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # it is flushed (a 512 MB read) before every timed step
+    flush = cache_flush()
     for _ in range(3):
         step()
     torch.cuda.synchronize()
     cma.timing_reset()
     cma.timing_enable(True)
     for i in range(reps):
-        flush.fill_(i & 0xff)
+        flush()
         step()
     torch.cuda.synchronize()
     cma.timing_enable(False)
