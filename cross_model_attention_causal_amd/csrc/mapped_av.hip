@@ -326,10 +326,12 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
   // r ^ 1: the transposing reads of senders j and j + 8 then fall in different
   // LDS banks.
   const uint32_t loff0 = 16u * lane, loff1 = 16u * (lane ^ 2);
+  // Non-temporal: a stored block is read by the two head groups' workgroups and then
+  // not again (2-3 % faster than the default policy).
   auto load_stage = [&](const SendSrc& ss, int jq, u32x4 (&S)[kSend / kWaves]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kSend / kWaves; ++u)  // sender wave + 8u: (j >> 3) & 1 == u & 1
-      S[u] = __builtin_amdgcn_raw_buffer_load_b128(ss.r[u], (u & 1) ? loff1 : loff0, jq * ss.step[u], 0);
+      S[u] = __builtin_amdgcn_raw_buffer_load_b128(ss.r[u], (u & 1) ? loff1 : loff0, jq * ss.step[u], kCacheNT);
   };
   static_assert(kSend / kWaves == 4 && kWaves * kSendStride * 2 == 8704, "the offsets below assume this geometry");
   auto store_stage = [&](const u32x4 (&S)[kSend / kWaves], int b) __attribute__((always_inline)) {
