@@ -655,7 +655,6 @@ int cma_mapped_av(const cma_maps_src* src, int32_t n_send, const float* M, int64
   }
   if (src->kind != CMA_SRC_BSR) return fail(CMA_EINVAL, "bad source kind");
   if (v_dt != CMA_BF16 || d != 128) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av needs bf16 V and d = 128");
-  if (n_send > 32) return fail(CMA_EUNSUPPORTED, "block-sparse mapped_av supports n_send <= 32");
   const bool tiles = v_layout == CMA_V_TOKEN_MAJOR || v_layout == CMA_V_KEY_MAJOR;
   if (tiles) {
     const size_t need = tiled_v_bytes(src, n_v_heads, d);

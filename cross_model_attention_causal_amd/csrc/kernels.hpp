@@ -141,6 +141,10 @@ struct MappedAvArgs {
   // dense path: partial rows of split rows (workspace; NULL: rows are not split)
   float* part;
   size_t part_bytes;
+  // block-sparse path: this launch's senders are send0 .. send0 + n_send - 1 of
+  // m_ld (the row length of M); accum adds the result to out instead of storing it
+  int32_t send0, m_ld;
+  bool accum;
 };
 constexpr int kDenseSplitMax = 8;  // workgroups per row of a dense launch of few rows
 hipError_t launch_mapped_av_dense(const MappedAvArgs& a, hipStream_t st);

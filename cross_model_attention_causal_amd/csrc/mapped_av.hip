@@ -208,13 +208,13 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
     __syncthreads();  // the previous row's readers are done with these arrays
     for (int x = tid; x < (ra + 1) * kSend; x += kThreads) tbl[x] = kNoBlock;
     for (int c = tid; c <= ra; c += kThreads) anyc[c] = 0;
-    if (tid < kSend) sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)tid * a.n_block_rows + roff + r] : 0;
+    if (tid < kSend) sbeg[tid] = (tid < a.n_send) ? a.row_ptr[(int64_t)(a.send0 + tid) * a.n_block_rows + roff + r] : 0;
     __syncthreads();
     {
       constexpr int kPer = kThreads / kSend;  // threads per sender
       const int j = tid / kPer, e0 = tid % kPer;
       if (j < a.n_send) {
-        const int64_t g = (int64_t)j * a.n_block_rows + roff + r;
+        const int64_t g = (int64_t)(a.send0 + j) * a.n_block_rows + roff + r;
         const int beg = a.row_ptr[g], end = a.row_end ? a.row_end[g] : a.row_ptr[g + 1];
         for (int e = beg + e0; e < end; e += kPer) {
           const int c = a.col_idx[e];
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = 8 * q + 2 * e2 + u;
-        const float x = (p < heads_here && j < a.n_send) ? Ms[(int64_t)h * a.n_send + j] : 0.0f;
+        const float x = (p < heads_here && j < a.n_send) ? Ms[(int64_t)h * a.m_ld + a.send0 + j] : 0.0f;
         xh[u] = bf2f(f2bf(x));
         xl[u] = x - xh[u];
       }
@@ -579,8 +579,13 @@ __global__ __launch_bounds__(kThreads) void k_mapped_av_bsr(MappedAvArgs a, int 
         const int row = row_base + 8 * (v >> 2) + 4 * q2 + (v & 3);
         if (row >= n) continue;
         const int64_t o = ((int64_t)h * a.vl.total_q + cu_q_of(a.vl, s) + row) * D + 32 * dt + n32;
-        if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(acc[k][v]);
-        else reinterpret_cast<float*>(a.out)[o] = acc[k][v];
+        if (a.out_bf16) {
+          uint16_t* po = reinterpret_cast<uint16_t*>(a.out) + o;
+          *po = f2bf(a.accum ? bf2f(*po) + acc[k][v] : acc[k][v]);
+        } else {
+          float* po = reinterpret_cast<float*>(a.out) + o;
+          *po = a.accum ? *po + acc[k][v] : acc[k][v];
+        }
       }
     }
     }  // pass
@@ -1206,11 +1211,22 @@ hipError_t launch_mapped_av_bsr(const MappedAvArgs& a, hipStream_t st) {
   const int64_t units = (int64_t)n_pairs * a.vl.n_seqs;
   const int64_t rounds = (units + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(rounds * kXcds * 2 * n_hg));
-  {
-    KernelTimer kt_("k_mapped_av_bsr", st);
-    hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, a, n_pairs, n_hg, hpg);
+  // More senders than one workgroup stages: one pass per group of kSend senders,
+  // each later pass adding its product to the output (the mix is linear in M).
+  for (int j0 = 0; j0 < a.n_send; j0 += kSend) {
+    MappedAvArgs g = a;
+    g.send0 = j0;
+    g.n_send = min(kSend, a.n_send - j0);
+    g.m_ld = a.n_send;
+    g.accum = j0 > 0;
+    {
+      KernelTimer kt_("k_mapped_av_bsr", st);
+      hipLaunchKernelGGL(k_mapped_av_bsr, grid, dim3(kThreads), 0, st, g, n_pairs, n_hg, hpg);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_mapped_av_indexed(const MappedAvArgs& a, hipStream_t st) {

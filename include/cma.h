@@ -326,13 +326,15 @@ typedef struct {
  * (M_seq_stride = 0: one matrix for all). v (n_v_heads heads) in `v_layout` (see
  * cma_v_layout, with n_v_heads in place of n_recv) and out [n_recv, total_q, d]
  * in v_dt / out_dt (bf16 or f32); accumulation is fp32. n_v_heads >= 1 must
- * divide n_recv. d in {64, 128}, 1 <= n_send <= 64 (dense) or <= 32 (BSR). A BSR
+ * divide n_recv. d in {64, 128}, 1 <= n_send <= 64. A BSR source with more than
+ * 32 senders runs one pass per group of 32 (later passes add into `out`, so bf16
+ * output is rounded once per group). A BSR
  * source needs bf16 V and d = 128; its sequences are whole prompts or prefill
  * chunks as in cma_block_compress (out holds the chunk's nq rows; V its nk keys,
  * nk <= 16384); with TOKEN_MAJOR or KEY_MAJOR V it first writes the TILED copy
  * of V into `workspace` (cma_mapped_av_workspace(...) bytes: n_v_heads *
  * n_key_blocks * 64 * d * 2), with TILED or PAGED V it needs no workspace and
- * runs as a single kernel. A dense source takes TOKEN_MAJOR or KEY_MAJOR V and
+ * launches only the fused pass. A dense source takes TOKEN_MAJOR or KEY_MAJOR V and
  * needs no workspace; given one of cma_mapped_av_workspace(...) bytes (2 MiB for
  * 256 CUs at d = 128), a launch of fewer rows than twice the CUs (a long-context
  * decode of a small batch) splits each row's keys over up to 8 workgroups and

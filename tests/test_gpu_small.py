@@ -356,6 +356,35 @@ def test_mapped_av_bsr_small(cma, n_recv, v_layout, v_heads):
     assert rel_l2(got, oracle.round_bf16(refO)) <= 1e-2
 
 
+# More senders than the fused pass stages at once (32): one pass per group of 32
+# senders, each later pass adding into the output. The oracle mixes all senders
+# at once; bf16 output is rounded once per group, so it keeps the bf16 bar.
+@pytest.mark.parametrize("n_send,n_recv,out_f32", [(40, 12, True), (64, 24, False), (33, 7, True)])
+def test_mapped_av_bsr_sender_groups(cma, n_send, n_recv, out_f32):
+    lens = [200, 64, 130]
+    say(f"mapped_av bsr sender groups lens={lens} n_send={n_send} n_recv={n_recv} out_f32={out_f32}")
+    x = synth.attention_inputs(411, n_send, lens, d=128)
+    ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9)
+    M = synth.mix_matrix_learned(412, n_recv, n_send)
+    T = int(x["cu_q"][-1])
+    V = synth.values(413, n_recv, T, 128)
+    vl = cma.Varlen(x["cu_q"], x["cu_q"])
+    src = dict(row_ptr=dev_i32(ref["row_ptr"]), col_idx=dev_i32(ref["col_idx"]),
+               vals=dev_bf16(bf16_bits_from_f64(blocks_to_panels(ref["vals"]))), n_block_rows=ref["r_tot"])
+    O = cma.mapped_av(src, n_send, dev_f32(M), n_recv, dev_bf16(V), vl,
+                      out_dtype=torch.float32 if out_f32 else torch.bfloat16)
+    torch.cuda.synchronize()
+    got = host64(O)
+    rows = [(s, r) for s in range(len(lens)) for r in range((lens[s] + 63) // 64)]
+    oo = oracle.mapped_av_bsr_rows(ref["row_ptr"], ref["col_idx"], ref["vals"], n_send, lens, M, f64(V),
+                                   x["cu_q"], rows)
+    refO = np.zeros_like(got)
+    for (s, r), o in oo.items():
+        a = x["cu_q"][s] + 64 * r
+        refO[:, a: a + o.shape[1]] = o
+    assert rel_l2(got, refO if out_f32 else oracle.round_bf16(refO)) <= 1e-2
+
+
 # ------------------------------------------------------------------ mapped_av, one sender per head
 # Sender indices per (sequence, receiver head) as the cosine argmax gives them:
 # O_h = A_{idx[h]} V_{h // g}. The oracle gets the one-hot M; the general path
