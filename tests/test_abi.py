@@ -285,6 +285,10 @@ def test_workspace_too_small_is_enospc(lib):
     assert run(fake, need - 1) == -3
     assert run(None, need) == -3
     assert run(fake + 8, need) == -1                               # workspace must be 16-byte aligned
+    # more senders than two groups of 32: refused before any device work
+    assert mav(ctypes.byref(src), 65, fake, 0, 24, 24, fake, 1, V_TOKEN_MAJOR, 128, ctypes.byref(vl),
+               fake, 1, fake, need, None) == -2
+    assert b"n_send" in lib.cma_last_error()
 
 
 def test_noalloc_compress_rejects_oversized_scratch(lib):
