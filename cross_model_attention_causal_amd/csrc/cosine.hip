@@ -19,7 +19,7 @@ namespace cma {
 constexpr int kGramRows = 128;     // receiver maps per workgroup
 constexpr int kGramK = 64;         // K elements per step
 constexpr int kGramThreads = 512;  // 8 waves = 4 groups of 32 receivers x 2 halves of the sender tiles
-constexpr int kMaxSteps = 64;      // K-steps of one split (4096 elements)
+constexpr int kMaxSteps = 128;     // K-steps of one split (8192 elements)
 
 // The sender slice of a step in LDS: row j (a sender map) holds 64 elements as 8
 // chunks of 16 bytes, chunk ch in slot ch ^ ((j >> 1) & 7), so that the 16 rows
