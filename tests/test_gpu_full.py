@@ -207,6 +207,40 @@ def test_cfg4_mapped_av_full(cma, cfg3_run):
     assert np.isfinite(got).all()
 
 
+def test_cfg4_mapped_av_sender_groups_full(cma, cfg3_run):
+    """The fused pass over 64 senders at full size (two groups of 32, the second
+    pass adding into the output): the 32-head compression of the 8192-token
+    sequence stacked twice. Mixing the two copies with weights M[:, :32] and
+    M[:, 32:] equals mixing one copy with their sum, so the output is compared
+    with the oracle's product for the summed weights on sampled block-rows."""
+    x, vl, bsr = cfg3_run
+    y = synth.cfg4()
+    Hs, Hr, n = y["n_send"], y["n_recv"], y["n"]
+    R = n // 64
+    nnz = int(bsr["nnz"].item())
+    rp = bsr["row_ptr"][: Hs * R + 1]
+    stacked = dict(row_ptr=torch.cat([rp[:-1], rp + nnz]), col_idx=torch.cat([bsr["col_idx"][:nnz]] * 2),
+                   vals=torch.cat([bsr["vals"][:nnz]] * 2), n_block_rows=R)
+    M2 = synth.mix_matrix_learned(171, Hr, 2 * Hs).astype(np.float32)
+    O = cma.mapped_av(stacked, 2 * Hs, dev_f32(M2), Hr, dev_bf16(y["v"]), vl, workspace=cma.Workspace())
+    torch.cuda.synchronize()
+    got = host64(O)
+    del stacked
+    row_ptr = host64(bsr["row_ptr"]).astype(np.int64)
+    col = host64(bsr["col_idx"][:nnz]).astype(np.int64)
+    V = f64(y["v"])
+    Msum = M2[..., :Hs].astype(np.float64) + M2[..., Hs:].astype(np.float64)
+    for r in (3, 77, 126):
+        refs = [oracle.compress_block_row(f64(x["q"][j]), f64(x["k"][j]), x["scale"][j], x["bias"][j], r, x["tau"])
+                for j in range(Hs)]
+        kept_lib = [list(col[row_ptr[j * R + r]: row_ptr[j * R + r + 1]]) for j in range(Hs)]
+        rp_, ci, vv = _bsr_row_reference(refs, kept_lib, Hs, R, r)
+        ref = oracle.mapped_av_bsr_rows(rp_, ci, vv, Hs, [n], Msum, V, np.array([0, n]), [(0, r)])[(0, r)]
+        assert rel_l2(got[:, 64 * r: 64 * r + 64], oracle.round_bf16(ref)) <= 1e-2, r
+    assert np.isfinite(got).all()
+    say("cfg4 with 64 senders (two stacked copies): 3 sampled block-rows equal the oracle's summed-weight product")
+
+
 # ------------------------------------------------------------------ serving mix, one mapped layer
 def test_cfg5_serving_layer_full(cma):
     """64 x 512 + 4 x 8192 prompts packed varlen, 28 sender / 64 receiver heads:
