@@ -139,12 +139,14 @@ def _paged(cma, v, vl, n_pages, seed):
     return dict(pages=pages, table=tab)
 
 
-def test_mapped_av_chunks_and_paged_v(cma):
+@pytest.mark.parametrize("Hs", [24, 40])
+def test_mapped_av_chunks_and_paged_v(cma, Hs):
     """The fused pass (learned M) and the indexed pass over chunked block-sparse
     maps, against the oracle; V token-major (tiled in the workspace), tiled by the
-    caller and paged through a shuffled table all give the same bits."""
+    caller and paged through a shuffled table all give the same bits. With 40
+    senders the fused pass runs as two sender groups."""
     lq, lk = [448, 70, 128], [576, 198, 128]
-    Hs, Hr, Hv = 24, 20, 10
+    Hr, Hv = 20, 10
     say(f"mapped_av on chunks lq={lq} lk={lk} Hs={Hs} Hr={Hr} Hv={Hv}")
     x = _chunk_inputs(971, Hs, lq, lk)
     ref = oracle.block_compress(f64(x["q"]), f64(x["k"]), x["scale"], x["bias"], x["cu_q"], 0.9, used=lq,
